@@ -1,0 +1,235 @@
+"""Seeded synthetic inputs for the routed-MoE expert layer.
+
+This module is shared by the tests, the benchmark and the CPU oracle's
+callers. It draws random numbers and casts them to the storage dtypes; it
+holds none of the layer's arithmetic (no routing, sorting, products,
+activations or combines).
+
+Conventions
+-----------
+* ``N(0, v)`` means mean 0 and *variance* v, so weights of fan-in ``f`` are
+  drawn with standard deviation ``sqrt(1/f)``.
+* Every draw is float32 from ``numpy.random.default_rng``; bf16 tensors are
+  the round-to-nearest-even cast done by ``torch.Tensor.to(torch.bfloat16)``.
+* Routing logits, the per-expert logit bias, ``x`` and the clamp limits come
+  from one generator seeded with ``seed``, drawn in that order. Expert ``e``'s
+  rows of ``w1`` and ``w2`` come from generators seeded with
+  ``[seed, 1, e]`` and ``[seed, 2, e]``, so banks of any size are drawn
+  expert by expert (and in parallel) without holding an fp32 copy of the bank.
+* The MX (MXFP8 / MXFP4) encoders here produce *inputs* only: block scales are
+  powers of two chosen so the block maximum fits the element format, and the
+  elements are rounded to nearest, ties to even.
+"""
+from __future__ import annotations
+
+import math
+import os
+from concurrent.futures import ThreadPoolExecutor
+from dataclasses import dataclass, field
+from typing import Optional
+
+import numpy as np
+import torch
+
+__all__ = [
+    "MoECase", "GroupedGemmCase", "moe_case", "tiny_moe", "mixtral_moe",
+    "expert_shard_moe", "grouped_gemm_case", "dirichlet_group_sizes",
+    "route_logits", "bf16_to_f32", "to_bf16",
+]
+
+_THREADS = max(1, min(16, os.cpu_count() or 1))
+
+
+def to_bf16(a: np.ndarray) -> torch.Tensor:
+    """fp32 numpy array -> bf16 CPU tensor (round to nearest even)."""
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(torch.bfloat16)
+
+
+def bf16_to_f32(t: torch.Tensor) -> np.ndarray:
+    """bf16 tensor (any device) -> fp32 numpy array; the widening is exact."""
+    return t.detach().to("cpu", torch.float32).numpy()
+
+
+def _normal_bank(shape, std: float, seed: int, stream: int) -> torch.Tensor:
+    """bf16 bank [E, rows, cols]; expert e drawn from default_rng([seed, stream, e])."""
+    E = shape[0]
+    out = torch.empty(shape, dtype=torch.bfloat16)
+
+    def fill(e: int) -> None:
+        g = np.random.default_rng([seed, stream, e])
+        a = g.standard_normal(shape[1:], dtype=np.float32)
+        a *= np.float32(std)
+        out[e].copy_(torch.from_numpy(a).to(torch.bfloat16))
+
+    if E == 1:
+        fill(0)
+    else:
+        with ThreadPoolExecutor(max_workers=min(_THREADS, E)) as ex:
+            list(ex.map(fill, range(E)))
+    return out
+
+
+@dataclass
+class MoECase:
+    """One synthetic MoE-forward problem.
+
+    logits:  float32 [T, E_g] router logits (per-expert bias already added)
+    x:       bf16 [T, H]
+    w1:      bf16 [L, 2I, H]; rows 0..I-1 are the up projection, I..2I-1 the gate
+    w2:      bf16 [L, H, I]
+    limits:  float32 [L] clamp limits for SwiGLUStep, or None
+    """
+    name: str
+    T: int
+    H: int
+    I: int
+    num_experts: int
+    num_local: int
+    local_offset: int
+    top_k: int
+    activation: str  # "swiglu" | "swiglu_step"
+    logits: np.ndarray
+    x: torch.Tensor
+    w1: torch.Tensor
+    w2: torch.Tensor
+    limits: Optional[np.ndarray] = None
+    meta: dict = field(default_factory=dict)
+
+
+def route_logits(g: np.random.Generator, T: int, E: int, bias_var: float = 0.0) -> np.ndarray:
+    """logits ~ N(0,1) [T,E] float32, plus a per-expert bias ~ N(0, bias_var) if bias_var > 0."""
+    logits = g.standard_normal((T, E), dtype=np.float32)
+    if bias_var > 0.0:
+        bias = g.standard_normal((E,), dtype=np.float32) * np.float32(math.sqrt(bias_var))
+        logits = logits + bias[None, :]
+    return np.ascontiguousarray(logits, dtype=np.float32)
+
+
+def moe_case(name: str, T: int, H: int, I: int, num_experts: int, top_k: int, *,
+             num_local: Optional[int] = None, local_offset: int = 0,
+             activation: str = "swiglu", bias_var: float = 0.0, x_scale: float = 1.0,
+             limit_range: Optional[tuple] = None, seed: int = 0,
+             with_weights: bool = True) -> MoECase:
+    """Generic MoE forward case; draw order logits -> bias -> x -> limits, then weights."""
+    L = num_experts if num_local is None else num_local
+    g = np.random.default_rng(seed)
+    logits = route_logits(g, T, num_experts, bias_var)
+    xa = g.standard_normal((T, H), dtype=np.float32)
+    if x_scale != 1.0:
+        xa *= np.float32(x_scale)
+    x = to_bf16(xa)
+    limits = None
+    if limit_range is not None:
+        lo, hi = limit_range
+        limits = g.uniform(lo, hi, size=(L,)).astype(np.float32)
+    if with_weights:
+        w1 = _normal_bank((L, 2 * I, H), math.sqrt(1.0 / H), seed, 1)
+        w2 = _normal_bank((L, H, I), math.sqrt(1.0 / I), seed, 2)
+    else:
+        w1 = torch.empty((0,), dtype=torch.bfloat16)
+        w2 = torch.empty((0,), dtype=torch.bfloat16)
+    return MoECase(name, T, H, I, num_experts, L, local_offset, top_k, activation,
+                   logits, x, w1, w2, limits,
+                   meta=dict(seed=seed, bias_var=bias_var, x_scale=x_scale,
+                             limit_range=limit_range))
+
+
+def tiny_moe(seed: int = 0) -> MoECase:
+    """Tiny bf16 forward: T=32, H=128, I=256, E=8, top-2, SwiGLU."""
+    return moe_case("tiny", 32, 128, 256, 8, 2, seed=seed)
+
+
+def mixtral_moe(seed: int = 0, T: int = 4096, with_weights: bool = True) -> MoECase:
+    """Mixtral-shaped forward: H=4096, I=14336, E=8, top-2, SwiGLU, logit bias N(0, 0.5)."""
+    return moe_case("mixtral", T, 4096, 14336, 8, 2, bias_var=0.5, seed=seed,
+                    with_weights=with_weights)
+
+
+def expert_shard_moe(seed: int = 0, T: int = 8192, clamp_active: bool = False,
+                     with_weights: bool = True) -> MoECase:
+    """Fine-grained expert shard: H=7168, I=2048, 256 experts, 32 local from id 64,
+    top-8, SwiGLUStep with per-expert limits ~ U[5, 9]. ``clamp_active`` scales x
+    by 8 so that the clamp fires on a large share of the pre-activations."""
+    return moe_case("expert_shard", T, 7168, 2048, 256, 8, num_local=32, local_offset=64,
+                    activation="swiglu_step", x_scale=8.0 if clamp_active else 1.0,
+                    limit_range=(5.0, 9.0), seed=seed, with_weights=with_weights)
+
+
+def dirichlet_group_sizes(E: int = 16, total: int = 8192, alpha: float = 0.3,
+                          seed: int = 0, tile: int = 64) -> np.ndarray:
+    """Imbalanced group sizes that include one empty group, one 1-row group and no
+    other size that is a multiple of ``tile``.
+
+    1. p ~ Dirichlet(alpha), m = floor(total * p).
+    2. The group with the smallest p gets 0 rows, the next smallest gets 1.
+    3. Every other group gets at least 2 rows, and +1 if its size is a tile multiple.
+    4. The remainder goes to the largest group; if that lands on a tile multiple,
+       one row moves to the second largest.
+    """
+    g = np.random.default_rng(seed)
+    p = g.dirichlet(np.full(E, alpha))
+    m = np.floor(total * p).astype(np.int64)
+    order = np.argsort(p, kind="stable")
+    m[order[0]] = 0
+    m[order[1]] = 1
+    for e in order[2:]:
+        m[e] = max(m[e], 2)
+        if m[e] % tile == 0:
+            m[e] += 1
+    big, second = order[-1], order[-2]
+    m[big] += total - int(m.sum())
+    if m[big] % tile == 0:
+        m[big] -= 1
+        m[second] += 1
+        if m[second] % tile == 0:
+            m[second] += 1
+            m[big] -= 1
+    assert int(m.sum()) == total and m.min() >= 0
+    return m.astype(np.int32)
+
+
+@dataclass
+class GroupedGemmCase:
+    """Ragged grouped GEMM problem: groups are consecutive row ranges of X and G.
+
+    sizes: int32 [E]; offs: int32 [E] cumulative ends
+    x: bf16 [sum_m, K]; g: bf16 [sum_m, N]; w: bf16 [E, N, K]
+    """
+    sizes: np.ndarray
+    offs: np.ndarray
+    x: torch.Tensor
+    g: torch.Tensor
+    w: torch.Tensor
+
+    @property
+    def E(self) -> int:
+        return int(self.sizes.shape[0])
+
+    @property
+    def sum_m(self) -> int:
+        return int(self.offs[-1]) if self.offs.size else 0
+
+
+def grouped_gemm_case(seed: int = 0, E: int = 16, sum_m: int = 8192, K: int = 2048,
+                      N: int = 4096, sizes: Optional[np.ndarray] = None,
+                      integer_valued: bool = False) -> GroupedGemmCase:
+    """Ragged bf16 grouped GEMM inputs. X, G ~ N(0,1); W ~ N(0, 1/K).
+
+    With ``integer_valued`` every operand is an integer in [-3, 3] (exact in
+    bf16), so every fp32 partial sum is an exact integer at these sizes.
+    """
+    if sizes is None:
+        sizes = dirichlet_group_sizes(E, sum_m, seed=seed)
+    sizes = np.asarray(sizes, dtype=np.int32)
+    offs = np.cumsum(sizes).astype(np.int32)
+    M = int(offs[-1]) if offs.size else 0
+    g = np.random.default_rng([seed, 7])
+    if integer_valued:
+        x = torch.from_numpy(g.integers(-3, 4, size=(M, K)).astype(np.float32)).to(torch.bfloat16)
+        gg = torch.from_numpy(g.integers(-3, 4, size=(M, N)).astype(np.float32)).to(torch.bfloat16)
+        w = torch.from_numpy(g.integers(-3, 4, size=(len(sizes), N, K)).astype(np.float32)).to(torch.bfloat16)
+    else:
+        x = to_bf16(g.standard_normal((M, K), dtype=np.float32))
+        gg = to_bf16(g.standard_normal((M, N), dtype=np.float32))
+        w = _normal_bank((len(sizes), N, K), math.sqrt(1.0 / K), seed, 3)
+    return GroupedGemmCase(sizes, offs, x, gg, w)
