@@ -1,0 +1,223 @@
+"""Benchmark: the Mixtral-shaped routed-MoE expert layer on one MI355X.
+
+One step = one pass of the whole hot path over a resident synthetic batch:
+route (top-2 of 8 from fp32 logits) -> sort -> FC1 + SwiGLU -> FC2 -> the
+deterministic finalize, at T=4096, H=4096, I=14336, E=8, top_k=2 (bf16
+operands, fp32 accumulation). The same step with the fused finalize is timed
+as well. Prints one JSON line.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE layer TFLOP/s + tokens/s (T=4096, Mixtral shape); % of MFMA peak"
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+HBM_PEAK_GBS = 8000.0
+FC1_KERNEL = "k_gemm_nt<1>"    # FC1 grouped GEMM with the SwiGLU epilogue
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fc1_mixtral_traffic.json")
+KERNEL_SOURCES = ["mixture_experts_expert_softmax_amd/csrc/gemm_bf16.hip",
+                  "mixture_experts_expert_softmax_amd/csrc/common.h"]
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def load_traffic():
+    """HBM bytes per FC1 launch from committed rocprofv3 counter runs, valid only
+    while the kernel source is unchanged since the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(case, ids, w, n_tokens, n_experts):
+    """Time the CPU oracle on a bounded sample of the same workload: the first
+    n_tokens tokens, evaluated on the shard of the first n_experts experts (routes
+    to other experts are skipped by the oracle's shard rule)."""
+    import numpy as np
+    import moe_synth as S
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    x = S.bf16_to_f32(case.x[:n_tokens])
+    w1 = S.bf16_to_f32(case.w1[:n_experts])
+    w2 = S.bf16_to_f32(case.w2[:n_experts])
+    ids_n, w_n = ids[:n_tokens], w[:n_tokens].astype(np.float64)
+    routes = int(np.count_nonzero(ids_n < n_experts))
+    t0 = time.perf_counter()
+    O.moe_forward(x, ids_n, w_n, w1, w2, num_experts=case.num_experts, local_offset=0)
+    dt = time.perf_counter() - t0
+    flops = 6.0 * case.H * case.I * routes
+    cpu = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    # tokens/s scaled from routes/s: a token carries top_k routes
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "tokens_per_s": routes / case.top_k / dt, "seconds": dt, "routes": routes,
+            "sample": f"{routes} routes: first {n_tokens} of {case.T} tokens on the shard of experts "
+                      f"0..{n_experts - 1} of {case.num_experts}; numpy float64 oracle incl. "
+                      f"per-expert weight widening; {cpu}"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cpu-tokens", type=int, default=512)
+    ap.add_argument("--cpu-experts", type=int, default=1)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import mixture_experts_expert_softmax_amd as M
+    import moe_synth as S
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    M.lib()  # fail loudly if the HIP library is missing
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    def progress(msg):
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+    progress("generating the synthetic Mixtral-shaped batch")
+    case = S.mixtral_moe(seed=0)
+    T, H, I, E, k = case.T, case.H, case.I, case.num_experts, case.top_k
+    logits = torch.from_numpy(case.logits).to(dev)
+    x, w1, w2 = case.x.to(dev), case.w1.to(dev), case.w2.to(dev)
+    ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    wts = torch.empty((T, k), dtype=torch.float32, device=dev)
+    sort_ws = torch.empty(max(M.lib().moe_sort_workspace_size(T, k, E), 16), dtype=torch.uint8, device=dev)
+    offs = torch.empty(E, dtype=torch.int32, device=dev)
+    e2p = torch.empty(T * k, dtype=torch.int32, device=dev)
+    p2e = torch.empty(T * k, dtype=torch.int32, device=dev)
+    nloc = torch.empty(1, dtype=torch.int32, device=dev)
+    act = torch.empty((T * k, I), dtype=torch.bfloat16, device=dev)
+    y = torch.empty((T * k, H), dtype=torch.bfloat16, device=dev)
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    out_fused = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    lib = M.lib()
+    P = M._ptr
+
+    def route():
+        M._check("moe_route", lib.moe_route(P(logits), T, E, k, P(ids), P(wts), M._stream()))
+
+    def sort():
+        M._check("moe_sort", lib.moe_sort(P(ids), T, k, E, E, 0, P(offs), None, P(e2p), P(p2e), P(nloc),
+                                          P(sort_ws), sort_ws.numel(), M._stream()))
+
+    def fc1():
+        M.moe_fc1(x, w1, offs, p2e, k, E, act=act)
+
+    def fc2(fused=False):
+        if fused:
+            M.moe_fc2(act, w2, offs, T, k, E, finalize="fused", p2e=p2e, topk_weights=wts, dst=out_fused)
+        else:
+            M.moe_fc2(act, w2, offs, T, k, E, dst=y)
+
+    def finalize():
+        M.moe_finalize(y, e2p, wts, out=out)
+
+    stages = [("route", route), ("sort", sort), ("fc1", fc1), ("fc2", fc2), ("finalize", finalize)]
+    stages_fused = [("route", route), ("sort", sort), ("fc1", fc1), ("fc2_fused", lambda: fc2(True))]
+
+    def run(stage_list, steps, warmup):
+        for _ in range(warmup):
+            for _, f in stage_list:
+                f()
+        torch.cuda.synchronize()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stage_list) + 1)] for _ in range(steps)]
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        start.record()
+        for s in range(steps):
+            ev[s][0].record()
+            for j, (_, f) in enumerate(stage_list):
+                f()
+                ev[s][j + 1].record()
+        end.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        total_ms = start.elapsed_time(end) / steps
+        per_stage = {name: float(np.mean([ev[s][j].elapsed_time(ev[s][j + 1]) for s in range(steps)]))
+                     for j, (name, _) in enumerate(stage_list)}
+        return total_ms, per_stage, wall
+
+    progress("timing the deterministic-finalize step")
+    ms, per_stage, wall = run(stages, args.steps, args.warmup)
+    progress("timing the fused-finalize step")
+    ms_f, per_stage_f, _ = run(stages_fused, args.steps, args.warmup)
+    n_local = int(nloc.item())
+    flops = 6.0 * H * I * n_local            # FC1 (4HI) + FC2 (2HI) per local route
+    fc1_flops = 4.0 * H * I * n_local
+    tflops = flops / (ms * 1e-3) / 1e12
+    fc1_tflops = fc1_flops / (per_stage["fc1"] * 1e-3) / 1e12
+    fc2_tflops = 2.0 * H * I * n_local / (per_stage["fc2"] * 1e-3) / 1e12
+    # finalize: reads n_local y rows + ids/weights, writes T output rows (bf16)
+    fin_bytes = n_local * H * 2 + T * H * 2 + T * k * 8
+    traffic = load_traffic()
+    cpu = None
+    if not args.no_cpu_baseline:
+        progress("timing the CPU oracle sample")
+        cpu = cpu_baseline(case, ids.cpu().numpy(), wts.cpu().numpy(), args.cpu_tokens, args.cpu_experts)
+    line = {
+        "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "mixtral_moe_forward", "T": T, "H": H, "I": I, "num_experts": E,
+                   "top_k": k, "activation": "swiglu", "finalize": "deterministic",
+                   "logit_bias_var": 0.5, "seed": 0, "n_local_routes": n_local},
+        "tokens_per_s": round(T / (ms * 1e-3), 1),
+        "mfma_frac_layer": round(tflops / BF16_PEAK_TFLOPS, 4),
+        "stage_ms": {k_: round(v, 4) for k_, v in per_stage.items()},
+        "fc2_tflops": round(fc2_tflops, 2),
+        "finalize_gbs": round(fin_bytes / (per_stage["finalize"] * 1e-3) / 1e9, 1),
+        "fused_finalize": {"ms_per_step": round(ms_f, 4),
+                           "value": round(flops / (ms_f * 1e-3) / 1e12, 2),
+                           "tokens_per_s": round(T / (ms_f * 1e-3), 1),
+                           "stage_ms": {k_: round(v, 4) for k_, v in per_stage_f.items()}},
+        "roofline": {"kernel": FC1_KERNEL, "bound": "mfma", "achieved": round(fc1_tflops, 2),
+                     "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(fc1_tflops / BF16_PEAK_TFLOPS, 4), "traffic": traffic},
+        "cpu_baseline": cpu,
+        "wall_s_timed": round(wall, 3),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,216 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) routed Mixture-of-Experts expert layer.
+ *
+ * The operations follow these documentation pages (cited by title and section):
+ *   [StepFun]  "flashinfer.experimental.cake_stepfun_moe": intro (stage list:
+ *              routing with Renormalize top-k, FC1 with the StepFun epilogue, FC2,
+ *              finalize), "Unified MoE API opt-in" (SwiGLUStep(limit) with a
+ *              per-expert clamp limit, default 7.0), "Prepared launches"
+ *              (no allocation, no host synchronisation; expanded_idx_to_permuted_idx).
+ *   [W4A8]     "flashinfer.fused_moe.cake / cake_cute (MXFP4 SiTU routed MoE)":
+ *              "Host plan" (workspace sized from the token count; canonical
+ *              [up | gate] w1 bank; tensor layouts; expert parallel arguments).
+ *   [GGEMM]    "Cake ragged BF16 grouped GEMM (experimental)": intro and operation
+ *              table (fwd / dgrad / wgrad; offs or m_indptr read on the device; no
+ *              padding; empty groups give zero weight gradients), "Prepared
+ *              launches" (new offsets may be written between launches).
+ *   [SM90]     "flashinfer.fused_moe.cute_dsl_fused_moe_bf16": formula
+ *              out[t] = sum_k scale[t,k] * ffn(x[t]; e[t,k]), "Supported
+ *              configuration" (shape rules, num_tokens == 0, EP shard),
+ *              Parameters (use_fused_finalize, moe_output).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every tensor argument is a DEVICE pointer to dense row-major memory owned by
+ *   the caller; bf16 tensors are passed as `const void*` (IEEE bfloat16 bits).
+ * - `stream` is a hipStream_t (NULL = the null stream). Work is only enqueued:
+ *   no call allocates device or host memory, synchronises the host, or reads
+ *   device memory from the host. Outputs are valid once the stream reaches them.
+ * - Device data is never validated (that would need a host synchronisation).
+ *   Routing ids outside [0, num_experts) are treated as routes to a foreign
+ *   expert; non-monotone group offsets are undefined behaviour.
+ * - Every call returns moe_status: MOE_OK (0) or an error; on error nothing has
+ *   been enqueued, except MOE_ERR_HIP (a launch failed after earlier launches of
+ *   the same call were enqueued). Nothing throws, aborts or prints.
+ * - Calls keep no state between invocations; concurrent calls on different
+ *   streams are safe when their outputs and workspaces are distinct.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t moe_status;
+
+#define MOE_OK               0
+#define MOE_ERR_NULL         1  /* a required pointer is NULL */
+#define MOE_ERR_SHAPE        2  /* a size is negative, zero where it must not be, or breaks a divisibility rule */
+#define MOE_ERR_DTYPE        3  /* unknown or unsupported dtype / mode enum */
+#define MOE_ERR_ALIGN        4  /* a tensor pointer is not 16-byte aligned */
+#define MOE_ERR_UNSUPPORTED  5  /* valid request this library does not serve */
+#define MOE_ERR_WORKSPACE    6  /* workspace NULL or smaller than the *_workspace_size query */
+#define MOE_ERR_HIP          7  /* a kernel launch failed */
+
+/* Element types. */
+#define MOE_DTYPE_BF16 0
+#define MOE_DTYPE_F32  1
+
+/* Activation applied to the FC1 output h = [up | gate] ([W4A8] Host plan: up rows then gate rows). */
+#define MOE_ACT_SWIGLU      0  /* silu(gate) * up  ([SM90] formula) */
+#define MOE_ACT_SWIGLU_STEP 1  /* silu(clamp(gate,-L,L)) * clamp(up,-L,L), L per expert ([StepFun]) */
+
+/* How moe_ffn_forward combines the top-k route outputs ([SM90] use_fused_finalize). */
+#define MOE_FINALIZE_DETERMINISTIC 0  /* FC2 rows, then the fixed-order fp32 combine (moe_finalize) */
+#define MOE_FINALIZE_FUSED         1  /* FC2 epilogue adds w*y into a zeroed output with bf16 atomics */
+#define MOE_FINALIZE_NONE          2  /* stop after FC2: return y rows and e2p ([StepFun] do_finalize=False) */
+
+/* Meaning of a grouped-GEMM offsets array ([GGEMM] intro). */
+#define MOE_OFFS_ENDS   0  /* offs[E]: cumulative end row of each group */
+#define MOE_OFFS_INDPTR 1  /* m_indptr[E+1]: leading zero, then cumulative ends */
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* moe_status_string(moe_status status);
+
+/* Library version string (static). */
+const char* moe_version(void);
+
+/*
+ * moe_route -- renormalized top-k routing from logits ([StepFun] intro: routing,
+ * Renormalize top-k).
+ *   logits        [T, num_experts] float32
+ *   topk_ids      [T, top_k] int32 out: slot s holds the expert with the (s+1)-th
+ *                 largest logit; equal logits go to the lower expert id
+ *   topk_weights  [T, top_k] float32 out: softmax of the selected logits (equal to
+ *                 softmax over all experts renormalized over the k selected)
+ * Rules: 1 <= num_experts <= 1024, 1 <= top_k <= min(num_experts, 16). T == 0 is a no-op.
+ * NaN logits are not supported.
+ */
+moe_status moe_route(const float* logits, int64_t T, int32_t num_experts, int32_t top_k,
+                     int32_t* topk_ids, float* topk_weights, void* stream);
+
+/*
+ * moe_sort -- stable, unpadded counting sort of the T*top_k routes by local expert
+ * ([GGEMM] intro: consecutive row groups, offs / m_indptr, no padding; [StepFun]
+ * Prepared launches: expanded_idx_to_permuted_idx; [SM90] Parameters: EP shard of
+ * num_local_experts experts starting at global id local_expert_offset).
+ * Expanded index i = t*top_k + s. Route i is local when
+ * 0 <= topk_ids[i] < num_experts and 0 <= topk_ids[i]-local_expert_offset < num_local_experts.
+ *   offs      [L] int32 out: cumulative end row of each local expert
+ *   m_indptr  [L+1] int32 out, may be NULL: [0, offs...]
+ *   e2p       [T*top_k] int32 out: permuted row of route i, -1 if foreign
+ *   p2e       [T*top_k] int32 out (capacity): p2e[p] = route i of permuted row p,
+ *             for p < n_local; entries past n_local are not written
+ *   n_local   [1] int32 out: number of local routes
+ *   ws        workspace of moe_sort_workspace_size(T, top_k, L) bytes (device)
+ * Within an expert, rows keep ascending expanded-index order. T == 0 still writes
+ * zero offsets and n_local = 0.
+ */
+size_t moe_sort_workspace_size(int64_t T, int32_t top_k, int32_t num_local_experts);
+moe_status moe_sort(const int32_t* topk_ids, int64_t T, int32_t top_k, int32_t num_experts,
+                    int32_t num_local_experts, int32_t local_expert_offset,
+                    int32_t* offs, int32_t* m_indptr, int32_t* e2p, int32_t* p2e,
+                    int32_t* n_local, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Ragged bf16 grouped GEMMs ([GGEMM] operation table). Group e owns rows
+ * [offs[e-1], offs[e]) of the packed row operands (offs[-1] = 0); `offs` is
+ * read on the device at every launch. fp32 accumulation in a fixed order (no
+ * atomics): results are bitwise reproducible. Rows past the last offset are
+ * neither read nor written (wgrad ignores them).
+ *   offs_kind  MOE_OFFS_ENDS (offs has E entries) or MOE_OFFS_INDPTR (E+1 entries)
+ * Shape rules: E >= 1, N % 32 == 0, K % 32 == 0, sum_m >= 0.
+ *
+ * grouped_gemm_fwd:   y[r] = x[r] @ w[e].T      x [sum_m,K], w [E,N,K] -> y [sum_m,N] bf16
+ * grouped_gemm_dgrad: dx[r] = g[r] @ w[e]       g [sum_m,N], w [E,N,K] -> dx [sum_m,K] bf16
+ *                     (w is read in place, not transposed or copied)
+ * grouped_gemm_wgrad: dw[e] = g[rows e].T @ x[rows e]  -> dw [E,N,K], out_dtype bf16 or f32;
+ *                     an empty group's dw[e] is written as exact zeros.
+ */
+moe_status grouped_gemm_fwd(const void* x, const void* w, const int32_t* offs, int32_t offs_kind,
+                            int32_t E, int64_t sum_m, int32_t N, int32_t K, void* y, void* stream);
+moe_status grouped_gemm_dgrad(const void* g, const void* w, const int32_t* offs, int32_t offs_kind,
+                              int32_t E, int64_t sum_m, int32_t N, int32_t K, void* dx, void* stream);
+size_t grouped_gemm_wgrad_workspace_size(int32_t E, int64_t sum_m, int32_t N, int32_t K,
+                                         int32_t out_dtype);
+moe_status grouped_gemm_wgrad(const void* g, const void* x, const int32_t* offs, int32_t offs_kind,
+                              int32_t E, int64_t sum_m, int32_t N, int32_t K, void* dw,
+                              int32_t out_dtype, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_ffn_forward -- the expert layer after routing ([SM90] formula):
+ *   out[t] = sum over slots s of topk_weights[t,s] * ffn(x[t]; topk_ids[t,s]),
+ *   ffn(x; e) = act(x @ w1[e].T) @ w2[e].T, routes to foreign experts contribute 0.
+ * Steps: moe_sort -> FC1 grouped GEMM over gathered x rows with the activation in
+ * its epilogue (act rows in bf16) -> FC2 grouped GEMM -> combine per finalize_mode.
+ */
+typedef struct moe_ffn_desc {
+  int64_t T;                  /* tokens (>= 0) */
+  int32_t H;                  /* hidden size, H % 64 == 0 */
+  int32_t I;                  /* intermediate size, I % 32 == 0 */
+  int32_t num_experts;        /* global experts E_g */
+  int32_t num_local_experts;  /* L; 0 means num_experts */
+  int32_t local_expert_offset;/* global id of local expert 0 */
+  int32_t top_k;              /* 1..16 */
+  int32_t activation;         /* MOE_ACT_* */
+  int32_t finalize_mode;      /* MOE_FINALIZE_* */
+} moe_ffn_desc;
+
+typedef struct moe_ffn_tensors {
+  const void* x;              /* [T, H] bf16 */
+  const int32_t* topk_ids;    /* [T, top_k] int32 global expert ids */
+  const float* topk_weights;  /* [T, top_k] float32, normalized by the caller */
+  const void* w1;             /* [L, 2I, H] bf16: rows 0..I-1 up, I..2I-1 gate */
+  const void* w2;             /* [L, H, I] bf16 */
+  const float* clamp_limit;   /* [L] float32 SwiGLUStep limits, or NULL for 7.0 */
+  void* out;                  /* [T, H] bf16 (DETERMINISTIC / FUSED), fully overwritten */
+  void* y;                    /* NONE only: [T*top_k, H] bf16 capacity, FC2 rows in permuted order */
+  int32_t* e2p;               /* NONE only (optional otherwise): [T*top_k] int32 */
+} moe_ffn_tensors;
+
+size_t moe_ffn_workspace_size(const moe_ffn_desc* desc);
+moe_status moe_ffn_forward(const moe_ffn_desc* desc, const moe_ffn_tensors* tensors,
+                           void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * The two GEMM stages of moe_ffn_forward as separate calls ([StepFun] "One-shot
+ * functions": fc1, fc2), for callers that run routing, sort and finalize
+ * themselves. `offs` [L] and `p2e` come from moe_sort over the same topk_ids;
+ * rows are in permuted (expert-sorted) order and only the first offs[L-1] rows
+ * are touched; row capacity is T*top_k.
+ *
+ * moe_fc1: act[p, :] = activation(x[p2e[p] / top_k] @ w1[e].T) for the rows p of
+ *          local expert e. x [T,H] bf16, w1 [L,2I,H] bf16 ([up | gate] rows),
+ *          clamp_limit [L] float32 or NULL (7.0) for MOE_ACT_SWIGLU_STEP,
+ *          act [T*top_k, I] bf16 out.
+ * moe_fc2: y[p, :] = act[p] @ w2[e].T. finalize_mode DETERMINISTIC or NONE writes
+ *          the unscaled rows to `dst` = y [T*top_k, H] bf16. FUSED zero-fills
+ *          `dst` = out [T, H] bf16 and adds topk_weights[p2e[p]] * y[p] into row
+ *          p2e[p] / top_k with bf16 atomics (not bitwise reproducible for top_k > 2).
+ */
+moe_status moe_fc1(const moe_ffn_desc* desc, const void* x, const void* w1,
+                   const float* clamp_limit, const int32_t* offs, const int32_t* p2e, void* act,
+                   void* stream);
+moe_status moe_fc2(const moe_ffn_desc* desc, const void* act, const void* w2,
+                   const int32_t* offs, const int32_t* p2e, const float* topk_weights, void* dst,
+                   void* stream);
+
+/*
+ * moe_finalize -- deterministic top-k combine ([SM90] use_fused_finalize=False):
+ *   out[t,:] = bf16_rne( sum over s = 0..top_k-1 with e2p[t*top_k+s] >= 0 of
+ *                        topk_weights[t,s] * y[e2p[t*top_k+s], :] )
+ * summed in float32 in ascending s, one rounding at the end; tokens with no local
+ * route get a zero row. y [*, H] bf16 rows in permuted order; out [T, H] bf16.
+ * Rules: H % 8 == 0, 1 <= top_k <= 16.
+ */
+moe_status moe_finalize(const void* y, const int32_t* e2p, const float* topk_weights, int64_t T,
+                        int32_t top_k, int32_t H, void* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_MI355X_H */

@@ -1,0 +1,310 @@
+"""MI355X (gfx950) routed Mixture-of-Experts expert layer.
+
+A thin ctypes binding over the HIP library ``libmoe_mi355x.so`` (built from
+``csrc/`` by ``_build.py``). Every function here only marshals arguments:
+PyTorch tensors provide device memory and the current HIP stream, and every
+step of the computation runs in the library's kernels. If the library is
+missing the functions raise; there is no fallback.
+
+Entry points (same names as the C ABI in include/moe.h):
+``moe_route``, ``moe_sort``, ``grouped_gemm_fwd``, ``grouped_gemm_dgrad``,
+``grouped_gemm_wgrad``, ``moe_ffn_forward``, ``moe_finalize``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+__all__ = [
+    "MoeError", "lib", "library_path", "EXPORTS", "moe_route", "moe_sort", "grouped_gemm_fwd",
+    "grouped_gemm_dgrad", "grouped_gemm_wgrad", "moe_ffn_forward", "moe_ffn_workspace_size",
+    "moe_finalize", "moe_fc1", "moe_fc2", "status_string", "ACT", "FINALIZE",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_HERE, "libmoe_mi355x.so")
+
+ACT = {"swiglu": 0, "swiglu_step": 1}
+FINALIZE = {"deterministic": 0, "fused": 1, "none": 2}
+OFFS = {"ends": 0, "indptr": 1}
+DTYPE = {torch.bfloat16: 0, torch.float32: 1}
+
+_i32, _i64, _u64, _vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64, ctypes.c_void_p
+_sz = ctypes.c_size_t
+
+
+class MoeFfnDesc(ctypes.Structure):
+    _fields_ = [("T", _i64), ("H", _i32), ("I", _i32), ("num_experts", _i32),
+                ("num_local_experts", _i32), ("local_expert_offset", _i32), ("top_k", _i32),
+                ("activation", _i32), ("finalize_mode", _i32)]
+
+
+class MoeFfnTensors(ctypes.Structure):
+    _fields_ = [("x", _vp), ("topk_ids", _vp), ("topk_weights", _vp), ("w1", _vp), ("w2", _vp),
+                ("clamp_limit", _vp), ("out", _vp), ("y", _vp), ("e2p", _vp)]
+
+
+# name -> (restype, argtypes)
+EXPORTS = {
+    "moe_status_string": (ctypes.c_char_p, [_i32]),
+    "moe_version": (ctypes.c_char_p, []),
+    "moe_route": (_i32, [_vp, _i64, _i32, _i32, _vp, _vp, _vp]),
+    "moe_sort_workspace_size": (_sz, [_i64, _i32, _i32]),
+    "moe_sort": (_i32, [_vp, _i64, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "grouped_gemm_fwd": (_i32, [_vp, _vp, _vp, _i32, _i32, _i64, _i32, _i32, _vp, _vp]),
+    "grouped_gemm_dgrad": (_i32, [_vp, _vp, _vp, _i32, _i32, _i64, _i32, _i32, _vp, _vp]),
+    "grouped_gemm_wgrad_workspace_size": (_sz, [_i32, _i64, _i32, _i32, _i32]),
+    "grouped_gemm_wgrad": (_i32, [_vp, _vp, _vp, _i32, _i32, _i64, _i32, _i32, _vp, _i32, _vp, _sz, _vp]),
+    "moe_ffn_workspace_size": (_sz, [ctypes.POINTER(MoeFfnDesc)]),
+    "moe_ffn_forward": (_i32, [ctypes.POINTER(MoeFfnDesc), ctypes.POINTER(MoeFfnTensors), _vp, _sz, _vp]),
+    "moe_finalize": (_i32, [_vp, _vp, _vp, _i64, _i32, _i32, _vp, _vp]),
+    "moe_fc1": (_i32, [ctypes.POINTER(MoeFfnDesc), _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "moe_fc2": (_i32, [ctypes.POINTER(MoeFfnDesc), _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+}
+
+_LIB: Optional[ctypes.CDLL] = None
+
+
+class MoeError(RuntimeError):
+    """A library call returned a non-zero moe_status."""
+
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn}: {status_string(status)} (status {status})")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """Load the HIP library (raises if it has not been built)."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(library_path):
+            raise ImportError(f"{library_path} is missing: build it with "
+                              "`python -m mixture_experts_expert_softmax_amd._build`")
+        h = ctypes.CDLL(library_path)
+        for name, (res, args) in EXPORTS.items():
+            f = getattr(h, name)
+            f.restype = res
+            f.argtypes = args
+        _LIB = h
+    return _LIB
+
+
+def status_string(status: int) -> str:
+    return lib().moe_status_string(int(status)).decode()
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise MoeError(fn, status)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dev(t: torch.Tensor, dtype, name: str) -> torch.Tensor:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+# --------------------------------------------------------------------------- routing
+def moe_route(logits: torch.Tensor, top_k: int, topk_ids=None, topk_weights=None):
+    """Renormalized top-k routing: logits [T, E] fp32 -> (ids [T,k] i32, weights [T,k] fp32)."""
+    _dev(logits, torch.float32, "logits")
+    T, E = logits.shape
+    if topk_ids is None:
+        topk_ids = torch.empty((T, top_k), dtype=torch.int32, device=logits.device)
+    if topk_weights is None:
+        topk_weights = torch.empty((T, top_k), dtype=torch.float32, device=logits.device)
+    _check("moe_route", lib().moe_route(_ptr(logits), T, E, top_k, _ptr(topk_ids),
+                                        _ptr(topk_weights), _stream()))
+    return topk_ids, topk_weights
+
+
+def moe_sort(topk_ids: torch.Tensor, num_experts: int, num_local_experts: Optional[int] = None,
+             local_expert_offset: int = 0, workspace: Optional[torch.Tensor] = None):
+    """Stable counting sort by local expert. Returns a dict of device tensors:
+    offs [L], m_indptr [L+1], e2p [T*k], p2e [T*k] (valid below n_local), n_local [1]."""
+    _dev(topk_ids, torch.int32, "topk_ids")
+    T, k = topk_ids.shape
+    L = num_experts if num_local_experts is None else num_local_experts
+    dev = topk_ids.device
+    h = lib()
+    ws_bytes = h.moe_sort_workspace_size(T, k, L)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    out = dict(offs=torch.empty(L, dtype=torch.int32, device=dev),
+               m_indptr=torch.empty(L + 1, dtype=torch.int32, device=dev),
+               e2p=torch.empty(max(T * k, 1), dtype=torch.int32, device=dev),
+               p2e=torch.empty(max(T * k, 1), dtype=torch.int32, device=dev),
+               n_local=torch.empty(1, dtype=torch.int32, device=dev))
+    _check("moe_sort", h.moe_sort(_ptr(topk_ids), T, k, num_experts, L, local_expert_offset,
+                                  _ptr(out["offs"]), _ptr(out["m_indptr"]), _ptr(out["e2p"]),
+                                  _ptr(out["p2e"]), _ptr(out["n_local"]), _ptr(workspace),
+                                  workspace.numel(), _stream()))
+    out["e2p"] = out["e2p"][: T * k]
+    return out
+
+
+# --------------------------------------------------------------------------- grouped GEMM
+def grouped_gemm_fwd(x: torch.Tensor, w: torch.Tensor, offs: torch.Tensor, out=None,
+                     offs_kind: Optional[str] = None):
+    """y[rows of e] = x[rows of e] @ w[e].T; x [M,K], w [E,N,K], offs int32 ends [E] (or indptr)."""
+    _dev(x, torch.bfloat16, "x"), _dev(w, torch.bfloat16, "w")
+    E, N, K = w.shape
+    kind = offs_kind or ("ends" if offs.numel() == E else "indptr")
+    _dev(offs, torch.int32, "offs")
+    M = x.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    _check("grouped_gemm_fwd", lib().grouped_gemm_fwd(_ptr(x), _ptr(w), _ptr(offs), OFFS[kind], E, M,
+                                                      N, K, _ptr(out), _stream()))
+    return out
+
+
+def grouped_gemm_dgrad(g: torch.Tensor, w: torch.Tensor, offs: torch.Tensor, out=None,
+                       offs_kind: Optional[str] = None):
+    """dx[rows of e] = g[rows of e] @ w[e]; g [M,N], w [E,N,K] -> dx [M,K] bf16."""
+    _dev(g, torch.bfloat16, "g"), _dev(w, torch.bfloat16, "w")
+    E, N, K = w.shape
+    kind = offs_kind or ("ends" if offs.numel() == E else "indptr")
+    _dev(offs, torch.int32, "offs")
+    M = g.shape[0]
+    if out is None:
+        out = torch.empty((M, K), dtype=torch.bfloat16, device=g.device)
+    _check("grouped_gemm_dgrad", lib().grouped_gemm_dgrad(_ptr(g), _ptr(w), _ptr(offs), OFFS[kind], E,
+                                                          M, N, K, _ptr(out), _stream()))
+    return out
+
+
+def grouped_gemm_wgrad(g: torch.Tensor, x: torch.Tensor, offs: torch.Tensor, E: Optional[int] = None,
+                       out=None, out_dtype=torch.bfloat16, offs_kind: Optional[str] = None):
+    """dw[e] = g[rows of e].T @ x[rows of e] -> [E, N, K] in bf16 or fp32."""
+    _dev(g, torch.bfloat16, "g"), _dev(x, torch.bfloat16, "x")
+    _dev(offs, torch.int32, "offs")
+    kind = offs_kind or "ends"
+    if E is None:
+        E = offs.numel() if kind == "ends" else offs.numel() - 1
+    M, N = g.shape
+    K = x.shape[1]
+    if out is None:
+        out = torch.empty((E, N, K), dtype=out_dtype, device=g.device)
+    h = lib()
+    ws = h.grouped_gemm_wgrad_workspace_size(E, M, N, K, DTYPE[out.dtype])
+    wsb = torch.empty(max(ws, 16), dtype=torch.uint8, device=g.device) if ws else None
+    _check("grouped_gemm_wgrad", h.grouped_gemm_wgrad(_ptr(g), _ptr(x), _ptr(offs), OFFS[kind], E, M, N,
+                                                      K, _ptr(out), DTYPE[out.dtype], _ptr(wsb), ws,
+                                                      _stream()))
+    return out
+
+
+# --------------------------------------------------------------------------- MoE layer
+def _ffn_desc(T, H, I, num_experts, L, off, k, activation, finalize):
+    return MoeFfnDesc(T, H, I, num_experts, L, off, k, ACT[activation], FINALIZE[finalize])
+
+
+def moe_ffn_workspace_size(T, H, I, num_experts, top_k, num_local_experts=None,
+                           local_expert_offset=0, activation="swiglu", finalize="deterministic"):
+    L = num_experts if num_local_experts is None else num_local_experts
+    d = _ffn_desc(T, H, I, num_experts, L, local_expert_offset, top_k, activation, finalize)
+    return lib().moe_ffn_workspace_size(ctypes.byref(d))
+
+
+def moe_ffn_forward(x: torch.Tensor, topk_ids: torch.Tensor, topk_weights: torch.Tensor,
+                    w1: torch.Tensor, w2: torch.Tensor, num_experts: int,
+                    num_local_experts: Optional[int] = None, local_expert_offset: int = 0,
+                    activation: str = "swiglu", clamp_limit: Optional[torch.Tensor] = None,
+                    finalize: str = "deterministic", out: Optional[torch.Tensor] = None,
+                    workspace: Optional[torch.Tensor] = None, y: Optional[torch.Tensor] = None,
+                    e2p: Optional[torch.Tensor] = None):
+    """out[t] = sum_s topk_weights[t,s] * ffn(x[t]; topk_ids[t,s]) (foreign routes give 0).
+
+    finalize="none" returns (y [T*k, H] rows in permuted order, e2p [T*k]) instead of out.
+    """
+    _dev(x, torch.bfloat16, "x"), _dev(w1, torch.bfloat16, "w1"), _dev(w2, torch.bfloat16, "w2")
+    _dev(topk_ids, torch.int32, "topk_ids"), _dev(topk_weights, torch.float32, "topk_weights")
+    if clamp_limit is not None:
+        _dev(clamp_limit, torch.float32, "clamp_limit")
+    T, H = x.shape
+    L, twoI, _ = w1.shape
+    I = twoI // 2
+    k = topk_ids.shape[1]
+    d = _ffn_desc(T, H, I, num_experts, L, local_expert_offset, k, activation, finalize)
+    h = lib()
+    ws_bytes = h.moe_ffn_workspace_size(ctypes.byref(d))
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=x.device)
+    if finalize == "none":
+        if y is None:
+            y = torch.empty((max(T * k, 1), H), dtype=torch.bfloat16, device=x.device)
+        if e2p is None:
+            e2p = torch.empty(max(T * k, 1), dtype=torch.int32, device=x.device)
+    elif out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
+    tens = MoeFfnTensors(x.data_ptr(), topk_ids.data_ptr(), topk_weights.data_ptr(), w1.data_ptr(),
+                         w2.data_ptr(), None if clamp_limit is None else clamp_limit.data_ptr(),
+                         None if out is None else out.data_ptr(), None if y is None else y.data_ptr(),
+                         None if e2p is None else e2p.data_ptr())
+    _check("moe_ffn_forward", h.moe_ffn_forward(ctypes.byref(d), ctypes.byref(tens), _ptr(workspace),
+                                                workspace.numel(), _stream()))
+    if finalize == "none":
+        return y, e2p[: T * k]
+    return out
+
+
+def moe_fc1(x: torch.Tensor, w1: torch.Tensor, offs: torch.Tensor, p2e: torch.Tensor, top_k: int,
+            num_experts: int, local_expert_offset: int = 0, activation: str = "swiglu",
+            clamp_limit: Optional[torch.Tensor] = None, act: Optional[torch.Tensor] = None):
+    """act[p] = activation(x[p2e[p] // top_k] @ w1[e].T) for the expert-sorted rows p."""
+    _dev(x, torch.bfloat16, "x"), _dev(w1, torch.bfloat16, "w1")
+    T, H = x.shape
+    L, twoI, _ = w1.shape
+    I = twoI // 2
+    d = _ffn_desc(T, H, I, num_experts, L, local_expert_offset, top_k, activation, "deterministic")
+    if act is None:
+        act = torch.empty((max(T * top_k, 1), I), dtype=torch.bfloat16, device=x.device)
+    _check("moe_fc1", lib().moe_fc1(ctypes.byref(d), _ptr(x), _ptr(w1), _ptr(clamp_limit), _ptr(offs),
+                                    _ptr(p2e), _ptr(act), _stream()))
+    return act
+
+
+def moe_fc2(act: torch.Tensor, w2: torch.Tensor, offs: torch.Tensor, T: int, top_k: int,
+            num_experts: int, local_expert_offset: int = 0, finalize: str = "deterministic",
+            p2e: Optional[torch.Tensor] = None, topk_weights: Optional[torch.Tensor] = None,
+            dst: Optional[torch.Tensor] = None):
+    """y[p] = act[p] @ w2[e].T (rows [T*k, H]); with finalize="fused" the scaled rows are
+    added into a zeroed out [T, H] instead."""
+    _dev(act, torch.bfloat16, "act"), _dev(w2, torch.bfloat16, "w2")
+    L, H, I = w2.shape
+    d = _ffn_desc(T, H, I, num_experts, L, local_expert_offset, top_k, "swiglu", finalize)
+    if dst is None:
+        rows = T if finalize == "fused" else max(T * top_k, 1)
+        dst = torch.empty((rows, H), dtype=torch.bfloat16, device=act.device)
+    _check("moe_fc2", lib().moe_fc2(ctypes.byref(d), _ptr(act), _ptr(w2), _ptr(offs), _ptr(p2e),
+                                    _ptr(topk_weights), _ptr(dst), _stream()))
+    return dst
+
+
+def moe_finalize(y: torch.Tensor, e2p: torch.Tensor, topk_weights: torch.Tensor, out=None):
+    """Deterministic combine: out[t] = bf16(sum_s w[t,s] * y[e2p[t*k+s]]) in fp32, s ascending."""
+    _dev(y, torch.bfloat16, "y"), _dev(e2p, torch.int32, "e2p")
+    _dev(topk_weights, torch.float32, "topk_weights")
+    T, k = topk_weights.shape
+    H = y.shape[1]
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=y.device)
+    _check("moe_finalize", lib().moe_finalize(_ptr(y), _ptr(e2p), _ptr(topk_weights), T, k, H,
+                                              _ptr(out), _stream()))
+    return out

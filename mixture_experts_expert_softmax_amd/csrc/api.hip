@@ -1,0 +1,247 @@
+// C-ABI entry points that chain the kernels: the grouped GEMMs and the MoE
+// expert-layer forward. Argument rules and layouts are documented in moe.h.
+#include <algorithm>
+
+#include "common.h"
+
+namespace moe {
+// defined in sort.hip / finalize.hip / gemm_bf16.hip
+size_t sort_workspace_bytes(int64_t T, int32_t k, int32_t L);
+moe_status sort_enqueue(const int32_t* ids, int64_t T, int32_t k, int32_t E, int32_t L,
+                        int32_t off, int32_t* offs, int32_t* m_indptr, int32_t* e2p,
+                        int32_t* p2e, int32_t* n_local, void* ws, hipStream_t st);
+moe_status finalize_enqueue(const void* y, const int32_t* e2p, const float* w, int64_t T, int k,
+                            int H, void* out, hipStream_t st);
+moe_status gemm_nt_enqueue(int epi, const void* A, const int32_t* a_gather, int a_div,
+                           const void* B, int NB, int E, const int32_t* ends, int64_t M, int N,
+                           int K, void* C, int64_t ldc, int I, const float* limits,
+                           float def_limit, const float* route_w, const int32_t* p2e, int top_k,
+                           hipStream_t st);
+moe_status gemm_dgrad_enqueue(const void* G, const void* W, const int32_t* ends, int E, int64_t M,
+                              int N, int K, void* DX, hipStream_t st);
+moe_status gemm_wgrad_enqueue(const void* G, const void* X, const int32_t* ends, int E, int64_t M,
+                              int N, int K, void* DW, bool out_f32, hipStream_t st);
+moe_status zero_fill(void* p, size_t bytes, hipStream_t st);
+
+int device_cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cached[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+namespace {
+constexpr int EPI_STORE = 0, EPI_SWIGLU = 1, EPI_SWIGLU_STEP = 2, EPI_FUSED = 3;
+constexpr int64_t U32_ELEMS = (int64_t)1 << 32;
+
+// Resolve an offsets argument to a pointer at E cumulative ends.
+inline const int32_t* ends_of(const int32_t* offs, int32_t kind) {
+  return kind == MOE_OFFS_INDPTR ? offs + 1 : offs;
+}
+
+moe_status check_gemm(const void* p0, const void* p1, const int32_t* offs, int32_t kind, int32_t E,
+                      int64_t M, int32_t N, int32_t K, const void* out) {
+  if (kind != MOE_OFFS_ENDS && kind != MOE_OFFS_INDPTR) return MOE_ERR_DTYPE;
+  if (E < 1 || M < 0 || N < 32 || K < 32 || N % 32 || K % 32) return MOE_ERR_SHAPE;
+  if (M > INT32_MAX || M * (int64_t)std::max(N, K) >= U32_ELEMS) return MOE_ERR_UNSUPPORTED;
+  if ((int64_t)N * K >= U32_ELEMS) return MOE_ERR_UNSUPPORTED;
+  if (!offs || !p1) return MOE_ERR_NULL;
+  if (M > 0 && (!p0 || !out)) return MOE_ERR_NULL;  // row operands may be empty
+  if (!aligned16(p0) || !aligned16(p1) || !aligned16(out)) return MOE_ERR_ALIGN;
+  return MOE_OK;
+}
+
+struct FfnLayout {
+  size_t sort_ws, offs, e2p, p2e, n_local, act, y, total;
+};
+
+FfnLayout ffn_layout(const moe_ffn_desc* d) {
+  FfnLayout l{};
+  const int64_t T = d->T;
+  const int32_t L = d->num_local_experts > 0 ? d->num_local_experts : d->num_experts;
+  const int64_t R = T * d->top_k;
+  size_t o = 0;
+  l.sort_ws = o; o += align_up(sort_workspace_bytes(T, d->top_k, L), 256);
+  l.offs = o;    o += align_up((size_t)L * 4, 256);
+  l.e2p = o;     o += align_up((size_t)R * 4, 256);
+  l.p2e = o;     o += align_up((size_t)R * 4, 256);
+  l.n_local = o; o += 256;
+  l.act = o;     o += align_up((size_t)R * d->I * 2, 256);
+  l.y = o;
+  if (d->finalize_mode == MOE_FINALIZE_DETERMINISTIC) o += align_up((size_t)R * d->H * 2, 256);
+  l.total = o;
+  return l;
+}
+}  // namespace
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" const char* moe_status_string(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_NULL: return "MOE_ERR_NULL: a required pointer is NULL";
+    case MOE_ERR_SHAPE: return "MOE_ERR_SHAPE: a size is out of range or breaks a divisibility rule";
+    case MOE_ERR_DTYPE: return "MOE_ERR_DTYPE: unknown or unsupported dtype / mode";
+    case MOE_ERR_ALIGN: return "MOE_ERR_ALIGN: a tensor pointer is not 16-byte aligned";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: request outside the served configurations";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace missing or too small";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP: a kernel launch failed";
+    default: return "unknown moe_status";
+  }
+}
+
+extern "C" const char* moe_version(void) { return "moe-mi355x 0.1 (gfx950)"; }
+
+extern "C" moe_status grouped_gemm_fwd(const void* x, const void* w, const int32_t* offs,
+                                       int32_t kind, int32_t E, int64_t M, int32_t N, int32_t K,
+                                       void* y, void* stream) {
+  moe_status s = check_gemm(x, w, offs, kind, E, M, N, K, y);
+  if (s != MOE_OK) return s;
+  return gemm_nt_enqueue(EPI_STORE, x, nullptr, 1, w, N, E, ends_of(offs, kind), M, N, K, y, N, 0,
+                         nullptr, 0.f, nullptr, nullptr, 1, as_stream(stream));
+}
+
+extern "C" moe_status grouped_gemm_dgrad(const void* g, const void* w, const int32_t* offs,
+                                         int32_t kind, int32_t E, int64_t M, int32_t N, int32_t K,
+                                         void* dx, void* stream) {
+  moe_status s = check_gemm(g, w, offs, kind, E, M, N, K, dx);
+  if (s != MOE_OK) return s;
+  return gemm_dgrad_enqueue(g, w, ends_of(offs, kind), E, M, N, K, dx, as_stream(stream));
+}
+
+extern "C" size_t grouped_gemm_wgrad_workspace_size(int32_t, int64_t, int32_t, int32_t, int32_t) {
+  return 0;  // the fixed-order wgrad needs no scratch memory
+}
+
+extern "C" moe_status grouped_gemm_wgrad(const void* g, const void* x, const int32_t* offs,
+                                         int32_t kind, int32_t E, int64_t M, int32_t N, int32_t K,
+                                         void* dw, int32_t out_dtype, void*, size_t, void* stream) {
+  if (out_dtype != MOE_DTYPE_BF16 && out_dtype != MOE_DTYPE_F32) return MOE_ERR_DTYPE;
+  if (M == 0) {  // only dW has to be written: zeros ([GGEMM] empty groups give zero gradients)
+    if (kind != MOE_OFFS_ENDS && kind != MOE_OFFS_INDPTR) return MOE_ERR_DTYPE;
+    if (E < 1 || N < 32 || K < 32 || N % 32 || K % 32) return MOE_ERR_SHAPE;
+    if (!dw) return MOE_ERR_NULL;
+    if (!aligned16(dw)) return MOE_ERR_ALIGN;
+    const size_t bytes = (size_t)E * N * K * (out_dtype == MOE_DTYPE_F32 ? 4 : 2);
+    return zero_fill(dw, bytes, as_stream(stream));
+  }
+  moe_status s = check_gemm(g, x, offs, kind, E, M, N, K, dw);
+  if (s != MOE_OK) return s;
+  return gemm_wgrad_enqueue(g, x, ends_of(offs, kind), E, M, N, K, dw,
+                            out_dtype == MOE_DTYPE_F32, as_stream(stream));
+}
+
+static moe_status check_ffn(const moe_ffn_desc* d) {
+  if (!d) return MOE_ERR_NULL;
+  const int32_t L = d->num_local_experts > 0 ? d->num_local_experts : d->num_experts;
+  if (d->T < 0 || d->H < 64 || d->H % 64 || d->I < 32 || d->I % 32) return MOE_ERR_SHAPE;
+  if (d->num_experts < 1 || d->num_experts > 1024 || d->num_local_experts < 0) return MOE_ERR_SHAPE;
+  if (d->local_expert_offset < 0 || d->local_expert_offset + L > d->num_experts) return MOE_ERR_SHAPE;
+  if (d->top_k < 1 || d->top_k > 16 || d->top_k > d->num_experts) return MOE_ERR_SHAPE;
+  if (d->activation != MOE_ACT_SWIGLU && d->activation != MOE_ACT_SWIGLU_STEP) return MOE_ERR_DTYPE;
+  if (d->finalize_mode < MOE_FINALIZE_DETERMINISTIC || d->finalize_mode > MOE_FINALIZE_NONE)
+    return MOE_ERR_DTYPE;
+  const int64_t R = d->T * d->top_k;
+  if (R > INT32_MAX || R * std::max(d->H, 2 * d->I) >= U32_ELEMS || d->T * d->H >= U32_ELEMS)
+    return MOE_ERR_UNSUPPORTED;
+  if ((int64_t)2 * d->I * d->H >= U32_ELEMS) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+// FC1 over gathered token rows; the activation runs in the GEMM epilogue.
+static moe_status fc1_enqueue(const moe_ffn_desc* d, const void* x, const void* w1,
+                              const float* limits, const int32_t* offs, const int32_t* p2e,
+                              void* act, hipStream_t st) {
+  const int32_t L = d->num_local_experts > 0 ? d->num_local_experts : d->num_experts;
+  const int64_t R = d->T * d->top_k;
+  const int epi = d->activation == MOE_ACT_SWIGLU_STEP ? EPI_SWIGLU_STEP : EPI_SWIGLU;
+  return gemm_nt_enqueue(epi, x, p2e, d->top_k, w1, 2 * d->I, L, offs, R, d->I, d->H, act, d->I,
+                         d->I, limits, 7.0f, nullptr, nullptr, d->top_k, st);
+}
+
+// FC2: unscaled rows in permuted order, or the fused scaled scatter-add into out.
+static moe_status fc2_enqueue(const moe_ffn_desc* d, const void* act, const void* w2,
+                              const int32_t* offs, const int32_t* p2e, const float* topk_weights,
+                              void* dst, hipStream_t st) {
+  const int32_t L = d->num_local_experts > 0 ? d->num_local_experts : d->num_experts;
+  const int64_t R = d->T * d->top_k;
+  if (d->finalize_mode == MOE_FINALIZE_FUSED) {
+    moe_status s = zero_fill(dst, (size_t)d->T * d->H * 2, st);
+    if (s != MOE_OK) return s;
+    return gemm_nt_enqueue(EPI_FUSED, act, nullptr, 1, w2, d->H, L, offs, R, d->H, d->I, dst, d->H,
+                           0, nullptr, 0.f, topk_weights, p2e, d->top_k, st);
+  }
+  return gemm_nt_enqueue(EPI_STORE, act, nullptr, 1, w2, d->H, L, offs, R, d->H, d->I, dst, d->H, 0,
+                         nullptr, 0.f, nullptr, nullptr, d->top_k, st);
+}
+
+extern "C" size_t moe_ffn_workspace_size(const moe_ffn_desc* d) {
+  if (check_ffn(d) != MOE_OK) return 0;
+  return ffn_layout(d).total;
+}
+
+extern "C" moe_status moe_ffn_forward(const moe_ffn_desc* d, const moe_ffn_tensors* t, void* ws,
+                                      size_t ws_bytes, void* stream) {
+  moe_status s = check_ffn(d);
+  if (s != MOE_OK) return s;
+  if (!t) return MOE_ERR_NULL;
+  if (d->T == 0) return MOE_OK;
+  const int32_t L = d->num_local_experts > 0 ? d->num_local_experts : d->num_experts;
+  const int fm = d->finalize_mode;
+  if (!t->x || !t->topk_ids || !t->topk_weights || !t->w1 || !t->w2) return MOE_ERR_NULL;
+  if (fm != MOE_FINALIZE_NONE && !t->out) return MOE_ERR_NULL;
+  if (fm == MOE_FINALIZE_NONE && (!t->y || !t->e2p)) return MOE_ERR_NULL;
+  if (!aligned16(t->x) || !aligned16(t->w1) || !aligned16(t->w2) ||
+      (t->out && !aligned16(t->out)) || (t->y && !aligned16(t->y)))
+    return MOE_ERR_ALIGN;
+  const FfnLayout l = ffn_layout(d);
+  if (!ws || ws_bytes < l.total || !aligned16(ws)) return MOE_ERR_WORKSPACE;
+  hipStream_t st = as_stream(stream);
+  char* w = reinterpret_cast<char*>(ws);
+  int32_t* offs = reinterpret_cast<int32_t*>(w + l.offs);
+  int32_t* e2p = t->e2p ? t->e2p : reinterpret_cast<int32_t*>(w + l.e2p);
+  int32_t* p2e = reinterpret_cast<int32_t*>(w + l.p2e);
+  int32_t* nloc = reinterpret_cast<int32_t*>(w + l.n_local);
+  void* act = w + l.act;
+  void* y = fm == MOE_FINALIZE_NONE ? t->y : w + l.y;
+  const int H = d->H;
+
+  s = sort_enqueue(t->topk_ids, d->T, d->top_k, d->num_experts, L, d->local_expert_offset, offs,
+                   nullptr, e2p, p2e, nloc, w + l.sort_ws, st);
+  if (s != MOE_OK) return s;
+  s = fc1_enqueue(d, t->x, t->w1, t->clamp_limit, offs, p2e, act, st);
+  if (s != MOE_OK) return s;
+  s = fc2_enqueue(d, act, t->w2, offs, p2e, t->topk_weights, fm == MOE_FINALIZE_FUSED ? t->out : y, st);
+  if (s != MOE_OK || fm != MOE_FINALIZE_DETERMINISTIC) return s;
+  return finalize_enqueue(y, e2p, t->topk_weights, d->T, d->top_k, H, t->out, st);
+}
+
+extern "C" moe_status moe_fc1(const moe_ffn_desc* d, const void* x, const void* w1,
+                              const float* clamp_limit, const int32_t* offs, const int32_t* p2e,
+                              void* act, void* stream) {
+  moe_status s = check_ffn(d);
+  if (s != MOE_OK) return s;
+  if (d->T == 0) return MOE_OK;
+  if (!x || !w1 || !offs || !p2e || !act) return MOE_ERR_NULL;
+  if (!aligned16(x) || !aligned16(w1) || !aligned16(act)) return MOE_ERR_ALIGN;
+  return fc1_enqueue(d, x, w1, clamp_limit, offs, p2e, act, as_stream(stream));
+}
+
+extern "C" moe_status moe_fc2(const moe_ffn_desc* d, const void* act, const void* w2,
+                              const int32_t* offs, const int32_t* p2e, const float* topk_weights,
+                              void* dst, void* stream) {
+  moe_status s = check_ffn(d);
+  if (s != MOE_OK) return s;
+  if (d->T == 0) return MOE_OK;
+  if (!act || !w2 || !offs || !dst) return MOE_ERR_NULL;
+  if (d->finalize_mode == MOE_FINALIZE_FUSED && (!p2e || !topk_weights)) return MOE_ERR_NULL;
+  if (!aligned16(act) || !aligned16(w2) || !aligned16(dst)) return MOE_ERR_ALIGN;
+  return fc2_enqueue(d, act, w2, offs, p2e, topk_weights, dst, as_stream(stream));
+}

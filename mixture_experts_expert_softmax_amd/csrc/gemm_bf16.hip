@@ -1,0 +1,604 @@
+// Ragged bf16 grouped GEMMs on gfx950 MFMA: fwd, dgrad, wgrad, and the MoE
+// FC1 (SwiGLU / SwiGLUStep epilogue) and FC2 (row store or fused finalize).
+//
+// Grouped-GEMM page, operation table:
+//   fwd    Y[rows of e]  = X[rows of e] @ W[e].T
+//   dgrad  dX[rows of e] = G[rows of e] @ W[e]      (W read in place)
+//   wgrad  dW[e]         = G[rows of e].T @ X[rows of e]   (empty group -> zeros)
+// with groups given by cumulative end offsets read on the device, fp32
+// accumulation and no atomics. SM90 fused-MoE page, formula: FC1 computes
+// x @ w1[e].T for the up and gate rows and applies silu(gate) * up in the
+// epilogue; FC2 computes act @ w2[e].T. StepFun page: SwiGLUStep clamps with a
+// per-expert limit. SM90 page, use_fused_finalize: the FC2 epilogue may add
+// the route-weighted rows straight into a zeroed output with bf16 atomics.
+//
+// Design (gfx950, wave64):
+//  * Workgroup tile 256 (weight rows) x 256 (activation rows) x 64 (contraction),
+//    256 threads = 4 waves arranged 2 x 2; each wave owns a 128 x 128 block held
+//    as 4 x 4 accumulators of v_mfma_f32_32x32x16_bf16 (256 fp32 per lane).
+//  * The MFMA "A" operand is the weight side and "B" the activation side, so a
+//    lane's accumulator holds 4 consecutive output columns of one output row:
+//    epilogue stores are 8-byte (bf16) or 16-byte (fp32) runs.
+//  * Both operand tiles are staged in LDS as [256 rows][8 chunks of 16 B] with
+//    the chunk index XOR-swizzled by (row & 7), double buffered (128 KB total);
+//    the next tile's global loads are issued before the current tile's MFMAs.
+//  * Ragged groups: an upper bound of M tiles is launched (no host sync); each
+//    workgroup decodes its (expert, row block) from the device offsets, clamps
+//    row reads inside its group and masks stores. Rows of a partial contraction
+//    tile are zero-filled.
+//  * blockIdx -> tile: consecutive workgroups land on different XCDs, so the
+//    block index is remapped to give every XCD a contiguous range of tiles, and
+//    tiles are rastered in groups of 4 row blocks so that operands are reused
+//    from the XCD's L2.
+#include "common.h"
+
+namespace moe {
+namespace {
+
+constexpr int TB = 256;        // tile rows on each side
+constexpr int TK = 64;         // contraction per stage
+constexpr int NTHREADS = 256;  // 4 waves
+constexpr int RASTER_M = 4;    // row blocks per raster group
+constexpr int TILE_U4 = TB * TK * 2 / 16;  // uint4 slots per operand tile (2048)
+
+enum Epi { EPI_STORE = 0, EPI_SWIGLU = 1, EPI_SWIGLU_STEP = 2, EPI_FUSED = 3 };
+
+struct NtArgs {
+  const uint16_t* A;         // activation rows, row stride K
+  const int32_t* a_gather;   // optional: row p reads A row a_gather[p] / a_div
+  int a_div;
+  const uint16_t* B;         // weights [E][NB][K]
+  int64_t b_stride;          // elements per expert
+  const int32_t* ends;       // [E] cumulative group ends
+  int E;
+  int m_cap;                 // rows available in A / C (clamp for offsets)
+  int NB;                    // weight rows per expert
+  int N;                     // output columns
+  int K;
+  int n_tiles;
+  int m_tiles;               // launched upper bound on row blocks
+  uint16_t* C;               // bf16 output, row stride ldc
+  int64_t ldc;
+  int I;                     // FC1: act width; gate rows start at I
+  const float* limits;       // FC1 step: [E] or NULL
+  float def_limit;
+  const float* route_w;      // fused finalize: topk weights [T*k]
+  const int32_t* p2e;        // fused finalize: route of permuted row
+  int top_k;
+};
+
+__device__ __forceinline__ int xcd_remap(int b, int nblocks) {
+  // hardware places consecutive workgroups on consecutive XCDs (8 of them)
+  const int per = nblocks >> 3;
+  return (b & 7) * per + (b >> 3);
+}
+
+// Row block mt of the concatenated groups -> (expert, first row, group end).
+__device__ __forceinline__ bool decode_row_block(const int32_t* __restrict__ ends, int E,
+                                                 int m_cap, int mt, int& e, int& m0, int& mend) {
+  int acc = 0, start = 0;
+  for (int g = 0; g < E; ++g) {
+    int end = ends[g];
+    end = end < start ? start : (end > m_cap ? m_cap : end);
+    const int te = (end - start + TB - 1) / TB;
+    if (mt < acc + te) {
+      e = g;
+      m0 = start + (mt - acc) * TB;
+      mend = end;
+      return true;
+    }
+    acc += te;
+    start = end;
+  }
+  return false;
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// One 64-deep stage of MFMAs: wave (wn, wm) multiplies its 128 weight rows by its
+// 128 activation rows.
+__device__ __forceinline__ void mma_stage(const uint4* __restrict__ Ws, const uint4* __restrict__ Xs,
+                                          int wn, int wm, int lane, f32x16 (&acc)[4][4]) {
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    const int ch = ((kk << 1) + (lane >> 5)) ^ (lane & 7);
+    bf16x8 wf[4], xf[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wf[i] = as_bf16x8(Ws[(wn * 128 + i * 32 + (lane & 31)) * 8 + ch]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) xf[j] = as_bf16x8(Xs[(wm * 128 + j * 32 + (lane & 31)) * 8 + ch]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[i], xf[j], acc[i][j], 0, 0, 0);
+  }
+}
+
+// Tile rows that are contiguous along the contraction: thread tid owns rows
+// (tid>>3) + 32j, 16-byte chunk (tid&7) of every 64-wide stage.
+struct RowLoader {
+  const uint16_t* base;
+  uint32_t off[8];
+  int K;
+  int ch;
+  uint4 r[8];
+  __device__ __forceinline__ void load(int kt) {
+    const int k0 = kt * TK + ch * 8;
+    const bool ok = k0 < K;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      r[j] = ok ? *reinterpret_cast<const uint4*>(base + off[j] + k0) : make_uint4(0, 0, 0, 0);
+  }
+  __device__ __forceinline__ void store(uint4* __restrict__ lds, int tid) const {
+    const int row = tid >> 3;
+    const int pc = ch ^ (row & 7);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) lds[(row + 32 * j) * 8 + pc] = r[j];
+  }
+};
+
+// Tile rows that are contiguous along the OUTPUT dimension (the operand is used
+// transposed): source rows are contraction indices. Thread tid reads contraction
+// row (tid & 63) and 8 output columns per chunk (tid >> 6) + 4j, and scatters
+// the 8 values into the [output row][contraction] LDS layout.
+struct ColLoader {
+  const uint16_t* base;   // points at source row r_begin, column c0
+  int64_t ld;             // source row stride (elements)
+  int rows_left0;         // valid contraction rows from r_begin
+  int cols_left;          // valid output columns from c0
+  uint4 r[8];
+  __device__ __forceinline__ void load(int kt, int tid) {
+    const int kr = kt * TK + (tid & 63);
+    const bool rok = kr < rows_left0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int cc = (tid >> 6) + 4 * j;
+      const bool ok = rok && (cc * 8 < cols_left);
+      r[j] = ok ? *reinterpret_cast<const uint4*>(base + (int64_t)kr * ld + cc * 8)
+                : make_uint4(0, 0, 0, 0);
+    }
+  }
+  __device__ __forceinline__ void store(uint4* __restrict__ lds, int tid) const {
+    uint16_t* l16 = reinterpret_cast<uint16_t*>(lds);
+    const int kr = tid & 63;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int cc = (tid >> 6) + 4 * j;
+      const uint32_t w[4] = {r[j].x, r[j].y, r[j].z, r[j].w};
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int n = cc * 8 + q;
+        const int pc = (kr >> 3) ^ (n & 7);
+        l16[n * 64 + pc * 8 + (kr & 7)] = (uint16_t)((q & 1) ? (w[q >> 1] >> 16) : (w[q >> 1] & 0xFFFFu));
+      }
+    }
+  }
+};
+
+__device__ __forceinline__ void zero_acc(f32x16 (&acc)[4][4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+}
+
+__device__ __forceinline__ void atomic_add_bf16x2(uint16_t* p, float a, float b) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const uint32_t bits = pack_bf16x2(a, b);
+  __builtin_amdgcn_global_atomic_fadd_v2bf16(reinterpret_cast<bf16x2_t*>(p),
+                                             __builtin_bit_cast(bf16x2_t, bits));
+}
+
+// ---------------------------------------------------------------------------
+// fwd / FC1 / FC2: both operands contiguous along the contraction.
+// ---------------------------------------------------------------------------
+template <int EPI>
+__global__ __launch_bounds__(NTHREADS, 1) void k_gemm_nt(NtArgs a) {
+  __shared__ uint4 smem[4 * TILE_U4];  // [stage][A tile | B tile], 128 KB
+  const int t = xcd_remap(blockIdx.x, gridDim.x);
+  const int span = RASTER_M * a.n_tiles;
+  const int grp = t / span;
+  const int first_mt = grp * RASTER_M;
+  const int gm = min(RASTER_M, a.m_tiles - first_mt);
+  if (gm <= 0) return;
+  const int within = t - grp * span;
+  const int mt = first_mt + within % gm;
+  const int nt = within / gm;
+  if (nt >= a.n_tiles) return;
+  int e, m0, mend;
+  if (!decode_row_block(a.ends, a.E, a.m_cap, mt, e, m0, mend)) return;
+
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int wn = wid & 1, wm = wid >> 1;
+  const int lrow = tid >> 3;
+
+  RowLoader la, lb;
+  la.base = a.A;
+  la.K = a.K;
+  la.ch = tid & 7;
+  lb.base = a.B + (int64_t)e * a.b_stride;
+  lb.K = a.K;
+  lb.ch = tid & 7;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    int p = m0 + lrow + 32 * j;
+    p = p < mend ? p : mend - 1;
+    const int src = a.a_gather ? a.a_gather[p] / a.a_div : p;
+    la.off[j] = (uint32_t)src * (uint32_t)a.K;
+    const int R = lrow + 32 * j;
+    int wrow;
+    if (EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_STEP) {
+      int c = nt * 128 + (R >> 7) * 64 + (R & 63);
+      c = c < a.I ? c : a.I - 1;
+      wrow = ((R >> 6) & 1) * a.I + c;
+    } else {
+      wrow = nt * TB + R;
+      wrow = wrow < a.NB ? wrow : a.NB - 1;
+    }
+    lb.off[j] = (uint32_t)wrow * (uint32_t)a.K;
+  }
+
+  f32x16 acc[4][4];
+  zero_acc(acc);
+  const int ktiles = (a.K + TK - 1) / TK;
+
+  la.load(0);
+  lb.load(0);
+  la.store(smem, tid);
+  lb.store((smem + TILE_U4), tid);
+  __syncthreads();
+  for (int kt = 0; kt < ktiles; ++kt) {
+    const int s = kt & 1;
+    const bool more = kt + 1 < ktiles;
+    if (more) {
+      la.load(kt + 1);
+      lb.load(kt + 1);
+    }
+    mma_stage((smem + TILE_U4 + s * 2 * TILE_U4), (smem + s * 2 * TILE_U4), wn, wm, lane, acc);
+    if (more) {
+      la.store((smem + (s ^ 1) * 2 * TILE_U4), tid);
+      lb.store((smem + TILE_U4 + (s ^ 1) * 2 * TILE_U4), tid);
+    }
+    __syncthreads();
+  }
+
+  // ---- epilogue: lane holds rows m, 4 consecutive columns per (i, q)
+  const int hi4 = (lane >> 5) * 4;
+  if (EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_STEP) {
+    float lim = 0.f;
+    if (EPI == EPI_SWIGLU_STEP) lim = a.limits ? a.limits[e] : a.def_limit;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int p = m0 + wm * 128 + j * 32 + (lane & 31);
+      if (p >= mend) continue;
+      uint16_t* crow = a.C + (int64_t)p * a.ldc;
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int col = nt * 128 + wn * 64 + i * 32 + q * 8 + hi4;
+          if (col >= a.I) continue;
+          float v[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            float u = acc[i][j][q * 4 + r];
+            float g = acc[i + 2][j][q * 4 + r];
+            if (EPI == EPI_SWIGLU_STEP) {
+              u = fminf(fmaxf(u, -lim), lim);
+              g = fminf(fmaxf(g, -lim), lim);
+            }
+            v[r] = silu_f32(g) * u;
+          }
+          *reinterpret_cast<uint2*>(crow + col) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+        }
+    }
+  } else if (EPI == EPI_FUSED) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int p = m0 + wm * 128 + j * 32 + (lane & 31);
+      if (p >= mend) continue;
+      const int route = a.p2e[p];
+      const float wgt = a.route_w[route];
+      uint16_t* crow = a.C + (int64_t)(route / a.top_k) * a.ldc;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int col = nt * TB + wn * 128 + i * 32 + q * 8 + hi4;
+          if (col >= a.N) continue;
+          atomic_add_bf16x2(crow + col, wgt * acc[i][j][q * 4 + 0], wgt * acc[i][j][q * 4 + 1]);
+          atomic_add_bf16x2(crow + col + 2, wgt * acc[i][j][q * 4 + 2], wgt * acc[i][j][q * 4 + 3]);
+        }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int p = m0 + wm * 128 + j * 32 + (lane & 31);
+      if (p >= mend) continue;
+      uint16_t* crow = a.C + (int64_t)p * a.ldc;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int col = nt * TB + wn * 128 + i * 32 + q * 8 + hi4;
+          if (col >= a.N) continue;
+          *reinterpret_cast<uint2*>(crow + col) =
+              make_uint2(pack_bf16x2(acc[i][j][q * 4 + 0], acc[i][j][q * 4 + 1]),
+                         pack_bf16x2(acc[i][j][q * 4 + 2], acc[i][j][q * 4 + 3]));
+        }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dgrad: dX[m, k] = sum_n G[m, n] W[e, n, k]. Weight side = k (read transposed
+// from W rows n), activation side = G rows m, contraction n.
+// ---------------------------------------------------------------------------
+struct DgradArgs {
+  const uint16_t* G; const uint16_t* W; const int32_t* ends; int E; int m_cap;
+  int N; int K; int n_tiles; int m_tiles; uint16_t* DX;
+};
+
+__global__ __launch_bounds__(NTHREADS, 1) void k_gemm_dgrad(DgradArgs a) {
+  __shared__ uint4 smem[4 * TILE_U4];
+  const int t = xcd_remap(blockIdx.x, gridDim.x);
+  const int span = RASTER_M * a.n_tiles;
+  const int grp = t / span;
+  const int first_mt = grp * RASTER_M;
+  const int gm = min(RASTER_M, a.m_tiles - first_mt);
+  if (gm <= 0) return;
+  const int within = t - grp * span;
+  const int mt = first_mt + within % gm;
+  const int nt = within / gm;  // tile of K (output columns)
+  if (nt >= a.n_tiles) return;
+  int e, m0, mend;
+  if (!decode_row_block(a.ends, a.E, a.m_cap, mt, e, m0, mend)) return;
+
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int wn = wid & 1, wm = wid >> 1;
+  const int lrow = tid >> 3;
+  const int c0 = nt * TB;
+
+  RowLoader lg;  // activation side: G rows, contraction along N
+  lg.base = a.G;
+  lg.K = a.N;
+  lg.ch = tid & 7;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    int p = m0 + lrow + 32 * j;
+    p = p < mend ? p : mend - 1;
+    lg.off[j] = (uint32_t)p * (uint32_t)a.N;
+  }
+  ColLoader lw;  // weight side: W[e] rows n (contraction), columns k
+  lw.base = a.W + (int64_t)e * a.N * a.K + c0;
+  lw.ld = a.K;
+  lw.rows_left0 = a.N;
+  lw.cols_left = a.K - c0;
+
+  f32x16 acc[4][4];
+  zero_acc(acc);
+  const int ktiles = (a.N + TK - 1) / TK;
+  lg.load(0);
+  lw.load(0, tid);
+  lg.store(smem, tid);
+  lw.store((smem + TILE_U4), tid);
+  __syncthreads();
+  for (int kt = 0; kt < ktiles; ++kt) {
+    const int s = kt & 1;
+    const bool more = kt + 1 < ktiles;
+    if (more) {
+      lg.load(kt + 1);
+      lw.load(kt + 1, tid);
+    }
+    mma_stage((smem + TILE_U4 + s * 2 * TILE_U4), (smem + s * 2 * TILE_U4), wn, wm, lane, acc);
+    if (more) {
+      lg.store((smem + (s ^ 1) * 2 * TILE_U4), tid);
+      lw.store((smem + TILE_U4 + (s ^ 1) * 2 * TILE_U4), tid);
+    }
+    __syncthreads();
+  }
+  const int hi4 = (lane >> 5) * 4;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int p = m0 + wm * 128 + j * 32 + (lane & 31);
+    if (p >= mend) continue;
+    uint16_t* crow = a.DX + (int64_t)p * a.K;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int col = c0 + wn * 128 + i * 32 + q * 8 + hi4;
+        if (col >= a.K) continue;
+        *reinterpret_cast<uint2*>(crow + col) =
+            make_uint2(pack_bf16x2(acc[i][j][q * 4 + 0], acc[i][j][q * 4 + 1]),
+                       pack_bf16x2(acc[i][j][q * 4 + 2], acc[i][j][q * 4 + 3]));
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// wgrad: dW[e, n, k] = sum over rows m of group e of G[m, n] X[m, k].
+// Weight side = k (X read transposed), activation side = n (G read transposed),
+// contraction over the group's rows, zero-filled past the group end.
+// ---------------------------------------------------------------------------
+struct WgradArgs {
+  const uint16_t* G; const uint16_t* X; const int32_t* ends; int E; int m_cap;
+  int N; int K; int n_tiles; int k_tiles; void* DW;
+};
+
+template <bool OUT_F32>
+__global__ __launch_bounds__(NTHREADS, 1) void k_gemm_wgrad(WgradArgs a) {
+  __shared__ uint4 smem[4 * TILE_U4];
+  const int t = xcd_remap(blockIdx.x, gridDim.x);
+  const int per_e = a.n_tiles * a.k_tiles;
+  const int e = t / per_e;
+  if (e >= a.E) return;
+  const int rem = t - e * per_e;
+  const int ntile = rem / a.k_tiles;   // rows n of dW
+  const int ktile = rem - ntile * a.k_tiles;
+  int start = 0;
+  for (int g = 0; g < e; ++g) {
+    int v = a.ends[g];
+    v = v < start ? start : (v > a.m_cap ? a.m_cap : v);
+    start = v;
+  }
+  int end = a.ends[e];
+  end = end < start ? start : (end > a.m_cap ? a.m_cap : end);
+  const int rows = end - start;
+  const int n0 = ntile * TB, c0 = ktile * TB;
+
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int wn = wid & 1, wm = wid >> 1;
+
+  ColLoader lx;  // weight side: output columns k from X rows
+  lx.base = a.X + (int64_t)start * a.K + c0;
+  lx.ld = a.K;
+  lx.rows_left0 = rows;
+  lx.cols_left = a.K - c0;
+  ColLoader lgd;  // activation side: output rows n from G rows
+  lgd.base = a.G + (int64_t)start * a.N + n0;
+  lgd.ld = a.N;
+  lgd.rows_left0 = rows;
+  lgd.cols_left = a.N - n0;
+
+  f32x16 acc[4][4];
+  zero_acc(acc);
+  const int ktiles = (rows + TK - 1) / TK;
+  if (ktiles > 0) {
+    lgd.load(0, tid);
+    lx.load(0, tid);
+    lgd.store(smem, tid);
+    lx.store((smem + TILE_U4), tid);
+    __syncthreads();
+  }
+  for (int kt = 0; kt < ktiles; ++kt) {
+    const int s = kt & 1;
+    const bool more = kt + 1 < ktiles;
+    if (more) {
+      lgd.load(kt + 1, tid);
+      lx.load(kt + 1, tid);
+    }
+    mma_stage((smem + TILE_U4 + s * 2 * TILE_U4), (smem + s * 2 * TILE_U4), wn, wm, lane, acc);
+    if (more) {
+      lgd.store((smem + (s ^ 1) * 2 * TILE_U4), tid);
+      lx.store((smem + TILE_U4 + (s ^ 1) * 2 * TILE_U4), tid);
+    }
+    __syncthreads();
+  }
+  const int hi4 = (lane >> 5) * 4;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int n = n0 + wm * 128 + j * 32 + (lane & 31);
+    if (n >= a.N) continue;
+    const int64_t rowoff = ((int64_t)e * a.N + n) * a.K;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int col = c0 + wn * 128 + i * 32 + q * 8 + hi4;
+        if (col >= a.K) continue;
+        if (OUT_F32) {
+          float* d = reinterpret_cast<float*>(a.DW) + rowoff + col;
+          *reinterpret_cast<float4*>(d) =
+              make_float4(acc[i][j][q * 4 + 0], acc[i][j][q * 4 + 1], acc[i][j][q * 4 + 2], acc[i][j][q * 4 + 3]);
+        } else {
+          uint16_t* d = reinterpret_cast<uint16_t*>(a.DW) + rowoff + col;
+          *reinterpret_cast<uint2*>(d) =
+              make_uint2(pack_bf16x2(acc[i][j][q * 4 + 0], acc[i][j][q * 4 + 1]),
+                         pack_bf16x2(acc[i][j][q * 4 + 2], acc[i][j][q * 4 + 3]));
+        }
+      }
+  }
+}
+
+// Zero fill of n 16-byte words (graph-safe replacement for a memset node).
+__global__ __launch_bounds__(256) void k_zero16(uint4* __restrict__ p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = make_uint4(0, 0, 0, 0);
+}
+
+inline int round_up8(int64_t v) { return (int)((v + 7) / 8 * 8); }
+
+}  // namespace
+
+// Upper bound on the row blocks of ragged groups: sum_e ceil(m_e/256) <= floor(M/256) + E.
+int row_block_bound(int64_t M, int E) { return (int)(M / TB) + E; }
+
+moe_status zero_fill(void* p, size_t bytes, hipStream_t st) {
+  if (bytes == 0) return MOE_OK;
+  const int64_t n = (int64_t)(bytes / 16);
+  const int blocks = (int)std::min<int64_t>((n + 255) / 256, 8192);
+  k_zero16<<<blocks, 256, 0, st>>>(reinterpret_cast<uint4*>(p), n);
+  return launch_status();
+}
+
+// C[rows, N] (bf16) = rows of A [*, K] times W[e]^T for ragged groups, with an epilogue.
+moe_status gemm_nt_enqueue(int epi, const void* A, const int32_t* a_gather, int a_div,
+                           const void* B, int NB, int E, const int32_t* ends, int64_t M, int N,
+                           int K, void* C, int64_t ldc, int I, const float* limits,
+                           float def_limit, const float* route_w, const int32_t* p2e, int top_k,
+                           hipStream_t st) {
+  if (M == 0) return MOE_OK;
+  NtArgs a;
+  a.A = reinterpret_cast<const uint16_t*>(A);
+  a.a_gather = a_gather;
+  a.a_div = a_div > 0 ? a_div : 1;
+  a.B = reinterpret_cast<const uint16_t*>(B);
+  a.b_stride = (int64_t)NB * K;
+  a.ends = ends;
+  a.E = E;
+  a.m_cap = (int)M;
+  a.NB = NB;
+  a.N = N;
+  a.K = K;
+  const bool fc1 = (epi == EPI_SWIGLU || epi == EPI_SWIGLU_STEP);
+  a.n_tiles = fc1 ? (I + 127) / 128 : (N + TB - 1) / TB;
+  a.m_tiles = row_block_bound(M, E);
+  a.C = reinterpret_cast<uint16_t*>(C);
+  a.ldc = ldc;
+  a.I = I;
+  a.limits = limits;
+  a.def_limit = def_limit;
+  a.route_w = route_w;
+  a.p2e = p2e;
+  a.top_k = top_k;
+  const int64_t tiles = (int64_t)a.m_tiles * a.n_tiles;
+  const int grid = round_up8(tiles);
+  switch (epi) {
+    case EPI_STORE: k_gemm_nt<EPI_STORE><<<grid, NTHREADS, 0, st>>>(a); break;
+    case EPI_SWIGLU: k_gemm_nt<EPI_SWIGLU><<<grid, NTHREADS, 0, st>>>(a); break;
+    case EPI_SWIGLU_STEP: k_gemm_nt<EPI_SWIGLU_STEP><<<grid, NTHREADS, 0, st>>>(a); break;
+    case EPI_FUSED: k_gemm_nt<EPI_FUSED><<<grid, NTHREADS, 0, st>>>(a); break;
+    default: return MOE_ERR_DTYPE;
+  }
+  return launch_status();
+}
+
+moe_status gemm_dgrad_enqueue(const void* G, const void* W, const int32_t* ends, int E, int64_t M,
+                              int N, int K, void* DX, hipStream_t st) {
+  if (M == 0) return MOE_OK;
+  DgradArgs a{reinterpret_cast<const uint16_t*>(G), reinterpret_cast<const uint16_t*>(W), ends, E,
+              (int)M, N, K, (K + TB - 1) / TB, row_block_bound(M, E),
+              reinterpret_cast<uint16_t*>(DX)};
+  const int grid = round_up8((int64_t)a.m_tiles * a.n_tiles);
+  k_gemm_dgrad<<<grid, NTHREADS, 0, st>>>(a);
+  return launch_status();
+}
+
+moe_status gemm_wgrad_enqueue(const void* G, const void* X, const int32_t* ends, int E, int64_t M,
+                              int N, int K, void* DW, bool out_f32, hipStream_t st) {
+  WgradArgs a{reinterpret_cast<const uint16_t*>(G), reinterpret_cast<const uint16_t*>(X), ends, E,
+              (int)M, N, K, (N + TB - 1) / TB, (K + TB - 1) / TB, DW};
+  const int grid = round_up8((int64_t)E * a.n_tiles * a.k_tiles);
+  if (out_f32)
+    k_gemm_wgrad<true><<<grid, NTHREADS, 0, st>>>(a);
+  else
+    k_gemm_wgrad<false><<<grid, NTHREADS, 0, st>>>(a);
+  return launch_status();
+}
+
+}  // namespace moe

@@ -1,0 +1,204 @@
+// Stable, unpadded counting sort of routes by local expert ("moe_sort").
+//
+// Grouped-GEMM page, intro: groups are consecutive row ranges described by
+// cumulative end offsets (or m_indptr with a leading zero); no padding.
+// StepFun page, "Prepared launches": expanded_idx_to_permuted_idx maps the
+// expanded index i = t*top_k + s to its row in the expert-sorted order.
+// SM90 fused-MoE page, Parameters: the EP shard holds num_local_experts experts
+// from global id local_expert_offset; other routes contribute nothing.
+//
+// Three launches over chunks of CHUNK routes (one wave64 per chunk):
+//  1. k_sort_count:   per-chunk histogram of local experts -> cnt[e][chunk]
+//  2. k_sort_scan:    one block per expert: exclusive scan of cnt[e][*] over
+//                     chunks (in place) and the expert total
+//  3. k_sort_scatter: scan of the totals -> expert start rows; every chunk walks
+//                     its routes in order, 64 at a time, ranking equal keys with
+//                     ballots (stable), and writes e2p / p2e.
+// The result is a pure function of the ids: no atomics decide any position.
+#include "common.h"
+
+namespace moe {
+namespace {
+
+constexpr int SORT_STEPS = 16;
+constexpr int CHUNK = 64 * SORT_STEPS;  // routes per wave64 chunk
+
+__device__ __forceinline__ int local_key(int32_t id, int E, int L, int off) {
+  int loc = id - off;
+  bool ok = (id >= 0) && (id < E) && (loc >= 0) && (loc < L);
+  return ok ? loc : L;  // L = foreign
+}
+
+__global__ __launch_bounds__(64) void k_sort_count(const int32_t* __restrict__ ids, int64_t n,
+                                                   int E, int L, int off, int nb,
+                                                   int32_t* __restrict__ cnt) {
+  extern __shared__ int32_t hist[];
+  const int lane = threadIdx.x;
+  for (int e = lane; e < L; e += 64) hist[e] = 0;
+  __syncthreads();
+  const int64_t base = (int64_t)blockIdx.x * CHUNK;
+  for (int step = 0; step < SORT_STEPS; ++step) {
+    int64_t i = base + step * 64 + lane;
+    if (i < n) {
+      int key = local_key(ids[i], E, L, off);
+      if (key < L) atomicAdd(&hist[key], 1);
+    }
+  }
+  __syncthreads();
+  for (int e = lane; e < L; e += 64) cnt[(int64_t)e * nb + blockIdx.x] = hist[e];
+}
+
+// Inclusive wave64 scan of an int.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    int o = __shfl_up(v, d);
+    if (lane >= d) v += o;
+  }
+  return v;
+}
+
+__global__ __launch_bounds__(256) void k_sort_scan(int32_t* __restrict__ cnt, int nb,
+                                                   int32_t* __restrict__ total) {
+  __shared__ int wsum[4];
+  const int e = blockIdx.x;
+  int32_t* col = cnt + (int64_t)e * nb;
+  const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
+  int carry = 0;
+  for (int c0 = 0; c0 < nb; c0 += 256) {
+    int b = c0 + tid;
+    int v = (b < nb) ? col[b] : 0;
+    int inc = wave_incl_scan(v);
+    if (lane == 63) wsum[wid] = inc;
+    __syncthreads();
+    int before = carry;
+    for (int w = 0; w < wid; ++w) before += wsum[w];
+    int chunk_total = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+    if (b < nb) col[b] = before + inc - v;  // exclusive
+    carry += chunk_total;
+    __syncthreads();
+  }
+  if (tid == 0) total[e] = carry;
+}
+
+__global__ __launch_bounds__(64) void k_sort_scatter(
+    const int32_t* __restrict__ ids, int64_t n, int E, int L, int off, int nb,
+    const int32_t* __restrict__ cnt, const int32_t* __restrict__ total,
+    int32_t* __restrict__ offs, int32_t* __restrict__ m_indptr, int32_t* __restrict__ n_local,
+    int32_t* __restrict__ e2p, int32_t* __restrict__ p2e) {
+  extern __shared__ int32_t run[];  // [L] next free row of each expert in this chunk
+  const int lane = threadIdx.x;
+  // exclusive scan of the expert totals: lane owns experts [lane*per, lane*per+per)
+  const int per = (L + 63) / 64;
+  int part = 0;
+  for (int j = 0; j < per; ++j) {
+    int e = lane * per + j;
+    if (e < L) part += total[e];
+  }
+  int excl = wave_incl_scan(part) - part;
+  for (int j = 0; j < per; ++j) {
+    int e = lane * per + j;
+    if (e < L) {
+      int te = total[e];
+      run[e] = excl + cnt[(int64_t)e * nb + blockIdx.x];
+      if (blockIdx.x == 0) {
+        offs[e] = excl + te;
+        if (m_indptr) m_indptr[e + 1] = excl + te;
+      }
+      excl += te;
+    }
+  }
+  if (blockIdx.x == 0 && lane == 63) {
+    *n_local = excl;  // lane 63 ends with the grand total
+    if (m_indptr) m_indptr[0] = 0;
+  }
+  __syncthreads();
+
+  int bits = 1;
+  while ((1 << bits) <= L) ++bits;  // keys 0..L fit
+  const uint64_t lt = (1ull << lane) - 1ull;
+  const int64_t base = (int64_t)blockIdx.x * CHUNK;
+  for (int step = 0; step < SORT_STEPS; ++step) {
+    int64_t i = base + step * 64 + lane;
+    bool valid = i < n;
+    int key = valid ? local_key(ids[i], E, L, off) : L;
+    uint64_t peers = __ballot(valid);
+    for (int b = 0; b < bits; ++b) {
+      uint64_t m = __ballot((key >> b) & 1);
+      peers &= ((key >> b) & 1) ? m : ~m;
+    }
+    int rank = __popcll(peers & lt);
+    int pos = -1;
+    if (valid && key < L) pos = run[key] + rank;
+    __syncthreads();
+    if (valid && key < L && rank == 0) run[key] += __popcll(peers);
+    __syncthreads();
+    if (valid) {
+      e2p[i] = pos;
+      if (pos >= 0) p2e[pos] = (int32_t)i;
+    }
+  }
+}
+
+__global__ void k_sort_empty(int L, int32_t* offs, int32_t* m_indptr, int32_t* n_local) {
+  for (int e = threadIdx.x; e < L; e += blockDim.x) {
+    offs[e] = 0;
+    if (m_indptr) m_indptr[e + 1] = 0;
+  }
+  if (threadIdx.x == 0) {
+    *n_local = 0;
+    if (m_indptr) m_indptr[0] = 0;
+  }
+}
+
+inline int64_t n_chunks(int64_t n) { return (n + CHUNK - 1) / CHUNK; }
+
+}  // namespace
+
+size_t sort_workspace_bytes(int64_t T, int32_t k, int32_t L) {
+  int64_t nb = n_chunks(T * (int64_t)k);
+  return align_up((size_t)(L * nb + L) * sizeof(int32_t), 256);
+}
+
+moe_status sort_enqueue(const int32_t* ids, int64_t T, int32_t k, int32_t E, int32_t L,
+                        int32_t off, int32_t* offs, int32_t* m_indptr, int32_t* e2p,
+                        int32_t* p2e, int32_t* n_local, void* ws, hipStream_t st) {
+  const int64_t n = T * (int64_t)k;
+  if (n == 0) {
+    k_sort_empty<<<1, 256, 0, st>>>(L, offs, m_indptr, n_local);
+    return launch_status();
+  }
+  const int64_t nb = n_chunks(n);
+  int32_t* cnt = reinterpret_cast<int32_t*>(ws);
+  int32_t* total = cnt + L * nb;
+  const size_t lds = (size_t)L * sizeof(int32_t);
+  k_sort_count<<<(unsigned)nb, 64, lds, st>>>(ids, n, E, L, off, (int)nb, cnt);
+  k_sort_scan<<<(unsigned)L, 256, 0, st>>>(cnt, (int)nb, total);
+  k_sort_scatter<<<(unsigned)nb, 64, lds, st>>>(ids, n, E, L, off, (int)nb, cnt, total, offs,
+                                                m_indptr, n_local, e2p, p2e);
+  return launch_status();
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" size_t moe_sort_workspace_size(int64_t T, int32_t top_k, int32_t L) {
+  if (T < 0 || top_k < 1 || L < 1) return 0;
+  return sort_workspace_bytes(T, top_k, L);
+}
+
+extern "C" moe_status moe_sort(const int32_t* topk_ids, int64_t T, int32_t top_k, int32_t E,
+                               int32_t L, int32_t off, int32_t* offs, int32_t* m_indptr,
+                               int32_t* e2p, int32_t* p2e, int32_t* n_local, void* ws,
+                               size_t ws_bytes, void* stream) {
+  if (T < 0 || top_k < 1 || top_k > 16 || E < 1 || E > 1024 || L < 1 || off < 0 || L + off > E)
+    return MOE_ERR_SHAPE;
+  if (!offs || !n_local) return MOE_ERR_NULL;
+  if (T > 0 && (!topk_ids || !e2p || !p2e)) return MOE_ERR_NULL;
+  if (T * (int64_t)top_k > (int64_t)INT32_MAX) return MOE_ERR_SHAPE;
+  if (T > 0 && (!ws || ws_bytes < sort_workspace_bytes(T, top_k, L))) return MOE_ERR_WORKSPACE;
+  return sort_enqueue(topk_ids, T, top_k, E, L, off, offs, m_indptr, e2p, p2e, n_local, ws,
+                      as_stream(stream));
+}

@@ -1,0 +1,139 @@
+"""GPU parity: the MoE expert layer (sort -> FC1+activation -> FC2 -> finalize)
+and the standalone finalize, against the oracle's per-token definition."""
+import numpy as np
+import pytest
+import torch
+
+import mixture_experts_expert_softmax_amd as M
+import moe_synth as S
+import oracle as O
+from parity import assert_close_bf16, to_np
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _run(c, finalize="deterministic", ids=None, w=None):
+    if ids is None:
+        ids, w = M.moe_route(torch.from_numpy(c.logits).to(DEV), c.top_k)
+    lim = None if c.limits is None else torch.from_numpy(c.limits).to(DEV)
+    res = M.moe_ffn_forward(c.x.to(DEV), ids, w, c.w1.to(DEV), c.w2.to(DEV), c.num_experts,
+                            c.num_local, c.local_offset, c.activation, lim, finalize=finalize)
+    return res, ids, w
+
+
+def _oracle(c, ids, w, tokens=None):
+    ids_n, w_n = ids.cpu().numpy(), w.cpu().numpy().astype(np.float64)
+    x = S.bf16_to_f32(c.x)
+    if tokens is not None:
+        x, ids_n, w_n = x[tokens], ids_n[tokens], w_n[tokens]
+    return O.moe_forward(x, ids_n, w_n, S.bf16_to_f32(c.w1), S.bf16_to_f32(c.w2),
+                         num_experts=c.num_experts, local_offset=c.local_offset,
+                         activation_kind=c.activation, limits=c.limits)
+
+
+@pytest.mark.parametrize("finalize", ["deterministic", "fused"])
+def test_tiny_forward(finalize):
+    c = S.tiny_moe()
+    out, ids, w = _run(c, finalize)
+    assert_close_bf16(out, _oracle(c, ids, w), what=f"tiny {finalize}")
+
+
+def test_tiny_forward_no_finalize_returns_rows_and_e2p():
+    c = S.tiny_moe()
+    (y, e2p), ids, w = _run(c, "none")
+    ref_sort = O.sort_routes(ids.cpu().numpy(), 8, 8, 0)
+    np.testing.assert_array_equal(e2p.cpu().numpy(), ref_sort["e2p"])
+    yr, _ = O.moe_route_outputs(S.bf16_to_f32(c.x), ids.cpu().numpy(), S.bf16_to_f32(c.w1),
+                                S.bf16_to_f32(c.w2), num_experts=8)
+    # y rows are in permuted order: row e2p[t*k+s] holds route (t, s)
+    T, k = ids.shape
+    got = to_np(y)[ref_sort["e2p"]].reshape(T, k, -1)
+    assert_close_bf16(got, yr, what="y rows")
+
+
+@pytest.mark.parametrize("clamp_active", [False, True])
+def test_expert_shard_small_step(clamp_active):
+    """256 experts, 32 local from id 64, top-8, SwiGLUStep, at a reduced H/I/T."""
+    c = S.moe_case("shard_small", 512, 256, 128, 256, 8, num_local=32, local_offset=64,
+                   activation="swiglu_step", limit_range=(5.0, 9.0),
+                   x_scale=8.0 if clamp_active else 1.0, seed=3)
+    out, ids, w = _run(c)
+    ref = _oracle(c, ids, w)
+    assert_close_bf16(out, ref, what="shard")
+    # tokens with no local route are exact zero rows
+    loc = O.local_expert(ids.cpu().numpy(), 256, 32, 64).reshape(ids.shape)
+    none_local = np.all(loc < 0, axis=1)
+    assert none_local.any()
+    assert torch.all(out[torch.from_numpy(none_local).to(DEV)] == 0)
+
+
+@pytest.mark.parametrize("T", [1, 7, 300])
+def test_odd_token_counts_and_shapes(T):
+    c = S.moe_case("odd", T, 192, 96, 6, 3, seed=T)   # I = 96: partial FC1 / FC2 tiles
+    out, ids, w = _run(c)
+    assert_close_bf16(out, _oracle(c, ids, w), what=f"T={T}")
+    out2, _, _ = _run(c, "fused", ids, w)
+    assert_close_bf16(out2, _oracle(c, ids, w), what=f"T={T} fused")
+
+
+def test_zero_tokens():
+    c = S.moe_case("empty", 0, 128, 64, 4, 2, seed=0)
+    ids = torch.empty((0, 2), dtype=torch.int32, device=DEV)
+    w = torch.empty((0, 2), dtype=torch.float32, device=DEV)
+    out, _, _ = _run(c, ids=ids, w=w)
+    assert out.shape == (0, 128)
+
+
+def test_all_routes_foreign_give_zeros():
+    c = S.moe_case("foreign", 64, 128, 64, 16, 2, num_local=4, local_offset=0, seed=1)
+    ids = torch.full((64, 2), 9, dtype=torch.int32, device=DEV)
+    w = torch.full((64, 2), 0.5, dtype=torch.float32, device=DEV)
+    for fin in ["deterministic", "fused"]:
+        out, _, _ = _run(c, fin, ids, w)
+        assert torch.all(out == 0)
+
+
+def test_deterministic_replay_is_bitwise():
+    c = S.moe_case("replay", 1000, 256, 256, 8, 2, seed=4)
+    o1, ids, w = _run(c)
+    o2, _, _ = _run(c, ids=ids, w=w)
+    assert torch.equal(o1, o2)
+
+
+@pytest.fixture(scope="module")
+def mixtral():
+    return S.mixtral_moe()
+
+
+@pytest.mark.parametrize("finalize", ["deterministic", "fused"])
+def test_mixtral_full_size_sampled(mixtral, finalize):
+    """T=4096, H=4096, I=14336, E=8, top-2 at full size; 12 sampled tokens checked."""
+    c = mixtral
+    out, ids, w = _run(c, finalize)
+    torch.cuda.synchronize()
+    tokens = np.random.default_rng(0).choice(c.T, 12, replace=False)
+    ref = _oracle(c, ids, w, tokens)
+    assert_close_bf16(to_np(out)[tokens], ref, what=f"mixtral {finalize}")
+
+
+# ------------------------------------------------------------------ finalize
+def test_finalize_parity_one_hot_and_replay():
+    g = np.random.default_rng(0)
+    T, k, H = 300, 8, 512
+    ids = g.integers(0, 40, size=(T, k)).astype(np.int32)
+    srt = O.sort_routes(ids, 64, 32, 0)
+    n = srt["n_local"]
+    y = S.to_bf16(g.standard_normal((n, H), dtype=np.float32))
+    w = g.random((T, k)).astype(np.float32)
+    e2p = torch.from_numpy(srt["e2p"]).to(DEV)
+    out = M.moe_finalize(y.to(DEV), e2p, torch.from_numpy(w).to(DEV))
+    ref = O.finalize(S.bf16_to_f32(y), srt["e2p"], w)
+    assert_close_bf16(out, ref, what="finalize")
+    out2 = M.moe_finalize(y.to(DEV), e2p, torch.from_numpy(w).to(DEV))
+    assert torch.equal(out, out2)
+    onehot = np.zeros_like(w)
+    onehot[np.arange(T), g.integers(0, k, T)] = 1.0
+    o1 = M.moe_finalize(y.to(DEV), e2p, torch.from_numpy(onehot).to(DEV))
+    r1 = O.finalize(S.bf16_to_f32(y), srt["e2p"], onehot)
+    np.testing.assert_array_equal(to_np(o1), r1)   # exact: one bf16 row, weight 1
