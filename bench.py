@@ -91,8 +91,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--cpu-tokens", type=int, default=512)
-    ap.add_argument("--cpu-experts", type=int, default=1)
+    ap.add_argument("--cpu-tokens", type=int, default=4096)
+    ap.add_argument("--cpu-experts", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:

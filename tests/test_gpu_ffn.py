@@ -60,7 +60,15 @@ def test_expert_shard_small_step(clamp_active):
                    x_scale=8.0 if clamp_active else 1.0, seed=3)
     out, ids, w = _run(c)
     ref = _oracle(c, ids, w)
-    assert_close_bf16(out, ref, what="shard")
+    # The layer hands act and y rows over in bf16, so the output error scales with
+    # the route outputs it is combined from; with x scaled by 8 those are far
+    # larger than 1, and both sides are normalised by the RMS of the route outputs.
+    y, local = O.moe_route_outputs(S.bf16_to_f32(c.x), ids.cpu().numpy(), S.bf16_to_f32(c.w1),
+                                   S.bf16_to_f32(c.w2), num_experts=c.num_experts,
+                                   local_offset=c.local_offset, activation_kind=c.activation,
+                                   limits=c.limits)
+    scale = max(1.0, float(np.sqrt(np.mean(y[local] ** 2))))
+    assert_close_bf16(to_np(out) / scale, ref / scale, what="shard")
     # tokens with no local route are exact zero rows
     loc = O.local_expert(ids.cpu().numpy(), 256, 32, 64).reshape(ids.shape)
     none_local = np.all(loc < 0, axis=1)
