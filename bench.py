@@ -21,7 +21,7 @@ sys.path.insert(0, ROOT)
 METRIC = "MoE layer TFLOP/s + tokens/s (T=4096, Mixtral shape); % of MFMA peak"
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 HBM_PEAK_GBS = 8000.0
-FC1_KERNEL = "k_gemm_nt<1>"    # FC1 grouped GEMM with the SwiGLU epilogue
+FC1_KERNEL = "k_gemm_nt<1, true>"  # FC1 grouped GEMM, SwiGLU epilogue, full-K path
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fc1_mixtral_traffic.json")
 KERNEL_SOURCES = ["mixture_experts_expert_softmax_amd/csrc/gemm_bf16.hip",
                   "mixture_experts_expert_softmax_amd/csrc/common.h"]

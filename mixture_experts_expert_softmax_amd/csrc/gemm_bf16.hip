@@ -192,10 +192,99 @@ __device__ __forceinline__ void atomic_add_bf16x2(uint16_t* p, float a, float b)
                                              __builtin_bit_cast(bf16x2_t, bits));
 }
 
+// Main loop for a contraction that is a whole number of 64-wide stages. The body
+// has no branches, so one explicit issue order can be given for it: the 8 weight /
+// activation fragment reads of the next 16-deep step are interleaved with the 16
+// MFMAs of the current one, the 16 global loads of the next stage are spread over
+// the first two steps, and its 16 LDS stores over the last. A lone wave per SIMD
+// only stalls on its own waits, so keeping LDS latency behind MFMA issue is what
+// keeps the matrix cores fed. The final stage re-loads itself (unused) so that
+// the body needs no condition.
+__device__ __forceinline__ void mainloop_full(RowLoader& la, RowLoader& lb, uint4* smem, int ktiles,
+                                              int tid, int lane, int wn, int wm, f32x16 (&acc)[4][4]) {
+  const int lrow = tid >> 3;
+  const int pc = la.ch ^ (lrow & 7);
+  const int rsel = lane & 31, kg = lane >> 5, sw = lane & 7;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    la.r[j] = *reinterpret_cast<const uint4*>(la.base + la.off[j] + la.ch * 8);
+    lb.r[j] = *reinterpret_cast<const uint4*>(lb.base + lb.off[j] + lb.ch * 8);
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    smem[(lrow + 32 * j) * 8 + pc] = la.r[j];
+    smem[TILE_U4 + (lrow + 32 * j) * 8 + pc] = lb.r[j];
+  }
+  __syncthreads();
+  for (int kt = 0; kt < ktiles; ++kt) {
+    const int s = kt & 1;
+    const int kn = (kt + 1 < ktiles ? kt + 1 : kt) * TK + la.ch * 8;
+    const uint4* Xs = smem + s * 2 * TILE_U4;
+    const uint4* Ws = Xs + TILE_U4;
+    uint4* Xn = smem + (s ^ 1) * 2 * TILE_U4;
+    uint4* Wn = Xn + TILE_U4;
+    bf16x8 wf[2][4], xf[2][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wf[0][i] = as_bf16x8(Ws[(wn * 128 + i * 32 + rsel) * 8 + (kg ^ sw)]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) xf[0][j] = as_bf16x8(Xs[(wm * 128 + j * 32 + rsel) * 8 + (kg ^ sw)]);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const int cur = kk & 1, nxt = cur ^ 1;
+      if (kk < 2) {
+#pragma unroll
+        for (int j = kk * 4; j < kk * 4 + 4; ++j) {
+          la.r[j] = *reinterpret_cast<const uint4*>(la.base + la.off[j] + kn);
+          lb.r[j] = *reinterpret_cast<const uint4*>(lb.base + lb.off[j] + kn);
+        }
+      }
+      if (kk < 3) {
+        const int c1 = (((kk + 1) << 1) + kg) ^ sw;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) wf[nxt][i] = as_bf16x8(Ws[(wn * 128 + i * 32 + rsel) * 8 + c1]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) xf[nxt][j] = as_bf16x8(Xs[(wm * 128 + j * 32 + rsel) * 8 + c1]);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[cur][i], xf[cur][j], acc[i][j], 0, 0, 0);
+      if (kk == 3) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          Xn[(lrow + 32 * j) * 8 + pc] = la.r[j];
+          Wn[(lrow + 32 * j) * 8 + pc] = lb.r[j];
+        }
+      }
+    }
+    // issue order (mask 0x008 MFMA, 0x100 LDS read, 0x200 LDS write, 0x020 global load)
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+    for (int q = 0; q < 2; ++q) {
+      for (int r = 0; r < 8; ++r) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      }
+    }
+    for (int r = 0; r < 8; ++r) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    }
+    for (int r = 0; r < 16; ++r) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+    }
+    __syncthreads();
+  }
+}
+
 // ---------------------------------------------------------------------------
 // fwd / FC1 / FC2: both operands contiguous along the contraction.
 // ---------------------------------------------------------------------------
-template <int EPI>
+template <int EPI, bool KFULL>
 __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_nt(NtArgs a) {
   __shared__ uint4 smem[4 * TILE_U4];  // [stage][A tile | B tile], 128 KB
   const int t = xcd_remap(blockIdx.x, gridDim.x);
@@ -245,24 +334,28 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_nt(NtArgs a) {
   zero_acc(acc);
   const int ktiles = (a.K + TK - 1) / TK;
 
-  la.load(0);
-  lb.load(0);
-  la.store(smem, tid);
-  lb.store((smem + TILE_U4), tid);
-  __syncthreads();
-  for (int kt = 0; kt < ktiles; ++kt) {
-    const int s = kt & 1;
-    const bool more = kt + 1 < ktiles;
-    if (more) {
-      la.load(kt + 1);
-      lb.load(kt + 1);
-    }
-    mma_stage((smem + TILE_U4 + s * 2 * TILE_U4), (smem + s * 2 * TILE_U4), wn, wm, lane, acc);
-    if (more) {
-      la.store((smem + (s ^ 1) * 2 * TILE_U4), tid);
-      lb.store((smem + TILE_U4 + (s ^ 1) * 2 * TILE_U4), tid);
-    }
+  if (KFULL) {
+    mainloop_full(la, lb, smem, ktiles, tid, lane, wn, wm, acc);
+  } else {
+    la.load(0);
+    lb.load(0);
+    la.store(smem, tid);
+    lb.store((smem + TILE_U4), tid);
     __syncthreads();
+    for (int kt = 0; kt < ktiles; ++kt) {
+      const int s = kt & 1;
+      const bool more = kt + 1 < ktiles;
+      if (more) {
+        la.load(kt + 1);
+        lb.load(kt + 1);
+      }
+      mma_stage((smem + TILE_U4 + s * 2 * TILE_U4), (smem + s * 2 * TILE_U4), wn, wm, lane, acc);
+      if (more) {
+        la.store((smem + (s ^ 1) * 2 * TILE_U4), tid);
+        lb.store((smem + TILE_U4 + (s ^ 1) * 2 * TILE_U4), tid);
+      }
+      __syncthreads();
+    }
   }
 
   // ---- epilogue: lane holds rows m, 4 consecutive columns per (i, q)
@@ -568,13 +661,18 @@ moe_status gemm_nt_enqueue(int epi, const void* A, const int32_t* a_gather, int 
   a.top_k = top_k;
   const int64_t tiles = (int64_t)a.m_tiles * a.n_tiles;
   const int grid = round_up8(tiles);
+  const bool kfull = (K % TK) == 0;
+#define MOE_LAUNCH_NT(E_)                                              \
+  (kfull ? k_gemm_nt<E_, true><<<grid, NTHREADS, 0, st>>>(a)           \
+         : k_gemm_nt<E_, false><<<grid, NTHREADS, 0, st>>>(a))
   switch (epi) {
-    case EPI_STORE: k_gemm_nt<EPI_STORE><<<grid, NTHREADS, 0, st>>>(a); break;
-    case EPI_SWIGLU: k_gemm_nt<EPI_SWIGLU><<<grid, NTHREADS, 0, st>>>(a); break;
-    case EPI_SWIGLU_STEP: k_gemm_nt<EPI_SWIGLU_STEP><<<grid, NTHREADS, 0, st>>>(a); break;
-    case EPI_FUSED: k_gemm_nt<EPI_FUSED><<<grid, NTHREADS, 0, st>>>(a); break;
+    case EPI_STORE: MOE_LAUNCH_NT(EPI_STORE); break;
+    case EPI_SWIGLU: MOE_LAUNCH_NT(EPI_SWIGLU); break;
+    case EPI_SWIGLU_STEP: MOE_LAUNCH_NT(EPI_SWIGLU_STEP); break;
+    case EPI_FUSED: MOE_LAUNCH_NT(EPI_FUSED); break;
     default: return MOE_ERR_DTYPE;
   }
+#undef MOE_LAUNCH_NT
   return launch_status();
 }
 
