@@ -94,11 +94,24 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=4096)
     ap.add_argument("--cpu-experts", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 512 MiB device-to-device copy (3x): the known-size "
+                         "reference for rocprofv3 FETCH_SIZE / WRITE_SIZE counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for {args.gpus}).",
               file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        import torch
+        n = 512 << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "copies": 3}), flush=True)
+        return
 
     import numpy as np
     import torch

@@ -26,10 +26,10 @@
 //    workgroup decodes its (expert, row block) from the device offsets, clamps
 //    row reads inside its group and masks stores. Rows of a partial contraction
 //    tile are zero-filled.
-//  * blockIdx -> tile: consecutive workgroups land on different XCDs, so the
-//    block index is remapped to give every XCD a contiguous range of tiles, and
-//    tiles are rastered in groups of 4 row blocks so that operands are reused
-//    from the XCD's L2.
+//  * blockIdx -> tile: consecutive workgroups land on different XCDs, so every
+//    XCD is given a contiguous range of the real tiles (counted on the device),
+//    ordered expert-major, column tile, row block: the row blocks sharing a
+//    weight tile run together on one XCD and read it from HBM once.
 #include "common.h"
 
 namespace moe {
@@ -38,7 +38,6 @@ namespace {
 constexpr int TB = 256;        // tile rows on each side
 constexpr int TK = 64;         // contraction per stage
 constexpr int NTHREADS = 256;  // 4 waves
-constexpr int RASTER_M = 4;    // row blocks per raster group
 constexpr int TILE_U4 = TB * TK * 2 / 16;  // uint4 slots per operand tile (2048)
 
 enum Epi { EPI_STORE = 0, EPI_SWIGLU = 1, EPI_SWIGLU_STEP = 2, EPI_FUSED = 3 };
@@ -73,21 +72,45 @@ __device__ __forceinline__ int xcd_remap(int b, int nblocks) {
   return (b & 7) * per + (b >> 3);
 }
 
-// Row block mt of the concatenated groups -> (expert, first row, group end).
-__device__ __forceinline__ bool decode_row_block(const int32_t* __restrict__ ends, int E,
-                                                 int m_cap, int mt, int& e, int& m0, int& mend) {
-  int acc = 0, start = 0;
+__device__ __forceinline__ int clamp_end(int v, int start, int m_cap) {
+  return v < start ? start : (v > m_cap ? m_cap : v);
+}
+
+// Tile of this workgroup for a ragged grouped GEMM with n_tiles column tiles.
+// The grid is an upper bound (no host sync), so every workgroup first counts the
+// real tiles from the device offsets and deals exactly those out: XCD x = b % 8
+// (the hardware's round-robin placement) takes the contiguous range
+// [x*per, (x+1)*per), so no XCD is left with only the empty tail. Tiles are
+// ordered expert-major, then column tile, then row block fastest: the row blocks
+// that share one weight tile run together on one XCD and read it once from HBM.
+__device__ __forceinline__ bool decode_tile(const int32_t* __restrict__ ends, int E, int m_cap,
+                                            int n_tiles, int& e, int& m0, int& mend, int& nt) {
+  int total = 0, start = 0;
   for (int g = 0; g < E; ++g) {
-    int end = ends[g];
-    end = end < start ? start : (end > m_cap ? m_cap : end);
+    const int end = clamp_end(ends[g], start, m_cap);
+    total += (end - start + TB - 1) / TB;
+    start = end;
+  }
+  total *= n_tiles;
+  const int per = (total + 7) >> 3;
+  const int slot = (int)(blockIdx.x >> 3);
+  const int t = (int)(blockIdx.x & 7) * per + slot;
+  if (slot >= per || t >= total) return false;
+  int acc = 0;
+  start = 0;
+  for (int g = 0; g < E; ++g) {
+    const int end = clamp_end(ends[g], start, m_cap);
     const int te = (end - start + TB - 1) / TB;
-    if (mt < acc + te) {
+    const int cnt = te * n_tiles;
+    if (t < acc + cnt) {
+      const int r = t - acc;
+      nt = r / te;
       e = g;
-      m0 = start + (mt - acc) * TB;
+      m0 = start + (r - nt * te) * TB;
       mend = end;
       return true;
     }
-    acc += te;
+    acc += cnt;
     start = end;
   }
   return false;
@@ -287,18 +310,8 @@ __device__ __forceinline__ void mainloop_full(RowLoader& la, RowLoader& lb, uint
 template <int EPI, bool KFULL>
 __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_nt(NtArgs a) {
   __shared__ uint4 smem[4 * TILE_U4];  // [stage][A tile | B tile], 128 KB
-  const int t = xcd_remap(blockIdx.x, gridDim.x);
-  const int span = RASTER_M * a.n_tiles;
-  const int grp = t / span;
-  const int first_mt = grp * RASTER_M;
-  const int gm = min(RASTER_M, a.m_tiles - first_mt);
-  if (gm <= 0) return;
-  const int within = t - grp * span;
-  const int mt = first_mt + within % gm;
-  const int nt = within / gm;
-  if (nt >= a.n_tiles) return;
-  int e, m0, mend;
-  if (!decode_row_block(a.ends, a.E, a.m_cap, mt, e, m0, mend)) return;
+  int e, m0, mend, nt;
+  if (!decode_tile(a.ends, a.E, a.m_cap, a.n_tiles, e, m0, mend, nt)) return;
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int wn = wid & 1, wm = wid >> 1;
@@ -437,18 +450,8 @@ struct DgradArgs {
 
 __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_dgrad(DgradArgs a) {
   __shared__ uint4 smem[4 * TILE_U4];
-  const int t = xcd_remap(blockIdx.x, gridDim.x);
-  const int span = RASTER_M * a.n_tiles;
-  const int grp = t / span;
-  const int first_mt = grp * RASTER_M;
-  const int gm = min(RASTER_M, a.m_tiles - first_mt);
-  if (gm <= 0) return;
-  const int within = t - grp * span;
-  const int mt = first_mt + within % gm;
-  const int nt = within / gm;  // tile of K (output columns)
-  if (nt >= a.n_tiles) return;
-  int e, m0, mend;
-  if (!decode_row_block(a.ends, a.E, a.m_cap, mt, e, m0, mend)) return;
+  int e, m0, mend, nt;  // nt: tile of K (output columns)
+  if (!decode_tile(a.ends, a.E, a.m_cap, a.n_tiles, e, m0, mend, nt)) return;
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int wn = wid & 1, wm = wid >> 1;
