@@ -94,6 +94,8 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=4096)
     ap.add_argument("--cpu-experts", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="skip the secondary rows (grouped GEMMs, expert shard, large route/sort/finalize)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 512 MiB device-to-device copy (3x): the known-size "
                          "reference for rocprofv3 FETCH_SIZE / WRITE_SIZE counters")
@@ -229,7 +231,113 @@ def main():
         "cpu_baseline": cpu,
         "wall_s_timed": round(wall, 3),
     }
+    if not args.no_secondary:
+        del x, w1, w2, act, y, out, out_fused
+        torch.cuda.empty_cache()
+        line["secondary"] = secondary_measurements(progress)
     print(json.dumps(line), flush=True)
+
+
+def _time(fn, reps=10, warmup=3):
+    """Mean milliseconds of fn() over reps, timed with events on the current stream."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(reps):
+        fn()
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / reps
+
+
+def secondary_measurements(progress):
+    """The other hot-path rows at their own workloads (not the headline step):
+    the standalone grouped GEMMs, the expert-shard forward, and routing / sort /
+    finalize at sizes large enough to load HBM."""
+    import numpy as np
+    import torch
+    import mixture_experts_expert_softmax_amd as M
+    import moe_synth as S
+    dev = "cuda"
+    res = {}
+
+    progress("secondary: grouped GEMM E=16 sum_m=8192 K=2048 N=4096")
+    c = S.grouped_gemm_case(seed=0)
+    x, g, w = c.x.to(dev), c.g.to(dev), c.w.to(dev)
+    offs = torch.from_numpy(c.offs).to(dev)
+    Mr, K, N, E = c.sum_m, 2048, 4096, c.E
+    fl = 2.0 * Mr * K * N
+    yb = torch.empty((Mr, N), dtype=torch.bfloat16, device=dev)
+    dxb = torch.empty((Mr, K), dtype=torch.bfloat16, device=dev)
+    dwb = torch.empty((E, N, K), dtype=torch.bfloat16, device=dev)
+    dwf = torch.empty((E, N, K), dtype=torch.float32, device=dev)
+    gg = {}
+    for name, fn in [("fwd", lambda: M.grouped_gemm_fwd(x, w, offs, out=yb)),
+                     ("dgrad", lambda: M.grouped_gemm_dgrad(g, w, offs, out=dxb)),
+                     ("wgrad_bf16", lambda: M.grouped_gemm_wgrad(g, x, offs, out=dwb)),
+                     ("wgrad_f32", lambda: M.grouped_gemm_wgrad(g, x, offs, out=dwf))]:
+        ms_ = _time(fn)
+        gg[name] = {"ms": round(ms_, 4), "tflops": round(fl / (ms_ * 1e-3) / 1e12, 1),
+                    "mfma_frac": round(fl / (ms_ * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
+    gg["group_sizes"] = c.sizes.tolist()
+    res["grouped_gemm"] = gg
+    del x, g, w, yb, dxb, dwb, dwf
+
+    progress("secondary: expert shard T=8192 H=7168 I=2048, 32 of 256 experts, top-8, SwiGLUStep")
+    cs = S.expert_shard_moe(seed=0)
+    lg = torch.from_numpy(cs.logits).to(dev)
+    xs, w1s, w2s = cs.x.to(dev), cs.w1.to(dev), cs.w2.to(dev)
+    lim = torch.from_numpy(cs.limits).to(dev)
+    ids, wts = M.moe_route(lg, cs.top_k)
+    outs = torch.empty((cs.T, cs.H), dtype=torch.bfloat16, device=dev)
+    ws_bytes = M.moe_ffn_workspace_size(cs.T, cs.H, cs.I, cs.num_experts, cs.top_k, cs.num_local,
+                                        cs.local_offset, "swiglu_step")
+    wsp = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+
+    def shard_step():
+        M.moe_route(lg, cs.top_k, ids, wts)
+        M.moe_ffn_forward(xs, ids, wts, w1s, w2s, cs.num_experts, cs.num_local, cs.local_offset,
+                          "swiglu_step", lim, out=outs, workspace=wsp)
+    ms_ = _time(shard_step)
+    srt = M.moe_sort(ids, cs.num_experts, cs.num_local, cs.local_offset)
+    n_loc = int(srt["n_local"].item())
+    fl = 6.0 * cs.H * cs.I * n_loc
+    wbytes = (w1s.numel() + w2s.numel()) * 2
+    res["expert_shard"] = {"ms": round(ms_, 4), "tflops": round(fl / (ms_ * 1e-3) / 1e12, 1),
+                           "tokens_per_s": round(cs.T / (ms_ * 1e-3), 1), "n_local_routes": n_loc,
+                           "weight_gbs": round(wbytes / (ms_ * 1e-3) / 1e9, 1)}
+    del xs, w1s, w2s, wsp, outs
+
+    progress("secondary: route + sort at T=262144, 256 experts, top-8")
+    T2, E2, k2 = 262144, 256, 8
+    lg2 = torch.from_numpy(S.route_logits(np.random.default_rng(1), T2, E2)).to(dev)
+    ids2 = torch.empty((T2, k2), dtype=torch.int32, device=dev)
+    w2t = torch.empty((T2, k2), dtype=torch.float32, device=dev)
+    ms_r = _time(lambda: M.moe_route(lg2, k2, ids2, w2t))
+    ws2 = torch.empty(M.lib().moe_sort_workspace_size(T2, k2, E2), dtype=torch.uint8, device=dev)
+    ms_s = _time(lambda: M.moe_sort(ids2, E2, workspace=ws2))
+    route_bytes = T2 * E2 * 4 + T2 * k2 * 8
+    sort_bytes = T2 * k2 * 4 * 2 + T2 * k2 * 8   # ids read twice, e2p + p2e written
+    res["route_large"] = {"ms": round(ms_r, 4), "gbs": round(route_bytes / (ms_r * 1e-3) / 1e9, 1),
+                          "hbm_frac": round(route_bytes / (ms_r * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    res["sort_large"] = {"ms": round(ms_s, 4), "gbs": round(sort_bytes / (ms_s * 1e-3) / 1e9, 1),
+                         "hbm_frac": round(sort_bytes / (ms_s * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                         "note": "includes the binding's output allocation"}
+
+    progress("secondary: finalize at T=65536, H=7168, top-8")
+    T3, H3, k3 = 65536, 7168, 8
+    e2p = torch.randperm(T3 * k3, device=dev).to(torch.int32)
+    yr = torch.randn((T3 * k3, H3), device=dev).to(torch.bfloat16)
+    w3 = torch.rand((T3, k3), device=dev)
+    o3 = torch.empty((T3, H3), dtype=torch.bfloat16, device=dev)
+    ms_f = _time(lambda: M.moe_finalize(yr, e2p, w3, out=o3))
+    fb = T3 * k3 * H3 * 2 + T3 * H3 * 2 + T3 * k3 * 8
+    res["finalize_large"] = {"ms": round(ms_f, 4), "gbs": round(fb / (ms_f * 1e-3) / 1e9, 1),
+                             "hbm_frac": round(fb / (ms_f * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    return res
 
 
 if __name__ == "__main__":
