@@ -69,6 +69,11 @@ typedef int32_t moe_status;
 #define MOE_FINALIZE_FUSED         1  /* FC2 epilogue adds w*y into a zeroed output with bf16 atomics */
 #define MOE_FINALIZE_NONE          2  /* stop after FC2: return y rows and e2p ([StepFun] do_finalize=False) */
 
+/* Number formats of moe_ffn_forward's operands ([W4A8] "Inputs"). */
+#define MOE_WFMT_BF16  0  /* x, w1, w2 in bf16 */
+#define MOE_WFMT_MXFP4 1  /* w1, w2 MXFP4 (e2m1 pairs + UE8M0 per 32), x MXFP8 (e4m3 + UE8M0 per 32);
+                             the FC1 output is requantized to MXFP8 with the round-up rule */
+
 /* Meaning of a grouped-GEMM offsets array ([GGEMM] intro). */
 #define MOE_OFFS_ENDS   0  /* offs[E]: cumulative end row of each group */
 #define MOE_OFFS_INDPTR 1  /* m_indptr[E+1]: leading zero, then cumulative ends */
@@ -157,19 +162,24 @@ typedef struct moe_ffn_desc {
   int32_t local_expert_offset;/* global id of local expert 0 */
   int32_t top_k;              /* 1..16 */
   int32_t activation;         /* MOE_ACT_* */
-  int32_t finalize_mode;      /* MOE_FINALIZE_* */
+  int32_t finalize_mode;      /* MOE_FINALIZE_* (MXFP4: DETERMINISTIC or NONE) */
+  int32_t weight_format;      /* MOE_WFMT_*; MXFP4 needs H % 128 == 0 and I % 128 == 0 */
 } moe_ffn_desc;
 
 typedef struct moe_ffn_tensors {
-  const void* x;              /* [T, H] bf16 */
+  const void* x;              /* [T, H] bf16, or e4m3fn codes (MXFP4 format) */
   const int32_t* topk_ids;    /* [T, top_k] int32 global expert ids */
   const float* topk_weights;  /* [T, top_k] float32, normalized by the caller */
-  const void* w1;             /* [L, 2I, H] bf16: rows 0..I-1 up, I..2I-1 gate */
-  const void* w2;             /* [L, H, I] bf16 */
+  const void* w1;             /* [L, 2I, H] bf16: rows 0..I-1 up, I..2I-1 gate
+                                 (MXFP4: [L, 2I, H/2] bytes, element 2j in the low nibble) */
+  const void* w2;             /* [L, H, I] bf16 (MXFP4: [L, H, I/2] bytes) */
   const float* clamp_limit;   /* [L] float32 SwiGLUStep limits, or NULL for 7.0 */
   void* out;                  /* [T, H] bf16 (DETERMINISTIC / FUSED), fully overwritten */
   void* y;                    /* NONE only: [T*top_k, H] bf16 capacity, FC2 rows in permuted order */
   int32_t* e2p;               /* NONE only (optional otherwise): [T*top_k] int32 */
+  const void* x_sf;           /* MXFP4 format: [T, H/32] UE8M0 codes (uint8) */
+  const void* w1_sf;          /* MXFP4 format: [L, 2I, H/32] UE8M0 */
+  const void* w2_sf;          /* MXFP4 format: [L, H, I/32] UE8M0 */
 } moe_ffn_tensors;
 
 size_t moe_ffn_workspace_size(const moe_ffn_desc* desc);
@@ -198,6 +208,22 @@ moe_status moe_fc1(const moe_ffn_desc* desc, const void* x, const void* w1,
 moe_status moe_fc2(const moe_ffn_desc* desc, const void* act, const void* w2,
                    const int32_t* offs, const int32_t* p2e, const float* topk_weights, void* dst,
                    void* stream);
+
+/*
+ * The MXFP4 (W4A8) stages ([W4A8] "Inputs"; intro: fp32 accumulation, UE8M0
+ * round-up requantization). desc->weight_format must be MOE_WFMT_MXFP4.
+ * moe_fc1_mx: act = MXFP8(activation(x[p2e[p]/top_k] @ w1[e].T)) with, per row and
+ *             block of 32 columns, the smallest power-of-two scale 2^s such that the
+ *             block maximum is <= 448 * 2^s (code s+127) and elements rounded to
+ *             nearest even e4m3fn. act [T*top_k, I] e4m3 codes, act_sf [T*top_k, I/32].
+ * moe_fc2_mx: y[p, :] = act[p] @ w2[e].T, bf16 rows [T*top_k, H] in permuted order.
+ */
+moe_status moe_fc1_mx(const moe_ffn_desc* desc, const void* x, const void* x_sf, const void* w1,
+                      const void* w1_sf, const float* clamp_limit, const int32_t* offs,
+                      const int32_t* p2e, void* act, void* act_sf, void* stream);
+moe_status moe_fc2_mx(const moe_ffn_desc* desc, const void* act, const void* act_sf,
+                      const void* w2, const void* w2_sf, const int32_t* offs, void* y,
+                      void* stream);
 
 /*
  * moe_finalize -- deterministic top-k combine ([SM90] use_fused_finalize=False):

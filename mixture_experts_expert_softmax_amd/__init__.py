@@ -21,7 +21,8 @@ import torch
 __all__ = [
     "MoeError", "lib", "library_path", "EXPORTS", "moe_route", "moe_sort", "grouped_gemm_fwd",
     "grouped_gemm_dgrad", "grouped_gemm_wgrad", "moe_ffn_forward", "moe_ffn_workspace_size",
-    "moe_finalize", "moe_fc1", "moe_fc2", "status_string", "ACT", "FINALIZE",
+    "moe_finalize", "moe_fc1", "moe_fc2", "status_string", "ACT", "FINALIZE", "WFMT",
+    "moe_ffn_forward_mx", "moe_fc1_mx", "moe_fc2_mx",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -36,15 +37,19 @@ _i32, _i64, _u64, _vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64, ctypes.
 _sz = ctypes.c_size_t
 
 
+WFMT = {"bf16": 0, "mxfp4": 1}
+
+
 class MoeFfnDesc(ctypes.Structure):
     _fields_ = [("T", _i64), ("H", _i32), ("I", _i32), ("num_experts", _i32),
                 ("num_local_experts", _i32), ("local_expert_offset", _i32), ("top_k", _i32),
-                ("activation", _i32), ("finalize_mode", _i32)]
+                ("activation", _i32), ("finalize_mode", _i32), ("weight_format", _i32)]
 
 
 class MoeFfnTensors(ctypes.Structure):
     _fields_ = [("x", _vp), ("topk_ids", _vp), ("topk_weights", _vp), ("w1", _vp), ("w2", _vp),
-                ("clamp_limit", _vp), ("out", _vp), ("y", _vp), ("e2p", _vp)]
+                ("clamp_limit", _vp), ("out", _vp), ("y", _vp), ("e2p", _vp),
+                ("x_sf", _vp), ("w1_sf", _vp), ("w2_sf", _vp)]
 
 
 # name -> (restype, argtypes)
@@ -63,6 +68,8 @@ EXPORTS = {
     "moe_finalize": (_i32, [_vp, _vp, _vp, _i64, _i32, _i32, _vp, _vp]),
     "moe_fc1": (_i32, [ctypes.POINTER(MoeFfnDesc), _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "moe_fc2": (_i32, [ctypes.POINTER(MoeFfnDesc), _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "moe_fc1_mx": (_i32, [ctypes.POINTER(MoeFfnDesc), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "moe_fc2_mx": (_i32, [ctypes.POINTER(MoeFfnDesc), _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
 }
 
 _LIB: Optional[ctypes.CDLL] = None
@@ -211,14 +218,16 @@ def grouped_gemm_wgrad(g: torch.Tensor, x: torch.Tensor, offs: torch.Tensor, E: 
 
 
 # --------------------------------------------------------------------------- MoE layer
-def _ffn_desc(T, H, I, num_experts, L, off, k, activation, finalize):
-    return MoeFfnDesc(T, H, I, num_experts, L, off, k, ACT[activation], FINALIZE[finalize])
+def _ffn_desc(T, H, I, num_experts, L, off, k, activation, finalize, wfmt="bf16"):
+    return MoeFfnDesc(T, H, I, num_experts, L, off, k, ACT[activation], FINALIZE[finalize], WFMT[wfmt])
 
 
 def moe_ffn_workspace_size(T, H, I, num_experts, top_k, num_local_experts=None,
-                           local_expert_offset=0, activation="swiglu", finalize="deterministic"):
+                           local_expert_offset=0, activation="swiglu", finalize="deterministic",
+                           weight_format="bf16"):
     L = num_experts if num_local_experts is None else num_local_experts
-    d = _ffn_desc(T, H, I, num_experts, L, local_expert_offset, top_k, activation, finalize)
+    d = _ffn_desc(T, H, I, num_experts, L, local_expert_offset, top_k, activation, finalize,
+                  weight_format)
     return lib().moe_ffn_workspace_size(ctypes.byref(d))
 
 
@@ -256,7 +265,7 @@ def moe_ffn_forward(x: torch.Tensor, topk_ids: torch.Tensor, topk_weights: torch
     tens = MoeFfnTensors(x.data_ptr(), topk_ids.data_ptr(), topk_weights.data_ptr(), w1.data_ptr(),
                          w2.data_ptr(), None if clamp_limit is None else clamp_limit.data_ptr(),
                          None if out is None else out.data_ptr(), None if y is None else y.data_ptr(),
-                         None if e2p is None else e2p.data_ptr())
+                         None if e2p is None else e2p.data_ptr(), None, None, None)
     _check("moe_ffn_forward", h.moe_ffn_forward(ctypes.byref(d), ctypes.byref(tens), _ptr(workspace),
                                                 workspace.numel(), _stream()))
     if finalize == "none":
@@ -295,6 +304,80 @@ def moe_fc2(act: torch.Tensor, w2: torch.Tensor, offs: torch.Tensor, T: int, top
     _check("moe_fc2", lib().moe_fc2(ctypes.byref(d), _ptr(act), _ptr(w2), _ptr(offs), _ptr(p2e),
                                     _ptr(topk_weights), _ptr(dst), _stream()))
     return dst
+
+
+def moe_ffn_forward_mx(x: torch.Tensor, x_sf: torch.Tensor, topk_ids: torch.Tensor,
+                       topk_weights: torch.Tensor, w1: torch.Tensor, w1_sf: torch.Tensor,
+                       w2: torch.Tensor, w2_sf: torch.Tensor, num_experts: int,
+                       num_local_experts: Optional[int] = None, local_expert_offset: int = 0,
+                       activation: str = "swiglu", clamp_limit: Optional[torch.Tensor] = None,
+                       finalize: str = "deterministic", out: Optional[torch.Tensor] = None,
+                       workspace: Optional[torch.Tensor] = None, y: Optional[torch.Tensor] = None,
+                       e2p: Optional[torch.Tensor] = None):
+    """W4A8 layer: x MXFP8 (uint8 e4m3 codes [T,H] + UE8M0 [T,H/32]), w1 / w2 MXFP4 (packed
+    uint8 [L,2I,H/2] / [L,H,I/2] + UE8M0 [L,2I,H/32] / [L,H,I/32]); bf16 output."""
+    for t_, n_ in [(x, "x"), (x_sf, "x_sf"), (w1, "w1"), (w1_sf, "w1_sf"), (w2, "w2"), (w2_sf, "w2_sf")]:
+        _dev(t_, torch.uint8, n_)
+    _dev(topk_ids, torch.int32, "topk_ids"), _dev(topk_weights, torch.float32, "topk_weights")
+    if clamp_limit is not None:
+        _dev(clamp_limit, torch.float32, "clamp_limit")
+    T, H = x.shape
+    L, twoI, _ = w1.shape
+    I = twoI // 2
+    k = topk_ids.shape[1]
+    d = _ffn_desc(T, H, I, num_experts, L, local_expert_offset, k, activation, finalize, "mxfp4")
+    h = lib()
+    ws_bytes = h.moe_ffn_workspace_size(ctypes.byref(d))
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=x.device)
+    if finalize == "none":
+        if y is None:
+            y = torch.empty((max(T * k, 1), H), dtype=torch.bfloat16, device=x.device)
+        if e2p is None:
+            e2p = torch.empty(max(T * k, 1), dtype=torch.int32, device=x.device)
+    elif out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
+    tens = MoeFfnTensors(x.data_ptr(), topk_ids.data_ptr(), topk_weights.data_ptr(), w1.data_ptr(),
+                         w2.data_ptr(), None if clamp_limit is None else clamp_limit.data_ptr(),
+                         None if out is None else out.data_ptr(), None if y is None else y.data_ptr(),
+                         None if e2p is None else e2p.data_ptr(), x_sf.data_ptr(), w1_sf.data_ptr(),
+                         w2_sf.data_ptr())
+    _check("moe_ffn_forward", h.moe_ffn_forward(ctypes.byref(d), ctypes.byref(tens), _ptr(workspace),
+                                                workspace.numel(), _stream()))
+    if finalize == "none":
+        return y, e2p[: T * k]
+    return out
+
+
+def moe_fc1_mx(x, x_sf, w1, w1_sf, offs, p2e, top_k, num_experts, local_expert_offset=0,
+               activation="swiglu", clamp_limit=None, act=None, act_sf=None):
+    """act (MXFP8 codes [T*k, I] + UE8M0 [T*k, I/32]) = requant(activation(FC1)) per permuted row."""
+    T, H = x.shape
+    L, twoI, _ = w1.shape
+    I = twoI // 2
+    d = _ffn_desc(T, H, I, num_experts, L, local_expert_offset, top_k, activation,
+                  "deterministic", "mxfp4")
+    if act is None:
+        act = torch.empty((max(T * top_k, 1), I), dtype=torch.uint8, device=x.device)
+    if act_sf is None:
+        act_sf = torch.empty((max(T * top_k, 1), I // 32), dtype=torch.uint8, device=x.device)
+    _check("moe_fc1_mx", lib().moe_fc1_mx(ctypes.byref(d), _ptr(x), _ptr(x_sf), _ptr(w1), _ptr(w1_sf),
+                                          _ptr(clamp_limit), _ptr(offs), _ptr(p2e), _ptr(act),
+                                          _ptr(act_sf), _stream()))
+    return act, act_sf
+
+
+def moe_fc2_mx(act, act_sf, w2, w2_sf, offs, T, top_k, num_experts, local_expert_offset=0, y=None):
+    """y [T*k, H] bf16 = act @ w2[e].T for the permuted rows (MXFP8 x MXFP4)."""
+    L, H, halfI = w2.shape
+    I = halfI * 2
+    d = _ffn_desc(T, H, I, num_experts, L, local_expert_offset, top_k, "swiglu", "deterministic",
+                  "mxfp4")
+    if y is None:
+        y = torch.empty((max(T * top_k, 1), H), dtype=torch.bfloat16, device=act.device)
+    _check("moe_fc2_mx", lib().moe_fc2_mx(ctypes.byref(d), _ptr(act), _ptr(act_sf), _ptr(w2), _ptr(w2_sf),
+                                          _ptr(offs), _ptr(y), _stream()))
+    return y
 
 
 def moe_finalize(y: torch.Tensor, e2p: torch.Tensor, topk_weights: torch.Tensor, out=None):

@@ -22,6 +22,14 @@ moe_status gemm_dgrad_enqueue(const void* G, const void* W, const int32_t* ends,
 moe_status gemm_wgrad_enqueue(const void* G, const void* X, const int32_t* ends, int E, int64_t M,
                               int N, int K, void* DW, bool out_f32, hipStream_t st);
 moe_status zero_fill(void* p, size_t bytes, hipStream_t st);
+// defined in gemm_mx.hip
+moe_status mx_fc1_enqueue(int activation, const void* x, const void* x_sf, const int32_t* p2e,
+                          int top_k, const void* w1, const void* w1_sf, int L, const int32_t* offs,
+                          int64_t R, int H, int I, const float* limits, void* act, void* act_sf,
+                          hipStream_t st);
+moe_status mx_fc2_enqueue(const void* act, const void* act_sf, const void* w2, const void* w2_sf,
+                          int L, const int32_t* offs, int64_t R, int H, int I, void* y,
+                          hipStream_t st);
 
 int device_cu_count() {
   static int cached[64] = {0};
@@ -58,7 +66,7 @@ moe_status check_gemm(const void* p0, const void* p1, const int32_t* offs, int32
 }
 
 struct FfnLayout {
-  size_t sort_ws, offs, e2p, p2e, n_local, act, y, total;
+  size_t sort_ws, offs, e2p, p2e, n_local, act, act_sf, y, total;
 };
 
 FfnLayout ffn_layout(const moe_ffn_desc* d) {
@@ -72,7 +80,9 @@ FfnLayout ffn_layout(const moe_ffn_desc* d) {
   l.e2p = o;     o += align_up((size_t)R * 4, 256);
   l.p2e = o;     o += align_up((size_t)R * 4, 256);
   l.n_local = o; o += 256;
-  l.act = o;     o += align_up((size_t)R * d->I * 2, 256);
+  const bool mx = d->weight_format == MOE_WFMT_MXFP4;
+  l.act = o;     o += align_up((size_t)R * d->I * (mx ? 1 : 2), 256);
+  l.act_sf = o;  o += mx ? align_up((size_t)R * (d->I / 32), 256) : 0;
   l.y = o;
   if (d->finalize_mode == MOE_FINALIZE_DETERMINISTIC) o += align_up((size_t)R * d->H * 2, 256);
   l.total = o;
@@ -148,6 +158,11 @@ static moe_status check_ffn(const moe_ffn_desc* d) {
   if (d->activation != MOE_ACT_SWIGLU && d->activation != MOE_ACT_SWIGLU_STEP) return MOE_ERR_DTYPE;
   if (d->finalize_mode < MOE_FINALIZE_DETERMINISTIC || d->finalize_mode > MOE_FINALIZE_NONE)
     return MOE_ERR_DTYPE;
+  if (d->weight_format != MOE_WFMT_BF16 && d->weight_format != MOE_WFMT_MXFP4) return MOE_ERR_DTYPE;
+  if (d->weight_format == MOE_WFMT_MXFP4) {
+    if (d->H % 128 || d->I % 128) return MOE_ERR_SHAPE;
+    if (d->finalize_mode == MOE_FINALIZE_FUSED) return MOE_ERR_UNSUPPORTED;
+  }
   const int64_t R = d->T * d->top_k;
   if (R > INT32_MAX || R * std::max(d->H, 2 * d->I) >= U32_ELEMS || d->T * d->H >= U32_ELEMS)
     return MOE_ERR_UNSUPPORTED;
@@ -195,11 +210,15 @@ extern "C" moe_status moe_ffn_forward(const moe_ffn_desc* d, const moe_ffn_tenso
   if (d->T == 0) return MOE_OK;
   const int32_t L = d->num_local_experts > 0 ? d->num_local_experts : d->num_experts;
   const int fm = d->finalize_mode;
+  const bool mx = d->weight_format == MOE_WFMT_MXFP4;
   if (!t->x || !t->topk_ids || !t->topk_weights || !t->w1 || !t->w2) return MOE_ERR_NULL;
+  if (mx && (!t->x_sf || !t->w1_sf || !t->w2_sf)) return MOE_ERR_NULL;
   if (fm != MOE_FINALIZE_NONE && !t->out) return MOE_ERR_NULL;
   if (fm == MOE_FINALIZE_NONE && (!t->y || !t->e2p)) return MOE_ERR_NULL;
   if (!aligned16(t->x) || !aligned16(t->w1) || !aligned16(t->w2) ||
       (t->out && !aligned16(t->out)) || (t->y && !aligned16(t->y)))
+    return MOE_ERR_ALIGN;
+  if (mx && (!aligned16(t->x_sf) || !aligned16(t->w1_sf) || !aligned16(t->w2_sf)))
     return MOE_ERR_ALIGN;
   const FfnLayout l = ffn_layout(d);
   if (!ws || ws_bytes < l.total || !aligned16(ws)) return MOE_ERR_WORKSPACE;
@@ -216,11 +235,50 @@ extern "C" moe_status moe_ffn_forward(const moe_ffn_desc* d, const moe_ffn_tenso
   s = sort_enqueue(t->topk_ids, d->T, d->top_k, d->num_experts, L, d->local_expert_offset, offs,
                    nullptr, e2p, p2e, nloc, w + l.sort_ws, st);
   if (s != MOE_OK) return s;
-  s = fc1_enqueue(d, t->x, t->w1, t->clamp_limit, offs, p2e, act, st);
-  if (s != MOE_OK) return s;
-  s = fc2_enqueue(d, act, t->w2, offs, p2e, t->topk_weights, fm == MOE_FINALIZE_FUSED ? t->out : y, st);
+  if (mx) {
+    const int64_t R = d->T * d->top_k;
+    s = mx_fc1_enqueue(d->activation, t->x, t->x_sf, p2e, d->top_k, t->w1, t->w1_sf, L, offs, R, H,
+                       d->I, t->clamp_limit, act, w + l.act_sf, st);
+    if (s != MOE_OK) return s;
+    s = mx_fc2_enqueue(act, w + l.act_sf, t->w2, t->w2_sf, L, offs, R, H, d->I, y, st);
+  } else {
+    s = fc1_enqueue(d, t->x, t->w1, t->clamp_limit, offs, p2e, act, st);
+    if (s != MOE_OK) return s;
+    s = fc2_enqueue(d, act, t->w2, offs, p2e, t->topk_weights, fm == MOE_FINALIZE_FUSED ? t->out : y,
+                    st);
+  }
   if (s != MOE_OK || fm != MOE_FINALIZE_DETERMINISTIC) return s;
   return finalize_enqueue(y, e2p, t->topk_weights, d->T, d->top_k, H, t->out, st);
+}
+
+extern "C" moe_status moe_fc1_mx(const moe_ffn_desc* d, const void* x, const void* x_sf,
+                                 const void* w1, const void* w1_sf, const float* clamp_limit,
+                                 const int32_t* offs, const int32_t* p2e, void* act, void* act_sf,
+                                 void* stream) {
+  moe_status s = check_ffn(d);
+  if (s != MOE_OK) return s;
+  if (d->weight_format != MOE_WFMT_MXFP4) return MOE_ERR_DTYPE;
+  if (d->T == 0) return MOE_OK;
+  if (!x || !x_sf || !w1 || !w1_sf || !offs || !p2e || !act || !act_sf) return MOE_ERR_NULL;
+  if (!aligned16(x) || !aligned16(w1) || !aligned16(act) || !aligned16(x_sf) || !aligned16(w1_sf))
+    return MOE_ERR_ALIGN;
+  const int32_t L = d->num_local_experts > 0 ? d->num_local_experts : d->num_experts;
+  return mx_fc1_enqueue(d->activation, x, x_sf, p2e, d->top_k, w1, w1_sf, L, offs,
+                        d->T * d->top_k, d->H, d->I, clamp_limit, act, act_sf, as_stream(stream));
+}
+
+extern "C" moe_status moe_fc2_mx(const moe_ffn_desc* d, const void* act, const void* act_sf,
+                                 const void* w2, const void* w2_sf, const int32_t* offs, void* y,
+                                 void* stream) {
+  moe_status s = check_ffn(d);
+  if (s != MOE_OK) return s;
+  if (d->weight_format != MOE_WFMT_MXFP4) return MOE_ERR_DTYPE;
+  if (d->T == 0) return MOE_OK;
+  if (!act || !act_sf || !w2 || !w2_sf || !offs || !y) return MOE_ERR_NULL;
+  if (!aligned16(act) || !aligned16(w2) || !aligned16(y) || !aligned16(w2_sf)) return MOE_ERR_ALIGN;
+  const int32_t L = d->num_local_experts > 0 ? d->num_local_experts : d->num_experts;
+  return mx_fc2_enqueue(act, act_sf, w2, w2_sf, L, offs, d->T * d->top_k, d->H, d->I, y,
+                        as_stream(stream));
 }
 
 extern "C" moe_status moe_fc1(const moe_ffn_desc* d, const void* x, const void* w1,
@@ -228,6 +286,7 @@ extern "C" moe_status moe_fc1(const moe_ffn_desc* d, const void* x, const void* 
                               void* act, void* stream) {
   moe_status s = check_ffn(d);
   if (s != MOE_OK) return s;
+  if (d->weight_format != MOE_WFMT_BF16) return MOE_ERR_DTYPE;
   if (d->T == 0) return MOE_OK;
   if (!x || !w1 || !offs || !p2e || !act) return MOE_ERR_NULL;
   if (!aligned16(x) || !aligned16(w1) || !aligned16(act)) return MOE_ERR_ALIGN;
@@ -239,6 +298,7 @@ extern "C" moe_status moe_fc2(const moe_ffn_desc* d, const void* act, const void
                               void* dst, void* stream) {
   moe_status s = check_ffn(d);
   if (s != MOE_OK) return s;
+  if (d->weight_format != MOE_WFMT_BF16) return MOE_ERR_DTYPE;
   if (d->T == 0) return MOE_OK;
   if (!act || !w2 || !offs || !dst) return MOE_ERR_NULL;
   if (d->finalize_mode == MOE_FINALIZE_FUSED && (!p2e || !topk_weights)) return MOE_ERR_NULL;

@@ -1,0 +1,359 @@
+// MXFP4-weight x MXFP8-activation grouped GEMMs (FC1 with the activation and the
+// MXFP8 requantization in its epilogue, FC2 to bf16 rows) on gfx950 scaled MFMA.
+//
+// W4A8 page ("flashinfer.fused_moe.cake / cake_cute (MXFP4 SiTU routed MoE)"),
+// "Inputs": activations are float8_e4m3fn with one UE8M0 scale per 32 values
+// along H; the expert bank is MXFP4 (two e2m1 values per byte) with UE8M0
+// block-32 scales, w1 holding the up rows then the gate rows. Intro: fp32
+// accumulation and "UE8M0 round-up" requantization of the FC1 output before FC2.
+//
+// v_mfma_scale_f32_32x32x64_f8f6f4 contract (checked on the device with exact
+// small-integer operands): with the e2m1 operand in the A slot, lane l supplies
+// row l%32, k = 32*(l/32) + e as nibble e (low nibble first) of 4 VGPRs; the
+// e4m3 operand in the B slot supplies column l%32 with bytes 0..15 at
+// k = 16*(l/32) + b and bytes 16..31 at k = 32 + 16*(l/32) + (b-16); the UE8M0
+// scale of 32-block kb of a row/column comes from byte 0 of the scale VGPR of
+// lane (row + 32*kb); D uses the usual 32x32 layout.
+//
+// Tile: 256 weight rows x 256 activation rows x 128 contraction per stage, 4 waves
+// of 128 x 128 (4 x 4 accumulators), weights as the A operand so a lane holds 4
+// consecutive output columns. LDS per stage: activation codes [256][8 x 16 B],
+// weight codes [256][4 x 16 B], and both operands' 4 scale bytes per row; two
+// stages (100 KB). Tiles are dealt out as in the bf16 kernels (device-counted,
+// XCD-balanced, expert-major).
+#include "common.h"
+
+namespace moe {
+namespace {
+
+constexpr int MTB = 256;          // tile rows on each side
+constexpr int MTK = 128;          // contraction per stage
+constexpr int MNT = 256;          // threads
+constexpr int XT_U4 = MTB * MTK / 16;        // 2048 uint4: activation codes
+constexpr int WT_U4 = MTB * MTK / 2 / 16;    // 1024 uint4: weight codes
+constexpr int STAGE_U4 = XT_U4 + WT_U4 + 2 * MTB / 4;  // + 2 x 256 u32 scales
+
+enum MxEpi { MX_FC1_SWIGLU = 0, MX_FC1_STEP = 1, MX_FC2 = 2 };
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+
+struct MxArgs {
+  const uint8_t* A;        // activation codes [rows][K]
+  const uint8_t* A_sf;     // [rows][K/32]
+  const int32_t* a_gather; // optional: row p reads A row a_gather[p] / a_div
+  int a_div;
+  const uint8_t* B;        // weight codes [E][NB][K/2]
+  const uint8_t* B_sf;     // [E][NB][K/32]
+  const int32_t* ends;
+  int E, m_cap, NB, N, K, n_tiles;
+  uint16_t* C;             // FC2: bf16 rows [rows][ldc]
+  int64_t ldc;
+  uint8_t* Cq;             // FC1: e4m3 act [rows][I]
+  uint8_t* Cq_sf;          // FC1: [rows][I/32]
+  int I;
+  const float* limits;
+  float def_limit;
+};
+
+__device__ __forceinline__ int mx_clamp_end(int v, int start, int m_cap) {
+  return v < start ? start : (v > m_cap ? m_cap : v);
+}
+
+// Same tile dealing as the bf16 kernels: device-counted tiles, XCD x = b % 8 takes
+// a contiguous share, expert-major, then column tile, row block fastest.
+__device__ __forceinline__ bool mx_decode_tile(const int32_t* __restrict__ ends, int E, int m_cap,
+                                               int n_tiles, int& e, int& m0, int& mend, int& nt) {
+  int total = 0, start = 0;
+  for (int g = 0; g < E; ++g) {
+    const int end = mx_clamp_end(ends[g], start, m_cap);
+    total += (end - start + MTB - 1) / MTB;
+    start = end;
+  }
+  total *= n_tiles;
+  const int per = (total + 7) >> 3;
+  const int slot = (int)(blockIdx.x >> 3);
+  const int t = (int)(blockIdx.x & 7) * per + slot;
+  if (slot >= per || t >= total) return false;
+  int acc = 0;
+  start = 0;
+  for (int g = 0; g < E; ++g) {
+    const int end = mx_clamp_end(ends[g], start, m_cap);
+    const int te = (end - start + MTB - 1) / MTB;
+    const int cnt = te * n_tiles;
+    if (t < acc + cnt) {
+      const int r = t - acc;
+      nt = r / te;
+      e = g;
+      m0 = start + (r - nt * te) * MTB;
+      mend = end;
+      return true;
+    }
+    acc += cnt;
+    start = end;
+  }
+  return false;
+}
+
+// Round-up UE8M0 code of a block maximum: the smallest e with amax <= 448 * 2^e,
+// as e + 127. With amax = (1+f) * 2^E, 448 = 1.75 * 2^8: e = E - 8 when
+// 1+f <= 1.75, else E - 7. An all-zero block takes code 0.
+__device__ __forceinline__ uint32_t ue8m0_round_up_448(float amax) {
+  const uint32_t bits = __float_as_uint(amax);
+  const int ex = (int)((bits >> 23) & 0xFF);
+  if (amax == 0.f) return 0u;
+  int c = ex - 8 + ((bits & 0x7FFFFF) > 0x600000 ? 1 : 0);
+  c = c < 0 ? 0 : (c > 253 ? 253 : c);
+  return (uint32_t)c;
+}
+
+template <int EPI>
+__global__ __launch_bounds__(MNT, 1) void k_gemm_mx(MxArgs a) {
+  __shared__ uint4 smem[2 * STAGE_U4];
+  int e, m0, mend, nt;
+  if (!mx_decode_tile(a.ends, a.E, a.m_cap, a.n_tiles, e, m0, mend, nt)) return;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int wn = wid & 1, wm = wid >> 1;
+  const int rsel = lane & 31, g = lane >> 5;
+  const int K = a.K, ks = K >> 5;   // bytes per scale row
+  const bool fc1 = EPI != MX_FC2;
+
+  // global -> register staging: activation codes rows (tid>>3)+32j, chunk tid&7;
+  // weight codes rows (tid>>2)+64j, chunk tid&3; scales: row tid of each operand
+  const int xr = tid >> 3, xc = tid & 7, wr = tid >> 2, wc = tid & 3;
+  uint32_t xoff[8], woff[4];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    int p = m0 + xr + 32 * j;
+    p = p < mend ? p : mend - 1;
+    const int src = a.a_gather ? a.a_gather[p] / a.a_div : p;
+    xoff[j] = (uint32_t)src * (uint32_t)K + xc * 16;
+  }
+  auto wrow_of = [&](int R) {
+    if (fc1) {
+      int c = nt * 128 + (R >> 7) * 64 + (R & 63);
+      c = c < a.I ? c : a.I - 1;
+      return ((R >> 6) & 1) * a.I + c;
+    }
+    const int r = nt * MTB + R;
+    return r < a.NB ? r : a.NB - 1;
+  };
+  const uint8_t* Bb = a.B + (int64_t)e * a.NB * (K / 2);
+  const uint8_t* Bs = a.B_sf + (int64_t)e * a.NB * ks;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) woff[j] = (uint32_t)wrow_of(wr + 64 * j) * (uint32_t)(K / 2) + wc * 16;
+  uint32_t xsoff, wsoff;
+  {
+    int p = m0 + tid;
+    p = p < mend ? p : mend - 1;
+    const int src = a.a_gather ? a.a_gather[p] / a.a_div : p;
+    xsoff = (uint32_t)src * (uint32_t)ks;
+    wsoff = (uint32_t)wrow_of(tid) * (uint32_t)ks;
+  }
+  uint4 rx[8], rw[4];
+  uint32_t rxs, rws;
+  auto gload = [&](int kt) {
+    const int kb = kt * MTK;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) rx[j] = *reinterpret_cast<const uint4*>(a.A + xoff[j] + kb);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) rw[j] = *reinterpret_cast<const uint4*>(Bb + woff[j] + kb / 2);
+    rxs = *reinterpret_cast<const uint32_t*>(a.A_sf + xsoff + kb / 32);
+    rws = *reinterpret_cast<const uint32_t*>(Bs + wsoff + kb / 32);
+  };
+  auto sstore = [&](int s) {
+    uint4* X = smem + s * STAGE_U4;
+    uint4* W = X + XT_U4;
+    uint32_t* XS = reinterpret_cast<uint32_t*>(W + WT_U4);
+    uint32_t* WS = XS + MTB;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int r = xr + 32 * j;
+      X[r * 8 + (xc ^ (r & 7))] = rx[j];
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = wr + 64 * j;
+      W[r * 4 + (wc ^ ((r >> 2) & 3))] = rw[j];
+    }
+    XS[tid] = rxs;
+    WS[tid] = rws;
+  };
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  const int ktiles = K / MTK;
+  gload(0);
+  sstore(0);
+  __syncthreads();
+  for (int kt = 0; kt < ktiles; ++kt) {
+    const int s = kt & 1;
+    const bool more = kt + 1 < ktiles;
+    if (more) gload(kt + 1);
+    const uint4* X = smem + s * STAGE_U4;
+    const uint4* W = X + XT_U4;
+    const uint32_t* XS = reinterpret_cast<const uint32_t*>(W + WT_U4);
+    const uint32_t* WS = XS + MTB;
+    uint32_t wsr[4], xsr[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wsr[i] = WS[wn * 128 + i * 32 + rsel];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) xsr[j] = XS[wm * 128 + j * 32 + rsel];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      v8i wf[4], xf[4];
+      int wsc[4], xsc[4];
+      const int sh = 8 * (2 * kk + g);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = wn * 128 + i * 32 + rsel;
+        const uint4 v = W[r * 4 + ((2 * kk + g) ^ ((r >> 2) & 3))];
+        wf[i] = v8i{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+        wsc[i] = (int)((wsr[i] >> sh) & 0xFF);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = wm * 128 + j * 32 + rsel;
+        const uint4 lo = X[r * 8 + ((4 * kk + g) ^ (r & 7))];
+        const uint4 hi = X[r * 8 + ((4 * kk + 2 + g) ^ (r & 7))];
+        xf[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        xsc[j] = (int)((xsr[j] >> sh) & 0xFF);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wf[i], xf[j], acc[i][j], 4, 0, 0,
+                                                                     wsc[i], 0, xsc[j]);
+    }
+    if (more) sstore(s ^ 1);
+    __syncthreads();
+  }
+
+  const int hi4 = (lane >> 5) * 4;
+  if (fc1) {
+    float lim = 0.f;
+    if (EPI == MX_FC1_STEP) lim = a.limits ? a.limits[e] : a.def_limit;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int p = m0 + wm * 128 + j * 32 + rsel;
+      const bool row_ok = p < mend;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int col0 = nt * 128 + wn * 64 + i * 32;   // one 32-column scale block
+        float v[16];
+        float amax = 0.f;
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          float u = acc[i][j][q];
+          float gt = acc[i + 2][j][q];
+          if (EPI == MX_FC1_STEP) {
+            u = fminf(fmaxf(u, -lim), lim);
+            gt = fminf(fmaxf(gt, -lim), lim);
+          }
+          v[q] = silu_f32(gt) * u;
+          amax = fmaxf(amax, fabsf(v[q]));
+        }
+        amax = fmaxf(amax, __shfl_xor(amax, 32));
+        const uint32_t code = ue8m0_round_up_448(amax);
+        const float inv = __uint_as_float((254u - code) << 23);   // 2^(127 - code)
+        if (!row_ok || col0 >= a.I) continue;
+        uint8_t* crow = a.Cq + (int64_t)p * a.I;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          int pk = __builtin_amdgcn_cvt_pk_fp8_f32(v[4 * q] * inv, v[4 * q + 1] * inv, 0, false);
+          pk = __builtin_amdgcn_cvt_pk_fp8_f32(v[4 * q + 2] * inv, v[4 * q + 3] * inv, pk, true);
+          *reinterpret_cast<uint32_t*>(crow + col0 + q * 8 + hi4) = (uint32_t)pk;
+        }
+        if (g == 0) a.Cq_sf[(int64_t)p * (a.I >> 5) + (col0 >> 5)] = (uint8_t)code;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int p = m0 + wm * 128 + j * 32 + rsel;
+      if (p >= mend) continue;
+      uint16_t* crow = a.C + (int64_t)p * a.ldc;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int col = nt * MTB + wn * 128 + i * 32 + q * 8 + hi4;
+          if (col >= a.N) continue;
+          *reinterpret_cast<uint2*>(crow + col) =
+              make_uint2(pack_bf16x2(acc[i][j][q * 4 + 0], acc[i][j][q * 4 + 1]),
+                         pack_bf16x2(acc[i][j][q * 4 + 2], acc[i][j][q * 4 + 3]));
+        }
+    }
+  }
+}
+
+}  // namespace
+
+// FC1: act (MXFP8) = requant(activation(x[p2e[p]/k] @ w1[e].T)) for permuted rows p.
+moe_status mx_fc1_enqueue(int activation, const void* x, const void* x_sf, const int32_t* p2e,
+                          int top_k, const void* w1, const void* w1_sf, int L, const int32_t* offs,
+                          int64_t R, int H, int I, const float* limits, void* act, void* act_sf,
+                          hipStream_t st) {
+  if (R == 0) return MOE_OK;
+  MxArgs a{};
+  a.A = reinterpret_cast<const uint8_t*>(x);
+  a.A_sf = reinterpret_cast<const uint8_t*>(x_sf);
+  a.a_gather = p2e;
+  a.a_div = top_k;
+  a.B = reinterpret_cast<const uint8_t*>(w1);
+  a.B_sf = reinterpret_cast<const uint8_t*>(w1_sf);
+  a.ends = offs;
+  a.E = L;
+  a.m_cap = (int)R;
+  a.NB = 2 * I;
+  a.N = I;
+  a.K = H;
+  a.n_tiles = (I + 127) / 128;
+  a.Cq = reinterpret_cast<uint8_t*>(act);
+  a.Cq_sf = reinterpret_cast<uint8_t*>(act_sf);
+  a.I = I;
+  a.limits = limits;
+  a.def_limit = 7.0f;
+  const int64_t tiles = ((int64_t)(R / MTB) + L) * a.n_tiles;
+  const int grid = (int)((tiles + 7) / 8 * 8);
+  if (activation == MOE_ACT_SWIGLU_STEP)
+    k_gemm_mx<MX_FC1_STEP><<<grid, MNT, 0, st>>>(a);
+  else
+    k_gemm_mx<MX_FC1_SWIGLU><<<grid, MNT, 0, st>>>(a);
+  return launch_status();
+}
+
+// FC2: y[p] (bf16) = act[p] @ w2[e].T with MXFP8 act and MXFP4 w2.
+moe_status mx_fc2_enqueue(const void* act, const void* act_sf, const void* w2, const void* w2_sf,
+                          int L, const int32_t* offs, int64_t R, int H, int I, void* y,
+                          hipStream_t st) {
+  if (R == 0) return MOE_OK;
+  MxArgs a{};
+  a.A = reinterpret_cast<const uint8_t*>(act);
+  a.A_sf = reinterpret_cast<const uint8_t*>(act_sf);
+  a.a_gather = nullptr;
+  a.a_div = 1;
+  a.B = reinterpret_cast<const uint8_t*>(w2);
+  a.B_sf = reinterpret_cast<const uint8_t*>(w2_sf);
+  a.ends = offs;
+  a.E = L;
+  a.m_cap = (int)R;
+  a.NB = H;
+  a.N = H;
+  a.K = I;
+  a.n_tiles = (H + MTB - 1) / MTB;
+  a.C = reinterpret_cast<uint16_t*>(y);
+  a.ldc = H;
+  const int64_t tiles = ((int64_t)(R / MTB) + L) * a.n_tiles;
+  const int grid = (int)((tiles + 7) / 8 * 8);
+  k_gemm_mx<MX_FC2><<<grid, MNT, 0, st>>>(a);
+  return launch_status();
+}
+
+}  // namespace moe

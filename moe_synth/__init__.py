@@ -34,7 +34,8 @@ import torch
 __all__ = [
     "MoECase", "GroupedGemmCase", "moe_case", "tiny_moe", "mixtral_moe",
     "expert_shard_moe", "grouped_gemm_case", "dirichlet_group_sizes",
-    "route_logits", "bf16_to_f32", "to_bf16",
+    "route_logits", "bf16_to_f32", "to_bf16", "mx_quant_e4m3", "mx_quant_e2m1", "W4A8Case",
+    "w4a8_moe",
 ]
 
 _THREADS = max(1, min(16, os.cpu_count() or 1))
@@ -233,3 +234,103 @@ def grouped_gemm_case(seed: int = 0, E: int = 16, sum_m: int = 8192, K: int = 20
         gg = to_bf16(g.standard_normal((M, N), dtype=np.float32))
         w = _normal_bank((len(sizes), N, K), math.sqrt(1.0 / K), seed, 3)
     return GroupedGemmCase(sizes, offs, x, gg, w)
+
+
+# ---------------------------------------------------------------------------
+# MX inputs (MXFP8 activations, MXFP4 weights) with UE8M0 block-32 scales.
+# Scale exponent of a block: the smallest e with amax <= elem_max * 2^e (so the
+# scaled block fits the element format); elements rounded to nearest, ties even.
+# ---------------------------------------------------------------------------
+def _block_exponent(amax: np.ndarray, elem_max: float) -> np.ndarray:
+    """smallest integer e with amax <= elem_max * 2^e (amax > 0), checked exactly."""
+    e = np.ceil(np.log2(np.where(amax > 0, amax, 1.0) / elem_max))
+    e = np.where(amax > elem_max * np.exp2(e), e + 1, e)
+    e = np.where(amax <= elem_max * np.exp2(e - 1), e - 1, e)
+    return np.where(amax > 0, e, -127.0)
+
+
+def _block_scales(a: np.ndarray, elem_max: float, block: int):
+    *lead, K = a.shape
+    ab = a.reshape(*lead, K // block, block)
+    e = _block_exponent(np.abs(ab).max(-1).astype(np.float64), elem_max)
+    sc = np.clip(e + 127, 0, 254).astype(np.uint8)
+    # dividing by a power of two is exact in float32 for these magnitudes
+    inv = np.exp2(127.0 - sc.astype(np.float64)).astype(np.float32)
+    return ab * inv[..., None], sc
+
+
+def mx_quant_e4m3(a: np.ndarray, block: int = 32):
+    """float32 [..., K] -> (e4m3fn codes uint8 [..., K], UE8M0 scales uint8 [..., K/32])."""
+    a = np.asarray(a, dtype=np.float32)
+    scaled, sc = _block_scales(a, 448.0, block)
+    codes = torch.from_numpy(np.ascontiguousarray(scaled.reshape(a.shape))).to(
+        torch.float8_e4m3fn).view(torch.uint8).numpy()
+    return codes, sc
+
+
+def mx_quant_e2m1(a: np.ndarray, block: int = 32):
+    """float32 [..., K] -> (packed e2m1 uint8 [..., K/2] (element 2j in the low nibble),
+    UE8M0 scales uint8 [..., K/32]). Magnitudes round to the nearest of
+    {0, .5, 1, 1.5, 2, 3, 4, 6}; a value exactly between two takes the even code."""
+    a = np.asarray(a, dtype=np.float32)
+    scaled, sc = _block_scales(a, 6.0, block)
+    m = np.abs(scaled)
+    code = ((m > 0.25).astype(np.uint8) + (m >= 0.75) + (m > 1.25) + (m >= 1.75) + (m > 2.5)
+            + (m >= 3.5) + (m > 5.0)).astype(np.uint8)
+    code = np.where((scaled < 0) & (code > 0), code | 8, code).astype(np.uint8).reshape(a.shape)
+    packed = (code[..., 0::2] | (code[..., 1::2] << 4)).astype(np.uint8)
+    return packed, sc
+
+
+@dataclass
+class W4A8Case:
+    """MXFP8-activation / MXFP4-weight MoE case (numpy arrays on the host).
+
+    x, x_sf:   uint8 [T, H] e4m3fn codes, uint8 [T, H/32] UE8M0
+    w1, w1_sf: uint8 [L, 2I, H/2] packed e2m1 ([up | gate] rows), uint8 [L, 2I, H/32]
+    w2, w2_sf: uint8 [L, H, I/2], uint8 [L, H, I/32]
+    """
+    T: int
+    H: int
+    I: int
+    num_experts: int
+    top_k: int
+    logits: np.ndarray
+    x: np.ndarray
+    x_sf: np.ndarray
+    w1: np.ndarray
+    w1_sf: np.ndarray
+    w2: np.ndarray
+    w2_sf: np.ndarray
+
+    @property
+    def num_local(self) -> int:
+        return self.num_experts
+
+
+def w4a8_moe(seed: int = 0, T: int = 8192, H: int = 7168, I: int = 2048, E: int = 64,
+             top_k: int = 8, x_scale: float = 1.0) -> W4A8Case:
+    """W4A8 MoE: logits N(0,1); x N(0,1) -> MXFP8; w1 N(0,1/H), w2 N(0,1/I) -> MXFP4,
+    quantized expert by expert (draw order as in moe_case)."""
+    g = np.random.default_rng(seed)
+    logits = route_logits(g, T, E)
+    xa = g.standard_normal((T, H), dtype=np.float32)
+    if x_scale != 1.0:
+        xa *= np.float32(x_scale)
+    x, x_sf = mx_quant_e4m3(xa)
+    w1 = np.empty((E, 2 * I, H // 2), np.uint8)
+    w1_sf = np.empty((E, 2 * I, H // 32), np.uint8)
+    w2 = np.empty((E, H, I // 2), np.uint8)
+    w2_sf = np.empty((E, H, I // 32), np.uint8)
+
+    def fill(e: int) -> None:
+        a = np.random.default_rng([seed, 1, e]).standard_normal((2 * I, H), dtype=np.float32)
+        a *= np.float32(math.sqrt(1.0 / H))
+        w1[e], w1_sf[e] = mx_quant_e2m1(a)
+        b = np.random.default_rng([seed, 2, e]).standard_normal((H, I), dtype=np.float32)
+        b *= np.float32(math.sqrt(1.0 / I))
+        w2[e], w2_sf[e] = mx_quant_e2m1(b)
+
+    with ThreadPoolExecutor(max_workers=min(_THREADS, E)) as ex:
+        list(ex.map(fill, range(E)))
+    return W4A8Case(T, H, I, E, top_k, logits, x, x_sf, w1, w1_sf, w2, w2_sf)

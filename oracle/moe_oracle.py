@@ -43,7 +43,8 @@ __all__ = [
     "route", "sort_routes", "grouped_gemm_fwd", "grouped_gemm_dgrad",
     "grouped_gemm_wgrad", "silu", "activation", "moe_forward", "moe_route_outputs",
     "finalize", "e4m3_decode", "e4m3_encode", "e2m1_decode", "ue8m0_decode",
-    "mx_dequant", "requant_e4m3", "minifloat_decode",
+    "mx_dequant", "requant_e4m3", "minifloat_decode", "unpack_e2m1", "mx_dequant_fp4",
+    "mx_dequant_fp8",
 ]
 
 
@@ -361,3 +362,23 @@ def requant_e4m3(a32, block: int = 32):
     q = e4m3_encode(ab / scale_used[..., None])
     vals = e4m3_decode(q).reshape(*lead, n)
     return vals, codes_scale
+
+
+def unpack_e2m1(packed):
+    """Two e2m1 codes per byte, element 2j in the low nibble, 2j+1 in the high one
+    (W4A8 page, "Inputs": w1 [L, 2I, H/2] packs two values per byte)."""
+    p = np.asarray(packed, dtype=np.uint8)
+    out = np.empty(p.shape[:-1] + (p.shape[-1] * 2,), dtype=np.uint8)
+    out[..., 0::2] = p & 0x0F
+    out[..., 1::2] = p >> 4
+    return out
+
+
+def mx_dequant_fp4(packed, scale_codes, block: int = 32):
+    """MXFP4 -> float64: e2m1 element value times 2^(scale - 127) per block of 32."""
+    return mx_dequant(e2m1_decode(unpack_e2m1(packed)), scale_codes, block)
+
+
+def mx_dequant_fp8(codes, scale_codes, block: int = 32):
+    """MXFP8 (e4m3fn codes) -> float64 with UE8M0 block-32 scales."""
+    return mx_dequant(e4m3_decode(codes), scale_codes, block)

@@ -1,0 +1,159 @@
+"""GPU parity: the MXFP4-weight / MXFP8-activation (W4A8) layer against the oracle.
+
+The oracle works on the dequantized operands in float64 and models the one
+lossy step of the method, the MXFP8 requantization of the FC1 output
+(W4A8 page, intro: UE8M0 round-up). Tolerance for fp8 / MXFP4 outputs:
+max-abs 8e-2 (applied as |d| / max(1, |ref|)) and relative L2 3e-2.
+"""
+import numpy as np
+import pytest
+import torch
+
+import mixture_experts_expert_softmax_amd as M
+import moe_synth as S
+import oracle as O
+from parity import assert_close_bf16, to_np
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+MX_MAX_ABS, MX_REL = 8e-2, 3e-2
+
+
+class _LazyBank:
+    """Expert bank that dequantizes one expert at a time for the oracle (optionally
+    remembering the experts it has decoded)."""
+
+    def __init__(self, codes, scales, cache=None):
+        self.codes, self.scales, self.cache = codes, scales, cache
+        self.shape = (codes.shape[0], codes.shape[1], codes.shape[2] * 2)
+
+    def __getitem__(self, e):
+        if self.cache is not None and e in self.cache:
+            return self.cache[e]
+        v = O.mx_dequant_fp4(self.codes[e], self.scales[e])
+        if self.cache is not None:
+            self.cache[e] = v
+        return v
+
+
+def _dev(c):
+    return {k: torch.from_numpy(np.ascontiguousarray(getattr(c, k))).to(DEV)
+            for k in ("x", "x_sf", "w1", "w1_sf", "w2", "w2_sf")}
+
+
+def _oracle(c, ids, w, tokens=None, num_experts=None, local_offset=0, L=None,
+            activation="swiglu", limits=None, cache1=None, cache2=None):
+    ids_n, w_n = ids.cpu().numpy(), w.cpu().numpy().astype(np.float64)
+    x, xs = c.x, c.x_sf
+    if tokens is not None:
+        x, xs, ids_n, w_n = x[tokens], xs[tokens], ids_n[tokens], w_n[tokens]
+    w1, w1s, w2, w2s = c.w1, c.w1_sf, c.w2, c.w2_sf
+    if L is not None:
+        w1, w1s = w1[local_offset:local_offset + L], w1s[local_offset:local_offset + L]
+        w2, w2s = w2[local_offset:local_offset + L], w2s[local_offset:local_offset + L]
+    return O.moe_forward(O.mx_dequant_fp8(x, xs), ids_n, w_n, _LazyBank(w1, w1s, cache1),
+                         _LazyBank(w2, w2s, cache2),
+                         num_experts=num_experts or c.num_experts, local_offset=local_offset,
+                         activation_kind=activation, limits=limits, requant=True)
+
+
+def _run(c, d, ids=None, w=None, **kw):
+    if ids is None:
+        ids, w = M.moe_route(torch.from_numpy(c.logits).to(DEV), c.top_k)
+    out = M.moe_ffn_forward_mx(d["x"], d["x_sf"], ids, w, d["w1"], d["w1_sf"], d["w2"], d["w2_sf"],
+                               c.num_experts, **kw)
+    return out, ids, w
+
+
+@pytest.mark.parametrize("T", [1, 16, 77, 300])
+def test_w4a8_small_layer(T):
+    c = S.w4a8_moe(seed=T, T=T, H=256, I=384, E=8, top_k=2)
+    out, ids, w = _run(c, _dev(c))
+    assert_close_bf16(out, _oracle(c, ids, w), MX_MAX_ABS, MX_REL, what=f"w4a8 T={T}")
+
+
+def test_w4a8_top8_of_64_small_dims():
+    c = S.w4a8_moe(seed=5, T=128, H=512, I=256, E=64, top_k=8)
+    out, ids, w = _run(c, _dev(c))
+    assert_close_bf16(out, _oracle(c, ids, w), MX_MAX_ABS, MX_REL, what="w4a8 E=64 k=8")
+
+
+def test_w4a8_shard_and_step_activation():
+    c = S.w4a8_moe(seed=6, T=200, H=256, I=256, E=16, top_k=4, x_scale=4.0)
+    d = _dev(c)
+    L, off = 6, 5
+    lim = torch.tensor(np.linspace(2.0, 4.0, L), dtype=torch.float32, device=DEV)
+    ids, w = M.moe_route(torch.from_numpy(c.logits).to(DEV), c.top_k)
+    out = M.moe_ffn_forward_mx(d["x"], d["x_sf"], ids, w, d["w1"][off:off + L], d["w1_sf"][off:off + L],
+                               d["w2"][off:off + L], d["w2_sf"][off:off + L], c.num_experts,
+                               num_local_experts=L, local_expert_offset=off, activation="swiglu_step",
+                               clamp_limit=lim)
+    ref = _oracle(c, ids, w, L=L, local_offset=off, activation="swiglu_step",
+                  limits=lim.cpu().numpy())
+    assert_close_bf16(out, ref, MX_MAX_ABS, MX_REL, what="w4a8 shard step")
+
+
+def test_fc1_requant_matches_oracle_rule():
+    """The fused UE8M0 round-up requantization: scale codes equal the oracle's (rare
+    one-step flips allowed where the float32 activations differ in the last bits),
+    and the dequantized act stays within half an e4m3 step of the exact activation."""
+    c = S.w4a8_moe(seed=7, T=256, H=512, I=512, E=4, top_k=2)
+    d = _dev(c)
+    ids, w = M.moe_route(torch.from_numpy(c.logits).to(DEV), c.top_k)
+    srt = M.moe_sort(ids, c.num_experts)
+    act, act_sf = M.moe_fc1_mx(d["x"], d["x_sf"], d["w1"], d["w1_sf"], srt["offs"], srt["p2e"],
+                               c.top_k, c.num_experts)
+    n = int(srt["n_local"].item())
+    p2e = srt["p2e"][:n].cpu().numpy()
+    offs = srt["offs"].cpu().numpy()
+    xd = O.mx_dequant_fp8(c.x, c.x_sf)
+    a_ref = np.zeros((n, c.I))
+    start = 0
+    for e in range(c.num_experts):
+        rows = slice(start, int(offs[e]))
+        h = xd[p2e[rows] // c.top_k] @ O.mx_dequant_fp4(c.w1[e], c.w1_sf[e]).T
+        a_ref[rows] = O.activation(h, "swiglu")
+        start = int(offs[e])
+    vals, codes = O.requant_e4m3(a_ref.astype(np.float32))
+    got_codes = act_sf[:n].cpu().numpy()
+    assert np.mean(got_codes == codes) > 0.995
+    assert np.all(np.abs(got_codes.astype(int) - codes.astype(int)) <= 1)
+    deq = O.mx_dequant_fp8(act[:n].cpu().numpy(), got_codes)
+    scale = np.repeat(np.exp2(got_codes.astype(np.float64) - 127), 32, axis=1)
+    # half an e4m3 step (2^-4 relative, 2^-10 of the scale in the subnormal range) plus slack
+    bound = np.maximum(np.abs(a_ref) * 2.0 ** -4, scale * 2.0 ** -10) * 1.01 + 1e-6 * np.abs(a_ref)
+    assert np.mean(np.abs(deq - a_ref) <= bound) > 0.999
+
+
+def test_w4a8_zero_tokens_and_replay():
+    c = S.w4a8_moe(seed=8, T=64, H=256, I=256, E=8, top_k=2)
+    d = _dev(c)
+    o1, ids, w = _run(c, d)
+    o2, _, _ = _run(c, d, ids, w)
+    assert torch.equal(o1, o2)
+    e = torch.empty((0, 2), dtype=torch.int32, device=DEV)
+    ew = torch.empty((0, 2), dtype=torch.float32, device=DEV)
+    z = M.moe_ffn_forward_mx(d["x"][:0], d["x_sf"][:0], e, ew, d["w1"], d["w1_sf"], d["w2"],
+                             d["w2_sf"], c.num_experts)
+    assert z.shape == (0, 256)
+
+
+@pytest.fixture(scope="module")
+def w4a8_full():
+    return S.w4a8_moe(seed=0, T=8192), {}, {}
+
+
+@pytest.mark.parametrize("T", [1, 16, 128, 8192])
+def test_w4a8_full_shape_sampled(w4a8_full, T):
+    """H=7168, I=2048, 64 experts, top-8 at the decode and prefill token counts;
+    two sampled tokens are checked against the oracle."""
+    full, cache1, cache2 = w4a8_full
+    c = S.W4A8Case(T, full.H, full.I, full.num_experts, full.top_k, full.logits[:T], full.x[:T],
+                   full.x_sf[:T], full.w1, full.w1_sf, full.w2, full.w2_sf)
+    out, ids, w = _run(c, _dev(c))
+    torch.cuda.synchronize()
+    # token 0 routes identically at every T (the logits are shared), so its experts are
+    # decoded once; the largest case also checks its last token
+    tokens = np.array([0, T - 1]) if T == 8192 else np.array([0])
+    ref = _oracle(c, ids, w, tokens=tokens, cache1=cache1, cache2=cache2)
+    assert_close_bf16(to_np(out)[tokens], ref, MX_MAX_ABS, MX_REL, what=f"w4a8 full T={T}")

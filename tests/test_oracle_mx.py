@@ -92,3 +92,26 @@ def test_requant_exact_power_of_two_boundary():
     a[1, 5] = np.nextafter(np.float32(448.0 * 2.0 ** -3), np.float32(1e9))
     _, sc = O.requant_e4m3(a)
     assert sc[0, 0] == 127 - 3 and sc[1, 0] == 127 - 2
+
+
+def test_fp4_packing_golden():
+    import json
+    import os
+    with open(os.path.join(os.path.dirname(__file__), "golden", "mxfp4_packing.json")) as f:
+        fx = json.load(f)
+    b = np.array(fx["bytes"], dtype=np.uint8)
+    np.testing.assert_array_equal(O.unpack_e2m1(b), fx["codes"])
+    np.testing.assert_array_equal(O.e2m1_decode(O.unpack_e2m1(b)), fx["values"])
+    # one 32-wide block: the fixture bytes followed by zeros
+    row = np.zeros(16, np.uint8)
+    row[:4] = b
+    v = O.mx_dequant_fp4(row[None], np.array([[fx["scale_code"]]], np.uint8))[0]
+    np.testing.assert_array_equal(v[:8], fx["scaled_values"])
+    assert np.all(v[8:] == 0)
+
+
+def test_mx_dequant_fp8_scales_each_block():
+    codes = np.full((1, 64), 0x38, np.uint8)            # e4m3 1.0 everywhere
+    v = O.mx_dequant_fp8(codes, np.array([[127 + 3, 127 - 2]], np.uint8))
+    np.testing.assert_array_equal(v[0, :32], 8.0)
+    np.testing.assert_array_equal(v[0, 32:], 0.25)
