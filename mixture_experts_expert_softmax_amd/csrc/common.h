@@ -23,6 +23,9 @@ int device_cu_count();
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+// register staging type for 16-byte copies: a vector, not an aggregate, so that a
+// load kept in registers and stored later is not merged into one memory-to-memory copy
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // float -> bf16 bits, round to nearest even (inputs here are finite).
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {

@@ -149,20 +149,20 @@ __global__ __launch_bounds__(MNT, 1) void k_gemm_mx(MxArgs a) {
     xsoff = (uint32_t)src * (uint32_t)ks;
     wsoff = (uint32_t)wrow_of(tid) * (uint32_t)ks;
   }
-  uint4 rx[8], rw[4];
+  u32x4 rx[8], rw[4];
   uint32_t rxs, rws;
   auto gload = [&](int kt) {
     const int kb = kt * MTK;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) rx[j] = *reinterpret_cast<const uint4*>(a.A + xoff[j] + kb);
+    for (int j = 0; j < 8; ++j) rx[j] = *reinterpret_cast<const u32x4*>(a.A + xoff[j] + kb);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) rw[j] = *reinterpret_cast<const uint4*>(Bb + woff[j] + kb / 2);
+    for (int j = 0; j < 4; ++j) rw[j] = *reinterpret_cast<const u32x4*>(Bb + woff[j] + kb / 2);
     rxs = *reinterpret_cast<const uint32_t*>(a.A_sf + xsoff + kb / 32);
     rws = *reinterpret_cast<const uint32_t*>(Bs + wsoff + kb / 32);
   };
   auto sstore = [&](int s) {
-    uint4* X = smem + s * STAGE_U4;
-    uint4* W = X + XT_U4;
+    u32x4* X = reinterpret_cast<u32x4*>(smem + s * STAGE_U4);
+    u32x4* W = X + XT_U4;
     uint32_t* XS = reinterpret_cast<uint32_t*>(W + WT_U4);
     uint32_t* WS = XS + MTB;
 #pragma unroll
@@ -187,14 +187,15 @@ __global__ __launch_bounds__(MNT, 1) void k_gemm_mx(MxArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
+  // Branch-free main loop (the last stage re-loads itself, unused) with one issue
+  // order: the next step's fragment reads and the next stage's global loads are
+  // interleaved with the first step's MFMAs, its LDS stores with the second's.
   const int ktiles = K / MTK;
   gload(0);
   sstore(0);
   __syncthreads();
   for (int kt = 0; kt < ktiles; ++kt) {
     const int s = kt & 1;
-    const bool more = kt + 1 < ktiles;
-    if (more) gload(kt + 1);
     const uint4* X = smem + s * STAGE_U4;
     const uint4* W = X + XT_U4;
     const uint32_t* XS = reinterpret_cast<const uint32_t*>(W + WT_U4);
@@ -204,34 +205,55 @@ __global__ __launch_bounds__(MNT, 1) void k_gemm_mx(MxArgs a) {
     for (int i = 0; i < 4; ++i) wsr[i] = WS[wn * 128 + i * 32 + rsel];
 #pragma unroll
     for (int j = 0; j < 4; ++j) xsr[j] = XS[wm * 128 + j * 32 + rsel];
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      v8i wf[4], xf[4];
-      int wsc[4], xsc[4];
-      const int sh = 8 * (2 * kk + g);
+    v8i wf[2][4], xf[2][4];
+    auto rd = [&](int kk, v8i (&wq)[4], v8i (&xq)[4]) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = wn * 128 + i * 32 + rsel;
         const uint4 v = W[r * 4 + ((2 * kk + g) ^ ((r >> 2) & 3))];
-        wf[i] = v8i{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
-        wsc[i] = (int)((wsr[i] >> sh) & 0xFF);
+        wq[i] = v8i{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int r = wm * 128 + j * 32 + rsel;
         const uint4 lo = X[r * 8 + ((4 * kk + g) ^ (r & 7))];
         const uint4 hi = X[r * 8 + ((4 * kk + 2 + g) ^ (r & 7))];
-        xf[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-        xsc[j] = (int)((xsr[j] >> sh) & 0xFF);
+        xq[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
       }
+    };
+    rd(0, wf[0], xf[0]);
+    gload(kt + 1 < ktiles ? kt + 1 : kt);
+    rd(1, wf[1], xf[1]);
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int sh = 8 * (2 * kk + g);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wf[i], xf[j], acc[i][j], 4, 0, 0,
-                                                                     wsc[i], 0, xsc[j]);
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              wf[kk][i], xf[kk][j], acc[i][j], 4, 0, 0, (int)((wsr[i] >> sh) & 0xFF), 0,
+              (int)((xsr[j] >> sh) & 0xFF));
+      if (kk == 1) sstore(s ^ 1);
     }
-    if (more) sstore(s ^ 1);
+    // issue order (0x008 MFMA, 0x100 LDS read, 0x200 LDS write, 0x020 global load):
+    // the scale reads (paired into 4) and step 0's 12 fragment reads first, then
+    // step 0's 16 MFMAs with step 1's 12 fragment reads and the 14 global loads
+    // between them, then step 1's 16 MFMAs with the 13 LDS stores (the two scale
+    // words go out as one paired store)
+    __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
+    for (int r = 0; r < 12; ++r) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
+    for (int r = 0; r < 13; ++r) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
     __syncthreads();
   }
 
