@@ -44,4 +44,76 @@ __device__ __forceinline__ float silu_f32(float z) {
   return z * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
+// Tile dealing shared by the grouped kernels. Group g < E owns rows
+// [end(g - 1), end(g)) of a row-sorted operand, the ends made non-decreasing and
+// capped at m_cap (a running maximum, starting from 0). A group's rows split into
+// ceil(rows / TM) row blocks times n_tiles column tiles; tiles are numbered
+// group-major, then column tile, row block fastest, and block b takes tile
+// (b % 8) * per + b / 8 with per = ceil(total / 8), so each of the 8 XCDs works
+// through one contiguous share (and its L2 sees few experts). Each wave does the
+// bookkeeping with lane-parallel scans over 64 groups at a time: a handful of
+// vector loads instead of a chain of dependent scalar loads.
+__device__ __forceinline__ int wave_scan_max(int v, int lane) {
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int u = __shfl_up(v, d, 64);
+    if (lane >= d) v = v > u ? v : u;
+  }
+  return v;
+}
+__device__ __forceinline__ int wave_scan_add(int v, int lane) {
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int u = __shfl_up(v, d, 64);
+    if (lane >= d) v += u;
+  }
+  return v;
+}
+
+template <int TM>
+__device__ __forceinline__ bool deal_tile(const int32_t* __restrict__ ends, int E, int m_cap,
+                                          int n_tiles, int& e, int& m0, int& mend, int& nt) {
+  const int lane = threadIdx.x & 63;
+  // one pass over 64 groups from c0: clamped end, previous end and inclusive tile
+  // count of this lane's group; carries the last end and count to the next pass
+  auto pass = [&](int c0, int& ce, int& tc, int& cend, int& pend, int& incl) {
+    const int g = c0 + lane;
+    const int v = wave_scan_max(g < E ? ends[g] : 0, lane);
+    cend = v > ce ? v : ce;
+    cend = cend < m_cap ? cend : m_cap;
+    pend = __shfl_up(cend, 1, 64);
+    if (lane == 0) pend = ce;
+    const int tl = g < E ? (cend - pend + TM - 1) / TM * n_tiles : 0;
+    incl = wave_scan_add(tl, lane) + tc;
+    ce = __builtin_amdgcn_readlane(cend, 63);
+    tc = __builtin_amdgcn_readlane(incl, 63);
+  };
+  int ce = 0, tc = 0, cend, pend, incl;
+  for (int c0 = 0; c0 < E; c0 += 64) pass(c0, ce, tc, cend, pend, incl);
+  const int total = tc;
+  const int per = (total + 7) >> 3;
+  const int slot = (int)(blockIdx.x >> 3);
+  const int t = (int)(blockIdx.x & 7) * per + slot;
+  if (slot >= per || t >= total) return false;
+  ce = 0;
+  tc = 0;
+  for (int c0 = 0; c0 < E; c0 += 64) {
+    pass(c0, ce, tc, cend, pend, incl);
+    if (t < tc) {
+      const unsigned long long hit = __ballot(incl > t);
+      const int L = __ffsll(hit) - 1;
+      const int ge = __builtin_amdgcn_readlane(cend, L);
+      const int gs = __builtin_amdgcn_readlane(pend, L);
+      const int te = (ge - gs + TM - 1) / TM;
+      const int r = t - (__builtin_amdgcn_readlane(incl, L) - te * n_tiles);
+      nt = r / te;
+      e = c0 + L;
+      m0 = gs + (r - nt * te) * TM;
+      mend = ge;
+      return true;
+    }
+  }
+  return false;
+}
+
 }  // namespace moe

@@ -72,50 +72,6 @@ __device__ __forceinline__ int xcd_remap(int b, int nblocks) {
   return (b & 7) * per + (b >> 3);
 }
 
-__device__ __forceinline__ int clamp_end(int v, int start, int m_cap) {
-  return v < start ? start : (v > m_cap ? m_cap : v);
-}
-
-// Tile of this workgroup for a ragged grouped GEMM with n_tiles column tiles.
-// The grid is an upper bound (no host sync), so every workgroup first counts the
-// real tiles from the device offsets and deals exactly those out: XCD x = b % 8
-// (the hardware's round-robin placement) takes the contiguous range
-// [x*per, (x+1)*per), so no XCD is left with only the empty tail. Tiles are
-// ordered expert-major, then column tile, then row block fastest: the row blocks
-// that share one weight tile run together on one XCD and read it once from HBM.
-__device__ __forceinline__ bool decode_tile(const int32_t* __restrict__ ends, int E, int m_cap,
-                                            int n_tiles, int& e, int& m0, int& mend, int& nt) {
-  int total = 0, start = 0;
-  for (int g = 0; g < E; ++g) {
-    const int end = clamp_end(ends[g], start, m_cap);
-    total += (end - start + TB - 1) / TB;
-    start = end;
-  }
-  total *= n_tiles;
-  const int per = (total + 7) >> 3;
-  const int slot = (int)(blockIdx.x >> 3);
-  const int t = (int)(blockIdx.x & 7) * per + slot;
-  if (slot >= per || t >= total) return false;
-  int acc = 0;
-  start = 0;
-  for (int g = 0; g < E; ++g) {
-    const int end = clamp_end(ends[g], start, m_cap);
-    const int te = (end - start + TB - 1) / TB;
-    const int cnt = te * n_tiles;
-    if (t < acc + cnt) {
-      const int r = t - acc;
-      nt = r / te;
-      e = g;
-      m0 = start + (r - nt * te) * TB;
-      mend = end;
-      return true;
-    }
-    acc += cnt;
-    start = end;
-  }
-  return false;
-}
-
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 
 // One 64-deep stage of MFMAs: wave (wn, wm) multiplies its 128 weight rows by its
@@ -311,7 +267,7 @@ template <int EPI, bool KFULL>
 __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_nt(NtArgs a) {
   __shared__ uint4 smem[4 * TILE_U4];  // [stage][A tile | B tile], 128 KB
   int e, m0, mend, nt;
-  if (!decode_tile(a.ends, a.E, a.m_cap, a.n_tiles, e, m0, mend, nt)) return;
+  if (!deal_tile<TB>(a.ends, a.E, a.m_cap, a.n_tiles, e, m0, mend, nt)) return;
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int wn = wid & 1, wm = wid >> 1;
@@ -451,7 +407,7 @@ struct DgradArgs {
 __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_dgrad(DgradArgs a) {
   __shared__ uint4 smem[4 * TILE_U4];
   int e, m0, mend, nt;  // nt: tile of K (output columns)
-  if (!decode_tile(a.ends, a.E, a.m_cap, a.n_tiles, e, m0, mend, nt)) return;
+  if (!deal_tile<TB>(a.ends, a.E, a.m_cap, a.n_tiles, e, m0, mend, nt)) return;
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int wn = wid & 1, wm = wid >> 1;
@@ -622,7 +578,9 @@ inline int round_up8(int64_t v) { return (int)((v + 7) / 8 * 8); }
 }  // namespace
 
 // Upper bound on the row blocks of ragged groups: sum_e ceil(m_e/256) <= floor(M/256) + E.
-int row_block_bound(int64_t M, int E) { return (int)(M / TB) + E; }
+// Row blocks over E groups holding M rows in all: at most one partial block per
+// non-empty group, and there are at most min(E, M) of those.
+int row_block_bound(int64_t M, int E) { return (int)(M / TB + (M < E ? M : E)); }
 
 moe_status zero_fill(void* p, size_t bytes, hipStream_t st) {
   if (bytes == 0) return MOE_OK;

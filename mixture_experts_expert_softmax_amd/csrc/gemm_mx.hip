@@ -55,45 +55,6 @@ struct MxArgs {
   float def_limit;
 };
 
-__device__ __forceinline__ int mx_clamp_end(int v, int start, int m_cap) {
-  return v < start ? start : (v > m_cap ? m_cap : v);
-}
-
-// Same tile dealing as the bf16 kernels: device-counted tiles, XCD x = b % 8 takes
-// a contiguous share, expert-major, then column tile, row block fastest.
-__device__ __forceinline__ bool mx_decode_tile(const int32_t* __restrict__ ends, int E, int m_cap,
-                                               int n_tiles, int& e, int& m0, int& mend, int& nt) {
-  int total = 0, start = 0;
-  for (int g = 0; g < E; ++g) {
-    const int end = mx_clamp_end(ends[g], start, m_cap);
-    total += (end - start + MTB - 1) / MTB;
-    start = end;
-  }
-  total *= n_tiles;
-  const int per = (total + 7) >> 3;
-  const int slot = (int)(blockIdx.x >> 3);
-  const int t = (int)(blockIdx.x & 7) * per + slot;
-  if (slot >= per || t >= total) return false;
-  int acc = 0;
-  start = 0;
-  for (int g = 0; g < E; ++g) {
-    const int end = mx_clamp_end(ends[g], start, m_cap);
-    const int te = (end - start + MTB - 1) / MTB;
-    const int cnt = te * n_tiles;
-    if (t < acc + cnt) {
-      const int r = t - acc;
-      nt = r / te;
-      e = g;
-      m0 = start + (r - nt * te) * MTB;
-      mend = end;
-      return true;
-    }
-    acc += cnt;
-    start = end;
-  }
-  return false;
-}
-
 // Round-up UE8M0 code of a block maximum: the smallest e with amax <= 448 * 2^e,
 // as e + 127. With amax = (1+f) * 2^E, 448 = 1.75 * 2^8: e = E - 8 when
 // 1+f <= 1.75, else E - 7. An all-zero block takes code 0.
@@ -110,7 +71,7 @@ template <int EPI>
 __global__ __launch_bounds__(MNT, 1) void k_gemm_mx(MxArgs a) {
   __shared__ uint4 smem[2 * STAGE_U4];
   int e, m0, mend, nt;
-  if (!mx_decode_tile(a.ends, a.E, a.m_cap, a.n_tiles, e, m0, mend, nt)) return;
+  if (!deal_tile<MTB>(a.ends, a.E, a.m_cap, a.n_tiles, e, m0, mend, nt)) return;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int wn = wid & 1, wm = wid >> 1;
   const int rsel = lane & 31, g = lane >> 5;
@@ -315,6 +276,231 @@ __global__ __launch_bounds__(MNT, 1) void k_gemm_mx(MxArgs a) {
   }
 }
 
+// Few rows per expert (decode): the cost is streaming the expert bank once. Tile:
+// 32 activation rows (one MFMA column block) by 64 weight rows (FC1: 32 up rows and
+// the 32 gate rows of the same output columns, i.e. one requantization block; FC2:
+// 64 output columns); the 4 waves split the contraction and meet in LDS at the end.
+// A wave streams its 64 rows x (its share of K) in stages of 4 steps of 64 values
+// (128 bytes per row): each load instruction takes 8 whole 128-byte lines (lane l:
+// row 8j + l / 8, 16-byte chunk l % 8). Weight stages are loaded two ahead into
+// registers and pass through a private LDS slot that turns them into MFMA fragments
+// (chunks swizzled by row & 7; one slot is enough because a wave's LDS operations
+// run in order). The weight scales of the wave's range are read into LDS once at the
+// start; the activation fragments come straight from global memory, one stage ahead
+// (for decode most tile rows repeat the same token, so those loads are cheap). Two
+// blocks share a CU.
+constexpr int STB = 32;         // activation rows per tile
+constexpr int SCW = 16;         // weight-scale dwords kept per row and wave
+constexpr int SMAX_STAGES = 8;  // stages per wave that they cover (2 dwords each)
+
+struct MxAct {
+  u32x4 xl[4], xh[4];
+  uint32_t sx[4];
+};
+struct MxW {
+  u32x4 v[8];
+};
+
+template <int EPI>
+__global__ __launch_bounds__(256, 2) void k_gemm_mx_stream(MxArgs a) {
+  __shared__ u32x4 ring[4][512];              // [wave][64 rows x 8 chunks]
+  __shared__ uint32_t scl[4][64][SCW];        // [wave][tile row][scale dwords]
+  int e, m0, mend, nt;
+  if (!deal_tile<STB>(a.ends, a.E, a.m_cap, a.n_tiles, e, m0, mend, nt)) return;
+  constexpr bool fc1 = EPI != MX_FC2;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r = lane & 31, g = lane >> 5;
+  const int K = a.K, ks = K >> 5;
+  const uint32_t kh = (uint32_t)(K >> 1);
+  // weight row (within the expert) of tile row R in [0, 64)
+  auto wrow_of = [&](int R) -> int {
+    if (fc1) return (R >> 5) * a.I + min(nt * 32 + (R & 31), a.I - 1);
+    return min(nt * 64 + R, a.NB - 1);
+  };
+  const int64_t eb = (int64_t)e * a.NB;
+  const uint8_t* Bw = a.B + eb * kh;
+  const uint8_t* Bs = a.B_sf + eb * ks;
+  // stages of 4 steps of 64 values (K is a multiple of 256); wave w takes stages
+  // [s0, s0 + nst)
+  const int nstg = K >> 8;
+  const int s0 = wid * nstg / 4;
+  const int nst = (wid + 1) * nstg / 4 - s0;
+
+  // weight scales of this wave's stages: 8 bytes per stage and row, from byte 8 * s0
+  uint32_t sreg[SCW];
+  {
+    const uint32_t* srow =
+        reinterpret_cast<const uint32_t*>(Bs + (int64_t)wrow_of(lane) * ks + 8 * s0);
+#pragma unroll
+    for (int d = 0; d < SCW; ++d) sreg[d] = d < 2 * nst ? srow[d] : 0u;
+  }
+
+  // 32-bit per-lane offsets from stage-uniform bases. Weights: instruction j loads
+  // tile row 8j + lane / 8, chunk (lane % 8) ^ (row & 7), and stores it to LDS chunk
+  // lane % 8 of that row.
+  uint32_t voff[8];
+  const int csw = (lane & 7) ^ ((lane >> 3) & 7);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) voff[j] = (uint32_t)wrow_of(8 * j + (lane >> 3)) * kh + 16u * csw;
+  int p = m0 + r;
+  p = p < mend ? p : mend - 1;
+  const int src = a.a_gather ? a.a_gather[p] / a.a_div : p;
+  const uint32_t xoff = (uint32_t)src * (uint32_t)K + 16u * g;
+  const uint32_t xsoff = (uint32_t)src * (uint32_t)ks + g;
+
+  // loads of stage q (clamped to the last stage: the extra copies are never used)
+  auto issue_w = [&](int q, MxW& w) {
+    const uint8_t* base = Bw + 128 * (s0 + min(q, nst - 1));
+#pragma unroll
+    for (int j = 0; j < 8; ++j) w.v[j] = *reinterpret_cast<const u32x4*>(base + voff[j]);
+  };
+  auto issue_a = [&](int q, MxAct& act) {
+    const int st = s0 + min(q, nst - 1);
+    const uint8_t* xb = a.A + 256 * st;
+    const uint8_t* sbp = a.A_sf + 8 * st;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      act.xl[s] = *reinterpret_cast<const u32x4*>(xb + xoff + 64 * s);
+      act.xh[s] = *reinterpret_cast<const u32x4*>(xb + xoff + 64 * s + 32);
+      act.sx[s] = sbp[xsoff + 2 * s];
+    }
+  };
+  auto stash = [&](const MxW& w) {
+    u32x4* dst = &ring[wid][0];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) dst[64 * j + lane] = w.v[j];
+  };
+  f32x16 acc0, acc1;
+#pragma unroll
+  for (int q = 0; q < 16; ++q) acc0[q] = acc1[q] = 0.f;
+  const uint8_t* sc0 = reinterpret_cast<const uint8_t*>(&scl[wid][r][0]);
+  const uint8_t* sc1 = reinterpret_cast<const uint8_t*>(&scl[wid][32 + r][0]);
+  auto compute = [&](int q, const MxAct& act) {
+    const u32x4* W = &ring[wid][0];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int c = (2 * s + g) ^ (r & 7);
+      const u32x4 w0 = W[r * 8 + c];
+      const u32x4 w1 = W[(32 + r) * 8 + c];
+      const int bi = 8 * q + 2 * s + g;
+      const v8i f0{(int)w0.x, (int)w0.y, (int)w0.z, (int)w0.w, 0, 0, 0, 0};
+      const v8i f1{(int)w1.x, (int)w1.y, (int)w1.z, (int)w1.w, 0, 0, 0, 0};
+      const v8i x{(int)act.xl[s].x, (int)act.xl[s].y, (int)act.xl[s].z, (int)act.xl[s].w,
+                  (int)act.xh[s].x, (int)act.xh[s].y, (int)act.xh[s].z, (int)act.xh[s].w};
+      acc0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f0, x, acc0, 4, 0, 0, (int)sc0[bi], 0,
+                                                             (int)act.sx[s]);
+      acc1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f1, x, acc1, 4, 0, 0, (int)sc1[bi], 0,
+                                                             (int)act.sx[s]);
+    }
+  };
+
+  if (nst > 0) {
+    // issue order W(0) A(0) W(1), then per stage q: W(q + 2) A(q + 1); stage q's
+    // MFMAs wait for A(q), by which time W(q + 1) is in too and goes to LDS after them
+    MxW W0, W1;
+    MxAct A0, A1;
+    issue_w(0, W0);
+    issue_a(0, A0);
+    issue_w(1, W1);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int d = 0; d < SCW; ++d) scl[wid][lane][d] = sreg[d];
+    stash(W0);
+    // (the scheduling barriers keep the compiler from sinking loads to their uses)
+    for (int q = 0; q < nst; q += 2) {
+      issue_w(q + 2, W0);
+      issue_a(q + 1, A1);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(q, A0);
+      if (q + 1 >= nst) break;
+      stash(W1);
+      issue_w(q + 3, W1);
+      issue_a(q + 2, A0);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(q + 1, A1);
+      if (q + 2 >= nst) break;
+      stash(W0);
+    }
+  }
+  __syncthreads();
+  float* red = reinterpret_cast<float*>(&ring[0][0]);   // [3][2][16][64]
+  if (wid > 0) {
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      red[(((wid - 1) * 2 + 0) * 16 + q) * 64 + lane] = acc0[q];
+      red[(((wid - 1) * 2 + 1) * 16 + q) * 64 + lane] = acc1[q];
+    }
+  }
+  __syncthreads();
+  if (wid != 0) return;
+#pragma unroll
+  for (int w = 0; w < 3; ++w)
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      acc0[q] += red[((w * 2 + 0) * 16 + q) * 64 + lane];
+      acc1[q] += red[((w * 2 + 1) * 16 + q) * 64 + lane];
+    }
+
+  // D layout: register q of lane l holds token m0 + l % 32 and output column
+  // 8 * (q / 4) + 4 * (l / 32) + q % 4 of its 32-column group
+  const int hi4 = g * 4;
+  const int prow = m0 + r;
+  if (fc1) {
+    float lim = 0.f;
+    if (EPI == MX_FC1_STEP) lim = a.limits ? a.limits[e] : a.def_limit;
+    float v[16];
+    float amax = 0.f;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      float u = acc0[q], gt = acc1[q];
+      if (EPI == MX_FC1_STEP) {
+        u = fminf(fmaxf(u, -lim), lim);
+        gt = fminf(fmaxf(gt, -lim), lim);
+      }
+      v[q] = silu_f32(gt) * u;
+      amax = fmaxf(amax, fabsf(v[q]));
+    }
+    amax = fmaxf(amax, __shfl_xor(amax, 32));
+    const uint32_t code = ue8m0_round_up_448(amax);
+    const float inv = __uint_as_float((254u - code) << 23);
+    if (prow >= mend) return;
+    uint8_t* crow = a.Cq + (int64_t)prow * a.I + nt * 32;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      int pk = __builtin_amdgcn_cvt_pk_fp8_f32(v[4 * q] * inv, v[4 * q + 1] * inv, 0, false);
+      pk = __builtin_amdgcn_cvt_pk_fp8_f32(v[4 * q + 2] * inv, v[4 * q + 3] * inv, pk, true);
+      *reinterpret_cast<uint32_t*>(crow + q * 8 + hi4) = (uint32_t)pk;
+    }
+    if (g == 0) a.Cq_sf[(int64_t)prow * (a.I >> 5) + nt] = (uint8_t)code;
+  } else {
+    if (prow >= mend) return;
+    uint16_t* crow = a.C + (int64_t)prow * a.ldc;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int col = nt * 64 + i * 32 + q * 8 + hi4;
+        if (col >= a.N) continue;
+        const f32x16& ac = i ? acc1 : acc0;
+        *reinterpret_cast<uint2*>(crow + col) =
+            make_uint2(pack_bf16x2(ac[q * 4 + 0], ac[q * 4 + 1]),
+                       pack_bf16x2(ac[q * 4 + 2], ac[q * 4 + 3]));
+      }
+  }
+}
+
+// The decode kernel takes over while the experts hold few rows on average: there the
+// 256-row tiles would be mostly padding and too few to fill the chip.
+inline bool mx_use_small(int64_t R, int L, int K, int NB, int64_t act_rows) {
+  return R <= 64LL * L && K % 256 == 0 && (K >> 8) <= 4 * SMAX_STAGES &&
+         (int64_t)NB * (K >> 1) < (1LL << 31) && act_rows * K < (1LL << 31);
+}
+
+// Row tiles of tm rows over L experts holding R rows in all: at most one partial
+// tile per non-empty expert, and there are at most min(L, R) of those.
+inline int64_t mx_row_tiles(int64_t R, int L, int tm) { return R / tm + (R < L ? R : L); }
+
 }  // namespace
 
 // FC1: act (MXFP8) = requant(activation(x[p2e[p]/k] @ w1[e].T)) for permuted rows p.
@@ -336,13 +522,23 @@ moe_status mx_fc1_enqueue(int activation, const void* x, const void* x_sf, const
   a.NB = 2 * I;
   a.N = I;
   a.K = H;
-  a.n_tiles = (I + 127) / 128;
   a.Cq = reinterpret_cast<uint8_t*>(act);
   a.Cq_sf = reinterpret_cast<uint8_t*>(act_sf);
   a.I = I;
   a.limits = limits;
   a.def_limit = 7.0f;
-  const int64_t tiles = ((int64_t)(R / MTB) + L) * a.n_tiles;
+  if (mx_use_small(R, L, H, 2 * I, R)) {
+    a.n_tiles = I / 32;
+    const int64_t tiles = mx_row_tiles(R, L, STB) * a.n_tiles;
+    const int grid = (int)((tiles + 7) / 8 * 8);
+    if (activation == MOE_ACT_SWIGLU_STEP)
+      k_gemm_mx_stream<MX_FC1_STEP><<<grid, 256, 0, st>>>(a);
+    else
+      k_gemm_mx_stream<MX_FC1_SWIGLU><<<grid, 256, 0, st>>>(a);
+    return launch_status();
+  }
+  a.n_tiles = (I + 127) / 128;
+  const int64_t tiles = mx_row_tiles(R, L, MTB) * a.n_tiles;
   const int grid = (int)((tiles + 7) / 8 * 8);
   if (activation == MOE_ACT_SWIGLU_STEP)
     k_gemm_mx<MX_FC1_STEP><<<grid, MNT, 0, st>>>(a);
@@ -369,10 +565,17 @@ moe_status mx_fc2_enqueue(const void* act, const void* act_sf, const void* w2, c
   a.NB = H;
   a.N = H;
   a.K = I;
-  a.n_tiles = (H + MTB - 1) / MTB;
   a.C = reinterpret_cast<uint16_t*>(y);
   a.ldc = H;
-  const int64_t tiles = ((int64_t)(R / MTB) + L) * a.n_tiles;
+  if (mx_use_small(R, L, I, H, R)) {
+    a.n_tiles = (H + 63) / 64;
+    const int64_t tiles = mx_row_tiles(R, L, STB) * a.n_tiles;
+    const int grid = (int)((tiles + 7) / 8 * 8);
+    k_gemm_mx_stream<MX_FC2><<<grid, 256, 0, st>>>(a);
+    return launch_status();
+  }
+  a.n_tiles = (H + MTB - 1) / MTB;
+  const int64_t tiles = mx_row_tiles(R, L, MTB) * a.n_tiles;
   const int grid = (int)((tiles + 7) / 8 * 8);
   k_gemm_mx<MX_FC2><<<grid, MNT, 0, st>>>(a);
   return launch_status();

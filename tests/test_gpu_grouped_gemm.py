@@ -17,6 +17,8 @@ DEV = "cuda"
 SMALL_SIZES = [
     [300, 0, 1, 257, 64, 513],       # spans several 256-row tiles, empty and 1-row groups
     [1], [0, 0, 5], [256, 256], [17, 90, 255, 1],
+    # 150 groups, many empty: the tile dealing scans 64 groups at a time (3 passes)
+    [int(v) for v in np.random.default_rng(7).integers(0, 12, 150) * (np.arange(150) % 3 > 0)],
 ]
 
 

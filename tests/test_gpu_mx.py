@@ -78,8 +78,18 @@ def test_w4a8_top8_of_64_small_dims():
     assert_close_bf16(out, _oracle(c, ids, w), MX_MAX_ABS, MX_REL, what="w4a8 E=64 k=8")
 
 
-def test_w4a8_shard_and_step_activation():
-    c = S.w4a8_moe(seed=6, T=200, H=256, I=256, E=16, top_k=4, x_scale=4.0)
+def test_w4a8_decode_uneven_contraction_split():
+    """H=1280 and I=768: 5 and 3 stages of 256 contraction values, split unevenly
+    over the decode kernel's 4 waves (one wave of FC2 gets none)."""
+    c = S.w4a8_moe(seed=9, T=5, H=1280, I=768, E=16, top_k=4)
+    out, ids, w = _run(c, _dev(c))
+    assert_close_bf16(out, _oracle(c, ids, w), MX_MAX_ABS, MX_REL, what="w4a8 uneven split")
+
+
+# T=200 runs the 256-row tile kernel, T=12 the decode kernel (few rows per expert)
+@pytest.mark.parametrize("T", [200, 12])
+def test_w4a8_shard_and_step_activation(T):
+    c = S.w4a8_moe(seed=6, T=T, H=256, I=256, E=16, top_k=4, x_scale=4.0)
     d = _dev(c)
     L, off = 6, 5
     lim = torch.tensor(np.linspace(2.0, 4.0, L), dtype=torch.float32, device=DEV)
@@ -93,11 +103,13 @@ def test_w4a8_shard_and_step_activation():
     assert_close_bf16(out, ref, MX_MAX_ABS, MX_REL, what="w4a8 shard step")
 
 
-def test_fc1_requant_matches_oracle_rule():
+@pytest.mark.parametrize("T", [256, 24])
+def test_fc1_requant_matches_oracle_rule(T):
     """The fused UE8M0 round-up requantization: scale codes equal the oracle's (rare
     one-step flips allowed where the float32 activations differ in the last bits),
-    and the dequantized act stays within half an e4m3 step of the exact activation."""
-    c = S.w4a8_moe(seed=7, T=256, H=512, I=512, E=4, top_k=2)
+    and the dequantized act stays within half an e4m3 step of the exact activation.
+    T=256 runs the 256-row tile kernel, T=24 the decode kernel."""
+    c = S.w4a8_moe(seed=7, T=T, H=512, I=512, E=4, top_k=2)
     d = _dev(c)
     ids, w = M.moe_route(torch.from_numpy(c.logits).to(DEV), c.top_k)
     srt = M.moe_sort(ids, c.num_experts)
