@@ -146,6 +146,8 @@ def main():
     out_fused = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
     lib = M.lib()
     P = M._ptr
+    # the GEMM stages' split-tile workspace (the layer call keeps one in its own workspace)
+    split_ws = torch.empty(lib.moe_gemm_split_workspace_size(), dtype=torch.uint8, device=dev)
 
     def route():
         M._check("moe_route", lib.moe_route(P(logits), T, E, k, P(ids), P(wts), M._stream()))
@@ -155,13 +157,14 @@ def main():
                                           P(sort_ws), sort_ws.numel(), M._stream()))
 
     def fc1():
-        M.moe_fc1(x, w1, offs, p2e, k, E, act=act)
+        M.moe_fc1(x, w1, offs, p2e, k, E, act=act, workspace=split_ws)
 
     def fc2(fused=False):
         if fused:
-            M.moe_fc2(act, w2, offs, T, k, E, finalize="fused", p2e=p2e, topk_weights=wts, dst=out_fused)
+            M.moe_fc2(act, w2, offs, T, k, E, finalize="fused", p2e=p2e, topk_weights=wts, dst=out_fused,
+                      workspace=split_ws)
         else:
-            M.moe_fc2(act, w2, offs, T, k, E, dst=y)
+            M.moe_fc2(act, w2, offs, T, k, E, dst=y, workspace=split_ws)
 
     def finalize():
         M.moe_finalize(y, e2p, wts, out=out)

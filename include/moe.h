@@ -201,13 +201,22 @@ moe_status moe_ffn_forward(const moe_ffn_desc* desc, const moe_ffn_tensors* tens
  *          the unscaled rows to `dst` = y [T*top_k, H] bf16. FUSED zero-fills
  *          `dst` = out [T, H] bf16 and adds topk_weights[p2e[p]] * y[p] into row
  *          p2e[p] / top_k with bf16 atomics (not bitwise reproducible for top_k > 2).
+ *
+ * ws / ws_bytes (optional, NULL / 0 allowed): at least
+ * moe_gemm_split_workspace_size() bytes, 16-byte aligned, owned by the caller and
+ * not shared by calls that may overlap. With it, the tiles of a last, mostly idle
+ * round of workgroups are cut along the contraction and their fp32 partials summed
+ * in a fixed order (same result on every run; rounding differs from the unsplit
+ * order within fp32). Without it no tile is cut. moe_ffn_forward does this with
+ * its own workspace. MOE_ERR_WORKSPACE if ws is given but too small or unaligned.
  */
+size_t moe_gemm_split_workspace_size(void);
 moe_status moe_fc1(const moe_ffn_desc* desc, const void* x, const void* w1,
                    const float* clamp_limit, const int32_t* offs, const int32_t* p2e, void* act,
-                   void* stream);
+                   void* ws, size_t ws_bytes, void* stream);
 moe_status moe_fc2(const moe_ffn_desc* desc, const void* act, const void* w2,
                    const int32_t* offs, const int32_t* p2e, const float* topk_weights, void* dst,
-                   void* stream);
+                   void* ws, size_t ws_bytes, void* stream);
 
 /*
  * The MXFP4 (W4A8) stages ([W4A8] "Inputs"; intro: fp32 accumulation, UE8M0

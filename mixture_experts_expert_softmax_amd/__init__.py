@@ -66,8 +66,9 @@ EXPORTS = {
     "moe_ffn_workspace_size": (_sz, [ctypes.POINTER(MoeFfnDesc)]),
     "moe_ffn_forward": (_i32, [ctypes.POINTER(MoeFfnDesc), ctypes.POINTER(MoeFfnTensors), _vp, _sz, _vp]),
     "moe_finalize": (_i32, [_vp, _vp, _vp, _i64, _i32, _i32, _vp, _vp]),
-    "moe_fc1": (_i32, [ctypes.POINTER(MoeFfnDesc), _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
-    "moe_fc2": (_i32, [ctypes.POINTER(MoeFfnDesc), _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "moe_gemm_split_workspace_size": (_sz, []),
+    "moe_fc1": (_i32, [ctypes.POINTER(MoeFfnDesc), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "moe_fc2": (_i32, [ctypes.POINTER(MoeFfnDesc), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "moe_fc1_mx": (_i32, [ctypes.POINTER(MoeFfnDesc), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "moe_fc2_mx": (_i32, [ctypes.POINTER(MoeFfnDesc), _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
 }
@@ -273,10 +274,23 @@ def moe_ffn_forward(x: torch.Tensor, topk_ids: torch.Tensor, topk_weights: torch
     return out
 
 
+def _split_ws(split: bool, workspace: Optional[torch.Tensor], device):
+    """(pointer, bytes) of the split-tile workspace of moe_fc1 / moe_fc2, or (None, 0)."""
+    if not split:
+        return None, 0
+    if workspace is None:
+        workspace = torch.empty(lib().moe_gemm_split_workspace_size(), dtype=torch.uint8,
+                                device=device)
+    return workspace, workspace.numel() * workspace.element_size()
+
+
 def moe_fc1(x: torch.Tensor, w1: torch.Tensor, offs: torch.Tensor, p2e: torch.Tensor, top_k: int,
             num_experts: int, local_expert_offset: int = 0, activation: str = "swiglu",
-            clamp_limit: Optional[torch.Tensor] = None, act: Optional[torch.Tensor] = None):
-    """act[p] = activation(x[p2e[p] // top_k] @ w1[e].T) for the expert-sorted rows p."""
+            clamp_limit: Optional[torch.Tensor] = None, act: Optional[torch.Tensor] = None,
+            split: bool = True, workspace: Optional[torch.Tensor] = None):
+    """act[p] = activation(x[p2e[p] // top_k] @ w1[e].T) for the expert-sorted rows p.
+    split: let a mostly idle last round of tiles be cut along K (workspace: optional
+    moe_gemm_split_workspace_size() bytes, allocated here if None)."""
     _dev(x, torch.bfloat16, "x"), _dev(w1, torch.bfloat16, "w1")
     T, H = x.shape
     L, twoI, _ = w1.shape
@@ -284,25 +298,28 @@ def moe_fc1(x: torch.Tensor, w1: torch.Tensor, offs: torch.Tensor, p2e: torch.Te
     d = _ffn_desc(T, H, I, num_experts, L, local_expert_offset, top_k, activation, "deterministic")
     if act is None:
         act = torch.empty((max(T * top_k, 1), I), dtype=torch.bfloat16, device=x.device)
+    ws, ws_bytes = _split_ws(split, workspace, x.device)
     _check("moe_fc1", lib().moe_fc1(ctypes.byref(d), _ptr(x), _ptr(w1), _ptr(clamp_limit), _ptr(offs),
-                                    _ptr(p2e), _ptr(act), _stream()))
+                                    _ptr(p2e), _ptr(act), _ptr(ws), ws_bytes, _stream()))
     return act
 
 
 def moe_fc2(act: torch.Tensor, w2: torch.Tensor, offs: torch.Tensor, T: int, top_k: int,
             num_experts: int, local_expert_offset: int = 0, finalize: str = "deterministic",
             p2e: Optional[torch.Tensor] = None, topk_weights: Optional[torch.Tensor] = None,
-            dst: Optional[torch.Tensor] = None):
+            dst: Optional[torch.Tensor] = None, split: bool = True,
+            workspace: Optional[torch.Tensor] = None):
     """y[p] = act[p] @ w2[e].T (rows [T*k, H]); with finalize="fused" the scaled rows are
-    added into a zeroed out [T, H] instead."""
+    added into a zeroed out [T, H] instead. split / workspace as for moe_fc1."""
     _dev(act, torch.bfloat16, "act"), _dev(w2, torch.bfloat16, "w2")
     L, H, I = w2.shape
     d = _ffn_desc(T, H, I, num_experts, L, local_expert_offset, top_k, "swiglu", finalize)
     if dst is None:
         rows = T if finalize == "fused" else max(T * top_k, 1)
         dst = torch.empty((rows, H), dtype=torch.bfloat16, device=act.device)
+    ws, ws_bytes = _split_ws(split, workspace, act.device)
     _check("moe_fc2", lib().moe_fc2(ctypes.byref(d), _ptr(act), _ptr(w2), _ptr(offs), _ptr(p2e),
-                                    _ptr(topk_weights), _ptr(dst), _stream()))
+                                    _ptr(topk_weights), _ptr(dst), _ptr(ws), ws_bytes, _stream()))
     return dst
 
 

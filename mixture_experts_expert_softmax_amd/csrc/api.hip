@@ -9,14 +9,16 @@ namespace moe {
 size_t sort_workspace_bytes(int64_t T, int32_t k, int32_t L);
 moe_status sort_enqueue(const int32_t* ids, int64_t T, int32_t k, int32_t E, int32_t L,
                         int32_t off, int32_t* offs, int32_t* m_indptr, int32_t* e2p,
-                        int32_t* p2e, int32_t* n_local, void* ws, hipStream_t st);
+                        int32_t* p2e, int32_t* n_local, void* ws, hipStream_t st,
+                        int32_t* zero = nullptr, int n_zero = 0);
 moe_status finalize_enqueue(const void* y, const int32_t* e2p, const float* w, int64_t T, int k,
                             int H, void* out, hipStream_t st);
 moe_status gemm_nt_enqueue(int epi, const void* A, const int32_t* a_gather, int a_div,
                            const void* B, int NB, int E, const int32_t* ends, int64_t M, int N,
                            int K, void* C, int64_t ldc, int I, const float* limits,
                            float def_limit, const float* route_w, const int32_t* p2e, int top_k,
-                           hipStream_t st);
+                           hipStream_t st, void* split_ws = nullptr,
+                           int32_t* split_cnt = nullptr);
 moe_status gemm_dgrad_enqueue(const void* G, const void* W, const int32_t* ends, int E, int64_t M,
                               int N, int K, void* DX, hipStream_t st);
 moe_status gemm_wgrad_enqueue(const void* G, const void* X, const int32_t* ends, int E, int64_t M,
@@ -66,7 +68,7 @@ moe_status check_gemm(const void* p0, const void* p1, const int32_t* offs, int32
 }
 
 struct FfnLayout {
-  size_t sort_ws, offs, e2p, p2e, n_local, act, act_sf, y, total;
+  size_t sort_ws, offs, e2p, p2e, n_local, act, act_sf, y, split, split_cnt, total;
 };
 
 FfnLayout ffn_layout(const moe_ffn_desc* d) {
@@ -85,6 +87,11 @@ FfnLayout ffn_layout(const moe_ffn_desc* d) {
   l.act_sf = o;  o += mx ? align_up((size_t)R * (d->I / 32), 256) : 0;
   l.y = o;
   if (d->finalize_mode == MOE_FINALIZE_DETERMINISTIC) o += align_up((size_t)R * d->H * 2, 256);
+  // bf16 FC1 / FC2 may cut their last round's tiles along K (fp32 partial tiles)
+  l.split = o;
+  if (!mx) o += (size_t)SPLIT_SLOTS * SPLIT_TILE_BYTES;
+  l.split_cnt = o;
+  if (!mx) o += align_up((size_t)SPLIT_SLOTS * 4, 256);
   l.total = o;
   return l;
 }
@@ -173,28 +180,30 @@ static moe_status check_ffn(const moe_ffn_desc* d) {
 // FC1 over gathered token rows; the activation runs in the GEMM epilogue.
 static moe_status fc1_enqueue(const moe_ffn_desc* d, const void* x, const void* w1,
                               const float* limits, const int32_t* offs, const int32_t* p2e,
-                              void* act, hipStream_t st) {
+                              void* act, hipStream_t st, void* split_ws = nullptr,
+                              int32_t* split_cnt = nullptr) {
   const int32_t L = d->num_local_experts > 0 ? d->num_local_experts : d->num_experts;
   const int64_t R = d->T * d->top_k;
   const int epi = d->activation == MOE_ACT_SWIGLU_STEP ? EPI_SWIGLU_STEP : EPI_SWIGLU;
   return gemm_nt_enqueue(epi, x, p2e, d->top_k, w1, 2 * d->I, L, offs, R, d->I, d->H, act, d->I,
-                         d->I, limits, 7.0f, nullptr, nullptr, d->top_k, st);
+                         d->I, limits, 7.0f, nullptr, nullptr, d->top_k, st, split_ws, split_cnt);
 }
 
 // FC2: unscaled rows in permuted order, or the fused scaled scatter-add into out.
 static moe_status fc2_enqueue(const moe_ffn_desc* d, const void* act, const void* w2,
                               const int32_t* offs, const int32_t* p2e, const float* topk_weights,
-                              void* dst, hipStream_t st) {
+                              void* dst, hipStream_t st, void* split_ws = nullptr,
+                              int32_t* split_cnt = nullptr) {
   const int32_t L = d->num_local_experts > 0 ? d->num_local_experts : d->num_experts;
   const int64_t R = d->T * d->top_k;
   if (d->finalize_mode == MOE_FINALIZE_FUSED) {
     moe_status s = zero_fill(dst, (size_t)d->T * d->H * 2, st);
     if (s != MOE_OK) return s;
     return gemm_nt_enqueue(EPI_FUSED, act, nullptr, 1, w2, d->H, L, offs, R, d->H, d->I, dst, d->H,
-                           0, nullptr, 0.f, topk_weights, p2e, d->top_k, st);
+                           0, nullptr, 0.f, topk_weights, p2e, d->top_k, st, split_ws, split_cnt);
   }
   return gemm_nt_enqueue(EPI_STORE, act, nullptr, 1, w2, d->H, L, offs, R, d->H, d->I, dst, d->H, 0,
-                         nullptr, 0.f, nullptr, nullptr, d->top_k, st);
+                         nullptr, 0.f, nullptr, nullptr, d->top_k, st, split_ws, split_cnt);
 }
 
 extern "C" size_t moe_ffn_workspace_size(const moe_ffn_desc* d) {
@@ -232,8 +241,11 @@ extern "C" moe_status moe_ffn_forward(const moe_ffn_desc* d, const moe_ffn_tenso
   void* y = fm == MOE_FINALIZE_NONE ? t->y : w + l.y;
   const int H = d->H;
 
+  int32_t* split_cnt = mx ? nullptr : reinterpret_cast<int32_t*>(w + l.split_cnt);
+  void* split_ws = mx ? nullptr : w + l.split;
+  // the sort also clears the split-tile arrival counters
   s = sort_enqueue(t->topk_ids, d->T, d->top_k, d->num_experts, L, d->local_expert_offset, offs,
-                   nullptr, e2p, p2e, nloc, w + l.sort_ws, st);
+                   nullptr, e2p, p2e, nloc, w + l.sort_ws, st, split_cnt, mx ? 0 : SPLIT_SLOTS);
   if (s != MOE_OK) return s;
   if (mx) {
     const int64_t R = d->T * d->top_k;
@@ -242,10 +254,10 @@ extern "C" moe_status moe_ffn_forward(const moe_ffn_desc* d, const moe_ffn_tenso
     if (s != MOE_OK) return s;
     s = mx_fc2_enqueue(act, w + l.act_sf, t->w2, t->w2_sf, L, offs, R, H, d->I, y, st);
   } else {
-    s = fc1_enqueue(d, t->x, t->w1, t->clamp_limit, offs, p2e, act, st);
+    s = fc1_enqueue(d, t->x, t->w1, t->clamp_limit, offs, p2e, act, st, split_ws, split_cnt);
     if (s != MOE_OK) return s;
     s = fc2_enqueue(d, act, t->w2, offs, p2e, t->topk_weights, fm == MOE_FINALIZE_FUSED ? t->out : y,
-                    st);
+                    st, split_ws, split_cnt);
   }
   if (s != MOE_OK || fm != MOE_FINALIZE_DETERMINISTIC) return s;
   return finalize_enqueue(y, e2p, t->topk_weights, d->T, d->top_k, H, t->out, st);
@@ -281,21 +293,43 @@ extern "C" moe_status moe_fc2_mx(const moe_ffn_desc* d, const void* act, const v
                         as_stream(stream));
 }
 
+// Split-tile workspace of the standalone GEMM stages: partial tiles, then the
+// arrival counters, which each call clears first.
+constexpr size_t SPLIT_CNT_OFF = (size_t)SPLIT_SLOTS * SPLIT_TILE_BYTES;
+constexpr size_t SPLIT_WS_BYTES = SPLIT_CNT_OFF + (size_t)SPLIT_SLOTS * 4;
+
+extern "C" size_t moe_gemm_split_workspace_size(void) { return SPLIT_WS_BYTES; }
+
+static moe_status split_args(void* ws, size_t ws_bytes, hipStream_t st, void*& split_ws,
+                             int32_t*& split_cnt) {
+  split_ws = nullptr;
+  split_cnt = nullptr;
+  if (!ws) return MOE_OK;
+  if (ws_bytes < SPLIT_WS_BYTES || !aligned16(ws)) return MOE_ERR_WORKSPACE;
+  split_ws = ws;
+  split_cnt = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(ws) + SPLIT_CNT_OFF);
+  return zero_fill(split_cnt, (size_t)SPLIT_SLOTS * 4, st);
+}
+
 extern "C" moe_status moe_fc1(const moe_ffn_desc* d, const void* x, const void* w1,
                               const float* clamp_limit, const int32_t* offs, const int32_t* p2e,
-                              void* act, void* stream) {
+                              void* act, void* ws, size_t ws_bytes, void* stream) {
   moe_status s = check_ffn(d);
   if (s != MOE_OK) return s;
   if (d->weight_format != MOE_WFMT_BF16) return MOE_ERR_DTYPE;
   if (d->T == 0) return MOE_OK;
   if (!x || !w1 || !offs || !p2e || !act) return MOE_ERR_NULL;
   if (!aligned16(x) || !aligned16(w1) || !aligned16(act)) return MOE_ERR_ALIGN;
-  return fc1_enqueue(d, x, w1, clamp_limit, offs, p2e, act, as_stream(stream));
+  void* split_ws;
+  int32_t* split_cnt;
+  s = split_args(ws, ws_bytes, as_stream(stream), split_ws, split_cnt);
+  if (s != MOE_OK) return s;
+  return fc1_enqueue(d, x, w1, clamp_limit, offs, p2e, act, as_stream(stream), split_ws, split_cnt);
 }
 
 extern "C" moe_status moe_fc2(const moe_ffn_desc* d, const void* act, const void* w2,
                               const int32_t* offs, const int32_t* p2e, const float* topk_weights,
-                              void* dst, void* stream) {
+                              void* dst, void* ws, size_t ws_bytes, void* stream) {
   moe_status s = check_ffn(d);
   if (s != MOE_OK) return s;
   if (d->weight_format != MOE_WFMT_BF16) return MOE_ERR_DTYPE;
@@ -303,5 +337,10 @@ extern "C" moe_status moe_fc2(const moe_ffn_desc* d, const void* act, const void
   if (!act || !w2 || !offs || !dst) return MOE_ERR_NULL;
   if (d->finalize_mode == MOE_FINALIZE_FUSED && (!p2e || !topk_weights)) return MOE_ERR_NULL;
   if (!aligned16(act) || !aligned16(w2) || !aligned16(dst)) return MOE_ERR_ALIGN;
-  return fc2_enqueue(d, act, w2, offs, p2e, topk_weights, dst, as_stream(stream));
+  void* split_ws;
+  int32_t* split_cnt;
+  s = split_args(ws, ws_bytes, as_stream(stream), split_ws, split_cnt);
+  if (s != MOE_OK) return s;
+  return fc2_enqueue(d, act, w2, offs, p2e, topk_weights, dst, as_stream(stream), split_ws,
+                     split_cnt);
 }

@@ -19,6 +19,11 @@ inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 // Number of compute units of the current device (cached per device id).
 int device_cu_count();
 
+// Split-K tiles of the bf16 grouped kernels: at most SPLIT_SLOTS fp32 partial
+// 256 x 256 tiles in flight, plus one arrival counter per remainder tile.
+constexpr int SPLIT_SLOTS = 256;
+constexpr size_t SPLIT_TILE_BYTES = 256 * 256 * 4;
+
 // ------------------------------------------------------------------ device side
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -70,35 +75,43 @@ __device__ __forceinline__ int wave_scan_add(int v, int lane) {
   return v;
 }
 
+// One pass of the scan over 64 groups from c0: this lane's group's clamped end,
+// previous end and inclusive tile count; carries the last end (ce) and count (tc).
 template <int TM>
-__device__ __forceinline__ bool deal_tile(const int32_t* __restrict__ ends, int E, int m_cap,
-                                          int n_tiles, int& e, int& m0, int& mend, int& nt) {
+__device__ __forceinline__ void tile_scan_pass(const int32_t* __restrict__ ends, int E, int m_cap,
+                                               int n_tiles, int c0, int lane, int& ce, int& tc,
+                                               int& cend, int& pend, int& incl) {
+  const int g = c0 + lane;
+  const int v = wave_scan_max(g < E ? ends[g] : 0, lane);
+  cend = v > ce ? v : ce;
+  cend = cend < m_cap ? cend : m_cap;
+  pend = __shfl_up(cend, 1, 64);
+  if (lane == 0) pend = ce;
+  const int tl = g < E ? (cend - pend + TM - 1) / TM * n_tiles : 0;
+  incl = wave_scan_add(tl, lane) + tc;
+  ce = __builtin_amdgcn_readlane(cend, 63);
+  tc = __builtin_amdgcn_readlane(incl, 63);
+}
+
+template <int TM>
+__device__ __forceinline__ int tile_count(const int32_t* __restrict__ ends, int E, int m_cap,
+                                          int n_tiles) {
   const int lane = threadIdx.x & 63;
-  // one pass over 64 groups from c0: clamped end, previous end and inclusive tile
-  // count of this lane's group; carries the last end and count to the next pass
-  auto pass = [&](int c0, int& ce, int& tc, int& cend, int& pend, int& incl) {
-    const int g = c0 + lane;
-    const int v = wave_scan_max(g < E ? ends[g] : 0, lane);
-    cend = v > ce ? v : ce;
-    cend = cend < m_cap ? cend : m_cap;
-    pend = __shfl_up(cend, 1, 64);
-    if (lane == 0) pend = ce;
-    const int tl = g < E ? (cend - pend + TM - 1) / TM * n_tiles : 0;
-    incl = wave_scan_add(tl, lane) + tc;
-    ce = __builtin_amdgcn_readlane(cend, 63);
-    tc = __builtin_amdgcn_readlane(incl, 63);
-  };
   int ce = 0, tc = 0, cend, pend, incl;
-  for (int c0 = 0; c0 < E; c0 += 64) pass(c0, ce, tc, cend, pend, incl);
-  const int total = tc;
-  const int per = (total + 7) >> 3;
-  const int slot = (int)(blockIdx.x >> 3);
-  const int t = (int)(blockIdx.x & 7) * per + slot;
-  if (slot >= per || t >= total) return false;
-  ce = 0;
-  tc = 0;
+  for (int c0 = 0; c0 < E; c0 += 64)
+    tile_scan_pass<TM>(ends, E, m_cap, n_tiles, c0, lane, ce, tc, cend, pend, incl);
+  return tc;
+}
+
+// (group, first row, group end, column tile) of tile t < tile_count
+template <int TM>
+__device__ __forceinline__ void tile_locate(const int32_t* __restrict__ ends, int E, int m_cap,
+                                            int n_tiles, int t, int& e, int& m0, int& mend,
+                                            int& nt) {
+  const int lane = threadIdx.x & 63;
+  int ce = 0, tc = 0, cend, pend, incl;
   for (int c0 = 0; c0 < E; c0 += 64) {
-    pass(c0, ce, tc, cend, pend, incl);
+    tile_scan_pass<TM>(ends, E, m_cap, n_tiles, c0, lane, ce, tc, cend, pend, incl);
     if (t < tc) {
       const unsigned long long hit = __ballot(incl > t);
       const int L = __ffsll(hit) - 1;
@@ -110,10 +123,21 @@ __device__ __forceinline__ bool deal_tile(const int32_t* __restrict__ ends, int 
       e = c0 + L;
       m0 = gs + (r - nt * te) * TM;
       mend = ge;
-      return true;
+      return;
     }
   }
-  return false;
+}
+
+template <int TM>
+__device__ __forceinline__ bool deal_tile(const int32_t* __restrict__ ends, int E, int m_cap,
+                                          int n_tiles, int& e, int& m0, int& mend, int& nt) {
+  const int total = tile_count<TM>(ends, E, m_cap, n_tiles);
+  const int per = (total + 7) >> 3;
+  const int slot = (int)(blockIdx.x >> 3);
+  const int t = (int)(blockIdx.x & 7) * per + slot;
+  if (slot >= per || t >= total) return false;
+  tile_locate<TM>(ends, E, m_cap, n_tiles, t, e, m0, mend, nt);
+  return true;
 }
 
 }  // namespace moe

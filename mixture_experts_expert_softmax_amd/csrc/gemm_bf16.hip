@@ -41,6 +41,7 @@ constexpr int NTHREADS = 256;  // 4 waves
 constexpr int TILE_U4 = TB * TK * 2 / 16;  // uint4 slots per operand tile (2048)
 
 enum Epi { EPI_STORE = 0, EPI_SWIGLU = 1, EPI_SWIGLU_STEP = 2, EPI_FUSED = 3 };
+constexpr int SPLIT_MAX = 8;   // parts a split tile is cut into at most
 
 struct NtArgs {
   const uint16_t* A;         // activation rows, row stride K
@@ -64,6 +65,9 @@ struct NtArgs {
   const float* route_w;      // fused finalize: topk weights [T*k]
   const int32_t* p2e;        // fused finalize: route of permuted row
   int top_k;
+  float* split_ws;           // split tiles: fp32 partial tiles [SPLIT_SLOTS][TB * TB]
+  int32_t* split_cnt;        // split tiles: arrival counters, 0 between launches
+  int n_res;                 // workgroups resident at once (0: never split)
 };
 
 __device__ __forceinline__ int xcd_remap(int b, int nblocks) {
@@ -73,6 +77,55 @@ __device__ __forceinline__ int xcd_remap(int b, int nblocks) {
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// Tile (and contraction range) of this workgroup in the NT kernel. With n_res
+// resident workgroups, total tiles take total / n_res full rounds; when the
+// remainder rem would leave most of the last round idle, each of those rem tiles
+// is cut along K into S = min(n_res / rem, SPLIT_MAX) parts instead, which run
+// side by side. The whole tiles are dealt as in deal_tile; part p of remainder
+// tile i is workgroup full + 8 * ((i / 8) * S + p) + i % 8, so all parts of a
+// tile share one XCD. slot = i * S + p indexes the partial-tile buffer, cidx = i
+// the arrival counter.
+__device__ __forceinline__ bool deal_tile_nt(const NtArgs& a, int ktiles, int& e, int& m0,
+                                             int& mend, int& nt, int& k0, int& nk, int& part,
+                                             int& S, int& slot, int& cidx) {
+  const int total = tile_count<TB>(a.ends, a.E, a.m_cap, a.n_tiles);
+  const int b = (int)blockIdx.x;
+  int full = total, rem = 0;
+  S = 1;
+  part = 0;
+  if (a.n_res > 0) {
+    full = total / a.n_res * a.n_res;
+    rem = total - full;
+    if (rem > 0) {
+      S = a.n_res / rem;
+      S = S < SPLIT_MAX ? S : SPLIT_MAX;
+      S = S < ktiles ? S : ktiles;
+    }
+  }
+  int t;
+  if (S < 2) {
+    S = 1;
+    const int per = (total + 7) >> 3;
+    t = (b & 7) * per + (b >> 3);
+    if ((b >> 3) >= per || t >= total) return false;
+  } else if (b < full) {
+    t = (b & 7) * (full >> 3) + (b >> 3);
+    S = 1;  // a whole tile
+  } else {
+    const int u = b - full, w = u >> 3;
+    const int i = (w / S) * 8 + (u & 7);
+    if (i >= rem) return false;
+    part = w % S;
+    t = full + i;
+    slot = i * S + part;
+    cidx = i;
+  }
+  tile_locate<TB>(a.ends, a.E, a.m_cap, a.n_tiles, t, e, m0, mend, nt);
+  k0 = ktiles * part / S;
+  nk = ktiles * (part + 1) / S - k0;
+  return true;
+}
 
 // One 64-deep stage of MFMAs: wave (wn, wm) multiplies its 128 weight rows by its
 // 128 activation rows.
@@ -179,15 +232,16 @@ __device__ __forceinline__ void atomic_add_bf16x2(uint16_t* p, float a, float b)
 // only stalls on its own waits, so keeping LDS latency behind MFMA issue is what
 // keeps the matrix cores fed. The final stage re-loads itself (unused) so that
 // the body needs no condition.
-__device__ __forceinline__ void mainloop_full(RowLoader& la, RowLoader& lb, uint4* smem, int ktiles,
-                                              int tid, int lane, int wn, int wm, f32x16 (&acc)[4][4]) {
+__device__ __forceinline__ void mainloop_full(RowLoader& la, RowLoader& lb, uint4* smem, int kbase,
+                                              int ktiles, int tid, int lane, int wn, int wm,
+                                              f32x16 (&acc)[4][4]) {
   const int lrow = tid >> 3;
   const int pc = la.ch ^ (lrow & 7);
   const int rsel = lane & 31, kg = lane >> 5, sw = lane & 7;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    la.r[j] = *reinterpret_cast<const uint4*>(la.base + la.off[j] + la.ch * 8);
-    lb.r[j] = *reinterpret_cast<const uint4*>(lb.base + lb.off[j] + lb.ch * 8);
+    la.r[j] = *reinterpret_cast<const uint4*>(la.base + la.off[j] + kbase + la.ch * 8);
+    lb.r[j] = *reinterpret_cast<const uint4*>(lb.base + lb.off[j] + kbase + lb.ch * 8);
   }
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
@@ -197,7 +251,7 @@ __device__ __forceinline__ void mainloop_full(RowLoader& la, RowLoader& lb, uint
   __syncthreads();
   for (int kt = 0; kt < ktiles; ++kt) {
     const int s = kt & 1;
-    const int kn = (kt + 1 < ktiles ? kt + 1 : kt) * TK + la.ch * 8;
+    const int kn = kbase + (kt + 1 < ktiles ? kt + 1 : kt) * TK + la.ch * 8;
     const uint4* Xs = smem + s * 2 * TILE_U4;
     const uint4* Ws = Xs + TILE_U4;
     uint4* Xn = smem + (s ^ 1) * 2 * TILE_U4;
@@ -266,8 +320,13 @@ __device__ __forceinline__ void mainloop_full(RowLoader& la, RowLoader& lb, uint
 template <int EPI, bool KFULL>
 __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_nt(NtArgs a) {
   __shared__ uint4 smem[4 * TILE_U4];  // [stage][A tile | B tile], 128 KB
-  int e, m0, mend, nt;
-  if (!deal_tile<TB>(a.ends, a.E, a.m_cap, a.n_tiles, e, m0, mend, nt)) return;
+  const int ktiles = (a.K + TK - 1) / TK;
+  int e, m0, mend, nt, k0 = 0, nk = ktiles, part = 0, S = 1, slot = 0, cidx = 0;
+  if (KFULL) {
+    if (!deal_tile_nt(a, ktiles, e, m0, mend, nt, k0, nk, part, S, slot, cidx)) return;
+  } else {
+    if (!deal_tile<TB>(a.ends, a.E, a.m_cap, a.n_tiles, e, m0, mend, nt)) return;
+  }
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int wn = wid & 1, wm = wid >> 1;
@@ -301,10 +360,56 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_nt(NtArgs a) {
 
   f32x16 acc[4][4];
   zero_acc(acc);
-  const int ktiles = (a.K + TK - 1) / TK;
 
   if (KFULL) {
-    mainloop_full(la, lb, smem, ktiles, tid, lane, wn, wm, acc);
+    mainloop_full(la, lb, smem, k0 * TK, nk, tid, lane, wn, wm, acc);
+    if (S > 1) {
+      // a part of a split tile: publish the fp32 partial; the last of the S parts
+      // to arrive sums all of them in part order (the same result whichever part
+      // arrives last) and goes on to the epilogue
+      constexpr int TILE_F4 = TB * TB / 4;
+      float4* mine = reinterpret_cast<float4*>(a.split_ws) + (size_t)slot * TILE_F4;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            mine[((i * 4 + j) * 4 + q) * NTHREADS + tid] =
+                make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                            acc[i][j][4 * q + 3]);
+      __syncthreads();
+      int* flag = reinterpret_cast<int*>(smem);
+      if (tid == 0) {
+        const int old = __hip_atomic_fetch_add(a.split_cnt + cidx, 1, __ATOMIC_ACQ_REL,
+                                               __HIP_MEMORY_SCOPE_AGENT);
+        flag[0] = old == S - 1;
+        if (old == S - 1) a.split_cnt[cidx] = 0;  // ready for the next launch
+      }
+      __syncthreads();
+      if (!flag[0]) return;
+      const float4* first = reinterpret_cast<const float4*>(a.split_ws) + (size_t)(slot - part) * TILE_F4;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int idx = ((i * 4 + j) * 4 + q) * NTHREADS + tid;
+            float4 v = first[idx];
+            for (int p = 1; p < S; ++p) {
+              const float4 w = first[(size_t)p * TILE_F4 + idx];
+              v.x += w.x;
+              v.y += w.y;
+              v.z += w.z;
+              v.w += w.w;
+            }
+            acc[i][j][4 * q] = v.x;
+            acc[i][j][4 * q + 1] = v.y;
+            acc[i][j][4 * q + 2] = v.z;
+            acc[i][j][4 * q + 3] = v.w;
+          }
+    }
   } else {
     la.load(0);
     lb.load(0);
@@ -595,7 +700,7 @@ moe_status gemm_nt_enqueue(int epi, const void* A, const int32_t* a_gather, int 
                            const void* B, int NB, int E, const int32_t* ends, int64_t M, int N,
                            int K, void* C, int64_t ldc, int I, const float* limits,
                            float def_limit, const float* route_w, const int32_t* p2e, int top_k,
-                           hipStream_t st) {
+                           hipStream_t st, void* split_ws, int32_t* split_cnt) {
   if (M == 0) return MOE_OK;
   NtArgs a;
   a.A = reinterpret_cast<const uint16_t*>(A);
@@ -620,9 +725,17 @@ moe_status gemm_nt_enqueue(int epi, const void* A, const int32_t* a_gather, int 
   a.route_w = route_w;
   a.p2e = p2e;
   a.top_k = top_k;
-  const int64_t tiles = (int64_t)a.m_tiles * a.n_tiles;
-  const int grid = round_up8(tiles);
   const bool kfull = (K % TK) == 0;
+  a.split_ws = reinterpret_cast<float*>(split_ws);
+  a.split_cnt = split_cnt;
+  a.n_res = 0;
+  if (split_ws && split_cnt && kfull) {
+    const int cu = device_cu_count();
+    a.n_res = (cu < SPLIT_SLOTS ? cu : SPLIT_SLOTS) & ~7;  // one 128 KB-LDS workgroup per CU
+  }
+  const int64_t tiles = (int64_t)a.m_tiles * a.n_tiles;
+  // parts of split tiles take at most n_res + 8 * SPLIT_MAX workgroups past the whole ones
+  const int grid = round_up8(tiles + (a.n_res > 0 ? a.n_res + 8 * SPLIT_MAX : 0));
 #define MOE_LAUNCH_NT(E_)                                              \
   (kfull ? k_gemm_nt<E_, true><<<grid, NTHREADS, 0, st>>>(a)           \
          : k_gemm_nt<E_, false><<<grid, NTHREADS, 0, st>>>(a))

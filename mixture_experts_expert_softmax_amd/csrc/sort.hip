@@ -60,9 +60,12 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
 }
 
 __global__ __launch_bounds__(256) void k_sort_scan(int32_t* __restrict__ cnt, int nb,
-                                                   int32_t* __restrict__ total) {
+                                                   int32_t* __restrict__ total,
+                                                   int32_t* __restrict__ zero, int n_zero) {
   __shared__ int wsum[4];
   const int e = blockIdx.x;
+  if (e == 0)  // a buffer the caller wants cleared before the GEMMs (no extra launch)
+    for (int i = threadIdx.x; i < n_zero; i += 256) zero[i] = 0;
   int32_t* col = cnt + (int64_t)e * nb;
   const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
   int carry = 0;
@@ -163,7 +166,8 @@ size_t sort_workspace_bytes(int64_t T, int32_t k, int32_t L) {
 
 moe_status sort_enqueue(const int32_t* ids, int64_t T, int32_t k, int32_t E, int32_t L,
                         int32_t off, int32_t* offs, int32_t* m_indptr, int32_t* e2p,
-                        int32_t* p2e, int32_t* n_local, void* ws, hipStream_t st) {
+                        int32_t* p2e, int32_t* n_local, void* ws, hipStream_t st, int32_t* zero,
+                        int n_zero) {
   const int64_t n = T * (int64_t)k;
   if (n == 0) {
     k_sort_empty<<<1, 256, 0, st>>>(L, offs, m_indptr, n_local);
@@ -174,7 +178,7 @@ moe_status sort_enqueue(const int32_t* ids, int64_t T, int32_t k, int32_t E, int
   int32_t* total = cnt + L * nb;
   const size_t lds = (size_t)L * sizeof(int32_t);
   k_sort_count<<<(unsigned)nb, 64, lds, st>>>(ids, n, E, L, off, (int)nb, cnt);
-  k_sort_scan<<<(unsigned)L, 256, 0, st>>>(cnt, (int)nb, total);
+  k_sort_scan<<<(unsigned)L, 256, 0, st>>>(cnt, (int)nb, total, zero, zero ? n_zero : 0);
   k_sort_scatter<<<(unsigned)nb, 64, lds, st>>>(ids, n, E, L, off, (int)nb, cnt, total, offs,
                                                 m_indptr, n_local, e2p, p2e);
   return launch_status();
@@ -200,5 +204,5 @@ extern "C" moe_status moe_sort(const int32_t* topk_ids, int64_t T, int32_t top_k
   if (T * (int64_t)top_k > (int64_t)INT32_MAX) return MOE_ERR_SHAPE;
   if (T > 0 && (!ws || ws_bytes < sort_workspace_bytes(T, top_k, L))) return MOE_ERR_WORKSPACE;
   return sort_enqueue(topk_ids, T, top_k, E, L, off, offs, m_indptr, e2p, p2e, n_local, ws,
-                      as_stream(stream));
+                      as_stream(stream), nullptr, 0);
 }

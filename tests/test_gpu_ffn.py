@@ -125,6 +125,30 @@ def test_mixtral_full_size_sampled(mixtral, finalize):
     assert_close_bf16(to_np(out)[tokens], ref, what=f"mixtral {finalize}")
 
 
+def test_mixtral_split_tiles_replay_and_match_unsplit(mixtral):
+    """At the Mixtral shape FC2 has 576 tiles of 256 x 256 for 256 CUs: the layer cuts
+    the last round's tiles along K and the last part to arrive sums the fp32 partials
+    in part order. y replays bitwise, matches the standalone FC1 / FC2 entries without
+    a split workspace (no tile cut) within the bf16 tolerance, and equals them bit for
+    bit with one."""
+    c = mixtral
+    ids, w = M.moe_route(torch.from_numpy(c.logits).to(DEV), c.top_k)
+    x, w1, w2 = c.x.to(DEV), c.w1.to(DEV), c.w2.to(DEV)
+    (y1, e2p), _, _ = _run(c, "none", ids, w)
+    (y2, _), _, _ = _run(c, "none", ids, w)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
+    srt = M.moe_sort(ids, c.num_experts)
+    n = int(srt["n_local"].item())
+    act = M.moe_fc1(x, w1, srt["offs"], srt["p2e"], c.top_k, c.num_experts, split=False)
+    y3 = M.moe_fc2(act, w2, srt["offs"], c.T, c.top_k, c.num_experts, split=False)
+    assert_close_bf16(to_np(y1[:n]), to_np(y3[:n]), what="split vs unsplit FC2 rows")
+    # the standalone entries with their split workspace give the layer's rows exactly
+    act4 = M.moe_fc1(x, w1, srt["offs"], srt["p2e"], c.top_k, c.num_experts)
+    y4 = M.moe_fc2(act4, w2, srt["offs"], c.T, c.top_k, c.num_experts)
+    assert torch.equal(y1[:n], y4[:n])
+
+
 # ------------------------------------------------------------------ finalize
 def test_finalize_parity_one_hot_and_replay():
     g = np.random.default_rng(0)
