@@ -8,8 +8,9 @@
 // Two kernels:
 //  * k_route_thread<EMAX>: one thread per token, the token's logits in registers
 //    (num_experts <= EMAX <= 32). Each thread reads one contiguous row.
-//  * k_route_wave<Q>: one wave64 per token, lane j holds experts j, j+64, ...
-//    (num_experts <= 64*Q); each of the k rounds is a wave arg-max by DPP/shuffle.
+//  * k_route_wave<Q>: one wave64 per token, lane l holds experts Q*l .. Q*l+Q-1
+//    (num_experts <= 64*Q) as keys sorted in the lane; each of the k rounds is a
+//    DPP wave maximum over the lanes' head values.
 #include "common.h"
 
 namespace moe {
@@ -65,6 +66,46 @@ __global__ __launch_bounds__(256) void k_route_thread(const float* __restrict__ 
   write_weights(sel, ids, k, ids_out + t * k, w_out + t * k);
 }
 
+// Selection key of (logit v, expert id): the float's bits made order-preserving as
+// an unsigned integer (with -0 folded onto +0), then the inverted id, so that the
+// larger key is the larger logit and, on a tie, the lower id. Key 0 is below every
+// real key and stands for "no expert".
+__device__ __forceinline__ uint64_t route_key(float v, int id) {
+  const uint32_t b = __float_as_uint(v + 0.0f);  // -0 + 0 = +0
+  const uint32_t o = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  return ((uint64_t)o << 32) | (uint32_t)~id;
+}
+__device__ __forceinline__ float key_value(uint64_t key) {
+  const uint32_t o = (uint32_t)(key >> 32);
+  return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
+}
+__device__ __forceinline__ int key_id(uint64_t key) { return (int)~(uint32_t)key; }
+
+// Wave maximum of a 32-bit unsigned value, returned to every lane (uniform):
+// rotations by 1, 2, 4, 8 inside each row of 16 lanes, then the GFX9 row
+// broadcasts 15 and 31 carry the row maxima up to lane 63, which is read back.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint32_t dpp_umax(uint32_t v) {
+  const uint32_t o = ROW_MASK == 0xF
+                         ? (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, true)
+                         : (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, ROW_MASK, 0xF, false);
+  return o > v ? o : v;
+}
+__device__ __forceinline__ uint32_t wave_umax(uint32_t v) {
+  v = dpp_umax<0x121, 0xF>(v);  // row_ror:1
+  v = dpp_umax<0x122, 0xF>(v);  // row_ror:2
+  v = dpp_umax<0x124, 0xF>(v);  // row_ror:4
+  v = dpp_umax<0x128, 0xF>(v);  // row_ror:8
+  v = dpp_umax<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+  v = dpp_umax<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+// One wave64 per token; lane l holds experts Q*l .. Q*l + Q - 1 (one vector load
+// when the row is whole) as selection keys, sorted in the lane once. Each of the
+// k rounds takes the wave maximum of the lanes' head keys by their high (value)
+// word; among the lanes whose head has that value the lowest one holds the lowest
+// id, its head is the winner, and that lane alone advances to its next key.
 template <int Q>
 __global__ __launch_bounds__(256) void k_route_wave(const float* __restrict__ logits, int64_t T,
                                                     int E, int k, int32_t* __restrict__ ids_out,
@@ -74,38 +115,56 @@ __global__ __launch_bounds__(256) void k_route_wave(const float* __restrict__ lo
   if (t >= T) return;  // uniform per wave
   const float* row = logits + t * E;
   float v[Q];
+  const int j0 = Q * lane;
+  if (E == 64 * Q && (Q == 1 || Q == 2 || Q % 4 == 0)) {
+    if (Q == 1) {
+      v[0] = row[j0];
+    } else if (Q == 2) {
+      const float2 p = *reinterpret_cast<const float2*>(row + j0);
+      v[0] = p.x;
+      v[1] = p.y;
+    } else {
 #pragma unroll
-  for (int q = 0; q < Q; ++q) {
-    int j = lane + 64 * q;
-    v[q] = (j < E) ? row[j] : -INFINITY;
+      for (int q = 0; q < Q; q += 4) {
+        const float4 p = *reinterpret_cast<const float4*>(row + j0 + q);
+        v[q] = p.x;
+        v[q + 1] = p.y;
+        v[q + 2] = p.z;
+        v[q + 3] = p.w;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < Q; ++q) v[q] = j0 + q < E ? row[j0 + q] : 0.f;
   }
-  uint32_t taken = 0;  // bit q: expert lane+64q already chosen
+  uint64_t key[Q];
+#pragma unroll
+  for (int q = 0; q < Q; ++q) key[q] = j0 + q < E ? route_key(v[q], j0 + q) : 0ull;
+  // descending in-lane sort (odd-even transposition; Q is small)
+#pragma unroll
+  for (int r = 0; r < Q; ++r)
+#pragma unroll
+    for (int q = r & 1; q + 1 < Q; q += 2) {
+      const uint64_t a = key[q], b = key[q + 1];
+      key[q] = a > b ? a : b;
+      key[q + 1] = a > b ? b : a;
+    }
   float sel[16];
   int ids[16];
   for (int s = 0; s < k; ++s) {
-    float bv = -INFINITY;
-    int bid = 0x7fffffff;
+    const uint32_t head = (uint32_t)(key[0] >> 32);
+    const uint32_t m = wave_umax(head);
+    const unsigned long long hit = __ballot(head == m);
+    const int L = __ffsll(hit) - 1;
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)key[0], L);
+    const uint64_t win = ((uint64_t)m << 32) | lo;
+    if (lane == L) {
 #pragma unroll
-    for (int q = 0; q < Q; ++q) {
-      int j = lane + 64 * q;
-      if (j < E && !((taken >> q) & 1u) && better(v[q], j, bv, bid)) {
-        bv = v[q];
-        bid = j;
-      }
+      for (int q = 0; q + 1 < Q; ++q) key[q] = key[q + 1];
+      key[Q - 1] = 0ull;
     }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      float ov = __shfl_xor(bv, off);
-      int oid = __shfl_xor(bid, off);
-      if (better(ov, oid, bv, bid)) {
-        bv = ov;
-        bid = oid;
-      }
-    }
-    // every lane now holds the winner; its owner marks it taken
-    if ((bid & 63) == lane) taken |= 1u << (bid >> 6);
-    sel[s] = bv;
-    ids[s] = bid;
+    sel[s] = key_value(win);
+    ids[s] = key_id(win);
   }
   if (lane == 0) write_weights(sel, ids, k, ids_out + t * k, w_out + t * k);
 }

@@ -7,7 +7,9 @@
 // SM90 fused-MoE page, Parameters: the EP shard holds num_local_experts experts
 // from global id local_expert_offset; other routes contribute nothing.
 //
-// Three launches over chunks of CHUNK routes (one wave64 per chunk):
+// Up to 65536 routes (and per-wave histograms that fit in 64 KB of LDS): one
+// workgroup does it all (k_sort_block). Beyond that, three launches over chunks
+// of CHUNK routes (one wave64 per chunk):
 //  1. k_sort_count:   per-chunk histogram of local experts -> cnt[e][chunk]
 //  2. k_sort_scan:    one block per expert: exclusive scan of cnt[e][*] over
 //                     chunks (in place) and the expert total
@@ -83,6 +85,92 @@ __global__ __launch_bounds__(256) void k_sort_scan(int32_t* __restrict__ cnt, in
     __syncthreads();
   }
   if (tid == 0) total[e] = carry;
+}
+
+// Up to SB_MAX routes: the whole sort in one workgroup of 16 waves (one launch;
+// for decode-sized inputs the three launches below cost more than the work).
+// Wave w owns the contiguous routes [w * seg, (w + 1) * seg): its per-expert
+// counts go to cnt[w][e]; a pass over the experts turns them into each wave's
+// first row per expert (expert start + the counts of earlier waves); then every
+// wave walks its routes in order, 64 at a time, ranking equal keys with ballots.
+constexpr int SB_WAVES = 16;
+constexpr int SB_MAX = 65536;
+
+__global__ __launch_bounds__(1024) void k_sort_block(
+    const int32_t* __restrict__ ids, int n, int E, int L, int off, int32_t* __restrict__ offs,
+    int32_t* __restrict__ m_indptr, int32_t* __restrict__ n_local, int32_t* __restrict__ e2p,
+    int32_t* __restrict__ p2e, int32_t* __restrict__ zero, int n_zero) {
+  extern __shared__ int32_t sm[];
+  int32_t* cnt = sm;                  // [SB_WAVES][L]
+  int32_t* start = sm + SB_WAVES * L; // [L]
+  int32_t* wsum = start + L;          // [SB_WAVES]
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  for (int i = tid; i < n_zero; i += 1024) zero[i] = 0;
+  for (int i = tid; i < SB_WAVES * L; i += 1024) cnt[i] = 0;
+  __syncthreads();
+  const int seg = ((n + SB_WAVES - 1) / SB_WAVES + 63) / 64 * 64;
+  const int b0 = w * seg, b1 = min(n, b0 + seg);
+  for (int i = b0 + lane; i < b1; i += 64) {
+    const int key = local_key(ids[i], E, L, off);
+    if (key < L) atomicAdd(&cnt[w * L + key], 1);
+  }
+  __syncthreads();
+  // per expert: counts of earlier waves (exclusive, in place) and the total
+  for (int e = tid; e < L; e += 1024) {
+    int run = 0;
+    for (int v = 0; v < SB_WAVES; ++v) {
+      const int c = cnt[v * L + e];
+      cnt[v * L + e] = run;
+      run += c;
+    }
+    start[e] = run;
+  }
+  __syncthreads();
+  // exclusive scan of the expert totals (L <= 1024: one expert per thread)
+  const int tot = tid < L ? start[tid] : 0;
+  const int inc = wave_incl_scan(tot);
+  if (lane == 63) wsum[w] = inc;
+  __syncthreads();
+  int before = 0;
+  for (int v = 0; v < w; ++v) before += wsum[v];
+  if (tid < L) {
+    const int st = before + inc - tot;
+    offs[tid] = st + tot;
+    if (m_indptr) m_indptr[tid + 1] = st + tot;
+    start[tid] = st;
+  }
+  if (tid == 0) {
+    int all = 0;
+    for (int v = 0; v < SB_WAVES; ++v) all += wsum[v];
+    *n_local = all;
+    if (m_indptr) m_indptr[0] = 0;
+  }
+  __syncthreads();
+  for (int i = tid; i < SB_WAVES * L; i += 1024) cnt[i] += start[i % L];
+  __syncthreads();
+  // stable scatter: wave w only touches its own row cnt[w][*]
+  int bits = 1;
+  while ((1 << bits) <= L) ++bits;  // keys 0..L fit
+  const uint64_t lt = (1ull << lane) - 1ull;
+  int32_t* run = cnt + w * L;
+  for (int base = b0; base < b1; base += 64) {
+    const int i = base + lane;
+    const bool valid = i < b1;
+    const int key = valid ? local_key(ids[i], E, L, off) : L;
+    uint64_t peers = __ballot(valid);
+    for (int b = 0; b < bits; ++b) {
+      const uint64_t m = __ballot((key >> b) & 1);
+      peers &= ((key >> b) & 1) ? m : ~m;
+    }
+    const int rank = __popcll(peers & lt);
+    const bool local = valid && key < L;
+    const int pos = local ? run[key] + rank : -1;
+    if (local && rank == 0) run[key] += __popcll(peers);
+    if (valid) {
+      e2p[i] = pos;
+      if (pos >= 0) p2e[pos] = i;
+    }
+  }
 }
 
 __global__ __launch_bounds__(64) void k_sort_scatter(
@@ -171,6 +259,12 @@ moe_status sort_enqueue(const int32_t* ids, int64_t T, int32_t k, int32_t E, int
   const int64_t n = T * (int64_t)k;
   if (n == 0) {
     k_sort_empty<<<1, 256, 0, st>>>(L, offs, m_indptr, n_local);
+    return launch_status();
+  }
+  const size_t sb_lds = (size_t)(SB_WAVES * L + L + SB_WAVES) * sizeof(int32_t);
+  if (n <= SB_MAX && sb_lds <= 65536) {
+    k_sort_block<<<1, 1024, sb_lds, st>>>(ids, (int)n, E, L, off, offs, m_indptr, n_local, e2p, p2e,
+                                          zero, zero ? n_zero : 0);
     return launch_status();
   }
   const int64_t nb = n_chunks(n);

@@ -27,6 +27,7 @@ ROUTE_CASES = [
     (1024, 64, 8, 0.0, False), (1, 64, 8, 0.0, False), (777, 8, 2, 0.0, True),
     (513, 256, 8, 0.0, True), (300, 1, 1, 0.0, False), (100, 1024, 16, 0.0, False),
     (65, 16, 16, 0.0, False), (129, 100, 5, 0.0, True), (40, 32, 3, 0.0, False),
+    (257, 128, 4, 0.0, False), (50, 200, 6, 0.0, True), (70, 512, 8, 0.0, True),
 ]
 
 
@@ -49,6 +50,8 @@ SORT_CASES = [
     (32, 2, 8, 8, 0), (4096, 2, 8, 8, 0), (8192, 8, 256, 32, 64), (8192, 8, 64, 64, 0),
     (1, 8, 64, 64, 0), (1, 1, 4, 4, 0), (1000, 3, 10, 3, 7), (65536, 8, 256, 256, 0),
     (3000, 16, 1024, 1000, 24),
+    # one-workgroup path at its limits (n = 64000 with 900 experts) and just past it
+    (4000, 16, 900, 900, 0), (8193, 8, 64, 64, 0),
 ]
 
 
