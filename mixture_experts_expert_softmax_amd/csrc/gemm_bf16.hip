@@ -174,39 +174,87 @@ struct RowLoader {
 // transposed): source rows are contraction indices. Thread tid reads contraction
 // row (tid & 63) and 8 output columns per chunk (tid >> 6) + 4j, and scatters
 // the 8 values into the [output row][contraction] LDS layout.
-struct ColLoader {
-  const uint16_t* base;   // points at source row r_begin, column c0
-  int64_t ld;             // source row stride (elements)
-  int rows_left0;         // valid contraction rows from r_begin
+// A K-major operand tile (contraction rows x output columns, rows contiguous in
+// memory): 64 contraction rows x 256 columns per stage. Thread t loads rows
+// t / 32 + 8j, 16-byte chunk t % 32 (whole 512-byte rows per 32 lanes) and stores
+// them unchanged into LDS rows of 32 chunks, chunk c of row r at c ^ ((r & 7) << 1)
+// so that the transposing fragment reads below hit distinct banks. Rows past the
+// contraction end read as zeros; columns are whole 16-byte chunks (multiples of 32).
+struct KLoader {
+  const uint16_t* base;   // contraction row 0 of the operand, column c0
+  int64_t ld;             // row stride (elements)
+  int rows_left0;         // valid contraction rows from base
   int cols_left;          // valid output columns from c0
   uint4 r[8];
   __device__ __forceinline__ void load(int kt, int tid) {
-    const int kr = kt * TK + (tid & 63);
-    const bool rok = kr < rows_left0;
+    const int c = tid & 31;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const int cc = (tid >> 6) + 4 * j;
-      const bool ok = rok && (cc * 8 < cols_left);
-      r[j] = ok ? *reinterpret_cast<const uint4*>(base + (int64_t)kr * ld + cc * 8)
+      const int kr = kt * TK + (tid >> 5) + 8 * j;
+      const bool ok = kr < rows_left0 && c * 8 < cols_left;
+      r[j] = ok ? *reinterpret_cast<const uint4*>(base + (int64_t)kr * ld + c * 8)
                 : make_uint4(0, 0, 0, 0);
     }
   }
   __device__ __forceinline__ void store(uint4* __restrict__ lds, int tid) const {
-    uint16_t* l16 = reinterpret_cast<uint16_t*>(lds);
-    const int kr = tid & 63;
+    const int c = tid & 31;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const int cc = (tid >> 6) + 4 * j;
-      const uint32_t w[4] = {r[j].x, r[j].y, r[j].z, r[j].w};
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const int n = cc * 8 + q;
-        const int pc = (kr >> 3) ^ (n & 7);
-        l16[n * 64 + pc * 8 + (kr & 7)] = (uint16_t)((q & 1) ? (w[q >> 1] >> 16) : (w[q >> 1] & 0xFFFFu));
-      }
+      const int row = (tid >> 5) + 8 * j;
+      lds[row * 32 + (c ^ ((row & 7) << 1))] = r[j];
     }
   }
 };
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+
+// MFMA fragment of a K-major LDS tile: lane L gets output column
+// cb + L % 32 and contraction values 16 kk + 8 (L / 32) + 0..7. ds_read_b64_tr_b16
+// works on groups of 16 lanes: lane 4j + a of a group addresses contraction row
+// kb + j, columns 4a .. 4a + 3 of the group's 16 columns, and lane i of the group
+// receives column i at rows kb .. kb + 3 (established on the device with an
+// index-valued tile). Two reads give the 8 contraction values.
+__device__ __forceinline__ bf16x8 ktile_frag(const uint4* __restrict__ lds, int kk, int cb, int lane) {
+  typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+  const int g = lane >> 4, i = lane & 15;
+  const int col = cb + 16 * (g & 1) + 4 * (i & 3);
+  const int row = kk * 16 + 8 * (g >> 1) + (i >> 2);
+  const int chunk = col >> 3, half = (col >> 2) & 1;
+  char* t = const_cast<char*>(reinterpret_cast<const char*>(lds));
+  const int o0 = row * 512 + ((chunk ^ ((row & 7) << 1)) << 4) + half * 8;
+  const int o1 = (row + 4) * 512 + ((chunk ^ (((row + 4) & 7) << 1)) << 4) + half * 8;
+  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(t + o0));
+  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(t + o1));
+  typedef short v8i16 __attribute__((ext_vector_type(8)));
+  const v8i16 both{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+  return __builtin_bit_cast(bf16x8, both);
+}
+
+// One 64-deep stage for operands of either layout: A (output columns wn*128 + ...)
+// and B (output rows wm*128 + ...) each come from a row-major tile ([256 rows][8
+// chunks], as in mma_stage) or a K-major tile (ktile_frag).
+template <bool A_K, bool B_K>
+__device__ __forceinline__ void mma_stage_t(const uint4* __restrict__ As, const uint4* __restrict__ Bs,
+                                            int wn, int wm, int lane, f32x16 (&acc)[4][4]) {
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    const int ch = ((kk << 1) + (lane >> 5)) ^ (lane & 7);
+    bf16x8 wf[4], xf[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      wf[i] = A_K ? ktile_frag(As, kk, wn * 128 + i * 32, lane)
+                  : as_bf16x8(As[(wn * 128 + i * 32 + (lane & 31)) * 8 + ch]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      xf[j] = B_K ? ktile_frag(Bs, kk, wm * 128 + j * 32, lane)
+                  : as_bf16x8(Bs[(wm * 128 + j * 32 + (lane & 31)) * 8 + ch]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[i], xf[j], acc[i][j], 0, 0, 0);
+  }
+}
 
 __device__ __forceinline__ void zero_acc(f32x16 (&acc)[4][4]) {
 #pragma unroll
@@ -529,7 +577,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_dgrad(DgradArgs a) {
     p = p < mend ? p : mend - 1;
     lg.off[j] = (uint32_t)p * (uint32_t)a.N;
   }
-  ColLoader lw;  // weight side: W[e] rows n (contraction), columns k
+  KLoader lw;  // weight side: W[e] rows n (contraction), columns k
   lw.base = a.W + (int64_t)e * a.N * a.K + c0;
   lw.ld = a.K;
   lw.rows_left0 = a.N;
@@ -550,7 +598,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_dgrad(DgradArgs a) {
       lg.load(kt + 1);
       lw.load(kt + 1, tid);
     }
-    mma_stage((smem + TILE_U4 + s * 2 * TILE_U4), (smem + s * 2 * TILE_U4), wn, wm, lane, acc);
+    mma_stage_t<true, false>((smem + TILE_U4 + s * 2 * TILE_U4), (smem + s * 2 * TILE_U4), wn, wm,
+                             lane, acc);
     if (more) {
       lg.store((smem + (s ^ 1) * 2 * TILE_U4), tid);
       lw.store((smem + TILE_U4 + (s ^ 1) * 2 * TILE_U4), tid);
@@ -610,12 +659,12 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_wgrad(WgradArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int wn = wid & 1, wm = wid >> 1;
 
-  ColLoader lx;  // weight side: output columns k from X rows
+  KLoader lx;  // weight side: output columns k from X rows
   lx.base = a.X + (int64_t)start * a.K + c0;
   lx.ld = a.K;
   lx.rows_left0 = rows;
   lx.cols_left = a.K - c0;
-  ColLoader lgd;  // activation side: output rows n from G rows
+  KLoader lgd;  // activation side: output rows n from G rows
   lgd.base = a.G + (int64_t)start * a.N + n0;
   lgd.ld = a.N;
   lgd.rows_left0 = rows;
@@ -638,7 +687,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_wgrad(WgradArgs a) {
       lgd.load(kt + 1, tid);
       lx.load(kt + 1, tid);
     }
-    mma_stage((smem + TILE_U4 + s * 2 * TILE_U4), (smem + s * 2 * TILE_U4), wn, wm, lane, acc);
+    mma_stage_t<true, true>((smem + TILE_U4 + s * 2 * TILE_U4), (smem + s * 2 * TILE_U4), wn, wm,
+                            lane, acc);
     if (more) {
       lgd.store((smem + (s ^ 1) * 2 * TILE_U4), tid);
       lx.store((smem + TILE_U4 + (s ^ 1) * 2 * TILE_U4), tid);

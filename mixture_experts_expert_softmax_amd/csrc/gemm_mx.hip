@@ -490,10 +490,12 @@ __global__ __launch_bounds__(256, 2) void k_gemm_mx_stream(MxArgs a) {
   }
 }
 
-// The decode kernel takes over while the experts hold few rows on average: there the
-// 256-row tiles would be mostly padding and too few to fill the chip.
-inline bool mx_use_small(int64_t R, int L, int K, int NB, int64_t act_rows) {
-  return R <= 64LL * L && K % 256 == 0 && (K >> 8) <= 4 * SMAX_STAGES &&
+// The decode kernel takes over while the experts hold few rows on average: there
+// the 256-row tiles would be mostly padding and too few to fill the chip. Measured
+// crossover (H=7168, I=2048, 64 experts): about 32 rows per expert for FC1 and 24
+// for FC2 (its contraction is 3.5x shorter, so its blocks live shorter).
+inline bool mx_use_small(int64_t R, int L, int K, int NB, int64_t act_rows, int rows_per_expert) {
+  return R <= (int64_t)rows_per_expert * L && K % 256 == 0 && (K >> 8) <= 4 * SMAX_STAGES &&
          (int64_t)NB * (K >> 1) < (1LL << 31) && act_rows * K < (1LL << 31);
 }
 
@@ -527,7 +529,7 @@ moe_status mx_fc1_enqueue(int activation, const void* x, const void* x_sf, const
   a.I = I;
   a.limits = limits;
   a.def_limit = 7.0f;
-  if (mx_use_small(R, L, H, 2 * I, R)) {
+  if (mx_use_small(R, L, H, 2 * I, R, 32)) {
     a.n_tiles = I / 32;
     const int64_t tiles = mx_row_tiles(R, L, STB) * a.n_tiles;
     const int grid = (int)((tiles + 7) / 8 * 8);
@@ -567,7 +569,7 @@ moe_status mx_fc2_enqueue(const void* act, const void* act_sf, const void* w2, c
   a.K = I;
   a.C = reinterpret_cast<uint16_t*>(y);
   a.ldc = H;
-  if (mx_use_small(R, L, I, H, R)) {
+  if (mx_use_small(R, L, I, H, R, 24)) {
     a.n_tiles = (H + 63) / 64;
     const int64_t tiles = mx_row_tiles(R, L, STB) * a.n_tiles;
     const int grid = (int)((tiles + 7) / 8 * 8);
