@@ -6,35 +6,47 @@
 // expanded_idx_to_permuted_idx (StepFun page, "Prepared launches").
 //
 // HBM-bound: every local FC2 row is read once and every output row written once.
-// One thread owns 8 consecutive columns (16-byte loads and stores); a block of
-// 256 threads sweeps 2048 columns of one token, so each y row is read as long
-// coalesced runs.
+// One thread owns 8 consecutive columns of one token (16-byte loads and stores);
+// consecutive threads take consecutive chunks of the flattened [T][H/8] output, so
+// each y row is read as long coalesced runs and no lane idles at the row end. A
+// thread issues all k row loads before it sums them in slot order.
 #include "common.h"
 
 namespace moe {
 namespace {
 
+template <int KMAX>
 __global__ __launch_bounds__(256) void k_finalize(const uint4* __restrict__ y,
                                                   const int32_t* __restrict__ e2p,
                                                   const float* __restrict__ w, int64_t T, int k,
                                                   int H8, uint4* __restrict__ out) {
-  const int64_t t = blockIdx.y + (int64_t)gridDim.y * blockIdx.z;
-  if (t >= T) return;
-  const int c = blockIdx.x * blockDim.x + threadIdx.x;  // 8-column chunk
-  if (c >= H8) return;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= T * H8) return;
+  const int64_t t = idx / H8;
+  const int c = (int)(idx - t * H8);  // 8-column chunk
+  // all of the token's row loads go out before the fixed-order sum
+  int p[KMAX];
+  float ws[KMAX];
+  uint4 v[KMAX];
+#pragma unroll
+  for (int s = 0; s < KMAX; ++s) {
+    p[s] = s < k ? e2p[t * k + s] : -1;
+    ws[s] = s < k ? w[t * k + s] : 0.f;
+  }
+#pragma unroll
+  for (int s = 0; s < KMAX; ++s)
+    v[s] = p[s] >= 0 ? y[(int64_t)p[s] * H8 + c] : make_uint4(0, 0, 0, 0);
   float acc[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) acc[j] = 0.f;
-  for (int s = 0; s < k; ++s) {
-    const int p = e2p[t * k + s];
-    if (p < 0) continue;
-    const float ws = w[t * k + s];
-    const uint4 v = y[(int64_t)p * H8 + c];
-    const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int s = 0; s < KMAX; ++s) {
+    if (p[s] < 0) continue;
+    const uint32_t u[4] = {v[s].x, v[s].y, v[s].z, v[s].w};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      acc[2 * j] += ws * bf16_bits_to_f32(u[j] & 0xFFFFu);
-      acc[2 * j + 1] += ws * bf16_bits_to_f32(u[j] >> 16);
+      acc[2 * j] += ws[s] * bf16_bits_to_f32(u[j] & 0xFFFFu);
+      acc[2 * j + 1] += ws[s] * bf16_bits_to_f32(u[j] >> 16);
     }
   }
   uint4 o;
@@ -42,7 +54,7 @@ __global__ __launch_bounds__(256) void k_finalize(const uint4* __restrict__ y,
   o.y = pack_bf16x2(acc[2], acc[3]);
   o.z = pack_bf16x2(acc[4], acc[5]);
   o.w = pack_bf16x2(acc[6], acc[7]);
-  out[t * H8 + c] = o;
+  out[idx] = o;
 }
 
 }  // namespace
@@ -51,11 +63,17 @@ moe_status finalize_enqueue(const void* y, const int32_t* e2p, const float* w, i
                             int H, void* out, hipStream_t st) {
   if (T == 0) return MOE_OK;
   const int H8 = H / 8;
-  const unsigned gx = (unsigned)((H8 + 255) / 256);
-  const int64_t gy = T < 65535 ? T : 65535;
-  const int64_t gz = (T + gy - 1) / gy;
-  k_finalize<<<dim3(gx, (unsigned)gy, (unsigned)gz), 256, 0, st>>>(
-      reinterpret_cast<const uint4*>(y), e2p, w, T, k, H8, reinterpret_cast<uint4*>(out));
+  const int64_t blocks = (T * H8 + 255) / 256;
+  if (blocks > 0x7fffffffLL) return MOE_ERR_UNSUPPORTED;
+  if (k <= 2)
+    k_finalize<2><<<(unsigned)blocks, 256, 0, st>>>(reinterpret_cast<const uint4*>(y), e2p, w, T, k,
+                                                    H8, reinterpret_cast<uint4*>(out));
+  else if (k <= 8)
+    k_finalize<8><<<(unsigned)blocks, 256, 0, st>>>(reinterpret_cast<const uint4*>(y), e2p, w, T, k,
+                                                    H8, reinterpret_cast<uint4*>(out));
+  else
+    k_finalize<16><<<(unsigned)blocks, 256, 0, st>>>(reinterpret_cast<const uint4*>(y), e2p, w, T, k,
+                                                     H8, reinterpret_cast<uint4*>(out));
   return launch_status();
 }
 
