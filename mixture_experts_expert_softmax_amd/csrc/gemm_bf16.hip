@@ -20,7 +20,7 @@
 //    lane's accumulator holds 4 consecutive output columns of one output row:
 //    epilogue stores are 8-byte (bf16) or 16-byte (fp32) runs.
 //  * Both operand tiles are staged in LDS as [256 rows][8 chunks of 16 B] with
-//    the chunk index XOR-swizzled by (row & 7), double buffered (128 KB total);
+//    the chunk index XOR-swizzled by (row >> 1) & 7, double buffered (128 KB total);
 //    the next tile's global loads are issued before the current tile's MFMAs.
 //  * Ragged groups: an upper bound of M tiles is launched (no host sync); each
 //    workgroup decodes its (expert, row block) from the device offsets, clamps
@@ -133,7 +133,7 @@ __device__ __forceinline__ void mma_stage(const uint4* __restrict__ Ws, const ui
                                           int wn, int wm, int lane, f32x16 (&acc)[4][4]) {
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
-    const int ch = ((kk << 1) + (lane >> 5)) ^ (lane & 7);
+    const int ch = ((kk << 1) + (lane >> 5)) ^ ((lane >> 1) & 7);
     bf16x8 wf[4], xf[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) wf[i] = as_bf16x8(Ws[(wn * 128 + i * 32 + (lane & 31)) * 8 + ch]);
@@ -164,7 +164,7 @@ struct RowLoader {
   }
   __device__ __forceinline__ void store(uint4* __restrict__ lds, int tid) const {
     const int row = tid >> 3;
-    const int pc = ch ^ (row & 7);
+    const int pc = ch ^ ((row >> 1) & 7);
 #pragma unroll
     for (int j = 0; j < 8; ++j) lds[(row + 32 * j) * 8 + pc] = r[j];
   }
@@ -177,7 +177,7 @@ struct RowLoader {
 // A K-major operand tile (contraction rows x output columns, rows contiguous in
 // memory): 64 contraction rows x 256 columns per stage. Thread t loads rows
 // t / 32 + 8j, 16-byte chunk t % 32 (whole 512-byte rows per 32 lanes) and stores
-// them unchanged into LDS rows of 32 chunks, chunk c of row r at c ^ ((r & 7) << 1)
+// them unchanged into LDS rows of 32 chunks, chunk c of row r at c ^ ((r & 3) << 2)
 // so that the transposing fragment reads below hit distinct banks. Rows past the
 // contraction end read as zeros; columns are whole 16-byte chunks (multiples of 32).
 struct KLoader {
@@ -201,7 +201,7 @@ struct KLoader {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int row = (tid >> 5) + 8 * j;
-      lds[row * 32 + (c ^ ((row & 7) << 1))] = r[j];
+      lds[row * 32 + (c ^ ((row & 3) << 2))] = r[j];
     }
   }
 };
@@ -221,8 +221,8 @@ __device__ __forceinline__ bf16x8 ktile_frag(const uint4* __restrict__ lds, int 
   const int row = kk * 16 + 8 * (g >> 1) + (i >> 2);
   const int chunk = col >> 3, half = (col >> 2) & 1;
   char* t = const_cast<char*>(reinterpret_cast<const char*>(lds));
-  const int o0 = row * 512 + ((chunk ^ ((row & 7) << 1)) << 4) + half * 8;
-  const int o1 = (row + 4) * 512 + ((chunk ^ (((row + 4) & 7) << 1)) << 4) + half * 8;
+  const int o0 = row * 512 + ((chunk ^ ((row & 3) << 2)) << 4) + half * 8;
+  const int o1 = (row + 4) * 512 + ((chunk ^ (((row + 4) & 3) << 2)) << 4) + half * 8;
   const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(t + o0));
   const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(t + o1));
   typedef short v8i16 __attribute__((ext_vector_type(8)));
@@ -238,7 +238,7 @@ __device__ __forceinline__ void mma_stage_t(const uint4* __restrict__ As, const 
                                             int wn, int wm, int lane, f32x16 (&acc)[4][4]) {
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
-    const int ch = ((kk << 1) + (lane >> 5)) ^ (lane & 7);
+    const int ch = ((kk << 1) + (lane >> 5)) ^ ((lane >> 1) & 7);
     bf16x8 wf[4], xf[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -284,8 +284,8 @@ __device__ __forceinline__ void mainloop_full(RowLoader& la, RowLoader& lb, uint
                                               int ktiles, int tid, int lane, int wn, int wm,
                                               f32x16 (&acc)[4][4]) {
   const int lrow = tid >> 3;
-  const int pc = la.ch ^ (lrow & 7);
-  const int rsel = lane & 31, kg = lane >> 5, sw = lane & 7;
+  const int pc = la.ch ^ ((lrow >> 1) & 7);
+  const int rsel = lane & 31, kg = lane >> 5, sw = (lane >> 1) & 7;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     la.r[j] = *reinterpret_cast<const uint4*>(la.base + la.off[j] + kbase + la.ch * 8);

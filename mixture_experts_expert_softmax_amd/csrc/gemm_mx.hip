@@ -129,7 +129,7 @@ __global__ __launch_bounds__(MNT, 1) void k_gemm_mx(MxArgs a) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int r = xr + 32 * j;
-      X[r * 8 + (xc ^ (r & 7))] = rx[j];
+      X[r * 8 + (xc ^ ((r >> 1) & 7))] = rx[j];
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -177,8 +177,8 @@ __global__ __launch_bounds__(MNT, 1) void k_gemm_mx(MxArgs a) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int r = wm * 128 + j * 32 + rsel;
-        const uint4 lo = X[r * 8 + ((4 * kk + g) ^ (r & 7))];
-        const uint4 hi = X[r * 8 + ((4 * kk + 2 + g) ^ (r & 7))];
+        const uint4 lo = X[r * 8 + ((4 * kk + g) ^ ((r >> 1) & 7))];
+        const uint4 hi = X[r * 8 + ((4 * kk + 2 + g) ^ ((r >> 1) & 7))];
         xq[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
       }
     };
@@ -284,7 +284,7 @@ __global__ __launch_bounds__(MNT, 1) void k_gemm_mx(MxArgs a) {
 // (128 bytes per row): each load instruction takes 8 whole 128-byte lines (lane l:
 // row 8j + l / 8, 16-byte chunk l % 8). Weight stages are loaded two ahead into
 // registers and pass through a private LDS slot that turns them into MFMA fragments
-// (chunks swizzled by row & 7; one slot is enough because a wave's LDS operations
+// (chunks swizzled by (row >> 1) & 7; one slot is enough because a wave's LDS operations
 // run in order). The weight scales of the wave's range are read into LDS once at the
 // start; the activation fragments come straight from global memory, one stage ahead
 // (for decode most tile rows repeat the same token, so those loads are cheap). Two
@@ -337,12 +337,14 @@ __global__ __launch_bounds__(256, 2) void k_gemm_mx_stream(MxArgs a) {
   }
 
   // 32-bit per-lane offsets from stage-uniform bases. Weights: instruction j loads
-  // tile row 8j + lane / 8, chunk (lane % 8) ^ (row & 7), and stores it to LDS chunk
-  // lane % 8 of that row.
+  // tile row R = 8j + lane / 8, chunk (lane % 8) ^ ((R >> 1) & 7), and stores it to
+  // LDS chunk lane % 8 of that row.
   uint32_t voff[8];
-  const int csw = (lane & 7) ^ ((lane >> 3) & 7);
 #pragma unroll
-  for (int j = 0; j < 8; ++j) voff[j] = (uint32_t)wrow_of(8 * j + (lane >> 3)) * kh + 16u * csw;
+  for (int j = 0; j < 8; ++j) {
+    const int R = 8 * j + (lane >> 3);
+    voff[j] = (uint32_t)wrow_of(R) * kh + 16u * ((lane & 7) ^ ((R >> 1) & 7));
+  }
   int p = m0 + r;
   p = p < mend ? p : mend - 1;
   const int src = a.a_gather ? a.a_gather[p] / a.a_div : p;
@@ -380,7 +382,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_mx_stream(MxArgs a) {
     const u32x4* W = &ring[wid][0];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      const int c = (2 * s + g) ^ (r & 7);
+      const int c = (2 * s + g) ^ ((r >> 1) & 7);
       const u32x4 w0 = W[r * 8 + c];
       const u32x4 w1 = W[(32 + r) * 8 + c];
       const int bi = 8 * q + 2 * s + g;
