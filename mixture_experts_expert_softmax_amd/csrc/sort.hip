@@ -39,13 +39,15 @@ __global__ __launch_bounds__(64) void k_sort_count(const int32_t* __restrict__ i
   for (int e = lane; e < L; e += 64) hist[e] = 0;
   __syncthreads();
   const int64_t base = (int64_t)blockIdx.x * CHUNK;
+  int key[SORT_STEPS];  // all of the chunk's ids are requested before any is used
+#pragma unroll
   for (int step = 0; step < SORT_STEPS; ++step) {
-    int64_t i = base + step * 64 + lane;
-    if (i < n) {
-      int key = local_key(ids[i], E, L, off);
-      if (key < L) atomicAdd(&hist[key], 1);
-    }
+    const int64_t i = base + step * 64 + lane;
+    key[step] = i < n ? local_key(ids[i], E, L, off) : L;
   }
+#pragma unroll
+  for (int step = 0; step < SORT_STEPS; ++step)
+    if (key[step] < L) atomicAdd(&hist[key[step]], 1);
   __syncthreads();
   for (int e = lane; e < L; e += 64) cnt[(int64_t)e * nb + blockIdx.x] = hist[e];
 }
@@ -210,10 +212,17 @@ __global__ __launch_bounds__(64) void k_sort_scatter(
   while ((1 << bits) <= L) ++bits;  // keys 0..L fit
   const uint64_t lt = (1ull << lane) - 1ull;
   const int64_t base = (int64_t)blockIdx.x * CHUNK;
+  int keys[SORT_STEPS];  // all of the chunk's ids are requested before any is used
+#pragma unroll
+  for (int step = 0; step < SORT_STEPS; ++step) {
+    const int64_t i = base + step * 64 + lane;
+    keys[step] = i < n ? local_key(ids[i], E, L, off) : L;
+  }
+#pragma unroll
   for (int step = 0; step < SORT_STEPS; ++step) {
     int64_t i = base + step * 64 + lane;
     bool valid = i < n;
-    int key = valid ? local_key(ids[i], E, L, off) : L;
+    int key = keys[step];
     uint64_t peers = __ballot(valid);
     for (int b = 0; b < bits; ++b) {
       uint64_t m = __ballot((key >> b) & 1);
@@ -222,9 +231,8 @@ __global__ __launch_bounds__(64) void k_sort_scatter(
     int rank = __popcll(peers & lt);
     int pos = -1;
     if (valid && key < L) pos = run[key] + rank;
-    __syncthreads();
+    // one wave per block: its LDS accesses take effect in order, no barrier needed
     if (valid && key < L && rank == 0) run[key] += __popcll(peers);
-    __syncthreads();
     if (valid) {
       e2p[i] = pos;
       if (pos >= 0) p2e[pos] = (int32_t)i;
