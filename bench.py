@@ -274,6 +274,59 @@ def _time(fn, reps=10, warmup=3, flush=None):
     return times[len(times) // 2]
 
 
+def _mx_sweep(wfmt, flush, dev):
+    """Block-scaled layer (MXFP8 activations, MXFP4 or MXFP8 weights) at H=7168, I=2048,
+    64 experts, top-8 over decode and prefill token counts, plus its two GEMM stages."""
+    import numpy as np
+    import torch
+    import mixture_experts_expert_softmax_amd as M
+    import moe_synth as S
+    cw = S.w4a8_moe(seed=0, T=8192, wfmt=wfmt)
+    dw = {k_: torch.from_numpy(np.ascontiguousarray(getattr(cw, k_))).to(dev)
+          for k_ in ("x", "x_sf", "w1", "w1_sf", "w2", "w2_sf")}
+    lgw = torch.from_numpy(cw.logits).to(dev)
+    per_expert_bytes = (dw["w1"][0].numel() + dw["w1_sf"][0].numel() + dw["w2"][0].numel()
+                        + dw["w2_sf"][0].numel())
+    sweep = {}
+    for Tw in (1, 16, 128, 1024, 8192):
+        idsw, wtsw = M.moe_route(lgw[:Tw], cw.top_k)
+        outw = torch.empty((Tw, cw.H), dtype=torch.bfloat16, device=dev)
+        wsw = torch.empty(M.moe_ffn_workspace_size(Tw, cw.H, cw.I, cw.num_experts, cw.top_k,
+                                                   weight_format=wfmt), dtype=torch.uint8, device=dev)
+
+        def mx_step():
+            M.moe_route(lgw[:Tw], cw.top_k, idsw, wtsw)
+            M.moe_ffn_forward_mx(dw["x"][:Tw], dw["x_sf"][:Tw], idsw, wtsw, dw["w1"], dw["w1_sf"],
+                                 dw["w2"], dw["w2_sf"], cw.num_experts, out=outw, workspace=wsw)
+        touched = int(torch.unique(idsw).numel())
+        small = touched * per_expert_bytes < (512 << 20)
+        ms_ = _time(mx_step, reps=50 if small else (20 if Tw < 1024 else 10),
+                    flush=flush if small else None)
+        fl = 6.0 * cw.H * cw.I * Tw * cw.top_k
+        wb = touched * per_expert_bytes
+        sweep[str(Tw)] = {"ms": round(ms_, 4), "tflops": round(fl / (ms_ * 1e-3) / 1e12, 2),
+                          "tokens_per_s": round(Tw / (ms_ * 1e-3), 1), "experts_touched": touched,
+                          "timing": "median of 50, MALL flushed" if small else "mean",
+                          "weight_gbs": round(wb / (ms_ * 1e-3) / 1e9, 1),
+                          "hbm_frac_weights": round(wb / (ms_ * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                          "fp8_mfma_frac": round(fl / (ms_ * 1e-3) / 1e12 / FP8_PEAK_TFLOPS, 4)}
+    # the two GEMM stages at T=8192 on their own
+    srt = M.moe_sort(idsw, cw.num_experts)
+    act = torch.empty((8192 * cw.top_k, cw.I), dtype=torch.uint8, device=dev)
+    act_sf = torch.empty((8192 * cw.top_k, cw.I // 32), dtype=torch.uint8, device=dev)
+    yw = torch.empty((8192 * cw.top_k, cw.H), dtype=torch.bfloat16, device=dev)
+    ms1 = _time(lambda: M.moe_fc1_mx(dw["x"], dw["x_sf"], dw["w1"], dw["w1_sf"], srt["offs"], srt["p2e"],
+                                     cw.top_k, cw.num_experts, act=act, act_sf=act_sf))
+    ms2 = _time(lambda: M.moe_fc2_mx(act, act_sf, dw["w2"], dw["w2_sf"], srt["offs"], 8192, cw.top_k,
+                                     cw.num_experts, y=yw))
+    R = 8192 * cw.top_k
+    sweep["8192_stages"] = {"fc1_ms": round(ms1, 4), "fc1_tflops": round(4.0 * cw.H * cw.I * R / (ms1 * 1e-3) / 1e12, 1),
+                            "fc2_ms": round(ms2, 4), "fc2_tflops": round(2.0 * cw.H * cw.I * R / (ms2 * 1e-3) / 1e12, 1),
+                            "peak_tflops_fp8": FP8_PEAK_TFLOPS}
+    del dw, act, act_sf, yw
+    return sweep
+
+
 def secondary_measurements(progress):
     """The other hot-path rows at their own workloads (not the headline step):
     the standalone grouped GEMMs, the expert-shard forward, and routing / sort /
@@ -335,51 +388,11 @@ def secondary_measurements(progress):
                            "weight_gbs": round(wbytes / (ms_ * 1e-3) / 1e9, 1)}
     del xs, w1s, w2s, wsp, outs
 
-    progress("secondary: W4A8 (MXFP4 weights, MXFP8 activations) H=7168 I=2048 64 experts top-8")
-    cw = S.w4a8_moe(seed=0, T=8192)
-    dw = {k_: torch.from_numpy(np.ascontiguousarray(getattr(cw, k_))).to(dev)
-          for k_ in ("x", "x_sf", "w1", "w1_sf", "w2", "w2_sf")}
-    lgw = torch.from_numpy(cw.logits).to(dev)
-    per_expert_bytes = (dw["w1"][0].numel() + dw["w1_sf"][0].numel() + dw["w2"][0].numel()
-                        + dw["w2_sf"][0].numel())
-    sweep = {}
-    for Tw in (1, 16, 128, 1024, 8192):
-        idsw, wtsw = M.moe_route(lgw[:Tw], cw.top_k)
-        outw = torch.empty((Tw, cw.H), dtype=torch.bfloat16, device=dev)
-        wsw = torch.empty(M.moe_ffn_workspace_size(Tw, cw.H, cw.I, cw.num_experts, cw.top_k,
-                                                   weight_format="mxfp4"), dtype=torch.uint8, device=dev)
+    for wfmt, key in (("mxfp4", "w4a8"), ("mxfp8", "mxfp8_weights")):
+        progress(f"secondary: {wfmt} weights, MXFP8 activations, H=7168 I=2048 64 experts top-8")
+        res[key] = _mx_sweep(wfmt, flush, dev)
+    del flush
 
-        def w4a8_step():
-            M.moe_route(lgw[:Tw], cw.top_k, idsw, wtsw)
-            M.moe_ffn_forward_mx(dw["x"][:Tw], dw["x_sf"][:Tw], idsw, wtsw, dw["w1"], dw["w1_sf"],
-                                 dw["w2"], dw["w2_sf"], cw.num_experts, out=outw, workspace=wsw)
-        touched = int(torch.unique(idsw).numel())
-        small = touched * per_expert_bytes < (512 << 20)
-        ms_ = _time(w4a8_step, reps=50 if small else (20 if Tw < 1024 else 10),
-                    flush=flush if small else None)
-        fl = 6.0 * cw.H * cw.I * Tw * cw.top_k
-        wb = touched * per_expert_bytes
-        sweep[str(Tw)] = {"ms": round(ms_, 4), "tflops": round(fl / (ms_ * 1e-3) / 1e12, 2),
-                          "tokens_per_s": round(Tw / (ms_ * 1e-3), 1), "experts_touched": touched,
-                          "timing": "median of 50, MALL flushed" if small else "mean",
-                          "weight_gbs": round(wb / (ms_ * 1e-3) / 1e9, 1),
-                          "hbm_frac_weights": round(wb / (ms_ * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                          "fp8_mfma_frac": round(fl / (ms_ * 1e-3) / 1e12 / FP8_PEAK_TFLOPS, 4)}
-    # the two GEMM stages at T=8192 on their own
-    srt = M.moe_sort(idsw, cw.num_experts)
-    act = torch.empty((8192 * cw.top_k, cw.I), dtype=torch.uint8, device=dev)
-    act_sf = torch.empty((8192 * cw.top_k, cw.I // 32), dtype=torch.uint8, device=dev)
-    yw = torch.empty((8192 * cw.top_k, cw.H), dtype=torch.bfloat16, device=dev)
-    ms1 = _time(lambda: M.moe_fc1_mx(dw["x"], dw["x_sf"], dw["w1"], dw["w1_sf"], srt["offs"], srt["p2e"],
-                                     cw.top_k, cw.num_experts, act=act, act_sf=act_sf))
-    ms2 = _time(lambda: M.moe_fc2_mx(act, act_sf, dw["w2"], dw["w2_sf"], srt["offs"], 8192, cw.top_k,
-                                     cw.num_experts, y=yw))
-    R = 8192 * cw.top_k
-    sweep["8192_stages"] = {"fc1_ms": round(ms1, 4), "fc1_tflops": round(4.0 * cw.H * cw.I * R / (ms1 * 1e-3) / 1e12, 1),
-                            "fc2_ms": round(ms2, 4), "fc2_tflops": round(2.0 * cw.H * cw.I * R / (ms2 * 1e-3) / 1e12, 1),
-                            "peak_tflops_fp8": FP8_PEAK_TFLOPS}
-    res["w4a8"] = sweep
-    del dw, act, act_sf, yw, flush
 
     progress("secondary: route + sort at T=262144, 256 experts, top-8")
     T2, E2, k2 = 262144, 256, 8

@@ -73,6 +73,8 @@ typedef int32_t moe_status;
 #define MOE_WFMT_BF16  0  /* x, w1, w2 in bf16 */
 #define MOE_WFMT_MXFP4 1  /* w1, w2 MXFP4 (e2m1 pairs + UE8M0 per 32), x MXFP8 (e4m3 + UE8M0 per 32);
                              the FC1 output is requantized to MXFP8 with the round-up rule */
+#define MOE_WFMT_MXFP8 2  /* as MXFP4 but w1, w2 MXFP8: one e4m3fn code byte per element, UE8M0
+                             per 32 ([StepFun] intro lists mxfp8 among the weight families) */
 
 /* Meaning of a grouped-GEMM offsets array ([GGEMM] intro). */
 #define MOE_OFFS_ENDS   0  /* offs[E]: cumulative end row of each group */
@@ -162,24 +164,25 @@ typedef struct moe_ffn_desc {
   int32_t local_expert_offset;/* global id of local expert 0 */
   int32_t top_k;              /* 1..16 */
   int32_t activation;         /* MOE_ACT_* */
-  int32_t finalize_mode;      /* MOE_FINALIZE_* (MXFP4: DETERMINISTIC or NONE) */
-  int32_t weight_format;      /* MOE_WFMT_*; MXFP4 needs H % 128 == 0 and I % 128 == 0 */
+  int32_t finalize_mode;      /* MOE_FINALIZE_* (MXFP4 / MXFP8: DETERMINISTIC or NONE) */
+  int32_t weight_format;      /* MOE_WFMT_*; MXFP4 / MXFP8 need H % 128 == 0 and I % 128 == 0 */
 } moe_ffn_desc;
 
 typedef struct moe_ffn_tensors {
-  const void* x;              /* [T, H] bf16, or e4m3fn codes (MXFP4 format) */
+  const void* x;              /* [T, H] bf16, or e4m3fn codes (MXFP4 / MXFP8 formats) */
   const int32_t* topk_ids;    /* [T, top_k] int32 global expert ids */
   const float* topk_weights;  /* [T, top_k] float32, normalized by the caller */
   const void* w1;             /* [L, 2I, H] bf16: rows 0..I-1 up, I..2I-1 gate
-                                 (MXFP4: [L, 2I, H/2] bytes, element 2j in the low nibble) */
-  const void* w2;             /* [L, H, I] bf16 (MXFP4: [L, H, I/2] bytes) */
+                                 (MXFP4: [L, 2I, H/2] bytes, element 2j in the low nibble;
+                                 MXFP8: [L, 2I, H] e4m3fn codes) */
+  const void* w2;             /* [L, H, I] bf16 (MXFP4: [L, H, I/2] bytes; MXFP8: [L, H, I] codes) */
   const float* clamp_limit;   /* [L] float32 SwiGLUStep limits, or NULL for 7.0 */
   void* out;                  /* [T, H] bf16 (DETERMINISTIC / FUSED), fully overwritten */
   void* y;                    /* NONE only: [T*top_k, H] bf16 capacity, FC2 rows in permuted order */
   int32_t* e2p;               /* NONE only (optional otherwise): [T*top_k] int32 */
-  const void* x_sf;           /* MXFP4 format: [T, H/32] UE8M0 codes (uint8) */
-  const void* w1_sf;          /* MXFP4 format: [L, 2I, H/32] UE8M0 */
-  const void* w2_sf;          /* MXFP4 format: [L, H, I/32] UE8M0 */
+  const void* x_sf;           /* MXFP4 / MXFP8 formats: [T, H/32] UE8M0 codes (uint8) */
+  const void* w1_sf;          /* MXFP4 / MXFP8 formats: [L, 2I, H/32] UE8M0 */
+  const void* w2_sf;          /* MXFP4 / MXFP8 formats: [L, H, I/32] UE8M0 */
 } moe_ffn_tensors;
 
 size_t moe_ffn_workspace_size(const moe_ffn_desc* desc);
@@ -219,8 +222,10 @@ moe_status moe_fc2(const moe_ffn_desc* desc, const void* act, const void* w2,
                    void* ws, size_t ws_bytes, void* stream);
 
 /*
- * The MXFP4 (W4A8) stages ([W4A8] "Inputs"; intro: fp32 accumulation, UE8M0
- * round-up requantization). desc->weight_format must be MOE_WFMT_MXFP4.
+ * The block-scaled stages ([W4A8] "Inputs"; intro: fp32 accumulation, UE8M0
+ * round-up requantization). desc->weight_format must be MOE_WFMT_MXFP4 (W4A8) or
+ * MOE_WFMT_MXFP8 (w1 / w2 as e4m3fn code bytes, same scale layout); otherwise
+ * MOE_ERR_DTYPE.
  * moe_fc1_mx: act = MXFP8(activation(x[p2e[p]/top_k] @ w1[e].T)) with, per row and
  *             block of 32 columns, the smallest power-of-two scale 2^s such that the
  *             block maximum is <= 448 * 2^s (code s+127) and elements rounded to

@@ -37,7 +37,7 @@ _i32, _i64, _u64, _vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64, ctypes.
 _sz = ctypes.c_size_t
 
 
-WFMT = {"bf16": 0, "mxfp4": 1}
+WFMT = {"bf16": 0, "mxfp4": 1, "mxfp8": 2}
 
 
 class MoeFfnDesc(ctypes.Structure):
@@ -323,6 +323,15 @@ def moe_fc2(act: torch.Tensor, w2: torch.Tensor, offs: torch.Tensor, T: int, top
     return dst
 
 
+def _mx_format(last_dim: int, K: int, name: str) -> str:
+    """Weight family of an MX bank from the bytes per row: K/2 (MXFP4) or K (MXFP8)."""
+    if last_dim == K:
+        return "mxfp8"
+    if 2 * last_dim == K:
+        return "mxfp4"
+    raise ValueError(f"{name}: {last_dim} bytes per row fit neither MXFP4 ({K // 2}) nor MXFP8 ({K})")
+
+
 def moe_ffn_forward_mx(x: torch.Tensor, x_sf: torch.Tensor, topk_ids: torch.Tensor,
                        topk_weights: torch.Tensor, w1: torch.Tensor, w1_sf: torch.Tensor,
                        w2: torch.Tensor, w2_sf: torch.Tensor, num_experts: int,
@@ -331,8 +340,9 @@ def moe_ffn_forward_mx(x: torch.Tensor, x_sf: torch.Tensor, topk_ids: torch.Tens
                        finalize: str = "deterministic", out: Optional[torch.Tensor] = None,
                        workspace: Optional[torch.Tensor] = None, y: Optional[torch.Tensor] = None,
                        e2p: Optional[torch.Tensor] = None):
-    """W4A8 layer: x MXFP8 (uint8 e4m3 codes [T,H] + UE8M0 [T,H/32]), w1 / w2 MXFP4 (packed
-    uint8 [L,2I,H/2] / [L,H,I/2] + UE8M0 [L,2I,H/32] / [L,H,I/32]); bf16 output."""
+    """Block-scaled layer: x MXFP8 (uint8 e4m3 codes [T,H] + UE8M0 [T,H/32]); w1 / w2 either
+    MXFP4 (packed uint8 [L,2I,H/2] / [L,H,I/2]) or MXFP8 (e4m3 codes [L,2I,H] / [L,H,I]), told
+    apart by their last dimension, with UE8M0 scales [L,2I,H/32] / [L,H,I/32]; bf16 output."""
     for t_, n_ in [(x, "x"), (x_sf, "x_sf"), (w1, "w1"), (w1_sf, "w1_sf"), (w2, "w2"), (w2_sf, "w2_sf")]:
         _dev(t_, torch.uint8, n_)
     _dev(topk_ids, torch.int32, "topk_ids"), _dev(topk_weights, torch.float32, "topk_weights")
@@ -342,7 +352,10 @@ def moe_ffn_forward_mx(x: torch.Tensor, x_sf: torch.Tensor, topk_ids: torch.Tens
     L, twoI, _ = w1.shape
     I = twoI // 2
     k = topk_ids.shape[1]
-    d = _ffn_desc(T, H, I, num_experts, L, local_expert_offset, k, activation, finalize, "mxfp4")
+    wfmt = _mx_format(w1.shape[2], H, "w1")
+    if w2.shape[2] != (I if wfmt == "mxfp8" else I // 2):
+        raise ValueError(f"w2 last dim {w2.shape[2]} does not match the {wfmt} w1")
+    d = _ffn_desc(T, H, I, num_experts, L, local_expert_offset, k, activation, finalize, wfmt)
     h = lib()
     ws_bytes = h.moe_ffn_workspace_size(ctypes.byref(d))
     if workspace is None:
@@ -368,12 +381,13 @@ def moe_ffn_forward_mx(x: torch.Tensor, x_sf: torch.Tensor, topk_ids: torch.Tens
 
 def moe_fc1_mx(x, x_sf, w1, w1_sf, offs, p2e, top_k, num_experts, local_expert_offset=0,
                activation="swiglu", clamp_limit=None, act=None, act_sf=None):
-    """act (MXFP8 codes [T*k, I] + UE8M0 [T*k, I/32]) = requant(activation(FC1)) per permuted row."""
+    """act (MXFP8 codes [T*k, I] + UE8M0 [T*k, I/32]) = requant(activation(FC1)) per permuted row;
+    w1 MXFP4 or MXFP8 (see moe_ffn_forward_mx)."""
     T, H = x.shape
     L, twoI, _ = w1.shape
     I = twoI // 2
     d = _ffn_desc(T, H, I, num_experts, L, local_expert_offset, top_k, activation,
-                  "deterministic", "mxfp4")
+                  "deterministic", _mx_format(w1.shape[2], H, "w1"))
     if act is None:
         act = torch.empty((max(T * top_k, 1), I), dtype=torch.uint8, device=x.device)
     if act_sf is None:
@@ -385,11 +399,11 @@ def moe_fc1_mx(x, x_sf, w1, w1_sf, offs, p2e, top_k, num_experts, local_expert_o
 
 
 def moe_fc2_mx(act, act_sf, w2, w2_sf, offs, T, top_k, num_experts, local_expert_offset=0, y=None):
-    """y [T*k, H] bf16 = act @ w2[e].T for the permuted rows (MXFP8 x MXFP4)."""
-    L, H, halfI = w2.shape
-    I = halfI * 2
+    """y [T*k, H] bf16 = act @ w2[e].T for the permuted rows (MXFP8 act, MXFP4 or MXFP8 w2)."""
+    L, H, _ = w2.shape
+    I = act.shape[1]
     d = _ffn_desc(T, H, I, num_experts, L, local_expert_offset, top_k, "swiglu", "deterministic",
-                  "mxfp4")
+                  _mx_format(w2.shape[2], I, "w2"))
     if y is None:
         y = torch.empty((max(T * top_k, 1), H), dtype=torch.bfloat16, device=act.device)
     _check("moe_fc2_mx", lib().moe_fc2_mx(ctypes.byref(d), _ptr(act), _ptr(act_sf), _ptr(w2), _ptr(w2_sf),

@@ -25,13 +25,13 @@ moe_status gemm_wgrad_enqueue(const void* G, const void* X, const int32_t* ends,
                               int N, int K, void* DW, bool out_f32, hipStream_t st);
 moe_status zero_fill(void* p, size_t bytes, hipStream_t st);
 // defined in gemm_mx.hip
-moe_status mx_fc1_enqueue(int activation, const void* x, const void* x_sf, const int32_t* p2e,
-                          int top_k, const void* w1, const void* w1_sf, int L, const int32_t* offs,
-                          int64_t R, int H, int I, const float* limits, void* act, void* act_sf,
-                          hipStream_t st);
-moe_status mx_fc2_enqueue(const void* act, const void* act_sf, const void* w2, const void* w2_sf,
-                          int L, const int32_t* offs, int64_t R, int H, int I, void* y,
-                          hipStream_t st);
+moe_status mx_fc1_enqueue(int activation, int wbits, const void* x, const void* x_sf,
+                          const int32_t* p2e, int top_k, const void* w1, const void* w1_sf, int L,
+                          const int32_t* offs, int64_t R, int H, int I, const float* limits,
+                          void* act, void* act_sf, hipStream_t st);
+moe_status mx_fc2_enqueue(int wbits, const void* act, const void* act_sf, const void* w2,
+                          const void* w2_sf, int L, const int32_t* offs, int64_t R, int H, int I,
+                          void* y, hipStream_t st);
 
 int device_cu_count() {
   static int cached[64] = {0};
@@ -47,6 +47,10 @@ int device_cu_count() {
 }
 
 namespace {
+// block-scaled weight formats and their element width in bits
+inline bool is_mx(int32_t wfmt) { return wfmt == MOE_WFMT_MXFP4 || wfmt == MOE_WFMT_MXFP8; }
+inline int mx_wbits(int32_t wfmt) { return wfmt == MOE_WFMT_MXFP8 ? 8 : 4; }
+
 constexpr int EPI_STORE = 0, EPI_SWIGLU = 1, EPI_SWIGLU_STEP = 2, EPI_FUSED = 3;
 constexpr int64_t U32_ELEMS = (int64_t)1 << 32;
 
@@ -82,7 +86,7 @@ FfnLayout ffn_layout(const moe_ffn_desc* d) {
   l.e2p = o;     o += align_up((size_t)R * 4, 256);
   l.p2e = o;     o += align_up((size_t)R * 4, 256);
   l.n_local = o; o += 256;
-  const bool mx = d->weight_format == MOE_WFMT_MXFP4;
+  const bool mx = is_mx(d->weight_format);
   l.act = o;     o += align_up((size_t)R * d->I * (mx ? 1 : 2), 256);
   l.act_sf = o;  o += mx ? align_up((size_t)R * (d->I / 32), 256) : 0;
   l.y = o;
@@ -165,8 +169,8 @@ static moe_status check_ffn(const moe_ffn_desc* d) {
   if (d->activation != MOE_ACT_SWIGLU && d->activation != MOE_ACT_SWIGLU_STEP) return MOE_ERR_DTYPE;
   if (d->finalize_mode < MOE_FINALIZE_DETERMINISTIC || d->finalize_mode > MOE_FINALIZE_NONE)
     return MOE_ERR_DTYPE;
-  if (d->weight_format != MOE_WFMT_BF16 && d->weight_format != MOE_WFMT_MXFP4) return MOE_ERR_DTYPE;
-  if (d->weight_format == MOE_WFMT_MXFP4) {
+  if (d->weight_format != MOE_WFMT_BF16 && !is_mx(d->weight_format)) return MOE_ERR_DTYPE;
+  if (is_mx(d->weight_format)) {
     if (d->H % 128 || d->I % 128) return MOE_ERR_SHAPE;
     if (d->finalize_mode == MOE_FINALIZE_FUSED) return MOE_ERR_UNSUPPORTED;
   }
@@ -219,7 +223,7 @@ extern "C" moe_status moe_ffn_forward(const moe_ffn_desc* d, const moe_ffn_tenso
   if (d->T == 0) return MOE_OK;
   const int32_t L = d->num_local_experts > 0 ? d->num_local_experts : d->num_experts;
   const int fm = d->finalize_mode;
-  const bool mx = d->weight_format == MOE_WFMT_MXFP4;
+  const bool mx = is_mx(d->weight_format);
   if (!t->x || !t->topk_ids || !t->topk_weights || !t->w1 || !t->w2) return MOE_ERR_NULL;
   if (mx && (!t->x_sf || !t->w1_sf || !t->w2_sf)) return MOE_ERR_NULL;
   if (fm != MOE_FINALIZE_NONE && !t->out) return MOE_ERR_NULL;
@@ -249,10 +253,11 @@ extern "C" moe_status moe_ffn_forward(const moe_ffn_desc* d, const moe_ffn_tenso
   if (s != MOE_OK) return s;
   if (mx) {
     const int64_t R = d->T * d->top_k;
-    s = mx_fc1_enqueue(d->activation, t->x, t->x_sf, p2e, d->top_k, t->w1, t->w1_sf, L, offs, R, H,
-                       d->I, t->clamp_limit, act, w + l.act_sf, st);
+    const int wb = mx_wbits(d->weight_format);
+    s = mx_fc1_enqueue(d->activation, wb, t->x, t->x_sf, p2e, d->top_k, t->w1, t->w1_sf, L, offs,
+                       R, H, d->I, t->clamp_limit, act, w + l.act_sf, st);
     if (s != MOE_OK) return s;
-    s = mx_fc2_enqueue(act, w + l.act_sf, t->w2, t->w2_sf, L, offs, R, H, d->I, y, st);
+    s = mx_fc2_enqueue(wb, act, w + l.act_sf, t->w2, t->w2_sf, L, offs, R, H, d->I, y, st);
   } else {
     s = fc1_enqueue(d, t->x, t->w1, t->clamp_limit, offs, p2e, act, st, split_ws, split_cnt);
     if (s != MOE_OK) return s;
@@ -269,13 +274,14 @@ extern "C" moe_status moe_fc1_mx(const moe_ffn_desc* d, const void* x, const voi
                                  void* stream) {
   moe_status s = check_ffn(d);
   if (s != MOE_OK) return s;
-  if (d->weight_format != MOE_WFMT_MXFP4) return MOE_ERR_DTYPE;
+  if (!is_mx(d->weight_format)) return MOE_ERR_DTYPE;
   if (d->T == 0) return MOE_OK;
   if (!x || !x_sf || !w1 || !w1_sf || !offs || !p2e || !act || !act_sf) return MOE_ERR_NULL;
   if (!aligned16(x) || !aligned16(w1) || !aligned16(act) || !aligned16(x_sf) || !aligned16(w1_sf))
     return MOE_ERR_ALIGN;
   const int32_t L = d->num_local_experts > 0 ? d->num_local_experts : d->num_experts;
-  return mx_fc1_enqueue(d->activation, x, x_sf, p2e, d->top_k, w1, w1_sf, L, offs,
+  return mx_fc1_enqueue(d->activation, mx_wbits(d->weight_format), x, x_sf, p2e, d->top_k, w1,
+                        w1_sf, L, offs,
                         d->T * d->top_k, d->H, d->I, clamp_limit, act, act_sf, as_stream(stream));
 }
 
@@ -284,12 +290,12 @@ extern "C" moe_status moe_fc2_mx(const moe_ffn_desc* d, const void* act, const v
                                  void* stream) {
   moe_status s = check_ffn(d);
   if (s != MOE_OK) return s;
-  if (d->weight_format != MOE_WFMT_MXFP4) return MOE_ERR_DTYPE;
+  if (!is_mx(d->weight_format)) return MOE_ERR_DTYPE;
   if (d->T == 0) return MOE_OK;
   if (!act || !act_sf || !w2 || !w2_sf || !offs || !y) return MOE_ERR_NULL;
   if (!aligned16(act) || !aligned16(w2) || !aligned16(y) || !aligned16(w2_sf)) return MOE_ERR_ALIGN;
   const int32_t L = d->num_local_experts > 0 ? d->num_local_experts : d->num_experts;
-  return mx_fc2_enqueue(act, act_sf, w2, w2_sf, L, offs, d->T * d->top_k, d->H, d->I, y,
+  return mx_fc2_enqueue(mx_wbits(d->weight_format), act, act_sf, w2, w2_sf, L, offs, d->T * d->top_k, d->H, d->I, y,
                         as_stream(stream));
 }
 

@@ -1,5 +1,7 @@
-// MXFP4-weight x MXFP8-activation grouped GEMMs (FC1 with the activation and the
+// MX-weight x MXFP8-activation grouped GEMMs (FC1 with the activation and the
 // MXFP8 requantization in its epilogue, FC2 to bf16 rows) on gfx950 scaled MFMA.
+// Two weight families: MXFP4 (e2m1 pairs) and MXFP8 (e4m3 bytes), both with one
+// UE8M0 scale per 32 values along the contraction.
 //
 // W4A8 page ("flashinfer.fused_moe.cake / cake_cute (MXFP4 SiTU routed MoE)"),
 // "Inputs": activations are float8_e4m3fn with one UE8M0 scale per 32 values
@@ -13,14 +15,15 @@
 // e4m3 operand in the B slot supplies column l%32 with bytes 0..15 at
 // k = 16*(l/32) + b and bytes 16..31 at k = 32 + 16*(l/32) + (b-16); the UE8M0
 // scale of 32-block kb of a row/column comes from byte 0 of the scale VGPR of
-// lane (row + 32*kb); D uses the usual 32x32 layout.
+// lane (row + 32*kb); D uses the usual 32x32 layout. An e4m3 operand in the A slot
+// (cbsz=0, MXFP8 weights) packs its bytes exactly as in the B slot.
 //
 // Tile: 256 weight rows x 256 activation rows x 128 contraction per stage, 4 waves
 // of 128 x 128 (4 x 4 accumulators), weights as the A operand so a lane holds 4
 // consecutive output columns. LDS per stage: activation codes [256][8 x 16 B],
-// weight codes [256][4 x 16 B], and both operands' 4 scale bytes per row; two
-// stages (100 KB). Tiles are dealt out as in the bf16 kernels (device-counted,
-// XCD-balanced, expert-major).
+// weight codes [256][4 x 16 B] (MXFP4) or [256][8 x 16 B] (MXFP8), and both
+// operands' 4 scale bytes per row; two stages (100 KB / 132 KB). Tiles are dealt
+// out as in the bf16 kernels (device-counted, XCD-balanced, expert-major).
 #include "common.h"
 
 namespace moe {
@@ -30,8 +33,14 @@ constexpr int MTB = 256;          // tile rows on each side
 constexpr int MTK = 128;          // contraction per stage
 constexpr int MNT = 256;          // threads
 constexpr int XT_U4 = MTB * MTK / 16;        // 2048 uint4: activation codes
-constexpr int WT_U4 = MTB * MTK / 2 / 16;    // 1024 uint4: weight codes
-constexpr int STAGE_U4 = XT_U4 + WT_U4 + 2 * MTB / 4;  // + 2 x 256 u32 scales
+
+// Weight element widths: MXFP4 (e2m1, 4 bits) or MXFP8 (e4m3, 8 bits).
+constexpr int MX_W4 = 4, MX_W8 = 8;
+// 16-byte chunks per weight row and stage, and the stage size in uint4
+template <int WB> constexpr int wch() { return MTK * WB / 8 / 16; }
+template <int WB> constexpr int stage_u4() { return XT_U4 + MTB * wch<WB>() + 2 * MTB / 4; }
+// scaled-MFMA format code of the weight (A-slot) operand
+template <int WB> constexpr int a_fmt() { return WB == MX_W4 ? 4 : 0; }
 
 enum MxEpi { MX_FC1_SWIGLU = 0, MX_FC1_STEP = 1, MX_FC2 = 2 };
 
@@ -42,7 +51,7 @@ struct MxArgs {
   const uint8_t* A_sf;     // [rows][K/32]
   const int32_t* a_gather; // optional: row p reads A row a_gather[p] / a_div
   int a_div;
-  const uint8_t* B;        // weight codes [E][NB][K/2]
+  const uint8_t* B;        // weight codes [E][NB][K/2] (MXFP4) or [E][NB][K] (MXFP8)
   const uint8_t* B_sf;     // [E][NB][K/32]
   const int32_t* ends;
   int E, m_cap, NB, N, K, n_tiles;
@@ -67,8 +76,10 @@ __device__ __forceinline__ uint32_t ue8m0_round_up_448(float amax) {
   return (uint32_t)c;
 }
 
-template <int EPI>
+template <int EPI, int WB>
 __global__ __launch_bounds__(MNT, 1) void k_gemm_mx(MxArgs a) {
+  constexpr int WCH = wch<WB>(), WT_U4 = MTB * WCH, STAGE_U4 = stage_u4<WB>();
+  constexpr int WLD = WT_U4 / MNT;   // weight loads per thread and stage (4 or 8)
   __shared__ uint4 smem[2 * STAGE_U4];
   int e, m0, mend, nt;
   if (!deal_tile<MTB>(a.ends, a.E, a.m_cap, a.n_tiles, e, m0, mend, nt)) return;
@@ -79,9 +90,11 @@ __global__ __launch_bounds__(MNT, 1) void k_gemm_mx(MxArgs a) {
   const bool fc1 = EPI != MX_FC2;
 
   // global -> register staging: activation codes rows (tid>>3)+32j, chunk tid&7;
-  // weight codes rows (tid>>2)+64j, chunk tid&3; scales: row tid of each operand
-  const int xr = tid >> 3, xc = tid & 7, wr = tid >> 2, wc = tid & 3;
-  uint32_t xoff[8], woff[4];
+  // weight codes rows tid/WCH + (256/WCH)j, chunk tid%WCH; scales: row tid of each
+  // operand
+  const int xr = tid >> 3, xc = tid & 7, wr = tid / WCH, wc = tid % WCH;
+  const uint32_t kw = (uint32_t)K * WB / 8;   // weight bytes per row
+  uint32_t xoff[8], woff[WLD];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     int p = m0 + xr + 32 * j;
@@ -98,10 +111,10 @@ __global__ __launch_bounds__(MNT, 1) void k_gemm_mx(MxArgs a) {
     const int r = nt * MTB + R;
     return r < a.NB ? r : a.NB - 1;
   };
-  const uint8_t* Bb = a.B + (int64_t)e * a.NB * (K / 2);
+  const uint8_t* Bb = a.B + (int64_t)e * a.NB * kw;
   const uint8_t* Bs = a.B_sf + (int64_t)e * a.NB * ks;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) woff[j] = (uint32_t)wrow_of(wr + 64 * j) * (uint32_t)(K / 2) + wc * 16;
+  for (int j = 0; j < WLD; ++j) woff[j] = (uint32_t)wrow_of(wr + (MTB / WLD) * j) * kw + wc * 16;
   uint32_t xsoff, wsoff;
   {
     int p = m0 + tid;
@@ -110,17 +123,20 @@ __global__ __launch_bounds__(MNT, 1) void k_gemm_mx(MxArgs a) {
     xsoff = (uint32_t)src * (uint32_t)ks;
     wsoff = (uint32_t)wrow_of(tid) * (uint32_t)ks;
   }
-  u32x4 rx[8], rw[4];
+  u32x4 rx[8], rw[WLD];
   uint32_t rxs, rws;
   auto gload = [&](int kt) {
     const int kb = kt * MTK;
 #pragma unroll
     for (int j = 0; j < 8; ++j) rx[j] = *reinterpret_cast<const u32x4*>(a.A + xoff[j] + kb);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) rw[j] = *reinterpret_cast<const u32x4*>(Bb + woff[j] + kb / 2);
+    for (int j = 0; j < WLD; ++j) rw[j] = *reinterpret_cast<const u32x4*>(Bb + woff[j] + kb * WB / 8);
     rxs = *reinterpret_cast<const uint32_t*>(a.A_sf + xsoff + kb / 32);
     rws = *reinterpret_cast<const uint32_t*>(Bs + wsoff + kb / 32);
   };
+  // weight chunk swizzle: 64-byte rows (MXFP4) by (r >> 2) & 3, 128-byte rows by
+  // (r >> 1) & 7, so that each 16-lane group of a fragment read hits 64 distinct banks
+  auto wswz = [](int r) { return WCH == 4 ? (r >> 2) & 3 : (r >> 1) & 7; };
   auto sstore = [&](int s) {
     u32x4* X = reinterpret_cast<u32x4*>(smem + s * STAGE_U4);
     u32x4* W = X + XT_U4;
@@ -132,9 +148,9 @@ __global__ __launch_bounds__(MNT, 1) void k_gemm_mx(MxArgs a) {
       X[r * 8 + (xc ^ ((r >> 1) & 7))] = rx[j];
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int r = wr + 64 * j;
-      W[r * 4 + (wc ^ ((r >> 2) & 3))] = rw[j];
+    for (int j = 0; j < WLD; ++j) {
+      const int r = wr + (MTB / WLD) * j;
+      W[r * WCH + (wc ^ wswz(r))] = rw[j];
     }
     XS[tid] = rxs;
     WS[tid] = rws;
@@ -171,8 +187,14 @@ __global__ __launch_bounds__(MNT, 1) void k_gemm_mx(MxArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = wn * 128 + i * 32 + rsel;
-        const uint4 v = W[r * 4 + ((2 * kk + g) ^ ((r >> 2) & 3))];
-        wq[i] = v8i{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+        if (WB == MX_W4) {
+          const uint4 v = W[r * 4 + ((2 * kk + g) ^ wswz(r))];
+          wq[i] = v8i{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+        } else {
+          const uint4 lo = W[r * 8 + ((4 * kk + g) ^ wswz(r))];
+          const uint4 hi = W[r * 8 + ((4 * kk + 2 + g) ^ wswz(r))];
+          wq[i] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        }
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -193,28 +215,32 @@ __global__ __launch_bounds__(MNT, 1) void k_gemm_mx(MxArgs a) {
 #pragma unroll
         for (int j = 0; j < 4; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-              wf[kk][i], xf[kk][j], acc[i][j], 4, 0, 0, (int)((wsr[i] >> sh) & 0xFF), 0,
+              wf[kk][i], xf[kk][j], acc[i][j], a_fmt<WB>(), 0, 0, (int)((wsr[i] >> sh) & 0xFF), 0,
               (int)((xsr[j] >> sh) & 0xFF));
       if (kk == 1) sstore(s ^ 1);
     }
     // issue order (0x008 MFMA, 0x100 LDS read, 0x200 LDS write, 0x020 global load):
-    // the scale reads (paired into 4) and step 0's 12 fragment reads first, then
-    // step 0's 16 MFMAs with step 1's 12 fragment reads and the 14 global loads
-    // between them, then step 1's 16 MFMAs with the 13 LDS stores (the two scale
-    // words go out as one paired store)
-    __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
-    for (int r = 0; r < 12; ++r) {
+    // the scale reads (paired into 4) and step 0's NRD fragment reads first, then
+    // step 0's 16 MFMAs with step 1's NRD fragment reads and the NGL global loads
+    // between them, then step 1's 16 MFMAs with the NST LDS stores (the two scale
+    // words go out as one paired store). MXFP4: NRD 12, NGL 14, NST 13; MXFP8: 16,
+    // 18, 17.
+    constexpr int NRD = 8 + 4 * (WCH / 4), NGL = 8 + WLD + 2, NST = 8 + WLD + 1;
+    __builtin_amdgcn_sched_group_barrier(0x100, 4 + NRD, 0);
+    for (int r = 0; r < NRD; ++r) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-    __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
-    for (int r = 0; r < 13; ++r) {
+    if (16 - NRD > 0) __builtin_amdgcn_sched_group_barrier(0x008, 16 - NRD, 0);
+    __builtin_amdgcn_sched_group_barrier(0x020, NGL - NRD, 0);
+    constexpr int NPAIR = NST < 16 ? NST : 16;
+    for (int r = 0; r < NPAIR; ++r) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
+    if (16 - NPAIR > 0) __builtin_amdgcn_sched_group_barrier(0x008, 16 - NPAIR, 0);
+    if (NST - NPAIR > 0) __builtin_amdgcn_sched_group_barrier(0x200, NST - NPAIR, 0);
     __syncthreads();
   }
 
@@ -280,9 +306,9 @@ __global__ __launch_bounds__(MNT, 1) void k_gemm_mx(MxArgs a) {
 // 32 activation rows (one MFMA column block) by 64 weight rows (FC1: 32 up rows and
 // the 32 gate rows of the same output columns, i.e. one requantization block; FC2:
 // 64 output columns); the 4 waves split the contraction and meet in LDS at the end.
-// A wave streams its 64 rows x (its share of K) in stages of 4 steps of 64 values
-// (128 bytes per row): each load instruction takes 8 whole 128-byte lines (lane l:
-// row 8j + l / 8, 16-byte chunk l % 8). Weight stages are loaded two ahead into
+// A wave streams its 64 rows x (its share of K) in stages of 128 weight bytes per row
+// (4 steps of 64 values for MXFP4, 2 for MXFP8): each load instruction takes 8 whole
+// 128-byte lines (lane l: row 8j + l / 8, 16-byte chunk l % 8). Weight stages are loaded two ahead into
 // registers and pass through a private LDS slot that turns them into MFMA fragments
 // (chunks swizzled by (row >> 1) & 7; one slot is enough because a wave's LDS operations
 // run in order). The weight scales of the wave's range are read into LDS once at the
@@ -291,18 +317,20 @@ __global__ __launch_bounds__(MNT, 1) void k_gemm_mx(MxArgs a) {
 // blocks share a CU.
 constexpr int STB = 32;         // activation rows per tile
 constexpr int SCW = 16;         // weight-scale dwords kept per row and wave
-constexpr int SMAX_STAGES = 8;  // stages per wave that they cover (2 dwords each)
+constexpr int SMAX_K = 2048;    // contraction per wave that they cover (one byte per 32)
 
+template <int NS>
 struct MxAct {
-  u32x4 xl[4], xh[4];
-  uint32_t sx[4];
+  u32x4 xl[NS], xh[NS];
+  uint32_t sx[NS];
 };
 struct MxW {
   u32x4 v[8];
 };
 
-template <int EPI>
+template <int EPI, int WB>
 __global__ __launch_bounds__(256, 2) void k_gemm_mx_stream(MxArgs a) {
+  constexpr int NS = 128 * 8 / WB / 64;   // 64-value steps per 128-byte stage: 4 or 2
   __shared__ u32x4 ring[4][512];              // [wave][64 rows x 8 chunks]
   __shared__ uint32_t scl[4][64][SCW];        // [wave][tile row][scale dwords]
   int e, m0, mend, nt;
@@ -312,7 +340,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_mx_stream(MxArgs a) {
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane & 31, g = lane >> 5;
   const int K = a.K, ks = K >> 5;
-  const uint32_t kh = (uint32_t)(K >> 1);
+  const uint32_t kh = (uint32_t)K * WB / 8;   // weight bytes per row
   // weight row (within the expert) of tile row R in [0, 64)
   auto wrow_of = [&](int R) -> int {
     if (fc1) return (R >> 5) * a.I + min(nt * 32 + (R & 31), a.I - 1);
@@ -321,19 +349,20 @@ __global__ __launch_bounds__(256, 2) void k_gemm_mx_stream(MxArgs a) {
   const int64_t eb = (int64_t)e * a.NB;
   const uint8_t* Bw = a.B + eb * kh;
   const uint8_t* Bs = a.B_sf + eb * ks;
-  // stages of 4 steps of 64 values (K is a multiple of 256); wave w takes stages
+  // stages of NS steps of 64 values (K is a multiple of 64 NS); wave w takes stages
   // [s0, s0 + nst)
-  const int nstg = K >> 8;
+  const int nstg = K / (64 * NS);
   const int s0 = wid * nstg / 4;
   const int nst = (wid + 1) * nstg / 4 - s0;
 
-  // weight scales of this wave's stages: 8 bytes per stage and row, from byte 8 * s0
+  // weight scales of this wave's stages: 2 NS bytes per stage and row, from byte
+  // 2 NS s0
   uint32_t sreg[SCW];
   {
     const uint32_t* srow =
-        reinterpret_cast<const uint32_t*>(Bs + (int64_t)wrow_of(lane) * ks + 8 * s0);
+        reinterpret_cast<const uint32_t*>(Bs + (int64_t)wrow_of(lane) * ks + 2 * NS * s0);
 #pragma unroll
-    for (int d = 0; d < SCW; ++d) sreg[d] = d < 2 * nst ? srow[d] : 0u;
+    for (int d = 0; d < SCW; ++d) sreg[d] = d < NS / 2 * nst ? srow[d] : 0u;
   }
 
   // 32-bit per-lane offsets from stage-uniform bases. Weights: instruction j loads
@@ -357,12 +386,12 @@ __global__ __launch_bounds__(256, 2) void k_gemm_mx_stream(MxArgs a) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) w.v[j] = *reinterpret_cast<const u32x4*>(base + voff[j]);
   };
-  auto issue_a = [&](int q, MxAct& act) {
+  auto issue_a = [&](int q, MxAct<NS>& act) {
     const int st = s0 + min(q, nst - 1);
-    const uint8_t* xb = a.A + 256 * st;
-    const uint8_t* sbp = a.A_sf + 8 * st;
+    const uint8_t* xb = a.A + 64 * NS * st;
+    const uint8_t* sbp = a.A_sf + 2 * NS * st;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
+    for (int s = 0; s < NS; ++s) {
       act.xl[s] = *reinterpret_cast<const u32x4*>(xb + xoff + 64 * s);
       act.xh[s] = *reinterpret_cast<const u32x4*>(xb + xoff + 64 * s + 32);
       act.sx[s] = sbp[xsoff + 2 * s];
@@ -378,22 +407,31 @@ __global__ __launch_bounds__(256, 2) void k_gemm_mx_stream(MxArgs a) {
   for (int q = 0; q < 16; ++q) acc0[q] = acc1[q] = 0.f;
   const uint8_t* sc0 = reinterpret_cast<const uint8_t*>(&scl[wid][r][0]);
   const uint8_t* sc1 = reinterpret_cast<const uint8_t*>(&scl[wid][32 + r][0]);
-  auto compute = [&](int q, const MxAct& act) {
+  // A fragment of weight row R for step s: MXFP4 one 16-byte chunk (2s + g), MXFP8
+  // the chunks 4s + g and 4s + 2 + g (k = 16g + b and 32 + 16g + b of the step)
+  auto wfrag = [&](const u32x4* W, int R, int s) -> v8i {
+    const int sw = (R >> 1) & 7;
+    if (WB == MX_W4) {
+      const u32x4 v = W[R * 8 + ((2 * s + g) ^ sw)];
+      return v8i{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+    }
+    const u32x4 lo = W[R * 8 + ((4 * s + g) ^ sw)];
+    const u32x4 hi = W[R * 8 + ((4 * s + 2 + g) ^ sw)];
+    return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+  };
+  auto compute = [&](int q, const MxAct<NS>& act) {
     const u32x4* W = &ring[wid][0];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int c = (2 * s + g) ^ ((r >> 1) & 7);
-      const u32x4 w0 = W[r * 8 + c];
-      const u32x4 w1 = W[(32 + r) * 8 + c];
-      const int bi = 8 * q + 2 * s + g;
-      const v8i f0{(int)w0.x, (int)w0.y, (int)w0.z, (int)w0.w, 0, 0, 0, 0};
-      const v8i f1{(int)w1.x, (int)w1.y, (int)w1.z, (int)w1.w, 0, 0, 0, 0};
+    for (int s = 0; s < NS; ++s) {
+      const int bi = 2 * NS * q + 2 * s + g;
+      const v8i f0 = wfrag(W, r, s);
+      const v8i f1 = wfrag(W, 32 + r, s);
       const v8i x{(int)act.xl[s].x, (int)act.xl[s].y, (int)act.xl[s].z, (int)act.xl[s].w,
                   (int)act.xh[s].x, (int)act.xh[s].y, (int)act.xh[s].z, (int)act.xh[s].w};
-      acc0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f0, x, acc0, 4, 0, 0, (int)sc0[bi], 0,
-                                                             (int)act.sx[s]);
-      acc1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f1, x, acc1, 4, 0, 0, (int)sc1[bi], 0,
-                                                             (int)act.sx[s]);
+      acc0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f0, x, acc0, a_fmt<WB>(), 0, 0,
+                                                             (int)sc0[bi], 0, (int)act.sx[s]);
+      acc1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f1, x, acc1, a_fmt<WB>(), 0, 0,
+                                                             (int)sc1[bi], 0, (int)act.sx[s]);
     }
   };
 
@@ -401,7 +439,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_mx_stream(MxArgs a) {
     // issue order W(0) A(0) W(1), then per stage q: W(q + 2) A(q + 1); stage q's
     // MFMAs wait for A(q), by which time W(q + 1) is in too and goes to LDS after them
     MxW W0, W1;
-    MxAct A0, A1;
+    MxAct<NS> A0, A1;
     issue_w(0, W0);
     issue_a(0, A0);
     issue_w(1, W1);
@@ -494,11 +532,13 @@ __global__ __launch_bounds__(256, 2) void k_gemm_mx_stream(MxArgs a) {
 
 // The decode kernel takes over while the experts hold few rows on average: there
 // the 256-row tiles would be mostly padding and too few to fill the chip. Measured
-// crossover (H=7168, I=2048, 64 experts): about 32 rows per expert for FC1 and 24
-// for FC2 (its contraction is 3.5x shorter, so its blocks live shorter).
-inline bool mx_use_small(int64_t R, int L, int K, int NB, int64_t act_rows, int rows_per_expert) {
-  return R <= (int64_t)rows_per_expert * L && K % 256 == 0 && (K >> 8) <= 4 * SMAX_STAGES &&
-         (int64_t)NB * (K >> 1) < (1LL << 31) && act_rows * K < (1LL << 31);
+// crossover (H=7168, I=2048, 64 experts, MXFP4): about 32 rows per expert for FC1
+// and 24 for FC2 (its contraction is 3.5x shorter, so its blocks live shorter).
+inline bool mx_use_small(int64_t R, int L, int K, int NB, int64_t act_rows, int rows_per_expert,
+                         int wb) {
+  const int stage_k = 128 * 8 / wb;
+  return R <= (int64_t)rows_per_expert * L && K % stage_k == 0 && K <= 4 * SMAX_K &&
+         (int64_t)NB * K * wb / 8 < (1LL << 31) && act_rows * K < (1LL << 31);
 }
 
 // Row tiles of tm rows over L experts holding R rows in all: at most one partial
@@ -507,12 +547,30 @@ inline int64_t mx_row_tiles(int64_t R, int L, int tm) { return R / tm + (R < L ?
 
 }  // namespace
 
-// FC1: act (MXFP8) = requant(activation(x[p2e[p]/k] @ w1[e].T)) for permuted rows p.
-moe_status mx_fc1_enqueue(int activation, const void* x, const void* x_sf, const int32_t* p2e,
-                          int top_k, const void* w1, const void* w1_sf, int L, const int32_t* offs,
-                          int64_t R, int H, int I, const float* limits, void* act, void* act_sf,
-                          hipStream_t st) {
+template <int EPI, int WB>
+moe_status mx_launch(const MxArgs& a, bool small, int64_t tiles, hipStream_t st) {
+  const int grid = (int)((tiles + 7) / 8 * 8);
+  if (small)
+    k_gemm_mx_stream<EPI, WB><<<grid, 256, 0, st>>>(a);
+  else
+    k_gemm_mx<EPI, WB><<<grid, MNT, 0, st>>>(a);
+  return launch_status();
+}
+
+template <int EPI>
+moe_status mx_launch_w(const MxArgs& a, int wb, bool small, int64_t tiles, hipStream_t st) {
+  return wb == MX_W8 ? mx_launch<EPI, MX_W8>(a, small, tiles, st)
+                     : mx_launch<EPI, MX_W4>(a, small, tiles, st);
+}
+
+// FC1: act (MXFP8) = requant(activation(x[p2e[p]/k] @ w1[e].T)) for permuted rows p;
+// w1 MXFP4 (wbits 4) or MXFP8 (wbits 8).
+moe_status mx_fc1_enqueue(int activation, int wbits, const void* x, const void* x_sf,
+                          const int32_t* p2e, int top_k, const void* w1, const void* w1_sf, int L,
+                          const int32_t* offs, int64_t R, int H, int I, const float* limits,
+                          void* act, void* act_sf, hipStream_t st) {
   if (R == 0) return MOE_OK;
+  if (wbits != MX_W4 && wbits != MX_W8) return MOE_ERR_DTYPE;
   MxArgs a{};
   a.A = reinterpret_cast<const uint8_t*>(x);
   a.A_sf = reinterpret_cast<const uint8_t*>(x_sf);
@@ -531,31 +589,19 @@ moe_status mx_fc1_enqueue(int activation, const void* x, const void* x_sf, const
   a.I = I;
   a.limits = limits;
   a.def_limit = 7.0f;
-  if (mx_use_small(R, L, H, 2 * I, R, 32)) {
-    a.n_tiles = I / 32;
-    const int64_t tiles = mx_row_tiles(R, L, STB) * a.n_tiles;
-    const int grid = (int)((tiles + 7) / 8 * 8);
-    if (activation == MOE_ACT_SWIGLU_STEP)
-      k_gemm_mx_stream<MX_FC1_STEP><<<grid, 256, 0, st>>>(a);
-    else
-      k_gemm_mx_stream<MX_FC1_SWIGLU><<<grid, 256, 0, st>>>(a);
-    return launch_status();
-  }
-  a.n_tiles = (I + 127) / 128;
-  const int64_t tiles = mx_row_tiles(R, L, MTB) * a.n_tiles;
-  const int grid = (int)((tiles + 7) / 8 * 8);
-  if (activation == MOE_ACT_SWIGLU_STEP)
-    k_gemm_mx<MX_FC1_STEP><<<grid, MNT, 0, st>>>(a);
-  else
-    k_gemm_mx<MX_FC1_SWIGLU><<<grid, MNT, 0, st>>>(a);
-  return launch_status();
+  const bool small = mx_use_small(R, L, H, 2 * I, R, 32, wbits);
+  a.n_tiles = small ? I / 32 : (I + 127) / 128;
+  const int64_t tiles = mx_row_tiles(R, L, small ? STB : MTB) * a.n_tiles;
+  if (activation == MOE_ACT_SWIGLU_STEP) return mx_launch_w<MX_FC1_STEP>(a, wbits, small, tiles, st);
+  return mx_launch_w<MX_FC1_SWIGLU>(a, wbits, small, tiles, st);
 }
 
-// FC2: y[p] (bf16) = act[p] @ w2[e].T with MXFP8 act and MXFP4 w2.
-moe_status mx_fc2_enqueue(const void* act, const void* act_sf, const void* w2, const void* w2_sf,
-                          int L, const int32_t* offs, int64_t R, int H, int I, void* y,
-                          hipStream_t st) {
+// FC2: y[p] (bf16) = act[p] @ w2[e].T with MXFP8 act and MXFP4 / MXFP8 w2.
+moe_status mx_fc2_enqueue(int wbits, const void* act, const void* act_sf, const void* w2,
+                          const void* w2_sf, int L, const int32_t* offs, int64_t R, int H, int I,
+                          void* y, hipStream_t st) {
   if (R == 0) return MOE_OK;
+  if (wbits != MX_W4 && wbits != MX_W8) return MOE_ERR_DTYPE;
   MxArgs a{};
   a.A = reinterpret_cast<const uint8_t*>(act);
   a.A_sf = reinterpret_cast<const uint8_t*>(act_sf);
@@ -571,18 +617,10 @@ moe_status mx_fc2_enqueue(const void* act, const void* act_sf, const void* w2, c
   a.K = I;
   a.C = reinterpret_cast<uint16_t*>(y);
   a.ldc = H;
-  if (mx_use_small(R, L, I, H, R, 24)) {
-    a.n_tiles = (H + 63) / 64;
-    const int64_t tiles = mx_row_tiles(R, L, STB) * a.n_tiles;
-    const int grid = (int)((tiles + 7) / 8 * 8);
-    k_gemm_mx_stream<MX_FC2><<<grid, 256, 0, st>>>(a);
-    return launch_status();
-  }
-  a.n_tiles = (H + MTB - 1) / MTB;
-  const int64_t tiles = mx_row_tiles(R, L, MTB) * a.n_tiles;
-  const int grid = (int)((tiles + 7) / 8 * 8);
-  k_gemm_mx<MX_FC2><<<grid, MNT, 0, st>>>(a);
-  return launch_status();
+  const bool small = mx_use_small(R, L, I, H, R, 24, wbits);
+  a.n_tiles = small ? (H + 63) / 64 : (H + MTB - 1) / MTB;
+  const int64_t tiles = mx_row_tiles(R, L, small ? STB : MTB) * a.n_tiles;
+  return mx_launch_w<MX_FC2>(a, wbits, small, tiles, st);
 }
 
 }  // namespace moe

@@ -284,11 +284,12 @@ def mx_quant_e2m1(a: np.ndarray, block: int = 32):
 
 @dataclass
 class W4A8Case:
-    """MXFP8-activation / MXFP4-weight MoE case (numpy arrays on the host).
+    """MXFP8-activation / MX-weight MoE case (numpy arrays on the host).
 
     x, x_sf:   uint8 [T, H] e4m3fn codes, uint8 [T, H/32] UE8M0
-    w1, w1_sf: uint8 [L, 2I, H/2] packed e2m1 ([up | gate] rows), uint8 [L, 2I, H/32]
-    w2, w2_sf: uint8 [L, H, I/2], uint8 [L, H, I/32]
+    w1, w1_sf: uint8 [L, 2I, H/2] packed e2m1 (wfmt "mxfp4") or [L, 2I, H] e4m3fn codes
+               (wfmt "mxfp8"), [up | gate] rows; uint8 [L, 2I, H/32]
+    w2, w2_sf: uint8 [L, H, I/2] or [L, H, I], uint8 [L, H, I/32]
     """
     T: int
     H: int
@@ -302,6 +303,7 @@ class W4A8Case:
     w1_sf: np.ndarray
     w2: np.ndarray
     w2_sf: np.ndarray
+    wfmt: str = "mxfp4"
 
     @property
     def num_local(self) -> int:
@@ -309,28 +311,33 @@ class W4A8Case:
 
 
 def w4a8_moe(seed: int = 0, T: int = 8192, H: int = 7168, I: int = 2048, E: int = 64,
-             top_k: int = 8, x_scale: float = 1.0) -> W4A8Case:
-    """W4A8 MoE: logits N(0,1); x N(0,1) -> MXFP8; w1 N(0,1/H), w2 N(0,1/I) -> MXFP4,
-    quantized expert by expert (draw order as in moe_case)."""
+             top_k: int = 8, x_scale: float = 1.0, wfmt: str = "mxfp4") -> W4A8Case:
+    """MX MoE: logits N(0,1); x N(0,1) -> MXFP8; w1 N(0,1/H), w2 N(0,1/I) -> MXFP4 (wfmt
+    "mxfp4", the W4A8 case) or MXFP8 (wfmt "mxfp8"), quantized expert by expert (draw
+    order as in moe_case)."""
+    if wfmt not in ("mxfp4", "mxfp8"):
+        raise ValueError(wfmt)
+    quant = mx_quant_e2m1 if wfmt == "mxfp4" else mx_quant_e4m3
+    per = 2 if wfmt == "mxfp4" else 1    # elements per byte
     g = np.random.default_rng(seed)
     logits = route_logits(g, T, E)
     xa = g.standard_normal((T, H), dtype=np.float32)
     if x_scale != 1.0:
         xa *= np.float32(x_scale)
     x, x_sf = mx_quant_e4m3(xa)
-    w1 = np.empty((E, 2 * I, H // 2), np.uint8)
+    w1 = np.empty((E, 2 * I, H // per), np.uint8)
     w1_sf = np.empty((E, 2 * I, H // 32), np.uint8)
-    w2 = np.empty((E, H, I // 2), np.uint8)
+    w2 = np.empty((E, H, I // per), np.uint8)
     w2_sf = np.empty((E, H, I // 32), np.uint8)
 
     def fill(e: int) -> None:
         a = np.random.default_rng([seed, 1, e]).standard_normal((2 * I, H), dtype=np.float32)
         a *= np.float32(math.sqrt(1.0 / H))
-        w1[e], w1_sf[e] = mx_quant_e2m1(a)
+        w1[e], w1_sf[e] = quant(a)
         b = np.random.default_rng([seed, 2, e]).standard_normal((H, I), dtype=np.float32)
         b *= np.float32(math.sqrt(1.0 / I))
-        w2[e], w2_sf[e] = mx_quant_e2m1(b)
+        w2[e], w2_sf[e] = quant(b)
 
     with ThreadPoolExecutor(max_workers=min(_THREADS, E)) as ex:
         list(ex.map(fill, range(E)))
-    return W4A8Case(T, H, I, E, top_k, logits, x, x_sf, w1, w1_sf, w2, w2_sf)
+    return W4A8Case(T, H, I, E, top_k, logits, x, x_sf, w1, w1_sf, w2, w2_sf, wfmt)

@@ -1,4 +1,5 @@
-"""GPU parity: the MXFP4-weight / MXFP8-activation (W4A8) layer against the oracle.
+"""GPU parity: the MX-weight / MXFP8-activation layers against the oracle: MXFP4 weights
+(the W4A8 page's layer) and MXFP8 weights (e4m3 codes, same UE8M0 block-32 scales).
 
 The oracle works on the dequantized operands in float64 and models the one
 lossy step of the method, the MXFP8 requantization of the FC1 output
@@ -19,18 +20,25 @@ DEV = "cuda"
 MX_MAX_ABS, MX_REL = 8e-2, 3e-2
 
 
+WFMTS = ["mxfp4", "mxfp8"]
+
+
+def _deq(wfmt, codes, scales):
+    return (O.mx_dequant_fp4 if wfmt == "mxfp4" else O.mx_dequant_fp8)(codes, scales)
+
+
 class _LazyBank:
     """Expert bank that dequantizes one expert at a time for the oracle (optionally
     remembering the experts it has decoded)."""
 
-    def __init__(self, codes, scales, cache=None):
-        self.codes, self.scales, self.cache = codes, scales, cache
-        self.shape = (codes.shape[0], codes.shape[1], codes.shape[2] * 2)
+    def __init__(self, codes, scales, wfmt, cache=None):
+        self.codes, self.scales, self.wfmt, self.cache = codes, scales, wfmt, cache
+        self.shape = (codes.shape[0], codes.shape[1], scales.shape[2] * 32)
 
     def __getitem__(self, e):
         if self.cache is not None and e in self.cache:
             return self.cache[e]
-        v = O.mx_dequant_fp4(self.codes[e], self.scales[e])
+        v = _deq(self.wfmt, self.codes[e], self.scales[e])
         if self.cache is not None:
             self.cache[e] = v
         return v
@@ -51,8 +59,8 @@ def _oracle(c, ids, w, tokens=None, num_experts=None, local_offset=0, L=None,
     if L is not None:
         w1, w1s = w1[local_offset:local_offset + L], w1s[local_offset:local_offset + L]
         w2, w2s = w2[local_offset:local_offset + L], w2s[local_offset:local_offset + L]
-    return O.moe_forward(O.mx_dequant_fp8(x, xs), ids_n, w_n, _LazyBank(w1, w1s, cache1),
-                         _LazyBank(w2, w2s, cache2),
+    return O.moe_forward(O.mx_dequant_fp8(x, xs), ids_n, w_n, _LazyBank(w1, w1s, c.wfmt, cache1),
+                         _LazyBank(w2, w2s, c.wfmt, cache2),
                          num_experts=num_experts or c.num_experts, local_offset=local_offset,
                          activation_kind=activation, limits=limits, requant=True)
 
@@ -65,31 +73,44 @@ def _run(c, d, ids=None, w=None, **kw):
     return out, ids, w
 
 
+@pytest.mark.parametrize("wfmt", WFMTS)
 @pytest.mark.parametrize("T", [1, 16, 77, 300])
-def test_w4a8_small_layer(T):
-    c = S.w4a8_moe(seed=T, T=T, H=256, I=384, E=8, top_k=2)
+def test_mx_small_layer(T, wfmt):
+    c = S.w4a8_moe(seed=T, T=T, H=256, I=384, E=8, top_k=2, wfmt=wfmt)
     out, ids, w = _run(c, _dev(c))
-    assert_close_bf16(out, _oracle(c, ids, w), MX_MAX_ABS, MX_REL, what=f"w4a8 T={T}")
+    assert_close_bf16(out, _oracle(c, ids, w), MX_MAX_ABS, MX_REL, what=f"{wfmt} T={T}")
 
 
-def test_w4a8_top8_of_64_small_dims():
-    c = S.w4a8_moe(seed=5, T=128, H=512, I=256, E=64, top_k=8)
+@pytest.mark.parametrize("wfmt", WFMTS)
+def test_mx_top8_of_64_small_dims(wfmt):
+    c = S.w4a8_moe(seed=5, T=128, H=512, I=256, E=64, top_k=8, wfmt=wfmt)
     out, ids, w = _run(c, _dev(c))
-    assert_close_bf16(out, _oracle(c, ids, w), MX_MAX_ABS, MX_REL, what="w4a8 E=64 k=8")
+    assert_close_bf16(out, _oracle(c, ids, w), MX_MAX_ABS, MX_REL, what=f"{wfmt} E=64 k=8")
 
 
-def test_w4a8_decode_uneven_contraction_split():
-    """H=1280 and I=768: 5 and 3 stages of 256 contraction values, split unevenly
-    over the decode kernel's 4 waves (one wave of FC2 gets none)."""
-    c = S.w4a8_moe(seed=9, T=5, H=1280, I=768, E=16, top_k=4)
+@pytest.mark.parametrize("wfmt", WFMTS)
+def test_mx_decode_uneven_contraction_split(wfmt):
+    """H=1280 and I=768: 5 and 3 stages of 256 contraction values (MXFP4) or 10 and 6
+    of 128 (MXFP8), split unevenly over the decode kernel's 4 waves (with MXFP4 one
+    wave of FC2 gets none)."""
+    c = S.w4a8_moe(seed=9, T=5, H=1280, I=768, E=16, top_k=4, wfmt=wfmt)
     out, ids, w = _run(c, _dev(c))
-    assert_close_bf16(out, _oracle(c, ids, w), MX_MAX_ABS, MX_REL, what="w4a8 uneven split")
+    assert_close_bf16(out, _oracle(c, ids, w), MX_MAX_ABS, MX_REL, what=f"{wfmt} uneven split")
+
+
+def test_mxfp8_decode_short_contraction():
+    """I=128 with MXFP8 weights: FC2 has one 128-value stage, so three of the decode
+    kernel's four waves get no contraction at all."""
+    c = S.w4a8_moe(seed=10, T=3, H=256, I=128, E=8, top_k=2, wfmt="mxfp8")
+    out, ids, w = _run(c, _dev(c))
+    assert_close_bf16(out, _oracle(c, ids, w), MX_MAX_ABS, MX_REL, what="mxfp8 I=128")
 
 
 # T=200 runs the 256-row tile kernel, T=12 the decode kernel (few rows per expert)
+@pytest.mark.parametrize("wfmt", WFMTS)
 @pytest.mark.parametrize("T", [200, 12])
-def test_w4a8_shard_and_step_activation(T):
-    c = S.w4a8_moe(seed=6, T=T, H=256, I=256, E=16, top_k=4, x_scale=4.0)
+def test_mx_shard_and_step_activation(T, wfmt):
+    c = S.w4a8_moe(seed=6, T=T, H=256, I=256, E=16, top_k=4, x_scale=4.0, wfmt=wfmt)
     d = _dev(c)
     L, off = 6, 5
     lim = torch.tensor(np.linspace(2.0, 4.0, L), dtype=torch.float32, device=DEV)
@@ -100,16 +121,17 @@ def test_w4a8_shard_and_step_activation(T):
                                clamp_limit=lim)
     ref = _oracle(c, ids, w, L=L, local_offset=off, activation="swiglu_step",
                   limits=lim.cpu().numpy())
-    assert_close_bf16(out, ref, MX_MAX_ABS, MX_REL, what="w4a8 shard step")
+    assert_close_bf16(out, ref, MX_MAX_ABS, MX_REL, what=f"{wfmt} shard step")
 
 
+@pytest.mark.parametrize("wfmt", WFMTS)
 @pytest.mark.parametrize("T", [256, 24])
-def test_fc1_requant_matches_oracle_rule(T):
+def test_fc1_requant_matches_oracle_rule(T, wfmt):
     """The fused UE8M0 round-up requantization: scale codes equal the oracle's (rare
     one-step flips allowed where the float32 activations differ in the last bits),
     and the dequantized act stays within half an e4m3 step of the exact activation.
     T=256 runs the 256-row tile kernel, T=24 the decode kernel."""
-    c = S.w4a8_moe(seed=7, T=T, H=512, I=512, E=4, top_k=2)
+    c = S.w4a8_moe(seed=7, T=T, H=512, I=512, E=4, top_k=2, wfmt=wfmt)
     d = _dev(c)
     ids, w = M.moe_route(torch.from_numpy(c.logits).to(DEV), c.top_k)
     srt = M.moe_sort(ids, c.num_experts)
@@ -123,7 +145,7 @@ def test_fc1_requant_matches_oracle_rule(T):
     start = 0
     for e in range(c.num_experts):
         rows = slice(start, int(offs[e]))
-        h = xd[p2e[rows] // c.top_k] @ O.mx_dequant_fp4(c.w1[e], c.w1_sf[e]).T
+        h = xd[p2e[rows] // c.top_k] @ _deq(wfmt, c.w1[e], c.w1_sf[e]).T
         a_ref[rows] = O.activation(h, "swiglu")
         start = int(offs[e])
     vals, codes = O.requant_e4m3(a_ref.astype(np.float32))
@@ -137,8 +159,9 @@ def test_fc1_requant_matches_oracle_rule(T):
     assert np.mean(np.abs(deq - a_ref) <= bound) > 0.999
 
 
-def test_w4a8_zero_tokens_and_replay():
-    c = S.w4a8_moe(seed=8, T=64, H=256, I=256, E=8, top_k=2)
+@pytest.mark.parametrize("wfmt", WFMTS)
+def test_mx_zero_tokens_and_replay(wfmt):
+    c = S.w4a8_moe(seed=8, T=64, H=256, I=256, E=8, top_k=2, wfmt=wfmt)
     d = _dev(c)
     o1, ids, w = _run(c, d)
     o2, _, _ = _run(c, d, ids, w)
@@ -150,22 +173,23 @@ def test_w4a8_zero_tokens_and_replay():
     assert z.shape == (0, 256)
 
 
-@pytest.fixture(scope="module")
-def w4a8_full():
-    return S.w4a8_moe(seed=0, T=8192), {}, {}
+@pytest.fixture(scope="module", params=WFMTS)
+def mx_full(request):
+    return S.w4a8_moe(seed=0, T=8192, wfmt=request.param), {}, {}
 
 
 @pytest.mark.parametrize("T", [1, 16, 128, 8192])
-def test_w4a8_full_shape_sampled(w4a8_full, T):
-    """H=7168, I=2048, 64 experts, top-8 at the decode and prefill token counts;
-    two sampled tokens are checked against the oracle."""
-    full, cache1, cache2 = w4a8_full
+def test_mx_full_shape_sampled(mx_full, T):
+    """H=7168, I=2048, 64 experts, top-8 at the decode and prefill token counts, for
+    both weight families; two sampled tokens are checked against the oracle."""
+    full, cache1, cache2 = mx_full
     c = S.W4A8Case(T, full.H, full.I, full.num_experts, full.top_k, full.logits[:T], full.x[:T],
-                   full.x_sf[:T], full.w1, full.w1_sf, full.w2, full.w2_sf)
+                   full.x_sf[:T], full.w1, full.w1_sf, full.w2, full.w2_sf, full.wfmt)
     out, ids, w = _run(c, _dev(c))
     torch.cuda.synchronize()
     # token 0 routes identically at every T (the logits are shared), so its experts are
     # decoded once; the largest case also checks its last token
     tokens = np.array([0, T - 1]) if T == 8192 else np.array([0])
     ref = _oracle(c, ids, w, tokens=tokens, cache1=cache1, cache2=cache2)
-    assert_close_bf16(to_np(out)[tokens], ref, MX_MAX_ABS, MX_REL, what=f"w4a8 full T={T}")
+    assert_close_bf16(to_np(out)[tokens], ref, MX_MAX_ABS, MX_REL,
+                      what=f"{full.wfmt} full T={T}")
