@@ -275,18 +275,20 @@ def _time(fn, reps=10, warmup=3, flush=None):
 
 
 def _mx_sweep(wfmt, flush, dev):
-    """Block-scaled layer (MXFP8 activations, MXFP4 or MXFP8 weights) at H=7168, I=2048,
-    64 experts, top-8 over decode and prefill token counts, plus its two GEMM stages."""
+    """fp8-activation layer (MXFP4 or MXFP8 weights with MXFP8 activations, or fp8 with
+    per-tensor scales) at H=7168, I=2048, 64 experts, top-8 over decode and prefill token
+    counts, plus its two GEMM stages."""
     import numpy as np
     import torch
     import mixture_experts_expert_softmax_amd as M
     import moe_synth as S
     cw = S.w4a8_moe(seed=0, T=8192, wfmt=wfmt)
-    dw = {k_: torch.from_numpy(np.ascontiguousarray(getattr(cw, k_))).to(dev)
-          for k_ in ("x", "x_sf", "w1", "w1_sf", "w2", "w2_sf")}
+    pt = wfmt == "fp8"
+    keys = ("x", "x_sf", "w1", "w1_sf", "w2", "w2_sf") + (("act_scale",) if pt else ())
+    dw = {k_: torch.from_numpy(np.ascontiguousarray(getattr(cw, k_))).to(dev) for k_ in keys}
     lgw = torch.from_numpy(cw.logits).to(dev)
-    per_expert_bytes = (dw["w1"][0].numel() + dw["w1_sf"][0].numel() + dw["w2"][0].numel()
-                        + dw["w2_sf"][0].numel())
+    per_expert_bytes = (dw["w1"][0].numel() + dw["w2"][0].numel()
+                        + (0 if pt else dw["w1_sf"][0].numel() + dw["w2_sf"][0].numel()))
     sweep = {}
     for Tw in (1, 16, 128, 1024, 8192):
         idsw, wtsw = M.moe_route(lgw[:Tw], cw.top_k)
@@ -296,8 +298,13 @@ def _mx_sweep(wfmt, flush, dev):
 
         def mx_step():
             M.moe_route(lgw[:Tw], cw.top_k, idsw, wtsw)
-            M.moe_ffn_forward_mx(dw["x"][:Tw], dw["x_sf"][:Tw], idsw, wtsw, dw["w1"], dw["w1_sf"],
-                                 dw["w2"], dw["w2_sf"], cw.num_experts, out=outw, workspace=wsw)
+            if pt:
+                M.moe_ffn_forward_fp8(dw["x"][:Tw], dw["x_sf"], idsw, wtsw, dw["w1"], dw["w1_sf"],
+                                      dw["w2"], dw["w2_sf"], dw["act_scale"], cw.num_experts,
+                                      out=outw, workspace=wsw)
+            else:
+                M.moe_ffn_forward_mx(dw["x"][:Tw], dw["x_sf"][:Tw], idsw, wtsw, dw["w1"], dw["w1_sf"],
+                                     dw["w2"], dw["w2_sf"], cw.num_experts, out=outw, workspace=wsw)
         touched = int(torch.unique(idsw).numel())
         small = touched * per_expert_bytes < (512 << 20)
         ms_ = _time(mx_step, reps=50 if small else (20 if Tw < 1024 else 10),
@@ -315,10 +322,16 @@ def _mx_sweep(wfmt, flush, dev):
     act = torch.empty((8192 * cw.top_k, cw.I), dtype=torch.uint8, device=dev)
     act_sf = torch.empty((8192 * cw.top_k, cw.I // 32), dtype=torch.uint8, device=dev)
     yw = torch.empty((8192 * cw.top_k, cw.H), dtype=torch.bfloat16, device=dev)
-    ms1 = _time(lambda: M.moe_fc1_mx(dw["x"], dw["x_sf"], dw["w1"], dw["w1_sf"], srt["offs"], srt["p2e"],
-                                     cw.top_k, cw.num_experts, act=act, act_sf=act_sf))
-    ms2 = _time(lambda: M.moe_fc2_mx(act, act_sf, dw["w2"], dw["w2_sf"], srt["offs"], 8192, cw.top_k,
-                                     cw.num_experts, y=yw))
+    if pt:
+        ms1 = _time(lambda: M.moe_fc1_fp8(dw["x"], dw["x_sf"], dw["w1"], dw["w1_sf"], dw["act_scale"],
+                                          srt["offs"], srt["p2e"], cw.top_k, cw.num_experts, act=act))
+        ms2 = _time(lambda: M.moe_fc2_fp8(act, dw["act_scale"], dw["w2"], dw["w2_sf"], srt["offs"], 8192,
+                                          cw.top_k, cw.num_experts, y=yw))
+    else:
+        ms1 = _time(lambda: M.moe_fc1_mx(dw["x"], dw["x_sf"], dw["w1"], dw["w1_sf"], srt["offs"],
+                                         srt["p2e"], cw.top_k, cw.num_experts, act=act, act_sf=act_sf))
+        ms2 = _time(lambda: M.moe_fc2_mx(act, act_sf, dw["w2"], dw["w2_sf"], srt["offs"], 8192,
+                                         cw.top_k, cw.num_experts, y=yw))
     R = 8192 * cw.top_k
     sweep["8192_stages"] = {"fc1_ms": round(ms1, 4), "fc1_tflops": round(4.0 * cw.H * cw.I * R / (ms1 * 1e-3) / 1e12, 1),
                             "fc2_ms": round(ms2, 4), "fc2_tflops": round(2.0 * cw.H * cw.I * R / (ms2 * 1e-3) / 1e12, 1),
@@ -388,7 +401,7 @@ def secondary_measurements(progress):
                            "weight_gbs": round(wbytes / (ms_ * 1e-3) / 1e9, 1)}
     del xs, w1s, w2s, wsp, outs
 
-    for wfmt, key in (("mxfp4", "w4a8"), ("mxfp8", "mxfp8_weights")):
+    for wfmt, key in (("mxfp4", "w4a8"), ("mxfp8", "mxfp8_weights"), ("fp8", "fp8_per_tensor")):
         progress(f"secondary: {wfmt} weights, MXFP8 activations, H=7168 I=2048 64 experts top-8")
         res[key] = _mx_sweep(wfmt, flush, dev)
     del flush

@@ -75,6 +75,11 @@ typedef int32_t moe_status;
                              the FC1 output is requantized to MXFP8 with the round-up rule */
 #define MOE_WFMT_MXFP8 2  /* as MXFP4 but w1, w2 MXFP8: one e4m3fn code byte per element, UE8M0
                              per 32 ([StepFun] intro lists mxfp8 among the weight families) */
+#define MOE_WFMT_FP8   3  /* fp8 with per-tensor scales ([StepFun] intro: "fp8 (per-tensor)"):
+                             x, w1, w2 e4m3fn code bytes; x_sf -> float x_scale [1], w1_sf ->
+                             float w1_scale [L], w2_sf -> float w2_scale [L] (value = code value *
+                             scale); the FC1 output is requantized with the caller's static
+                             act_scale: code = e4m3_rne(clamp(a * (1/act_scale), -448, 448)) */
 
 /* Meaning of a grouped-GEMM offsets array ([GGEMM] intro). */
 #define MOE_OFFS_ENDS   0  /* offs[E]: cumulative end row of each group */
@@ -164,25 +169,26 @@ typedef struct moe_ffn_desc {
   int32_t local_expert_offset;/* global id of local expert 0 */
   int32_t top_k;              /* 1..16 */
   int32_t activation;         /* MOE_ACT_* */
-  int32_t finalize_mode;      /* MOE_FINALIZE_* (MXFP4 / MXFP8: DETERMINISTIC or NONE) */
-  int32_t weight_format;      /* MOE_WFMT_*; MXFP4 / MXFP8 need H % 128 == 0 and I % 128 == 0 */
+  int32_t finalize_mode;      /* MOE_FINALIZE_* (MXFP4 / MXFP8 / FP8: DETERMINISTIC or NONE) */
+  int32_t weight_format;      /* MOE_WFMT_*; MXFP4 / MXFP8 / FP8 need H % 128 == 0, I % 128 == 0 */
 } moe_ffn_desc;
 
 typedef struct moe_ffn_tensors {
-  const void* x;              /* [T, H] bf16, or e4m3fn codes (MXFP4 / MXFP8 formats) */
+  const void* x;              /* [T, H] bf16, or e4m3fn codes (MXFP4 / MXFP8 / FP8 formats) */
   const int32_t* topk_ids;    /* [T, top_k] int32 global expert ids */
   const float* topk_weights;  /* [T, top_k] float32, normalized by the caller */
   const void* w1;             /* [L, 2I, H] bf16: rows 0..I-1 up, I..2I-1 gate
                                  (MXFP4: [L, 2I, H/2] bytes, element 2j in the low nibble;
-                                 MXFP8: [L, 2I, H] e4m3fn codes) */
-  const void* w2;             /* [L, H, I] bf16 (MXFP4: [L, H, I/2] bytes; MXFP8: [L, H, I] codes) */
+                                 MXFP8, FP8: [L, 2I, H] e4m3fn codes) */
+  const void* w2;             /* [L, H, I] bf16 (MXFP4: [L, H, I/2] bytes; MXFP8, FP8: [L, H, I] codes) */
   const float* clamp_limit;   /* [L] float32 SwiGLUStep limits, or NULL for 7.0 */
   void* out;                  /* [T, H] bf16 (DETERMINISTIC / FUSED), fully overwritten */
   void* y;                    /* NONE only: [T*top_k, H] bf16 capacity, FC2 rows in permuted order */
   int32_t* e2p;               /* NONE only (optional otherwise): [T*top_k] int32 */
-  const void* x_sf;           /* MXFP4 / MXFP8 formats: [T, H/32] UE8M0 codes (uint8) */
-  const void* w1_sf;          /* MXFP4 / MXFP8 formats: [L, 2I, H/32] UE8M0 */
-  const void* w2_sf;          /* MXFP4 / MXFP8 formats: [L, H, I/32] UE8M0 */
+  const void* x_sf;           /* MXFP4 / MXFP8 formats: [T, H/32] UE8M0 codes (uint8); FP8: float [1] */
+  const void* w1_sf;          /* MXFP4 / MXFP8 formats: [L, 2I, H/32] UE8M0; FP8: float [L] */
+  const void* w2_sf;          /* MXFP4 / MXFP8 formats: [L, H, I/32] UE8M0; FP8: float [L] */
+  const float* act_scale;     /* FP8 only: [1] float32 scale of the requantized FC1 output */
 } moe_ffn_tensors;
 
 size_t moe_ffn_workspace_size(const moe_ffn_desc* desc);
@@ -238,6 +244,25 @@ moe_status moe_fc1_mx(const moe_ffn_desc* desc, const void* x, const void* x_sf,
 moe_status moe_fc2_mx(const moe_ffn_desc* desc, const void* act, const void* act_sf,
                       const void* w2, const void* w2_sf, const int32_t* offs, void* y,
                       void* stream);
+
+/*
+ * The fp8 per-tensor stages ([StepFun] intro: "fp8 (per-tensor)" weight family);
+ * desc->weight_format must be MOE_WFMT_FP8, otherwise MOE_ERR_DTYPE. x, w1, w2, act
+ * are e4m3fn code bytes; x_scale [1], w1_scale / w2_scale [L] and act_scale [1] are
+ * float32 device values (value = code value * scale). fp32 accumulation.
+ * moe_fc1_fp8: act[p, :] = e4m3_rne(clamp(activation(x_scale * w1_scale[e] *
+ *              (x[p2e[p]/top_k] @ w1[e].T)) * (1/act_scale), -448, 448)), the
+ *              reciprocal taken in float32. act [T*top_k, I] e4m3 codes.
+ * moe_fc2_fp8: y[p, :] = bf16(act_scale * w2_scale[e] * (act[p] @ w2[e].T)), rows in
+ *              permuted order [T*top_k, H].
+ */
+moe_status moe_fc1_fp8(const moe_ffn_desc* desc, const void* x, const float* x_scale,
+                       const void* w1, const float* w1_scale, const float* act_scale,
+                       const float* clamp_limit, const int32_t* offs, const int32_t* p2e,
+                       void* act, void* stream);
+moe_status moe_fc2_fp8(const moe_ffn_desc* desc, const void* act, const float* act_scale,
+                       const void* w2, const float* w2_scale, const int32_t* offs, void* y,
+                       void* stream);
 
 /*
  * moe_finalize -- deterministic top-k combine ([SM90] use_fused_finalize=False):

@@ -22,7 +22,8 @@ __all__ = [
     "MoeError", "lib", "library_path", "EXPORTS", "moe_route", "moe_sort", "grouped_gemm_fwd",
     "grouped_gemm_dgrad", "grouped_gemm_wgrad", "moe_ffn_forward", "moe_ffn_workspace_size",
     "moe_finalize", "moe_fc1", "moe_fc2", "status_string", "ACT", "FINALIZE", "WFMT",
-    "moe_ffn_forward_mx", "moe_fc1_mx", "moe_fc2_mx",
+    "moe_ffn_forward_mx", "moe_fc1_mx", "moe_fc2_mx", "moe_ffn_forward_fp8", "moe_fc1_fp8",
+    "moe_fc2_fp8",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -37,7 +38,7 @@ _i32, _i64, _u64, _vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64, ctypes.
 _sz = ctypes.c_size_t
 
 
-WFMT = {"bf16": 0, "mxfp4": 1, "mxfp8": 2}
+WFMT = {"bf16": 0, "mxfp4": 1, "mxfp8": 2, "fp8": 3}
 
 
 class MoeFfnDesc(ctypes.Structure):
@@ -49,7 +50,7 @@ class MoeFfnDesc(ctypes.Structure):
 class MoeFfnTensors(ctypes.Structure):
     _fields_ = [("x", _vp), ("topk_ids", _vp), ("topk_weights", _vp), ("w1", _vp), ("w2", _vp),
                 ("clamp_limit", _vp), ("out", _vp), ("y", _vp), ("e2p", _vp),
-                ("x_sf", _vp), ("w1_sf", _vp), ("w2_sf", _vp)]
+                ("x_sf", _vp), ("w1_sf", _vp), ("w2_sf", _vp), ("act_scale", _vp)]
 
 
 # name -> (restype, argtypes)
@@ -71,6 +72,8 @@ EXPORTS = {
     "moe_fc2": (_i32, [ctypes.POINTER(MoeFfnDesc), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "moe_fc1_mx": (_i32, [ctypes.POINTER(MoeFfnDesc), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "moe_fc2_mx": (_i32, [ctypes.POINTER(MoeFfnDesc), _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "moe_fc1_fp8": (_i32, [ctypes.POINTER(MoeFfnDesc), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "moe_fc2_fp8": (_i32, [ctypes.POINTER(MoeFfnDesc), _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
 }
 
 _LIB: Optional[ctypes.CDLL] = None
@@ -345,6 +348,45 @@ def moe_ffn_forward_mx(x: torch.Tensor, x_sf: torch.Tensor, topk_ids: torch.Tens
     apart by their last dimension, with UE8M0 scales [L,2I,H/32] / [L,H,I/32]; bf16 output."""
     for t_, n_ in [(x, "x"), (x_sf, "x_sf"), (w1, "w1"), (w1_sf, "w1_sf"), (w2, "w2"), (w2_sf, "w2_sf")]:
         _dev(t_, torch.uint8, n_)
+    H = x.shape[1]
+    I = w1.shape[1] // 2
+    wfmt = _mx_format(w1.shape[2], H, "w1")
+    if w2.shape[2] != (I if wfmt == "mxfp8" else I // 2):
+        raise ValueError(f"w2 last dim {w2.shape[2]} does not match the {wfmt} w1")
+    return _ffn_forward_fp8act(wfmt, x, x_sf, topk_ids, topk_weights, w1, w1_sf, w2, w2_sf, None,
+                               num_experts, num_local_experts, local_expert_offset, activation,
+                               clamp_limit, finalize, out, workspace, y, e2p)
+
+
+def moe_ffn_forward_fp8(x: torch.Tensor, x_scale: torch.Tensor, topk_ids: torch.Tensor,
+                        topk_weights: torch.Tensor, w1: torch.Tensor, w1_scale: torch.Tensor,
+                        w2: torch.Tensor, w2_scale: torch.Tensor, act_scale: torch.Tensor,
+                        num_experts: int, num_local_experts: Optional[int] = None,
+                        local_expert_offset: int = 0, activation: str = "swiglu",
+                        clamp_limit: Optional[torch.Tensor] = None, finalize: str = "deterministic",
+                        out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                        y: Optional[torch.Tensor] = None, e2p: Optional[torch.Tensor] = None):
+    """fp8 per-tensor layer: x, w1 [L,2I,H], w2 [L,H,I] e4m3 codes (uint8); x_scale [1],
+    w1_scale / w2_scale [L] and act_scale [1] (the static scale of the requantized FC1
+    output) float32 device tensors; bf16 output."""
+    for t_, n_ in [(x, "x"), (w1, "w1"), (w2, "w2")]:
+        _dev(t_, torch.uint8, n_)
+    for t_, n_ in [(x_scale, "x_scale"), (w1_scale, "w1_scale"), (w2_scale, "w2_scale"),
+                   (act_scale, "act_scale")]:
+        _dev(t_, torch.float32, n_)
+    L, twoI, H = w1.shape
+    if H != x.shape[1] or tuple(w2.shape) != (L, H, twoI // 2):
+        raise ValueError("fp8: w1 must be [L, 2I, H] and w2 [L, H, I] e4m3 codes")
+    if w1_scale.numel() != L or w2_scale.numel() != L or x_scale.numel() < 1 or act_scale.numel() < 1:
+        raise ValueError("fp8: x_scale / act_scale need one value, w1_scale / w2_scale one per expert")
+    return _ffn_forward_fp8act("fp8", x, x_scale, topk_ids, topk_weights, w1, w1_scale, w2, w2_scale,
+                               act_scale, num_experts, num_local_experts, local_expert_offset,
+                               activation, clamp_limit, finalize, out, workspace, y, e2p)
+
+
+def _ffn_forward_fp8act(wfmt, x, x_sf, topk_ids, topk_weights, w1, w1_sf, w2, w2_sf, act_scale,
+                        num_experts, num_local_experts, local_expert_offset, activation,
+                        clamp_limit, finalize, out, workspace, y, e2p):
     _dev(topk_ids, torch.int32, "topk_ids"), _dev(topk_weights, torch.float32, "topk_weights")
     if clamp_limit is not None:
         _dev(clamp_limit, torch.float32, "clamp_limit")
@@ -352,9 +394,6 @@ def moe_ffn_forward_mx(x: torch.Tensor, x_sf: torch.Tensor, topk_ids: torch.Tens
     L, twoI, _ = w1.shape
     I = twoI // 2
     k = topk_ids.shape[1]
-    wfmt = _mx_format(w1.shape[2], H, "w1")
-    if w2.shape[2] != (I if wfmt == "mxfp8" else I // 2):
-        raise ValueError(f"w2 last dim {w2.shape[2]} does not match the {wfmt} w1")
     d = _ffn_desc(T, H, I, num_experts, L, local_expert_offset, k, activation, finalize, wfmt)
     h = lib()
     ws_bytes = h.moe_ffn_workspace_size(ctypes.byref(d))
@@ -371,7 +410,7 @@ def moe_ffn_forward_mx(x: torch.Tensor, x_sf: torch.Tensor, topk_ids: torch.Tens
                          w2.data_ptr(), None if clamp_limit is None else clamp_limit.data_ptr(),
                          None if out is None else out.data_ptr(), None if y is None else y.data_ptr(),
                          None if e2p is None else e2p.data_ptr(), x_sf.data_ptr(), w1_sf.data_ptr(),
-                         w2_sf.data_ptr())
+                         w2_sf.data_ptr(), None if act_scale is None else act_scale.data_ptr())
     _check("moe_ffn_forward", h.moe_ffn_forward(ctypes.byref(d), ctypes.byref(tens), _ptr(workspace),
                                                 workspace.numel(), _stream()))
     if finalize == "none":
@@ -408,6 +447,35 @@ def moe_fc2_mx(act, act_sf, w2, w2_sf, offs, T, top_k, num_experts, local_expert
         y = torch.empty((max(T * top_k, 1), H), dtype=torch.bfloat16, device=act.device)
     _check("moe_fc2_mx", lib().moe_fc2_mx(ctypes.byref(d), _ptr(act), _ptr(act_sf), _ptr(w2), _ptr(w2_sf),
                                           _ptr(offs), _ptr(y), _stream()))
+    return y
+
+
+def moe_fc1_fp8(x, x_scale, w1, w1_scale, act_scale, offs, p2e, top_k, num_experts,
+                local_expert_offset=0, activation="swiglu", clamp_limit=None, act=None):
+    """act (e4m3 codes [T*k, I]) = per-tensor requant(activation(FC1)) per permuted row."""
+    T, H = x.shape
+    L, twoI, _ = w1.shape
+    I = twoI // 2
+    d = _ffn_desc(T, H, I, num_experts, L, local_expert_offset, top_k, activation,
+                  "deterministic", "fp8")
+    if act is None:
+        act = torch.empty((max(T * top_k, 1), I), dtype=torch.uint8, device=x.device)
+    _check("moe_fc1_fp8", lib().moe_fc1_fp8(ctypes.byref(d), _ptr(x), _ptr(x_scale), _ptr(w1),
+                                            _ptr(w1_scale), _ptr(act_scale), _ptr(clamp_limit),
+                                            _ptr(offs), _ptr(p2e), _ptr(act), _stream()))
+    return act
+
+
+def moe_fc2_fp8(act, act_scale, w2, w2_scale, offs, T, top_k, num_experts, local_expert_offset=0,
+                y=None):
+    """y [T*k, H] bf16 = act_scale * w2_scale[e] * (act @ w2[e].T) for the permuted rows."""
+    L, H, I = w2.shape
+    d = _ffn_desc(T, H, I, num_experts, L, local_expert_offset, top_k, "swiglu", "deterministic",
+                  "fp8")
+    if y is None:
+        y = torch.empty((max(T * top_k, 1), H), dtype=torch.bfloat16, device=act.device)
+    _check("moe_fc2_fp8", lib().moe_fc2_fp8(ctypes.byref(d), _ptr(act), _ptr(act_scale), _ptr(w2),
+                                            _ptr(w2_scale), _ptr(offs), _ptr(y), _stream()))
     return y
 
 

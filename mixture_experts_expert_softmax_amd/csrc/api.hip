@@ -25,11 +25,11 @@ moe_status gemm_wgrad_enqueue(const void* G, const void* X, const int32_t* ends,
                               int N, int K, void* DW, bool out_f32, hipStream_t st);
 moe_status zero_fill(void* p, size_t bytes, hipStream_t st);
 // defined in gemm_mx.hip
-moe_status mx_fc1_enqueue(int activation, int wbits, const void* x, const void* x_sf,
+moe_status mx_fc1_enqueue(int activation, int wf, const void* x, const void* x_sf,
                           const int32_t* p2e, int top_k, const void* w1, const void* w1_sf, int L,
                           const int32_t* offs, int64_t R, int H, int I, const float* limits,
-                          void* act, void* act_sf, hipStream_t st);
-moe_status mx_fc2_enqueue(int wbits, const void* act, const void* act_sf, const void* w2,
+                          void* act, void* act_sf, const float* act_scale, hipStream_t st);
+moe_status mx_fc2_enqueue(int wf, const void* act, const void* act_sf, const void* w2,
                           const void* w2_sf, int L, const int32_t* offs, int64_t R, int H, int I,
                           void* y, hipStream_t st);
 
@@ -47,9 +47,13 @@ int device_cu_count() {
 }
 
 namespace {
-// block-scaled weight formats and their element width in bits
-inline bool is_mx(int32_t wfmt) { return wfmt == MOE_WFMT_MXFP4 || wfmt == MOE_WFMT_MXFP8; }
-inline int mx_wbits(int32_t wfmt) { return wfmt == MOE_WFMT_MXFP8 ? 8 : 4; }
+// the fp8-activation weight formats (MXFP4, MXFP8: block scales; FP8: per-tensor
+// scales), all served by the scaled-MFMA kernels, and their index there
+inline bool is_mx(int32_t wfmt) {
+  return wfmt == MOE_WFMT_MXFP4 || wfmt == MOE_WFMT_MXFP8 || wfmt == MOE_WFMT_FP8;
+}
+inline bool block_scaled(int32_t wfmt) { return wfmt == MOE_WFMT_MXFP4 || wfmt == MOE_WFMT_MXFP8; }
+inline int mx_wf(int32_t wfmt) { return wfmt - MOE_WFMT_MXFP4; }
 
 constexpr int EPI_STORE = 0, EPI_SWIGLU = 1, EPI_SWIGLU_STEP = 2, EPI_FUSED = 3;
 constexpr int64_t U32_ELEMS = (int64_t)1 << 32;
@@ -88,7 +92,7 @@ FfnLayout ffn_layout(const moe_ffn_desc* d) {
   l.n_local = o; o += 256;
   const bool mx = is_mx(d->weight_format);
   l.act = o;     o += align_up((size_t)R * d->I * (mx ? 1 : 2), 256);
-  l.act_sf = o;  o += mx ? align_up((size_t)R * (d->I / 32), 256) : 0;
+  l.act_sf = o;  o += block_scaled(d->weight_format) ? align_up((size_t)R * (d->I / 32), 256) : 0;
   l.y = o;
   if (d->finalize_mode == MOE_FINALIZE_DETERMINISTIC) o += align_up((size_t)R * d->H * 2, 256);
   // bf16 FC1 / FC2 may cut their last round's tiles along K (fp32 partial tiles)
@@ -226,12 +230,14 @@ extern "C" moe_status moe_ffn_forward(const moe_ffn_desc* d, const moe_ffn_tenso
   const bool mx = is_mx(d->weight_format);
   if (!t->x || !t->topk_ids || !t->topk_weights || !t->w1 || !t->w2) return MOE_ERR_NULL;
   if (mx && (!t->x_sf || !t->w1_sf || !t->w2_sf)) return MOE_ERR_NULL;
+  if (d->weight_format == MOE_WFMT_FP8 && !t->act_scale) return MOE_ERR_NULL;
   if (fm != MOE_FINALIZE_NONE && !t->out) return MOE_ERR_NULL;
   if (fm == MOE_FINALIZE_NONE && (!t->y || !t->e2p)) return MOE_ERR_NULL;
   if (!aligned16(t->x) || !aligned16(t->w1) || !aligned16(t->w2) ||
       (t->out && !aligned16(t->out)) || (t->y && !aligned16(t->y)))
     return MOE_ERR_ALIGN;
-  if (mx && (!aligned16(t->x_sf) || !aligned16(t->w1_sf) || !aligned16(t->w2_sf)))
+  if (mx && block_scaled(d->weight_format) &&
+      (!aligned16(t->x_sf) || !aligned16(t->w1_sf) || !aligned16(t->w2_sf)))
     return MOE_ERR_ALIGN;
   const FfnLayout l = ffn_layout(d);
   if (!ws || ws_bytes < l.total || !aligned16(ws)) return MOE_ERR_WORKSPACE;
@@ -253,11 +259,14 @@ extern "C" moe_status moe_ffn_forward(const moe_ffn_desc* d, const moe_ffn_tenso
   if (s != MOE_OK) return s;
   if (mx) {
     const int64_t R = d->T * d->top_k;
-    const int wb = mx_wbits(d->weight_format);
-    s = mx_fc1_enqueue(d->activation, wb, t->x, t->x_sf, p2e, d->top_k, t->w1, t->w1_sf, L, offs,
-                       R, H, d->I, t->clamp_limit, act, w + l.act_sf, st);
+    const int wf = mx_wf(d->weight_format);
+    // FP8: act carries the caller's per-tensor scale instead of block scales
+    const void* act_sf = block_scaled(d->weight_format) ? (const void*)(w + l.act_sf)
+                                                        : (const void*)t->act_scale;
+    s = mx_fc1_enqueue(d->activation, wf, t->x, t->x_sf, p2e, d->top_k, t->w1, t->w1_sf, L, offs,
+                       R, H, d->I, t->clamp_limit, act, w + l.act_sf, t->act_scale, st);
     if (s != MOE_OK) return s;
-    s = mx_fc2_enqueue(wb, act, w + l.act_sf, t->w2, t->w2_sf, L, offs, R, H, d->I, y, st);
+    s = mx_fc2_enqueue(wf, act, act_sf, t->w2, t->w2_sf, L, offs, R, H, d->I, y, st);
   } else {
     s = fc1_enqueue(d, t->x, t->w1, t->clamp_limit, offs, p2e, act, st, split_ws, split_cnt);
     if (s != MOE_OK) return s;
@@ -274,15 +283,15 @@ extern "C" moe_status moe_fc1_mx(const moe_ffn_desc* d, const void* x, const voi
                                  void* stream) {
   moe_status s = check_ffn(d);
   if (s != MOE_OK) return s;
-  if (!is_mx(d->weight_format)) return MOE_ERR_DTYPE;
+  if (!block_scaled(d->weight_format)) return MOE_ERR_DTYPE;
   if (d->T == 0) return MOE_OK;
   if (!x || !x_sf || !w1 || !w1_sf || !offs || !p2e || !act || !act_sf) return MOE_ERR_NULL;
   if (!aligned16(x) || !aligned16(w1) || !aligned16(act) || !aligned16(x_sf) || !aligned16(w1_sf))
     return MOE_ERR_ALIGN;
   const int32_t L = d->num_local_experts > 0 ? d->num_local_experts : d->num_experts;
-  return mx_fc1_enqueue(d->activation, mx_wbits(d->weight_format), x, x_sf, p2e, d->top_k, w1,
-                        w1_sf, L, offs,
-                        d->T * d->top_k, d->H, d->I, clamp_limit, act, act_sf, as_stream(stream));
+  return mx_fc1_enqueue(d->activation, mx_wf(d->weight_format), x, x_sf, p2e, d->top_k, w1, w1_sf,
+                        L, offs, d->T * d->top_k, d->H, d->I, clamp_limit, act, act_sf, nullptr,
+                        as_stream(stream));
 }
 
 extern "C" moe_status moe_fc2_mx(const moe_ffn_desc* d, const void* act, const void* act_sf,
@@ -290,13 +299,43 @@ extern "C" moe_status moe_fc2_mx(const moe_ffn_desc* d, const void* act, const v
                                  void* stream) {
   moe_status s = check_ffn(d);
   if (s != MOE_OK) return s;
-  if (!is_mx(d->weight_format)) return MOE_ERR_DTYPE;
+  if (!block_scaled(d->weight_format)) return MOE_ERR_DTYPE;
   if (d->T == 0) return MOE_OK;
   if (!act || !act_sf || !w2 || !w2_sf || !offs || !y) return MOE_ERR_NULL;
   if (!aligned16(act) || !aligned16(w2) || !aligned16(y) || !aligned16(w2_sf)) return MOE_ERR_ALIGN;
   const int32_t L = d->num_local_experts > 0 ? d->num_local_experts : d->num_experts;
-  return mx_fc2_enqueue(mx_wbits(d->weight_format), act, act_sf, w2, w2_sf, L, offs, d->T * d->top_k, d->H, d->I, y,
+  return mx_fc2_enqueue(mx_wf(d->weight_format), act, act_sf, w2, w2_sf, L, offs, d->T * d->top_k, d->H, d->I, y,
                         as_stream(stream));
+}
+
+extern "C" moe_status moe_fc1_fp8(const moe_ffn_desc* d, const void* x, const float* x_scale,
+                                  const void* w1, const float* w1_scale, const float* act_scale,
+                                  const float* clamp_limit, const int32_t* offs, const int32_t* p2e,
+                                  void* act, void* stream) {
+  moe_status s = check_ffn(d);
+  if (s != MOE_OK) return s;
+  if (d->weight_format != MOE_WFMT_FP8) return MOE_ERR_DTYPE;
+  if (d->T == 0) return MOE_OK;
+  if (!x || !x_scale || !w1 || !w1_scale || !act_scale || !offs || !p2e || !act) return MOE_ERR_NULL;
+  if (!aligned16(x) || !aligned16(w1) || !aligned16(act)) return MOE_ERR_ALIGN;
+  const int32_t L = d->num_local_experts > 0 ? d->num_local_experts : d->num_experts;
+  return mx_fc1_enqueue(d->activation, mx_wf(MOE_WFMT_FP8), x, x_scale, p2e, d->top_k, w1, w1_scale,
+                        L, offs, d->T * d->top_k, d->H, d->I, clamp_limit, act, nullptr, act_scale,
+                        as_stream(stream));
+}
+
+extern "C" moe_status moe_fc2_fp8(const moe_ffn_desc* d, const void* act, const float* act_scale,
+                                  const void* w2, const float* w2_scale, const int32_t* offs,
+                                  void* y, void* stream) {
+  moe_status s = check_ffn(d);
+  if (s != MOE_OK) return s;
+  if (d->weight_format != MOE_WFMT_FP8) return MOE_ERR_DTYPE;
+  if (d->T == 0) return MOE_OK;
+  if (!act || !act_scale || !w2 || !w2_scale || !offs || !y) return MOE_ERR_NULL;
+  if (!aligned16(act) || !aligned16(w2) || !aligned16(y)) return MOE_ERR_ALIGN;
+  const int32_t L = d->num_local_experts > 0 ? d->num_local_experts : d->num_experts;
+  return mx_fc2_enqueue(mx_wf(MOE_WFMT_FP8), act, act_scale, w2, w2_scale, L, offs, d->T * d->top_k,
+                        d->H, d->I, y, as_stream(stream));
 }
 
 // Split-tile workspace of the standalone GEMM stages: partial tiles, then the

@@ -1,7 +1,12 @@
-// MX-weight x MXFP8-activation grouped GEMMs (FC1 with the activation and the
-// MXFP8 requantization in its epilogue, FC2 to bf16 rows) on gfx950 scaled MFMA.
-// Two weight families: MXFP4 (e2m1 pairs) and MXFP8 (e4m3 bytes), both with one
-// UE8M0 scale per 32 values along the contraction.
+// fp8-activation grouped GEMMs on gfx950 scaled MFMA: FC1 with the activation and
+// the fp8 requantization in its epilogue, FC2 to bf16 rows. Three weight families:
+//   MXFP4  e2m1 pairs, one UE8M0 scale per 32 values along the contraction;
+//   MXFP8  e4m3 bytes, same scales (activations MXFP8 in both MX families);
+//   FP8    e4m3 bytes with one fp32 scale per expert matrix, activations e4m3 with
+//          one fp32 scale for the tensor (StepFun page, intro: "fp8 (per-tensor)").
+//          The MFMA runs with unit block scales and the per-tensor factors are
+//          applied in the epilogue; the FC1 output is requantized with a given
+//          per-tensor scale, saturating at +-448.
 //
 // W4A8 page ("flashinfer.fused_moe.cake / cake_cute (MXFP4 SiTU routed MoE)"),
 // "Inputs": activations are float8_e4m3fn with one UE8M0 scale per 32 values
@@ -34,13 +39,19 @@ constexpr int MTK = 128;          // contraction per stage
 constexpr int MNT = 256;          // threads
 constexpr int XT_U4 = MTB * MTK / 16;        // 2048 uint4: activation codes
 
-// Weight element widths: MXFP4 (e2m1, 4 bits) or MXFP8 (e4m3, 8 bits).
-constexpr int MX_W4 = 4, MX_W8 = 8;
+// Weight formats (the order of MOE_WFMT_MXFP4, MOE_WFMT_MXFP8, MOE_WFMT_FP8 minus 1).
+constexpr int WF_MXFP4 = 0, WF_MXFP8 = 1, WF_FP8 = 2;
+template <int WF> constexpr int wbits() { return WF == WF_MXFP4 ? 4 : 8; }
+template <int WF> constexpr bool block_scaled() { return WF != WF_FP8; }
 // 16-byte chunks per weight row and stage, and the stage size in uint4
-template <int WB> constexpr int wch() { return MTK * WB / 8 / 16; }
-template <int WB> constexpr int stage_u4() { return XT_U4 + MTB * wch<WB>() + 2 * MTB / 4; }
+template <int WF> constexpr int wch() { return MTK * wbits<WF>() / 8 / 16; }
+template <int WF> constexpr int stage_u4() {
+  return XT_U4 + MTB * wch<WF>() + (block_scaled<WF>() ? 2 * MTB / 4 : 0);
+}
 // scaled-MFMA format code of the weight (A-slot) operand
-template <int WB> constexpr int a_fmt() { return WB == MX_W4 ? 4 : 0; }
+template <int WF> constexpr int a_fmt() { return WF == WF_MXFP4 ? 4 : 0; }
+constexpr int UNIT_SCALE = 127;              // UE8M0 code of 1.0
+constexpr uint32_t UNIT_SCALE4 = 0x7F7F7F7Fu;
 
 enum MxEpi { MX_FC1_SWIGLU = 0, MX_FC1_STEP = 1, MX_FC2 = 2 };
 
@@ -58,11 +69,29 @@ struct MxArgs {
   uint16_t* C;             // FC2: bf16 rows [rows][ldc]
   int64_t ldc;
   uint8_t* Cq;             // FC1: e4m3 act [rows][I]
-  uint8_t* Cq_sf;          // FC1: [rows][I/32]
+  uint8_t* Cq_sf;          // FC1: [rows][I/32] (MX families)
   int I;
   const float* limits;
   float def_limit;
+  // FP8 family: A-operand tensor scale [1], weight scales [E], FC1 output scale [1]
+  const float* a_scale;
+  const float* w_scale;
+  const float* q_scale;
 };
+
+// Per-tensor factor of an output element (FP8 family): a_scale * w_scale[e].
+template <int WF>
+__device__ __forceinline__ float pt_alpha(const MxArgs& a, int e) {
+  return block_scaled<WF>() ? 1.f : a.a_scale[0] * a.w_scale[e];
+}
+
+// e4m3 code input of a requantized FC1 value v * inv: the MX families' block scale
+// keeps it within +-448 by construction; the per-tensor scale may not, so it saturates.
+template <int WF>
+__device__ __forceinline__ float q_in(float v, float inv) {
+  const float y = v * inv;
+  return block_scaled<WF>() ? y : fminf(fmaxf(y, -448.f), 448.f);
+}
 
 // Round-up UE8M0 code of a block maximum: the smallest e with amax <= 448 * 2^e,
 // as e + 127. With amax = (1+f) * 2^E, 448 = 1.75 * 2^8: e = E - 8 when
@@ -76,9 +105,11 @@ __device__ __forceinline__ uint32_t ue8m0_round_up_448(float amax) {
   return (uint32_t)c;
 }
 
-template <int EPI, int WB>
+template <int EPI, int WF>
 __global__ __launch_bounds__(MNT, 1) void k_gemm_mx(MxArgs a) {
-  constexpr int WCH = wch<WB>(), WT_U4 = MTB * WCH, STAGE_U4 = stage_u4<WB>();
+  constexpr int WB = wbits<WF>();
+  constexpr bool BS = block_scaled<WF>();
+  constexpr int WCH = wch<WF>(), WT_U4 = MTB * WCH, STAGE_U4 = stage_u4<WF>();
   constexpr int WLD = WT_U4 / MNT;   // weight loads per thread and stage (4 or 8)
   __shared__ uint4 smem[2 * STAGE_U4];
   int e, m0, mend, nt;
@@ -131,8 +162,10 @@ __global__ __launch_bounds__(MNT, 1) void k_gemm_mx(MxArgs a) {
     for (int j = 0; j < 8; ++j) rx[j] = *reinterpret_cast<const u32x4*>(a.A + xoff[j] + kb);
 #pragma unroll
     for (int j = 0; j < WLD; ++j) rw[j] = *reinterpret_cast<const u32x4*>(Bb + woff[j] + kb * WB / 8);
-    rxs = *reinterpret_cast<const uint32_t*>(a.A_sf + xsoff + kb / 32);
-    rws = *reinterpret_cast<const uint32_t*>(Bs + wsoff + kb / 32);
+    if (BS) {
+      rxs = *reinterpret_cast<const uint32_t*>(a.A_sf + xsoff + kb / 32);
+      rws = *reinterpret_cast<const uint32_t*>(Bs + wsoff + kb / 32);
+    }
   };
   // weight chunk swizzle: 64-byte rows (MXFP4) by (r >> 2) & 3, 128-byte rows by
   // (r >> 1) & 7, so that each 16-lane group of a fragment read hits 64 distinct banks
@@ -152,8 +185,10 @@ __global__ __launch_bounds__(MNT, 1) void k_gemm_mx(MxArgs a) {
       const int r = wr + (MTB / WLD) * j;
       W[r * WCH + (wc ^ wswz(r))] = rw[j];
     }
-    XS[tid] = rxs;
-    WS[tid] = rws;
+    if (BS) {
+      XS[tid] = rxs;
+      WS[tid] = rws;
+    }
   };
 
   f32x16 acc[4][4];
@@ -179,15 +214,15 @@ __global__ __launch_bounds__(MNT, 1) void k_gemm_mx(MxArgs a) {
     const uint32_t* WS = XS + MTB;
     uint32_t wsr[4], xsr[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) wsr[i] = WS[wn * 128 + i * 32 + rsel];
+    for (int i = 0; i < 4; ++i) wsr[i] = BS ? WS[wn * 128 + i * 32 + rsel] : UNIT_SCALE4;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) xsr[j] = XS[wm * 128 + j * 32 + rsel];
+    for (int j = 0; j < 4; ++j) xsr[j] = BS ? XS[wm * 128 + j * 32 + rsel] : UNIT_SCALE4;
     v8i wf[2][4], xf[2][4];
     auto rd = [&](int kk, v8i (&wq)[4], v8i (&xq)[4]) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = wn * 128 + i * 32 + rsel;
-        if (WB == MX_W4) {
+        if (WF == WF_MXFP4) {
           const uint4 v = W[r * 4 + ((2 * kk + g) ^ wswz(r))];
           wq[i] = v8i{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
         } else {
@@ -215,7 +250,7 @@ __global__ __launch_bounds__(MNT, 1) void k_gemm_mx(MxArgs a) {
 #pragma unroll
         for (int j = 0; j < 4; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-              wf[kk][i], xf[kk][j], acc[i][j], a_fmt<WB>(), 0, 0, (int)((wsr[i] >> sh) & 0xFF), 0,
+              wf[kk][i], xf[kk][j], acc[i][j], a_fmt<WF>(), 0, 0, (int)((wsr[i] >> sh) & 0xFF), 0,
               (int)((xsr[j] >> sh) & 0xFF));
       if (kk == 1) sstore(s ^ 1);
     }
@@ -224,16 +259,17 @@ __global__ __launch_bounds__(MNT, 1) void k_gemm_mx(MxArgs a) {
     // step 0's 16 MFMAs with step 1's NRD fragment reads and the NGL global loads
     // between them, then step 1's 16 MFMAs with the NST LDS stores (the two scale
     // words go out as one paired store). MXFP4: NRD 12, NGL 14, NST 13; MXFP8: 16,
-    // 18, 17.
-    constexpr int NRD = 8 + 4 * (WCH / 4), NGL = 8 + WLD + 2, NST = 8 + WLD + 1;
-    __builtin_amdgcn_sched_group_barrier(0x100, 4 + NRD, 0);
+    // 18, 17; FP8 (no block scales): 16, 16, 16.
+    constexpr int SC = BS ? 1 : 0;
+    constexpr int NRD = 8 + 4 * (WCH / 4), NGL = 8 + WLD + 2 * SC, NST = 8 + WLD + SC;
+    __builtin_amdgcn_sched_group_barrier(0x100, 4 * SC + NRD, 0);
     for (int r = 0; r < NRD; ++r) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
     }
     if (16 - NRD > 0) __builtin_amdgcn_sched_group_barrier(0x008, 16 - NRD, 0);
-    __builtin_amdgcn_sched_group_barrier(0x020, NGL - NRD, 0);
+    if (NGL - NRD > 0) __builtin_amdgcn_sched_group_barrier(0x020, NGL - NRD, 0);
     constexpr int NPAIR = NST < 16 ? NST : 16;
     for (int r = 0; r < NPAIR; ++r) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -245,9 +281,11 @@ __global__ __launch_bounds__(MNT, 1) void k_gemm_mx(MxArgs a) {
   }
 
   const int hi4 = (lane >> 5) * 4;
+  const float alpha = pt_alpha<WF>(a, e);
   if (fc1) {
     float lim = 0.f;
     if (EPI == MX_FC1_STEP) lim = a.limits ? a.limits[e] : a.def_limit;
+    const float qinv = BS ? 1.f : 1.0f / a.q_scale[0];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int p = m0 + wm * 128 + j * 32 + rsel;
@@ -259,8 +297,8 @@ __global__ __launch_bounds__(MNT, 1) void k_gemm_mx(MxArgs a) {
         float amax = 0.f;
 #pragma unroll
         for (int q = 0; q < 16; ++q) {
-          float u = acc[i][j][q];
-          float gt = acc[i + 2][j][q];
+          float u = acc[i][j][q] * alpha;
+          float gt = acc[i + 2][j][q] * alpha;
           if (EPI == MX_FC1_STEP) {
             u = fminf(fmaxf(u, -lim), lim);
             gt = fminf(fmaxf(gt, -lim), lim);
@@ -268,18 +306,24 @@ __global__ __launch_bounds__(MNT, 1) void k_gemm_mx(MxArgs a) {
           v[q] = silu_f32(gt) * u;
           amax = fmaxf(amax, fabsf(v[q]));
         }
-        amax = fmaxf(amax, __shfl_xor(amax, 32));
-        const uint32_t code = ue8m0_round_up_448(amax);
-        const float inv = __uint_as_float((254u - code) << 23);   // 2^(127 - code)
+        uint32_t code = 0;
+        float inv = qinv;
+        if (BS) {
+          amax = fmaxf(amax, __shfl_xor(amax, 32));
+          code = ue8m0_round_up_448(amax);
+          inv = __uint_as_float((254u - code) << 23);   // 2^(127 - code)
+        }
         if (!row_ok || col0 >= a.I) continue;
         uint8_t* crow = a.Cq + (int64_t)p * a.I;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          int pk = __builtin_amdgcn_cvt_pk_fp8_f32(v[4 * q] * inv, v[4 * q + 1] * inv, 0, false);
-          pk = __builtin_amdgcn_cvt_pk_fp8_f32(v[4 * q + 2] * inv, v[4 * q + 3] * inv, pk, true);
+          int pk = __builtin_amdgcn_cvt_pk_fp8_f32(q_in<WF>(v[4 * q], inv), q_in<WF>(v[4 * q + 1], inv),
+                                                   0, false);
+          pk = __builtin_amdgcn_cvt_pk_fp8_f32(q_in<WF>(v[4 * q + 2], inv), q_in<WF>(v[4 * q + 3], inv),
+                                               pk, true);
           *reinterpret_cast<uint32_t*>(crow + col0 + q * 8 + hi4) = (uint32_t)pk;
         }
-        if (g == 0) a.Cq_sf[(int64_t)p * (a.I >> 5) + (col0 >> 5)] = (uint8_t)code;
+        if (BS && g == 0) a.Cq_sf[(int64_t)p * (a.I >> 5) + (col0 >> 5)] = (uint8_t)code;
       }
     }
   } else {
@@ -295,8 +339,8 @@ __global__ __launch_bounds__(MNT, 1) void k_gemm_mx(MxArgs a) {
           const int col = nt * MTB + wn * 128 + i * 32 + q * 8 + hi4;
           if (col >= a.N) continue;
           *reinterpret_cast<uint2*>(crow + col) =
-              make_uint2(pack_bf16x2(acc[i][j][q * 4 + 0], acc[i][j][q * 4 + 1]),
-                         pack_bf16x2(acc[i][j][q * 4 + 2], acc[i][j][q * 4 + 3]));
+              make_uint2(pack_bf16x2(acc[i][j][q * 4 + 0] * alpha, acc[i][j][q * 4 + 1] * alpha),
+                         pack_bf16x2(acc[i][j][q * 4 + 2] * alpha, acc[i][j][q * 4 + 3] * alpha));
         }
     }
   }
@@ -328,8 +372,10 @@ struct MxW {
   u32x4 v[8];
 };
 
-template <int EPI, int WB>
+template <int EPI, int WF>
 __global__ __launch_bounds__(256, 2) void k_gemm_mx_stream(MxArgs a) {
+  constexpr int WB = wbits<WF>();
+  constexpr bool BS = block_scaled<WF>();
   constexpr int NS = 128 * 8 / WB / 64;   // 64-value steps per 128-byte stage: 4 or 2
   __shared__ u32x4 ring[4][512];              // [wave][64 rows x 8 chunks]
   __shared__ uint32_t scl[4][64][SCW];        // [wave][tile row][scale dwords]
@@ -358,7 +404,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_mx_stream(MxArgs a) {
   // weight scales of this wave's stages: 2 NS bytes per stage and row, from byte
   // 2 NS s0
   uint32_t sreg[SCW];
-  {
+  if (BS) {
     const uint32_t* srow =
         reinterpret_cast<const uint32_t*>(Bs + (int64_t)wrow_of(lane) * ks + 2 * NS * s0);
 #pragma unroll
@@ -394,7 +440,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_mx_stream(MxArgs a) {
     for (int s = 0; s < NS; ++s) {
       act.xl[s] = *reinterpret_cast<const u32x4*>(xb + xoff + 64 * s);
       act.xh[s] = *reinterpret_cast<const u32x4*>(xb + xoff + 64 * s + 32);
-      act.sx[s] = sbp[xsoff + 2 * s];
+      act.sx[s] = BS ? sbp[xsoff + 2 * s] : UNIT_SCALE;
     }
   };
   auto stash = [&](const MxW& w) {
@@ -411,7 +457,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_mx_stream(MxArgs a) {
   // the chunks 4s + g and 4s + 2 + g (k = 16g + b and 32 + 16g + b of the step)
   auto wfrag = [&](const u32x4* W, int R, int s) -> v8i {
     const int sw = (R >> 1) & 7;
-    if (WB == MX_W4) {
+    if (WF == WF_MXFP4) {
       const u32x4 v = W[R * 8 + ((2 * s + g) ^ sw)];
       return v8i{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
     }
@@ -428,10 +474,11 @@ __global__ __launch_bounds__(256, 2) void k_gemm_mx_stream(MxArgs a) {
       const v8i f1 = wfrag(W, 32 + r, s);
       const v8i x{(int)act.xl[s].x, (int)act.xl[s].y, (int)act.xl[s].z, (int)act.xl[s].w,
                   (int)act.xh[s].x, (int)act.xh[s].y, (int)act.xh[s].z, (int)act.xh[s].w};
-      acc0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f0, x, acc0, a_fmt<WB>(), 0, 0,
-                                                             (int)sc0[bi], 0, (int)act.sx[s]);
-      acc1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f1, x, acc1, a_fmt<WB>(), 0, 0,
-                                                             (int)sc1[bi], 0, (int)act.sx[s]);
+      const int s0w = BS ? (int)sc0[bi] : UNIT_SCALE, s1w = BS ? (int)sc1[bi] : UNIT_SCALE;
+      acc0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f0, x, acc0, a_fmt<WF>(), 0, 0, s0w, 0,
+                                                             (int)act.sx[s]);
+      acc1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f1, x, acc1, a_fmt<WF>(), 0, 0, s1w, 0,
+                                                             (int)act.sx[s]);
     }
   };
 
@@ -444,8 +491,10 @@ __global__ __launch_bounds__(256, 2) void k_gemm_mx_stream(MxArgs a) {
     issue_a(0, A0);
     issue_w(1, W1);
     __builtin_amdgcn_sched_barrier(0);
+    if (BS) {
 #pragma unroll
-    for (int d = 0; d < SCW; ++d) scl[wid][lane][d] = sreg[d];
+      for (int d = 0; d < SCW; ++d) scl[wid][lane][d] = sreg[d];
+    }
     stash(W0);
     // (the scheduling barriers keep the compiler from sinking loads to their uses)
     for (int q = 0; q < nst; q += 2) {
@@ -486,6 +535,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_mx_stream(MxArgs a) {
   // 8 * (q / 4) + 4 * (l / 32) + q % 4 of its 32-column group
   const int hi4 = g * 4;
   const int prow = m0 + r;
+  const float alpha = pt_alpha<WF>(a, e);
   if (fc1) {
     float lim = 0.f;
     if (EPI == MX_FC1_STEP) lim = a.limits ? a.limits[e] : a.def_limit;
@@ -493,7 +543,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_mx_stream(MxArgs a) {
     float amax = 0.f;
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
-      float u = acc0[q], gt = acc1[q];
+      float u = acc0[q] * alpha, gt = acc1[q] * alpha;
       if (EPI == MX_FC1_STEP) {
         u = fminf(fmaxf(u, -lim), lim);
         gt = fminf(fmaxf(gt, -lim), lim);
@@ -501,18 +551,26 @@ __global__ __launch_bounds__(256, 2) void k_gemm_mx_stream(MxArgs a) {
       v[q] = silu_f32(gt) * u;
       amax = fmaxf(amax, fabsf(v[q]));
     }
-    amax = fmaxf(amax, __shfl_xor(amax, 32));
-    const uint32_t code = ue8m0_round_up_448(amax);
-    const float inv = __uint_as_float((254u - code) << 23);
+    uint32_t code = 0;
+    float inv;
+    if (BS) {
+      amax = fmaxf(amax, __shfl_xor(amax, 32));
+      code = ue8m0_round_up_448(amax);
+      inv = __uint_as_float((254u - code) << 23);
+    } else {
+      inv = 1.0f / a.q_scale[0];
+    }
     if (prow >= mend) return;
     uint8_t* crow = a.Cq + (int64_t)prow * a.I + nt * 32;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      int pk = __builtin_amdgcn_cvt_pk_fp8_f32(v[4 * q] * inv, v[4 * q + 1] * inv, 0, false);
-      pk = __builtin_amdgcn_cvt_pk_fp8_f32(v[4 * q + 2] * inv, v[4 * q + 3] * inv, pk, true);
+      int pk = __builtin_amdgcn_cvt_pk_fp8_f32(q_in<WF>(v[4 * q], inv), q_in<WF>(v[4 * q + 1], inv), 0,
+                                               false);
+      pk = __builtin_amdgcn_cvt_pk_fp8_f32(q_in<WF>(v[4 * q + 2], inv), q_in<WF>(v[4 * q + 3], inv), pk,
+                                           true);
       *reinterpret_cast<uint32_t*>(crow + q * 8 + hi4) = (uint32_t)pk;
     }
-    if (g == 0) a.Cq_sf[(int64_t)prow * (a.I >> 5) + nt] = (uint8_t)code;
+    if (BS && g == 0) a.Cq_sf[(int64_t)prow * (a.I >> 5) + nt] = (uint8_t)code;
   } else {
     if (prow >= mend) return;
     uint16_t* crow = a.C + (int64_t)prow * a.ldc;
@@ -524,8 +582,8 @@ __global__ __launch_bounds__(256, 2) void k_gemm_mx_stream(MxArgs a) {
         if (col >= a.N) continue;
         const f32x16& ac = i ? acc1 : acc0;
         *reinterpret_cast<uint2*>(crow + col) =
-            make_uint2(pack_bf16x2(ac[q * 4 + 0], ac[q * 4 + 1]),
-                       pack_bf16x2(ac[q * 4 + 2], ac[q * 4 + 3]));
+            make_uint2(pack_bf16x2(ac[q * 4 + 0] * alpha, ac[q * 4 + 1] * alpha),
+                       pack_bf16x2(ac[q * 4 + 2] * alpha, ac[q * 4 + 3] * alpha));
       }
   }
 }
@@ -547,30 +605,34 @@ inline int64_t mx_row_tiles(int64_t R, int L, int tm) { return R / tm + (R < L ?
 
 }  // namespace
 
-template <int EPI, int WB>
+template <int EPI, int WF>
 moe_status mx_launch(const MxArgs& a, bool small, int64_t tiles, hipStream_t st) {
   const int grid = (int)((tiles + 7) / 8 * 8);
   if (small)
-    k_gemm_mx_stream<EPI, WB><<<grid, 256, 0, st>>>(a);
+    k_gemm_mx_stream<EPI, WF><<<grid, 256, 0, st>>>(a);
   else
-    k_gemm_mx<EPI, WB><<<grid, MNT, 0, st>>>(a);
+    k_gemm_mx<EPI, WF><<<grid, MNT, 0, st>>>(a);
   return launch_status();
 }
 
 template <int EPI>
-moe_status mx_launch_w(const MxArgs& a, int wb, bool small, int64_t tiles, hipStream_t st) {
-  return wb == MX_W8 ? mx_launch<EPI, MX_W8>(a, small, tiles, st)
-                     : mx_launch<EPI, MX_W4>(a, small, tiles, st);
+moe_status mx_launch_w(const MxArgs& a, int wf, bool small, int64_t tiles, hipStream_t st) {
+  if (wf == WF_FP8) return mx_launch<EPI, WF_FP8>(a, small, tiles, st);
+  if (wf == WF_MXFP8) return mx_launch<EPI, WF_MXFP8>(a, small, tiles, st);
+  return mx_launch<EPI, WF_MXFP4>(a, small, tiles, st);
 }
 
-// FC1: act (MXFP8) = requant(activation(x[p2e[p]/k] @ w1[e].T)) for permuted rows p;
-// w1 MXFP4 (wbits 4) or MXFP8 (wbits 8).
-moe_status mx_fc1_enqueue(int activation, int wbits, const void* x, const void* x_sf,
+inline int wf_bits(int wf) { return wf == WF_MXFP4 ? 4 : 8; }
+
+// FC1: act (e4m3) = requant(activation(x[p2e[p]/k] @ w1[e].T)) for permuted rows p.
+// wf: WF_MXFP4 / WF_MXFP8 (x_sf, w1_sf UE8M0 block scales; act_sf out) or WF_FP8
+// (x_sf float [1], w1_sf float [L], act_scale float [1] in; act_sf unused).
+moe_status mx_fc1_enqueue(int activation, int wf, const void* x, const void* x_sf,
                           const int32_t* p2e, int top_k, const void* w1, const void* w1_sf, int L,
                           const int32_t* offs, int64_t R, int H, int I, const float* limits,
-                          void* act, void* act_sf, hipStream_t st) {
+                          void* act, void* act_sf, const float* act_scale, hipStream_t st) {
   if (R == 0) return MOE_OK;
-  if (wbits != MX_W4 && wbits != MX_W8) return MOE_ERR_DTYPE;
+  if (wf != WF_MXFP4 && wf != WF_MXFP8 && wf != WF_FP8) return MOE_ERR_DTYPE;
   MxArgs a{};
   a.A = reinterpret_cast<const uint8_t*>(x);
   a.A_sf = reinterpret_cast<const uint8_t*>(x_sf);
@@ -589,19 +651,23 @@ moe_status mx_fc1_enqueue(int activation, int wbits, const void* x, const void* 
   a.I = I;
   a.limits = limits;
   a.def_limit = 7.0f;
-  const bool small = mx_use_small(R, L, H, 2 * I, R, 32, wbits);
+  a.a_scale = reinterpret_cast<const float*>(x_sf);
+  a.w_scale = reinterpret_cast<const float*>(w1_sf);
+  a.q_scale = act_scale;
+  const bool small = mx_use_small(R, L, H, 2 * I, R, 32, wf_bits(wf));
   a.n_tiles = small ? I / 32 : (I + 127) / 128;
   const int64_t tiles = mx_row_tiles(R, L, small ? STB : MTB) * a.n_tiles;
-  if (activation == MOE_ACT_SWIGLU_STEP) return mx_launch_w<MX_FC1_STEP>(a, wbits, small, tiles, st);
-  return mx_launch_w<MX_FC1_SWIGLU>(a, wbits, small, tiles, st);
+  if (activation == MOE_ACT_SWIGLU_STEP) return mx_launch_w<MX_FC1_STEP>(a, wf, small, tiles, st);
+  return mx_launch_w<MX_FC1_SWIGLU>(a, wf, small, tiles, st);
 }
 
-// FC2: y[p] (bf16) = act[p] @ w2[e].T with MXFP8 act and MXFP4 / MXFP8 w2.
-moe_status mx_fc2_enqueue(int wbits, const void* act, const void* act_sf, const void* w2,
+// FC2: y[p] (bf16) = act[p] @ w2[e].T; act_sf / w2_sf as x_sf / w1_sf above (FP8:
+// act_sf is the float [1] scale of act).
+moe_status mx_fc2_enqueue(int wf, const void* act, const void* act_sf, const void* w2,
                           const void* w2_sf, int L, const int32_t* offs, int64_t R, int H, int I,
                           void* y, hipStream_t st) {
   if (R == 0) return MOE_OK;
-  if (wbits != MX_W4 && wbits != MX_W8) return MOE_ERR_DTYPE;
+  if (wf != WF_MXFP4 && wf != WF_MXFP8 && wf != WF_FP8) return MOE_ERR_DTYPE;
   MxArgs a{};
   a.A = reinterpret_cast<const uint8_t*>(act);
   a.A_sf = reinterpret_cast<const uint8_t*>(act_sf);
@@ -617,10 +683,12 @@ moe_status mx_fc2_enqueue(int wbits, const void* act, const void* act_sf, const 
   a.K = I;
   a.C = reinterpret_cast<uint16_t*>(y);
   a.ldc = H;
-  const bool small = mx_use_small(R, L, I, H, R, 24, wbits);
+  a.a_scale = reinterpret_cast<const float*>(act_sf);
+  a.w_scale = reinterpret_cast<const float*>(w2_sf);
+  const bool small = mx_use_small(R, L, I, H, R, 24, wf_bits(wf));
   a.n_tiles = small ? (H + 63) / 64 : (H + MTB - 1) / MTB;
   const int64_t tiles = mx_row_tiles(R, L, small ? STB : MTB) * a.n_tiles;
-  return mx_launch_w<MX_FC2>(a, wbits, small, tiles, st);
+  return mx_launch_w<MX_FC2>(a, wf, small, tiles, st);
 }
 
 }  // namespace moe

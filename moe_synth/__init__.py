@@ -18,7 +18,10 @@ Conventions
   expert by expert (and in parallel) without holding an fp32 copy of the bank.
 * The MX (MXFP8 / MXFP4) encoders here produce *inputs* only: block scales are
   powers of two chosen so the block maximum fits the element format, and the
-  elements are rounded to nearest, ties to even.
+  elements are rounded to nearest, ties to even. The per-tensor fp8 encoder
+  takes scale = amax / 448 (float32) for the whole tensor (x) or expert matrix
+  (w1[e], w2[e]); the static scale of the requantized FC1 output is a case
+  parameter, not derived from any layer output.
 """
 from __future__ import annotations
 
@@ -35,7 +38,7 @@ __all__ = [
     "MoECase", "GroupedGemmCase", "moe_case", "tiny_moe", "mixtral_moe",
     "expert_shard_moe", "grouped_gemm_case", "dirichlet_group_sizes",
     "route_logits", "bf16_to_f32", "to_bf16", "mx_quant_e4m3", "mx_quant_e2m1", "W4A8Case",
-    "w4a8_moe",
+    "w4a8_moe", "fp8_quant_per_tensor", "FP8_ACT_SCALE",
 ]
 
 _THREADS = max(1, min(16, os.cpu_count() or 1))
@@ -282,6 +285,23 @@ def mx_quant_e2m1(a: np.ndarray, block: int = 32):
     return packed, sc
 
 
+def fp8_quant_per_tensor(a: np.ndarray):
+    """float32 array -> (e4m3fn codes uint8, float32 scale) with scale = amax / 448
+    (1.0 for an all-zero array); codes are torch's RNE cast of a / scale in float32."""
+    a = np.asarray(a, dtype=np.float32)
+    amax = float(np.abs(a).max()) if a.size else 0.0
+    sc = np.float32(amax / 448.0) if amax > 0 else np.float32(1.0)
+    codes = torch.from_numpy(np.ascontiguousarray(a / sc)).to(torch.float8_e4m3fn).view(
+        torch.uint8).numpy()
+    return codes, sc
+
+
+# Static FC1-output scale of the per-tensor fp8 cases: codes reach 448 * 0.0357 = 16,
+# about 4 sigma of silu(gate) * up for unit-variance pre-activations; deliberately
+# not a power of two, so that the float32 reciprocal matters.
+FP8_ACT_SCALE = 0.0357
+
+
 @dataclass
 class W4A8Case:
     """MXFP8-activation / MX-weight MoE case (numpy arrays on the host).
@@ -290,6 +310,8 @@ class W4A8Case:
     w1, w1_sf: uint8 [L, 2I, H/2] packed e2m1 (wfmt "mxfp4") or [L, 2I, H] e4m3fn codes
                (wfmt "mxfp8"), [up | gate] rows; uint8 [L, 2I, H/32]
     w2, w2_sf: uint8 [L, H, I/2] or [L, H, I], uint8 [L, H, I/32]
+    wfmt "fp8" (per-tensor): x, w1, w2 e4m3fn codes as for "mxfp8"; x_sf float32 [1],
+               w1_sf / w2_sf float32 [L]; act_scale float32 [1] (FC1 output scale)
     """
     T: int
     H: int
@@ -304,6 +326,7 @@ class W4A8Case:
     w2: np.ndarray
     w2_sf: np.ndarray
     wfmt: str = "mxfp4"
+    act_scale: Optional[np.ndarray] = None
 
     @property
     def num_local(self) -> int:
@@ -312,23 +335,29 @@ class W4A8Case:
 
 def w4a8_moe(seed: int = 0, T: int = 8192, H: int = 7168, I: int = 2048, E: int = 64,
              top_k: int = 8, x_scale: float = 1.0, wfmt: str = "mxfp4") -> W4A8Case:
-    """MX MoE: logits N(0,1); x N(0,1) -> MXFP8; w1 N(0,1/H), w2 N(0,1/I) -> MXFP4 (wfmt
-    "mxfp4", the W4A8 case) or MXFP8 (wfmt "mxfp8"), quantized expert by expert (draw
-    order as in moe_case)."""
-    if wfmt not in ("mxfp4", "mxfp8"):
+    """fp8-activation MoE: logits N(0,1); x N(0,1); w1 N(0,1/H), w2 N(0,1/I), quantized
+    expert by expert (draw order as in moe_case) to MXFP4 (wfmt "mxfp4", the W4A8 case;
+    x MXFP8), MXFP8 (wfmt "mxfp8"; x MXFP8) or per-tensor fp8 (wfmt "fp8"; x too, and
+    the FC1 output scale is FP8_ACT_SCALE)."""
+    if wfmt not in ("mxfp4", "mxfp8", "fp8"):
         raise ValueError(wfmt)
-    quant = mx_quant_e2m1 if wfmt == "mxfp4" else mx_quant_e4m3
+    pt = wfmt == "fp8"
+    quant = {"mxfp4": mx_quant_e2m1, "mxfp8": mx_quant_e4m3, "fp8": fp8_quant_per_tensor}[wfmt]
     per = 2 if wfmt == "mxfp4" else 1    # elements per byte
     g = np.random.default_rng(seed)
     logits = route_logits(g, T, E)
     xa = g.standard_normal((T, H), dtype=np.float32)
     if x_scale != 1.0:
         xa *= np.float32(x_scale)
-    x, x_sf = mx_quant_e4m3(xa)
+    if pt:
+        x, xs = fp8_quant_per_tensor(xa)
+        x_sf = np.array([xs], np.float32)
+    else:
+        x, x_sf = mx_quant_e4m3(xa)
     w1 = np.empty((E, 2 * I, H // per), np.uint8)
-    w1_sf = np.empty((E, 2 * I, H // 32), np.uint8)
+    w1_sf = np.empty((E,), np.float32) if pt else np.empty((E, 2 * I, H // 32), np.uint8)
     w2 = np.empty((E, H, I // per), np.uint8)
-    w2_sf = np.empty((E, H, I // 32), np.uint8)
+    w2_sf = np.empty((E,), np.float32) if pt else np.empty((E, H, I // 32), np.uint8)
 
     def fill(e: int) -> None:
         a = np.random.default_rng([seed, 1, e]).standard_normal((2 * I, H), dtype=np.float32)
@@ -340,4 +369,5 @@ def w4a8_moe(seed: int = 0, T: int = 8192, H: int = 7168, I: int = 2048, E: int 
 
     with ThreadPoolExecutor(max_workers=min(_THREADS, E)) as ex:
         list(ex.map(fill, range(E)))
-    return W4A8Case(T, H, I, E, top_k, logits, x, x_sf, w1, w1_sf, w2, w2_sf, wfmt)
+    act_scale = np.array([FP8_ACT_SCALE], np.float32) if pt else None
+    return W4A8Case(T, H, I, E, top_k, logits, x, x_sf, w1, w1_sf, w2, w2_sf, wfmt, act_scale)

@@ -9,8 +9,9 @@ function follows one passage of the documentation pages it cites:
 
 * "flashinfer.experimental.cake_stepfun_moe" (the StepFun page): stage list
   (routing "Renormalize top-k", FC1 with the StepFun epilogue, FC2, finalize),
-  the per-expert clamp limit of SwiGLUStep (default 7.0), and the
-  ``expanded_idx_to_permuted_idx`` output of the prepared launch.
+  the per-expert clamp limit of SwiGLUStep (default 7.0), the
+  ``expanded_idx_to_permuted_idx`` output of the prepared launch, and its list
+  of weight families (bf16, fp8 per-tensor, mxfp8 among them).
 * "flashinfer.fused_moe.cake / cake_cute (MXFP4 SiTU routed MoE)" (the W4A8
   page): the MXFP8 activation / MXFP4 weight layouts with UE8M0 block-32
   scales, the canonical [up | gate] w1 bank, fp32 accumulation and the UE8M0
@@ -28,7 +29,10 @@ Readings taken where the pages are silent (each is listed in the design doc):
 routing selects on the raw logits with ties to the lower expert id; the sort
 is stable and unpadded; SwiGLUStep clamps both halves symmetrically; a route
 to an expert outside the local shard (or outside [0, E)) contributes zero; the
-requantized scale is the smallest power of two that fits the block maximum.
+requantized scale is the smallest power of two that fits the block maximum;
+the fp8 per-tensor family (named on the StepFun page without a layout) holds
+e4m3fn codes with one float32 scale for x, one per expert matrix, and a static
+float32 scale for the requantized FC1 output, whose codes saturate at +-448.
 
 Parity pins for every function live in tests/test_oracle_*.py. Parity
 unpinned: none of the functions below; the SwiGLUStep formula itself is a
@@ -44,7 +48,7 @@ __all__ = [
     "grouped_gemm_wgrad", "silu", "activation", "moe_forward", "moe_route_outputs",
     "finalize", "e4m3_decode", "e4m3_encode", "e2m1_decode", "ue8m0_decode",
     "mx_dequant", "requant_e4m3", "minifloat_decode", "unpack_e2m1", "mx_dequant_fp4",
-    "mx_dequant_fp8",
+    "mx_dequant_fp8", "fp8_dequant", "requant_e4m3_per_tensor",
 ]
 
 
@@ -200,13 +204,16 @@ def activation(h, kind: str, limit: float = 7.0):
 
 
 def moe_route_outputs(x, topk_ids, w1, w2, *, num_experts, local_offset=0,
-                      activation_kind="swiglu", limits=None, requant=False):
+                      activation_kind="swiglu", limits=None, requant=False, act_scale=None):
     """y[t, s] = ffn(x[t]; e[t,s]) for every route to a local expert (zeros for
     foreign routes). Returns float64 [T, k, H] and the local-route mask [T, k].
 
     ``requant`` applies the MXFP8 requantization of the activation (W4A8 page,
-    intro: UE8M0 round-up requantization) before FC2.
+    intro: UE8M0 round-up requantization) before FC2; ``act_scale`` instead
+    applies the fp8 per-tensor requantization with that static scale.
     """
+    if requant and act_scale is not None:
+        raise ValueError("requant and act_scale are exclusive")
     x = np.asarray(x, dtype=np.float64)
     ids = np.asarray(topk_ids, dtype=np.int64)
     T, k = ids.shape
@@ -225,17 +232,19 @@ def moe_route_outputs(x, topk_ids, w1, w2, *, num_experts, local_offset=0,
         a = activation(h, activation_kind, lim)
         if requant:
             a = mx_dequant(*requant_e4m3(a.astype(np.float32)))
+        elif act_scale is not None:
+            a = requant_e4m3_per_tensor(a.astype(np.float32), act_scale)[0]
         y[tt, ss] = a @ w2e.T
     return y, loc >= 0
 
 
 def moe_forward(x, topk_ids, topk_weights, w1, w2, *, num_experts, local_offset=0,
-                activation_kind="swiglu", limits=None, requant=False):
+                activation_kind="swiglu", limits=None, requant=False, act_scale=None):
     """out[t] = sum over slots s (ascending) of w[t,s] * ffn(x[t]; e[t,s]),
     foreign routes contributing zero -> float64 [T, H] (unrounded)."""
     y, local = moe_route_outputs(x, topk_ids, w1, w2, num_experts=num_experts,
                                  local_offset=local_offset, activation_kind=activation_kind,
-                                 limits=limits, requant=requant)
+                                 limits=limits, requant=requant, act_scale=act_scale)
     w = np.asarray(topk_weights, dtype=np.float64)
     out = np.zeros((y.shape[0], y.shape[2]))
     for s in range(y.shape[1]):
@@ -382,3 +391,30 @@ def mx_dequant_fp4(packed, scale_codes, block: int = 32):
 def mx_dequant_fp8(codes, scale_codes, block: int = 32):
     """MXFP8 (e4m3fn codes) -> float64 with UE8M0 block-32 scales."""
     return mx_dequant(e4m3_decode(codes), scale_codes, block)
+
+
+# ---------------------------------------------------------------------------
+# fp8 with per-tensor scales -- StepFun page, intro (the "fp8 (per-tensor)"
+# weight family). The pages give no layout; the reading taken: e4m3fn codes, one
+# float32 scale per tensor (x, the FC1 output) or per expert matrix (w1[e], w2[e]).
+# ---------------------------------------------------------------------------
+def fp8_dequant(codes, scale):
+    """value = e4m3fn code value * scale; ``scale`` broadcasts against the leading
+    axes (a scalar, or one value per expert for a [L, rows, cols] bank)."""
+    v = e4m3_decode(codes)
+    sc = np.asarray(scale, dtype=np.float64)
+    return v * sc.reshape(sc.shape + (1,) * (v.ndim - sc.ndim))
+
+
+def requant_e4m3_per_tensor(a32, scale):
+    """Per-tensor fp8 requantization of float32 values with a static scale:
+    code = RNE_e4m3(clamp(a * r, -448, 448)) where r = float32(1 / scale) and the
+    product is rounded to float32 (the decision is taken in float32); saturating,
+    since a static scale need not fit the data. Returns (code value * scale as
+    float64, codes uint8)."""
+    a = np.asarray(a32, dtype=np.float32)
+    s32 = np.float32(scale)
+    r = np.float32(1.0) / s32
+    y = np.clip((a * r).astype(np.float32), np.float32(-448.0), np.float32(448.0))
+    codes = e4m3_encode(y.astype(np.float64))
+    return e4m3_decode(codes) * float(s32), codes

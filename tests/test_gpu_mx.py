@@ -1,10 +1,12 @@
-"""GPU parity: the MX-weight / MXFP8-activation layers against the oracle: MXFP4 weights
-(the W4A8 page's layer) and MXFP8 weights (e4m3 codes, same UE8M0 block-32 scales).
+"""GPU parity: the fp8-activation layers against the oracle: MXFP4 weights (the W4A8
+page's layer), MXFP8 weights (e4m3 codes, same UE8M0 block-32 scales) and fp8 with
+per-tensor scales (StepFun page, intro: the fp8 per-tensor weight family).
 
 The oracle works on the dequantized operands in float64 and models the one
-lossy step of the method, the MXFP8 requantization of the FC1 output
-(W4A8 page, intro: UE8M0 round-up). Tolerance for fp8 / MXFP4 outputs:
-max-abs 8e-2 (applied as |d| / max(1, |ref|)) and relative L2 3e-2.
+lossy step of the method, the requantization of the FC1 output (MXFP8 with the
+UE8M0 round-up of the W4A8 page's intro, or e4m3 with the static per-tensor
+scale). Tolerance for these outputs: max-abs 8e-2 (applied as |d| / max(1, |ref|))
+and relative L2 3e-2.
 """
 import numpy as np
 import pytest
@@ -20,10 +22,12 @@ DEV = "cuda"
 MX_MAX_ABS, MX_REL = 8e-2, 3e-2
 
 
-WFMTS = ["mxfp4", "mxfp8"]
+WFMTS = ["mxfp4", "mxfp8", "fp8"]
 
 
 def _deq(wfmt, codes, scales):
+    if wfmt == "fp8":
+        return O.fp8_dequant(codes, scales)
     return (O.mx_dequant_fp4 if wfmt == "mxfp4" else O.mx_dequant_fp8)(codes, scales)
 
 
@@ -33,7 +37,7 @@ class _LazyBank:
 
     def __init__(self, codes, scales, wfmt, cache=None):
         self.codes, self.scales, self.wfmt, self.cache = codes, scales, wfmt, cache
-        self.shape = (codes.shape[0], codes.shape[1], scales.shape[2] * 32)
+        self.shape = (codes.shape[0], codes.shape[1], codes.shape[2] * (2 if wfmt == "mxfp4" else 1))
 
     def __getitem__(self, e):
         if self.cache is not None and e in self.cache:
@@ -45,8 +49,8 @@ class _LazyBank:
 
 
 def _dev(c):
-    return {k: torch.from_numpy(np.ascontiguousarray(getattr(c, k))).to(DEV)
-            for k in ("x", "x_sf", "w1", "w1_sf", "w2", "w2_sf")}
+    keys = ("x", "x_sf", "w1", "w1_sf", "w2", "w2_sf") + (("act_scale",) if c.wfmt == "fp8" else ())
+    return {k: torch.from_numpy(np.ascontiguousarray(getattr(c, k))).to(DEV) for k in keys}
 
 
 def _oracle(c, ids, w, tokens=None, num_experts=None, local_offset=0, L=None,
@@ -54,22 +58,33 @@ def _oracle(c, ids, w, tokens=None, num_experts=None, local_offset=0, L=None,
     ids_n, w_n = ids.cpu().numpy(), w.cpu().numpy().astype(np.float64)
     x, xs = c.x, c.x_sf
     if tokens is not None:
-        x, xs, ids_n, w_n = x[tokens], xs[tokens], ids_n[tokens], w_n[tokens]
+        x, ids_n, w_n = x[tokens], ids_n[tokens], w_n[tokens]
+        xs = xs if c.wfmt == "fp8" else xs[tokens]
     w1, w1s, w2, w2s = c.w1, c.w1_sf, c.w2, c.w2_sf
     if L is not None:
         w1, w1s = w1[local_offset:local_offset + L], w1s[local_offset:local_offset + L]
         w2, w2s = w2[local_offset:local_offset + L], w2s[local_offset:local_offset + L]
-    return O.moe_forward(O.mx_dequant_fp8(x, xs), ids_n, w_n, _LazyBank(w1, w1s, c.wfmt, cache1),
+    pt = c.wfmt == "fp8"
+    xd = O.fp8_dequant(x, xs[0]) if pt else O.mx_dequant_fp8(x, xs)
+    return O.moe_forward(xd, ids_n, w_n, _LazyBank(w1, w1s, c.wfmt, cache1),
                          _LazyBank(w2, w2s, c.wfmt, cache2),
                          num_experts=num_experts or c.num_experts, local_offset=local_offset,
-                         activation_kind=activation, limits=limits, requant=True)
+                         activation_kind=activation, limits=limits, requant=not pt,
+                         act_scale=float(c.act_scale[0]) if pt else None)
+
+
+def _fwd(c, d, ids, w, w1, w1s, w2, w2s, **kw):
+    """The layer through the entry point of the case's weight family."""
+    if c.wfmt == "fp8":
+        return M.moe_ffn_forward_fp8(d["x"], d["x_sf"], ids, w, w1, w1s, w2, w2s, d["act_scale"],
+                                     c.num_experts, **kw)
+    return M.moe_ffn_forward_mx(d["x"], d["x_sf"], ids, w, w1, w1s, w2, w2s, c.num_experts, **kw)
 
 
 def _run(c, d, ids=None, w=None, **kw):
     if ids is None:
         ids, w = M.moe_route(torch.from_numpy(c.logits).to(DEV), c.top_k)
-    out = M.moe_ffn_forward_mx(d["x"], d["x_sf"], ids, w, d["w1"], d["w1_sf"], d["w2"], d["w2_sf"],
-                               c.num_experts, **kw)
+    out = _fwd(c, d, ids, w, d["w1"], d["w1_sf"], d["w2"], d["w2_sf"], **kw)
     return out, ids, w
 
 
@@ -115,16 +130,15 @@ def test_mx_shard_and_step_activation(T, wfmt):
     L, off = 6, 5
     lim = torch.tensor(np.linspace(2.0, 4.0, L), dtype=torch.float32, device=DEV)
     ids, w = M.moe_route(torch.from_numpy(c.logits).to(DEV), c.top_k)
-    out = M.moe_ffn_forward_mx(d["x"], d["x_sf"], ids, w, d["w1"][off:off + L], d["w1_sf"][off:off + L],
-                               d["w2"][off:off + L], d["w2_sf"][off:off + L], c.num_experts,
-                               num_local_experts=L, local_expert_offset=off, activation="swiglu_step",
-                               clamp_limit=lim)
+    out = _fwd(c, d, ids, w, d["w1"][off:off + L], d["w1_sf"][off:off + L], d["w2"][off:off + L],
+               d["w2_sf"][off:off + L], num_local_experts=L, local_expert_offset=off,
+               activation="swiglu_step", clamp_limit=lim)
     ref = _oracle(c, ids, w, L=L, local_offset=off, activation="swiglu_step",
                   limits=lim.cpu().numpy())
     assert_close_bf16(out, ref, MX_MAX_ABS, MX_REL, what=f"{wfmt} shard step")
 
 
-@pytest.mark.parametrize("wfmt", WFMTS)
+@pytest.mark.parametrize("wfmt", ["mxfp4", "mxfp8"])
 @pytest.mark.parametrize("T", [256, 24])
 def test_fc1_requant_matches_oracle_rule(T, wfmt):
     """The fused UE8M0 round-up requantization: scale codes equal the oracle's (rare
@@ -159,6 +173,56 @@ def test_fc1_requant_matches_oracle_rule(T, wfmt):
     assert np.mean(np.abs(deq - a_ref) <= bound) > 0.999
 
 
+@pytest.mark.parametrize("T", [256, 24])
+def test_fp8_fc1_per_tensor_requant_matches_oracle_rule(T):
+    """The per-tensor requantization (static scale, float32 reciprocal, saturation at
+    +-448): codes equal the oracle's apart from rare flips within the float32
+    accumulation error of the activation. x_scale 4 drives some activations past the
+    saturation point 448 * act_scale = 16. T=256 runs the 256-row tile kernel, T=24
+    the decode kernel."""
+    c = S.w4a8_moe(seed=7, T=T, H=512, I=512, E=4, top_k=2, wfmt="fp8", x_scale=4.0)
+    d = _dev(c)
+    ids, w = M.moe_route(torch.from_numpy(c.logits).to(DEV), c.top_k)
+    srt = M.moe_sort(ids, c.num_experts)
+    act = M.moe_fc1_fp8(d["x"], d["x_sf"], d["w1"], d["w1_sf"], d["act_scale"], srt["offs"],
+                        srt["p2e"], c.top_k, c.num_experts)
+    n = int(srt["n_local"].item())
+    p2e = srt["p2e"][:n].cpu().numpy()
+    offs = srt["offs"].cpu().numpy()
+    xd = O.fp8_dequant(c.x, c.x_sf[0])
+    I = c.I
+    h = np.zeros((n, 2 * I))
+    habs = np.zeros((n, 2 * I))      # sum over k of |x_k w_k|, which bounds the rounding
+    start = 0
+    for e in range(c.num_experts):
+        rows = slice(start, int(offs[e]))
+        w1 = O.fp8_dequant(c.w1[e], c.w1_sf[e])
+        xr = xd[p2e[rows] // c.top_k]
+        h[rows] = xr @ w1.T
+        habs[rows] = np.abs(xr) @ np.abs(w1).T
+        start = int(offs[e])
+    a_ref = O.activation(h, "swiglu")
+    _, codes = O.requant_e4m3_per_tensor(a_ref.astype(np.float32), c.act_scale[0])
+    got = act[:n].cpu().numpy()
+    sat = np.abs(a_ref) > 16.5
+    assert np.mean(sat) > 1e-4                               # saturation is exercised
+    assert np.all(O.e4m3_decode(got[sat]) == 448.0 * np.sign(a_ref[sat]))
+    assert np.mean(got == codes) > 0.995
+    # where they differ, by one code step plus the float32 accumulation error of the
+    # activation: a float32 sum of K = 512 products is off by at most
+    # K * 2^-24 * sum|x_k w_k| = 2^-15 * sum|x_k w_k| (2^-14 taken for margin), carried
+    # through silu(g) * u; it matters where u or g nearly cancels and in the subnormal
+    # codes (steps of 2^-9 * act_scale)
+    s = float(c.act_scale[0])
+    gv, rv = O.e4m3_decode(got) * s, O.e4m3_decode(codes) * s
+    u, g = h[:, :I], h[:, I:]
+    sig = 1.0 / (1.0 + np.exp(-g))
+    dsilu = np.abs(sig * (1.0 + g * (1.0 - sig)))
+    da = 2.0 ** -14 * (np.abs(g * sig) * habs[:, :I] + dsilu * np.abs(u) * habs[:, I:])
+    step = np.maximum(np.abs(rv), np.abs(gv)) * 2.0 ** -3 + 2.0 ** -9 * s
+    assert np.all(np.abs(gv - rv) <= step + da)
+
+
 @pytest.mark.parametrize("wfmt", WFMTS)
 def test_mx_zero_tokens_and_replay(wfmt):
     c = S.w4a8_moe(seed=8, T=64, H=256, I=256, E=8, top_k=2, wfmt=wfmt)
@@ -168,8 +232,8 @@ def test_mx_zero_tokens_and_replay(wfmt):
     assert torch.equal(o1, o2)
     e = torch.empty((0, 2), dtype=torch.int32, device=DEV)
     ew = torch.empty((0, 2), dtype=torch.float32, device=DEV)
-    z = M.moe_ffn_forward_mx(d["x"][:0], d["x_sf"][:0], e, ew, d["w1"], d["w1_sf"], d["w2"],
-                             d["w2_sf"], c.num_experts)
+    d0 = dict(d, x=d["x"][:0], x_sf=d["x_sf"] if wfmt == "fp8" else d["x_sf"][:0])
+    z = _fwd(c, d0, e, ew, d["w1"], d["w1_sf"], d["w2"], d["w2_sf"])
     assert z.shape == (0, 256)
 
 
@@ -183,8 +247,9 @@ def test_mx_full_shape_sampled(mx_full, T):
     """H=7168, I=2048, 64 experts, top-8 at the decode and prefill token counts, for
     both weight families; two sampled tokens are checked against the oracle."""
     full, cache1, cache2 = mx_full
+    x_sf = full.x_sf if full.wfmt == "fp8" else full.x_sf[:T]
     c = S.W4A8Case(T, full.H, full.I, full.num_experts, full.top_k, full.logits[:T], full.x[:T],
-                   full.x_sf[:T], full.w1, full.w1_sf, full.w2, full.w2_sf, full.wfmt)
+                   x_sf, full.w1, full.w1_sf, full.w2, full.w2_sf, full.wfmt, full.act_scale)
     out, ids, w = _run(c, _dev(c))
     torch.cuda.synchronize()
     # token 0 routes identically at every T (the logits are shared), so its experts are

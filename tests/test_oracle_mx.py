@@ -115,3 +115,88 @@ def test_mx_dequant_fp8_scales_each_block():
     v = O.mx_dequant_fp8(codes, np.array([[127 + 3, 127 - 2]], np.uint8))
     np.testing.assert_array_equal(v[0, :32], 8.0)
     np.testing.assert_array_equal(v[0, 32:], 0.25)
+
+
+# --- fp8 per-tensor family (StepFun page, intro: fp8 per-tensor weights) ----------
+def _torch_pt_codes(a32, scale):
+    """Independent route: torch float32 reciprocal and product, clamp, float8 cast."""
+    t = torch.from_numpy(np.asarray(a32, np.float32))
+    r = torch.tensor(1.0, dtype=torch.float32) / torch.tensor(scale, dtype=torch.float32)
+    y = (t * r).clamp(-448.0, 448.0)
+    return y.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+@pytest.mark.parametrize("scale", [0.5, 3.0, 0.0357, 1.7e-3])
+def test_per_tensor_requant_matches_torch_float32_route(scale):
+    g = np.random.default_rng(11)
+    a = (g.standard_normal(200000) * np.exp(g.uniform(-10, 9, 200000))).astype(np.float32)
+    vals, codes = O.requant_e4m3_per_tensor(a, scale)
+    ref = _torch_pt_codes(a, scale)
+    same = (codes == ref) | (((codes & 0x7F) == 0) & ((ref & 0x7F) == 0))
+    assert same.all(), a[~same][:8]
+    np.testing.assert_array_equal(
+        vals, torch.from_numpy(codes).view(torch.float8_e4m3fn).double().numpy() * float(np.float32(scale)))
+
+
+def test_per_tensor_requant_saturates_and_keeps_sign():
+    s = 0.25
+    a = np.array([1e30, -1e30, 448 * s, -448 * s, 464 * s, 0.0, -0.0], np.float32)
+    vals, codes = O.requant_e4m3_per_tensor(a, s)
+    assert list(codes[:5]) == [0x7E, 0xFE, 0x7E, 0xFE, 0x7E]          # +-448, never NaN
+    np.testing.assert_array_equal(vals[:2], [448 * s, -448 * s])
+    assert np.all(vals[5:] == 0)
+
+
+def test_per_tensor_requant_decides_on_the_float32_reciprocal():
+    # a = 7 * 0.048828125 is exact in float32, and a / 7 = 0.048828125 is the tie
+    # between the e4m3 values 0.046875 (even mantissa) and 0.05078125; the float32
+    # reciprocal of 7 is rounded up, so the float32 product lands just above the tie
+    # and the code rounds up, where an exact division would round down
+    a = np.array([0.341796875], np.float32)
+    assert float(a[0]) / 7.0 == 0.048828125
+    assert float(np.float32(a[0] * (np.float32(1.0) / np.float32(7.0)))) > 0.048828125
+    _, codes = O.requant_e4m3_per_tensor(a, 7.0)
+    assert O.e4m3_decode(codes)[0] == 0.05078125
+    assert _torch_pt_codes(a, 7.0)[0] == codes[0]
+
+
+def test_fp8_dequant_per_expert_broadcast():
+    codes = np.full((3, 2, 4), 0x38, np.uint8)                 # e4m3 1.0
+    v = O.fp8_dequant(codes, np.array([1.0, 2.0, 0.5], np.float32))
+    np.testing.assert_array_equal(v[:, 0, 0], [1.0, 2.0, 0.5])
+    assert np.all(v == v[:, :1, :1])
+    np.testing.assert_array_equal(O.fp8_dequant(np.array([0xB8, 0x7E], np.uint8), 0.5), [-0.5, 224.0])
+
+
+def test_moe_forward_fp8_per_tensor_matches_torch_pipeline():
+    """The forward with the per-tensor requantization against a torch pipeline that
+    decodes with torch's float8 type and re-encodes with torch's cast."""
+    import math
+    g = np.random.default_rng(12)
+    T, H, I, E, k = 6, 32, 16, 3, 2
+    xq = torch.from_numpy(g.standard_normal((T, H)).astype(np.float32) * 3).to(torch.float8_e4m3fn)
+    w1q = torch.from_numpy((g.standard_normal((E, 2 * I, H)) / math.sqrt(H)).astype(np.float32) * 64).to(
+        torch.float8_e4m3fn)
+    w2q = torch.from_numpy((g.standard_normal((E, H, I)) / math.sqrt(I)).astype(np.float32) * 64).to(
+        torch.float8_e4m3fn)
+    xs = np.float32(0.5)
+    w1s = np.array([1 / 64, 1 / 32, 3 / 256], np.float32)
+    w2s = np.array([1 / 64, 1 / 128, 5 / 256], np.float32)
+    act_s = 0.03
+    ids = np.stack([g.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    w = g.random((T, k))
+    got = O.moe_forward(O.fp8_dequant(xq.view(torch.uint8).numpy(), xs), ids, w,
+                        O.fp8_dequant(w1q.view(torch.uint8).numpy(), w1s),
+                        O.fp8_dequant(w2q.view(torch.uint8).numpy(), w2s), num_experts=E,
+                        act_scale=act_s)
+    ref = torch.zeros((T, H), dtype=torch.float64)
+    xd = xq.double() * float(xs)
+    for t in range(T):
+        for s in range(k):
+            e = int(ids[t, s])
+            h = xd[t] @ (w1q[e].double() * float(w1s[e])).T
+            a = torch.nn.functional.silu(h[I:]) * h[:I]
+            aq = torch.from_numpy(_torch_pt_codes(a.float().numpy(), act_s)).view(torch.float8_e4m3fn)
+            y = (aq.double() * float(np.float32(act_s))) @ (w2q[e].double() * float(w2s[e])).T
+            ref[t] += w[t, s] * y
+    np.testing.assert_allclose(got, ref.numpy(), rtol=1e-12, atol=1e-12)
