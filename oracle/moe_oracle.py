@@ -17,7 +17,8 @@ function follows one passage of the documentation pages it cites:
   scales, the canonical [up | gate] w1 bank, fp32 accumulation and the UE8M0
   round-up requantization.
 * "Cake ragged BF16 grouped GEMM (experimental)" (the grouped-GEMM page): the
-  fwd / dgrad / wgrad operation table and the ragged ``offs`` convention.
+  fwd / dgrad / wgrad operation table and the ragged ``offs`` convention; its
+  Autograd section (a backward made of dgrad and wgrad) for the layer backward.
 * "flashinfer.fused_moe.cute_dsl_fused_moe_bf16" (the SM90 fused-MoE page):
   the forward formula, the EP shard rule and the two finalize paths.
 
@@ -48,7 +49,8 @@ __all__ = [
     "grouped_gemm_wgrad", "silu", "activation", "moe_forward", "moe_route_outputs",
     "finalize", "e4m3_decode", "e4m3_encode", "e2m1_decode", "ue8m0_decode",
     "mx_dequant", "requant_e4m3", "minifloat_decode", "unpack_e2m1", "mx_dequant_fp4",
-    "mx_dequant_fp8", "fp8_dequant", "requant_e4m3_per_tensor",
+    "mx_dequant_fp8", "fp8_dequant", "requant_e4m3_per_tensor", "activation_backward",
+    "moe_backward", "route_backward",
 ]
 
 
@@ -418,3 +420,96 @@ def requant_e4m3_per_tensor(a32, scale):
     y = np.clip((a * r).astype(np.float32), np.float32(-448.0), np.float32(448.0))
     codes = e4m3_encode(y.astype(np.float64))
     return e4m3_decode(codes) * float(s32), codes
+
+
+# ---------------------------------------------------------------------------
+# Backward of the layer -- grouped-GEMM page, operation table and Autograd
+# section: the backward of each grouped product is its dgrad (dX = G W) and its
+# wgrad (dW = G^T X, exactly zero for an empty group). The rest is the chain rule
+# through the forward formula of the SM90 fused-MoE page and the activation; the
+# clamp of SwiGLUStep passes the gradient where min <= v <= max (a reading: the
+# pages give no backward).
+# ---------------------------------------------------------------------------
+def activation_backward(h, da, kind: str, limit: float = 7.0):
+    """dh [..., 2I] = d activation(h) / d h applied to da [..., I] (h = [up | gate]).
+
+    swiglu:      du = da * silu(g),  dg = da * u * silu'(g),
+                 silu'(g) = s (1 + g (1 - s)) with s = 1 / (1 + exp(-g))
+    swiglu_step: the same at the clamped values, times [-L <= u <= L] for du and
+                 [-L <= g <= L] for dg
+    """
+    h = np.asarray(h, dtype=np.float64)
+    da = np.asarray(da, dtype=np.float64)
+    I = h.shape[-1] // 2
+    u, g = h[..., :I], h[..., I:]
+    mu = np.ones_like(u)
+    mg = np.ones_like(g)
+    if kind == "swiglu_step":
+        mu = ((u >= -limit) & (u <= limit)).astype(np.float64)
+        mg = ((g >= -limit) & (g <= limit)).astype(np.float64)
+        u, g = np.clip(u, -limit, limit), np.clip(g, -limit, limit)
+    elif kind != "swiglu":
+        raise ValueError(kind)
+    with np.errstate(over="ignore"):
+        sg = 1.0 / (1.0 + np.exp(-g))
+    du = da * g * sg * mu
+    dg = da * u * sg * (1.0 + g * (1.0 - sg)) * mg
+    return np.concatenate([du, dg], axis=-1)
+
+
+def moe_backward(x, topk_ids, topk_weights, w1, w2, dout, *, num_experts, local_offset=0,
+                 activation_kind="swiglu", limits=None):
+    """Gradients of moe_forward (same arguments) for an upstream gradient dout [T, H]:
+    returns (dx [T, H], dw1 [L, 2I, H], dw2 [L, H, I], dtopk_weights [T, k]), float64.
+
+    For a route (t, s) to local expert e, with h = x[t] @ w1[e].T, a = act(h),
+    y = a @ w2[e].T:  dtopk_weights[t, s] = <dout[t], y>;  dy = w[t, s] dout[t];
+    dw2[e] += dy^T a;  da = dy @ w2[e];  dh = act'(h) da;  dw1[e] += dh^T x[t];
+    dx[t] += dh @ w1[e]. Foreign routes contribute nothing (their weight gradient
+    is 0), and an expert without routes gets exactly zero weight gradients.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    dout = np.asarray(dout, dtype=np.float64)
+    w = np.asarray(topk_weights, dtype=np.float64)
+    ids = np.asarray(topk_ids, dtype=np.int64)
+    T, k = ids.shape
+    L = w1.shape[0]
+    loc = local_expert(ids, num_experts, L, local_offset).reshape(T, k)
+    dx = np.zeros_like(x)
+    dw1 = np.zeros((L,) + tuple(w1.shape[1:]))
+    dw2 = np.zeros((L,) + tuple(w2.shape[1:]))
+    dwt = np.zeros((T, k))
+    for e in range(L):
+        tt, ss = np.nonzero(loc == e)
+        if tt.size == 0:
+            continue
+        w1e = np.asarray(w1[e], dtype=np.float64)
+        w2e = np.asarray(w2[e], dtype=np.float64)
+        lim = 7.0 if limits is None else float(limits[e])
+        h = x[tt] @ w1e.T
+        a = activation(h, activation_kind, lim)
+        y = a @ w2e.T
+        dwt[tt, ss] = np.sum(dout[tt] * y, axis=1)
+        dy = w[tt, ss][:, None] * dout[tt]
+        dw2[e] = dy.T @ a
+        dh = activation_backward(h, dy @ w2e, activation_kind, lim)
+        dw1[e] = dh.T @ x[tt]
+        np.add.at(dx, tt, dh @ w1e)
+    return dx, dw1, dw2, dwt
+
+
+def route_backward(topk_ids, topk_weights, dtopk_weights, num_experts: int):
+    """Gradient of the routing logits through the Renormalize weights (StepFun page,
+    intro): w = softmax over the k selected logits, so for a selected expert j at
+    slot s, dlogits[t, j] = w[t, s] (dw[t, s] - sum_r w[t, r] dw[t, r]); the
+    selection itself is piecewise constant, so unselected logits get 0."""
+    ids = np.asarray(topk_ids, dtype=np.int64)
+    w = np.asarray(topk_weights, dtype=np.float64)
+    dw = np.asarray(dtopk_weights, dtype=np.float64)
+    T, k = ids.shape
+    dl = np.zeros((T, num_experts))
+    inner = np.sum(w * dw, axis=1, keepdims=True)
+    g = w * (dw - inner)
+    for s in range(k):
+        dl[np.arange(T), ids[:, s]] += g[:, s]
+    return dl
