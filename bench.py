@@ -236,10 +236,37 @@ def main():
         "wall_s_timed": round(wall, 3),
     }
     if not args.no_secondary:
+        progress("timing the training forward and the backward at the same shape")
+        line["training"] = _training(x, w1, w2, ids, wts, E, n_local)
         del x, w1, w2, act, y, out, out_fused
         torch.cuda.empty_cache()
         line["secondary"] = secondary_measurements(progress)
     print(json.dumps(line), flush=True)
+
+
+def _training(x, w1, w2, ids, wts, E, n_local):
+    """The bf16 layer's training forward (which also keeps h, act, y) and its backward
+    (dx, dw1, dw2 in bf16, routing-weight gradients) on the benchmark batch; the upstream
+    gradient is seeded N(0, 1). Backward work: dgrad + wgrad of both grouped products,
+    12 H I flop per local route."""
+    import ctypes
+    import torch
+    import mixture_experts_expert_softmax_amd as M
+    import moe_synth as S
+    T, H = x.shape
+    I = w2.shape[2]
+    dout = S.upstream_grad(0, T, H).to(x.device)
+    out_t, saved = M.moe_ffn_forward_train(x, ids, wts, w1, w2, E)
+    d = M._train_desc(x, ids, w1, E, None, 0, "swiglu")
+    bws = torch.empty(max(M.lib().moe_ffn_backward_workspace_size(ctypes.byref(d)), 16),
+                      dtype=torch.uint8, device=x.device)
+    ms_f = _time(lambda: M.moe_ffn_forward_train(x, ids, wts, w1, w2, E, out=out_t, saved=saved))
+    ms_b = _time(lambda: M.moe_ffn_backward(dout, saved, x, ids, wts, w1, w2, E, workspace=bws))
+    fl_b = 12.0 * H * I * n_local
+    return {"fwd_train_ms": round(ms_f, 4), "bwd_ms": round(ms_b, 4),
+            "bwd_tflops": round(fl_b / (ms_b * 1e-3) / 1e12, 1),
+            "bwd_mfma_frac": round(fl_b / (ms_b * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+            "step_ms": round(ms_f + ms_b, 4), "timing": "mean of 10 back to back"}
 
 
 def _time(fn, reps=10, warmup=3, flush=None):

@@ -265,6 +265,62 @@ moe_status moe_fc2_fp8(const moe_ffn_desc* desc, const void* act, const float* a
                        void* stream);
 
 /*
+ * Training: forward with saved tensors, then the backward ([GGEMM] Autograd
+ * section: the backward of a grouped product is its dgrad and wgrad; the rest is
+ * the chain rule through the [SM90] formula). bf16 weights and
+ * MOE_FINALIZE_DETERMINISTIC only, otherwise MOE_ERR_UNSUPPORTED (size functions
+ * return 0).
+ *
+ * moe_ffn_forward_train: moe_ffn_forward (same tensors; tensors->e2p is ignored)
+ *   whose workspace is the caller's `saved` buffer of moe_ffn_saved_size(desc)
+ *   bytes, which afterwards holds what the backward reads: the routing metadata,
+ *   the FC1 pre-activations h [T*k, 2I] ([up | gate], float32: the values the
+ *   forward's activation and clamp saw), act and the unscaled FC2 rows y (bf16),
+ *   all in permuted order. Keep it unchanged until the backward.
+ * moe_ffn_backward: for the upstream gradient dout = d loss / d out [T, H] bf16,
+ *   with the same desc and tensors (x, topk_weights, w1, w2, clamp_limit):
+ *     dtopk_weights[t,s] = <dout[t], y[t,s]> (0 for foreign routes; float32),
+ *     dy = w[t,s] dout[t];  dw2[e] = sum over e's routes of dy^T act;
+ *     dh = act'(h) (dy @ w2[e]) -- SwiGLU: du = da silu(g), dg = da u silu'(g);
+ *       SwiGLUStep: the same at the clamped values, zero where |v| > L;
+ *     dw1[e] = sum of dh^T x[t];  dx[t] = sum over the token's local routes of
+ *     dh @ w1[e] (float32, slots ascending, one rounding; 0 for no local route).
+ *   dw1 [L, 2I, H], dw2 [L, H, I] in grad_dtype (fully overwritten; exactly zero
+ *   for an expert without routes), dx [T, H] bf16. Intermediates dy, dh are bf16;
+ *   every sum runs in a fixed order (bitwise reproducible). ws: at least
+ *   moe_ffn_backward_workspace_size(desc) bytes, 16-byte aligned.
+ */
+typedef struct moe_ffn_grads {
+  const void* dout;           /* [T, H] bf16 */
+  void* dx;                   /* [T, H] bf16 out */
+  void* dw1;                  /* [L, 2I, H] out, grad_dtype */
+  void* dw2;                  /* [L, H, I] out, grad_dtype */
+  float* dtopk_weights;       /* [T, top_k] float32 out, or NULL */
+  int32_t grad_dtype;         /* MOE_DTYPE_BF16 or MOE_DTYPE_F32 */
+} moe_ffn_grads;
+
+size_t moe_ffn_saved_size(const moe_ffn_desc* desc);
+moe_status moe_ffn_forward_train(const moe_ffn_desc* desc, const moe_ffn_tensors* tensors,
+                                 void* saved, size_t saved_bytes, void* stream);
+size_t moe_ffn_backward_workspace_size(const moe_ffn_desc* desc);
+moe_status moe_ffn_backward(const moe_ffn_desc* desc, const moe_ffn_tensors* tensors,
+                            const moe_ffn_grads* grads, const void* saved, size_t saved_bytes,
+                            void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_route_backward -- gradient of the routing logits through the Renormalize
+ * weights ([StepFun] intro): w[t,:] = softmax of the k selected logits, so for the
+ * expert j selected at slot s, dlogits[t, j] = w[t,s] (dw[t,s] - sum_r w[t,r] dw[t,r])
+ * (float32, r ascending); every other logit gets 0 (the selection is piecewise
+ * constant). topk_ids / topk_weights as returned by moe_route, dtopk_weights
+ * [T, top_k] float32, dlogits [T, num_experts] float32 fully overwritten.
+ * Rules as moe_route.
+ */
+moe_status moe_route_backward(const int32_t* topk_ids, const float* topk_weights,
+                              const float* dtopk_weights, int64_t T, int32_t num_experts,
+                              int32_t top_k, float* dlogits, void* stream);
+
+/*
  * moe_finalize -- deterministic top-k combine ([SM90] use_fused_finalize=False):
  *   out[t,:] = bf16_rne( sum over s = 0..top_k-1 with e2p[t*top_k+s] >= 0 of
  *                        topk_weights[t,s] * y[e2p[t*top_k+s], :] )

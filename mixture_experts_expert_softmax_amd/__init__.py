@@ -23,7 +23,7 @@ __all__ = [
     "grouped_gemm_dgrad", "grouped_gemm_wgrad", "moe_ffn_forward", "moe_ffn_workspace_size",
     "moe_finalize", "moe_fc1", "moe_fc2", "status_string", "ACT", "FINALIZE", "WFMT",
     "moe_ffn_forward_mx", "moe_fc1_mx", "moe_fc2_mx", "moe_ffn_forward_fp8", "moe_fc1_fp8",
-    "moe_fc2_fp8",
+    "moe_fc2_fp8", "moe_ffn_forward_train", "moe_ffn_backward", "moe_route_backward", "MoEFunction",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -53,6 +53,11 @@ class MoeFfnTensors(ctypes.Structure):
                 ("x_sf", _vp), ("w1_sf", _vp), ("w2_sf", _vp), ("act_scale", _vp)]
 
 
+class MoeFfnGrads(ctypes.Structure):
+    _fields_ = [("dout", _vp), ("dx", _vp), ("dw1", _vp), ("dw2", _vp), ("dtopk_weights", _vp),
+                ("grad_dtype", _i32)]
+
+
 # name -> (restype, argtypes)
 EXPORTS = {
     "moe_status_string": (ctypes.c_char_p, [_i32]),
@@ -74,6 +79,13 @@ EXPORTS = {
     "moe_fc2_mx": (_i32, [ctypes.POINTER(MoeFfnDesc), _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "moe_fc1_fp8": (_i32, [ctypes.POINTER(MoeFfnDesc), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "moe_fc2_fp8": (_i32, [ctypes.POINTER(MoeFfnDesc), _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "moe_ffn_saved_size": (_sz, [ctypes.POINTER(MoeFfnDesc)]),
+    "moe_ffn_forward_train": (_i32, [ctypes.POINTER(MoeFfnDesc), ctypes.POINTER(MoeFfnTensors), _vp,
+                                     _sz, _vp]),
+    "moe_ffn_backward_workspace_size": (_sz, [ctypes.POINTER(MoeFfnDesc)]),
+    "moe_ffn_backward": (_i32, [ctypes.POINTER(MoeFfnDesc), ctypes.POINTER(MoeFfnTensors),
+                                ctypes.POINTER(MoeFfnGrads), _vp, _sz, _vp, _sz, _vp]),
+    "moe_route_backward": (_i32, [_vp, _vp, _vp, _i64, _i32, _i32, _vp, _vp]),
 }
 
 _LIB: Optional[ctypes.CDLL] = None
@@ -275,6 +287,113 @@ def moe_ffn_forward(x: torch.Tensor, topk_ids: torch.Tensor, topk_weights: torch
     if finalize == "none":
         return y, e2p[: T * k]
     return out
+
+
+def _train_desc(x, topk_ids, w1, num_experts, num_local_experts, local_expert_offset, activation):
+    _dev(x, torch.bfloat16, "x"), _dev(w1, torch.bfloat16, "w1")
+    _dev(topk_ids, torch.int32, "topk_ids")
+    T, H = x.shape
+    L, twoI, _ = w1.shape
+    if num_local_experts is not None and num_local_experts != L:
+        raise ValueError("num_local_experts must equal w1.shape[0]")
+    return _ffn_desc(T, H, twoI // 2, num_experts, L, local_expert_offset, topk_ids.shape[1],
+                     activation, "deterministic")
+
+
+def moe_ffn_forward_train(x: torch.Tensor, topk_ids: torch.Tensor, topk_weights: torch.Tensor,
+                          w1: torch.Tensor, w2: torch.Tensor, num_experts: int,
+                          num_local_experts: Optional[int] = None, local_expert_offset: int = 0,
+                          activation: str = "swiglu", clamp_limit: Optional[torch.Tensor] = None,
+                          out: Optional[torch.Tensor] = None, saved: Optional[torch.Tensor] = None):
+    """The bf16 layer forward (deterministic finalize) that also keeps what the backward
+    needs. Returns (out [T, H] bf16, saved): pass `saved` unchanged to moe_ffn_backward."""
+    _dev(w2, torch.bfloat16, "w2"), _dev(topk_weights, torch.float32, "topk_weights")
+    if clamp_limit is not None:
+        _dev(clamp_limit, torch.float32, "clamp_limit")
+    d = _train_desc(x, topk_ids, w1, num_experts, num_local_experts, local_expert_offset, activation)
+    h = lib()
+    nbytes = h.moe_ffn_saved_size(ctypes.byref(d))
+    if saved is None:
+        saved = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=x.device)
+    if out is None:
+        out = torch.empty(tuple(x.shape), dtype=torch.bfloat16, device=x.device)
+    tens = MoeFfnTensors(x.data_ptr(), topk_ids.data_ptr(), topk_weights.data_ptr(), w1.data_ptr(),
+                         w2.data_ptr(), None if clamp_limit is None else clamp_limit.data_ptr(),
+                         out.data_ptr(), None, None, None, None, None)
+    _check("moe_ffn_forward_train", h.moe_ffn_forward_train(ctypes.byref(d), ctypes.byref(tens),
+                                                            _ptr(saved), saved.numel(), _stream()))
+    return out, saved
+
+
+def moe_ffn_backward(dout: torch.Tensor, saved: torch.Tensor, x: torch.Tensor,
+                     topk_ids: torch.Tensor, topk_weights: torch.Tensor, w1: torch.Tensor,
+                     w2: torch.Tensor, num_experts: int, num_local_experts: Optional[int] = None,
+                     local_expert_offset: int = 0, activation: str = "swiglu",
+                     clamp_limit: Optional[torch.Tensor] = None, grad_dtype=torch.bfloat16,
+                     need_topk_grad: bool = True, workspace: Optional[torch.Tensor] = None):
+    """Gradients of the layer for dout [T, H] bf16, with the tensors and `saved` of
+    moe_ffn_forward_train. Returns (dx [T,H] bf16, dw1 [L,2I,H], dw2 [L,H,I] in grad_dtype,
+    dtopk_weights [T,k] float32 or None)."""
+    _dev(dout, torch.bfloat16, "dout"), _dev(w2, torch.bfloat16, "w2")
+    _dev(topk_weights, torch.float32, "topk_weights"), _dev(saved, torch.uint8, "saved")
+    d = _train_desc(x, topk_ids, w1, num_experts, num_local_experts, local_expert_offset, activation)
+    h = lib()
+    ws = h.moe_ffn_backward_workspace_size(ctypes.byref(d))
+    if workspace is None:
+        workspace = torch.empty(max(ws, 16), dtype=torch.uint8, device=x.device)
+    dx = torch.empty(tuple(x.shape), dtype=torch.bfloat16, device=x.device)
+    dw1 = torch.empty(tuple(w1.shape), dtype=grad_dtype, device=x.device)
+    dw2 = torch.empty(tuple(w2.shape), dtype=grad_dtype, device=x.device)
+    dtw = torch.empty(tuple(topk_ids.shape), dtype=torch.float32, device=x.device) if need_topk_grad else None
+    tens = MoeFfnTensors(x.data_ptr(), topk_ids.data_ptr(), topk_weights.data_ptr(), w1.data_ptr(),
+                         w2.data_ptr(), None if clamp_limit is None else clamp_limit.data_ptr(),
+                         None, None, None, None, None, None)
+    grads = MoeFfnGrads(dout.data_ptr(), dx.data_ptr(), dw1.data_ptr(), dw2.data_ptr(),
+                        None if dtw is None else dtw.data_ptr(), DTYPE[grad_dtype])
+    _check("moe_ffn_backward", h.moe_ffn_backward(ctypes.byref(d), ctypes.byref(tens), ctypes.byref(grads),
+                                                  _ptr(saved), saved.numel(), _ptr(workspace),
+                                                  workspace.numel(), _stream()))
+    return dx, dw1, dw2, dtw
+
+
+def moe_route_backward(topk_ids: torch.Tensor, topk_weights: torch.Tensor,
+                       dtopk_weights: torch.Tensor, num_experts: int, dlogits=None):
+    """d loss / d logits [T, E] float32 through the Renormalize weights of moe_route."""
+    _dev(topk_ids, torch.int32, "topk_ids"), _dev(topk_weights, torch.float32, "topk_weights")
+    _dev(dtopk_weights, torch.float32, "dtopk_weights")
+    T, k = topk_ids.shape
+    if dlogits is None:
+        dlogits = torch.empty((T, num_experts), dtype=torch.float32, device=topk_ids.device)
+    _check("moe_route_backward", lib().moe_route_backward(_ptr(topk_ids), _ptr(topk_weights),
+                                                          _ptr(dtopk_weights), T, num_experts, k,
+                                                          _ptr(dlogits), _stream()))
+    return dlogits
+
+
+class MoEFunction(torch.autograd.Function):
+    """Autograd wrapper of the bf16 layer: out = MoEFunction.apply(x, topk_weights, w1, w2,
+    topk_ids, num_experts, local_expert_offset, activation, clamp_limit). Gradients flow to
+    x, topk_weights, w1 and w2 (bf16, like the parameters), each step in the library."""
+
+    @staticmethod
+    def forward(ctx, x, topk_weights, w1, w2, topk_ids, num_experts, local_expert_offset=0,
+                activation="swiglu", clamp_limit=None):
+        out, saved = moe_ffn_forward_train(x, topk_ids, topk_weights, w1, w2, num_experts,
+                                           local_expert_offset=local_expert_offset,
+                                           activation=activation, clamp_limit=clamp_limit)
+        ctx.save_for_backward(x, topk_weights, w1, w2, topk_ids, saved)
+        ctx.cfg = (num_experts, local_expert_offset, activation, clamp_limit)
+        return out
+
+    @staticmethod
+    def backward(ctx, dout):
+        x, topk_weights, w1, w2, topk_ids, saved = ctx.saved_tensors
+        num_experts, off, activation, clamp_limit = ctx.cfg
+        dx, dw1, dw2, dtw = moe_ffn_backward(
+            dout.contiguous(), saved, x, topk_ids, topk_weights, w1, w2, num_experts,
+            local_expert_offset=off, activation=activation, clamp_limit=clamp_limit,
+            need_topk_grad=ctx.needs_input_grad[1])
+        return dx, dtw, dw1, dw2, None, None, None, None, None
 
 
 def _split_ws(split: bool, workspace: Optional[torch.Tensor], device):

@@ -18,11 +18,18 @@ moe_status gemm_nt_enqueue(int epi, const void* A, const int32_t* a_gather, int 
                            int K, void* C, int64_t ldc, int I, const float* limits,
                            float def_limit, const float* route_w, const int32_t* p2e, int top_k,
                            hipStream_t st, void* split_ws = nullptr,
-                           int32_t* split_cnt = nullptr);
+                           int32_t* split_cnt = nullptr, void* h_out = nullptr);
 moe_status gemm_dgrad_enqueue(const void* G, const void* W, const int32_t* ends, int E, int64_t M,
-                              int N, int K, void* DX, hipStream_t st);
+                              int N, int K, void* DX, hipStream_t st, int act = 0,
+                              const void* h = nullptr, const float* limits = nullptr,
+                              float def_limit = 7.0f);
 moe_status gemm_wgrad_enqueue(const void* G, const void* X, const int32_t* ends, int E, int64_t M,
                               int N, int K, void* DW, bool out_f32, hipStream_t st);
+// defined in backward.hip
+moe_status gather_rows_enqueue(const void* src, const int32_t* p2e, const int32_t* ends, int L,
+                               int k, int H, int64_t R, void* dst, hipStream_t st);
+moe_status permute_bwd_enqueue(const void* dout, const int32_t* e2p, const float* w, const void* y,
+                               int64_t T, int k, int H, void* dy, float* dw, hipStream_t st);
 moe_status zero_fill(void* p, size_t bytes, hipStream_t st);
 // defined in gemm_mx.hip
 moe_status mx_fc1_enqueue(int activation, int wf, const void* x, const void* x_sf,
@@ -76,10 +83,14 @@ moe_status check_gemm(const void* p0, const void* p1, const int32_t* offs, int32
 }
 
 struct FfnLayout {
-  size_t sort_ws, offs, e2p, p2e, n_local, act, act_sf, y, split, split_cnt, total;
+  size_t sort_ws, offs, e2p, p2e, n_local, act, act_sf, y, split, split_cnt, h, total;
 };
 
-FfnLayout ffn_layout(const moe_ffn_desc* d) {
+// The forward's workspace; with `train`, followed by the FC1 pre-activations h
+// [T*k, 2I] float32 that the backward needs (the training forward's saved buffer):
+// fp32, the values the forward's activation saw, so that the backward's SwiGLUStep
+// clamp masks agree with the forward's clamp.
+FfnLayout ffn_layout(const moe_ffn_desc* d, bool train = false) {
   FfnLayout l{};
   const int64_t T = d->T;
   const int32_t L = d->num_local_experts > 0 ? d->num_local_experts : d->num_experts;
@@ -100,6 +111,25 @@ FfnLayout ffn_layout(const moe_ffn_desc* d) {
   if (!mx) o += (size_t)SPLIT_SLOTS * SPLIT_TILE_BYTES;
   l.split_cnt = o;
   if (!mx) o += align_up((size_t)SPLIT_SLOTS * 4, 256);
+  l.h = o;
+  if (train) o += align_up((size_t)R * 2 * d->I * 4, 256);
+  l.total = o;
+  return l;
+}
+
+// Backward workspace: dy [T*k, H] (later the gathered x rows), dh [T*k, 2I], dx rows
+// [T*k, H] (bf16, permuted order).
+struct BwdLayout {
+  size_t dy, dh, dxp, total;
+};
+
+BwdLayout bwd_layout(const moe_ffn_desc* d) {
+  BwdLayout l{};
+  const int64_t R = d->T * d->top_k;
+  size_t o = 0;
+  l.dy = o;  o += align_up((size_t)R * d->H * 2, 256);
+  l.dh = o;  o += align_up((size_t)R * 2 * d->I * 2, 256);
+  l.dxp = o; o += align_up((size_t)R * d->H * 2, 256);
   l.total = o;
   return l;
 }
@@ -189,12 +219,13 @@ static moe_status check_ffn(const moe_ffn_desc* d) {
 static moe_status fc1_enqueue(const moe_ffn_desc* d, const void* x, const void* w1,
                               const float* limits, const int32_t* offs, const int32_t* p2e,
                               void* act, hipStream_t st, void* split_ws = nullptr,
-                              int32_t* split_cnt = nullptr) {
+                              int32_t* split_cnt = nullptr, void* h_out = nullptr) {
   const int32_t L = d->num_local_experts > 0 ? d->num_local_experts : d->num_experts;
   const int64_t R = d->T * d->top_k;
   const int epi = d->activation == MOE_ACT_SWIGLU_STEP ? EPI_SWIGLU_STEP : EPI_SWIGLU;
   return gemm_nt_enqueue(epi, x, p2e, d->top_k, w1, 2 * d->I, L, offs, R, d->I, d->H, act, d->I,
-                         d->I, limits, 7.0f, nullptr, nullptr, d->top_k, st, split_ws, split_cnt);
+                         d->I, limits, 7.0f, nullptr, nullptr, d->top_k, st, split_ws, split_cnt,
+                         h_out);
 }
 
 // FC2: unscaled rows in permuted order, or the fused scaled scatter-add into out.
@@ -219,11 +250,13 @@ extern "C" size_t moe_ffn_workspace_size(const moe_ffn_desc* d) {
   return ffn_layout(d).total;
 }
 
-extern "C" moe_status moe_ffn_forward(const moe_ffn_desc* d, const moe_ffn_tensors* t, void* ws,
-                                      size_t ws_bytes, void* stream) {
+static moe_status ffn_forward(const moe_ffn_desc* d, const moe_ffn_tensors* t, void* ws,
+                              size_t ws_bytes, void* stream, bool train) {
   moe_status s = check_ffn(d);
   if (s != MOE_OK) return s;
   if (!t) return MOE_ERR_NULL;
+  if (train && (d->weight_format != MOE_WFMT_BF16 || d->finalize_mode != MOE_FINALIZE_DETERMINISTIC))
+    return MOE_ERR_UNSUPPORTED;
   if (d->T == 0) return MOE_OK;
   const int32_t L = d->num_local_experts > 0 ? d->num_local_experts : d->num_experts;
   const int fm = d->finalize_mode;
@@ -239,12 +272,13 @@ extern "C" moe_status moe_ffn_forward(const moe_ffn_desc* d, const moe_ffn_tenso
   if (mx && block_scaled(d->weight_format) &&
       (!aligned16(t->x_sf) || !aligned16(t->w1_sf) || !aligned16(t->w2_sf)))
     return MOE_ERR_ALIGN;
-  const FfnLayout l = ffn_layout(d);
+  const FfnLayout l = ffn_layout(d, train);
   if (!ws || ws_bytes < l.total || !aligned16(ws)) return MOE_ERR_WORKSPACE;
   hipStream_t st = as_stream(stream);
   char* w = reinterpret_cast<char*>(ws);
   int32_t* offs = reinterpret_cast<int32_t*>(w + l.offs);
-  int32_t* e2p = t->e2p ? t->e2p : reinterpret_cast<int32_t*>(w + l.e2p);
+  // training keeps e2p in the saved buffer for the backward
+  int32_t* e2p = t->e2p && !train ? t->e2p : reinterpret_cast<int32_t*>(w + l.e2p);
   int32_t* p2e = reinterpret_cast<int32_t*>(w + l.p2e);
   int32_t* nloc = reinterpret_cast<int32_t*>(w + l.n_local);
   void* act = w + l.act;
@@ -268,13 +302,99 @@ extern "C" moe_status moe_ffn_forward(const moe_ffn_desc* d, const moe_ffn_tenso
     if (s != MOE_OK) return s;
     s = mx_fc2_enqueue(wf, act, act_sf, t->w2, t->w2_sf, L, offs, R, H, d->I, y, st);
   } else {
-    s = fc1_enqueue(d, t->x, t->w1, t->clamp_limit, offs, p2e, act, st, split_ws, split_cnt);
+    s = fc1_enqueue(d, t->x, t->w1, t->clamp_limit, offs, p2e, act, st, split_ws, split_cnt,
+                    train ? w + l.h : nullptr);
     if (s != MOE_OK) return s;
     s = fc2_enqueue(d, act, t->w2, offs, p2e, t->topk_weights, fm == MOE_FINALIZE_FUSED ? t->out : y,
                     st, split_ws, split_cnt);
   }
   if (s != MOE_OK || fm != MOE_FINALIZE_DETERMINISTIC) return s;
   return finalize_enqueue(y, e2p, t->topk_weights, d->T, d->top_k, H, t->out, st);
+}
+
+extern "C" moe_status moe_ffn_forward(const moe_ffn_desc* d, const moe_ffn_tensors* t, void* ws,
+                                      size_t ws_bytes, void* stream) {
+  return ffn_forward(d, t, ws, ws_bytes, stream, false);
+}
+
+static bool trainable(const moe_ffn_desc* d) {
+  return d->weight_format == MOE_WFMT_BF16 && d->finalize_mode == MOE_FINALIZE_DETERMINISTIC;
+}
+
+extern "C" size_t moe_ffn_saved_size(const moe_ffn_desc* d) {
+  if (check_ffn(d) != MOE_OK || !trainable(d)) return 0;
+  return ffn_layout(d, true).total;
+}
+
+extern "C" moe_status moe_ffn_forward_train(const moe_ffn_desc* d, const moe_ffn_tensors* t,
+                                            void* saved, size_t saved_bytes, void* stream) {
+  return ffn_forward(d, t, saved, saved_bytes, stream, true);
+}
+
+extern "C" size_t moe_ffn_backward_workspace_size(const moe_ffn_desc* d) {
+  if (check_ffn(d) != MOE_OK || !trainable(d)) return 0;
+  return bwd_layout(d).total;
+}
+
+extern "C" moe_status moe_ffn_backward(const moe_ffn_desc* d, const moe_ffn_tensors* t,
+                                       const moe_ffn_grads* g, const void* saved,
+                                       size_t saved_bytes, void* ws, size_t ws_bytes,
+                                       void* stream) {
+  moe_status s = check_ffn(d);
+  if (s != MOE_OK) return s;
+  if (!trainable(d)) return MOE_ERR_UNSUPPORTED;
+  if (!t || !g) return MOE_ERR_NULL;
+  if (g->grad_dtype != MOE_DTYPE_BF16 && g->grad_dtype != MOE_DTYPE_F32) return MOE_ERR_DTYPE;
+  if (!g->dw1 || !g->dw2 || !t->w1 || !t->w2) return MOE_ERR_NULL;
+  if (!aligned16(g->dw1) || !aligned16(g->dw2) || !aligned16(t->w1) || !aligned16(t->w2))
+    return MOE_ERR_ALIGN;
+  const int32_t L = d->num_local_experts > 0 ? d->num_local_experts : d->num_experts;
+  const bool f32 = g->grad_dtype == MOE_DTYPE_F32;
+  hipStream_t st = as_stream(stream);
+  const int H = d->H, I = d->I, k = d->top_k;
+  if (d->T == 0) {  // no rows: the weight gradients are exactly zero
+    const size_t es = f32 ? 4 : 2;
+    s = zero_fill(g->dw1, (size_t)L * 2 * I * H * es, st);
+    if (s != MOE_OK) return s;
+    return zero_fill(g->dw2, (size_t)L * H * I * es, st);
+  }
+  if (!g->dout || !g->dx || !t->x || !t->topk_weights) return MOE_ERR_NULL;
+  if (!aligned16(g->dout) || !aligned16(g->dx) || !aligned16(t->x)) return MOE_ERR_ALIGN;
+  const FfnLayout l = ffn_layout(d, true);
+  if (!saved || saved_bytes < l.total || !aligned16(saved)) return MOE_ERR_WORKSPACE;
+  const BwdLayout b = bwd_layout(d);
+  if (!ws || ws_bytes < b.total || !aligned16(ws)) return MOE_ERR_WORKSPACE;
+  const char* sv = reinterpret_cast<const char*>(saved);
+  const int32_t* offs = reinterpret_cast<const int32_t*>(sv + l.offs);
+  const int32_t* e2p = reinterpret_cast<const int32_t*>(sv + l.e2p);
+  const int32_t* p2e = reinterpret_cast<const int32_t*>(sv + l.p2e);
+  const void* h = sv + l.h;
+  const void* act = sv + l.act;
+  const void* y = sv + l.y;
+  char* w = reinterpret_cast<char*>(ws);
+  void* dy = w + b.dy;
+  void* dh = w + b.dh;
+  void* dxp = w + b.dxp;
+  const int64_t R = d->T * k;
+  // out[t] = sum_s w y  ->  dy rows and the routing-weight gradients
+  s = permute_bwd_enqueue(g->dout, e2p, t->topk_weights, y, d->T, k, H, dy, g->dtopk_weights, st);
+  if (s != MOE_OK) return s;
+  // y = act @ w2^T  ->  da = dy @ w2 (with dh = act'(h) da in the epilogue), dw2 = dy^T act
+  const int actk = d->activation == MOE_ACT_SWIGLU_STEP ? 2 : 1;
+  s = gemm_dgrad_enqueue(dy, t->w2, offs, L, R, H, I, dh, st, actk, h, t->clamp_limit, 7.0f);
+  if (s != MOE_OK) return s;
+  s = gemm_wgrad_enqueue(dy, act, offs, L, R, H, I, g->dw2, f32, st);
+  if (s != MOE_OK) return s;
+  // h = x[p2e / k] @ w1^T  ->  dx rows = dh @ w1, dw1 = dh^T x[p2e / k]; the x rows are
+  // gathered once into permuted order (into dy's buffer, free after dw2)
+  s = gemm_dgrad_enqueue(dh, t->w1, offs, L, R, 2 * I, H, dxp, st);
+  if (s != MOE_OK) return s;
+  s = gather_rows_enqueue(t->x, p2e, offs, L, k, H, R, dy, st);
+  if (s != MOE_OK) return s;
+  s = gemm_wgrad_enqueue(dh, dy, offs, L, R, 2 * I, H, g->dw1, f32, st);
+  if (s != MOE_OK) return s;
+  // the un-permute: dx[t] = sum over the token's local routes of its dx rows
+  return finalize_enqueue(dxp, e2p, nullptr, d->T, k, H, g->dx, st);
 }
 
 extern "C" moe_status moe_fc1_mx(const moe_ffn_desc* d, const void* x, const void* x_sf,

@@ -31,7 +31,7 @@ __global__ __launch_bounds__(256) void k_finalize(const uint4* __restrict__ y,
 #pragma unroll
   for (int s = 0; s < KMAX; ++s) {
     p[s] = s < k ? e2p[t * k + s] : -1;
-    ws[s] = s < k ? w[t * k + s] : 0.f;
+    ws[s] = s < k ? (w ? w[t * k + s] : 1.f) : 0.f;   // no weights: a plain sum
   }
 #pragma unroll
   for (int s = 0; s < KMAX; ++s)

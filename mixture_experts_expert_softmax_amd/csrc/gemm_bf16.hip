@@ -65,6 +65,7 @@ struct NtArgs {
   const float* route_w;      // fused finalize: topk weights [T*k]
   const int32_t* p2e;        // fused finalize: route of permuted row
   int top_k;
+  float* h_out;              // FC1 (optional): fp32 pre-activations [rows][2I], up then gate
   float* split_ws;           // split tiles: fp32 partial tiles [SPLIT_SLOTS][TB * TB]
   int32_t* split_cnt;        // split tiles: arrival counters, 0 between launches
   int n_res;                 // workgroups resident at once (0: never split)
@@ -162,6 +163,15 @@ struct RowLoader {
     for (int j = 0; j < 8; ++j)
       r[j] = ok ? *reinterpret_cast<const uint4*>(base + off[j] + k0) : make_uint4(0, 0, 0, 0);
   }
+  __device__ __forceinline__ void load(int kt, int) { load(kt); }
+  // loads j0 .. j0 + 3 of stage kt (the scheduled loop issues a stage in two halves)
+  __device__ __forceinline__ void load4(int kt, int, int j0) {
+    const int k0 = kt * TK + ch * 8;
+    const bool ok = k0 < K;
+#pragma unroll
+    for (int j = j0; j < j0 + 4; ++j)
+      r[j] = ok ? *reinterpret_cast<const uint4*>(base + off[j] + k0) : make_uint4(0, 0, 0, 0);
+  }
   __device__ __forceinline__ void store(uint4* __restrict__ lds, int tid) const {
     const int row = tid >> 3;
     const int pc = ch ^ ((row >> 1) & 7);
@@ -190,6 +200,16 @@ struct KLoader {
     const int c = tid & 31;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
+      const int kr = kt * TK + (tid >> 5) + 8 * j;
+      const bool ok = kr < rows_left0 && c * 8 < cols_left;
+      r[j] = ok ? *reinterpret_cast<const uint4*>(base + (int64_t)kr * ld + c * 8)
+                : make_uint4(0, 0, 0, 0);
+    }
+  }
+  __device__ __forceinline__ void load4(int kt, int tid, int j0) {
+    const int c = tid & 31;
+#pragma unroll
+    for (int j = j0; j < j0 + 4; ++j) {
       const int kr = kt * TK + (tid >> 5) + 8 * j;
       const bool ok = kr < rows_left0 && c * 8 < cols_left;
       r[j] = ok ? *reinterpret_cast<const uint4*>(base + (int64_t)kr * ld + c * 8)
@@ -230,29 +250,79 @@ __device__ __forceinline__ bf16x8 ktile_frag(const uint4* __restrict__ lds, int 
   return __builtin_bit_cast(bf16x8, both);
 }
 
-// One 64-deep stage for operands of either layout: A (output columns wn*128 + ...)
-// and B (output rows wm*128 + ...) each come from a row-major tile ([256 rows][8
-// chunks], as in mma_stage) or a K-major tile (ktile_frag).
-template <bool A_K, bool B_K>
-__device__ __forceinline__ void mma_stage_t(const uint4* __restrict__ As, const uint4* __restrict__ Bs,
-                                            int wn, int wm, int lane, f32x16 (&acc)[4][4]) {
+// Scheduled main loop for the dgrad / wgrad operand layouts (A = weight side, output
+// columns; B = activation side, output rows; either row-major [256][8 chunks] or
+// K-major [64][32 chunks] in LDS; tile A at smem + TILE_U4, B at smem, per stage).
+// The same issue order as the forward loop: the next 16-deep step's fragment reads
+// go between the current step's 16 MFMAs, half of the next stage's global loads
+// each into steps 0 and 1 and its LDS stores into step 3. Loads past the operand
+// read as zeros, so the last stage loads (and stores) an unused one and the body
+// has no branches.
+template <bool A_K, bool B_K, class LA, class LB>
+__device__ __forceinline__ void mainloop_sched(LA& la, LB& lb, uint4* smem, int ktiles, int tid,
+                                               int lane, int wn, int wm, f32x16 (&acc)[4][4]) {
+  la.load(0, tid);
+  lb.load(0, tid);
+  lb.store(smem, tid);
+  la.store(smem + TILE_U4, tid);
+  __syncthreads();
+  for (int kt = 0; kt < ktiles; ++kt) {
+    const int s = kt & 1;
+    const uint4* Bs = smem + s * 2 * TILE_U4;
+    const uint4* As = Bs + TILE_U4;
+    uint4* Bn = smem + (s ^ 1) * 2 * TILE_U4;
+    uint4* An = Bn + TILE_U4;
+    bf16x8 wf[2][4], xf[2][4];
+    auto rd = [&](int kk, bf16x8 (&wq)[4], bf16x8 (&xq)[4]) {
+      const int ch = ((kk << 1) + (lane >> 5)) ^ ((lane >> 1) & 7);
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk) {
-    const int ch = ((kk << 1) + (lane >> 5)) ^ ((lane >> 1) & 7);
-    bf16x8 wf[4], xf[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      wf[i] = A_K ? ktile_frag(As, kk, wn * 128 + i * 32, lane)
-                  : as_bf16x8(As[(wn * 128 + i * 32 + (lane & 31)) * 8 + ch]);
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      xf[j] = B_K ? ktile_frag(Bs, kk, wm * 128 + j * 32, lane)
-                  : as_bf16x8(Bs[(wm * 128 + j * 32 + (lane & 31)) * 8 + ch]);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 4; ++i)
+        wq[i] = A_K ? ktile_frag(As, kk, wn * 128 + i * 32, lane)
+                    : as_bf16x8(As[(wn * 128 + i * 32 + (lane & 31)) * 8 + ch]);
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[i], xf[j], acc[i][j], 0, 0, 0);
+        xq[j] = B_K ? ktile_frag(Bs, kk, wm * 128 + j * 32, lane)
+                    : as_bf16x8(Bs[(wm * 128 + j * 32 + (lane & 31)) * 8 + ch]);
+    };
+    rd(0, wf[0], xf[0]);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const int cur = kk & 1, nxt = cur ^ 1;
+      if (kk < 2) {
+        la.load4(kt + 1, tid, kk * 4);
+        lb.load4(kt + 1, tid, kk * 4);
+      }
+      if (kk < 3) rd(kk + 1, wf[nxt], xf[nxt]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[cur][i], xf[cur][j], acc[i][j], 0, 0, 0);
+      if (kk == 3) {
+        lb.store(Bn, tid);
+        la.store(An, tid);
+      }
+    }
+    // issue order (0x008 MFMA, 0x100 LDS read, 0x200 LDS write, 0x020 global load);
+    // NR fragment reads per step: 4 per row-major operand, 8 per K-major one (two
+    // transposing 8-byte reads per fragment)
+    constexpr int NR = (A_K ? 8 : 4) + (B_K ? 8 : 4);
+    __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
+    for (int q = 0; q < 2; ++q)
+      for (int r = 0; r < 16; ++r) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (r < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        if (r & 1) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      }
+    for (int r = 0; r < 16; ++r) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (r < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    for (int r = 0; r < 16; ++r) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+    }
+    __syncthreads();
   }
 }
 
@@ -496,6 +566,15 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_nt(NtArgs a) {
         for (int q = 0; q < 4; ++q) {
           const int col = nt * 128 + wn * 64 + i * 32 + q * 8 + hi4;
           if (col >= a.I) continue;
+          if (a.h_out) {   // exactly the values the activation below sees
+            float* hrow = a.h_out + (int64_t)p * 2 * a.I;
+            *reinterpret_cast<float4*>(hrow + col) =
+                make_float4(acc[i][j][q * 4 + 0], acc[i][j][q * 4 + 1], acc[i][j][q * 4 + 2],
+                            acc[i][j][q * 4 + 3]);
+            *reinterpret_cast<float4*>(hrow + a.I + col) =
+                make_float4(acc[i + 2][j][q * 4 + 0], acc[i + 2][j][q * 4 + 1],
+                            acc[i + 2][j][q * 4 + 2], acc[i + 2][j][q * 4 + 3]);
+          }
           float v[4];
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
@@ -555,8 +634,14 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_nt(NtArgs a) {
 struct DgradArgs {
   const uint16_t* G; const uint16_t* W; const int32_t* ends; int E; int m_cap;
   int N; int K; int n_tiles; int m_tiles; uint16_t* DX;
+  // activation backward (ACT > 0): DX is dh [rows][2K] = [du | dg], from the fp32
+  // pre-activations h [rows][2K] = [u | g] and the clamp limits of SwiGLUStep
+  const float* h; const float* limits; float def_limit;
 };
 
+// dgrad: dX[m, k] = sum_n G[m, n] W[e, n, k]; ACT 0 stores dX, ACT 1 / 2 treat dX as
+// da, the gradient of the SwiGLU / SwiGLUStep output, and store dh = act'(h) da.
+template <int ACT>
 __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_dgrad(DgradArgs a) {
   __shared__ uint4 smem[4 * TILE_U4];
   int e, m0, mend, nt;  // nt: tile of K (output columns)
@@ -585,42 +670,51 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_dgrad(DgradArgs a) {
 
   f32x16 acc[4][4];
   zero_acc(acc);
-  const int ktiles = (a.N + TK - 1) / TK;
-  lg.load(0);
-  lw.load(0, tid);
-  lg.store(smem, tid);
-  lw.store((smem + TILE_U4), tid);
-  __syncthreads();
-  for (int kt = 0; kt < ktiles; ++kt) {
-    const int s = kt & 1;
-    const bool more = kt + 1 < ktiles;
-    if (more) {
-      lg.load(kt + 1);
-      lw.load(kt + 1, tid);
-    }
-    mma_stage_t<true, false>((smem + TILE_U4 + s * 2 * TILE_U4), (smem + s * 2 * TILE_U4), wn, wm,
-                             lane, acc);
-    if (more) {
-      lg.store((smem + (s ^ 1) * 2 * TILE_U4), tid);
-      lw.store((smem + TILE_U4 + (s ^ 1) * 2 * TILE_U4), tid);
-    }
-    __syncthreads();
-  }
+  mainloop_sched<true, false>(lw, lg, smem, (a.N + TK - 1) / TK, tid, lane, wn, wm, acc);
   const int hi4 = (lane >> 5) * 4;
+  float lim = 0.f;
+  if (ACT == 2) lim = a.limits ? a.limits[e] : a.def_limit;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int p = m0 + wm * 128 + j * 32 + (lane & 31);
     if (p >= mend) continue;
-    uint16_t* crow = a.DX + (int64_t)p * a.K;
+    uint16_t* crow = a.DX + (int64_t)p * (ACT ? 2 * a.K : a.K);
+    const float* hrow = ACT ? a.h + (int64_t)p * 2 * a.K : nullptr;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int col = c0 + wn * 128 + i * 32 + q * 8 + hi4;
         if (col >= a.K) continue;
-        *reinterpret_cast<uint2*>(crow + col) =
-            make_uint2(pack_bf16x2(acc[i][j][q * 4 + 0], acc[i][j][q * 4 + 1]),
-                       pack_bf16x2(acc[i][j][q * 4 + 2], acc[i][j][q * 4 + 3]));
+        if (ACT == 0) {
+          *reinterpret_cast<uint2*>(crow + col) =
+              make_uint2(pack_bf16x2(acc[i][j][q * 4 + 0], acc[i][j][q * 4 + 1]),
+                         pack_bf16x2(acc[i][j][q * 4 + 2], acc[i][j][q * 4 + 3]));
+        } else {
+          const float4 hu = *reinterpret_cast<const float4*>(hrow + col);
+          const float4 hg = *reinterpret_cast<const float4*>(hrow + a.K + col);
+          const float us[4] = {hu.x, hu.y, hu.z, hu.w};
+          const float gs[4] = {hg.x, hg.y, hg.z, hg.w};
+          float du[4], dg[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float da = acc[i][j][q * 4 + r];
+            float u = us[r], g = gs[r];
+            float mu = 1.f, mg = 1.f;
+            if (ACT == 2) {   // the clamp passes the gradient where -L <= v <= L
+              mu = (u >= -lim && u <= lim) ? 1.f : 0.f;
+              mg = (g >= -lim && g <= lim) ? 1.f : 0.f;
+              u = fminf(fmaxf(u, -lim), lim);
+              g = fminf(fmaxf(g, -lim), lim);
+            }
+            const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-g * 1.4426950408889634f));
+            du[r] = da * (g * sg) * mu;
+            dg[r] = da * u * (sg * (1.0f + g * (1.0f - sg))) * mg;
+          }
+          *reinterpret_cast<uint2*>(crow + col) = make_uint2(pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3]));
+          *reinterpret_cast<uint2*>(crow + a.K + col) =
+              make_uint2(pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3]));
+        }
       }
   }
 }
@@ -673,28 +767,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_wgrad(WgradArgs a) {
   f32x16 acc[4][4];
   zero_acc(acc);
   const int ktiles = (rows + TK - 1) / TK;
-  if (ktiles > 0) {
-    lgd.load(0, tid);
-    lx.load(0, tid);
-    lgd.store(smem, tid);
-    lx.store((smem + TILE_U4), tid);
-    __syncthreads();
-  }
-  for (int kt = 0; kt < ktiles; ++kt) {
-    const int s = kt & 1;
-    const bool more = kt + 1 < ktiles;
-    if (more) {
-      lgd.load(kt + 1, tid);
-      lx.load(kt + 1, tid);
-    }
-    mma_stage_t<true, true>((smem + TILE_U4 + s * 2 * TILE_U4), (smem + s * 2 * TILE_U4), wn, wm,
-                            lane, acc);
-    if (more) {
-      lgd.store((smem + (s ^ 1) * 2 * TILE_U4), tid);
-      lx.store((smem + TILE_U4 + (s ^ 1) * 2 * TILE_U4), tid);
-    }
-    __syncthreads();
-  }
+  if (ktiles > 0) mainloop_sched<true, true>(lx, lgd, smem, ktiles, tid, lane, wn, wm, acc);
   const int hi4 = (lane >> 5) * 4;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -750,7 +823,7 @@ moe_status gemm_nt_enqueue(int epi, const void* A, const int32_t* a_gather, int 
                            const void* B, int NB, int E, const int32_t* ends, int64_t M, int N,
                            int K, void* C, int64_t ldc, int I, const float* limits,
                            float def_limit, const float* route_w, const int32_t* p2e, int top_k,
-                           hipStream_t st, void* split_ws, int32_t* split_cnt) {
+                           hipStream_t st, void* split_ws, int32_t* split_cnt, void* h_out) {
   if (M == 0) return MOE_OK;
   NtArgs a;
   a.A = reinterpret_cast<const uint16_t*>(A);
@@ -775,6 +848,7 @@ moe_status gemm_nt_enqueue(int epi, const void* A, const int32_t* a_gather, int 
   a.route_w = route_w;
   a.p2e = p2e;
   a.top_k = top_k;
+  a.h_out = reinterpret_cast<float*>(h_out);
   const bool kfull = (K % TK) == 0;
   a.split_ws = reinterpret_cast<float*>(split_ws);
   a.split_cnt = split_cnt;
@@ -800,14 +874,23 @@ moe_status gemm_nt_enqueue(int epi, const void* A, const int32_t* a_gather, int 
   return launch_status();
 }
 
+// act: 0 plain dgrad into DX [M, K]; 1 / 2 (SwiGLU / SwiGLUStep backward): DX is dh
+// [M, 2K] and h [M, 2K] the saved fp32 pre-activations.
 moe_status gemm_dgrad_enqueue(const void* G, const void* W, const int32_t* ends, int E, int64_t M,
-                              int N, int K, void* DX, hipStream_t st) {
+                              int N, int K, void* DX, hipStream_t st, int act, const void* h,
+                              const float* limits, float def_limit) {
   if (M == 0) return MOE_OK;
   DgradArgs a{reinterpret_cast<const uint16_t*>(G), reinterpret_cast<const uint16_t*>(W), ends, E,
               (int)M, N, K, (K + TB - 1) / TB, row_block_bound(M, E),
-              reinterpret_cast<uint16_t*>(DX)};
+              reinterpret_cast<uint16_t*>(DX), reinterpret_cast<const float*>(h), limits,
+              def_limit};
   const int grid = round_up8((int64_t)a.m_tiles * a.n_tiles);
-  k_gemm_dgrad<<<grid, NTHREADS, 0, st>>>(a);
+  if (act == 1)
+    k_gemm_dgrad<1><<<grid, NTHREADS, 0, st>>>(a);
+  else if (act == 2)
+    k_gemm_dgrad<2><<<grid, NTHREADS, 0, st>>>(a);
+  else
+    k_gemm_dgrad<0><<<grid, NTHREADS, 0, st>>>(a);
   return launch_status();
 }
 

@@ -38,7 +38,7 @@ __all__ = [
     "MoECase", "GroupedGemmCase", "moe_case", "tiny_moe", "mixtral_moe",
     "expert_shard_moe", "grouped_gemm_case", "dirichlet_group_sizes",
     "route_logits", "bf16_to_f32", "to_bf16", "mx_quant_e4m3", "mx_quant_e2m1", "W4A8Case",
-    "w4a8_moe", "fp8_quant_per_tensor", "FP8_ACT_SCALE",
+    "w4a8_moe", "fp8_quant_per_tensor", "FP8_ACT_SCALE", "upstream_grad",
 ]
 
 _THREADS = max(1, min(16, os.cpu_count() or 1))
@@ -157,6 +157,16 @@ def expert_shard_moe(seed: int = 0, T: int = 8192, clamp_active: bool = False,
     return moe_case("expert_shard", T, 7168, 2048, 256, 8, num_local=32, local_offset=64,
                     activation="swiglu_step", x_scale=8.0 if clamp_active else 1.0,
                     limit_range=(5.0, 9.0), seed=seed, with_weights=with_weights)
+
+
+def upstream_grad(seed: int, T: int, H: int, scale: float = 1.0) -> torch.Tensor:
+    """Upstream gradient d loss / d out for the backward: bf16 [T, H], N(0, scale^2), drawn
+    from default_rng([seed, 3]) (a stream of its own, so the forward case is unchanged)."""
+    g = np.random.default_rng([seed, 3])
+    a = g.standard_normal((T, H), dtype=np.float32)
+    if scale != 1.0:
+        a *= np.float32(scale)
+    return to_bf16(a)
 
 
 def dirichlet_group_sizes(E: int = 16, total: int = 8192, alpha: float = 0.3,
