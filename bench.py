@@ -244,6 +244,22 @@ def main():
     print(json.dumps(line), flush=True)
 
 
+def _capture(fn):
+    """fn captured into a graph (after a warm-up run on a side stream)."""
+    import torch
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        fn()
+    torch.cuda.current_stream().wait_stream(st)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
 def _training(x, w1, w2, ids, wts, E, n_local):
     """The bf16 layer's training forward (which also keeps h, act, y) and its backward
     (dx, dw1, dw2 in bf16, routing-weight gradients) on the benchmark batch; the upstream
@@ -334,8 +350,12 @@ def _mx_sweep(wfmt, flush, dev):
                                      dw["w2"], dw["w2_sf"], cw.num_experts, out=outw, workspace=wsw)
         touched = int(torch.unique(idsw).numel())
         small = touched * per_expert_bytes < (512 << 20)
-        ms_ = _time(mx_step, reps=50 if small else (20 if Tw < 1024 else 10),
-                    flush=flush if small else None)
+        reps = 50 if small else (20 if Tw < 1024 else 10)
+        ms_ = _time(mx_step, reps=reps, flush=flush if small else None)
+        ms_graph = None
+        if Tw <= 128:   # the same step captured once and replayed (prepared launches)
+            g = _capture(mx_step)
+            ms_graph = _time(g.replay, reps=reps, flush=flush if small else None)
         fl = 6.0 * cw.H * cw.I * Tw * cw.top_k
         wb = touched * per_expert_bytes
         sweep[str(Tw)] = {"ms": round(ms_, 4), "tflops": round(fl / (ms_ * 1e-3) / 1e12, 2),
@@ -344,6 +364,15 @@ def _mx_sweep(wfmt, flush, dev):
                           "weight_gbs": round(wb / (ms_ * 1e-3) / 1e9, 1),
                           "hbm_frac_weights": round(wb / (ms_ * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                           "fp8_mfma_frac": round(fl / (ms_ * 1e-3) / 1e12 / FP8_PEAK_TFLOPS, 4)}
+        if ms_graph is not None:
+            sweep[str(Tw)]["graph_ms"] = round(ms_graph, 4)
+        # the per-bucket tuner: time both tile families of FC1 / FC2 on this batch
+        choice = M.moe_tune_mx(dw["x"][:Tw], dw["x_sf"] if pt else dw["x_sf"][:Tw], idsw, wtsw,
+                               dw["w1"], dw["w1_sf"], dw["w2"], dw["w2_sf"], cw.num_experts,
+                               act_scale=dw["act_scale"] if pt else None, workspace=wsw)
+        sweep[str(Tw)]["tuned_ms"] = round(_time(mx_step, reps=reps, flush=flush if small else None), 4)
+        sweep[str(Tw)]["tuned_tiles"] = ["streaming" if ch else "256-row" for ch in choice]
+        M.moe_tune_clear()
     # the two GEMM stages at T=8192 on their own
     srt = M.moe_sort(idsw, cw.num_experts)
     act = torch.empty((8192 * cw.top_k, cw.I), dtype=torch.uint8, device=dev)

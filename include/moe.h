@@ -246,6 +246,28 @@ moe_status moe_fc2_mx(const moe_ffn_desc* desc, const void* act, const void* act
                       void* stream);
 
 /*
+ * moe_tune_mx -- per-bucket tile choice for the fp8-activation GEMM stages ([SM90]
+ * Parameters: the autotuner profiles the legal tiles per token bucket and caches
+ * the winner). For the layer described by desc / tensors (weight_format MXFP4,
+ * MXFP8 or FP8; x, x_sf, topk_ids, w1, w1_sf, w2, w2_sf, act_scale, clamp_limit
+ * read), it sorts the routes, then times FC1 and FC2 with each tile family -- the
+ * 256-row tile and, where the shape allows it, the 32-row streaming tile -- one
+ * warm-up and 3 timed launches each, and records the faster family under (stage,
+ * weight format, H, I, L, rows per local expert rounded up to a power of two).
+ * Later launches of that stage, shape and bucket, by any entry point of this
+ * process, use the recorded family; everything else keeps the built-in rule (the
+ * streaming tile below 32 rows per expert for FC1 and 24 for FC2). choice
+ * (optional, [2]) receives the FC1 / FC2 picks: 1 streaming, 0 256-row.
+ * Unlike every other entry point this call synchronises the stream (it is a tuning
+ * step, not a prepared launch); ws as moe_ffn_workspace_size for the same desc
+ * with MOE_FINALIZE_DETERMINISTIC. Thread-safe; results are per process.
+ * moe_tune_clear forgets every recorded choice.
+ */
+moe_status moe_tune_mx(const moe_ffn_desc* desc, const moe_ffn_tensors* tensors, void* ws,
+                       size_t ws_bytes, void* stream, int32_t* choice);
+void moe_tune_clear(void);
+
+/*
  * The fp8 per-tensor stages ([StepFun] intro: "fp8 (per-tensor)" weight family);
  * desc->weight_format must be MOE_WFMT_FP8, otherwise MOE_ERR_DTYPE. x, w1, w2, act
  * are e4m3fn code bytes; x_scale [1], w1_scale / w2_scale [L] and act_scale [1] are

@@ -24,6 +24,7 @@ __all__ = [
     "moe_finalize", "moe_fc1", "moe_fc2", "status_string", "ACT", "FINALIZE", "WFMT",
     "moe_ffn_forward_mx", "moe_fc1_mx", "moe_fc2_mx", "moe_ffn_forward_fp8", "moe_fc1_fp8",
     "moe_fc2_fp8", "moe_ffn_forward_train", "moe_ffn_backward", "moe_route_backward", "MoEFunction",
+    "moe_tune_mx", "moe_tune_clear",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -86,6 +87,8 @@ EXPORTS = {
     "moe_ffn_backward": (_i32, [ctypes.POINTER(MoeFfnDesc), ctypes.POINTER(MoeFfnTensors),
                                 ctypes.POINTER(MoeFfnGrads), _vp, _sz, _vp, _sz, _vp]),
     "moe_route_backward": (_i32, [_vp, _vp, _vp, _i64, _i32, _i32, _vp, _vp]),
+    "moe_tune_mx": (_i32, [ctypes.POINTER(MoeFfnDesc), ctypes.POINTER(MoeFfnTensors), _vp, _sz, _vp, _vp]),
+    "moe_tune_clear": (None, []),
 }
 
 _LIB: Optional[ctypes.CDLL] = None
@@ -535,6 +538,38 @@ def _ffn_forward_fp8act(wfmt, x, x_sf, topk_ids, topk_weights, w1, w1_sf, w2, w2
     if finalize == "none":
         return y, e2p[: T * k]
     return out
+
+
+def moe_tune_mx(x, x_sf, topk_ids, topk_weights, w1, w1_sf, w2, w2_sf, num_experts,
+                num_local_experts=None, local_expert_offset=0, activation="swiglu", clamp_limit=None,
+                act_scale=None, workspace=None):
+    """Times both tile families of the fp8-activation FC1 / FC2 on these inputs and records
+    the faster one for this shape and token bucket (synchronises). Arguments as
+    moe_ffn_forward_mx (or moe_ffn_forward_fp8 with act_scale). Returns (fc1, fc2) picks:
+    1 = 32-row streaming tile, 0 = 256-row tile."""
+    T, H = x.shape
+    L, twoI, _ = w1.shape
+    I = twoI // 2
+    wfmt = "fp8" if act_scale is not None else _mx_format(w1.shape[2], H, "w1")
+    k = topk_ids.shape[1]
+    d = _ffn_desc(T, H, I, num_experts, L, local_expert_offset, k, activation, "deterministic", wfmt)
+    h = lib()
+    if workspace is None:
+        workspace = torch.empty(max(h.moe_ffn_workspace_size(ctypes.byref(d)), 16), dtype=torch.uint8,
+                                device=x.device)
+    tens = MoeFfnTensors(x.data_ptr(), topk_ids.data_ptr(), topk_weights.data_ptr(), w1.data_ptr(),
+                         w2.data_ptr(), None if clamp_limit is None else clamp_limit.data_ptr(),
+                         None, None, None, x_sf.data_ptr(), w1_sf.data_ptr(), w2_sf.data_ptr(),
+                         None if act_scale is None else act_scale.data_ptr())
+    choice = (ctypes.c_int32 * 2)(-1, -1)
+    _check("moe_tune_mx", h.moe_tune_mx(ctypes.byref(d), ctypes.byref(tens), _ptr(workspace),
+                                        workspace.numel(), _stream(), choice))
+    return int(choice[0]), int(choice[1])
+
+
+def moe_tune_clear():
+    """Forget every tile choice recorded by moe_tune_mx."""
+    lib().moe_tune_clear()
 
 
 def moe_fc1_mx(x, x_sf, w1, w1_sf, offs, p2e, top_k, num_experts, local_expert_offset=0,

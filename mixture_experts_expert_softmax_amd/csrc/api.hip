@@ -35,10 +35,14 @@ moe_status zero_fill(void* p, size_t bytes, hipStream_t st);
 moe_status mx_fc1_enqueue(int activation, int wf, const void* x, const void* x_sf,
                           const int32_t* p2e, int top_k, const void* w1, const void* w1_sf, int L,
                           const int32_t* offs, int64_t R, int H, int I, const float* limits,
-                          void* act, void* act_sf, const float* act_scale, hipStream_t st);
+                          void* act, void* act_sf, const float* act_scale, hipStream_t st,
+                          int force = -1);
 moe_status mx_fc2_enqueue(int wf, const void* act, const void* act_sf, const void* w2,
                           const void* w2_sf, int L, const int32_t* offs, int64_t R, int H, int I,
-                          void* y, hipStream_t st);
+                          void* y, hipStream_t st, int force = -1);
+bool mx_small_possible(int stage, int wf, int H, int I, int64_t R);
+// defined in tune.hip
+void tune_store(int stage, int wf, int K, int NB, int L, int64_t R, int choice);
 
 int device_cu_count() {
   static int cached[64] = {0};
@@ -426,6 +430,111 @@ extern "C" moe_status moe_fc2_mx(const moe_ffn_desc* d, const void* act, const v
   const int32_t L = d->num_local_experts > 0 ? d->num_local_experts : d->num_experts;
   return mx_fc2_enqueue(mx_wf(d->weight_format), act, act_sf, w2, w2_sf, L, offs, d->T * d->top_k, d->H, d->I, y,
                         as_stream(stream));
+}
+
+// Times a stage launch: one warm-up, then the mean of `reps` event-timed launches.
+static moe_status time_launches(hipStream_t st, int reps, float* ms,
+                                moe_status (*launch)(void*), void* ctx) {
+  hipEvent_t a, b;
+  if (hipEventCreate(&a) != hipSuccess) return MOE_ERR_HIP;
+  if (hipEventCreate(&b) != hipSuccess) {
+    (void)hipEventDestroy(a);
+    return MOE_ERR_HIP;
+  }
+  moe_status s = launch(ctx);
+  if (s == MOE_OK && hipEventRecord(a, st) != hipSuccess) s = MOE_ERR_HIP;
+  for (int r = 0; s == MOE_OK && r < reps; ++r) s = launch(ctx);
+  if (s == MOE_OK && hipEventRecord(b, st) != hipSuccess) s = MOE_ERR_HIP;
+  if (s == MOE_OK && hipEventSynchronize(b) != hipSuccess) s = MOE_ERR_HIP;
+  if (s == MOE_OK && hipEventElapsedTime(ms, a, b) != hipSuccess) s = MOE_ERR_HIP;
+  if (s == MOE_OK) *ms /= reps;
+  (void)hipEventDestroy(a);
+  (void)hipEventDestroy(b);
+  return s;
+}
+
+struct TuneCtx {
+  const moe_ffn_desc* d;
+  const moe_ffn_tensors* t;
+  const int32_t* offs;
+  const int32_t* p2e;
+  void* act;
+  void* act_sf;
+  const void* act_sf_in;
+  void* y;
+  hipStream_t st;
+  int force;
+};
+
+static moe_status tune_fc1(void* p) {
+  const TuneCtx& c = *reinterpret_cast<TuneCtx*>(p);
+  const int32_t L = c.d->num_local_experts > 0 ? c.d->num_local_experts : c.d->num_experts;
+  return mx_fc1_enqueue(c.d->activation, mx_wf(c.d->weight_format), c.t->x, c.t->x_sf, c.p2e,
+                        c.d->top_k, c.t->w1, c.t->w1_sf, L, c.offs, c.d->T * c.d->top_k, c.d->H,
+                        c.d->I, c.t->clamp_limit, c.act, c.act_sf, c.t->act_scale, c.st, c.force);
+}
+
+static moe_status tune_fc2(void* p) {
+  const TuneCtx& c = *reinterpret_cast<TuneCtx*>(p);
+  const int32_t L = c.d->num_local_experts > 0 ? c.d->num_local_experts : c.d->num_experts;
+  return mx_fc2_enqueue(mx_wf(c.d->weight_format), c.act, c.act_sf_in, c.t->w2, c.t->w2_sf, L,
+                        c.offs, c.d->T * c.d->top_k, c.d->H, c.d->I, c.y, c.st, c.force);
+}
+
+extern "C" moe_status moe_tune_mx(const moe_ffn_desc* d, const moe_ffn_tensors* t, void* ws,
+                                  size_t ws_bytes, void* stream, int32_t* choice) {
+  moe_status s = check_ffn(d);
+  if (s != MOE_OK) return s;
+  if (!is_mx(d->weight_format)) return MOE_ERR_DTYPE;
+  if (!t) return MOE_ERR_NULL;
+  if (d->T == 0) return MOE_OK;
+  if (!t->x || !t->topk_ids || !t->w1 || !t->w2 || !t->x_sf || !t->w1_sf || !t->w2_sf)
+    return MOE_ERR_NULL;
+  if (d->weight_format == MOE_WFMT_FP8 && !t->act_scale) return MOE_ERR_NULL;
+  if (!aligned16(t->x) || !aligned16(t->w1) || !aligned16(t->w2)) return MOE_ERR_ALIGN;
+  // the layer's workspace, with room for the FC2 rows (DETERMINISTIC layout)
+  moe_ffn_desc dd = *d;
+  dd.finalize_mode = MOE_FINALIZE_DETERMINISTIC;
+  const FfnLayout l = ffn_layout(&dd);
+  if (!ws || ws_bytes < l.total || !aligned16(ws)) return MOE_ERR_WORKSPACE;
+  hipStream_t st = as_stream(stream);
+  const int32_t L = d->num_local_experts > 0 ? d->num_local_experts : d->num_experts;
+  const int64_t R = d->T * d->top_k;
+  const int wf = mx_wf(d->weight_format);
+  char* w = reinterpret_cast<char*>(ws);
+  int32_t* offs = reinterpret_cast<int32_t*>(w + l.offs);
+  int32_t* p2e = reinterpret_cast<int32_t*>(w + l.p2e);
+  s = sort_enqueue(t->topk_ids, d->T, d->top_k, d->num_experts, L, d->local_expert_offset, offs,
+                   nullptr, reinterpret_cast<int32_t*>(w + l.e2p), p2e,
+                   reinterpret_cast<int32_t*>(w + l.n_local), w + l.sort_ws, st);
+  if (s != MOE_OK) return s;
+  TuneCtx c{d, t, offs, p2e, w + l.act, w + l.act_sf,
+            block_scaled(d->weight_format) ? (const void*)(w + l.act_sf) : (const void*)t->act_scale,
+            w + l.y, st, 0};
+  for (int stage = 1; stage <= 2; ++stage) {
+    int best = 0;
+    if (mx_small_possible(stage, wf, d->H, d->I, R)) {
+      float ms[2];
+      for (int f = 0; f < 2; ++f) {
+        c.force = f;
+        s = time_launches(st, 3, &ms[f], stage == 1 ? tune_fc1 : tune_fc2, &c);
+        if (s != MOE_OK) return s;
+      }
+      best = ms[1] < ms[0] ? 1 : 0;
+    }
+    if (stage == 1)
+      tune_store(1, wf, d->H, 2 * d->I, L, R, best);
+    else
+      tune_store(2, wf, d->I, d->H, L, R, best);
+    if (choice) choice[stage - 1] = best;
+    // FC2's inputs: act from FC1 with the recorded choice
+    if (stage == 1) {
+      c.force = best;
+      s = tune_fc1(&c);
+      if (s != MOE_OK) return s;
+    }
+  }
+  return hipStreamSynchronize(st) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
 extern "C" moe_status moe_fc1_fp8(const moe_ffn_desc* d, const void* x, const float* x_scale,

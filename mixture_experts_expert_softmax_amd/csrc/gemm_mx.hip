@@ -32,6 +32,9 @@
 #include "common.h"
 
 namespace moe {
+// recorded tile choices (tune.hip): 1 streaming, 0 256-row, -1 none
+int tune_lookup(int stage, int wf, int K, int NB, int L, int64_t R);
+
 namespace {
 
 constexpr int MTB = 256;          // tile rows on each side
@@ -592,11 +595,21 @@ __global__ __launch_bounds__(256, 2) void k_gemm_mx_stream(MxArgs a) {
 // the 256-row tiles would be mostly padding and too few to fill the chip. Measured
 // crossover (H=7168, I=2048, 64 experts, MXFP4): about 32 rows per expert for FC1
 // and 24 for FC2 (its contraction is 3.5x shorter, so its blocks live shorter).
-inline bool mx_use_small(int64_t R, int L, int K, int NB, int64_t act_rows, int rows_per_expert,
-                         int wb) {
+inline bool mx_small_fits(int K, int NB, int64_t act_rows, int wb) {
   const int stage_k = 128 * 8 / wb;
-  return R <= (int64_t)rows_per_expert * L && K % stage_k == 0 && K <= 4 * SMAX_K &&
-         (int64_t)NB * K * wb / 8 < (1LL << 31) && act_rows * K < (1LL << 31);
+  return K % stage_k == 0 && K <= 4 * SMAX_K && (int64_t)NB * K * wb / 8 < (1LL << 31) &&
+         act_rows * K < (1LL << 31);
+}
+
+// Tile family of a stage: `force` 0 / 1 picks the 256-row / streaming tile (the
+// latter only where it fits), -1 a choice recorded by moe_tune_mx for this shape and
+// bucket, else the built-in rule.
+inline bool mx_use_small(int64_t R, int L, int K, int NB, int64_t act_rows, int rows_per_expert,
+                         int wb, int stage, int wf, int force) {
+  if (!mx_small_fits(K, NB, act_rows, wb)) return false;
+  if (force < 0) force = tune_lookup(stage, wf, K, NB, L, R);
+  if (force >= 0) return force == 1;
+  return R <= (int64_t)rows_per_expert * L;
 }
 
 // Row tiles of tm rows over L experts holding R rows in all: at most one partial
@@ -624,13 +637,19 @@ moe_status mx_launch_w(const MxArgs& a, int wf, bool small, int64_t tiles, hipSt
 
 inline int wf_bits(int wf) { return wf == WF_MXFP4 ? 4 : 8; }
 
+// Whether the streaming tile can serve a stage of this shape (for the tuner).
+bool mx_small_possible(int stage, int wf, int H, int I, int64_t R) {
+  return stage == 1 ? mx_small_fits(H, 2 * I, R, wf_bits(wf)) : mx_small_fits(I, H, R, wf_bits(wf));
+}
+
 // FC1: act (e4m3) = requant(activation(x[p2e[p]/k] @ w1[e].T)) for permuted rows p.
 // wf: WF_MXFP4 / WF_MXFP8 (x_sf, w1_sf UE8M0 block scales; act_sf out) or WF_FP8
 // (x_sf float [1], w1_sf float [L], act_scale float [1] in; act_sf unused).
 moe_status mx_fc1_enqueue(int activation, int wf, const void* x, const void* x_sf,
                           const int32_t* p2e, int top_k, const void* w1, const void* w1_sf, int L,
                           const int32_t* offs, int64_t R, int H, int I, const float* limits,
-                          void* act, void* act_sf, const float* act_scale, hipStream_t st) {
+                          void* act, void* act_sf, const float* act_scale, hipStream_t st,
+                          int force) {
   if (R == 0) return MOE_OK;
   if (wf != WF_MXFP4 && wf != WF_MXFP8 && wf != WF_FP8) return MOE_ERR_DTYPE;
   MxArgs a{};
@@ -654,7 +673,7 @@ moe_status mx_fc1_enqueue(int activation, int wf, const void* x, const void* x_s
   a.a_scale = reinterpret_cast<const float*>(x_sf);
   a.w_scale = reinterpret_cast<const float*>(w1_sf);
   a.q_scale = act_scale;
-  const bool small = mx_use_small(R, L, H, 2 * I, R, 32, wf_bits(wf));
+  const bool small = mx_use_small(R, L, H, 2 * I, R, 32, wf_bits(wf), 1, wf, force);
   a.n_tiles = small ? I / 32 : (I + 127) / 128;
   const int64_t tiles = mx_row_tiles(R, L, small ? STB : MTB) * a.n_tiles;
   if (activation == MOE_ACT_SWIGLU_STEP) return mx_launch_w<MX_FC1_STEP>(a, wf, small, tiles, st);
@@ -665,7 +684,7 @@ moe_status mx_fc1_enqueue(int activation, int wf, const void* x, const void* x_s
 // act_sf is the float [1] scale of act).
 moe_status mx_fc2_enqueue(int wf, const void* act, const void* act_sf, const void* w2,
                           const void* w2_sf, int L, const int32_t* offs, int64_t R, int H, int I,
-                          void* y, hipStream_t st) {
+                          void* y, hipStream_t st, int force) {
   if (R == 0) return MOE_OK;
   if (wf != WF_MXFP4 && wf != WF_MXFP8 && wf != WF_FP8) return MOE_ERR_DTYPE;
   MxArgs a{};
@@ -685,7 +704,7 @@ moe_status mx_fc2_enqueue(int wf, const void* act, const void* act_sf, const voi
   a.ldc = H;
   a.a_scale = reinterpret_cast<const float*>(act_sf);
   a.w_scale = reinterpret_cast<const float*>(w2_sf);
-  const bool small = mx_use_small(R, L, I, H, R, 24, wf_bits(wf));
+  const bool small = mx_use_small(R, L, I, H, R, 24, wf_bits(wf), 2, wf, force);
   a.n_tiles = small ? (H + 63) / 64 : (H + MTB - 1) / MTB;
   const int64_t tiles = mx_row_tiles(R, L, small ? STB : MTB) * a.n_tiles;
   return mx_launch_w<MX_FC2>(a, wf, small, tiles, st);
