@@ -21,6 +21,8 @@ function follows one passage of the documentation pages it cites:
   Autograd section (a backward made of dgrad and wgrad) for the layer backward.
 * "flashinfer.fused_moe.cute_dsl_fused_moe_bf16" (the SM90 fused-MoE page):
   the forward formula, the EP shard rule and the two finalize paths.
+* "flashinfer.fused_moe.prepare_bgmv_moe" (the BGMV page): the MoE-LoRA shrink
+  and expand over routed (token, expert) pairs.
 
 Where a step reaches a result with a plain definition, the function computes
 that definition directly; the sort and the requantization are the method's
@@ -50,7 +52,7 @@ __all__ = [
     "finalize", "e4m3_decode", "e4m3_encode", "e2m1_decode", "ue8m0_decode",
     "mx_dequant", "requant_e4m3", "minifloat_decode", "unpack_e2m1", "mx_dequant_fp4",
     "mx_dequant_fp8", "fp8_dequant", "requant_e4m3_per_tensor", "activation_backward",
-    "moe_backward", "route_backward",
+    "moe_backward", "route_backward", "bgmv_shrink", "bgmv_expand", "bgmv_moe",
 ]
 
 
@@ -513,3 +515,68 @@ def route_backward(topk_ids, topk_weights, dtopk_weights, num_experts: int):
     for s in range(k):
         dl[np.arange(T), ids[:, s]] += g[:, s]
     return dl
+
+
+# ---------------------------------------------------------------------------
+# BGMV MoE-LoRA -- "flashinfer.fused_moe.prepare_bgmv_moe" page (the BGMV page):
+# signature and Parameters (x [T, H]; one LoRA slice with A [num_loras, E, rank, H]
+# and B [num_loras, E, feat_out, rank]; per routed pair a token index, an expert
+# index and an FP32 routing weight; a LoRA index per token; shrink output of shape
+# [num_pairs, rank] in the weight dtype; FP32 output accumulator [T, feat_out]) and
+# the description (each output accumulates its routes in fixed input order).
+# Readings: the output is written, not added onto earlier contents; a pair whose
+# token, expert or LoRA index is out of range contributes zero.
+# ---------------------------------------------------------------------------
+def _bgmv_valid(sorted_token_ids, expert_ids, lora_indices, num_tokens, num_experts, num_loras):
+    t = np.asarray(sorted_token_ids, dtype=np.int64)
+    e = np.asarray(expert_ids, dtype=np.int64)
+    li = np.asarray(lora_indices, dtype=np.int64)
+    ok = (t >= 0) & (t < num_tokens) & (e >= 0) & (e < num_experts)
+    lp = np.where(ok, li[np.clip(t, 0, max(num_tokens - 1, 0))] if num_tokens else -1, -1)
+    ok &= (lp >= 0) & (lp < num_loras)
+    return t, e, lp, ok
+
+
+def bgmv_shrink(x, lora_a, sorted_token_ids, expert_ids, lora_indices, shrink_dtype=None):
+    """shrink[p, :] = x[t_p] @ lora_a[l, e_p].T with t_p = sorted_token_ids[p],
+    l = lora_indices[t_p] (float64; rows of invalid pairs are 0). shrink_dtype="bf16"
+    rounds the result to bfloat16 (nearest even), the dtype the page gives the shrink
+    output when the weights are bf16."""
+    x = np.asarray(x, dtype=np.float64)
+    A = lora_a
+    num_loras, E, r, H = A.shape
+    t, e, l, ok = _bgmv_valid(sorted_token_ids, expert_ids, lora_indices, x.shape[0], E, num_loras)
+    out = np.zeros((t.shape[0], r))
+    for p in np.nonzero(ok)[0]:
+        out[p] = np.asarray(A[l[p], e[p]], dtype=np.float64) @ x[t[p]]
+    if shrink_dtype == "bf16":
+        import torch
+        out = torch.from_numpy(out).to(torch.bfloat16).to(torch.float64).numpy()
+    elif shrink_dtype is not None:
+        raise ValueError(shrink_dtype)
+    return out
+
+
+def bgmv_expand(shrink, lora_b, sorted_token_ids, expert_ids, lora_indices, topk_weights,
+                num_tokens):
+    """y[t, :] = sum over the pairs p of token t, ascending p, of
+    topk_weights[p] * (shrink[p] @ lora_b[l, e_p].T) (float64; tokens without a valid
+    pair get 0)."""
+    s = np.asarray(shrink, dtype=np.float64)
+    B = lora_b
+    num_loras, E, N, r = B.shape
+    t, e, l, ok = _bgmv_valid(sorted_token_ids, expert_ids, lora_indices, num_tokens, E, num_loras)
+    w = np.asarray(topk_weights, dtype=np.float64)
+    y = np.zeros((num_tokens, N))
+    for p in np.nonzero(ok)[0]:        # ascending pair index
+        y[t[p]] += w[p] * (np.asarray(B[l[p], e[p]], dtype=np.float64) @ s[p])
+    return y
+
+
+def bgmv_moe(x, lora_a, lora_b, sorted_token_ids, expert_ids, lora_indices, topk_weights,
+             shrink_dtype=None):
+    """Shrink then expand; returns (y [T, feat_out], shrink [num_pairs, rank])."""
+    s = bgmv_shrink(x, lora_a, sorted_token_ids, expert_ids, lora_indices, shrink_dtype)
+    y = bgmv_expand(s, lora_b, sorted_token_ids, expert_ids, lora_indices, topk_weights,
+                    np.asarray(x).shape[0])
+    return y, s
