@@ -396,6 +396,38 @@ def _mx_sweep(wfmt, flush, dev):
     return sweep
 
 
+def _bgmv_points(flush, dev):
+    """BGMV MoE-LoRA shrink + expand at the page's measured shape (hidden 3072, rank 32,
+    top-2 contiguous pairs, 4 LoRAs x 8 experts) for 16 and 2048 tokens. Bytes: the
+    LoRA weights of the touched (LoRA, expert) pairs once, x read, y written (float32);
+    per-pair weight bytes (every pair reads its A and B slices, mostly from cache)
+    are reported beside them."""
+    import numpy as np
+    import torch
+    import mixture_experts_expert_softmax_amd as M
+    import moe_synth as S
+    out = {}
+    for T in (16, 2048):
+        c = S.bgmv_case(seed=0, T=T, H=3072, rank=32, num_loras=4, E=8, top_k=2)
+        d = [c.x.to(dev), c.lora_a.to(dev), c.lora_b.to(dev)] + [
+            torch.from_numpy(v).to(dev) for v in (c.sorted_token_ids, c.expert_ids, c.lora_indices,
+                                                  c.topk_weights)]
+        y = torch.empty((T, 3072), dtype=torch.float32, device=dev)
+        ws = torch.empty(1 << 24, dtype=torch.uint8, device=dev)
+        P = c.sorted_token_ids.shape[0]
+        fn = lambda: M.moe_bgmv(*d, c.num_experts, y_accum=y, workspace=ws)
+        ms_ = _time(fn, reps=50, flush=flush)
+        pairs = {(int(c.lora_indices[t]), int(e)) for t, e in zip(c.sorted_token_ids, c.expert_ids)}
+        wbytes = len(pairs) * 2 * (32 * 3072 * 2)
+        alg = wbytes + T * 3072 * 2 + T * 3072 * 4
+        out[str(T)] = {"ms": round(ms_, 4), "pairs_per_s": round(P / (ms_ * 1e-3), 1),
+                       "algorithmic_gbs": round(alg / (ms_ * 1e-3) / 1e9, 1),
+                       "hbm_frac": round(alg / (ms_ * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                       "per_pair_weight_gbs": round(P * 2 * 32 * 3072 * 2 / (ms_ * 1e-3) / 1e9, 1),
+                       "timing": "median of 50, MALL flushed"}
+    return out
+
+
 def secondary_measurements(progress):
     """The other hot-path rows at their own workloads (not the headline step):
     the standalone grouped GEMMs, the expert-shard forward, and routing / sort /
@@ -460,8 +492,10 @@ def secondary_measurements(progress):
     for wfmt, key in (("mxfp4", "w4a8"), ("mxfp8", "mxfp8_weights"), ("fp8", "fp8_per_tensor")):
         progress(f"secondary: {wfmt} weights, MXFP8 activations, H=7168 I=2048 64 experts top-8")
         res[key] = _mx_sweep(wfmt, flush, dev)
-    del flush
 
+    progress("secondary: BGMV MoE-LoRA H=3072 rank 32, 4 LoRAs x 8 experts, top-2")
+    res["bgmv"] = _bgmv_points(flush, dev)
+    del flush
 
     progress("secondary: route + sort at T=262144, 256 experts, top-8")
     T2, E2, k2 = 262144, 256, 8

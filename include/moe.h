@@ -14,6 +14,9 @@
  *              table (fwd / dgrad / wgrad; offs or m_indptr read on the device; no
  *              padding; empty groups give zero weight gradients), "Prepared
  *              launches" (new offsets may be written between launches).
+ *   [BGMV]     "flashinfer.fused_moe.prepare_bgmv_moe": signature, Parameters and
+ *              description (MoE-LoRA shrink + expand, fixed-order accumulation,
+ *              hidden split with a last-workgroup reduction).
  *   [SM90]     "flashinfer.fused_moe.cute_dsl_fused_moe_bf16": formula
  *              out[t] = sum_k scale[t,k] * ffn(x[t]; e[t,k]), "Supported
  *              configuration" (shape rules, num_tokens == 0, EP shard),
@@ -341,6 +344,42 @@ moe_status moe_ffn_backward(const moe_ffn_desc* desc, const moe_ffn_tensors* ten
 moe_status moe_route_backward(const int32_t* topk_ids, const float* topk_weights,
                               const float* dtopk_weights, int64_t T, int32_t num_experts,
                               int32_t top_k, float* dlogits, void* stream);
+
+/*
+ * moe_bgmv -- BGMV MoE-LoRA shrink + expand over routed pairs ([BGMV] signature,
+ * Parameters, description). For pair p with token t = sorted_token_ids[p], expert
+ * e = expert_ids[p] and LoRA l = lora_indices[t]:
+ *   shrink_out[p, :] = bf16_rne(x[t] @ lora_a[l, e].T)                    (rank values)
+ *   y_accum[t, :]    = sum over t's pairs in ascending p of
+ *                      topk_weights[p] * (shrink_out[p] @ lora_b[l, e].T)   (float32)
+ * y_accum rows are fully overwritten (row stride ldy >= feat_out elements; it may be
+ * a column slice of a wider buffer); a token without a valid pair gets a zero row.
+ * A pair whose token, expert or LoRA index is out of range contributes nothing
+ * (its shrink row is zero); indices are not validated otherwise (device data).
+ * Shapes: x [T, H] bf16; lora_a [num_loras, E, rank, H] bf16; lora_b
+ * [num_loras, E, feat_out, rank] bf16 (one LoRA slice); sorted_token_ids,
+ * expert_ids [num_pairs] int32 in any order; lora_indices [T] int32; topk_weights
+ * [num_pairs] float32; shrink_out [num_pairs, rank] bf16 or NULL (kept in ws).
+ * Rules: rank in {8, 16, 32, 64}; H and feat_out multiples of 8; x, lora_a,
+ * lora_b, shrink_out 16-byte aligned. Bitwise reproducible: every output has one
+ * owner that sums in a fixed order. ws: moe_bgmv_workspace_size(desc) bytes.
+ */
+typedef struct moe_bgmv_desc {
+  int64_t num_tokens;         /* T */
+  int64_t num_pairs;          /* routed (token, expert) pairs */
+  int32_t hidden;             /* H */
+  int32_t feat_out;           /* LoRA-B output width */
+  int32_t rank;
+  int32_t num_loras;
+  int32_t num_experts;
+} moe_bgmv_desc;
+
+size_t moe_bgmv_workspace_size(const moe_bgmv_desc* desc);
+moe_status moe_bgmv(const moe_bgmv_desc* desc, const void* x, const void* lora_a,
+                    const void* lora_b, const int32_t* sorted_token_ids,
+                    const int32_t* expert_ids, const int32_t* lora_indices,
+                    const float* topk_weights, void* shrink_out, float* y_accum, int64_t ldy,
+                    void* ws, size_t ws_bytes, void* stream);
 
 /*
  * moe_finalize -- deterministic top-k combine ([SM90] use_fused_finalize=False):

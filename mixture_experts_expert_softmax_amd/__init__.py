@@ -24,7 +24,7 @@ __all__ = [
     "moe_finalize", "moe_fc1", "moe_fc2", "status_string", "ACT", "FINALIZE", "WFMT",
     "moe_ffn_forward_mx", "moe_fc1_mx", "moe_fc2_mx", "moe_ffn_forward_fp8", "moe_fc1_fp8",
     "moe_fc2_fp8", "moe_ffn_forward_train", "moe_ffn_backward", "moe_route_backward", "MoEFunction",
-    "moe_tune_mx", "moe_tune_clear",
+    "moe_tune_mx", "moe_tune_clear", "moe_bgmv",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -59,6 +59,11 @@ class MoeFfnGrads(ctypes.Structure):
                 ("grad_dtype", _i32)]
 
 
+class MoeBgmvDesc(ctypes.Structure):
+    _fields_ = [("num_tokens", _i64), ("num_pairs", _i64), ("hidden", _i32), ("feat_out", _i32),
+                ("rank", _i32), ("num_loras", _i32), ("num_experts", _i32)]
+
+
 # name -> (restype, argtypes)
 EXPORTS = {
     "moe_status_string": (ctypes.c_char_p, [_i32]),
@@ -89,6 +94,9 @@ EXPORTS = {
     "moe_route_backward": (_i32, [_vp, _vp, _vp, _i64, _i32, _i32, _vp, _vp]),
     "moe_tune_mx": (_i32, [ctypes.POINTER(MoeFfnDesc), ctypes.POINTER(MoeFfnTensors), _vp, _sz, _vp, _vp]),
     "moe_tune_clear": (None, []),
+    "moe_bgmv_workspace_size": (_sz, [ctypes.POINTER(MoeBgmvDesc)]),
+    "moe_bgmv": (_i32, [ctypes.POINTER(MoeBgmvDesc), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64,
+                        _vp, _sz, _vp]),
 }
 
 _LIB: Optional[ctypes.CDLL] = None
@@ -631,6 +639,43 @@ def moe_fc2_fp8(act, act_scale, w2, w2_scale, offs, T, top_k, num_experts, local
     _check("moe_fc2_fp8", lib().moe_fc2_fp8(ctypes.byref(d), _ptr(act), _ptr(act_scale), _ptr(w2),
                                             _ptr(w2_scale), _ptr(offs), _ptr(y), _stream()))
     return y
+
+
+def moe_bgmv(x: torch.Tensor, lora_a: torch.Tensor, lora_b: torch.Tensor,
+             sorted_token_ids: torch.Tensor, expert_ids: torch.Tensor, lora_indices: torch.Tensor,
+             topk_weights: torch.Tensor, num_experts: int, shrink_out: Optional[torch.Tensor] = None,
+             y_accum: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+    """BGMV MoE-LoRA shrink + expand. x [T,H] bf16, lora_a [nl,E,rank,H], lora_b [nl,E,N,rank]
+    bf16, sorted_token_ids / expert_ids [P] int32, lora_indices [T] int32, topk_weights [P]
+    float32. Returns (y_accum [T, N] float32 (or the given, possibly strided, view), shrink
+    [P, rank] bf16)."""
+    _dev(x, torch.bfloat16, "x"), _dev(lora_a, torch.bfloat16, "lora_a"), _dev(lora_b, torch.bfloat16, "lora_b")
+    for t_, n_ in ((sorted_token_ids, "sorted_token_ids"), (expert_ids, "expert_ids"),
+                   (lora_indices, "lora_indices")):
+        _dev(t_, torch.int32, n_)
+    _dev(topk_weights, torch.float32, "topk_weights")
+    T, H = x.shape
+    nl, E, r, H2 = lora_a.shape
+    N = lora_b.shape[2]
+    if H2 != H or tuple(lora_b.shape) != (nl, E, N, r) or E != num_experts:
+        raise ValueError("bgmv: lora_a must be [nl, E, rank, H] and lora_b [nl, E, N, rank]")
+    P = sorted_token_ids.numel()
+    d = MoeBgmvDesc(T, P, H, N, r, nl, num_experts)
+    h = lib()
+    if workspace is None:
+        workspace = torch.empty(max(h.moe_bgmv_workspace_size(ctypes.byref(d)), 16), dtype=torch.uint8,
+                                device=x.device)
+    if shrink_out is None:
+        shrink_out = torch.empty((max(P, 1), r), dtype=torch.bfloat16, device=x.device)
+    if y_accum is None:
+        y_accum = torch.empty((T, N), dtype=torch.float32, device=x.device)
+    if y_accum.dtype != torch.float32 or y_accum.shape != (T, N) or y_accum.stride(1) != 1:
+        raise ValueError("bgmv: y_accum must be float32 [T, feat_out] with unit column stride")
+    _check("moe_bgmv", h.moe_bgmv(ctypes.byref(d), _ptr(x), _ptr(lora_a), _ptr(lora_b), _ptr(sorted_token_ids),
+                                  _ptr(expert_ids), _ptr(lora_indices), _ptr(topk_weights), _ptr(shrink_out),
+                                  _ptr(y_accum), y_accum.stride(0), _ptr(workspace), workspace.numel(),
+                                  _stream()))
+    return y_accum, shrink_out[:P]
 
 
 def moe_finalize(y: torch.Tensor, e2p: torch.Tensor, topk_weights: torch.Tensor, out=None):

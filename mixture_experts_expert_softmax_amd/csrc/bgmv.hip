@@ -1,0 +1,355 @@
+// BGMV MoE-LoRA shrink + expand over routed (token, expert) pairs.
+//
+// BGMV page ("flashinfer.fused_moe.prepare_bgmv_moe"), signature, Parameters and
+// description: per pair p with token t = sorted_token_ids[p], expert e =
+// expert_ids[p] and LoRA l = lora_indices[t],
+//   shrink  s[p, :] = x[t] @ A[l, e].T           (rank values, stored in bf16)
+//   expand  y[t, :] = sum over t's pairs, ascending p, of w[p] * (s[p] @ B[l, e].T)
+// with y in float32. Every output has one owner that sums its routes in that fixed
+// order, so results are the same on every run. Few pairs: the shrink splits the
+// hidden dimension over extra workgroups and the last one of a pair to finish sums
+// the fp32 partials in split order.
+//
+// Both steps stream LoRA weights (cache- / HBM-bound GEMV work): one workgroup per
+// (pair, hidden split) for the shrink -- the x segment staged in LDS, each wave
+// owning rank rows and each lane 16-byte chunks of a row, butterfly-reduced -- and
+// one per (token, 256 output columns) for the expand, each thread one column whose
+// B row (rank values) it reads with 16-byte loads. The shrink publishes each pair in
+// a 16-slot token -> pair index; the expand sorts a token's slots ascending, or
+// scans all pairs in order for a token with more than 16.
+#include <algorithm>
+
+#include "common.h"
+
+namespace moe {
+namespace {
+
+constexpr int BG_SLOTS = 16;
+constexpr int BG_SPLIT_MAX = 8;
+constexpr int BG_XSEG = 2048;   // 16-byte x chunks staged per shrink workgroup (32 KB)
+
+struct BgArgs {
+  const uint4* x;              // [T][H/8]
+  const uint4* A;              // [nl][E][r][H/8]
+  const uint4* B;              // [nl][E][N][r/8]
+  const int32_t* tok;          // [P]
+  const int32_t* ex;           // [P]
+  const int32_t* lidx;         // [T]
+  const float* w;              // [P]
+  uint16_t* s;                 // [P][r] bf16
+  float* y;                    // [T][ldy]
+  int64_t ldy;
+  int32_t* cnt;                // [T] routes published per token
+  int32_t* ri;                 // [T][BG_SLOTS]
+  float* part;                 // [P][S][r]
+  int32_t* scnt;               // [P] arrivals
+  int64_t T, P;
+  int H8, N, r, nl, E, S;
+};
+
+__device__ __forceinline__ bool pair_ok(const BgArgs& a, int64_t p, int& t, int& e, int& l) {
+  t = a.tok[p];
+  e = a.ex[p];
+  if (t < 0 || t >= a.T || e < 0 || e >= a.E) return false;
+  l = a.lidx[t];
+  return l >= 0 && l < a.nl;
+}
+
+__device__ __forceinline__ float dot8(uint4 u, uint4 v, float acc) {
+  const uint32_t a[4] = {u.x, u.y, u.z, u.w};
+  const uint32_t b[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    acc = fmaf(__uint_as_float(a[q] << 16), __uint_as_float(b[q] << 16), acc);
+    acc = fmaf(__uint_as_float(a[q] & 0xFFFF0000u), __uint_as_float(b[q] & 0xFFFF0000u), acc);
+  }
+  return acc;
+}
+
+__global__ __launch_bounds__(256) void k_bgmv_zero(int32_t* __restrict__ cnt, int64_t T,
+                                                   int32_t* __restrict__ scnt, int64_t P) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < T) cnt[i] = 0;
+  if (scnt && i < P) scnt[i] = 0;
+}
+
+// Workgroup (pair p, split sp) of the shrink; wave w owns rank rows w + 4i (RPW of
+// them). A lane walks its chunks c = lane, lane + 64, ... and loads chunk c of all its
+// rows together (independent loads, one latency for all rows), keeping one fp32 sum per
+// row in chunk order; the rows are then reduced across the wave by butterflies.
+template <int RPW>
+__global__ __launch_bounds__(256) void k_bgmv_shrink(BgArgs a) {
+  __shared__ uint4 xs[BG_XSEG];
+  __shared__ int last;
+  const int64_t p = blockIdx.x / a.S;
+  const int sp = (int)(blockIdx.x - p * a.S);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  int t, e, l;
+  if (!pair_ok(a, p, t, e, l)) {   // contributes nothing; its shrink row reads as zeros
+    if (sp == 0 && tid < a.r) a.s[p * a.r + tid] = 0;
+    return;
+  }
+  if (sp == 0 && tid == 0) {
+    const int slot = atomicAdd(a.cnt + t, 1);
+    if (slot < BG_SLOTS) a.ri[(int64_t)t * BG_SLOTS + slot] = (int32_t)p;
+  }
+  const int c0 = (int)((int64_t)a.H8 * sp / a.S), c1 = (int)((int64_t)a.H8 * (sp + 1) / a.S);
+  const int nc = c1 - c0;
+  for (int c = tid; c < nc; c += 256) xs[c] = a.x[(int64_t)t * a.H8 + c0 + c];
+  __syncthreads();
+  const uint4* Ab = a.A + (((int64_t)l * a.E + e) * a.r + wid) * a.H8 + c0;
+  float acc[RPW];
+#pragma unroll
+  for (int i = 0; i < RPW; ++i) acc[i] = 0.f;
+  for (int c = lane; c < nc; c += 64) {
+    uint4 v[RPW];
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) v[i] = Ab[(int64_t)(4 * i) * a.H8 + c];
+    const uint4 xv = xs[c];
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) acc[i] = dot8(xv, v[i], acc[i]);
+  }
+#pragma unroll
+  for (int i = 0; i < RPW; ++i) {
+    float v = acc[i];
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
+    acc[i] = v;
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) {
+      const int j = wid + 4 * i;
+      if (a.S == 1)
+        a.s[p * a.r + j] = (uint16_t)(pack_bf16x2(acc[i], 0.f) & 0xFFFFu);
+      else
+        a.part[(p * a.S + sp) * a.r + j] = acc[i];
+    }
+    if (a.S > 1) __threadfence();   // visible to the split that sums the partials
+  }
+  if (a.S == 1) return;
+  // the last split of the pair to arrive sums the partials in split order
+  __syncthreads();
+  if (tid == 0) {
+    const int old = __hip_atomic_fetch_add(a.scnt + p, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    last = old == a.S - 1;
+  }
+  __syncthreads();
+  if (!last || tid >= a.r) return;
+  __atomic_thread_fence(__ATOMIC_ACQUIRE);
+  float v = 0.f;
+  for (int q = 0; q < a.S; ++q)
+    v += __hip_atomic_load(a.part + (p * a.S + q) * a.r + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  a.s[p * a.r + tid] = (uint16_t)(pack_bf16x2(v, 0.f) & 0xFFFFu);
+}
+
+// Workgroup (token t, 256-column tile) of the expand; thread = output column. The
+// token's pairs are taken in ascending order in batches of up to 16: their shrink
+// rows, weights and experts are staged in LDS (shared by all columns), then each
+// thread loads the B rows of 4 pairs at a time (independent loads) and adds the
+// pairs' terms in order. RC = rank / 8 (16-byte chunks of a row).
+template <int RC>
+__global__ __launch_bounds__(256) void k_bgmv_expand(BgArgs a, int col_tiles) {
+  __shared__ int32_t plist[256];
+  __shared__ uint4 ssh[BG_SLOTS][RC];
+  __shared__ float wsh[BG_SLOTS];
+  __shared__ int esh[BG_SLOTS];
+  __shared__ int nlist;
+  __shared__ int wcount[4];
+  const int64_t t = blockIdx.x / col_tiles;
+  const int ct = (int)(blockIdx.x - t * col_tiles);
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int c = ct * 256 + tid;
+  const bool col_ok = c < a.N;
+  const int l = a.lidx[t];
+  float acc = 0.f;
+  // pairs plist[i0 .. i0 + nb), nb <= 16, in order
+  auto run_batch = [&](int i0, int nb) {
+    if (tid < nb * RC) {
+      const int u = tid / RC, q = tid - u * RC;
+      const int64_t p = plist[i0 + u];
+      ssh[u][q] = reinterpret_cast<const uint4*>(a.s + p * a.r)[q];
+      if (q == 0) {
+        wsh[u] = a.w[p];
+        esh[u] = a.ex[p];
+      }
+    }
+    __syncthreads();
+    const int64_t cc = col_ok ? c : 0;
+    for (int u0 = 0; u0 < nb; u0 += 4) {
+      uint4 bv[4][RC];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (u0 + u < nb) {
+          const uint4* bp = a.B + (((int64_t)l * a.E + esh[u0 + u]) * a.N + cc) * RC;
+#pragma unroll
+          for (int q = 0; q < RC; ++q) bv[u][q] = bp[q];
+        }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (u0 + u < nb) {
+          float d = 0.f;
+#pragma unroll
+          for (int q = 0; q < RC; ++q) d = dot8(ssh[u0 + u][q], bv[u][q], d);
+          acc = fmaf(wsh[u0 + u], d, acc);
+        }
+    }
+    __syncthreads();
+  };
+  const int n = a.cnt[t];
+  if (n <= BG_SLOTS) {
+    // the published slots in ascending order: slot i goes to its rank among the n
+    // (pair indices are distinct)
+    if (tid < n) {
+      const int v = a.ri[t * BG_SLOTS + tid];
+      int rank = 0;
+      for (int k = 0; k < n; ++k) rank += a.ri[t * BG_SLOTS + k] < v;
+      plist[rank] = v;
+    }
+    __syncthreads();
+    if (n > 0) run_batch(0, n);
+  } else {   // more than 16 routes: scan every pair in order, 256 at a time
+    for (int64_t base = 0; base < a.P; base += 256) {
+      const int64_t p = base + tid;
+      int tt = -1, ee = 0, ll = 0;
+      const bool hit = p < a.P && pair_ok(a, p, tt, ee, ll) && tt == t;
+      const uint64_t m = __ballot(hit);
+      if (lane == 0) wcount[wid] = __popcll(m);
+      __syncthreads();
+      const int before = (wid > 0 ? wcount[0] : 0) + (wid > 1 ? wcount[1] : 0) + (wid > 2 ? wcount[2] : 0);
+      if (hit) plist[before + __popcll(m & ((1ull << lane) - 1))] = (int32_t)p;
+      if (tid == 0) nlist = wcount[0] + wcount[1] + wcount[2] + wcount[3];
+      __syncthreads();
+      const int nl = nlist;
+      for (int i = 0; i < nl; i += BG_SLOTS) run_batch(i, nl - i < BG_SLOTS ? nl - i : BG_SLOTS);
+      __syncthreads();   // wcount / nlist / plist are rewritten by the next chunk
+    }
+  }
+  if (col_ok) a.y[t * a.ldy + c] = acc;
+}
+
+}  // namespace
+
+size_t bgmv_workspace_bytes(int64_t T, int64_t P, int r) {
+  size_t o = 0;
+  o += align_up((size_t)T * 4, 256);                       // cnt
+  o += align_up((size_t)T * BG_SLOTS * 4, 256);            // ri
+  o += align_up((size_t)P * BG_SPLIT_MAX * r * 4, 256);    // split partials
+  o += align_up((size_t)P * 4, 256);                       // split arrivals
+  o += align_up((size_t)P * r * 2, 256);                   // shrink rows (if not the caller's)
+  return o;
+}
+
+moe_status bgmv_enqueue(const void* x, const void* A, const void* B, const int32_t* tok,
+                        const int32_t* ex, const int32_t* lidx, const float* w, void* shrink,
+                        float* y, int64_t ldy, int64_t T, int64_t P, int H, int N, int r, int nl,
+                        int E, void* ws, hipStream_t st) {
+  if (T == 0) return MOE_OK;
+  char* wp = reinterpret_cast<char*>(ws);
+  BgArgs a{};
+  a.x = reinterpret_cast<const uint4*>(x);
+  a.A = reinterpret_cast<const uint4*>(A);
+  a.B = reinterpret_cast<const uint4*>(B);
+  a.tok = tok;
+  a.ex = ex;
+  a.lidx = lidx;
+  a.w = w;
+  a.y = y;
+  a.ldy = ldy;
+  a.T = T;
+  a.P = P;
+  a.H8 = H / 8;
+  a.N = N;
+  a.r = r;
+  a.nl = nl;
+  a.E = E;
+  size_t o = 0;
+  a.cnt = reinterpret_cast<int32_t*>(wp + o);  o += align_up((size_t)T * 4, 256);
+  a.ri = reinterpret_cast<int32_t*>(wp + o);   o += align_up((size_t)T * BG_SLOTS * 4, 256);
+  a.part = reinterpret_cast<float*>(wp + o);   o += align_up((size_t)P * BG_SPLIT_MAX * r * 4, 256);
+  a.scnt = reinterpret_cast<int32_t*>(wp + o); o += align_up((size_t)P * 4, 256);
+  a.s = shrink ? reinterpret_cast<uint16_t*>(shrink) : reinterpret_cast<uint16_t*>(wp + o);
+  // hidden splits: enough workgroups for two per CU, each split at least 64 chunks
+  // per lane row pass and at most BG_XSEG chunks (its x segment lives in LDS)
+  const int cu = device_cu_count();
+  int S = 1;
+  if (P > 0) {
+    S = (int)std::min<int64_t>((2 * cu + P - 1) / P, BG_SPLIT_MAX);
+    S = std::min(S, std::max(1, a.H8 / 64));
+  }
+  while ((a.H8 + S - 1) / S > BG_XSEG) ++S;
+  if (S > BG_SPLIT_MAX) return MOE_ERR_UNSUPPORTED;
+  a.S = S;
+  const int64_t nz = std::max(T, P);
+  k_bgmv_zero<<<(unsigned)((nz + 255) / 256), 256, 0, st>>>(a.cnt, T, a.scnt, P);
+  moe_status s = launch_status();
+  if (s != MOE_OK) return s;
+  if (P > 0) {
+    if (P * S > INT32_MAX) return MOE_ERR_UNSUPPORTED;
+    const unsigned g = (unsigned)(P * S);
+    if (r == 8)
+      k_bgmv_shrink<2><<<g, 256, 0, st>>>(a);
+    else if (r == 16)
+      k_bgmv_shrink<4><<<g, 256, 0, st>>>(a);
+    else if (r == 32)
+      k_bgmv_shrink<8><<<g, 256, 0, st>>>(a);
+    else
+      k_bgmv_shrink<16><<<g, 256, 0, st>>>(a);
+    s = launch_status();
+    if (s != MOE_OK) return s;
+  }
+  const int col_tiles = (N + 255) / 256;
+  if (T * col_tiles > INT32_MAX) return MOE_ERR_UNSUPPORTED;
+  const unsigned ge = (unsigned)(T * col_tiles);
+  if (r == 8)
+    k_bgmv_expand<1><<<ge, 256, 0, st>>>(a, col_tiles);
+  else if (r == 16)
+    k_bgmv_expand<2><<<ge, 256, 0, st>>>(a, col_tiles);
+  else if (r == 32)
+    k_bgmv_expand<4><<<ge, 256, 0, st>>>(a, col_tiles);
+  else
+    k_bgmv_expand<8><<<ge, 256, 0, st>>>(a, col_tiles);
+  return launch_status();
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+static moe_status check_bgmv(const moe_bgmv_desc* d) {
+  if (!d) return MOE_ERR_NULL;
+  if (d->num_tokens < 0 || d->num_pairs < 0 || d->num_pairs > INT32_MAX) return MOE_ERR_SHAPE;
+  if (d->hidden < 8 || d->hidden % 8 || d->feat_out < 8 || d->feat_out % 8) return MOE_ERR_SHAPE;
+  if (d->rank != 8 && d->rank != 16 && d->rank != 32 && d->rank != 64) return MOE_ERR_SHAPE;
+  if (d->num_loras < 1 || d->num_experts < 1) return MOE_ERR_SHAPE;
+  if (d->hidden / 8 > BG_XSEG * BG_SPLIT_MAX) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+extern "C" size_t moe_bgmv_workspace_size(const moe_bgmv_desc* d) {
+  if (check_bgmv(d) != MOE_OK) return 0;
+  return bgmv_workspace_bytes(d->num_tokens, d->num_pairs, d->rank);
+}
+
+extern "C" moe_status moe_bgmv(const moe_bgmv_desc* d, const void* x, const void* lora_a,
+                               const void* lora_b, const int32_t* sorted_token_ids,
+                               const int32_t* expert_ids, const int32_t* lora_indices,
+                               const float* topk_weights, void* shrink_out, float* y_accum,
+                               int64_t ldy, void* ws, size_t ws_bytes, void* stream) {
+  moe_status s = check_bgmv(d);
+  if (s != MOE_OK) return s;
+  if (d->num_tokens == 0) return MOE_OK;
+  if (ldy < d->feat_out) return MOE_ERR_SHAPE;
+  if (!x || !lora_indices || !y_accum) return MOE_ERR_NULL;
+  if (d->num_pairs > 0 && (!lora_a || !lora_b || !sorted_token_ids || !expert_ids || !topk_weights))
+    return MOE_ERR_NULL;
+  if (!aligned16(x) || !aligned16(lora_a) || !aligned16(lora_b) ||
+      (shrink_out && !aligned16(shrink_out)))
+    return MOE_ERR_ALIGN;
+  if (!ws || ws_bytes < bgmv_workspace_bytes(d->num_tokens, d->num_pairs, d->rank) || !aligned16(ws))
+    return MOE_ERR_WORKSPACE;
+  return bgmv_enqueue(x, lora_a, lora_b, sorted_token_ids, expert_ids, lora_indices, topk_weights,
+                      shrink_out, y_accum, ldy, d->num_tokens, d->num_pairs, d->hidden, d->feat_out,
+                      d->rank, d->num_loras, d->num_experts, ws, as_stream(stream));
+}

@@ -38,7 +38,8 @@ __all__ = [
     "MoECase", "GroupedGemmCase", "moe_case", "tiny_moe", "mixtral_moe",
     "expert_shard_moe", "grouped_gemm_case", "dirichlet_group_sizes",
     "route_logits", "bf16_to_f32", "to_bf16", "mx_quant_e4m3", "mx_quant_e2m1", "W4A8Case",
-    "w4a8_moe", "fp8_quant_per_tensor", "FP8_ACT_SCALE", "upstream_grad",
+    "w4a8_moe", "fp8_quant_per_tensor", "FP8_ACT_SCALE", "upstream_grad", "BgmvCase",
+    "bgmv_case",
 ]
 
 _THREADS = max(1, min(16, os.cpu_count() or 1))
@@ -381,3 +382,49 @@ def w4a8_moe(seed: int = 0, T: int = 8192, H: int = 7168, I: int = 2048, E: int 
         list(ex.map(fill, range(E)))
     act_scale = np.array([FP8_ACT_SCALE], np.float32) if pt else None
     return W4A8Case(T, H, I, E, top_k, logits, x, x_sf, w1, w1_sf, w2, w2_sf, wfmt, act_scale)
+
+
+# ---------------------------------------------------------------------------
+# BGMV MoE-LoRA inputs: x N(0,1), LoRA-A N(0, 1/H), LoRA-B N(0, 1/rank) (bf16);
+# per token top_k distinct experts drawn uniformly and Dirichlet(1) routing weights;
+# LoRA index per token uniform in [0, num_loras) (a share of -1 = no adapter if
+# asked). Pair order: "contiguous" (p = t * top_k + s), "expert" (stable by expert)
+# or "random" (a permutation).
+# ---------------------------------------------------------------------------
+@dataclass
+class BgmvCase:
+    x: torch.Tensor            # [T, H] bf16
+    lora_a: torch.Tensor       # [num_loras, E, rank, H] bf16
+    lora_b: torch.Tensor       # [num_loras, E, feat_out, rank] bf16
+    sorted_token_ids: np.ndarray   # [P] int32
+    expert_ids: np.ndarray         # [P] int32
+    lora_indices: np.ndarray       # [T] int32
+    topk_weights: np.ndarray       # [P] float32
+    num_experts: int
+
+
+def bgmv_case(seed: int = 0, T: int = 2048, H: int = 3072, rank: int = 32, num_loras: int = 4,
+              E: int = 8, top_k: int = 2, feat_out: Optional[int] = None, order: str = "contiguous",
+              no_lora_share: float = 0.0) -> BgmvCase:
+    g = np.random.default_rng(seed)
+    N = H if feat_out is None else feat_out
+    x = to_bf16(g.standard_normal((T, H), dtype=np.float32))
+    a = g.standard_normal((num_loras, E, rank, H), dtype=np.float32) * np.float32(math.sqrt(1.0 / H))
+    b = g.standard_normal((num_loras, E, N, rank), dtype=np.float32) * np.float32(math.sqrt(1.0 / rank))
+    ex = np.stack([g.permutation(E)[:top_k] for _ in range(T)]).astype(np.int32)
+    wt = g.dirichlet(np.ones(top_k), size=T).astype(np.float32)
+    li = g.integers(0, num_loras, T).astype(np.int32)
+    if no_lora_share > 0:
+        li[g.random(T) < no_lora_share] = -1
+    tok = np.repeat(np.arange(T, dtype=np.int32), top_k)
+    ex, wt = ex.reshape(-1), wt.reshape(-1)
+    if order == "expert":
+        perm = np.argsort(ex, kind="stable")
+    elif order == "random":
+        perm = g.permutation(tok.shape[0])
+    elif order == "contiguous":
+        perm = np.arange(tok.shape[0])
+    else:
+        raise ValueError(order)
+    return BgmvCase(x, to_bf16(a), to_bf16(b), tok[perm].copy(), ex[perm].copy(), li,
+                    wt[perm].copy(), E)
