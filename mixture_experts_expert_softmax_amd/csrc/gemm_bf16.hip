@@ -342,94 +342,109 @@ __device__ __forceinline__ void atomic_add_bf16x2(uint16_t* p, float a, float b)
                                              __builtin_bit_cast(bf16x2_t, bits));
 }
 
-// Main loop for a contraction that is a whole number of 64-wide stages. The body
-// has no branches, so one explicit issue order can be given for it: the 8 weight /
-// activation fragment reads of the next 16-deep step are interleaved with the 16
-// MFMAs of the current one, the 16 global loads of the next stage are spread over
-// the first two steps, and its 16 LDS stores over the last. A lone wave per SIMD
-// only stalls on its own waits, so keeping LDS latency behind MFMA issue is what
-// keeps the matrix cores fed. The final stage re-loads itself (unused) so that
-// the body needs no condition.
-__device__ __forceinline__ void mainloop_full(RowLoader& la, RowLoader& lb, uint4* smem, int kbase,
-                                              int ktiles, int tid, int lane, int wn, int wm,
-                                              f32x16 (&acc)[4][4]) {
-  const int lrow = tid >> 3;
-  const int pc = la.ch ^ ((lrow >> 1) & 7);
-  const int rsel = lane & 31, kg = lane >> 5, sw = (lane >> 1) & 7;
+// Direct-to-LDS copy of one 16-byte chunk per lane: the chunk at g lands at LDS byte
+// address lds + 16 * lane (lds goes to M0). The compiler does not see this LDS
+// write, so the loop below counts copies in flight itself (vmcnt) before each barrier
+// that publishes a stage.
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(lds) : "memory");
+}
+
+// Main loop for a contraction that is a whole number of 64-wide stages, as a
+// pipeline of DMA_SLOTS 32-deep stages fetched straight into LDS without passing
+// through registers (32 KB a stage: the 256 activation rows, then the 256 weight
+// rows, 64 bytes each). Stage s + DMA_SLOTS - 1 is requested while stage s is
+// consumed, so a copy has three stages of MFMA work to land, and each copy is issued
+// right after one fragment read so the copies go out spread over the stage's MFMAs
+// (issued back to back, they stall the wave on the address unit ahead of its
+// MFMAs). A row's four 16-byte chunks are stored at chunk ^ ((row / 4) % 4), which
+// keeps the 32-row fragment reads free of bank conflicts; copy j of wave w covers
+// rows 64 j + 16 w + lane / 4, so lane l fetches global chunk (l % 4) ^ ((l / 16) % 4).
+// The loop is rotated by one 16-deep step: the last step of a stage runs after the
+// barrier, under the first fragment reads of the next. Stages past the end re-load
+// the last one into a slot nobody reads, which keeps the copy count uniform.
+constexpr int DMA_SLOTS = 4;
+constexpr int DMA_STAGE_U4 = 2 * TB * 32 * 2 / 16;   // uint4 slots per 32-deep stage
+static_assert(DMA_SLOTS * DMA_STAGE_U4 <= 4 * TILE_U4, "stages exceed the kernel's LDS");
+
+__device__ __forceinline__ void mainloop_dma(const uint16_t* abase, const uint32_t (&aoff)[4],
+                                             const uint16_t* bbase, const uint32_t (&boff)[4],
+                                             uint4* smem, int kbase, int nsub, int tid, int lane,
+                                             int wn, int wm, f32x16 (&acc)[4][4]) {
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int gch = (lane & 3) ^ ((lane >> 4) & 3);
+  const uint32_t lds0 = (uint32_t)(uintptr_t)smem + (uint32_t)w * 1024u;
+  const int rsel = lane & 31, kg = lane >> 5, sw = (rsel >> 2) & 3;
+  constexpr uint32_t STAGE_B = DMA_STAGE_U4 * 16, HALF_B = STAGE_B / 2;
+  // all 8 copies of stage `sub` into `slot` (the pipeline fill)
+  auto issue = [&](int sub, int slot) {
+    const int k = kbase + sub * 32 + gch * 8;
+    const uint32_t d = lds0 + (uint32_t)slot * STAGE_B;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    la.r[j] = *reinterpret_cast<const uint4*>(la.base + la.off[j] + kbase + la.ch * 8);
-    lb.r[j] = *reinterpret_cast<const uint4*>(lb.base + lb.off[j] + kbase + lb.ch * 8);
-  }
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    smem[(lrow + 32 * j) * 8 + pc] = la.r[j];
-    smem[TILE_U4 + (lrow + 32 * j) * 8 + pc] = lb.r[j];
-  }
-  __syncthreads();
-  for (int kt = 0; kt < ktiles; ++kt) {
-    const int s = kt & 1;
-    const int kn = kbase + (kt + 1 < ktiles ? kt + 1 : kt) * TK + la.ch * 8;
-    const uint4* Xs = smem + s * 2 * TILE_U4;
-    const uint4* Ws = Xs + TILE_U4;
-    uint4* Xn = smem + (s ^ 1) * 2 * TILE_U4;
-    uint4* Wn = Xn + TILE_U4;
-    bf16x8 wf[2][4], xf[2][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) wf[0][i] = as_bf16x8(Ws[(wn * 128 + i * 32 + rsel) * 8 + (kg ^ sw)]);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) xf[0][j] = as_bf16x8(Xs[(wm * 128 + j * 32 + rsel) * 8 + (kg ^ sw)]);
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const int cur = kk & 1, nxt = cur ^ 1;
-      if (kk < 2) {
-#pragma unroll
-        for (int j = kk * 4; j < kk * 4 + 4; ++j) {
-          la.r[j] = *reinterpret_cast<const uint4*>(la.base + la.off[j] + kn);
-          lb.r[j] = *reinterpret_cast<const uint4*>(lb.base + lb.off[j] + kn);
-        }
-      }
-      if (kk < 3) {
-        const int c1 = (((kk + 1) << 1) + kg) ^ sw;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) wf[nxt][i] = as_bf16x8(Ws[(wn * 128 + i * 32 + rsel) * 8 + c1]);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) xf[nxt][j] = as_bf16x8(Xs[(wm * 128 + j * 32 + rsel) * 8 + c1]);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[cur][i], xf[cur][j], acc[i][j], 0, 0, 0);
-      if (kk == 3) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          Xn[(lrow + 32 * j) * 8 + pc] = la.r[j];
-          Wn[(lrow + 32 * j) * 8 + pc] = lb.r[j];
-        }
-      }
+    for (int j = 0; j < 4; ++j) {
+      dma16(abase + aoff[j] + k, d + j * 4096u);
+      dma16(bbase + boff[j] + k, d + HALF_B + j * 4096u);
     }
-    // issue order (mask 0x008 MFMA, 0x100 LDS read, 0x200 LDS write, 0x020 global load)
-    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
-    for (int q = 0; q < 2; ++q) {
+  };
+  bf16x8 wf[2][4], xf[2][4];
+  // fragment reads of step kk (of 2) of the stage in `slot`; after every second read
+  // one copy of half h of stage `sub` into slot `dslot`
+  auto rd_issue = [&](int slot, int kk, int set, int sub, int dslot, int h) {
+    const uint4* Xs = smem + slot * DMA_STAGE_U4;
+    const uint4* Ws = Xs + DMA_STAGE_U4 / 2;
+    const int c = ((kk << 1) + kg) ^ sw;
+    const int k = kbase + sub * 32 + gch * 8;
+    const uint32_t d = lds0 + (uint32_t)dslot * STAGE_B + (uint32_t)h * HALF_B;
+    const uint16_t* base = h ? bbase : abase;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      wf[set][i] = as_bf16x8(Ws[(wn * 128 + i * 32 + rsel) * 4 + c]);
+      if (i & 1) dma16(base + (h ? boff[i >> 1] : aoff[i >> 1]) + k, d + (i >> 1) * 4096u);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      xf[set][j] = as_bf16x8(Xs[(wm * 128 + j * 32 + rsel) * 4 + c]);
+      if (j & 1) dma16(base + (h ? boff[2 + (j >> 1)] : aoff[2 + (j >> 1)]) + k, d + (2 + (j >> 1)) * 4096u);
+    }
+  };
+  auto mm = [&](int set) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[set][i], xf[set][j], acc[i][j], 0, 0, 0);
+  };
+  auto body = [&](int sub, bool first) {
+    const int slot = sub & (DMA_SLOTS - 1);
+    const int nxt = sub + DMA_SLOTS - 1 < nsub ? sub + DMA_SLOTS - 1 : nsub - 1;
+    const int dslot = (sub + DMA_SLOTS - 1) & (DMA_SLOTS - 1);
+    rd_issue(slot, 0, 0, nxt, dslot, 0);
+    if (!first) mm(1);   // the previous stage's last step
+    rd_issue(slot, 1, 1, nxt, dslot, 1);
+    mm(0);
+    // issue order (mask 0x008 MFMA, 0x100 LDS read): each read between two MFMAs
+    if (first) __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+    for (int q = 0; q < (first ? 1 : 2); ++q)
       for (int r = 0; r < 8; ++r) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
       }
-    }
-    for (int r = 0; r < 8; ++r) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    }
-    for (int r = 0; r < 16; ++r) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
-    }
+    __builtin_amdgcn_sched_barrier(0);
+    // copies complete in issue order: at most the 8 of each of the two younger
+    // stages still in flight means stage sub + 1 has landed
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(8 * (DMA_SLOTS - 2)) : "memory");
     __syncthreads();
-  }
+  };
+  static_assert((DMA_SLOTS & (DMA_SLOTS - 1)) == 0, "slot index is taken with a mask");
+#pragma unroll
+  for (int q = 0; q < DMA_SLOTS - 1; ++q) issue(q < nsub ? q : nsub - 1, q);
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(8 * (DMA_SLOTS - 2)) : "memory");
+  __syncthreads();
+  body(0, true);
+  for (int sub = 1; sub < nsub; ++sub) body(sub, false);
+  mm(1);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // LDS is reused after the loop
 }
 
 // ---------------------------------------------------------------------------
@@ -437,7 +452,8 @@ __device__ __forceinline__ void mainloop_full(RowLoader& la, RowLoader& lb, uint
 // ---------------------------------------------------------------------------
 template <int EPI, bool KFULL>
 __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_nt(NtArgs a) {
-  __shared__ uint4 smem[4 * TILE_U4];  // [stage][A tile | B tile], 128 KB
+  // 128 KB: two 64-deep stages [A tile | B tile], or the full-K path's four 32-deep ones
+  __shared__ uint4 smem[4 * TILE_U4];
   const int ktiles = (a.K + TK - 1) / TK;
   int e, m0, mend, nt, k0 = 0, nk = ktiles, part = 0, S = 1, slot = 0, cidx = 0;
   if (KFULL) {
@@ -480,7 +496,27 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_nt(NtArgs a) {
   zero_acc(acc);
 
   if (KFULL) {
-    mainloop_full(la, lb, smem, k0 * TK, nk, tid, lane, wn, wm, acc);
+    // rows (tid / 4) + 64 j of both operands, in the order the copies fill a stage
+    uint32_t aoff[4], boff[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int R = (tid >> 2) + 64 * j;
+      int p = m0 + R;
+      p = p < mend ? p : mend - 1;
+      const int src = a.a_gather ? a.a_gather[p] / a.a_div : p;
+      aoff[j] = (uint32_t)src * (uint32_t)a.K;
+      int wrow;
+      if (EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_STEP) {
+        int c = nt * 128 + (R >> 7) * 64 + (R & 63);
+        c = c < a.I ? c : a.I - 1;
+        wrow = ((R >> 6) & 1) * a.I + c;
+      } else {
+        wrow = nt * TB + R;
+        wrow = wrow < a.NB ? wrow : a.NB - 1;
+      }
+      boff[j] = (uint32_t)wrow * (uint32_t)a.K;
+    }
+    mainloop_dma(a.A, aoff, lb.base, boff, smem, k0 * TK, nk * 2, tid, lane, wn, wm, acc);
     if (S > 1) {
       // a part of a split tile: publish the fp32 partial; the last of the S parts
       // to arrive sums all of them in part order (the same result whichever part
