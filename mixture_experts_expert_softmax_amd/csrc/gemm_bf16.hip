@@ -30,6 +30,8 @@
 //    XCD is given a contiguous range of the real tiles (counted on the device),
 //    ordered expert-major, column tile, row block: the row blocks sharing a
 //    weight tile run together on one XCD and read it from HBM once.
+#include <type_traits>
+
 #include "common.h"
 
 namespace moe {
@@ -447,6 +449,167 @@ __device__ __forceinline__ void mainloop_dma(const uint16_t* abase, const uint32
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // LDS is reused after the loop
 }
 
+// Copy of one 16-byte chunk per lane through a buffer resource: lands at LDS byte
+// address lds + 16 * lane; offsets at or past the resource's record count read as
+// zeros, which is how the copies below end ragged contractions and matrix edges.
+__device__ __forceinline__ void dma16_buf(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t lds) {
+  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(r), "{m0}"(lds) : "memory");
+}
+
+// Copy sources of the backward kernels' operands, for the same four-slot pipeline of
+// 32-deep stages (activation side in the first 16 KB of a stage, weight side in the
+// second). A copy instruction of wave w fills LDS bytes 4096 j + 1024 w .. + 1023
+// of its half, i.e.
+//  - row-major (contraction contiguous): rows 64 j + 16 w + lane / 4, 64 bytes
+//    each, chunk swizzle (row / 4) % 4 -- as in the forward loop;
+//  - K-major (contraction rows of 256 output columns, 512 bytes): contraction
+//    rows 8 j + 2 w + lane / 32, chunk (lane % 32) ^ ((row % 4) << 2) -- the
+//    layout the transposing fragment reads expect.
+struct RmSrc {              // row-major operand
+  const uint16_t* base;
+  uint32_t off[4];          // element offsets of the thread's 4 rows
+  int gch;                  // global chunk the lane fetches
+  __device__ __forceinline__ void init(int tid) {
+    const int lane = tid & 63;
+    gch = (lane & 3) ^ ((lane >> 4) & 3);
+  }
+};
+struct KmSrc {              // K-major operand: contraction row 0, first output column
+  const char* base;
+  int64_t ld2;              // bytes per contraction row
+  int rows;                 // valid contraction rows from base
+  int cols2;                // valid bytes of a row from base
+  uint32_t voff[4];         // byte offsets of the thread's chunks within a stage
+  __device__ __forceinline__ void init(int tid) {
+    const int lane = tid & 63, w = tid >> 6;
+    const int c = (lane & 31) ^ (((2 * w + (lane >> 5)) & 3) << 2);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      voff[j] = (uint32_t)((8 * j + 2 * w + (lane >> 5)) * ld2) + (uint32_t)c * 16u;
+  }
+  // resource over stage `sub` (< ceil(rows / 32), so at least one valid row): records
+  // end at the last valid byte of the operand. A stage reads at most 31 rows past its
+  // first plus one row, so counting at most 33 rows keeps the count exact in 32 bits.
+  __device__ __forceinline__ __amdgpu_buffer_rsrc_t stage(int sub) const {
+    int left = rows - sub * 32;
+    left = left < 33 ? left : 33;
+    const int n = (left - 1) * (int)ld2 + cols2;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base + (int64_t)sub * 32 * ld2),
+                                             (short)0, n, 0x00020000);
+  }
+};
+
+// Backward main loop: the forward's direct-to-LDS pipeline (four 32-deep slots,
+// copies three stages ahead interleaved with fragment reads, rotated by one step)
+// for operands in either layout. A = weight side (output columns), B = activation
+// side (output rows); kbase is the row-major operand's first contraction element.
+template <bool A_K, bool B_K, class SA, class SB>
+__device__ __forceinline__ void mainloop_dma_g(const SA& sa, const SB& sb, uint4* smem, int kbase,
+                                               int nsub, int tid, int lane, int wn, int wm,
+                                               f32x16 (&acc)[4][4]) {
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const uint32_t lds0 = (uint32_t)(uintptr_t)smem + (uint32_t)w * 1024u;
+  const int rsel = lane & 31, kg = lane >> 5, sw = (rsel >> 2) & 3;
+  constexpr uint32_t STAGE_B = DMA_STAGE_U4 * 16, HALF_B = STAGE_B / 2;
+  // the 4 copies of one operand's part of stage `sub` into LDS half at byte d
+  auto copy_rm = [&](const RmSrc& src, int sub, uint32_t d, int j) {
+    dma16(src.base + src.off[j] + kbase + sub * 32 + src.gch * 8, d + j * 4096u);
+  };
+
+  bf16x8 wf[2][4], xf[2][4];
+  auto rd_a = [&](const uint4* As, int kk, int set, int i) {
+    if constexpr (A_K) wf[set][i] = ktile_frag(As, kk, wn * 128 + i * 32, lane);
+    else wf[set][i] = as_bf16x8(As[(wn * 128 + i * 32 + rsel) * 4 + (((kk << 1) + kg) ^ sw)]);
+  };
+  auto rd_b = [&](const uint4* Bs, int kk, int set, int j) {
+    if constexpr (B_K) xf[set][j] = ktile_frag(Bs, kk, wm * 128 + j * 32, lane);
+    else xf[set][j] = as_bf16x8(Bs[(wm * 128 + j * 32 + rsel) * 4 + (((kk << 1) + kg) ^ sw)]);
+  };
+  // fragment reads of step kk of the stage in `slot`, each of the first four
+  // followed by one copy of operand H (0: B, 1: A) of stage `sub` into slot `dslot`
+  auto rd_issue = [&](int slot, int kk, int set, int sub, int dslot, auto hsel) {
+    constexpr int H = decltype(hsel)::value;
+    constexpr bool KM = H == 0 ? B_K : A_K;
+    const uint4* Bs = smem + slot * DMA_STAGE_U4;
+    const uint4* As = Bs + DMA_STAGE_U4 / 2;
+    const uint32_t d = lds0 + (uint32_t)dslot * STAGE_B + (uint32_t)H * HALF_B;
+    const auto& src = [&]() -> const auto& {
+      if constexpr (H == 0) return sb; else return sa;
+    }();
+    if constexpr (KM) {
+      const __amdgpu_buffer_rsrc_t r = src.stage(sub);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        rd_a(As, kk, set, i);
+        dma16_buf(r, src.voff[i], d + i * 4096u);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        rd_a(As, kk, set, i);
+        copy_rm(src, sub, d, i);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) rd_b(Bs, kk, set, j);
+  };
+  auto mm = [&](int set) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[set][i], xf[set][j], acc[i][j], 0, 0, 0);
+  };
+  auto issue = [&](int sub, int slot) {
+    const uint32_t d = lds0 + (uint32_t)slot * STAGE_B;
+    if constexpr (B_K) {
+      const __amdgpu_buffer_rsrc_t r = sb.stage(sub);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) dma16_buf(r, sb.voff[j], d + j * 4096u);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) copy_rm(sb, sub, d, j);
+    }
+    if constexpr (A_K) {
+      const __amdgpu_buffer_rsrc_t r = sa.stage(sub);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) dma16_buf(r, sa.voff[j], d + HALF_B + j * 4096u);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) copy_rm(sa, sub, d + HALF_B, j);
+    }
+  };
+  auto body = [&](int sub, bool first) {
+    const int slot = sub & (DMA_SLOTS - 1);
+    const int nxt = sub + DMA_SLOTS - 1 < nsub ? sub + DMA_SLOTS - 1 : nsub - 1;
+    const int dslot = (sub + DMA_SLOTS - 1) & (DMA_SLOTS - 1);
+    rd_issue(slot, 0, 0, nxt, dslot, std::integral_constant<int, 0>{});
+    if (!first) mm(1);
+    rd_issue(slot, 1, 1, nxt, dslot, std::integral_constant<int, 1>{});
+    mm(0);
+    // a step's NR fragment reads (two transposing reads per K-major fragment) go
+    // between the previous step's 16 MFMAs
+    constexpr int NR = (A_K ? 8 : 4) + (B_K ? 8 : 4);
+    if (first) __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
+    for (int q = 0; q < (first ? 1 : 2); ++q)
+      for (int r = 0; r < 16; ++r) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (r < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(8 * (DMA_SLOTS - 2)) : "memory");
+    __syncthreads();
+  };
+#pragma unroll
+  for (int q = 0; q < DMA_SLOTS - 1; ++q) issue(q < nsub ? q : nsub - 1, q);
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(8 * (DMA_SLOTS - 2)) : "memory");
+  __syncthreads();
+  body(0, true);
+  for (int sub = 1; sub < nsub; ++sub) body(sub, false);
+  mm(1);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
 // ---------------------------------------------------------------------------
 // fwd / FC1 / FC2: both operands contiguous along the contraction.
 // ---------------------------------------------------------------------------
@@ -688,25 +851,43 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_dgrad(DgradArgs a) {
   const int lrow = tid >> 3;
   const int c0 = nt * TB;
 
-  RowLoader lg;  // activation side: G rows, contraction along N
-  lg.base = a.G;
-  lg.K = a.N;
-  lg.ch = tid & 7;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    int p = m0 + lrow + 32 * j;
-    p = p < mend ? p : mend - 1;
-    lg.off[j] = (uint32_t)p * (uint32_t)a.N;
-  }
-  KLoader lw;  // weight side: W[e] rows n (contraction), columns k
-  lw.base = a.W + (int64_t)e * a.N * a.K + c0;
-  lw.ld = a.K;
-  lw.rows_left0 = a.N;
-  lw.cols_left = a.K - c0;
-
   f32x16 acc[4][4];
   zero_acc(acc);
-  mainloop_sched<true, false>(lw, lg, smem, (a.N + TK - 1) / TK, tid, lane, wn, wm, acc);
+  if (a.N % 32 == 0) {   // whole 32-deep stages: the direct-to-LDS pipeline
+    KmSrc sw;   // weight side: W[e] rows n (contraction), columns k
+    sw.base = reinterpret_cast<const char*>(a.W + (int64_t)e * a.N * a.K + c0);
+    sw.ld2 = 2 * (int64_t)a.K;
+    sw.rows = a.N;
+    sw.cols2 = 2 * (a.K - c0);
+    sw.init(tid);
+    RmSrc sg;   // activation side: G rows, contraction along N
+    sg.base = a.G;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      int p = m0 + (tid >> 2) + 64 * j;
+      p = p < mend ? p : mend - 1;
+      sg.off[j] = (uint32_t)p * (uint32_t)a.N;
+    }
+    sg.init(tid);
+    mainloop_dma_g<true, false>(sw, sg, smem, 0, a.N / 32, tid, lane, wn, wm, acc);
+  } else {
+    RowLoader lg;  // activation side: G rows, contraction along N
+    lg.base = a.G;
+    lg.K = a.N;
+    lg.ch = tid & 7;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      int p = m0 + lrow + 32 * j;
+      p = p < mend ? p : mend - 1;
+      lg.off[j] = (uint32_t)p * (uint32_t)a.N;
+    }
+    KLoader lw;  // weight side: W[e] rows n (contraction), columns k
+    lw.base = a.W + (int64_t)e * a.N * a.K + c0;
+    lw.ld = a.K;
+    lw.rows_left0 = a.N;
+    lw.cols_left = a.K - c0;
+    mainloop_sched<true, false>(lw, lg, smem, (a.N + TK - 1) / TK, tid, lane, wn, wm, acc);
+  }
   const int hi4 = (lane >> 5) * 4;
   float lim = 0.f;
   if (ACT == 2) lim = a.limits ? a.limits[e] : a.def_limit;
@@ -789,21 +970,25 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_wgrad(WgradArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int wn = wid & 1, wm = wid >> 1;
 
-  KLoader lx;  // weight side: output columns k from X rows
-  lx.base = a.X + (int64_t)start * a.K + c0;
-  lx.ld = a.K;
-  lx.rows_left0 = rows;
-  lx.cols_left = a.K - c0;
-  KLoader lgd;  // activation side: output rows n from G rows
-  lgd.base = a.G + (int64_t)start * a.N + n0;
-  lgd.ld = a.N;
-  lgd.rows_left0 = rows;
-  lgd.cols_left = a.N - n0;
+  // both operands K-major (contraction = the group's rows); copies past the group's
+  // last row or a matrix edge read as zeros
+  KmSrc sx;   // weight side: output columns k from X rows
+  sx.base = reinterpret_cast<const char*>(a.X + (int64_t)start * a.K + c0);
+  sx.ld2 = 2 * (int64_t)a.K;
+  sx.rows = rows;
+  sx.cols2 = 2 * (a.K - c0);
+  sx.init(tid);
+  KmSrc sgd;  // activation side: output rows n from G rows
+  sgd.base = reinterpret_cast<const char*>(a.G + (int64_t)start * a.N + n0);
+  sgd.ld2 = 2 * (int64_t)a.N;
+  sgd.rows = rows;
+  sgd.cols2 = 2 * (a.N - n0);
+  sgd.init(tid);
 
   f32x16 acc[4][4];
   zero_acc(acc);
-  const int ktiles = (rows + TK - 1) / TK;
-  if (ktiles > 0) mainloop_sched<true, true>(lx, lgd, smem, ktiles, tid, lane, wn, wm, acc);
+  const int nsub = (rows + 31) / 32;
+  if (nsub > 0) mainloop_dma_g<true, true>(sx, sgd, smem, 0, nsub, tid, lane, wn, wm, acc);
   const int hi4 = (lane >> 5) * 4;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
