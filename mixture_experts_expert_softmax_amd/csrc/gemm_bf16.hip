@@ -165,66 +165,11 @@ struct RowLoader {
     for (int j = 0; j < 8; ++j)
       r[j] = ok ? *reinterpret_cast<const uint4*>(base + off[j] + k0) : make_uint4(0, 0, 0, 0);
   }
-  __device__ __forceinline__ void load(int kt, int) { load(kt); }
-  // loads j0 .. j0 + 3 of stage kt (the scheduled loop issues a stage in two halves)
-  __device__ __forceinline__ void load4(int kt, int, int j0) {
-    const int k0 = kt * TK + ch * 8;
-    const bool ok = k0 < K;
-#pragma unroll
-    for (int j = j0; j < j0 + 4; ++j)
-      r[j] = ok ? *reinterpret_cast<const uint4*>(base + off[j] + k0) : make_uint4(0, 0, 0, 0);
-  }
   __device__ __forceinline__ void store(uint4* __restrict__ lds, int tid) const {
     const int row = tid >> 3;
     const int pc = ch ^ ((row >> 1) & 7);
 #pragma unroll
     for (int j = 0; j < 8; ++j) lds[(row + 32 * j) * 8 + pc] = r[j];
-  }
-};
-
-// Tile rows that are contiguous along the OUTPUT dimension (the operand is used
-// transposed): source rows are contraction indices. Thread tid reads contraction
-// row (tid & 63) and 8 output columns per chunk (tid >> 6) + 4j, and scatters
-// the 8 values into the [output row][contraction] LDS layout.
-// A K-major operand tile (contraction rows x output columns, rows contiguous in
-// memory): 64 contraction rows x 256 columns per stage. Thread t loads rows
-// t / 32 + 8j, 16-byte chunk t % 32 (whole 512-byte rows per 32 lanes) and stores
-// them unchanged into LDS rows of 32 chunks, chunk c of row r at c ^ ((r & 3) << 2)
-// so that the transposing fragment reads below hit distinct banks. Rows past the
-// contraction end read as zeros; columns are whole 16-byte chunks (multiples of 32).
-struct KLoader {
-  const uint16_t* base;   // contraction row 0 of the operand, column c0
-  int64_t ld;             // row stride (elements)
-  int rows_left0;         // valid contraction rows from base
-  int cols_left;          // valid output columns from c0
-  uint4 r[8];
-  __device__ __forceinline__ void load(int kt, int tid) {
-    const int c = tid & 31;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int kr = kt * TK + (tid >> 5) + 8 * j;
-      const bool ok = kr < rows_left0 && c * 8 < cols_left;
-      r[j] = ok ? *reinterpret_cast<const uint4*>(base + (int64_t)kr * ld + c * 8)
-                : make_uint4(0, 0, 0, 0);
-    }
-  }
-  __device__ __forceinline__ void load4(int kt, int tid, int j0) {
-    const int c = tid & 31;
-#pragma unroll
-    for (int j = j0; j < j0 + 4; ++j) {
-      const int kr = kt * TK + (tid >> 5) + 8 * j;
-      const bool ok = kr < rows_left0 && c * 8 < cols_left;
-      r[j] = ok ? *reinterpret_cast<const uint4*>(base + (int64_t)kr * ld + c * 8)
-                : make_uint4(0, 0, 0, 0);
-    }
-  }
-  __device__ __forceinline__ void store(uint4* __restrict__ lds, int tid) const {
-    const int c = tid & 31;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int row = (tid >> 5) + 8 * j;
-      lds[row * 32 + (c ^ ((row & 3) << 2))] = r[j];
-    }
   }
 };
 
@@ -250,82 +195,6 @@ __device__ __forceinline__ bf16x8 ktile_frag(const uint4* __restrict__ lds, int 
   typedef short v8i16 __attribute__((ext_vector_type(8)));
   const v8i16 both{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
   return __builtin_bit_cast(bf16x8, both);
-}
-
-// Scheduled main loop for the dgrad / wgrad operand layouts (A = weight side, output
-// columns; B = activation side, output rows; either row-major [256][8 chunks] or
-// K-major [64][32 chunks] in LDS; tile A at smem + TILE_U4, B at smem, per stage).
-// The same issue order as the forward loop: the next 16-deep step's fragment reads
-// go between the current step's 16 MFMAs, half of the next stage's global loads
-// each into steps 0 and 1 and its LDS stores into step 3. Loads past the operand
-// read as zeros, so the last stage loads (and stores) an unused one and the body
-// has no branches.
-template <bool A_K, bool B_K, class LA, class LB>
-__device__ __forceinline__ void mainloop_sched(LA& la, LB& lb, uint4* smem, int ktiles, int tid,
-                                               int lane, int wn, int wm, f32x16 (&acc)[4][4]) {
-  la.load(0, tid);
-  lb.load(0, tid);
-  lb.store(smem, tid);
-  la.store(smem + TILE_U4, tid);
-  __syncthreads();
-  for (int kt = 0; kt < ktiles; ++kt) {
-    const int s = kt & 1;
-    const uint4* Bs = smem + s * 2 * TILE_U4;
-    const uint4* As = Bs + TILE_U4;
-    uint4* Bn = smem + (s ^ 1) * 2 * TILE_U4;
-    uint4* An = Bn + TILE_U4;
-    bf16x8 wf[2][4], xf[2][4];
-    auto rd = [&](int kk, bf16x8 (&wq)[4], bf16x8 (&xq)[4]) {
-      const int ch = ((kk << 1) + (lane >> 5)) ^ ((lane >> 1) & 7);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        wq[i] = A_K ? ktile_frag(As, kk, wn * 128 + i * 32, lane)
-                    : as_bf16x8(As[(wn * 128 + i * 32 + (lane & 31)) * 8 + ch]);
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        xq[j] = B_K ? ktile_frag(Bs, kk, wm * 128 + j * 32, lane)
-                    : as_bf16x8(Bs[(wm * 128 + j * 32 + (lane & 31)) * 8 + ch]);
-    };
-    rd(0, wf[0], xf[0]);
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const int cur = kk & 1, nxt = cur ^ 1;
-      if (kk < 2) {
-        la.load4(kt + 1, tid, kk * 4);
-        lb.load4(kt + 1, tid, kk * 4);
-      }
-      if (kk < 3) rd(kk + 1, wf[nxt], xf[nxt]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[cur][i], xf[cur][j], acc[i][j], 0, 0, 0);
-      if (kk == 3) {
-        lb.store(Bn, tid);
-        la.store(An, tid);
-      }
-    }
-    // issue order (0x008 MFMA, 0x100 LDS read, 0x200 LDS write, 0x020 global load);
-    // NR fragment reads per step: 4 per row-major operand, 8 per K-major one (two
-    // transposing 8-byte reads per fragment)
-    constexpr int NR = (A_K ? 8 : 4) + (B_K ? 8 : 4);
-    __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
-    for (int q = 0; q < 2; ++q)
-      for (int r = 0; r < 16; ++r) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        if (r < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        if (r & 1) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-      }
-    for (int r = 0; r < 16; ++r) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (r < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-    for (int r = 0; r < 16; ++r) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
-    }
-    __syncthreads();
-  }
 }
 
 __device__ __forceinline__ void zero_acc(f32x16 (&acc)[4][4]) {
@@ -848,46 +717,27 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_dgrad(DgradArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int wn = wid & 1, wm = wid >> 1;
-  const int lrow = tid >> 3;
   const int c0 = nt * TB;
 
   f32x16 acc[4][4];
   zero_acc(acc);
-  if (a.N % 32 == 0) {   // whole 32-deep stages: the direct-to-LDS pipeline
-    KmSrc sw;   // weight side: W[e] rows n (contraction), columns k
-    sw.base = reinterpret_cast<const char*>(a.W + (int64_t)e * a.N * a.K + c0);
-    sw.ld2 = 2 * (int64_t)a.K;
-    sw.rows = a.N;
-    sw.cols2 = 2 * (a.K - c0);
-    sw.init(tid);
-    RmSrc sg;   // activation side: G rows, contraction along N
-    sg.base = a.G;
+  // (the contraction N is a multiple of 32: whole 32-deep stages)
+  KmSrc sw;   // weight side: W[e] rows n (contraction), columns k
+  sw.base = reinterpret_cast<const char*>(a.W + (int64_t)e * a.N * a.K + c0);
+  sw.ld2 = 2 * (int64_t)a.K;
+  sw.rows = a.N;
+  sw.cols2 = 2 * (a.K - c0);
+  sw.init(tid);
+  RmSrc sg;   // activation side: G rows, contraction along N
+  sg.base = a.G;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      int p = m0 + (tid >> 2) + 64 * j;
-      p = p < mend ? p : mend - 1;
-      sg.off[j] = (uint32_t)p * (uint32_t)a.N;
-    }
-    sg.init(tid);
-    mainloop_dma_g<true, false>(sw, sg, smem, 0, a.N / 32, tid, lane, wn, wm, acc);
-  } else {
-    RowLoader lg;  // activation side: G rows, contraction along N
-    lg.base = a.G;
-    lg.K = a.N;
-    lg.ch = tid & 7;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      int p = m0 + lrow + 32 * j;
-      p = p < mend ? p : mend - 1;
-      lg.off[j] = (uint32_t)p * (uint32_t)a.N;
-    }
-    KLoader lw;  // weight side: W[e] rows n (contraction), columns k
-    lw.base = a.W + (int64_t)e * a.N * a.K + c0;
-    lw.ld = a.K;
-    lw.rows_left0 = a.N;
-    lw.cols_left = a.K - c0;
-    mainloop_sched<true, false>(lw, lg, smem, (a.N + TK - 1) / TK, tid, lane, wn, wm, acc);
+  for (int j = 0; j < 4; ++j) {
+    int p = m0 + (tid >> 2) + 64 * j;
+    p = p < mend ? p : mend - 1;
+    sg.off[j] = (uint32_t)p * (uint32_t)a.N;
   }
+  sg.init(tid);
+  mainloop_dma_g<true, false>(sw, sg, smem, 0, a.N / 32, tid, lane, wn, wm, acc);
   const int hi4 = (lane >> 5) * 4;
   float lim = 0.f;
   if (ACT == 2) lim = a.limits ? a.limits[e] : a.def_limit;
