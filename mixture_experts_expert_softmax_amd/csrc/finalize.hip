@@ -15,6 +15,8 @@
 namespace moe {
 namespace {
 
+typedef unsigned u32x4n __attribute__((ext_vector_type(4)));   // for nontemporal access
+
 template <int KMAX>
 __global__ __launch_bounds__(256) void k_finalize(const uint4* __restrict__ y,
                                                   const int32_t* __restrict__ e2p,
@@ -33,9 +35,17 @@ __global__ __launch_bounds__(256) void k_finalize(const uint4* __restrict__ y,
     p[s] = s < k ? e2p[t * k + s] : -1;
     ws[s] = s < k ? (w ? w[t * k + s] : 1.f) : 0.f;   // no weights: a plain sum
   }
+  // y rows are read once and out written once: nontemporal accesses keep them from
+  // displacing cached lines (measured 5.07 -> 5.54 TB/s at T = 65536, H = 7168, k = 8)
 #pragma unroll
-  for (int s = 0; s < KMAX; ++s)
-    v[s] = p[s] >= 0 ? y[(int64_t)p[s] * H8 + c] : make_uint4(0, 0, 0, 0);
+  for (int s = 0; s < KMAX; ++s) {
+    if (p[s] >= 0) {
+      const u32x4n r = __builtin_nontemporal_load(reinterpret_cast<const u32x4n*>(y + (int64_t)p[s] * H8 + c));
+      v[s] = make_uint4(r.x, r.y, r.z, r.w);
+    } else {
+      v[s] = make_uint4(0, 0, 0, 0);
+    }
+  }
   float acc[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) acc[j] = 0.f;
@@ -54,7 +64,7 @@ __global__ __launch_bounds__(256) void k_finalize(const uint4* __restrict__ y,
   o.y = pack_bf16x2(acc[2], acc[3]);
   o.z = pack_bf16x2(acc[4], acc[5]);
   o.w = pack_bf16x2(acc[6], acc[7]);
-  out[idx] = o;
+  __builtin_nontemporal_store(u32x4n{o.x, o.y, o.z, o.w}, reinterpret_cast<u32x4n*>(out + idx));
 }
 
 }  // namespace
