@@ -74,6 +74,39 @@ def test_grouped_gemm_integer_exact_small():
                                   bf16_round(ref_dw))
 
 
+def _sweep_shapes(n=10, seed=11):
+    """Seeded random shapes: N and K multiples of 32 at every residue modulo the
+    256-wide tiles, ragged groups (empty ones, single rows, counts that are not
+    multiples of 32, and more than one 256-row tile)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        E = int(rng.integers(1, 9))
+        K = 32 * int(rng.integers(1, 25))
+        N = 32 * int(rng.integers(1, 25))
+        sizes = rng.choice([0, 1, int(rng.integers(2, 40)), int(rng.integers(40, 300)),
+                            int(rng.integers(300, 700))], size=E)
+        out.append((i, K, N, [int(v) for v in sizes]))
+    return out
+
+
+@pytest.mark.parametrize("i,K,N,sizes", _sweep_shapes())
+def test_grouped_gemm_shape_sweep_integer_exact(i, K, N, sizes):
+    """fwd / dgrad / wgrad on integer-valued operands are exact at any shape, so the
+    tile edges (rows, columns and contraction past a 256 or 32 boundary, empty and
+    1-row groups) must match the oracle bit for bit."""
+    c = S.grouped_gemm_case(seed=100 + i, sizes=np.array(sizes), K=K, N=N, integer_valued=True)
+    x, g, w, offs = _to_dev(c)
+    np.testing.assert_array_equal(to_np(M.grouped_gemm_fwd(x, w, offs)),
+                                  bf16_round(O.grouped_gemm_fwd(_f(c.x), _f(c.w), c.offs)))
+    np.testing.assert_array_equal(to_np(M.grouped_gemm_dgrad(g, w, offs)),
+                                  bf16_round(O.grouped_gemm_dgrad(_f(c.g), _f(c.w), c.offs)))
+    ref_dw = O.grouped_gemm_wgrad(_f(c.g), _f(c.x), c.offs)
+    np.testing.assert_array_equal(to_np(M.grouped_gemm_wgrad(g, x, offs, out_dtype=torch.float32)), ref_dw)
+    np.testing.assert_array_equal(to_np(M.grouped_gemm_wgrad(g, x, offs, out_dtype=torch.bfloat16)),
+                                  bf16_round(ref_dw))
+
+
 @pytest.fixture(scope="module")
 def full_int():
     return S.grouped_gemm_case(seed=0, integer_valued=True)
