@@ -29,6 +29,8 @@
 // weight codes [256][4 x 16 B] (MXFP4) or [256][8 x 16 B] (MXFP8), and both
 // operands' 4 scale bytes per row; two stages (100 KB / 132 KB). Tiles are dealt
 // out as in the bf16 kernels (device-counted, XCD-balanced, expert-major).
+#include <type_traits>
+
 #include "common.h"
 
 namespace moe {
@@ -59,6 +61,18 @@ constexpr uint32_t UNIT_SCALE4 = 0x7F7F7F7Fu;
 enum MxEpi { MX_FC1_SWIGLU = 0, MX_FC1_STEP = 1, MX_FC2 = 2 };
 
 typedef int v8i __attribute__((ext_vector_type(8)));
+
+// Direct-to-LDS copies (MXFP4 256-row kernel): lane l's 16 (4) bytes from g land at
+// LDS byte address lds + 16 l (4 l). The compiler does not see these LDS writes; the
+// loop counts the copies in flight itself (vmcnt) before each barrier.
+__device__ __forceinline__ void mx_dma16(const void* g, uint32_t lds) {
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(lds) : "memory");
+}
+__device__ __forceinline__ void mx_dma4(const void* g, uint32_t lds) {
+  asm volatile("global_load_lds_dword %0, off" ::"v"(g), "{m0}"(lds) : "memory");
+}
+// MXFP4 stages in LDS: three slots (150 KB), copies two stages ahead
+constexpr int MX_DMA_SLOTS = 3;
 
 struct MxArgs {
   const uint8_t* A;        // activation codes [rows][K]
@@ -114,7 +128,7 @@ __global__ __launch_bounds__(MNT, 1) void k_gemm_mx(MxArgs a) {
   constexpr bool BS = block_scaled<WF>();
   constexpr int WCH = wch<WF>(), WT_U4 = MTB * WCH, STAGE_U4 = stage_u4<WF>();
   constexpr int WLD = WT_U4 / MNT;   // weight loads per thread and stage (4 or 8)
-  __shared__ uint4 smem[2 * STAGE_U4];
+  __shared__ uint4 smem[(WF == WF_MXFP4 ? MX_DMA_SLOTS : 2) * STAGE_U4];
   int e, m0, mend, nt;
   if (!deal_tile<MTB>(a.ends, a.E, a.m_cap, a.n_tiles, e, m0, mend, nt)) return;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
@@ -202,10 +216,131 @@ __global__ __launch_bounds__(MNT, 1) void k_gemm_mx(MxArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
+  const int ktiles = K / MTK;
+  if constexpr (WF == WF_MXFP4) {
+    // MXFP4: stages copied straight into LDS, MX_DMA_SLOTS slots, two stages ahead.
+    // Copy j of wave w: activation rows 32 j + 8 w + lane / 8 (whole 128-byte rows,
+    // global chunk (lane % 8) ^ ((row / 2) % 8)); weight rows 64 j + 16 w + lane / 4
+    // (64-byte rows, chunk (lane % 4) ^ ((row / 4) % 4)); scale words of rows
+    // 64 w + lane. These are the layouts the fragment reads below expect. The loop
+    // is rotated by one step: a stage's second step runs after the barrier, under
+    // the first fragment reads of the next stage.
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const uint32_t lds0 = (uint32_t)(uintptr_t)smem + (uint32_t)w * 1024u;
+    const uint32_t lds0s = (uint32_t)(uintptr_t)smem + (uint32_t)w * 256u;
+    constexpr uint32_t XT_B = XT_U4 * 16, WT_B = WT_U4 * 16, STAGE_B = STAGE_U4 * 16;
+    const int gx = (lane & 7) ^ ((4 * w + (lane >> 4)) & 7);
+    const int gw = (lane & 3) ^ ((lane >> 4) & 3);
+    uint32_t xrow[8], wrowb[4];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) xrow[j] = xoff[j] - xc * 16;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) wrowb[j] = woff[j] - wc * 16;
+    // copy c (0..13) of stage q into the slot at byte offset d: 8 activation-row
+    // copies, 4 weight-row copies, then the two scale words
+    auto cp = [&](int c, int q, uint32_t d) {
+      if (c < 8) {
+        mx_dma16(a.A + xrow[c] + q * MTK + gx * 16, lds0 + d + c * 4096u);
+      } else if (c < 12) {
+        mx_dma16(Bb + wrowb[c - 8] + q * (MTK / 2) + gw * 16, lds0 + d + XT_B + (c - 8) * 4096u);
+      } else if (c == 12) {
+        mx_dma4(a.A_sf + xsoff + q * (MTK / 32), lds0s + d + XT_B + WT_B);
+      } else {
+        mx_dma4(Bs + wsoff + q * (MTK / 32), lds0s + d + XT_B + WT_B + 1024u);
+      }
+    };
+    v8i wf[2][4], xf[2][4];
+    // scale words of the current stage and of the previous one (whose second step
+    // runs at the start of the current stage)
+    uint32_t wsr[4], xsr[4], wsp[4], xsp[4];
+    auto rd_scales = [&](int slot) {
+      const uint32_t* XS = reinterpret_cast<const uint32_t*>(smem + slot * STAGE_U4 + XT_U4 + WT_U4);
+      const uint32_t* WS = XS + MTB;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) wsr[i] = WS[wn * 128 + i * 32 + rsel];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) xsr[j] = XS[wm * 128 + j * 32 + rsel];
+    };
+    // fragment reads of step kk of `slot` (4 weight, 8 activation), copies c0..c0+6
+    // of stage q into slot offset d after the first seven of them
+    auto rd_issue = [&](int slot, int kk, int set, int q, uint32_t d, int c0) {
+      const uint4* X = smem + slot * STAGE_U4;
+      const uint4* W = X + XT_U4;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = wn * 128 + i * 32 + rsel;
+        const uint4 v = W[r * 4 + ((2 * kk + g) ^ ((r >> 2) & 3))];
+        wf[set][i] = v8i{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+        cp(c0 + i, q, d);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = wm * 128 + j * 32 + rsel;
+        const uint4 lo = X[r * 8 + ((4 * kk + g) ^ ((r >> 1) & 7))];
+        if (j < 3) cp(c0 + 4 + j, q, d);
+        const uint4 hi = X[r * 8 + ((4 * kk + 2 + g) ^ ((r >> 1) & 7))];
+        xf[set][j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      }
+    };
+    auto mm = [&](int set, int kk, const uint32_t (&ws)[4], const uint32_t (&xs)[4]) {
+      const int sh = 8 * (2 * kk + g);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              wf[set][i], xf[set][j], acc[i][j], a_fmt<WF>(), 0, 0, (int)((ws[i] >> sh) & 0xFF), 0,
+              (int)((xs[j] >> sh) & 0xFF));
+    };
+    auto body = [&](int st, bool first) {
+      const int slot = st % MX_DMA_SLOTS;
+      const int q = st + MX_DMA_SLOTS - 1 < ktiles ? st + MX_DMA_SLOTS - 1 : ktiles - 1;
+      const uint32_t d = (uint32_t)((st + MX_DMA_SLOTS - 1) % MX_DMA_SLOTS) * STAGE_B;
+      rd_scales(slot);
+      rd_issue(slot, 0, 0, q, d, 0);
+      if (!first) mm(1, 1, wsp, xsp);   // the previous stage's second step
+      rd_issue(slot, 1, 1, q, d, 7);
+      mm(0, 0, wsr, xsr);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        wsp[i] = wsr[i];
+        xsp[i] = xsr[i];
+      }
+      // issue order (0x008 MFMA, 0x100 LDS read): the 8 scale reads and step 0's 12
+      // fragment reads, then step 1's 12 between step 0's MFMAs (non-first: the
+      // 20 between the previous stage's last step)
+      if (first) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 20, 0);
+      } else {
+        for (int r = 0; r < 16; ++r) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          if (r & 3) {} else __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+      }
+      for (int r = 0; r < 16; ++r) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (r < 12) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // copies complete in issue order: the younger stage's 14 may still be in flight
+      asm volatile("s_waitcnt vmcnt(14)" ::: "memory");
+      __syncthreads();
+    };
+#pragma unroll
+    for (int q = 0; q < MX_DMA_SLOTS - 1; ++q)
+#pragma unroll
+      for (int c = 0; c < 14; ++c) cp(c, q < ktiles ? q : ktiles - 1, (uint32_t)q * STAGE_B);
+    asm volatile("s_waitcnt vmcnt(14)" ::: "memory");
+    __syncthreads();
+    body(0, true);
+    for (int st = 1; st < ktiles; ++st) body(st, false);
+    mm(1, 1, wsp, xsp);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  } else {
   // Branch-free main loop (the last stage re-loads itself, unused) with one issue
   // order: the next step's fragment reads and the next stage's global loads are
   // interleaved with the first step's MFMAs, its LDS stores with the second's.
-  const int ktiles = K / MTK;
   gload(0);
   sstore(0);
   __syncthreads();
@@ -281,6 +416,7 @@ __global__ __launch_bounds__(MNT, 1) void k_gemm_mx(MxArgs a) {
     if (16 - NPAIR > 0) __builtin_amdgcn_sched_group_barrier(0x008, 16 - NPAIR, 0);
     if (NST - NPAIR > 0) __builtin_amdgcn_sched_group_barrier(0x200, NST - NPAIR, 0);
     __syncthreads();
+  }
   }
 
   const int hi4 = (lane >> 5) * 4;
