@@ -73,6 +73,10 @@ __device__ __forceinline__ void mx_dma4(const void* g, uint32_t lds) {
 }
 // MXFP4 stages in LDS: three slots (150 KB), copies two stages ahead
 constexpr int MX_DMA_SLOTS = 3;
+// 8-bit weight families: four slots of 64-deep stages (activation and weight codes,
+// 16 KB each, then both operands' scale words for MXFP8), copies three stages ahead
+constexpr int MX8_SLOTS = 4;
+template <int WF> constexpr int MX8_STAGE_U4() { return 2 * 1024 + (WF == 2 ? 0 : 2 * 64); }
 
 struct MxArgs {
   const uint8_t* A;        // activation codes [rows][K]
@@ -128,7 +132,7 @@ __global__ __launch_bounds__(MNT, 1) void k_gemm_mx(MxArgs a) {
   constexpr bool BS = block_scaled<WF>();
   constexpr int WCH = wch<WF>(), WT_U4 = MTB * WCH, STAGE_U4 = stage_u4<WF>();
   constexpr int WLD = WT_U4 / MNT;   // weight loads per thread and stage (4 or 8)
-  __shared__ uint4 smem[(WF == WF_MXFP4 ? MX_DMA_SLOTS : 2) * STAGE_U4];
+  __shared__ uint4 smem[WF == WF_MXFP4 ? MX_DMA_SLOTS * STAGE_U4 : MX8_SLOTS * MX8_STAGE_U4<WF>()];
   int e, m0, mend, nt;
   if (!deal_tile<MTB>(a.ends, a.E, a.m_cap, a.n_tiles, e, m0, mend, nt)) return;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
@@ -171,43 +175,6 @@ __global__ __launch_bounds__(MNT, 1) void k_gemm_mx(MxArgs a) {
     xsoff = (uint32_t)src * (uint32_t)ks;
     wsoff = (uint32_t)wrow_of(tid) * (uint32_t)ks;
   }
-  u32x4 rx[8], rw[WLD];
-  uint32_t rxs, rws;
-  auto gload = [&](int kt) {
-    const int kb = kt * MTK;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) rx[j] = *reinterpret_cast<const u32x4*>(a.A + xoff[j] + kb);
-#pragma unroll
-    for (int j = 0; j < WLD; ++j) rw[j] = *reinterpret_cast<const u32x4*>(Bb + woff[j] + kb * WB / 8);
-    if (BS) {
-      rxs = *reinterpret_cast<const uint32_t*>(a.A_sf + xsoff + kb / 32);
-      rws = *reinterpret_cast<const uint32_t*>(Bs + wsoff + kb / 32);
-    }
-  };
-  // weight chunk swizzle: 64-byte rows (MXFP4) by (r >> 2) & 3, 128-byte rows by
-  // (r >> 1) & 7, so that each 16-lane group of a fragment read hits 64 distinct banks
-  auto wswz = [](int r) { return WCH == 4 ? (r >> 2) & 3 : (r >> 1) & 7; };
-  auto sstore = [&](int s) {
-    u32x4* X = reinterpret_cast<u32x4*>(smem + s * STAGE_U4);
-    u32x4* W = X + XT_U4;
-    uint32_t* XS = reinterpret_cast<uint32_t*>(W + WT_U4);
-    uint32_t* WS = XS + MTB;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int r = xr + 32 * j;
-      X[r * 8 + (xc ^ ((r >> 1) & 7))] = rx[j];
-    }
-#pragma unroll
-    for (int j = 0; j < WLD; ++j) {
-      const int r = wr + (MTB / WLD) * j;
-      W[r * WCH + (wc ^ wswz(r))] = rw[j];
-    }
-    if (BS) {
-      XS[tid] = rxs;
-      WS[tid] = rws;
-    }
-  };
-
   f32x16 acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -338,85 +305,146 @@ __global__ __launch_bounds__(MNT, 1) void k_gemm_mx(MxArgs a) {
     mm(1, 1, wsp, xsp);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   } else {
-  // Branch-free main loop (the last stage re-loads itself, unused) with one issue
-  // order: the next step's fragment reads and the next stage's global loads are
-  // interleaved with the first step's MFMAs, its LDS stores with the second's.
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < ktiles; ++kt) {
-    const int s = kt & 1;
-    const uint4* X = smem + s * STAGE_U4;
-    const uint4* W = X + XT_U4;
-    const uint32_t* XS = reinterpret_cast<const uint32_t*>(W + WT_U4);
-    const uint32_t* WS = XS + MTB;
-    uint32_t wsr[4], xsr[4];
+    // MXFP8 / FP8: 64-deep stages copied straight into LDS, MX8_SLOTS slots, three
+    // stages ahead; each stage is one scaled-MFMA step. Copy j of wave w covers rows
+    // 64 j + 16 w + lane / 4 of the activation and of the weight codes (64-byte rows,
+    // global chunk (lane % 4) ^ ((row / 4) % 4)); MXFP8 also copies the scale word of
+    // the stage's 128-deep block for rows 64 w + lane. Loop rotated by one step: the
+    // previous stage's MFMAs run under the current stage's fragment reads.
+    constexpr uint32_t CODE_B = 16384, SLOT_B = MX8_STAGE_U4<WF>() * 16;
+    // Copies per wave: 8 code copies per stage, plus (MXFP8) the 2 scale words for
+    // even stages only -- both stages of a 128-deep block use the even one's words.
+    // An odd-parity body issues an even stage (or, clamped at the end, a copy nobody
+    // reads) and copies the words; an even-parity body does not. Any two consecutive
+    // bodies therefore have NWAIT copies in flight at a barrier.
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const uint32_t lds0 = (uint32_t)(uintptr_t)smem + (uint32_t)w * 1024u;
+    const uint32_t lds0s = (uint32_t)(uintptr_t)smem + (uint32_t)w * 256u;
+    const int gc = (lane & 3) ^ ((lane >> 4) & 3);
+    uint32_t xrow[4], wrow[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) wsr[i] = BS ? WS[wn * 128 + i * 32 + rsel] : UNIT_SCALE4;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) xsr[j] = BS ? XS[wm * 128 + j * 32 + rsel] : UNIT_SCALE4;
+    for (int j = 0; j < 4; ++j) {
+      const int R = (tid >> 2) + 64 * j;
+      int p = m0 + R;
+      p = p < mend ? p : mend - 1;
+      const int src = a.a_gather ? a.a_gather[p] / a.a_div : p;
+      xrow[j] = (uint32_t)src * (uint32_t)K + gc * 16;
+      wrow[j] = (uint32_t)wrow_of(R) * kw + gc * 16;
+    }
+    const int nsub = K / 64;
+    auto cp = [&](int c, int q, uint32_t d) {
+      if (c < 4) {
+        mx_dma16(a.A + xrow[c] + q * 64, lds0 + d + c * 4096u);
+      } else if (c < 8) {
+        mx_dma16(Bb + wrow[c - 4] + q * 64, lds0 + d + CODE_B + (c - 4) * 4096u);
+      } else if (c == 8) {
+        mx_dma4(a.A_sf + xsoff + (q >> 1) * 4, lds0s + d + 2 * CODE_B);
+      } else {
+        mx_dma4(Bs + wsoff + (q >> 1) * 4, lds0s + d + 2 * CODE_B + 1024u);
+      }
+    };
     v8i wf[2][4], xf[2][4];
-    auto rd = [&](int kk, v8i (&wq)[4], v8i (&xq)[4]) {
+    uint32_t wsr[4], xsr[4], wsp[4], xsp[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wsr[i] = xsr[i] = wsp[i] = xsp[i] = UNIT_SCALE4;
+    constexpr int NWAIT = BS ? 18 : 16;
+    // fragment reads of the stage in `slot` (two 16-byte chunks per fragment), with
+    // the copies of stage q into slot offset d spread among them
+    auto rd_issue = [&](int slot, int set, int q, uint32_t d) {
+      const uint4* X = smem + slot * MX8_STAGE_U4<WF>();
+      const uint4* W = X + 1024;
+      // the two stages of a 128-deep block share their scale words: the odd stage
+      // keeps the even one's in registers
+      if (BS && set == 0) {
+        const uint32_t* XS = reinterpret_cast<const uint32_t*>(W + 1024);
+        const uint32_t* WS = XS + MTB;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) wsr[i] = WS[wn * 128 + i * 32 + rsel];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) xsr[j] = XS[wm * 128 + j * 32 + rsel];
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = wn * 128 + i * 32 + rsel;
-        if (WF == WF_MXFP4) {
-          const uint4 v = W[r * 4 + ((2 * kk + g) ^ wswz(r))];
-          wq[i] = v8i{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
-        } else {
-          const uint4 lo = W[r * 8 + ((4 * kk + g) ^ wswz(r))];
-          const uint4 hi = W[r * 8 + ((4 * kk + 2 + g) ^ wswz(r))];
-          wq[i] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-        }
+        const uint4 lo = W[r * 4 + (g ^ ((r >> 2) & 3))];
+        const uint4 hi = W[r * 4 + ((2 + g) ^ ((r >> 2) & 3))];
+        wf[set][i] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        cp(i, q, d);
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int r = wm * 128 + j * 32 + rsel;
-        const uint4 lo = X[r * 8 + ((4 * kk + g) ^ ((r >> 1) & 7))];
-        const uint4 hi = X[r * 8 + ((4 * kk + 2 + g) ^ ((r >> 1) & 7))];
-        xq[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        const uint4 lo = X[r * 4 + (g ^ ((r >> 2) & 3))];
+        const uint4 hi = X[r * 4 + ((2 + g) ^ ((r >> 2) & 3))];
+        xf[set][j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        cp(4 + j, q, d);
+      }
+      if (BS && set == 1) {   // this body issues an even stage
+        cp(8, q, d);
+        cp(9, q, d);
       }
     };
-    rd(0, wf[0], xf[0]);
-    gload(kt + 1 < ktiles ? kt + 1 : kt);
-    rd(1, wf[1], xf[1]);
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const int sh = 8 * (2 * kk + g);
+    // MFMAs of the stage with parity sp (its scale byte is 2 (sp) + g of the word)
+    auto mm = [&](int set, int sp, const uint32_t (&ws)[4], const uint32_t (&xs)[4]) {
+      const int sh = 8 * (2 * sp + g);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-              wf[kk][i], xf[kk][j], acc[i][j], a_fmt<WF>(), 0, 0, (int)((wsr[i] >> sh) & 0xFF), 0,
-              (int)((xsr[j] >> sh) & 0xFF));
-      if (kk == 1) sstore(s ^ 1);
-    }
-    // issue order (0x008 MFMA, 0x100 LDS read, 0x200 LDS write, 0x020 global load):
-    // the scale reads (paired into 4) and step 0's NRD fragment reads first, then
-    // step 0's 16 MFMAs with step 1's NRD fragment reads and the NGL global loads
-    // between them, then step 1's 16 MFMAs with the NST LDS stores (the two scale
-    // words go out as one paired store). MXFP4: NRD 12, NGL 14, NST 13; MXFP8: 16,
-    // 18, 17; FP8 (no block scales): 16, 16, 16.
-    constexpr int SC = BS ? 1 : 0;
-    constexpr int NRD = 8 + 4 * (WCH / 4), NGL = 8 + WLD + 2 * SC, NST = 8 + WLD + SC;
-    __builtin_amdgcn_sched_group_barrier(0x100, 4 * SC + NRD, 0);
-    for (int r = 0; r < NRD; ++r) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-    }
-    if (16 - NRD > 0) __builtin_amdgcn_sched_group_barrier(0x008, 16 - NRD, 0);
-    if (NGL - NRD > 0) __builtin_amdgcn_sched_group_barrier(0x020, NGL - NRD, 0);
-    constexpr int NPAIR = NST < 16 ? NST : 16;
-    for (int r = 0; r < NPAIR; ++r) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
-    }
-    if (16 - NPAIR > 0) __builtin_amdgcn_sched_group_barrier(0x008, 16 - NPAIR, 0);
-    if (NST - NPAIR > 0) __builtin_amdgcn_sched_group_barrier(0x200, NST - NPAIR, 0);
+              wf[set][i], xf[set][j], acc[i][j], a_fmt<WF>(), 0, 0, (int)((ws[i] >> sh) & 0xFF), 0,
+              (int)((xs[j] >> sh) & 0xFF));
+    };
+    // P: the stage's parity as a constant (stages come in pairs: K is a multiple of
+    // 128), which picks the fragment registers and the scale byte
+    auto body = [&](int st, bool first, auto pc) {
+      constexpr int P = decltype(pc)::value;
+      const int slot = st & (MX8_SLOTS - 1);
+      const int q = st + MX8_SLOTS - 1 < nsub ? st + MX8_SLOTS - 1 : nsub - 1;
+      const uint32_t d = (uint32_t)((st + MX8_SLOTS - 1) & (MX8_SLOTS - 1)) * SLOT_B;
+      rd_issue(slot, P, q, d);
+      if (!first) mm(P ^ 1, P ^ 1, wsp, xsp);   // the previous stage
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        wsp[i] = wsr[i];
+        xsp[i] = xsr[i];
+      }
+      // issue order (0x008 MFMA, 0x100 LDS read): the stage's (8 +) 16 reads between
+      // the previous stage's 16 MFMAs
+      constexpr int NR = 16 + (BS && P == 0 ? 8 : 0);
+      if (first) {
+        __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
+      } else {
+        for (int r = 0; r < 16; ++r) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          if (BS && P == 0 && (r & 1) == 0) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // copies complete in issue order: the two younger stages' may still be in flight
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NWAIT) : "memory");
+      __syncthreads();
+    };
+    static_assert((MX8_SLOTS & (MX8_SLOTS - 1)) == 0, "slot index is taken with a mask");
+    static_assert(MX8_SLOTS == 4, "the prologue and the wait count assume four slots");
+#pragma unroll
+    for (int q = 0; q < MX8_SLOTS - 1; ++q)   // stages 0 (+words), 1, 2 (+words)
+#pragma unroll
+      for (int c = 0; c < ((BS && (q & 1) == 0) ? 10 : 8); ++c)
+        cp(c, q < nsub ? q : nsub - 1, (uint32_t)q * SLOT_B);
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NWAIT) : "memory");
     __syncthreads();
-  }
+    using P0 = std::integral_constant<int, 0>;
+    using P1 = std::integral_constant<int, 1>;
+    body(0, true, P0{});
+    body(1, false, P1{});
+    for (int st = 2; st < nsub; st += 2) {
+      body(st, false, P0{});
+      body(st + 1, false, P1{});
+    }
+    mm(1, 1, wsp, xsp);   // the last stage (odd)
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
 
   const int hi4 = (lane >> 5) * 4;
