@@ -23,12 +23,14 @@
 // lane (row + 32*kb); D uses the usual 32x32 layout. An e4m3 operand in the A slot
 // (cbsz=0, MXFP8 weights) packs its bytes exactly as in the B slot.
 //
-// Tile: 256 weight rows x 256 activation rows x 128 contraction per stage, 4 waves
-// of 128 x 128 (4 x 4 accumulators), weights as the A operand so a lane holds 4
-// consecutive output columns. LDS per stage: activation codes [256][8 x 16 B],
-// weight codes [256][4 x 16 B] (MXFP4) or [256][8 x 16 B] (MXFP8), and both
-// operands' 4 scale bytes per row; two stages (100 KB / 132 KB). Tiles are dealt
-// out as in the bf16 kernels (device-counted, XCD-balanced, expert-major).
+// Tile: 256 weight rows x 256 activation rows, 4 waves of 128 x 128 (4 x 4
+// accumulators), weights as the A operand so a lane holds 4 consecutive output
+// columns. Operands are copied straight from global memory into LDS, several stages
+// ahead. MXFP4: 128-deep stages of activation codes [256][8 x 16 B], weight codes
+// [256][4 x 16 B] and both operands' 4 scale bytes per row (50 KB), three slots.
+// MXFP8 / FP8: 64-deep stages of activation and weight codes [256][4 x 16 B] each
+// (plus the scale words for MXFP8), four slots. Tiles are dealt out as in the bf16
+// kernels (device-counted, XCD-balanced, expert-major).
 #include <type_traits>
 
 #include "common.h"
@@ -141,8 +143,8 @@ __global__ __launch_bounds__(MNT, 1) void k_gemm_mx(MxArgs a) {
   const int K = a.K, ks = K >> 5;   // bytes per scale row
   const bool fc1 = EPI != MX_FC2;
 
-  // global -> register staging: activation codes rows (tid>>3)+32j, chunk tid&7;
-  // weight codes rows tid/WCH + (256/WCH)j, chunk tid%WCH; scales: row tid of each
+  // per-thread source rows: activation codes rows (tid>>3)+32j, weight codes rows
+  // tid/WCH + (256/WCH)j (the MXFP4 copies use these rows), scales: row tid of each
   // operand
   const int xr = tid >> 3, xc = tid & 7, wr = tid / WCH, wc = tid % WCH;
   const uint32_t kw = (uint32_t)K * WB / 8;   // weight bytes per row
