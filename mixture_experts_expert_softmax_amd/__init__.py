@@ -168,9 +168,12 @@ def moe_route(logits: torch.Tensor, top_k: int, topk_ids=None, topk_weights=None
 
 
 def moe_sort(topk_ids: torch.Tensor, num_experts: int, num_local_experts: Optional[int] = None,
-             local_expert_offset: int = 0, workspace: Optional[torch.Tensor] = None):
+             local_expert_offset: int = 0, workspace: Optional[torch.Tensor] = None,
+             out: Optional[dict] = None):
     """Stable counting sort by local expert. Returns a dict of device tensors:
-    offs [L], m_indptr [L+1], e2p [T*k], p2e [T*k] (valid below n_local), n_local [1]."""
+    offs [L], m_indptr [L+1], e2p [T*k], p2e [T*k] (valid below n_local), n_local [1].
+    ``out`` may hold preallocated int32 tensors under those names (as returned by an
+    earlier call with the same shape); they are written in place."""
     _dev(topk_ids, torch.int32, "topk_ids")
     T, k = topk_ids.shape
     L = num_experts if num_local_experts is None else num_local_experts
@@ -179,11 +182,16 @@ def moe_sort(topk_ids: torch.Tensor, num_experts: int, num_local_experts: Option
     ws_bytes = h.moe_sort_workspace_size(T, k, L)
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
-    out = dict(offs=torch.empty(L, dtype=torch.int32, device=dev),
-               m_indptr=torch.empty(L + 1, dtype=torch.int32, device=dev),
-               e2p=torch.empty(max(T * k, 1), dtype=torch.int32, device=dev),
-               p2e=torch.empty(max(T * k, 1), dtype=torch.int32, device=dev),
-               n_local=torch.empty(1, dtype=torch.int32, device=dev))
+    need = dict(offs=L, m_indptr=L + 1, e2p=T * k, p2e=T * k, n_local=1)   # elements written
+    if out is None:
+        out = {n: torch.empty(max(sz, 1), dtype=torch.int32, device=dev) for n, sz in need.items()}
+    else:
+        for n, sz in need.items():
+            t = out[n]
+            if t.numel() < sz or t.dtype != torch.int32 or t.device != dev or not t.is_contiguous():
+                raise ValueError(f"moe_sort: out[{n!r}] must be a contiguous int32 tensor of at "
+                                 f"least {sz} elements on {dev}")
+        out = dict(out)
     _check("moe_sort", h.moe_sort(_ptr(topk_ids), T, k, num_experts, L, local_expert_offset,
                                   _ptr(out["offs"]), _ptr(out["m_indptr"]), _ptr(out["e2p"]),
                                   _ptr(out["p2e"]), _ptr(out["n_local"]), _ptr(workspace),

@@ -93,3 +93,23 @@ def test_sort_all_routes_on_one_expert():
     ref = O.sort_routes(ids.cpu().numpy(), 8, 8, 0)
     np.testing.assert_array_equal(r["offs"].cpu().numpy(), ref["offs"])
     np.testing.assert_array_equal(r["p2e"][:10000].cpu().numpy(), np.arange(10000))
+
+
+def test_sort_into_preallocated_outputs():
+    """Outputs passed back in are overwritten completely: a second sort of different ids
+    into the first call's tensors matches a fresh sort of those ids."""
+    g = np.random.default_rng(5)
+    a = torch.from_numpy(g.integers(0, 64, size=(3000, 8)).astype(np.int32)).to(DEV)
+    b = torch.from_numpy(g.integers(0, 64, size=(3000, 8)).astype(np.int32)).to(DEV)
+    r1 = M.moe_sort(a, 64, 16, 8)
+    r2 = M.moe_sort(b, 64, 16, 8, out=r1)
+    assert r2["e2p"].data_ptr() == r1["e2p"].data_ptr()
+    ref = O.sort_routes(b.cpu().numpy(), 64, 16, 8)
+    n = int(r2["n_local"].item())
+    assert n == ref["n_local"]
+    np.testing.assert_array_equal(r2["offs"].cpu().numpy(), ref["offs"])
+    np.testing.assert_array_equal(r2["m_indptr"].cpu().numpy(), ref["m_indptr"])
+    np.testing.assert_array_equal(r2["e2p"].cpu().numpy(), ref["e2p"])
+    np.testing.assert_array_equal(r2["p2e"][:n].cpu().numpy(), ref["p2e"])
+    with pytest.raises(ValueError):
+        M.moe_sort(b, 64, 16, 8, out=dict(r1, e2p=r1["e2p"][:10]))
