@@ -221,10 +221,10 @@ __device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
   asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(lds) : "memory");
 }
 
-// Main loop for a contraction that is a whole number of 64-wide stages, as a
-// pipeline of DMA_SLOTS 32-deep stages fetched straight into LDS without passing
-// through registers (32 KB a stage: the 256 activation rows, then the 256 weight
-// rows, 64 bytes each). Stage s + DMA_SLOTS - 1 is requested while stage s is
+// The full-K main loop (mainloop_dma_g below, for the forward and both backward
+// products) is a pipeline of DMA_SLOTS 32-deep stages fetched straight into LDS
+// without passing through registers (32 KB a stage: the 256 activation rows, then
+// the 256 weight rows, 64 bytes each in the row-major layout). Stage s + DMA_SLOTS - 1 is requested while stage s is
 // consumed, so a copy has three stages of MFMA work to land, and each copy is issued
 // right after one fragment read so the copies go out spread over the stage's MFMAs
 // (issued back to back, they stall the wave on the address unit ahead of its
@@ -238,85 +238,6 @@ constexpr int DMA_SLOTS = 4;
 constexpr int DMA_STAGE_U4 = 2 * TB * 32 * 2 / 16;   // uint4 slots per 32-deep stage
 static_assert(DMA_SLOTS * DMA_STAGE_U4 <= 4 * TILE_U4, "stages exceed the kernel's LDS");
 
-__device__ __forceinline__ void mainloop_dma(const uint16_t* abase, const uint32_t (&aoff)[4],
-                                             const uint16_t* bbase, const uint32_t (&boff)[4],
-                                             uint4* smem, int kbase, int nsub, int tid, int lane,
-                                             int wn, int wm, f32x16 (&acc)[4][4]) {
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int gch = (lane & 3) ^ ((lane >> 4) & 3);
-  const uint32_t lds0 = (uint32_t)(uintptr_t)smem + (uint32_t)w * 1024u;
-  const int rsel = lane & 31, kg = lane >> 5, sw = (rsel >> 2) & 3;
-  constexpr uint32_t STAGE_B = DMA_STAGE_U4 * 16, HALF_B = STAGE_B / 2;
-  // all 8 copies of stage `sub` into `slot` (the pipeline fill)
-  auto issue = [&](int sub, int slot) {
-    const int k = kbase + sub * 32 + gch * 8;
-    const uint32_t d = lds0 + (uint32_t)slot * STAGE_B;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      dma16(abase + aoff[j] + k, d + j * 4096u);
-      dma16(bbase + boff[j] + k, d + HALF_B + j * 4096u);
-    }
-  };
-  bf16x8 wf[2][4], xf[2][4];
-  // fragment reads of step kk (of 2) of the stage in `slot`; after every second read
-  // one copy of half h of stage `sub` into slot `dslot`
-  auto rd_issue = [&](int slot, int kk, int set, int sub, int dslot, int h) {
-    const uint4* Xs = smem + slot * DMA_STAGE_U4;
-    const uint4* Ws = Xs + DMA_STAGE_U4 / 2;
-    const int c = ((kk << 1) + kg) ^ sw;
-    const int k = kbase + sub * 32 + gch * 8;
-    const uint32_t d = lds0 + (uint32_t)dslot * STAGE_B + (uint32_t)h * HALF_B;
-    const uint16_t* base = h ? bbase : abase;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      wf[set][i] = as_bf16x8(Ws[(wn * 128 + i * 32 + rsel) * 4 + c]);
-      if (i & 1) dma16(base + (h ? boff[i >> 1] : aoff[i >> 1]) + k, d + (i >> 1) * 4096u);
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      xf[set][j] = as_bf16x8(Xs[(wm * 128 + j * 32 + rsel) * 4 + c]);
-      if (j & 1) dma16(base + (h ? boff[2 + (j >> 1)] : aoff[2 + (j >> 1)]) + k, d + (2 + (j >> 1)) * 4096u);
-    }
-  };
-  auto mm = [&](int set) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[set][i], xf[set][j], acc[i][j], 0, 0, 0);
-  };
-  auto body = [&](int sub, bool first) {
-    const int slot = sub & (DMA_SLOTS - 1);
-    const int nxt = sub + DMA_SLOTS - 1 < nsub ? sub + DMA_SLOTS - 1 : nsub - 1;
-    const int dslot = (sub + DMA_SLOTS - 1) & (DMA_SLOTS - 1);
-    rd_issue(slot, 0, 0, nxt, dslot, 0);
-    if (!first) mm(1);   // the previous stage's last step
-    rd_issue(slot, 1, 1, nxt, dslot, 1);
-    mm(0);
-    // issue order (mask 0x008 MFMA, 0x100 LDS read): each read between two MFMAs
-    if (first) __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
-    for (int q = 0; q < (first ? 1 : 2); ++q)
-      for (int r = 0; r < 8; ++r) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      }
-    __builtin_amdgcn_sched_barrier(0);
-    // copies complete in issue order: at most the 8 of each of the two younger
-    // stages still in flight means stage sub + 1 has landed
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(8 * (DMA_SLOTS - 2)) : "memory");
-    __syncthreads();
-  };
-  static_assert((DMA_SLOTS & (DMA_SLOTS - 1)) == 0, "slot index is taken with a mask");
-#pragma unroll
-  for (int q = 0; q < DMA_SLOTS - 1; ++q) issue(q < nsub ? q : nsub - 1, q);
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(8 * (DMA_SLOTS - 2)) : "memory");
-  __syncthreads();
-  body(0, true);
-  for (int sub = 1; sub < nsub; ++sub) body(sub, false);
-  mm(1);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // LDS is reused after the loop
-}
 
 // Copy of one 16-byte chunk per lane through a buffer resource: lands at LDS byte
 // address lds + 16 * lane; offsets at or past the resource's record count read as
@@ -412,15 +333,28 @@ __device__ __forceinline__ void mainloop_dma_g(const SA& sa, const SB& sb, uint4
         rd_a(As, kk, set, i);
         dma16_buf(r, src.voff[i], d + i * 4096u);
       }
-    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) rd_b(Bs, kk, set, j);
+    } else if constexpr (A_K || B_K) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         rd_a(As, kk, set, i);
         copy_rm(src, sub, d, i);
       }
-    }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) rd_b(Bs, kk, set, j);
+      for (int j = 0; j < 4; ++j) rd_b(Bs, kk, set, j);
+    } else {   // both row-major (the forward): a copy after every second read
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        rd_a(As, kk, set, i);
+        if (i & 1) copy_rm(src, sub, d, i >> 1);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        rd_b(Bs, kk, set, j);
+        if (j & 1) copy_rm(src, sub, d, 2 + (j >> 1));
+      }
+    }
   };
   auto mm = [&](int set) {
 #pragma unroll
@@ -460,11 +394,20 @@ __device__ __forceinline__ void mainloop_dma_g(const SA& sa, const SB& sb, uint4
     // between the previous step's 16 MFMAs
     constexpr int NR = (A_K ? 8 : 4) + (B_K ? 8 : 4);
     if (first) __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
-    for (int q = 0; q < (first ? 1 : 2); ++q)
-      for (int r = 0; r < 16; ++r) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        if (r < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    for (int q = 0; q < (first ? 1 : 2); ++q) {
+      if constexpr (!A_K && !B_K) {   // 8 reads: one between each pair of MFMAs
+        for (int r = 0; r < 8; ++r) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        }
+      } else {
+        for (int r = 0; r < 16; ++r) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          if (r < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
       }
+    }
     __builtin_amdgcn_sched_barrier(0);
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(8 * (DMA_SLOTS - 2)) : "memory");
     __syncthreads();
@@ -548,7 +491,17 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_nt(NtArgs a) {
       }
       boff[j] = (uint32_t)wrow * (uint32_t)a.K;
     }
-    mainloop_dma(a.A, aoff, lb.base, boff, smem, k0 * TK, nk * 2, tid, lane, wn, wm, acc);
+    RmSrc sw, sx;   // weight side, activation side
+    sw.base = lb.base;
+    sx.base = a.A;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      sw.off[j] = boff[j];
+      sx.off[j] = aoff[j];
+    }
+    sw.init(tid);
+    sx.init(tid);
+    mainloop_dma_g<false, false>(sw, sx, smem, k0 * TK, nk * 2, tid, lane, wn, wm, acc);
     if (S > 1) {
       // a part of a split tile: publish the fp32 partial; the last of the S parts
       // to arrive sums all of them in part order (the same result whichever part
