@@ -50,7 +50,9 @@ SORT_CASES = [
     (32, 2, 8, 8, 0), (4096, 2, 8, 8, 0), (8192, 8, 256, 32, 64), (8192, 8, 64, 64, 0),
     (1, 8, 64, 64, 0), (1, 1, 4, 4, 0), (1000, 3, 10, 3, 7), (65536, 8, 256, 256, 0),
     (3000, 16, 1024, 1000, 24),
-    # one-workgroup path at its limits (n = 64000 with 900 experts) and just past it
+    # one-workgroup path at its limit (n = 16384) and just past it (chunked path)
+    (1024, 16, 900, 900, 0), (2049, 8, 64, 64, 0), (4096, 4, 256, 128, 64),
+    # chunked path with many experts and a partial last chunk
     (4000, 16, 900, 900, 0), (8193, 8, 64, 64, 0),
 ]
 
