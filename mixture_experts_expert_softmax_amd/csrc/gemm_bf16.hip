@@ -19,9 +19,14 @@
 //  * The MFMA "A" operand is the weight side and "B" the activation side, so a
 //    lane's accumulator holds 4 consecutive output columns of one output row:
 //    epilogue stores are 8-byte (bf16) or 16-byte (fp32) runs.
-//  * Both operand tiles are staged in LDS as [256 rows][8 chunks of 16 B] with
-//    the chunk index XOR-swizzled by (row >> 1) & 7, double buffered (128 KB total);
-//    the next tile's global loads are issued before the current tile's MFMAs.
+//  * Whole 64-deep contractions (every case but a ragged fwd K): operands are
+//    copied straight from global memory into LDS (global_load_lds_dwordx4, or a
+//    buffer copy whose record count zero-fills past a ragged group or a matrix
+//    edge) in four slots of 32-deep stages, three stages ahead; row-major tiles
+//    are [256 rows][4 chunks of 16 B] swizzled by (row >> 2) & 3, K-major tiles
+//    [32 contraction rows][32 chunks] swizzled by (row & 3) << 2 and read with
+//    transposing ds_read_b64_tr_b16. Otherwise the tiles are staged through
+//    registers as [256 rows][8 chunks] swizzled by (row >> 1) & 7, double buffered.
 //  * Ragged groups: an upper bound of M tiles is launched (no host sync); each
 //    workgroup decodes its (expert, row block) from the device offsets, clamps
 //    row reads inside its group and masks stores. Rows of a partial contraction
