@@ -298,7 +298,11 @@ struct KmSrc {              // K-major operand: contraction row 0, first output 
 // copies three stages ahead interleaved with fragment reads, rotated by one step)
 // for operands in either layout. A = weight side (output columns), B = activation
 // side (output rows); kbase is the row-major operand's first contraction element.
-template <bool A_K, bool B_K, class SA, class SB>
+// JN = 32-row activation blocks per wave: 4 for the whole 256-row tile; 1 (row-major
+// activation side only) for a tile of at most 64 rows, where row-wave wm takes rows
+// 32 wm .. 32 wm + 31, each wave issues only its first activation copy (rows 0..63)
+// and a step has 4 MFMAs instead of 16 -- the ragged last tile of a group.
+template <bool A_K, bool B_K, int JN, class SA, class SB>
 __device__ __forceinline__ void mainloop_dma_g(const SA& sa, const SB& sb, uint4* smem, int kbase,
                                                int nsub, int tid, int lane, int wn, int wm,
                                                f32x16 (&acc)[4][4]) {
@@ -306,6 +310,7 @@ __device__ __forceinline__ void mainloop_dma_g(const SA& sa, const SB& sb, uint4
   const uint32_t lds0 = (uint32_t)(uintptr_t)smem + (uint32_t)w * 1024u;
   const int rsel = lane & 31, kg = lane >> 5, sw = (rsel >> 2) & 3;
   constexpr uint32_t STAGE_B = DMA_STAGE_U4 * 16, HALF_B = STAGE_B / 2;
+  constexpr int NCOPY = 4 + (B_K ? 4 : JN);   // copies per wave per stage
   // the 4 copies of one operand's part of stage `sub` into LDS half at byte d
   auto copy_rm = [&](const RmSrc& src, int sub, uint32_t d, int j) {
     dma16(src.base + src.off[j] + kbase + sub * 32 + src.gch * 8, d + j * 4096u);
@@ -318,7 +323,7 @@ __device__ __forceinline__ void mainloop_dma_g(const SA& sa, const SB& sb, uint4
   };
   auto rd_b = [&](const uint4* Bs, int kk, int set, int j) {
     if constexpr (B_K) xf[set][j] = ktile_frag(Bs, kk, wm * 128 + j * 32, lane);
-    else xf[set][j] = as_bf16x8(Bs[(wm * 128 + j * 32 + rsel) * 4 + (((kk << 1) + kg) ^ sw)]);
+    else xf[set][j] = as_bf16x8(Bs[(wm * JN * 32 + j * 32 + rsel) * 4 + (((kk << 1) + kg) ^ sw)]);
   };
   // fragment reads of step kk of the stage in `slot`, each of the first four
   // followed by one copy of operand H (0: B, 1: A) of stage `sub` into slot `dslot`
@@ -349,15 +354,16 @@ __device__ __forceinline__ void mainloop_dma_g(const SA& sa, const SB& sb, uint4
 #pragma unroll
       for (int j = 0; j < 4; ++j) rd_b(Bs, kk, set, j);
     } else {   // both row-major (the forward): a copy after every second read
+      constexpr int NC = H == 0 ? JN : 4;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         rd_a(As, kk, set, i);
-        if (i & 1) copy_rm(src, sub, d, i >> 1);
+        if ((i & 1) && (i >> 1) < NC) copy_rm(src, sub, d, i >> 1);
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        rd_b(Bs, kk, set, j);
-        if (j & 1) copy_rm(src, sub, d, 2 + (j >> 1));
+        if (j < JN) rd_b(Bs, kk, set, j);
+        if ((j & 1) && 2 + (j >> 1) < NC) copy_rm(src, sub, d, 2 + (j >> 1));
       }
     }
   };
@@ -365,7 +371,7 @@ __device__ __forceinline__ void mainloop_dma_g(const SA& sa, const SB& sb, uint4
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < JN; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[set][i], xf[set][j], acc[i][j], 0, 0, 0);
   };
   auto issue = [&](int sub, int slot) {
@@ -376,7 +382,7 @@ __device__ __forceinline__ void mainloop_dma_g(const SA& sa, const SB& sb, uint4
       for (int j = 0; j < 4; ++j) dma16_buf(r, sb.voff[j], d + j * 4096u);
     } else {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) copy_rm(sb, sub, d, j);
+      for (int j = 0; j < JN; ++j) copy_rm(sb, sub, d, j);
     }
     if constexpr (A_K) {
       const __amdgpu_buffer_rsrc_t r = sa.stage(sub);
@@ -397,29 +403,30 @@ __device__ __forceinline__ void mainloop_dma_g(const SA& sa, const SB& sb, uint4
     mm(0);
     // a step's NR fragment reads (two transposing reads per K-major fragment) go
     // between the previous step's 16 MFMAs
-    constexpr int NR = (A_K ? 8 : 4) + (B_K ? 8 : 4);
+    constexpr int NR = (A_K ? 8 : 4) + (B_K ? 8 : JN);
+    constexpr int NM = 4 * JN;
     if (first) __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
     for (int q = 0; q < (first ? 1 : 2); ++q) {
-      if constexpr (!A_K && !B_K) {   // 8 reads: one between each pair of MFMAs
+      if constexpr (!A_K && !B_K && JN == 4) {   // 8 reads: one between each pair of MFMAs
         for (int r = 0; r < 8; ++r) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
           __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         }
       } else {
-        for (int r = 0; r < 16; ++r) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        for (int r = 0; r < (NM > NR ? NM : NR); ++r) {
+          if (r < NM) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
           if (r < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
       }
     }
     __builtin_amdgcn_sched_barrier(0);
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(8 * (DMA_SLOTS - 2)) : "memory");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NCOPY * (DMA_SLOTS - 2)) : "memory");
     __syncthreads();
   };
 #pragma unroll
   for (int q = 0; q < DMA_SLOTS - 1; ++q) issue(q < nsub ? q : nsub - 1, q);
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(8 * (DMA_SLOTS - 2)) : "memory");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NCOPY * (DMA_SLOTS - 2)) : "memory");
   __syncthreads();
   body(0, true);
   for (int sub = 1; sub < nsub; ++sub) body(sub, false);
@@ -474,6 +481,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_nt(NtArgs a) {
 
   f32x16 acc[4][4];
   zero_acc(acc);
+  int jn = 4;   // 32-row blocks per wave
 
   if (KFULL) {
     // rows (tid / 4) + 64 j of both operands, in the order the copies fill a stage
@@ -506,7 +514,12 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_nt(NtArgs a) {
     }
     sw.init(tid);
     sx.init(tid);
-    mainloop_dma_g<false, false>(sw, sx, smem, k0 * TK, nk * 2, tid, lane, wn, wm, acc);
+    if (mend - m0 <= 64) {   // a short last tile of its group: a quarter of the work
+      jn = 1;
+      mainloop_dma_g<false, false, 1>(sw, sx, smem, k0 * TK, nk * 2, tid, lane, wn, wm, acc);
+    } else {
+      mainloop_dma_g<false, false, 4>(sw, sx, smem, k0 * TK, nk * 2, tid, lane, wn, wm, acc);
+    }
     if (S > 1) {
       // a part of a split tile: publish the fp32 partial; the last of the S parts
       // to arrive sums all of them in part order (the same result whichever part
@@ -576,15 +589,16 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_nt(NtArgs a) {
     }
   }
 
-  // ---- epilogue: lane holds rows m, 4 consecutive columns per (i, q)
+  // ---- epilogue: lane holds rows m, 4 consecutive columns per (i, q); row block j
+  // of wave row wm starts at row 32 (wm jn + j) of the tile
   const int hi4 = (lane >> 5) * 4;
   if (EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_STEP) {
     float lim = 0.f;
     if (EPI == EPI_SWIGLU_STEP) lim = a.limits ? a.limits[e] : a.def_limit;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int p = m0 + wm * 128 + j * 32 + (lane & 31);
-      if (p >= mend) continue;
+      const int p = m0 + wm * jn * 32 + j * 32 + (lane & 31);
+      if (j >= jn || p >= mend) continue;
       uint16_t* crow = a.C + (int64_t)p * a.ldc;
 #pragma unroll
       for (int i = 0; i < 2; ++i)
@@ -618,8 +632,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_nt(NtArgs a) {
   } else if (EPI == EPI_FUSED) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int p = m0 + wm * 128 + j * 32 + (lane & 31);
-      if (p >= mend) continue;
+      const int p = m0 + wm * jn * 32 + j * 32 + (lane & 31);
+      if (j >= jn || p >= mend) continue;
       const int route = a.p2e[p];
       const float wgt = a.route_w[route];
       uint16_t* crow = a.C + (int64_t)(route / a.top_k) * a.ldc;
@@ -636,8 +650,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_nt(NtArgs a) {
   } else {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int p = m0 + wm * 128 + j * 32 + (lane & 31);
-      if (p >= mend) continue;
+      const int p = m0 + wm * jn * 32 + j * 32 + (lane & 31);
+      if (j >= jn || p >= mend) continue;
       uint16_t* crow = a.C + (int64_t)p * a.ldc;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
@@ -695,7 +709,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_dgrad(DgradArgs a) {
     sg.off[j] = (uint32_t)p * (uint32_t)a.N;
   }
   sg.init(tid);
-  mainloop_dma_g<true, false>(sw, sg, smem, 0, a.N / 32, tid, lane, wn, wm, acc);
+  mainloop_dma_g<true, false, 4>(sw, sg, smem, 0, a.N / 32, tid, lane, wn, wm, acc);
   const int hi4 = (lane >> 5) * 4;
   float lim = 0.f;
   if (ACT == 2) lim = a.limits ? a.limits[e] : a.def_limit;
@@ -796,7 +810,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_wgrad(WgradArgs a) {
   f32x16 acc[4][4];
   zero_acc(acc);
   const int nsub = (rows + 31) / 32;
-  if (nsub > 0) mainloop_dma_g<true, true>(sx, sgd, smem, 0, nsub, tid, lane, wn, wm, acc);
+  if (nsub > 0) mainloop_dma_g<true, true, 4>(sx, sgd, smem, 0, nsub, tid, lane, wn, wm, acc);
   const int hi4 = (lane >> 5) * 4;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {

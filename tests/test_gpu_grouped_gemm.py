@@ -189,3 +189,26 @@ def test_grouped_gemm_empty_rows():
     dw = torch.full((3, 64, 32), 7.0, device=DEV)
     M.grouped_gemm_wgrad(g, x, offs, out=dw)
     assert torch.all(dw == 0)
+
+
+def test_fc2_short_tiles_cut_along_k_integer_exact():
+    """32 groups of 256 rows and a last group of 40 rows at N = 2048: 264 tiles of
+    256 x 256, so on a 256-CU device the last round is the last group's 8 short tiles,
+    each cut along K into parts whose fp32 partials the last part sums. A tile of at
+    most 64 rows runs a quarter of the MFMAs (32 rows per wave); on integer-valued
+    operands the result is exact, with or without the cut."""
+    sizes = np.array([256] * 32 + [40])
+    K, N = 1024, 2048
+    c = S.grouped_gemm_case(seed=21, sizes=sizes, K=K, N=N, integer_valued=True)
+    act, w2 = c.x.to(DEV), c.w.to(DEV)
+    offs = torch.from_numpy(c.offs).to(DEV)
+    M_ = int(sizes.sum())
+    y_cut = M.moe_fc2(act, w2, offs, M_, 1, len(sizes))
+    y_whole = M.moe_fc2(act, w2, offs, M_, 1, len(sizes), split=False)
+    torch.cuda.synchronize()
+    assert torch.equal(y_cut, y_whole)
+    got = to_np(y_cut)
+    x64, w64 = _f(c.x), _f(c.w)
+    last = slice(M_ - 40, M_)
+    np.testing.assert_array_equal(got[last], bf16_round(O.grouped_gemm_fwd(x64[last], w64[-1:], [40])))
+    np.testing.assert_array_equal(got[:256], bf16_round(O.grouped_gemm_fwd(x64[:256], w64[:1], [256])))
