@@ -78,12 +78,6 @@ struct NtArgs {
   int n_res;                 // workgroups resident at once (0: never split)
 };
 
-__device__ __forceinline__ int xcd_remap(int b, int nblocks) {
-  // hardware places consecutive workgroups on consecutive XCDs (8 of them)
-  const int per = nblocks >> 3;
-  return (b & 7) * per + (b >> 3);
-}
-
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 
 // Tile (and contraction range) of this workgroup in the NT kernel. With n_res
@@ -771,7 +765,13 @@ struct WgradArgs {
 template <bool OUT_F32>
 __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_wgrad(WgradArgs a) {
   __shared__ uint4 smem[4 * TILE_U4];
-  const int t = xcd_remap(blockIdx.x, gridDim.x);
+  // A tile's cost is its group's row count. Chunks of k_tiles tiles (one row of
+  // output tiles, sharing one G slice) go round-robin over the 8 XCDs, so every XCD
+  // works through its share of each group at the same time: contiguous ranges would
+  // hand whole groups to single XCDs, and the XCDs with small groups would idle
+  // while the one with the largest group still takes new workgroups.
+  const int x = (int)(blockIdx.x & 7), s = (int)(blockIdx.x >> 3);
+  const int t = ((s / a.k_tiles) * 8 + x) * a.k_tiles + s % a.k_tiles;
   const int per_e = a.n_tiles * a.k_tiles;
   const int e = t / per_e;
   if (e >= a.E) return;
@@ -941,7 +941,8 @@ moe_status gemm_wgrad_enqueue(const void* G, const void* X, const int32_t* ends,
                               int N, int K, void* DW, bool out_f32, hipStream_t st) {
   WgradArgs a{reinterpret_cast<const uint16_t*>(G), reinterpret_cast<const uint16_t*>(X), ends, E,
               (int)M, N, K, (N + TB - 1) / TB, (K + TB - 1) / TB, DW};
-  const int grid = round_up8((int64_t)E * a.n_tiles * a.k_tiles);
+  // every XCD holds ceil(chunks / 8) chunks of k_tiles tiles; the excess exits
+  const int grid = 8 * ((E * a.n_tiles + 7) / 8) * a.k_tiles;
   if (out_f32)
     k_gemm_wgrad<true><<<grid, NTHREADS, 0, st>>>(a);
   else
