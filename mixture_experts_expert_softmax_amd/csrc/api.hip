@@ -22,7 +22,8 @@ moe_status gemm_nt_enqueue(int epi, const void* A, const int32_t* a_gather, int 
 moe_status gemm_dgrad_enqueue(const void* G, const void* W, const int32_t* ends, int E, int64_t M,
                               int N, int K, void* DX, hipStream_t st, int act = 0,
                               const void* h = nullptr, const float* limits = nullptr,
-                              float def_limit = 7.0f);
+                              float def_limit = 7.0f, void* split_ws = nullptr,
+                              int32_t* split_cnt = nullptr);
 moe_status gemm_wgrad_enqueue(const void* G, const void* X, const int32_t* ends, int E, int64_t M,
                               int N, int K, void* DW, bool out_f32, hipStream_t st);
 // defined in backward.hip
@@ -124,7 +125,7 @@ FfnLayout ffn_layout(const moe_ffn_desc* d, bool train = false) {
 // Backward workspace: dy [T*k, H] (later the gathered x rows), dh [T*k, 2I], dx rows
 // [T*k, H] (bf16, permuted order).
 struct BwdLayout {
-  size_t dy, dh, dxp, total;
+  size_t dy, dh, dxp, split, split_cnt, total;
 };
 
 BwdLayout bwd_layout(const moe_ffn_desc* d) {
@@ -134,6 +135,9 @@ BwdLayout bwd_layout(const moe_ffn_desc* d) {
   l.dy = o;  o += align_up((size_t)R * d->H * 2, 256);
   l.dh = o;  o += align_up((size_t)R * 2 * d->I * 2, 256);
   l.dxp = o; o += align_up((size_t)R * d->H * 2, 256);
+  // fp32 partial tiles and arrival counters of the dgrad tiles cut along N
+  l.split = o; o += (size_t)SPLIT_SLOTS * SPLIT_TILE_BYTES;
+  l.split_cnt = o; o += align_up((size_t)SPLIT_SLOTS * 4, 256);
   l.total = o;
   return l;
 }
@@ -379,19 +383,26 @@ extern "C" moe_status moe_ffn_backward(const moe_ffn_desc* d, const moe_ffn_tens
   void* dy = w + b.dy;
   void* dh = w + b.dh;
   void* dxp = w + b.dxp;
+  void* split_ws = w + b.split;
+  int32_t* split_cnt = reinterpret_cast<int32_t*>(w + b.split_cnt);
   const int64_t R = d->T * k;
+  // the counters start at zero; the last part of each split tile resets its own
+  s = zero_fill(split_cnt, (size_t)SPLIT_SLOTS * 4, st);
+  if (s != MOE_OK) return s;
   // out[t] = sum_s w y  ->  dy rows and the routing-weight gradients
   s = permute_bwd_enqueue(g->dout, e2p, t->topk_weights, y, d->T, k, H, dy, g->dtopk_weights, st);
   if (s != MOE_OK) return s;
   // y = act @ w2^T  ->  da = dy @ w2 (with dh = act'(h) da in the epilogue), dw2 = dy^T act
   const int actk = d->activation == MOE_ACT_SWIGLU_STEP ? 2 : 1;
-  s = gemm_dgrad_enqueue(dy, t->w2, offs, L, R, H, I, dh, st, actk, h, t->clamp_limit, 7.0f);
+  s = gemm_dgrad_enqueue(dy, t->w2, offs, L, R, H, I, dh, st, actk, h, t->clamp_limit, 7.0f,
+                         split_ws, split_cnt);
   if (s != MOE_OK) return s;
   s = gemm_wgrad_enqueue(dy, act, offs, L, R, H, I, g->dw2, f32, st);
   if (s != MOE_OK) return s;
   // h = x[p2e / k] @ w1^T  ->  dx rows = dh @ w1, dw1 = dh^T x[p2e / k]; the x rows are
   // gathered once into permuted order (into dy's buffer, free after dw2)
-  s = gemm_dgrad_enqueue(dh, t->w1, offs, L, R, 2 * I, H, dxp, st);
+  s = gemm_dgrad_enqueue(dh, t->w1, offs, L, R, 2 * I, H, dxp, st, 0, nullptr, nullptr, 7.0f,
+                         split_ws, split_cnt);
   if (s != MOE_OK) return s;
   s = gather_rows_enqueue(t->x, p2e, offs, L, k, H, R, dy, st);
   if (s != MOE_OK) return s;

@@ -80,27 +80,28 @@ struct NtArgs {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 
-// Tile (and contraction range) of this workgroup in the NT kernel. With n_res
-// resident workgroups, total tiles take total / n_res full rounds; when the
+// Tile (and contraction range, in units of ktiles) of this workgroup in the NT and
+// dgrad kernels. With n_res resident workgroups, total tiles take total / n_res full rounds; when the
 // remainder rem would leave most of the last round idle, each of those rem tiles
 // is cut along K into S = min(n_res / rem, SPLIT_MAX) parts instead, which run
 // side by side. The whole tiles are dealt as in deal_tile; part p of remainder
 // tile i is workgroup full + 8 * ((i / 8) * S + p) + i % 8, so all parts of a
 // tile share one XCD. slot = i * S + p indexes the partial-tile buffer, cidx = i
 // the arrival counter.
-__device__ __forceinline__ bool deal_tile_nt(const NtArgs& a, int ktiles, int& e, int& m0,
-                                             int& mend, int& nt, int& k0, int& nk, int& part,
-                                             int& S, int& slot, int& cidx) {
-  const int total = tile_count<TB>(a.ends, a.E, a.m_cap, a.n_tiles);
+__device__ __forceinline__ bool deal_tile_split(const int32_t* ends, int E, int m_cap, int n_tiles,
+                                                int n_res, int ktiles, int& e, int& m0, int& mend,
+                                                int& nt, int& k0, int& nk, int& part, int& S,
+                                                int& slot, int& cidx) {
+  const int total = tile_count<TB>(ends, E, m_cap, n_tiles);
   const int b = (int)blockIdx.x;
   int full = total, rem = 0;
   S = 1;
   part = 0;
-  if (a.n_res > 0) {
-    full = total / a.n_res * a.n_res;
+  if (n_res > 0) {
+    full = total / n_res * n_res;
     rem = total - full;
     if (rem > 0) {
-      S = a.n_res / rem;
+      S = n_res / rem;
       S = S < SPLIT_MAX ? S : SPLIT_MAX;
       S = S < ktiles ? S : ktiles;
     }
@@ -123,9 +124,61 @@ __device__ __forceinline__ bool deal_tile_nt(const NtArgs& a, int ktiles, int& e
     slot = i * S + part;
     cidx = i;
   }
-  tile_locate<TB>(a.ends, a.E, a.m_cap, a.n_tiles, t, e, m0, mend, nt);
+  tile_locate<TB>(ends, E, m_cap, n_tiles, t, e, m0, mend, nt);
   k0 = ktiles * part / S;
   nk = ktiles * (part + 1) / S - k0;
+  return true;
+}
+
+// Part `part` of S of a split tile publishes its fp32 partial into slot `slot` of
+// the split workspace; the last of the S parts to arrive (counter cidx) sums all of
+// them in part order -- the same result whichever part arrives last -- into acc and
+// returns true (it goes on to the epilogue); the others return false.
+__device__ __forceinline__ bool split_reduce(f32x16 (&acc)[4][4], float* split_ws, int32_t* split_cnt,
+                                             int slot, int part, int S, int cidx, uint4* smem,
+                                             int tid) {
+  constexpr int TILE_F4 = TB * TB / 4;
+  float4* mine = reinterpret_cast<float4*>(split_ws) + (size_t)slot * TILE_F4;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        mine[((i * 4 + j) * 4 + q) * NTHREADS + tid] =
+            make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                        acc[i][j][4 * q + 3]);
+  __syncthreads();
+  int* flag = reinterpret_cast<int*>(smem);
+  if (tid == 0) {
+    const int old = __hip_atomic_fetch_add(split_cnt + cidx, 1, __ATOMIC_ACQ_REL,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+    flag[0] = old == S - 1;
+    if (old == S - 1) split_cnt[cidx] = 0;  // ready for the next launch
+  }
+  __syncthreads();
+  if (!flag[0]) return false;
+  const float4* first = reinterpret_cast<const float4*>(split_ws) + (size_t)(slot - part) * TILE_F4;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int idx = ((i * 4 + j) * 4 + q) * NTHREADS + tid;
+        float4 v = first[idx];
+        for (int p = 1; p < S; ++p) {
+          const float4 w = first[(size_t)p * TILE_F4 + idx];
+          v.x += w.x;
+          v.y += w.y;
+          v.z += w.z;
+          v.w += w.w;
+        }
+        acc[i][j][4 * q] = v.x;
+        acc[i][j][4 * q + 1] = v.y;
+        acc[i][j][4 * q + 2] = v.z;
+        acc[i][j][4 * q + 3] = v.w;
+      }
   return true;
 }
 
@@ -438,7 +491,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_nt(NtArgs a) {
   const int ktiles = (a.K + TK - 1) / TK;
   int e, m0, mend, nt, k0 = 0, nk = ktiles, part = 0, S = 1, slot = 0, cidx = 0;
   if (KFULL) {
-    if (!deal_tile_nt(a, ktiles, e, m0, mend, nt, k0, nk, part, S, slot, cidx)) return;
+    if (!deal_tile_split(a.ends, a.E, a.m_cap, a.n_tiles, a.n_res, ktiles, e, m0, mend, nt, k0,
+                         nk, part, S, slot, cidx))
+      return;
   } else {
     if (!deal_tile<TB>(a.ends, a.E, a.m_cap, a.n_tiles, e, m0, mend, nt)) return;
   }
@@ -514,53 +569,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_nt(NtArgs a) {
     } else {
       mainloop_dma_g<false, false, 4>(sw, sx, smem, k0 * TK, nk * 2, tid, lane, wn, wm, acc);
     }
-    if (S > 1) {
-      // a part of a split tile: publish the fp32 partial; the last of the S parts
-      // to arrive sums all of them in part order (the same result whichever part
-      // arrives last) and goes on to the epilogue
-      constexpr int TILE_F4 = TB * TB / 4;
-      float4* mine = reinterpret_cast<float4*>(a.split_ws) + (size_t)slot * TILE_F4;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-            mine[((i * 4 + j) * 4 + q) * NTHREADS + tid] =
-                make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
-                            acc[i][j][4 * q + 3]);
-      __syncthreads();
-      int* flag = reinterpret_cast<int*>(smem);
-      if (tid == 0) {
-        const int old = __hip_atomic_fetch_add(a.split_cnt + cidx, 1, __ATOMIC_ACQ_REL,
-                                               __HIP_MEMORY_SCOPE_AGENT);
-        flag[0] = old == S - 1;
-        if (old == S - 1) a.split_cnt[cidx] = 0;  // ready for the next launch
-      }
-      __syncthreads();
-      if (!flag[0]) return;
-      const float4* first = reinterpret_cast<const float4*>(a.split_ws) + (size_t)(slot - part) * TILE_F4;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int idx = ((i * 4 + j) * 4 + q) * NTHREADS + tid;
-            float4 v = first[idx];
-            for (int p = 1; p < S; ++p) {
-              const float4 w = first[(size_t)p * TILE_F4 + idx];
-              v.x += w.x;
-              v.y += w.y;
-              v.z += w.z;
-              v.w += w.w;
-            }
-            acc[i][j][4 * q] = v.x;
-            acc[i][j][4 * q + 1] = v.y;
-            acc[i][j][4 * q + 2] = v.z;
-            acc[i][j][4 * q + 3] = v.w;
-          }
-    }
+    // a part of a split tile: the last of its parts to arrive finishes the tile
+    if (S > 1 && !split_reduce(acc, a.split_ws, a.split_cnt, slot, part, S, cidx, smem, tid))
+      return;
   } else {
     la.load(0);
     lb.load(0);
@@ -671,6 +682,8 @@ struct DgradArgs {
   // activation backward (ACT > 0): DX is dh [rows][2K] = [du | dg], from the fp32
   // pre-activations h [rows][2K] = [u | g] and the clamp limits of SwiGLUStep
   const float* h; const float* limits; float def_limit;
+  // optional split of the last round's tiles along N, as in the forward
+  float* split_ws; int32_t* split_cnt; int n_res;
 };
 
 // dgrad: dX[m, k] = sum_n G[m, n] W[e, n, k]; ACT 0 stores dX, ACT 1 / 2 treat dX as
@@ -678,8 +691,11 @@ struct DgradArgs {
 template <int ACT>
 __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_dgrad(DgradArgs a) {
   __shared__ uint4 smem[4 * TILE_U4];
-  int e, m0, mend, nt;  // nt: tile of K (output columns)
-  if (!deal_tile<TB>(a.ends, a.E, a.m_cap, a.n_tiles, e, m0, mend, nt)) return;
+  // nt: tile of K (output columns); [k0, k0 + nk): this workgroup's 32-deep stages of N
+  int e, m0, mend, nt, k0, nk, part, S, slot = 0, cidx = 0;
+  if (!deal_tile_split(a.ends, a.E, a.m_cap, a.n_tiles, a.n_res, a.N / 32, e, m0, mend, nt, k0, nk,
+                       part, S, slot, cidx))
+    return;
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int wn = wid & 1, wm = wid >> 1;
@@ -689,9 +705,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_dgrad(DgradArgs a) {
   zero_acc(acc);
   // (the contraction N is a multiple of 32: whole 32-deep stages)
   KmSrc sw;   // weight side: W[e] rows n (contraction), columns k
-  sw.base = reinterpret_cast<const char*>(a.W + (int64_t)e * a.N * a.K + c0);
+  sw.base = reinterpret_cast<const char*>(a.W + ((int64_t)e * a.N + (int64_t)k0 * 32) * a.K + c0);
   sw.ld2 = 2 * (int64_t)a.K;
-  sw.rows = a.N;
+  sw.rows = nk * 32;
   sw.cols2 = 2 * (a.K - c0);
   sw.init(tid);
   RmSrc sg;   // activation side: G rows, contraction along N
@@ -703,7 +719,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_dgrad(DgradArgs a) {
     sg.off[j] = (uint32_t)p * (uint32_t)a.N;
   }
   sg.init(tid);
-  mainloop_dma_g<true, false, 4>(sw, sg, smem, 0, a.N / 32, tid, lane, wn, wm, acc);
+  mainloop_dma_g<true, false, 4>(sw, sg, smem, k0 * 32, nk, tid, lane, wn, wm, acc);
+  if (S > 1 && !split_reduce(acc, a.split_ws, a.split_cnt, slot, part, S, cidx, smem, tid)) return;
   const int hi4 = (lane >> 5) * 4;
   float lim = 0.f;
   if (ACT == 2) lim = a.limits ? a.limits[e] : a.def_limit;
@@ -921,13 +938,20 @@ moe_status gemm_nt_enqueue(int epi, const void* A, const int32_t* a_gather, int 
 // [M, 2K] and h [M, 2K] the saved fp32 pre-activations.
 moe_status gemm_dgrad_enqueue(const void* G, const void* W, const int32_t* ends, int E, int64_t M,
                               int N, int K, void* DX, hipStream_t st, int act, const void* h,
-                              const float* limits, float def_limit) {
+                              const float* limits, float def_limit, void* split_ws,
+                              int32_t* split_cnt) {
   if (M == 0) return MOE_OK;
   DgradArgs a{reinterpret_cast<const uint16_t*>(G), reinterpret_cast<const uint16_t*>(W), ends, E,
               (int)M, N, K, (K + TB - 1) / TB, row_block_bound(M, E),
               reinterpret_cast<uint16_t*>(DX), reinterpret_cast<const float*>(h), limits,
-              def_limit};
-  const int grid = round_up8((int64_t)a.m_tiles * a.n_tiles);
+              def_limit, reinterpret_cast<float*>(split_ws), split_cnt, 0};
+  if (split_ws && split_cnt) {
+    const int cu = device_cu_count();
+    a.n_res = (cu < SPLIT_SLOTS ? cu : SPLIT_SLOTS) & ~7;  // one 128 KB-LDS workgroup per CU
+  }
+  // parts of split tiles take at most n_res + 8 * SPLIT_MAX workgroups past the whole ones
+  const int grid = round_up8((int64_t)a.m_tiles * a.n_tiles +
+                             (a.n_res > 0 ? a.n_res + 8 * SPLIT_MAX : 0));
   if (act == 1)
     k_gemm_dgrad<1><<<grid, NTHREADS, 0, st>>>(a);
   else if (act == 2)
