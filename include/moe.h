@@ -313,7 +313,10 @@ moe_status moe_fc2_fp8(const moe_ffn_desc* desc, const void* act, const float* a
  *   dw1 [L, 2I, H], dw2 [L, H, I] in grad_dtype (fully overwritten; exactly zero
  *   for an expert without routes), dx [T, H] bf16. Intermediates dy, dh are bf16;
  *   every sum runs in a fixed order (bitwise reproducible). ws: at least
- *   moe_ffn_backward_workspace_size(desc) bytes, 16-byte aligned.
+ *   moe_ffn_backward_workspace_size(desc) bytes, 16-byte aligned; it holds dy, dh,
+ *   the dx rows and 64 MiB of fp32 partial tiles with their arrival counters (the
+ *   dgrad's last round of tiles is cut along the contraction), so calls sharing
+ *   one ws must not overlap.
  */
 typedef struct moe_ffn_grads {
   const void* dout;           /* [T, H] bf16 */
