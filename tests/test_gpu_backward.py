@@ -19,7 +19,7 @@ import torch
 import mixture_experts_expert_softmax_amd as M
 import moe_synth as S
 import oracle as O
-from parity import to_np
+from parity import check_grads as _check, grad_bounds as _grad_bounds, to_np
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -41,59 +41,6 @@ def _oracle(c, ids, w, dout):
                           S.bf16_to_f32(c.w1), S.bf16_to_f32(c.w2), S.bf16_to_f32(dout),
                           num_experts=c.num_experts, local_offset=c.local_offset,
                           activation_kind=c.activation, limits=c.limits)
-
-
-U = 2.0 ** -8   # unit roundoff of bf16 (8 significand bits, round to nearest even)
-
-
-def _grad_bounds(c, ids, w, dout):
-    """First-order error bounds of (dx, dw1, dw2, dtopk_weights) from the bf16 hand-offs,
-    from absolute values of the exact intermediates (float32 accumulation over a length n
-    adds n 2^-24 of the absolute sum)."""
-    x, w1, w2 = (S.bf16_to_f32(t).astype(np.float64) for t in (c.x, c.w1, c.w2))
-    ids = ids.cpu().numpy()
-    w = w.cpu().numpy().astype(np.float64)
-    dout = S.bf16_to_f32(dout).astype(np.float64)
-    T, k = ids.shape
-    L, H = w1.shape[0], x.shape[1]
-    loc = O.local_expert(ids, c.num_experts, L, c.local_offset).reshape(T, k)
-    bx, bw1, bw2 = np.zeros_like(x), np.zeros_like(w1), np.zeros_like(w2)
-    bdw = np.zeros((T, k))
-    ax = np.abs(x)
-    for e in range(L):
-        tt, ss = np.nonzero(loc == e)
-        if tt.size == 0:
-            continue
-        lim = 7.0 if c.limits is None else float(c.limits[e])
-        h = x[tt] @ w1[e].T
-        a = O.activation(h, c.activation, lim)
-        y = a @ w2[e].T
-        dy = w[tt, ss][:, None] * dout[tt]
-        da = dy @ w2[e]
-        dh = O.activation_backward(h, da, c.activation, lim)
-        # d dh / d da (dh is linear in da), applied to the error of da
-        sens = np.abs(O.activation_backward(h, np.ones_like(da), c.activation, lim))
-        eda = (U + H * 2.0 ** -24) * (np.abs(dy) @ np.abs(w2[e]))
-        bdh = sens * np.concatenate([eda, eda], axis=1) + U * np.abs(dh)
-        bw1[e] = bdh.T @ ax[tt] + U * np.abs(dh.T @ x[tt])
-        bw2[e] = 2 * U * (np.abs(dy).T @ np.abs(a)) + U * np.abs(dy.T @ a)
-        np.add.at(bx, tt, bdh @ np.abs(w1[e]) + U * np.abs(dh @ w1[e]))
-        bdw[tt, ss] = (U + H * 2.0 ** -24) * np.sum(np.abs(dout[tt]) * np.abs(y), axis=1)
-    return bx, bw1, bw2, bdw
-
-
-def _check(grads, ref, bounds, what):
-    for name, g, r, b in zip(("dx", "dw1", "dw2", "dtopk_weights"), grads, ref, bounds):
-        g = to_np(g).astype(np.float64)
-        assert np.all(np.isfinite(g)), f"{what} {name}: non-finite"
-        d = np.abs(g - r)
-        # the output's own rounding, and a floor for elements whose bound is 0
-        lim = b + U * np.abs(r) + 1e-30
-        bad = d > lim
-        assert not bad.any(), (f"{what} {name}: {bad.sum()} elements beyond the bound, worst "
-                               f"{(d / lim).max():.3f}x")
-        rl = np.linalg.norm(g - r) / max(np.linalg.norm(r), 1e-300)
-        assert rl <= 1e-2, f"{what} {name}: relative L2 {rl:.3e}"
 
 
 @pytest.mark.parametrize("activation", ["swiglu", "swiglu_step"])

@@ -5,8 +5,9 @@ no allocation and no host synchronisation in a launch; grouped-GEMM page,
 Each test captures library calls into one hipGraph (torch.cuda.CUDAGraph on
 ROCm), then replays it several times with new inputs written into the captured
 buffers, running the eager computation and synchronising between replays, and
-checks every replay bitwise against the eager result. The library clears its
-counters and outputs with kernels, never with memset nodes.
+checks every replay bitwise against the eager result and against the oracle (to
+the same bar as the eager tests of each path). The library clears its counters and
+outputs with kernels, never with memset nodes.
 """
 import numpy as np
 import pytest
@@ -14,6 +15,8 @@ import torch
 
 import mixture_experts_expert_softmax_amd as M
 import moe_synth as S
+import oracle as O
+from parity import (assert_close_bf16, check_grads, grad_bounds, mx_dequant_table, to_np)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -66,6 +69,11 @@ def test_bf16_layer_graph_replays_with_new_inputs():
                                 clamp_limit=lim)
         torch.cuda.synchronize()
         assert torch.equal(got, ref)
+        oref = O.moe_forward(S.bf16_to_f32(c.x), ids_e.cpu().numpy(),
+                             w_e.cpu().numpy().astype(np.float64), S.bf16_to_f32(c0.w1),
+                             S.bf16_to_f32(c0.w2), num_experts=E, activation_kind="swiglu_step",
+                             limits=c0.limits)
+        assert_close_bf16(got, oref, what=f"graph replay seed {c.meta['seed']}")
 
 
 def test_w4a8_decode_graph_replays():
@@ -87,6 +95,8 @@ def test_w4a8_decode_graph_replays():
                              full.num_experts, out=out, workspace=ws)
 
     g = _capture(step)
+    w1d = mx_dequant_table("mxfp4", full.w1, full.w1_sf)
+    w2d = mx_dequant_table("mxfp4", full.w2, full.w2_sf)
     for t0 in (8, 20, 40, 0):
         sl = slice(t0, t0 + T)
         logits.copy_(torch.from_numpy(full.logits[sl]))
@@ -100,6 +110,10 @@ def test_w4a8_decode_graph_replays():
                                    d["w1"], d["w1_sf"], d["w2"], d["w2_sf"], full.num_experts)
         torch.cuda.synchronize()
         assert torch.equal(got, ref)
+        oref = O.moe_forward(O.mx_dequant_fp8(full.x[sl], full.x_sf[sl]), ids_e.cpu().numpy(),
+                             w_e.cpu().numpy().astype(np.float64), w1d, w2d,
+                             num_experts=full.num_experts, requant=True)
+        assert_close_bf16(got, oref, 8e-2, 3e-2, what=f"MXFP4 graph replay tokens {t0}..")
 
 
 def test_grouped_gemm_graph_with_offsets_rewritten():
@@ -124,6 +138,8 @@ def test_grouped_gemm_graph_with_offsets_rewritten():
         torch.cuda.synchronize()
         n = int(np.sum(sz))
         assert torch.equal(got[:n], ref[:n])
+        oref = O.grouped_gemm_fwd(S.bf16_to_f32(x)[:n], S.bf16_to_f32(w), np.cumsum(sz))
+        assert_close_bf16(got[:n], oref, what="grouped fwd graph replay")
 
 
 def test_training_step_graph_replays():
@@ -152,3 +168,7 @@ def test_training_step_graph_replays():
         torch.cuda.synchronize()
         for a, b in zip(got, ref):
             assert torch.equal(a, b)
+        oref = O.moe_backward(S.bf16_to_f32(c.x), ids.cpu().numpy(),
+                              w.cpu().numpy().astype(np.float64), S.bf16_to_f32(c.w1),
+                              S.bf16_to_f32(c.w2), S.bf16_to_f32(dout), num_experts=E)
+        check_grads(got, oref, grad_bounds(c, ids, w, dout), f"graph training replay {seed}")

@@ -15,7 +15,7 @@ import torch
 import mixture_experts_expert_softmax_amd as M
 import moe_synth as S
 import oracle as O
-from parity import assert_close_bf16, to_np
+from parity import assert_close_bf16, mx_dequant_table, to_np
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -28,7 +28,7 @@ WFMTS = ["mxfp4", "mxfp8", "fp8"]
 def _deq(wfmt, codes, scales):
     if wfmt == "fp8":
         return O.fp8_dequant(codes, scales)
-    return (O.mx_dequant_fp4 if wfmt == "mxfp4" else O.mx_dequant_fp8)(codes, scales)
+    return mx_dequant_table(wfmt, codes, scales)
 
 
 class _LazyBank:
@@ -44,7 +44,9 @@ class _LazyBank:
             return self.cache[e]
         v = _deq(self.wfmt, self.codes[e], self.scales[e])
         if self.cache is not None:
-            self.cache[e] = v
+            # float32 halves the memory of a decoded bank: exact for the MX families
+            # (code value times a power of two), within 2^-24 relative for fp8 per-tensor
+            self.cache[e] = v = v.astype(np.float32)
         return v
 
 
@@ -242,19 +244,37 @@ def mx_full(request):
     return S.w4a8_moe(seed=0, T=8192, wfmt=request.param), {}, {}
 
 
-@pytest.mark.parametrize("T", [1, 16, 128, 8192])
-def test_mx_full_shape_sampled(mx_full, T):
-    """H=7168, I=2048, 64 experts, top-8 at the decode and prefill token counts, for
-    both weight families; two sampled tokens are checked against the oracle."""
+def _tile_cover_tokens(ids, num_experts, tile=256):
+    """Tokens that own the first and the last row of every 256-row tile of every
+    expert's group in the sorted order: every tile of both GEMMs gets compared."""
+    T, k = ids.shape
+    srt = O.sort_routes(ids, num_experts, num_experts, 0)
+    rows, start = [], 0
+    for end in srt["offs"].tolist():
+        for r0 in range(start, end, tile):
+            rows += [r0, min(r0 + tile, end) - 1]
+        start = end
+    return np.unique(srt["p2e"][np.asarray(rows, np.int64)] // k)
+
+
+@pytest.mark.parametrize("T", [1, 16, 128, 1024, 8192])
+def test_mx_full_shape(mx_full, T):
+    """H=7168, I=2048, 64 experts, top-8 over the decode-to-prefill sweep, for the three
+    weight families: every token against the oracle up to T=1024; at T=8192 the tokens
+    that own the first and last rows of every 256-row tile of every expert, plus 64
+    random ones."""
     full, cache1, cache2 = mx_full
     x_sf = full.x_sf if full.wfmt == "fp8" else full.x_sf[:T]
     c = S.W4A8Case(T, full.H, full.I, full.num_experts, full.top_k, full.logits[:T], full.x[:T],
                    x_sf, full.w1, full.w1_sf, full.w2, full.w2_sf, full.wfmt, full.act_scale)
     out, ids, w = _run(c, _dev(c))
     torch.cuda.synchronize()
-    # token 0 routes identically at every T (the logits are shared), so its experts are
-    # decoded once; the largest case also checks its last token
-    tokens = np.array([0, T - 1]) if T == 8192 else np.array([0])
+    tokens = None
+    if T > 1024:
+        cover = _tile_cover_tokens(ids.cpu().numpy(), c.num_experts)
+        extra = np.random.default_rng(T).choice(T, 64, replace=False)
+        tokens = np.unique(np.concatenate([cover, extra]))
+        assert tokens.size >= 2 * c.num_experts
     ref = _oracle(c, ids, w, tokens=tokens, cache1=cache1, cache2=cache2)
-    assert_close_bf16(to_np(out)[tokens], ref, MX_MAX_ABS, MX_REL,
-                      what=f"{full.wfmt} full T={T}")
+    got = to_np(out) if tokens is None else to_np(out)[tokens]
+    assert_close_bf16(got, ref, MX_MAX_ABS, MX_REL, what=f"{full.wfmt} full T={T}")

@@ -200,3 +200,16 @@ def test_moe_forward_fp8_per_tensor_matches_torch_pipeline():
             y = (aq.double() * float(np.float32(act_s))) @ (w2q[e].double() * float(w2s[e])).T
             ref[t] += w[t, s] * y
     np.testing.assert_allclose(got, ref.numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_table_dequant_helper_equals_oracle():
+    """The GPU tests decode full expert banks through parity.mx_dequant_table; it must
+    give exactly the oracle's values (NaN codes aside, which the inputs never hold)."""
+    from parity import mx_dequant_table
+    g = np.random.default_rng(7)
+    packed = g.integers(0, 256, size=(64, 96), dtype=np.uint8)
+    codes8 = g.integers(0, 256, size=(64, 192), dtype=np.uint8)
+    codes8[(codes8 & 0x7F) == 0x7F] = 0
+    sc = g.integers(100, 160, size=(64, 6), dtype=np.uint8)
+    np.testing.assert_array_equal(mx_dequant_table("mxfp4", packed, sc), O.mx_dequant_fp4(packed, sc))
+    np.testing.assert_array_equal(mx_dequant_table("mxfp8", codes8, sc), O.mx_dequant_fp8(codes8, sc))
