@@ -58,6 +58,7 @@ typedef int32_t moe_status;
 #define MOE_ERR_UNSUPPORTED  5  /* valid request this library does not serve */
 #define MOE_ERR_WORKSPACE    6  /* workspace NULL or smaller than the *_workspace_size query */
 #define MOE_ERR_HIP          7  /* a kernel launch failed */
+#define MOE_ERR_TOO_LARGE    8  /* moe_ffn_forward_noalloc: the request needs more than its fixed scratch */
 
 /* Element types. */
 #define MOE_DTYPE_BF16 0
@@ -197,6 +198,27 @@ typedef struct moe_ffn_tensors {
 size_t moe_ffn_workspace_size(const moe_ffn_desc* desc);
 moe_status moe_ffn_forward(const moe_ffn_desc* desc, const moe_ffn_tensors* tensors,
                            void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_ffn_forward_noalloc -- moe_ffn_forward without a caller workspace, for callers
+ * that cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc. Same desc, tensors, kernels and results as
+ * moe_ffn_forward (the outputs are bitwise equal); the workspace is instead a fixed
+ * device array of MOE_NOALLOC_SCRATCH_BYTES inside the library, one per GPU, held until
+ * the process ends. The call itself allocates nothing. A request whose
+ * moe_ffn_workspace_size(desc) exceeds MOE_NOALLOC_SCRATCH_BYTES returns
+ * MOE_ERR_TOO_LARGE with nothing enqueued (for bf16 weights the workspace is 64 MiB
+ * of split-tile partials plus about (I + H) * 2 bytes per route: e.g. T * top_k up to
+ * ~3600 routes at H = 7168, I = 2048). The first call on a device looks up the array's
+ * device address (a host-side query, no allocation); a caller that captures graphs
+ * makes one call before capturing. Every call on a GPU shares that GPU's array, and
+ * nothing needs it cleared between calls (the sort clears the split-tile counters on
+ * every call), but calls that overlap in time on one GPU (other streams or threads)
+ * race on it: serialise them.
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES (128u << 20)
+moe_status moe_ffn_forward_noalloc(const moe_ffn_desc* desc, const moe_ffn_tensors* tensors,
+                                   void* stream);
 
 /*
  * The two GEMM stages of moe_ffn_forward as separate calls ([StepFun] "One-shot

@@ -24,7 +24,7 @@ __all__ = [
     "moe_finalize", "moe_fc1", "moe_fc2", "status_string", "ACT", "FINALIZE", "WFMT",
     "moe_ffn_forward_mx", "moe_fc1_mx", "moe_fc2_mx", "moe_ffn_forward_fp8", "moe_fc1_fp8",
     "moe_fc2_fp8", "moe_ffn_forward_train", "moe_ffn_backward", "moe_route_backward", "MoEFunction",
-    "moe_tune_mx", "moe_tune_clear", "moe_bgmv",
+    "moe_tune_mx", "moe_tune_clear", "moe_bgmv", "moe_ffn_forward_noalloc", "NOALLOC_SCRATCH_BYTES",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -40,6 +40,7 @@ _sz = ctypes.c_size_t
 
 
 WFMT = {"bf16": 0, "mxfp4": 1, "mxfp8": 2, "fp8": 3}
+NOALLOC_SCRATCH_BYTES = 128 << 20   # MOE_NOALLOC_SCRATCH_BYTES of include/moe.h
 
 
 class MoeFfnDesc(ctypes.Structure):
@@ -77,6 +78,7 @@ EXPORTS = {
     "grouped_gemm_wgrad": (_i32, [_vp, _vp, _vp, _i32, _i32, _i64, _i32, _i32, _vp, _i32, _vp, _sz, _vp]),
     "moe_ffn_workspace_size": (_sz, [ctypes.POINTER(MoeFfnDesc)]),
     "moe_ffn_forward": (_i32, [ctypes.POINTER(MoeFfnDesc), ctypes.POINTER(MoeFfnTensors), _vp, _sz, _vp]),
+    "moe_ffn_forward_noalloc": (_i32, [ctypes.POINTER(MoeFfnDesc), ctypes.POINTER(MoeFfnTensors), _vp]),
     "moe_finalize": (_i32, [_vp, _vp, _vp, _i64, _i32, _i32, _vp, _vp]),
     "moe_gemm_split_workspace_size": (_sz, []),
     "moe_fc1": (_i32, [ctypes.POINTER(MoeFfnDesc), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
@@ -303,6 +305,46 @@ def moe_ffn_forward(x: torch.Tensor, topk_ids: torch.Tensor, topk_weights: torch
                          None if e2p is None else e2p.data_ptr(), None, None, None)
     _check("moe_ffn_forward", h.moe_ffn_forward(ctypes.byref(d), ctypes.byref(tens), _ptr(workspace),
                                                 workspace.numel(), _stream()))
+    if finalize == "none":
+        return y, e2p[: T * k]
+    return out
+
+
+def moe_ffn_forward_noalloc(x: torch.Tensor, topk_ids: torch.Tensor, topk_weights: torch.Tensor,
+                            w1: torch.Tensor, w2: torch.Tensor, num_experts: int,
+                            num_local_experts: Optional[int] = None, local_expert_offset: int = 0,
+                            activation: str = "swiglu", clamp_limit: Optional[torch.Tensor] = None,
+                            finalize: str = "deterministic", out: Optional[torch.Tensor] = None,
+                            y: Optional[torch.Tensor] = None, e2p: Optional[torch.Tensor] = None,
+                            weight_format: str = "bf16", x_sf: Optional[torch.Tensor] = None,
+                            w1_sf: Optional[torch.Tensor] = None, w2_sf: Optional[torch.Tensor] = None,
+                            act_scale: Optional[torch.Tensor] = None):
+    """moe_ffn_forward with the library's fixed scratch memory instead of a workspace: the
+    same layer and bits. Outputs (out, or y and e2p for finalize="none") must be passed in
+    by a caller that cannot allocate; here they are created when omitted. weight_format
+    "mxfp4" / "mxfp8" / "fp8" takes the operands of moe_ffn_forward_mx / _fp8 (x_sf, w1_sf,
+    w2_sf hold x_scale, w1_scale, w2_scale for "fp8")."""
+    wdt = torch.bfloat16 if weight_format == "bf16" else torch.uint8
+    _dev(x, wdt, "x"), _dev(w1, wdt, "w1"), _dev(w2, wdt, "w2")
+    _dev(topk_ids, torch.int32, "topk_ids"), _dev(topk_weights, torch.float32, "topk_weights")
+    T, H = x.shape
+    L, twoI, _ = w1.shape
+    I = twoI // 2
+    k = topk_ids.shape[1]
+    d = _ffn_desc(T, H, I, num_experts, L, local_expert_offset, k, activation, finalize,
+                  weight_format)
+    if finalize == "none":
+        if y is None:
+            y = torch.empty((max(T * k, 1), H), dtype=torch.bfloat16, device=x.device)
+        if e2p is None:
+            e2p = torch.empty(max(T * k, 1), dtype=torch.int32, device=x.device)
+    elif out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
+    p = lambda t_: None if t_ is None else t_.data_ptr()  # noqa: E731
+    tens = MoeFfnTensors(p(x), p(topk_ids), p(topk_weights), p(w1), p(w2), p(clamp_limit), p(out),
+                         p(y), p(e2p), p(x_sf), p(w1_sf), p(w2_sf), p(act_scale))
+    _check("moe_ffn_forward_noalloc", lib().moe_ffn_forward_noalloc(ctypes.byref(d), ctypes.byref(tens),
+                                                                    _stream()))
     if finalize == "none":
         return y, e2p[: T * k]
     return out

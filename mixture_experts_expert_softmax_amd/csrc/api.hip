@@ -1,6 +1,7 @@
 // C-ABI entry points that chain the kernels: the grouped GEMMs and the MoE
 // expert-layer forward. Argument rules and layouts are documented in moe.h.
 #include <algorithm>
+#include <mutex>
 
 #include "common.h"
 
@@ -156,6 +157,8 @@ extern "C" const char* moe_status_string(moe_status s) {
     case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: request outside the served configurations";
     case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace missing or too small";
     case MOE_ERR_HIP: return "MOE_ERR_HIP: a kernel launch failed";
+    case MOE_ERR_TOO_LARGE:
+      return "MOE_ERR_TOO_LARGE: the request needs more than the no-allocation scratch memory";
     default: return "unknown moe_status";
   }
 }
@@ -628,4 +631,45 @@ extern "C" moe_status moe_fc2(const moe_ffn_desc* d, const void* act, const void
   if (s != MOE_OK) return s;
   return fc2_enqueue(d, act, w2, offs, p2e, topk_weights, dst, as_stream(stream), split_ws,
                      split_cnt);
+}
+
+// ---------------------------------------------------------------------------
+// moe_ffn_forward_noalloc: moe_ffn_forward with its workspace in a file-scope device
+// array (one copy per device, held until the process ends) instead of a caller buffer.
+// Host code never passes the array's name to a kernel: its address on the current
+// device is looked up once per device and kept below, and only that address is used.
+// ---------------------------------------------------------------------------
+__device__ __align__(256) char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int MAX_DEVICES = 64;
+std::mutex scratch_mu;
+void* scratch_ptr[MAX_DEVICES] = {};
+
+// Address of this device's copy of `scratch`, resolved on the first call per device.
+moe_status scratch_of_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return MOE_ERR_HIP;
+  if (dev >= MAX_DEVICES) return MOE_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOE_ERR_HIP;
+    scratch_ptr[dev] = p;
+  }
+  *out = scratch_ptr[dev];
+  return MOE_OK;
+}
+}  // namespace
+
+extern "C" moe_status moe_ffn_forward_noalloc(const moe_ffn_desc* d, const moe_ffn_tensors* t,
+                                              void* stream) {
+  moe_status s = check_ffn(d);
+  if (s != MOE_OK) return s;
+  // the same workspace layout as moe_ffn_forward, so both run identical launches
+  if (ffn_layout(d).total > (size_t)MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_TOO_LARGE;
+  void* ws = nullptr;
+  s = scratch_of_current_device(&ws);
+  if (s != MOE_OK) return s;
+  return ffn_forward(d, t, ws, (size_t)MOE_NOALLOC_SCRATCH_BYTES, stream, false);
 }

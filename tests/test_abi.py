@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for code in range(8):
+    for code in range(9):
         s = M.status_string(code)
         assert s.startswith("MOE_"), s
     assert "unknown" in M.status_string(99)
@@ -73,3 +73,14 @@ def test_workspace_queries(lib):
     assert lib.moe_ffn_workspace_size(ctypes.byref(d)) == 0
     bad = M.MoeFfnDesc(16, 128, 256, 8, 8, 0, 2, 0, 5)
     assert lib.moe_ffn_forward(ctypes.byref(bad), None, None, 0, None) == 3
+
+
+def test_noalloc_rejects_requests_beyond_its_scratch(lib):
+    # decided from the shapes on the host, before the device or the scratch is touched
+    d = M.MoeFfnDesc(4096, 4096, 14336, 8, 8, 0, 2, 0, 0)
+    assert lib.moe_ffn_workspace_size(ctypes.byref(d)) > M.NOALLOC_SCRATCH_BYTES
+    t = M.MoeFfnTensors()
+    assert lib.moe_ffn_forward_noalloc(ctypes.byref(d), ctypes.byref(t), None) == 8
+    assert "scratch" in M.status_string(8)
+    bad = M.MoeFfnDesc(16, 100, 256, 8, 8, 0, 2, 0, 0)   # H % 64
+    assert lib.moe_ffn_forward_noalloc(ctypes.byref(bad), ctypes.byref(t), None) == 2
