@@ -146,11 +146,21 @@ moe_status moe_sort(const int32_t* topk_ids, int64_t T, int32_t top_k, int32_t n
  *                     (w is read in place, not transposed or copied)
  * grouped_gemm_wgrad: dw[e] = g[rows e].T @ x[rows e]  -> dw [E,N,K], out_dtype bf16 or f32;
  *                     an empty group's dw[e] is written as exact zeros.
+ * fwd / dgrad ws, ws_bytes (optional, NULL / 0 allowed): the split workspace of moe_fc1 /
+ * moe_fc2 (at least moe_gemm_split_workspace_size() bytes, 16-byte aligned, not shared
+ * by calls that may overlap). With it, the tiles of a last, mostly idle round of
+ * workgroups are cut along the contraction and their fp32 partials summed in a fixed
+ * order: the same result on every run, whose rounding differs from the uncut order
+ * within fp32 and depends on the tile count. Without it every tile is whole, and each
+ * output element's summation order depends only on K (the same bits for a group
+ * computed alone or among others).
  */
 moe_status grouped_gemm_fwd(const void* x, const void* w, const int32_t* offs, int32_t offs_kind,
-                            int32_t E, int64_t sum_m, int32_t N, int32_t K, void* y, void* stream);
+                            int32_t E, int64_t sum_m, int32_t N, int32_t K, void* y, void* ws,
+                            size_t ws_bytes, void* stream);
 moe_status grouped_gemm_dgrad(const void* g, const void* w, const int32_t* offs, int32_t offs_kind,
-                              int32_t E, int64_t sum_m, int32_t N, int32_t K, void* dx, void* stream);
+                              int32_t E, int64_t sum_m, int32_t N, int32_t K, void* dx, void* ws,
+                              size_t ws_bytes, void* stream);
 size_t grouped_gemm_wgrad_workspace_size(int32_t E, int64_t sum_m, int32_t N, int32_t K,
                                          int32_t out_dtype);
 moe_status grouped_gemm_wgrad(const void* g, const void* x, const int32_t* offs, int32_t offs_kind,

@@ -72,8 +72,8 @@ EXPORTS = {
     "moe_route": (_i32, [_vp, _i64, _i32, _i32, _vp, _vp, _vp]),
     "moe_sort_workspace_size": (_sz, [_i64, _i32, _i32]),
     "moe_sort": (_i32, [_vp, _i64, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
-    "grouped_gemm_fwd": (_i32, [_vp, _vp, _vp, _i32, _i32, _i64, _i32, _i32, _vp, _vp]),
-    "grouped_gemm_dgrad": (_i32, [_vp, _vp, _vp, _i32, _i32, _i64, _i32, _i32, _vp, _vp]),
+    "grouped_gemm_fwd": (_i32, [_vp, _vp, _vp, _i32, _i32, _i64, _i32, _i32, _vp, _vp, _sz, _vp]),
+    "grouped_gemm_dgrad": (_i32, [_vp, _vp, _vp, _i32, _i32, _i64, _i32, _i32, _vp, _vp, _sz, _vp]),
     "grouped_gemm_wgrad_workspace_size": (_sz, [_i32, _i64, _i32, _i32, _i32]),
     "grouped_gemm_wgrad": (_i32, [_vp, _vp, _vp, _i32, _i32, _i64, _i32, _i32, _vp, _i32, _vp, _sz, _vp]),
     "moe_ffn_workspace_size": (_sz, [ctypes.POINTER(MoeFfnDesc)]),
@@ -204,8 +204,10 @@ def moe_sort(topk_ids: torch.Tensor, num_experts: int, num_local_experts: Option
 
 # --------------------------------------------------------------------------- grouped GEMM
 def grouped_gemm_fwd(x: torch.Tensor, w: torch.Tensor, offs: torch.Tensor, out=None,
-                     offs_kind: Optional[str] = None):
-    """y[rows of e] = x[rows of e] @ w[e].T; x [M,K], w [E,N,K], offs int32 ends [E] (or indptr)."""
+                     offs_kind: Optional[str] = None, workspace: Optional[torch.Tensor] = None):
+    """y[rows of e] = x[rows of e] @ w[e].T; x [M,K], w [E,N,K], offs int32 ends [E] (or indptr).
+    workspace (optional, >= moe_gemm_split_workspace_size() bytes) lets the last round of
+    tiles be cut along K (fixed-order fp32 partial sums)."""
     _dev(x, torch.bfloat16, "x"), _dev(w, torch.bfloat16, "w")
     E, N, K = w.shape
     kind = offs_kind or ("ends" if offs.numel() == E else "indptr")
@@ -213,14 +215,17 @@ def grouped_gemm_fwd(x: torch.Tensor, w: torch.Tensor, offs: torch.Tensor, out=N
     M = x.shape[0]
     if out is None:
         out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    nws = 0 if workspace is None else workspace.numel()
     _check("grouped_gemm_fwd", lib().grouped_gemm_fwd(_ptr(x), _ptr(w), _ptr(offs), OFFS[kind], E, M,
-                                                      N, K, _ptr(out), _stream()))
+                                                      N, K, _ptr(out), _ptr(workspace), nws,
+                                                      _stream()))
     return out
 
 
 def grouped_gemm_dgrad(g: torch.Tensor, w: torch.Tensor, offs: torch.Tensor, out=None,
-                       offs_kind: Optional[str] = None):
-    """dx[rows of e] = g[rows of e] @ w[e]; g [M,N], w [E,N,K] -> dx [M,K] bf16."""
+                       offs_kind: Optional[str] = None, workspace: Optional[torch.Tensor] = None):
+    """dx[rows of e] = g[rows of e] @ w[e]; g [M,N], w [E,N,K] -> dx [M,K] bf16 (workspace as
+    grouped_gemm_fwd: the last round's tiles cut along N)."""
     _dev(g, torch.bfloat16, "g"), _dev(w, torch.bfloat16, "w")
     E, N, K = w.shape
     kind = offs_kind or ("ends" if offs.numel() == E else "indptr")
@@ -228,8 +233,10 @@ def grouped_gemm_dgrad(g: torch.Tensor, w: torch.Tensor, offs: torch.Tensor, out
     M = g.shape[0]
     if out is None:
         out = torch.empty((M, K), dtype=torch.bfloat16, device=g.device)
+    nws = 0 if workspace is None else workspace.numel()
     _check("grouped_gemm_dgrad", lib().grouped_gemm_dgrad(_ptr(g), _ptr(w), _ptr(offs), OFFS[kind], E,
-                                                          M, N, K, _ptr(out), _stream()))
+                                                          M, N, K, _ptr(out), _ptr(workspace), nws,
+                                                          _stream()))
     return out
 
 

@@ -165,21 +165,49 @@ extern "C" const char* moe_status_string(moe_status s) {
 
 extern "C" const char* moe_version(void) { return "moe-mi355x 0.1 (gfx950)"; }
 
+constexpr size_t SPLIT_CNT_OFF = (size_t)SPLIT_SLOTS * SPLIT_TILE_BYTES;
+constexpr size_t SPLIT_WS_BYTES = SPLIT_CNT_OFF + (size_t)SPLIT_SLOTS * 4;
+
+extern "C" size_t moe_gemm_split_workspace_size(void) { return SPLIT_WS_BYTES; }
+
+static moe_status split_args(void* ws, size_t ws_bytes, hipStream_t st, void*& split_ws,
+                             int32_t*& split_cnt) {
+  split_ws = nullptr;
+  split_cnt = nullptr;
+  if (!ws) return MOE_OK;
+  if (ws_bytes < SPLIT_WS_BYTES || !aligned16(ws)) return MOE_ERR_WORKSPACE;
+  split_ws = ws;
+  split_cnt = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(ws) + SPLIT_CNT_OFF);
+  return zero_fill(split_cnt, (size_t)SPLIT_SLOTS * 4, st);
+}
+
 extern "C" moe_status grouped_gemm_fwd(const void* x, const void* w, const int32_t* offs,
                                        int32_t kind, int32_t E, int64_t M, int32_t N, int32_t K,
-                                       void* y, void* stream) {
+                                       void* y, void* ws, size_t ws_bytes, void* stream) {
   moe_status s = check_gemm(x, w, offs, kind, E, M, N, K, y);
   if (s != MOE_OK) return s;
+  if (M == 0) return MOE_OK;
+  void* split_ws;
+  int32_t* split_cnt;
+  s = split_args(ws, ws_bytes, as_stream(stream), split_ws, split_cnt);
+  if (s != MOE_OK) return s;
   return gemm_nt_enqueue(EPI_STORE, x, nullptr, 1, w, N, E, ends_of(offs, kind), M, N, K, y, N, 0,
-                         nullptr, 0.f, nullptr, nullptr, 1, as_stream(stream));
+                         nullptr, 0.f, nullptr, nullptr, 1, as_stream(stream), split_ws,
+                         split_cnt);
 }
 
 extern "C" moe_status grouped_gemm_dgrad(const void* g, const void* w, const int32_t* offs,
                                          int32_t kind, int32_t E, int64_t M, int32_t N, int32_t K,
-                                         void* dx, void* stream) {
+                                         void* dx, void* ws, size_t ws_bytes, void* stream) {
   moe_status s = check_gemm(g, w, offs, kind, E, M, N, K, dx);
   if (s != MOE_OK) return s;
-  return gemm_dgrad_enqueue(g, w, ends_of(offs, kind), E, M, N, K, dx, as_stream(stream));
+  if (M == 0) return MOE_OK;
+  void* split_ws;
+  int32_t* split_cnt;
+  s = split_args(ws, ws_bytes, as_stream(stream), split_ws, split_cnt);
+  if (s != MOE_OK) return s;
+  return gemm_dgrad_enqueue(g, w, ends_of(offs, kind), E, M, N, K, dx, as_stream(stream), 0,
+                            nullptr, nullptr, 7.0f, split_ws, split_cnt);
 }
 
 extern "C" size_t grouped_gemm_wgrad_workspace_size(int32_t, int64_t, int32_t, int32_t, int32_t) {
@@ -583,22 +611,6 @@ extern "C" moe_status moe_fc2_fp8(const moe_ffn_desc* d, const void* act, const 
 
 // Split-tile workspace of the standalone GEMM stages: partial tiles, then the
 // arrival counters, which each call clears first.
-constexpr size_t SPLIT_CNT_OFF = (size_t)SPLIT_SLOTS * SPLIT_TILE_BYTES;
-constexpr size_t SPLIT_WS_BYTES = SPLIT_CNT_OFF + (size_t)SPLIT_SLOTS * 4;
-
-extern "C" size_t moe_gemm_split_workspace_size(void) { return SPLIT_WS_BYTES; }
-
-static moe_status split_args(void* ws, size_t ws_bytes, hipStream_t st, void*& split_ws,
-                             int32_t*& split_cnt) {
-  split_ws = nullptr;
-  split_cnt = nullptr;
-  if (!ws) return MOE_OK;
-  if (ws_bytes < SPLIT_WS_BYTES || !aligned16(ws)) return MOE_ERR_WORKSPACE;
-  split_ws = ws;
-  split_cnt = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(ws) + SPLIT_CNT_OFF);
-  return zero_fill(split_cnt, (size_t)SPLIT_SLOTS * 4, st);
-}
-
 extern "C" moe_status moe_fc1(const moe_ffn_desc* d, const void* x, const void* w1,
                               const float* clamp_limit, const int32_t* offs, const int32_t* p2e,
                               void* act, void* ws, size_t ws_bytes, void* stream) {

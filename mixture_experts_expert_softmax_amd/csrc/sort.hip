@@ -8,16 +8,18 @@
 // from global id local_expert_offset; other routes contribute nothing.
 //
 // Up to 16384 routes (and per-wave histograms that fit in 64 KB of LDS): one
-// workgroup does it all (k_sort_block); one launch wins while the routes are few
-// (measured: 15-22 us against 25-30 us up to 8192 routes, equal at 16384, and
-// 73-82 us against 28-31 us at 65536 for 64 or 256 experts). Beyond that, three
-// launches over chunks of CHUNK routes (one wave64 per chunk):
-//  1. k_sort_count:   per-chunk histogram of local experts -> cnt[e][chunk]
-//  2. k_sort_scan:    one block per expert: exclusive scan of cnt[e][*] over
-//                     chunks (in place) and the expert total
-//  3. k_sort_scatter: scan of the totals -> expert start rows; every chunk walks
-//                     its routes in order, 64 at a time, ranking equal keys with
-//                     ballots (stable), and writes e2p / p2e.
+// workgroup does it all (k_sort_block); one launch wins while the routes are few.
+// Beyond that, three launches over chunks of CHUNK routes (one 256-thread
+// workgroup per chunk, wave w owning the chunk's w-th quarter):
+//  1. k_sort_count:   per-chunk histogram of local experts -> cnt[chunk][e]
+//                     (one coalesced row per chunk)
+//  2. k_sort_scan:    per expert, the exclusive prefix of cnt[*][e] over the
+//                     chunks (in place) and the expert total; 64 experts per
+//                     workgroup, each column split over 16 slices of chunks
+//  3. k_sort_scatter: an exclusive scan of the totals -> expert start rows; each
+//                     wave counts its quarter, then walks its routes in order, 64
+//                     at a time, ranking equal keys with ballots (stable), and
+//                     writes e2p / p2e.
 // The result is a pure function of the ids: no atomics decide any position.
 #include "common.h"
 
@@ -25,7 +27,8 @@ namespace moe {
 namespace {
 
 constexpr int SORT_STEPS = 16;
-constexpr int CHUNK = 64 * SORT_STEPS;  // routes per wave64 chunk
+constexpr int SORT_WAVES = 4;
+constexpr int CHUNK = 64 * SORT_STEPS * SORT_WAVES;  // routes per 256-thread chunk
 
 __device__ __forceinline__ int local_key(int32_t id, int E, int L, int off) {
   int loc = id - off;
@@ -33,25 +36,26 @@ __device__ __forceinline__ int local_key(int32_t id, int E, int L, int off) {
   return ok ? loc : L;  // L = foreign
 }
 
-__global__ __launch_bounds__(64) void k_sort_count(const int32_t* __restrict__ ids, int64_t n,
-                                                   int E, int L, int off, int nb,
-                                                   int32_t* __restrict__ cnt) {
+__global__ __launch_bounds__(256) void k_sort_count(const int32_t* __restrict__ ids, int64_t n,
+                                                    int E, int L, int off,
+                                                    int32_t* __restrict__ cnt) {
   extern __shared__ int32_t hist[];
-  const int lane = threadIdx.x;
-  for (int e = lane; e < L; e += 64) hist[e] = 0;
+  const int tid = threadIdx.x;
+  for (int e = tid; e < L; e += 256) hist[e] = 0;
   __syncthreads();
   const int64_t base = (int64_t)blockIdx.x * CHUNK;
-  int key[SORT_STEPS];  // all of the chunk's ids are requested before any is used
+  int key[SORT_STEPS];  // all of the thread's ids are requested before any is used
 #pragma unroll
   for (int step = 0; step < SORT_STEPS; ++step) {
-    const int64_t i = base + step * 64 + lane;
+    const int64_t i = base + step * 256 + tid;
     key[step] = i < n ? local_key(ids[i], E, L, off) : L;
   }
 #pragma unroll
   for (int step = 0; step < SORT_STEPS; ++step)
     if (key[step] < L) atomicAdd(&hist[key[step]], 1);
   __syncthreads();
-  for (int e = lane; e < L; e += 64) cnt[(int64_t)e * nb + blockIdx.x] = hist[e];
+  int32_t* row = cnt + (int64_t)blockIdx.x * L;
+  for (int e = tid; e < L; e += 256) row[e] = hist[e];
 }
 
 // Inclusive wave64 scan of an int.
@@ -65,30 +69,36 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
   return v;
 }
 
-__global__ __launch_bounds__(256) void k_sort_scan(int32_t* __restrict__ cnt, int nb,
-                                                   int32_t* __restrict__ total,
-                                                   int32_t* __restrict__ zero, int n_zero) {
-  __shared__ int wsum[4];
-  const int e = blockIdx.x;
-  if (e == 0)  // a buffer the caller wants cleared before the GEMMs (no extra launch)
-    for (int i = threadIdx.x; i < n_zero; i += 256) zero[i] = 0;
-  int32_t* col = cnt + (int64_t)e * nb;
-  const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
-  int carry = 0;
-  for (int c0 = 0; c0 < nb; c0 += 256) {
-    int b = c0 + tid;
-    int v = (b < nb) ? col[b] : 0;
-    int inc = wave_incl_scan(v);
-    if (lane == 63) wsum[wid] = inc;
-    __syncthreads();
-    int before = carry;
-    for (int w = 0; w < wid; ++w) before += wsum[w];
-    int chunk_total = wsum[0] + wsum[1] + wsum[2] + wsum[3];
-    if (b < nb) col[b] = before + inc - v;  // exclusive
-    carry += chunk_total;
-    __syncthreads();
+// Column prefixes of cnt [nb][L]: workgroup b owns experts 64 b .. 64 b + 63; thread
+// (slice s, expert lane) sums chunks [s * per, (s + 1) * per) of its column, the
+// slice sums are combined through LDS, and a second pass writes the exclusive prefix.
+constexpr int SCAN_SLICES = 16;
+__global__ __launch_bounds__(1024) void k_sort_scan(int32_t* __restrict__ cnt, int nb, int L,
+                                                    int32_t* __restrict__ total,
+                                                    int32_t* __restrict__ zero, int n_zero) {
+  __shared__ int ssum[SCAN_SLICES][64];
+  const int tid = threadIdx.x, el = tid & 63, sl = tid >> 6;
+  if (blockIdx.x == 0)  // a buffer the caller wants cleared before the GEMMs (no extra launch)
+    for (int i = tid; i < n_zero; i += 1024) zero[i] = 0;
+  const int e = blockIdx.x * 64 + el;
+  const int per = (nb + SCAN_SLICES - 1) / SCAN_SLICES;
+  const int c0 = sl * per, c1 = min(nb, c0 + per);
+  int part = 0;
+  if (e < L)
+    for (int c = c0; c < c1; ++c) part += cnt[(int64_t)c * L + e];
+  ssum[sl][el] = part;
+  __syncthreads();
+  int run = 0;
+  for (int s2 = 0; s2 < sl; ++s2) run += ssum[s2][el];
+  if (e < L) {
+    for (int c = c0; c < c1; ++c) {
+      int32_t* p = cnt + (int64_t)c * L + e;
+      const int v = *p;
+      *p = run;
+      run += v;
+    }
+    if (sl == SCAN_SLICES - 1) total[e] = run;
   }
-  if (tid == 0) total[e] = carry;
 }
 
 // Up to SB_MAX routes: the whole sort in one workgroup of 16 waves (one launch;
@@ -177,64 +187,91 @@ __global__ __launch_bounds__(1024) void k_sort_block(
   }
 }
 
-__global__ __launch_bounds__(64) void k_sort_scatter(
-    const int32_t* __restrict__ ids, int64_t n, int E, int L, int off, int nb,
+// Chunk c's scatter. Every workgroup scans the L expert totals itself (L <= 1024,
+// four per thread): cheaper than another launch.
+__global__ __launch_bounds__(256) void k_sort_scatter(
+    const int32_t* __restrict__ ids, int64_t n, int E, int L, int off,
     const int32_t* __restrict__ cnt, const int32_t* __restrict__ total,
     int32_t* __restrict__ offs, int32_t* __restrict__ m_indptr, int32_t* __restrict__ n_local,
     int32_t* __restrict__ e2p, int32_t* __restrict__ p2e) {
-  extern __shared__ int32_t run[];  // [L] next free row of each expert in this chunk
-  const int lane = threadIdx.x;
-  // exclusive scan of the expert totals: lane owns experts [lane*per, lane*per+per)
-  const int per = (L + 63) / 64;
-  int part = 0;
-  for (int j = 0; j < per; ++j) {
-    int e = lane * per + j;
-    if (e < L) part += total[e];
-  }
-  int excl = wave_incl_scan(part) - part;
-  for (int j = 0; j < per; ++j) {
-    int e = lane * per + j;
-    if (e < L) {
-      int te = total[e];
-      run[e] = excl + cnt[(int64_t)e * nb + blockIdx.x];
-      if (blockIdx.x == 0) {
-        offs[e] = excl + te;
-        if (m_indptr) m_indptr[e + 1] = excl + te;
-      }
-      excl += te;
-    }
-  }
-  if (blockIdx.x == 0 && lane == 63) {
-    *n_local = excl;  // lane 63 ends with the grand total
-    if (m_indptr) m_indptr[0] = 0;
-  }
-  __syncthreads();
-
-  int bits = 1;
-  while ((1 << bits) <= L) ++bits;  // keys 0..L fit
-  const uint64_t lt = (1ull << lane) - 1ull;
-  const int64_t base = (int64_t)blockIdx.x * CHUNK;
-  int keys[SORT_STEPS];  // all of the chunk's ids are requested before any is used
+  extern __shared__ int32_t sm[];
+  int32_t* run = sm;                        // [SORT_WAVES][L]: next row per wave and expert
+  int32_t* start = sm + SORT_WAVES * L;     // [L]
+  __shared__ int wsum[SORT_WAVES];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int64_t base = (int64_t)blockIdx.x * CHUNK + (int64_t)w * (CHUNK / SORT_WAVES);
+  int keys[SORT_STEPS];  // all of the wave's ids are requested before any is used
 #pragma unroll
   for (int step = 0; step < SORT_STEPS; ++step) {
     const int64_t i = base + step * 64 + lane;
     keys[step] = i < n ? local_key(ids[i], E, L, off) : L;
   }
+  for (int i = tid; i < SORT_WAVES * L; i += 256) run[i] = 0;
+  // exclusive scan of the expert totals: thread tid owns experts [4 tid, 4 tid + 4)
+  int tv[4], part = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = 4 * tid + j;
+    tv[j] = e < L ? total[e] : 0;
+    part += tv[j];
+  }
+  const int inc = wave_incl_scan(part);
+  if (lane == 63) wsum[w] = inc;
+  __syncthreads();
+  int excl = inc - part;
+  for (int v = 0; v < w; ++v) excl += wsum[v];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = 4 * tid + j;
+    if (e < L) {
+      start[e] = excl;
+      if (blockIdx.x == 0) {
+        offs[e] = excl + tv[j];
+        if (m_indptr) m_indptr[e + 1] = excl + tv[j];
+      }
+    }
+    excl += tv[j];
+  }
+  if (blockIdx.x == 0 && tid == 255) {
+    *n_local = excl;  // the last thread ends with the grand total
+    if (m_indptr) m_indptr[0] = 0;
+  }
+  // each wave's count of its quarter, per expert
+#pragma unroll
+  for (int step = 0; step < SORT_STEPS; ++step)
+    if (keys[step] < L) atomicAdd(&run[w * L + keys[step]], 1);
+  __syncthreads();
+  // first row of each (wave, expert): expert start + chunk prefix + earlier waves
+  const int32_t* pre = cnt + (int64_t)blockIdx.x * L;
+  for (int e = tid; e < L; e += 256) {
+    int acc = start[e] + pre[e];
+#pragma unroll
+    for (int v = 0; v < SORT_WAVES; ++v) {
+      const int h = run[v * L + e];
+      run[v * L + e] = acc;
+      acc += h;
+    }
+  }
+  __syncthreads();
+  int bits = 1;
+  while ((1 << bits) <= L) ++bits;  // keys 0..L fit
+  const uint64_t lt = (1ull << lane) - 1ull;
+  int32_t* myrun = run + w * L;
 #pragma unroll
   for (int step = 0; step < SORT_STEPS; ++step) {
-    int64_t i = base + step * 64 + lane;
-    bool valid = i < n;
-    int key = keys[step];
+    const int64_t i = base + step * 64 + lane;
+    const bool valid = i < n;
+    const int key = keys[step];
     uint64_t peers = __ballot(valid);
     for (int b = 0; b < bits; ++b) {
-      uint64_t m = __ballot((key >> b) & 1);
+      const uint64_t m = __ballot((key >> b) & 1);
       peers &= ((key >> b) & 1) ? m : ~m;
     }
-    int rank = __popcll(peers & lt);
+    const int rank = __popcll(peers & lt);
     int pos = -1;
-    if (valid && key < L) pos = run[key] + rank;
-    // one wave per block: its LDS accesses take effect in order, no barrier needed
-    if (valid && key < L && rank == 0) run[key] += __popcll(peers);
+    if (valid && key < L) pos = myrun[key] + rank;
+    // the wave alone uses its run row: its LDS accesses take effect in order
+    if (valid && key < L && rank == 0) myrun[key] += __popcll(peers);
     if (valid) {
       e2p[i] = pos;
       if (pos >= 0) p2e[pos] = (int32_t)i;
@@ -280,11 +317,11 @@ moe_status sort_enqueue(const int32_t* ids, int64_t T, int32_t k, int32_t E, int
   const int64_t nb = n_chunks(n);
   int32_t* cnt = reinterpret_cast<int32_t*>(ws);
   int32_t* total = cnt + L * nb;
-  const size_t lds = (size_t)L * sizeof(int32_t);
-  k_sort_count<<<(unsigned)nb, 64, lds, st>>>(ids, n, E, L, off, (int)nb, cnt);
-  k_sort_scan<<<(unsigned)L, 256, 0, st>>>(cnt, (int)nb, total, zero, zero ? n_zero : 0);
-  k_sort_scatter<<<(unsigned)nb, 64, lds, st>>>(ids, n, E, L, off, (int)nb, cnt, total, offs,
-                                                m_indptr, n_local, e2p, p2e);
+  k_sort_count<<<(unsigned)nb, 256, (size_t)L * sizeof(int32_t), st>>>(ids, n, E, L, off, cnt);
+  k_sort_scan<<<(unsigned)((L + 63) / 64), 1024, 0, st>>>(cnt, (int)nb, L, total, zero,
+                                                          zero ? n_zero : 0);
+  k_sort_scatter<<<(unsigned)nb, 256, (size_t)(SORT_WAVES + 1) * L * sizeof(int32_t), st>>>(
+      ids, n, E, L, off, cnt, total, offs, m_indptr, n_local, e2p, p2e);
   return launch_status();
 }
 

@@ -48,12 +48,12 @@ def test_host_side_errors_need_no_gpu(lib):
     assert lib.moe_route(None, 4, 8, 9, None, None, None) == 2          # k > E
     assert lib.moe_route(None, 4, 8, 2, None, None, None) == 1          # null
     assert lib.moe_route(None, 0, 8, 2, None, None, None) == 0          # T == 0: no-op
-    assert lib.grouped_gemm_fwd(None, None, None, 0, 4, 64, 100, 64, None, None) == 2   # N % 32
-    assert lib.grouped_gemm_fwd(None, None, None, 5, 4, 64, 64, 64, None, None) == 3    # offs kind
-    assert lib.grouped_gemm_fwd(None, None, None, 0, 4, 64, 64, 64, None, None) == 1    # null
+    assert lib.grouped_gemm_fwd(None, None, None, 0, 4, 64, 100, 64, None, None, 0, None) == 2   # N % 32
+    assert lib.grouped_gemm_fwd(None, None, None, 5, 4, 64, 64, 64, None, None, 0, None) == 3    # offs kind
+    assert lib.grouped_gemm_fwd(None, None, None, 0, 4, 64, 64, 64, None, None, 0, None) == 1    # null
     p = ctypes.c_void_p(16)
     q = ctypes.c_void_p(24)  # misaligned
-    assert lib.grouped_gemm_fwd(p, q, p, 0, 4, 64, 64, 64, p, None) == 4
+    assert lib.grouped_gemm_fwd(p, q, p, 0, 4, 64, 64, 64, p, None, 0, None) == 4
     assert lib.grouped_gemm_wgrad(p, p, p, 0, 4, 64, 64, 64, p, 7, None, 0, None) == 3  # out dtype
     assert lib.moe_finalize(None, None, None, 4, 2, 12, None, None) == 2  # H % 8
     assert lib.moe_sort(None, 4, 2, 8, 4, 6, None, None, None, None, None, None, 0, None) == 2  # L+off > E
