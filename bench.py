@@ -100,6 +100,9 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 512 MiB device-to-device copy (3x): the known-size "
                          "reference for rocprofv3 FETCH_SIZE / WRITE_SIZE counters")
+    ap.add_argument("--profile", choices=sorted(PROFILE_WORKLOADS),
+                    help="only run one workload a few times (3 warm-up, 5 measured calls), for "
+                         "rocprofv3 kernel traces and counters; prints its mean event time")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for {args.gpus}).",
@@ -114,6 +117,10 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes": n, "copies": 3}), flush=True)
+        return
+
+    if args.profile:
+        profile_workload(args.profile)
         return
 
     import numpy as np
@@ -367,9 +374,10 @@ def _mx_sweep(wfmt, flush, dev):
         if ms_graph is not None:
             sweep[str(Tw)]["graph_ms"] = round(ms_graph, 4)
         # the per-bucket tuner: time both tile families of FC1 / FC2 on this batch
-        choice = M.moe_tune_mx(dw["x"][:Tw], dw["x_sf"] if pt else dw["x_sf"][:Tw], idsw, wtsw,
-                               dw["w1"], dw["w1_sf"], dw["w2"], dw["w2_sf"], cw.num_experts,
-                               act_scale=dw["act_scale"] if pt else None, workspace=wsw)
+        choice = M.moe_tune(dw["x"][:Tw], idsw, wtsw, dw["w1"], dw["w2"], cw.num_experts,
+                            x_sf=dw["x_sf"] if pt else dw["x_sf"][:Tw], w1_sf=dw["w1_sf"],
+                            w2_sf=dw["w2_sf"], act_scale=dw["act_scale"] if pt else None,
+                            workspace=wsw)
         sweep[str(Tw)]["tuned_ms"] = round(_time(mx_step, reps=reps, flush=flush if small else None), 4)
         sweep[str(Tw)]["tuned_tiles"] = ["streaming" if ch else "256-row" for ch in choice]
         M.moe_tune_clear()
@@ -525,6 +533,136 @@ def secondary_measurements(progress):
     res["finalize_large"] = {"ms": round(ms_f, 4), "gbs": round(fb / (ms_f * 1e-3) / 1e9, 1),
                              "hbm_frac": round(fb / (ms_f * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
     return res
+
+
+def _profile_calls(name):
+    """(description, list of (label, fn)) of one profiling workload; every fn is one
+    library call (or a short chain) on inputs resident on the device."""
+    import numpy as np
+    import torch
+    import mixture_experts_expert_softmax_amd as M
+    import moe_synth as S
+    dev = "cuda"
+    if name in ("layer", "backward"):
+        c = S.mixtral_moe(seed=0)
+        x, w1, w2 = c.x.to(dev), c.w1.to(dev), c.w2.to(dev)
+        lg = torch.from_numpy(c.logits).to(dev)
+        ids, w = M.moe_route(lg, c.top_k)
+        srt = M.moe_sort(ids, c.num_experts)
+        ws = torch.empty(M.lib().moe_gemm_split_workspace_size(), dtype=torch.uint8, device=dev)
+        act = M.moe_fc1(x, w1, srt["offs"], srt["p2e"], c.top_k, c.num_experts, workspace=ws)
+        y = M.moe_fc2(act, w2, srt["offs"], c.T, c.top_k, c.num_experts, workspace=ws)
+        out = torch.empty((c.T, c.H), dtype=torch.bfloat16, device=dev)
+        if name == "backward":
+            import ctypes
+            dout = S.upstream_grad(0, c.T, c.H).to(dev)
+            _, saved = M.moe_ffn_forward_train(x, ids, w, w1, w2, c.num_experts)
+            d = M._train_desc(x, ids, w1, c.num_experts, None, 0, "swiglu")
+            bws = torch.empty(M.lib().moe_ffn_backward_workspace_size(ctypes.byref(d)),
+                              dtype=torch.uint8, device=dev)
+            return ("Mixtral-shaped layer backward (T=4096, H=4096, I=14336, 8 experts, top-2)",
+                    [("backward", lambda: M.moe_ffn_backward(dout, saved, x, ids, w, w1, w2,
+                                                             c.num_experts, workspace=bws))])
+        return ("Mixtral-shaped layer forward (T=4096, H=4096, I=14336, 8 experts, top-2)", [
+            ("route", lambda: M.moe_route(lg, c.top_k, ids, w)),
+            ("sort", lambda: M.moe_sort(ids, c.num_experts, out=srt)),
+            ("fc1", lambda: M.moe_fc1(x, w1, srt["offs"], srt["p2e"], c.top_k, c.num_experts,
+                                      act=act, workspace=ws)),
+            ("fc2", lambda: M.moe_fc2(act, w2, srt["offs"], c.T, c.top_k, c.num_experts, dst=y,
+                                      workspace=ws)),
+            ("finalize", lambda: M.moe_finalize(y, srt["e2p"], w, out=out)),
+            ("fc2_fused", lambda: M.moe_fc2(act, w2, srt["offs"], c.T, c.top_k, c.num_experts,
+                                            finalize="fused", p2e=srt["p2e"], topk_weights=w,
+                                            dst=out, workspace=ws))])
+    if name == "grouped_gemm":
+        c = S.grouped_gemm_case(seed=0)
+        x, g, w = c.x.to(dev), c.g.to(dev), c.w.to(dev)
+        offs = torch.from_numpy(c.offs).to(dev)
+        ws = torch.empty(M.lib().moe_gemm_split_workspace_size(), dtype=torch.uint8, device=dev)
+        yb = torch.empty((c.sum_m, 4096), dtype=torch.bfloat16, device=dev)
+        dxb = torch.empty((c.sum_m, 2048), dtype=torch.bfloat16, device=dev)
+        dwb = torch.empty((c.E, 4096, 2048), dtype=torch.bfloat16, device=dev)
+        dwf = torch.empty((c.E, 4096, 2048), dtype=torch.float32, device=dev)
+        return ("ragged grouped GEMM, 16 groups, sum_m=8192, K=2048, N=4096", [
+            ("fwd", lambda: M.grouped_gemm_fwd(x, w, offs, out=yb, workspace=ws)),
+            ("dgrad", lambda: M.grouped_gemm_dgrad(g, w, offs, out=dxb, workspace=ws)),
+            ("wgrad_bf16", lambda: M.grouped_gemm_wgrad(g, x, offs, out=dwb)),
+            ("wgrad_f32", lambda: M.grouped_gemm_wgrad(g, x, offs, out=dwf))])
+    if name == "expert_shard":
+        cs = S.expert_shard_moe(seed=0)
+        lg = torch.from_numpy(cs.logits).to(dev)
+        xs, w1s, w2s = cs.x.to(dev), cs.w1.to(dev), cs.w2.to(dev)
+        lim = torch.from_numpy(cs.limits).to(dev)
+        ids, wts = M.moe_route(lg, cs.top_k)
+        outs = torch.empty((cs.T, cs.H), dtype=torch.bfloat16, device=dev)
+        wsp = torch.empty(M.moe_ffn_workspace_size(cs.T, cs.H, cs.I, cs.num_experts, cs.top_k,
+                                                   cs.num_local, cs.local_offset, "swiglu_step"),
+                          dtype=torch.uint8, device=dev)
+        return ("expert shard T=8192, H=7168, I=2048, experts 64..95 of 256, top-8, SwiGLUStep", [
+            ("step", lambda: (M.moe_route(lg, cs.top_k, ids, wts),
+                              M.moe_ffn_forward(xs, ids, wts, w1s, w2s, cs.num_experts, cs.num_local,
+                                                cs.local_offset, "swiglu_step", lim, out=outs,
+                                                workspace=wsp)))])
+    if name.startswith("w4a8_"):
+        Tw = int(name.split("_")[1])
+        cw = S.w4a8_moe(seed=0, T=Tw, wfmt="mxfp4")
+        dw = {k_: torch.from_numpy(np.ascontiguousarray(getattr(cw, k_))).to(dev)
+              for k_ in ("x", "x_sf", "w1", "w1_sf", "w2", "w2_sf")}
+        lgw = torch.from_numpy(cw.logits).to(dev)
+        idsw, wtsw = M.moe_route(lgw, cw.top_k)
+        outw = torch.empty((Tw, cw.H), dtype=torch.bfloat16, device=dev)
+        wsw = torch.empty(M.moe_ffn_workspace_size(Tw, cw.H, cw.I, cw.num_experts, cw.top_k,
+                                                   weight_format="mxfp4"), dtype=torch.uint8, device=dev)
+        return (f"W4A8 layer T={Tw}, H=7168, I=2048, 64 experts, top-8 (MXFP4 weights, MXFP8 "
+                "activations)", [
+            ("step", lambda: (M.moe_route(lgw, cw.top_k, idsw, wtsw),
+                              M.moe_ffn_forward_mx(dw["x"], dw["x_sf"], idsw, wtsw, dw["w1"],
+                                                   dw["w1_sf"], dw["w2"], dw["w2_sf"], cw.num_experts,
+                                                   out=outw, workspace=wsw)))])
+    if name == "route_sort":
+        T2, E2, k2 = 262144, 256, 8
+        lg2 = torch.from_numpy(S.route_logits(np.random.default_rng(1), T2, E2)).to(dev)
+        ids2 = torch.empty((T2, k2), dtype=torch.int32, device=dev)
+        w2t = torch.empty((T2, k2), dtype=torch.float32, device=dev)
+        M.moe_route(lg2, k2, ids2, w2t)
+        ws2 = torch.empty(M.lib().moe_sort_workspace_size(T2, k2, E2), dtype=torch.uint8, device=dev)
+        so2 = M.moe_sort(ids2, E2, workspace=ws2)
+        return ("route + sort, T=262144, 256 experts, top-8", [
+            ("route", lambda: M.moe_route(lg2, k2, ids2, w2t)),
+            ("sort", lambda: M.moe_sort(ids2, E2, workspace=ws2, out=so2))])
+    if name == "finalize":
+        T3, H3, k3 = 65536, 7168, 8
+        e2p = torch.randperm(T3 * k3, device=dev).to(torch.int32)
+        yr = torch.randn((T3 * k3, H3), device=dev).to(torch.bfloat16)
+        w3 = torch.rand((T3, k3), device=dev)
+        o3 = torch.empty((T3, H3), dtype=torch.bfloat16, device=dev)
+        return ("finalize T=65536, H=7168, top-8", [
+            ("finalize", lambda: M.moe_finalize(yr, e2p, w3, out=o3))])
+    raise ValueError(name)
+
+
+PROFILE_WORKLOADS = ("layer", "backward", "grouped_gemm", "expert_shard", "w4a8_1024", "w4a8_8192",
+                     "route_sort", "finalize")
+
+
+def profile_workload(name, warmup=3, reps=5):
+    """Run one workload's calls warmup + reps times and print their mean event times."""
+    import torch
+    torch.cuda.set_device(0)
+    desc, calls = _profile_calls(name)
+    res = {}
+    for label, fn in calls:
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(reps):
+            fn()
+        e.record()
+        torch.cuda.synchronize()
+        res[label] = round(s.elapsed_time(e) / reps, 4)
+    print(json.dumps({"profile": name, "workload": desc, "mean_ms": res}), flush=True)
 
 
 if __name__ == "__main__":

@@ -36,7 +36,10 @@
  *   been enqueued, except MOE_ERR_HIP (a launch failed after earlier launches of
  *   the same call were enqueued). Nothing throws, aborts or prints.
  * - Calls keep no state between invocations; concurrent calls on different
- *   streams are safe when their outputs and workspaces are distinct.
+ *   streams are safe when their outputs and workspaces are distinct. Exceptions:
+ *   moe_tune (which also synchronises its stream) records tile choices in a
+ *   per-process table that moe_tune_clear empties and the GEMM stages read, and
+ *   moe_ffn_forward_noalloc uses one fixed scratch array per device.
  */
 #ifndef MOE_MI355X_H
 #define MOE_MI355X_H
@@ -73,13 +76,13 @@ typedef int32_t moe_status;
 #define MOE_FINALIZE_FUSED         1  /* FC2 epilogue adds w*y into a zeroed output with bf16 atomics */
 #define MOE_FINALIZE_NONE          2  /* stop after FC2: return y rows and e2p ([StepFun] do_finalize=False) */
 
-/* Number formats of moe_ffn_forward's operands ([W4A8] "Inputs"). */
+/* Number formats of moe_ffn_forward's operands ([W4A8] Host plan, Inputs). */
 #define MOE_WFMT_BF16  0  /* x, w1, w2 in bf16 */
 #define MOE_WFMT_MXFP4 1  /* w1, w2 MXFP4 (e2m1 pairs + UE8M0 per 32), x MXFP8 (e4m3 + UE8M0 per 32);
                              the FC1 output is requantized to MXFP8 with the round-up rule */
 #define MOE_WFMT_MXFP8 2  /* as MXFP4 but w1, w2 MXFP8: one e4m3fn code byte per element, UE8M0
                              per 32 ([StepFun] intro lists mxfp8 among the weight families) */
-#define MOE_WFMT_FP8   3  /* fp8 with per-tensor scales ([StepFun] intro: "fp8 (per-tensor)"):
+#define MOE_WFMT_FP8   3  /* fp8 with per-tensor scales ([StepFun] intro: its list of weight families):
                              x, w1, w2 e4m3fn code bytes; x_sf -> float x_scale [1], w1_sf ->
                              float w1_scale [L], w2_sf -> float w2_scale [L] (value = code value *
                              scale); the FC1 output is requantized with the caller's static
@@ -231,8 +234,8 @@ moe_status moe_ffn_forward_noalloc(const moe_ffn_desc* desc, const moe_ffn_tenso
                                    void* stream);
 
 /*
- * The two GEMM stages of moe_ffn_forward as separate calls ([StepFun] "One-shot
- * functions": fc1, fc2), for callers that run routing, sort and finalize
+ * The two GEMM stages of moe_ffn_forward as separate calls ([StepFun] One-shot
+ * functions: fc1, fc2), for callers that run routing, sort and finalize
  * themselves. `offs` [L] and `p2e` come from moe_sort over the same topk_ids;
  * rows are in permuted (expert-sorted) order and only the first offs[L-1] rows
  * are touched; row capacity is T*top_k.
@@ -263,7 +266,7 @@ moe_status moe_fc2(const moe_ffn_desc* desc, const void* act, const void* w2,
                    void* ws, size_t ws_bytes, void* stream);
 
 /*
- * The block-scaled stages ([W4A8] "Inputs"; intro: fp32 accumulation, UE8M0
+ * The block-scaled stages ([W4A8] Host plan, Inputs; intro: fp32 accumulation, UE8M0
  * round-up requantization). desc->weight_format must be MOE_WFMT_MXFP4 (W4A8) or
  * MOE_WFMT_MXFP8 (w1 / w2 as e4m3fn code bytes, same scale layout); otherwise
  * MOE_ERR_DTYPE.
@@ -281,29 +284,38 @@ moe_status moe_fc2_mx(const moe_ffn_desc* desc, const void* act, const void* act
                       void* stream);
 
 /*
- * moe_tune_mx -- per-bucket tile choice for the fp8-activation GEMM stages ([SM90]
- * Parameters: the autotuner profiles the legal tiles per token bucket and caches
- * the winner). For the layer described by desc / tensors (weight_format MXFP4,
- * MXFP8 or FP8; x, x_sf, topk_ids, w1, w1_sf, w2, w2_sf, act_scale, clamp_limit
- * read), it sorts the routes, then times FC1 and FC2 with each tile family -- the
- * 256-row tile and, where the shape allows it, the 32-row streaming tile -- one
- * warm-up and 3 timed launches each, and records the faster family under (stage,
- * weight format, H, I, L, rows per local expert rounded up to a power of two).
- * Later launches of that stage, shape and bucket, by any entry point of this
- * process, use the recorded family; everything else keeps the built-in rule (the
- * streaming tile below 32 rows per expert for FC1 and 24 for FC2). choice
- * (optional, [2]) receives the FC1 / FC2 picks: 1 streaming, 0 256-row.
- * Unlike every other entry point this call synchronises the stream (it is a tuning
- * step, not a prepared launch); ws as moe_ffn_workspace_size for the same desc
- * with MOE_FINALIZE_DETERMINISTIC. Thread-safe; results are per process.
- * moe_tune_clear forgets every recorded choice.
+ * moe_tune -- per-bucket tile choice for the layer's two GEMM stages ([SM90]
+ * Parameters: the autotuner profiles the legal tiles per token bucket and caches the
+ * winner; tile_size follows the rows per expert). For the layer described by desc /
+ * tensors (any weight_format; x, topk_ids, w1, w2, clamp_limit and, for the
+ * fp8-activation formats, x_sf, w1_sf, w2_sf, act_scale are read), it sorts the
+ * routes, then times FC1 and FC2 with each tile family -- bf16: the 256-row tile and
+ * the 128-row tile (when the stage's contraction is a multiple of 64); MXFP4 / MXFP8 /
+ * FP8: the 256-row tile and, where the shape allows it, the 32-row streaming tile --
+ * one warm-up and 3 timed launches each, and records the faster family under (stage,
+ * weight format, H, I, L, rows per local expert rounded up to a power of two). Later
+ * launches of that stage, shape and bucket, by any entry point of this process
+ * (moe_ffn_forward and its variants, moe_fc1 / moe_fc2 and the fp8-activation stages),
+ * use the recorded family; everything else keeps the built-in rule (bf16: the 128-row
+ * tile when T * top_k <= 64 * num_experts, else the 256-row tile; fp8 activations: the
+ * streaming tile below 32 rows per expert for FC1 and 24 for FC2). choice (optional, [2]) receives the FC1 / FC2 picks: 1 the smaller family
+ * (128-row or streaming), 0 the 256-row tile.
+ * This call and moe_tune_clear are the exceptions to the conventions above: moe_tune
+ * synchronises the stream (it is a tuning step, not a prepared launch) and both act on a
+ * per-process table, which the other entry points only read. ws as
+ * moe_ffn_workspace_size for the same desc with MOE_FINALIZE_DETERMINISTIC.
+ * Thread-safe. moe_tune_clear forgets every recorded choice.
  */
-moe_status moe_tune_mx(const moe_ffn_desc* desc, const moe_ffn_tensors* tensors, void* ws,
-                       size_t ws_bytes, void* stream, int32_t* choice);
+moe_status moe_tune(const moe_ffn_desc* desc, const moe_ffn_tensors* tensors, void* ws,
+                    size_t ws_bytes, void* stream, int32_t* choice);
+/* moe_tune_set records a choice (0 / 1 as above) for stage 1 (FC1) or 2 (FC2) of the
+ * shape and bucket that desc describes, as moe_tune would after timing it: for callers
+ * that keep tuned choices across processes, and for tests of each family. */
+moe_status moe_tune_set(const moe_ffn_desc* desc, int32_t stage, int32_t choice);
 void moe_tune_clear(void);
 
 /*
- * The fp8 per-tensor stages ([StepFun] intro: "fp8 (per-tensor)" weight family);
+ * The fp8 per-tensor stages ([StepFun] intro: the per-tensor fp8 weight family);
  * desc->weight_format must be MOE_WFMT_FP8, otherwise MOE_ERR_DTYPE. x, w1, w2, act
  * are e4m3fn code bytes; x_scale [1], w1_scale / w2_scale [L] and act_scale [1] are
  * float32 device values (value = code value * scale). fp32 accumulation.

@@ -24,7 +24,7 @@ __all__ = [
     "moe_finalize", "moe_fc1", "moe_fc2", "status_string", "ACT", "FINALIZE", "WFMT",
     "moe_ffn_forward_mx", "moe_fc1_mx", "moe_fc2_mx", "moe_ffn_forward_fp8", "moe_fc1_fp8",
     "moe_fc2_fp8", "moe_ffn_forward_train", "moe_ffn_backward", "moe_route_backward", "MoEFunction",
-    "moe_tune_mx", "moe_tune_clear", "moe_bgmv", "moe_ffn_forward_noalloc", "NOALLOC_SCRATCH_BYTES",
+    "moe_tune", "moe_tune_set", "moe_tune_clear", "moe_bgmv", "moe_ffn_forward_noalloc", "NOALLOC_SCRATCH_BYTES",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -94,8 +94,9 @@ EXPORTS = {
     "moe_ffn_backward": (_i32, [ctypes.POINTER(MoeFfnDesc), ctypes.POINTER(MoeFfnTensors),
                                 ctypes.POINTER(MoeFfnGrads), _vp, _sz, _vp, _sz, _vp]),
     "moe_route_backward": (_i32, [_vp, _vp, _vp, _i64, _i32, _i32, _vp, _vp]),
-    "moe_tune_mx": (_i32, [ctypes.POINTER(MoeFfnDesc), ctypes.POINTER(MoeFfnTensors), _vp, _sz, _vp, _vp]),
+    "moe_tune": (_i32, [ctypes.POINTER(MoeFfnDesc), ctypes.POINTER(MoeFfnTensors), _vp, _sz, _vp, _vp]),
     "moe_tune_clear": (None, []),
+    "moe_tune_set": (_i32, [ctypes.POINTER(MoeFfnDesc), _i32, _i32]),
     "moe_bgmv_workspace_size": (_sz, [ctypes.POINTER(MoeBgmvDesc)]),
     "moe_bgmv": (_i32, [ctypes.POINTER(MoeBgmvDesc), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64,
                         _vp, _sz, _vp]),
@@ -605,35 +606,49 @@ def _ffn_forward_fp8act(wfmt, x, x_sf, topk_ids, topk_weights, w1, w1_sf, w2, w2
     return out
 
 
-def moe_tune_mx(x, x_sf, topk_ids, topk_weights, w1, w1_sf, w2, w2_sf, num_experts,
-                num_local_experts=None, local_expert_offset=0, activation="swiglu", clamp_limit=None,
-                act_scale=None, workspace=None):
-    """Times both tile families of the fp8-activation FC1 / FC2 on these inputs and records
-    the faster one for this shape and token bucket (synchronises). Arguments as
-    moe_ffn_forward_mx (or moe_ffn_forward_fp8 with act_scale). Returns (fc1, fc2) picks:
-    1 = 32-row streaming tile, 0 = 256-row tile."""
+def moe_tune(x, topk_ids, topk_weights, w1, w2, num_experts, num_local_experts=None,
+             local_expert_offset=0, activation="swiglu", clamp_limit=None, x_sf=None, w1_sf=None,
+             w2_sf=None, act_scale=None, workspace=None):
+    """Times both tile families of the layer's FC1 / FC2 on these inputs and records the
+    faster one for this shape and token bucket (synchronises). bf16 operands (x bf16) or
+    the operands of moe_ffn_forward_mx (x_sf, w1_sf, w2_sf) / moe_ffn_forward_fp8 (x_sf,
+    w1_sf, w2_sf holding x_scale, w1_scale, w2_scale, plus act_scale). Returns the (fc1,
+    fc2) picks: 1 = the smaller family (128-row bf16 tile or 32-row streaming tile), 0 =
+    the 256-row tile."""
     T, H = x.shape
     L, twoI, _ = w1.shape
     I = twoI // 2
-    wfmt = "fp8" if act_scale is not None else _mx_format(w1.shape[2], H, "w1")
+    if x.dtype == torch.bfloat16:
+        wfmt = "bf16"
+    else:
+        wfmt = "fp8" if act_scale is not None else _mx_format(w1.shape[2], H, "w1")
     k = topk_ids.shape[1]
     d = _ffn_desc(T, H, I, num_experts, L, local_expert_offset, k, activation, "deterministic", wfmt)
     h = lib()
     if workspace is None:
         workspace = torch.empty(max(h.moe_ffn_workspace_size(ctypes.byref(d)), 16), dtype=torch.uint8,
                                 device=x.device)
-    tens = MoeFfnTensors(x.data_ptr(), topk_ids.data_ptr(), topk_weights.data_ptr(), w1.data_ptr(),
-                         w2.data_ptr(), None if clamp_limit is None else clamp_limit.data_ptr(),
-                         None, None, None, x_sf.data_ptr(), w1_sf.data_ptr(), w2_sf.data_ptr(),
-                         None if act_scale is None else act_scale.data_ptr())
+    p = lambda t_: None if t_ is None else t_.data_ptr()  # noqa: E731
+    tens = MoeFfnTensors(p(x), p(topk_ids), p(topk_weights), p(w1), p(w2), p(clamp_limit), None, None,
+                         None, p(x_sf), p(w1_sf), p(w2_sf), p(act_scale))
     choice = (ctypes.c_int32 * 2)(-1, -1)
-    _check("moe_tune_mx", h.moe_tune_mx(ctypes.byref(d), ctypes.byref(tens), _ptr(workspace),
-                                        workspace.numel(), _stream(), choice))
+    _check("moe_tune", h.moe_tune(ctypes.byref(d), ctypes.byref(tens), _ptr(workspace),
+                                  workspace.numel(), _stream(), choice))
     return int(choice[0]), int(choice[1])
 
 
+def moe_tune_set(T, H, I, num_experts, top_k, stage, choice, num_local_experts=None,
+                 local_expert_offset=0, weight_format="bf16"):
+    """Record a tile family for one stage (1 = FC1, 2 = FC2) of this shape and token
+    bucket, as moe_tune would after timing: 1 = the smaller family, 0 = the 256-row tile."""
+    L = num_experts if num_local_experts is None else num_local_experts
+    d = _ffn_desc(T, H, I, num_experts, L, local_expert_offset, top_k, "swiglu", "deterministic",
+                  weight_format)
+    _check("moe_tune_set", lib().moe_tune_set(ctypes.byref(d), stage, choice))
+
+
 def moe_tune_clear():
-    """Forget every tile choice recorded by moe_tune_mx."""
+    """Forget every tile choice recorded by moe_tune / moe_tune_set."""
     lib().moe_tune_clear()
 
 

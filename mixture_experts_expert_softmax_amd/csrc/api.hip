@@ -19,7 +19,7 @@ moe_status gemm_nt_enqueue(int epi, const void* A, const int32_t* a_gather, int 
                            int K, void* C, int64_t ldc, int I, const float* limits,
                            float def_limit, const float* route_w, const int32_t* p2e, int top_k,
                            hipStream_t st, void* split_ws = nullptr,
-                           int32_t* split_cnt = nullptr, void* h_out = nullptr);
+                           int32_t* split_cnt = nullptr, void* h_out = nullptr, int tm = 256);
 moe_status gemm_dgrad_enqueue(const void* G, const void* W, const int32_t* ends, int E, int64_t M,
                               int N, int K, void* DX, hipStream_t st, int act = 0,
                               const void* h = nullptr, const float* limits = nullptr,
@@ -45,6 +45,7 @@ moe_status mx_fc2_enqueue(int wf, const void* act, const void* act_sf, const voi
 bool mx_small_possible(int stage, int wf, int H, int I, int64_t R);
 // defined in tune.hip
 void tune_store(int stage, int wf, int K, int NB, int L, int64_t R, int choice);
+int tune_lookup(int stage, int wf, int K, int NB, int L, int64_t R);
 
 int device_cu_count() {
   static int cached[64] = {0};
@@ -254,34 +255,51 @@ static moe_status check_ffn(const moe_ffn_desc* d) {
   return MOE_OK;
 }
 
+// Tile family of the bf16 FC1 (stage 1) and FC2 (stage 2): activation rows per tile,
+// 256 or 128. force 0 / 1 picks 256 / 128; otherwise a choice recorded by moe_tune for
+// this stage, shape and bucket, else the built-in rule: 128-row tiles when the routes
+// spread evenly would give each expert at most 64 rows (measured at H = 4096 / 7168:
+// 2-4% faster there, 6-13% slower at 256 and 1024 rows per expert).
+constexpr int TUNE_BF16 = -1;   // weight-format key of the bf16 stages in the tune table
+static int bf16_tile_rows(const moe_ffn_desc* d, int stage, int K, int NB, int L, int64_t R,
+                          int force) {
+  if (force < 0) force = tune_lookup(stage, TUNE_BF16, K, NB, L, R);
+  if (force < 0) force = R <= (int64_t)64 * d->num_experts ? 1 : 0;
+  return force == 1 ? 128 : 256;
+}
+
 // FC1 over gathered token rows; the activation runs in the GEMM epilogue.
 static moe_status fc1_enqueue(const moe_ffn_desc* d, const void* x, const void* w1,
                               const float* limits, const int32_t* offs, const int32_t* p2e,
                               void* act, hipStream_t st, void* split_ws = nullptr,
-                              int32_t* split_cnt = nullptr, void* h_out = nullptr) {
+                              int32_t* split_cnt = nullptr, void* h_out = nullptr,
+                              int force = -1) {
   const int32_t L = d->num_local_experts > 0 ? d->num_local_experts : d->num_experts;
   const int64_t R = d->T * d->top_k;
   const int epi = d->activation == MOE_ACT_SWIGLU_STEP ? EPI_SWIGLU_STEP : EPI_SWIGLU;
   return gemm_nt_enqueue(epi, x, p2e, d->top_k, w1, 2 * d->I, L, offs, R, d->I, d->H, act, d->I,
                          d->I, limits, 7.0f, nullptr, nullptr, d->top_k, st, split_ws, split_cnt,
-                         h_out);
+                         h_out, bf16_tile_rows(d, 1, d->H, 2 * d->I, L, R, force));
 }
 
 // FC2: unscaled rows in permuted order, or the fused scaled scatter-add into out.
 static moe_status fc2_enqueue(const moe_ffn_desc* d, const void* act, const void* w2,
                               const int32_t* offs, const int32_t* p2e, const float* topk_weights,
                               void* dst, hipStream_t st, void* split_ws = nullptr,
-                              int32_t* split_cnt = nullptr) {
+                              int32_t* split_cnt = nullptr, int force = -1) {
   const int32_t L = d->num_local_experts > 0 ? d->num_local_experts : d->num_experts;
   const int64_t R = d->T * d->top_k;
+  const int tm = bf16_tile_rows(d, 2, d->I, d->H, L, R, force);
   if (d->finalize_mode == MOE_FINALIZE_FUSED) {
     moe_status s = zero_fill(dst, (size_t)d->T * d->H * 2, st);
     if (s != MOE_OK) return s;
     return gemm_nt_enqueue(EPI_FUSED, act, nullptr, 1, w2, d->H, L, offs, R, d->H, d->I, dst, d->H,
-                           0, nullptr, 0.f, topk_weights, p2e, d->top_k, st, split_ws, split_cnt);
+                           0, nullptr, 0.f, topk_weights, p2e, d->top_k, st, split_ws, split_cnt,
+                           nullptr, tm);
   }
   return gemm_nt_enqueue(EPI_STORE, act, nullptr, 1, w2, d->H, L, offs, R, d->H, d->I, dst, d->H, 0,
-                         nullptr, 0.f, nullptr, nullptr, d->top_k, st, split_ws, split_cnt);
+                         nullptr, 0.f, nullptr, nullptr, d->top_k, st, split_ws, split_cnt, nullptr,
+                         tm);
 }
 
 extern "C" size_t moe_ffn_workspace_size(const moe_ffn_desc* d) {
@@ -506,11 +524,16 @@ struct TuneCtx {
   void* y;
   hipStream_t st;
   int force;
+  void* split_ws;        // bf16 stages: the layer's split-tile workspace
+  int32_t* split_cnt;
 };
 
 static moe_status tune_fc1(void* p) {
   const TuneCtx& c = *reinterpret_cast<TuneCtx*>(p);
   const int32_t L = c.d->num_local_experts > 0 ? c.d->num_local_experts : c.d->num_experts;
+  if (c.d->weight_format == MOE_WFMT_BF16)
+    return fc1_enqueue(c.d, c.t->x, c.t->w1, c.t->clamp_limit, c.offs, c.p2e, c.act, c.st,
+                       c.split_ws, c.split_cnt, nullptr, c.force);
   return mx_fc1_enqueue(c.d->activation, mx_wf(c.d->weight_format), c.t->x, c.t->x_sf, c.p2e,
                         c.d->top_k, c.t->w1, c.t->w1_sf, L, c.offs, c.d->T * c.d->top_k, c.d->H,
                         c.d->I, c.t->clamp_limit, c.act, c.act_sf, c.t->act_scale, c.st, c.force);
@@ -519,19 +542,36 @@ static moe_status tune_fc1(void* p) {
 static moe_status tune_fc2(void* p) {
   const TuneCtx& c = *reinterpret_cast<TuneCtx*>(p);
   const int32_t L = c.d->num_local_experts > 0 ? c.d->num_local_experts : c.d->num_experts;
+  if (c.d->weight_format == MOE_WFMT_BF16)
+    return fc2_enqueue(c.d, c.act, c.t->w2, c.offs, nullptr, nullptr, c.y, c.st, c.split_ws,
+                       c.split_cnt, c.force);
   return mx_fc2_enqueue(mx_wf(c.d->weight_format), c.act, c.act_sf_in, c.t->w2, c.t->w2_sf, L,
                         c.offs, c.d->T * c.d->top_k, c.d->H, c.d->I, c.y, c.st, c.force);
 }
 
-extern "C" moe_status moe_tune_mx(const moe_ffn_desc* d, const moe_ffn_tensors* t, void* ws,
-                                  size_t ws_bytes, void* stream, int32_t* choice) {
+extern "C" moe_status moe_tune_set(const moe_ffn_desc* d, int32_t stage, int32_t choice) {
   moe_status s = check_ffn(d);
   if (s != MOE_OK) return s;
-  if (!is_mx(d->weight_format)) return MOE_ERR_DTYPE;
+  if ((stage != 1 && stage != 2) || (choice != 0 && choice != 1)) return MOE_ERR_SHAPE;
+  const int32_t L = d->num_local_experts > 0 ? d->num_local_experts : d->num_experts;
+  const int64_t R = d->T * d->top_k;
+  const int wf = is_mx(d->weight_format) ? mx_wf(d->weight_format) : TUNE_BF16;
+  if (stage == 1)
+    tune_store(1, wf, d->H, 2 * d->I, L, R, choice);
+  else
+    tune_store(2, wf, d->I, d->H, L, R, choice);
+  return MOE_OK;
+}
+
+extern "C" moe_status moe_tune(const moe_ffn_desc* d, const moe_ffn_tensors* t, void* ws,
+                               size_t ws_bytes, void* stream, int32_t* choice) {
+  moe_status s = check_ffn(d);
+  if (s != MOE_OK) return s;
+  const bool mx = is_mx(d->weight_format);
   if (!t) return MOE_ERR_NULL;
   if (d->T == 0) return MOE_OK;
-  if (!t->x || !t->topk_ids || !t->w1 || !t->w2 || !t->x_sf || !t->w1_sf || !t->w2_sf)
-    return MOE_ERR_NULL;
+  if (!t->x || !t->topk_ids || !t->w1 || !t->w2) return MOE_ERR_NULL;
+  if (mx && (!t->x_sf || !t->w1_sf || !t->w2_sf)) return MOE_ERR_NULL;
   if (d->weight_format == MOE_WFMT_FP8 && !t->act_scale) return MOE_ERR_NULL;
   if (!aligned16(t->x) || !aligned16(t->w1) || !aligned16(t->w2)) return MOE_ERR_ALIGN;
   // the layer's workspace, with room for the FC2 rows (DETERMINISTIC layout)
@@ -542,20 +582,25 @@ extern "C" moe_status moe_tune_mx(const moe_ffn_desc* d, const moe_ffn_tensors* 
   hipStream_t st = as_stream(stream);
   const int32_t L = d->num_local_experts > 0 ? d->num_local_experts : d->num_experts;
   const int64_t R = d->T * d->top_k;
-  const int wf = mx_wf(d->weight_format);
+  const int wf = mx ? mx_wf(d->weight_format) : TUNE_BF16;
   char* w = reinterpret_cast<char*>(ws);
   int32_t* offs = reinterpret_cast<int32_t*>(w + l.offs);
   int32_t* p2e = reinterpret_cast<int32_t*>(w + l.p2e);
+  int32_t* split_cnt = mx ? nullptr : reinterpret_cast<int32_t*>(w + l.split_cnt);
   s = sort_enqueue(t->topk_ids, d->T, d->top_k, d->num_experts, L, d->local_expert_offset, offs,
                    nullptr, reinterpret_cast<int32_t*>(w + l.e2p), p2e,
-                   reinterpret_cast<int32_t*>(w + l.n_local), w + l.sort_ws, st);
+                   reinterpret_cast<int32_t*>(w + l.n_local), w + l.sort_ws, st, split_cnt,
+                   mx ? 0 : SPLIT_SLOTS);
   if (s != MOE_OK) return s;
-  TuneCtx c{d, t, offs, p2e, w + l.act, w + l.act_sf,
+  TuneCtx c{&dd, t, offs, p2e, w + l.act, w + l.act_sf,
             block_scaled(d->weight_format) ? (const void*)(w + l.act_sf) : (const void*)t->act_scale,
-            w + l.y, st, 0};
+            w + l.y, st, 0, mx ? nullptr : w + l.split, split_cnt};
   for (int stage = 1; stage <= 2; ++stage) {
     int best = 0;
-    if (mx_small_possible(stage, wf, d->H, d->I, R)) {
+    // the candidates: the 256-row tile and the streaming tile (fp8 activations) or the
+    // 128-row tile (bf16), where the shape allows it
+    if (mx ? mx_small_possible(stage, wf, d->H, d->I, R)
+           : (stage == 1 ? d->H : d->I) % 64 == 0) {
       float ms[2];
       for (int f = 0; f < 2; ++f) {
         c.force = f;

@@ -76,6 +76,7 @@ struct NtArgs {
   float* split_ws;           // split tiles: fp32 partial tiles [SPLIT_SLOTS][TB * TB]
   int32_t* split_cnt;        // split tiles: arrival counters, 0 between launches
   int n_res;                 // workgroups resident at once (0: never split)
+  bool mmajor;               // deal tiles column tile first (deal_tile_split)
 };
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
@@ -88,11 +89,15 @@ __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast
 // tile i is workgroup full + 8 * ((i / 8) * S + p) + i % 8, so all parts of a
 // tile share one XCD. slot = i * S + p indexes the partial-tile buffer, cidx = i
 // the arrival counter.
+// With mmajor the tiles are numbered column tile first (every group's row blocks of
+// column tile 0, then of column tile 1, ...) instead of group first, so that the
+// workgroups in flight on an XCD cover one band of output columns.
+template <int TM = TB>
 __device__ __forceinline__ bool deal_tile_split(const int32_t* ends, int E, int m_cap, int n_tiles,
                                                 int n_res, int ktiles, int& e, int& m0, int& mend,
                                                 int& nt, int& k0, int& nk, int& part, int& S,
-                                                int& slot, int& cidx) {
-  const int total = tile_count<TB>(ends, E, m_cap, n_tiles);
+                                                int& slot, int& cidx, bool mmajor = false) {
+  const int total = tile_count<TM>(ends, E, m_cap, n_tiles);
   const int b = (int)blockIdx.x;
   int full = total, rem = 0;
   S = 1;
@@ -124,7 +129,14 @@ __device__ __forceinline__ bool deal_tile_split(const int32_t* ends, int E, int 
     slot = i * S + part;
     cidx = i;
   }
-  tile_locate<TB>(ends, E, m_cap, n_tiles, t, e, m0, mend, nt);
+  if (mmajor) {
+    const int rb = total / n_tiles;   // row blocks over all groups
+    int unused;
+    tile_locate<TM>(ends, E, m_cap, 1, t % rb, e, m0, mend, unused);
+    nt = t / rb;
+  } else {
+    tile_locate<TM>(ends, E, m_cap, n_tiles, t, e, m0, mend, nt);
+  }
   k0 = ktiles * part / S;
   nk = ktiles * (part + 1) / S - k0;
   return true;
@@ -484,15 +496,18 @@ __device__ __forceinline__ void mainloop_dma_g(const SA& sa, const SB& sb, uint4
 // ---------------------------------------------------------------------------
 // fwd / FC1 / FC2: both operands contiguous along the contraction.
 // ---------------------------------------------------------------------------
-template <int EPI, bool KFULL>
+// TM: activation rows per tile, 256 or (full-K path only) 128 -- the family for few
+// rows per expert, where each row-wave takes 64 rows (two 32-row blocks).
+template <int EPI, bool KFULL, int TM = TB>
 __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_nt(NtArgs a) {
+  static_assert(TM == TB || (TM == 128 && KFULL), "128-row tiles need whole 64-deep stages");
   // 128 KB: two 64-deep stages [A tile | B tile], or the full-K path's four 32-deep ones
   __shared__ uint4 smem[4 * TILE_U4];
   const int ktiles = (a.K + TK - 1) / TK;
   int e, m0, mend, nt, k0 = 0, nk = ktiles, part = 0, S = 1, slot = 0, cidx = 0;
   if (KFULL) {
-    if (!deal_tile_split(a.ends, a.E, a.m_cap, a.n_tiles, a.n_res, ktiles, e, m0, mend, nt, k0,
-                         nk, part, S, slot, cidx))
+    if (!deal_tile_split<TM>(a.ends, a.E, a.m_cap, a.n_tiles, a.n_res, ktiles, e, m0, mend, nt,
+                             k0, nk, part, S, slot, cidx, a.mmajor))
       return;
   } else {
     if (!deal_tile<TB>(a.ends, a.E, a.m_cap, a.n_tiles, e, m0, mend, nt)) return;
@@ -566,6 +581,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_nt(NtArgs a) {
     if (mend - m0 <= 64) {   // a short last tile of its group: a quarter of the work
       jn = 1;
       mainloop_dma_g<false, false, 1>(sw, sx, smem, k0 * TK, nk * 2, tid, lane, wn, wm, acc);
+    } else if (TM == 128) {
+      jn = 2;
+      mainloop_dma_g<false, false, 2>(sw, sx, smem, k0 * TK, nk * 2, tid, lane, wn, wm, acc);
     } else {
       mainloop_dma_g<false, false, 4>(sw, sx, smem, k0 * TK, nk * 2, tid, lane, wn, wm, acc);
     }
@@ -868,7 +886,7 @@ inline int round_up8(int64_t v) { return (int)((v + 7) / 8 * 8); }
 // Upper bound on the row blocks of ragged groups: sum_e ceil(m_e/256) <= floor(M/256) + E.
 // Row blocks over E groups holding M rows in all: at most one partial block per
 // non-empty group, and there are at most min(E, M) of those.
-int row_block_bound(int64_t M, int E) { return (int)(M / TB + (M < E ? M : E)); }
+int row_block_bound(int64_t M, int E, int tm = TB) { return (int)(M / tm + (M < E ? M : E)); }
 
 moe_status zero_fill(void* p, size_t bytes, hipStream_t st) {
   if (bytes == 0) return MOE_OK;
@@ -879,11 +897,14 @@ moe_status zero_fill(void* p, size_t bytes, hipStream_t st) {
 }
 
 // C[rows, N] (bf16) = rows of A [*, K] times W[e]^T for ragged groups, with an epilogue.
+// tm: activation rows per tile, 256 or 128 (128 only when K is a multiple of 64;
+// otherwise 256 is used)
 moe_status gemm_nt_enqueue(int epi, const void* A, const int32_t* a_gather, int a_div,
                            const void* B, int NB, int E, const int32_t* ends, int64_t M, int N,
                            int K, void* C, int64_t ldc, int I, const float* limits,
                            float def_limit, const float* route_w, const int32_t* p2e, int top_k,
-                           hipStream_t st, void* split_ws, int32_t* split_cnt, void* h_out) {
+                           hipStream_t st, void* split_ws, int32_t* split_cnt, void* h_out,
+                           int tm) {
   if (M == 0) return MOE_OK;
   NtArgs a;
   a.A = reinterpret_cast<const uint16_t*>(A);
@@ -899,7 +920,9 @@ moe_status gemm_nt_enqueue(int epi, const void* A, const int32_t* a_gather, int 
   a.K = K;
   const bool fc1 = (epi == EPI_SWIGLU || epi == EPI_SWIGLU_STEP);
   a.n_tiles = fc1 ? (I + 127) / 128 : (N + TB - 1) / TB;
-  a.m_tiles = row_block_bound(M, E);
+  const bool kfull = (K % TK) == 0;
+  if (tm != 128 || !kfull) tm = TB;
+  a.m_tiles = row_block_bound(M, E, tm);
   a.C = reinterpret_cast<uint16_t*>(C);
   a.ldc = ldc;
   a.I = I;
@@ -909,10 +932,18 @@ moe_status gemm_nt_enqueue(int epi, const void* A, const int32_t* a_gather, int 
   a.p2e = p2e;
   a.top_k = top_k;
   a.h_out = reinterpret_cast<float*>(h_out);
-  const bool kfull = (K % TK) == 0;
   a.split_ws = reinterpret_cast<float*>(split_ws);
   a.split_cnt = split_cnt;
   a.n_res = 0;
+  // SM90 fused-MoE page, Parameters (gemm2_raster_along_m): the fused finalize deals its
+  // tiles column tile first when the output it scatters into is large and the
+  // contraction short -- at least 32 MiB for I <= 192, 64 MiB for I <= 384 -- so that
+  // the workgroups in flight add into one band of output columns. At the layer shapes
+  // here (I >= 2048) the rule never applies; at the Mixtral shape dealing column tile
+  // first measured the same as group first (1.27 vs 1.26 ms).
+  const size_t out_bytes = (size_t)(M / (top_k > 0 ? top_k : 1)) * N * 2;
+  a.mmajor = epi == EPI_FUSED && ((K <= 192 && out_bytes >= (32u << 20)) ||
+                                  (K <= 384 && out_bytes >= (64u << 20)));
   if (split_ws && split_cnt && kfull) {
     const int cu = device_cu_count();
     a.n_res = (cu < SPLIT_SLOTS ? cu : SPLIT_SLOTS) & ~7;  // one 128 KB-LDS workgroup per CU
@@ -920,9 +951,10 @@ moe_status gemm_nt_enqueue(int epi, const void* A, const int32_t* a_gather, int 
   const int64_t tiles = (int64_t)a.m_tiles * a.n_tiles;
   // parts of split tiles take at most n_res + 8 * SPLIT_MAX workgroups past the whole ones
   const int grid = round_up8(tiles + (a.n_res > 0 ? a.n_res + 8 * SPLIT_MAX : 0));
-#define MOE_LAUNCH_NT(E_)                                              \
-  (kfull ? k_gemm_nt<E_, true><<<grid, NTHREADS, 0, st>>>(a)           \
-         : k_gemm_nt<E_, false><<<grid, NTHREADS, 0, st>>>(a))
+#define MOE_LAUNCH_NT(E_)                                                  \
+  (tm == 128 ? k_gemm_nt<E_, true, 128><<<grid, NTHREADS, 0, st>>>(a)      \
+   : kfull   ? k_gemm_nt<E_, true><<<grid, NTHREADS, 0, st>>>(a)           \
+             : k_gemm_nt<E_, false><<<grid, NTHREADS, 0, st>>>(a))
   switch (epi) {
     case EPI_STORE: MOE_LAUNCH_NT(EPI_STORE); break;
     case EPI_SWIGLU: MOE_LAUNCH_NT(EPI_SWIGLU); break;

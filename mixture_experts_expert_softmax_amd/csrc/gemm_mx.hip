@@ -3,16 +3,17 @@
 //   MXFP4  e2m1 pairs, one UE8M0 scale per 32 values along the contraction;
 //   MXFP8  e4m3 bytes, same scales (activations MXFP8 in both MX families);
 //   FP8    e4m3 bytes with one fp32 scale per expert matrix, activations e4m3 with
-//          one fp32 scale for the tensor (StepFun page, intro: "fp8 (per-tensor)").
+//          one fp32 scale for the tensor (StepFun page, intro: the per-tensor fp8 weight family).
 //          The MFMA runs with unit block scales and the per-tensor factors are
 //          applied in the epilogue; the FC1 output is requantized with a given
 //          per-tensor scale, saturating at +-448.
 //
 // W4A8 page ("flashinfer.fused_moe.cake / cake_cute (MXFP4 SiTU routed MoE)"),
-// "Inputs": activations are float8_e4m3fn with one UE8M0 scale per 32 values
+// Host plan, Inputs: activations are float8_e4m3fn with one UE8M0 scale per 32 values
 // along H; the expert bank is MXFP4 (two e2m1 values per byte) with UE8M0
 // block-32 scales, w1 holding the up rows then the gate rows. Intro: fp32
-// accumulation and "UE8M0 round-up" requantization of the FC1 output before FC2.
+// accumulation, and the FC1 output requantized with UE8M0 scales rounded up
+// before FC2.
 //
 // v_mfma_scale_f32_32x32x64_f8f6f4 contract (checked on the device with exact
 // small-integer operands): with the e2m1 operand in the A slot, lane l supplies
@@ -768,7 +769,7 @@ inline bool mx_small_fits(int K, int NB, int64_t act_rows, int wb) {
 }
 
 // Tile family of a stage: `force` 0 / 1 picks the 256-row / streaming tile (the
-// latter only where it fits), -1 a choice recorded by moe_tune_mx for this shape and
+// latter only where it fits), -1 a choice recorded by moe_tune for this shape and
 // bucket, else the built-in rule.
 inline bool mx_use_small(int64_t R, int L, int K, int NB, int64_t act_rows, int rows_per_expert,
                          int wb, int stage, int wf, int force) {

@@ -1,16 +1,18 @@
 // Renormalized top-k routing from fp32 logits.
 //
-// StepFun MoE page, intro: the routing stage is "Renormalize top-k": the k
+// StepFun MoE page, intro: the routing stage is the Renormalize top-k mode: the k
 // largest experts are kept and their softmax weights renormalized to sum to 1.
 // Selecting on the raw logits is equivalent (softmax is increasing) and makes the
 // chosen ids independent of the exponential's rounding. Ties go to the lower id.
 //
-// Two kernels:
+// Three kernels:
 //  * k_route_thread<EMAX>: one thread per token, the token's logits in registers
 //    (num_experts <= EMAX <= 32). Each thread reads one contiguous row.
-//  * k_route_rank<Q, K2>: one wave64 per token, lane l holds experts Q*l .. Q*l+Q-1
-//    (num_experts <= 64*Q); a threshold from disjoint group maxima leaves a short
-//    list of candidates, whose ranks give the k slots.
+//  * k_route_rank4<QL, K2, FULL>: four tokens per wave, one per row of 16 lanes
+//    (32 < num_experts <= 256); a threshold from disjoint group maxima leaves a
+//    short list of candidates, whose ranks give the k slots.
+//  * k_route_rank<Q, K2>: the same selection with one wave64 per token, lane l
+//    holding experts Q*l .. Q*l+Q-1 (256 < num_experts <= 1024).
 #include "common.h"
 
 namespace moe {

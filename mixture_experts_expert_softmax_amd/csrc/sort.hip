@@ -14,8 +14,8 @@
 //  1. k_sort_count:   per-chunk histogram of local experts -> cnt[chunk][e]
 //                     (one coalesced row per chunk)
 //  2. k_sort_scan:    per expert, the exclusive prefix of cnt[*][e] over the
-//                     chunks (in place) and the expert total; 64 experts per
-//                     workgroup, each column split over 16 slices of chunks
+//                     chunks (in place) and the expert total; 16 experts per
+//                     workgroup, each column split over 64 slices of chunks
 //  3. k_sort_scatter: an exclusive scan of the totals -> expert start rows; each
 //                     wave counts its quarter, then walks its routes in order, 64
 //                     at a time, ranking equal keys with ballots (stable), and
@@ -69,18 +69,21 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
   return v;
 }
 
-// Column prefixes of cnt [nb][L]: workgroup b owns experts 64 b .. 64 b + 63; thread
-// (slice s, expert lane) sums chunks [s * per, (s + 1) * per) of its column, the
-// slice sums are combined through LDS, and a second pass writes the exclusive prefix.
-constexpr int SCAN_SLICES = 16;
+// Column prefixes of cnt [nb][L]: workgroup b owns experts SCAN_E b .. SCAN_E b +
+// SCAN_E - 1; thread (slice s, expert lane) sums chunks [s * per, (s + 1) * per) of its
+// column, the slice sums are combined through LDS, and a second pass writes the
+// exclusive prefix. Few experts per workgroup and many slices keep the dependent
+// loads per thread short (the kernel is latency-bound).
+constexpr int SCAN_E = 16;
+constexpr int SCAN_SLICES = 1024 / SCAN_E;
 __global__ __launch_bounds__(1024) void k_sort_scan(int32_t* __restrict__ cnt, int nb, int L,
                                                     int32_t* __restrict__ total,
                                                     int32_t* __restrict__ zero, int n_zero) {
-  __shared__ int ssum[SCAN_SLICES][64];
-  const int tid = threadIdx.x, el = tid & 63, sl = tid >> 6;
+  __shared__ int ssum[SCAN_SLICES][SCAN_E];
+  const int tid = threadIdx.x, el = tid % SCAN_E, sl = tid / SCAN_E;
   if (blockIdx.x == 0)  // a buffer the caller wants cleared before the GEMMs (no extra launch)
     for (int i = tid; i < n_zero; i += 1024) zero[i] = 0;
-  const int e = blockIdx.x * 64 + el;
+  const int e = blockIdx.x * SCAN_E + el;
   const int per = (nb + SCAN_SLICES - 1) / SCAN_SLICES;
   const int c0 = sl * per, c1 = min(nb, c0 + per);
   int part = 0;
@@ -318,7 +321,7 @@ moe_status sort_enqueue(const int32_t* ids, int64_t T, int32_t k, int32_t E, int
   int32_t* cnt = reinterpret_cast<int32_t*>(ws);
   int32_t* total = cnt + L * nb;
   k_sort_count<<<(unsigned)nb, 256, (size_t)L * sizeof(int32_t), st>>>(ids, n, E, L, off, cnt);
-  k_sort_scan<<<(unsigned)((L + 63) / 64), 1024, 0, st>>>(cnt, (int)nb, L, total, zero,
+  k_sort_scan<<<(unsigned)((L + SCAN_E - 1) / SCAN_E), 1024, 0, st>>>(cnt, (int)nb, L, total, zero,
                                                           zero ? n_zero : 0);
   k_sort_scatter<<<(unsigned)nb, 256, (size_t)(SORT_WAVES + 1) * L * sizeof(int32_t), st>>>(
       ids, n, E, L, off, cnt, total, offs, m_indptr, n_local, e2p, p2e);

@@ -1,11 +1,12 @@
-// Recorded tile-family choices of the fp8-activation GEMM stages.
+// Recorded tile-family choices of the layer's GEMM stages.
 //
 // SM90 fused-MoE page, Parameters: an autotuner profiles the legal tiles of each
 // GEMM per token bucket and caches the winner; the built-in tile rule goes by rows
-// per local expert. Here the candidates are the two tile families of gemm_mx.hip
-// (the 32-row streaming tile and the 256-row tile); moe_tune_mx (api.hip) times
-// both on the caller's data and stores the faster one under the stage, weight
-// format, shape and bucket = rows per local expert rounded up to a power of two.
+// per local expert. Here the candidates are two tile families per stage (bf16: the
+// 256-row and 128-row tiles of gemm_bf16.hip; fp8 activations: the 256-row and the
+// 32-row streaming tiles of gemm_mx.hip); moe_tune (api.hip) times both on the
+// caller's data and stores the faster one under the stage, weight format (-1 for
+// bf16), shape and bucket = rows per local expert rounded up to a power of two.
 // Host-only code; one table per process, guarded by a mutex.
 #include <map>
 #include <mutex>
