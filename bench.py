@@ -406,7 +406,8 @@ def _mx_sweep(wfmt, flush, dev):
 
 def _bgmv_points(flush, dev):
     """BGMV MoE-LoRA shrink + expand at the page's measured shape (hidden 3072, rank 32,
-    top-2 contiguous pairs, 4 LoRAs x 8 experts) for 16 and 2048 tokens. Bytes: the
+    top-2 contiguous pairs, 4 LoRAs x 8 experts) for 16, 2048 and 8192 tokens (the
+    library's automatic choice of pipeline: per pair at 16, grouped by bin at 2048 and 8192). Bytes: the
     LoRA weights of the touched (LoRA, expert) pairs once, x read, y written (float32);
     per-pair weight bytes (every pair reads its A and B slices, mostly from cache)
     are reported beside them."""
@@ -415,14 +416,15 @@ def _bgmv_points(flush, dev):
     import mixture_experts_expert_softmax_amd as M
     import moe_synth as S
     out = {}
-    for T in (16, 2048):
+    for T in (16, 2048, 8192):
         c = S.bgmv_case(seed=0, T=T, H=3072, rank=32, num_loras=4, E=8, top_k=2)
         d = [c.x.to(dev), c.lora_a.to(dev), c.lora_b.to(dev)] + [
             torch.from_numpy(v).to(dev) for v in (c.sorted_token_ids, c.expert_ids, c.lora_indices,
                                                   c.topk_weights)]
         y = torch.empty((T, 3072), dtype=torch.float32, device=dev)
-        ws = torch.empty(1 << 24, dtype=torch.uint8, device=dev)
         P = c.sorted_token_ids.shape[0]
+        ws = torch.empty(M.moe_bgmv_workspace_bytes(T, P, 3072, 3072, 32, 4, 8), dtype=torch.uint8,
+                         device=dev)
         fn = lambda: M.moe_bgmv(*d, c.num_experts, y_accum=y, workspace=ws)
         ms_ = _time(fn, reps=50, flush=flush)
         pairs = {(int(c.lora_indices[t]), int(e)) for t, e in zip(c.sorted_token_ids, c.expert_ids)}
@@ -449,6 +451,23 @@ def secondary_measurements(progress):
     # read through between timed reps wherever the touched data is under ~0.5 GB
     flush = torch.ones(512 << 20, dtype=torch.uint8, device=dev)
 
+    progress("secondary: tiny layer T=32 H=128 I=256 E=8 top-2")
+    ct = S.tiny_moe(seed=0)
+    lgt = torch.from_numpy(ct.logits).to(dev)
+    xt, w1t, w2t = ct.x.to(dev), ct.w1.to(dev), ct.w2.to(dev)
+    idt, wtt = M.moe_route(lgt, ct.top_k)
+    outt = torch.empty((ct.T, ct.H), dtype=torch.bfloat16, device=dev)
+    wst = torch.empty(M.moe_ffn_workspace_size(ct.T, ct.H, ct.I, ct.num_experts, ct.top_k),
+                      dtype=torch.uint8, device=dev)
+
+    def tiny_step():
+        M.moe_route(lgt, ct.top_k, idt, wtt)
+        M.moe_ffn_forward(xt, idt, wtt, w1t, w2t, ct.num_experts, out=outt, workspace=wst)
+    ms_t = _time(tiny_step, reps=50)
+    res["tiny"] = {"ms": round(ms_t, 4), "tokens_per_s": round(ct.T / (ms_t * 1e-3), 1),
+                   "timing": "mean of 50 back to back (launch-latency bound)"}
+    del xt, w1t, w2t
+
     progress("secondary: grouped GEMM E=16 sum_m=8192 K=2048 N=4096")
     c = S.grouped_gemm_case(seed=0)
     x, g, w = c.x.to(dev), c.g.to(dev), c.w.to(dev)
@@ -460,15 +479,17 @@ def secondary_measurements(progress):
     dwb = torch.empty((E, N, K), dtype=torch.bfloat16, device=dev)
     dwf = torch.empty((E, N, K), dtype=torch.float32, device=dev)
     gg = {}
-    for name, fn in [("fwd", lambda: M.grouped_gemm_fwd(x, w, offs, out=yb)),
-                     ("dgrad", lambda: M.grouped_gemm_dgrad(g, w, offs, out=dxb)),
+    sws = torch.empty(M.lib().moe_gemm_split_workspace_size(), dtype=torch.uint8, device=dev)
+    for name, fn in [("fwd", lambda: M.grouped_gemm_fwd(x, w, offs, out=yb, workspace=sws)),
+                     ("dgrad", lambda: M.grouped_gemm_dgrad(g, w, offs, out=dxb, workspace=sws)),
                      ("wgrad_bf16", lambda: M.grouped_gemm_wgrad(g, x, offs, out=dwb)),
                      ("wgrad_f32", lambda: M.grouped_gemm_wgrad(g, x, offs, out=dwf))]:
         ms_ = _time(fn, reps=20, flush=flush)  # ~370 MB of operands
         gg[name] = {"ms": round(ms_, 4), "tflops": round(fl / (ms_ * 1e-3) / 1e12, 1),
                     "mfma_frac": round(fl / (ms_ * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
     gg["group_sizes"] = c.sizes.tolist()
-    gg["timing"] = "median of 20, MALL flushed"
+    gg["timing"] = "median of 20, MALL flushed; fwd / dgrad with the split workspace"
+    del sws
     res["grouped_gemm"] = gg
     del x, g, w, yb, dxb, dwb, dwf
 

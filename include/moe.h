@@ -419,7 +419,20 @@ typedef struct moe_bgmv_desc {
   int32_t rank;
   int32_t num_loras;
   int32_t num_experts;
+  int32_t mode;               /* MOE_BGMV_* */
 } moe_bgmv_desc;
+
+/* Pipelines of moe_bgmv ([BGMV] Parameters: grouped). The per-pair pipeline reads
+ * every pair's LoRA slices; the grouped one sorts the pairs stably by (LoRA, expert)
+ * bin, runs the shrink and the expand as ragged grouped GEMMs over the bins (each
+ * bin's weights streamed once per tile of pairs), stores w[p] times each pair's fp32
+ * expand row and sums a token's rows in ascending pair order. Both are deterministic;
+ * they round differently within float32 (the expand's rank sum runs in another
+ * order). AUTO takes the grouped pipeline when num_pairs >= 96 * num_loras *
+ * num_experts; GROUPED needs num_loras * num_experts <= 1024. */
+#define MOE_BGMV_AUTO     0
+#define MOE_BGMV_PER_PAIR 1
+#define MOE_BGMV_GROUPED  2
 
 size_t moe_bgmv_workspace_size(const moe_bgmv_desc* desc);
 moe_status moe_bgmv(const moe_bgmv_desc* desc, const void* x, const void* lora_a,

@@ -24,7 +24,8 @@ __all__ = [
     "moe_finalize", "moe_fc1", "moe_fc2", "status_string", "ACT", "FINALIZE", "WFMT",
     "moe_ffn_forward_mx", "moe_fc1_mx", "moe_fc2_mx", "moe_ffn_forward_fp8", "moe_fc1_fp8",
     "moe_fc2_fp8", "moe_ffn_forward_train", "moe_ffn_backward", "moe_route_backward", "MoEFunction",
-    "moe_tune", "moe_tune_set", "moe_tune_clear", "moe_bgmv", "moe_ffn_forward_noalloc", "NOALLOC_SCRATCH_BYTES",
+    "moe_tune", "moe_tune_set", "moe_tune_clear", "moe_bgmv", "moe_bgmv_workspace_bytes",
+    "moe_ffn_forward_noalloc", "NOALLOC_SCRATCH_BYTES",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -62,7 +63,7 @@ class MoeFfnGrads(ctypes.Structure):
 
 class MoeBgmvDesc(ctypes.Structure):
     _fields_ = [("num_tokens", _i64), ("num_pairs", _i64), ("hidden", _i32), ("feat_out", _i32),
-                ("rank", _i32), ("num_loras", _i32), ("num_experts", _i32)]
+                ("rank", _i32), ("num_loras", _i32), ("num_experts", _i32), ("mode", _i32)]
 
 
 # name -> (restype, argtypes)
@@ -713,14 +714,24 @@ def moe_fc2_fp8(act, act_scale, w2, w2_scale, offs, T, top_k, num_experts, local
     return y
 
 
+def moe_bgmv_workspace_bytes(T: int, P: int, H: int, feat_out: int, rank: int, num_loras: int,
+                             num_experts: int, grouped: Optional[bool] = None) -> int:
+    """Workspace bytes moe_bgmv needs for these sizes (grouped as in moe_bgmv)."""
+    d = MoeBgmvDesc(T, P, H, feat_out, rank, num_loras, num_experts,
+                    0 if grouped is None else (2 if grouped else 1))
+    return int(lib().moe_bgmv_workspace_size(ctypes.byref(d)))
+
+
 def moe_bgmv(x: torch.Tensor, lora_a: torch.Tensor, lora_b: torch.Tensor,
              sorted_token_ids: torch.Tensor, expert_ids: torch.Tensor, lora_indices: torch.Tensor,
              topk_weights: torch.Tensor, num_experts: int, shrink_out: Optional[torch.Tensor] = None,
-             y_accum: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+             y_accum: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+             grouped: Optional[bool] = None):
     """BGMV MoE-LoRA shrink + expand. x [T,H] bf16, lora_a [nl,E,rank,H], lora_b [nl,E,N,rank]
     bf16, sorted_token_ids / expert_ids [P] int32, lora_indices [T] int32, topk_weights [P]
-    float32. Returns (y_accum [T, N] float32 (or the given, possibly strided, view), shrink
-    [P, rank] bf16)."""
+    float32. grouped: None lets the library choose the pipeline, True / False force the
+    grouped / per-pair one. Returns (y_accum [T, N] float32 (or the given, possibly
+    strided, view), shrink [P, rank] bf16)."""
     _dev(x, torch.bfloat16, "x"), _dev(lora_a, torch.bfloat16, "lora_a"), _dev(lora_b, torch.bfloat16, "lora_b")
     for t_, n_ in ((sorted_token_ids, "sorted_token_ids"), (expert_ids, "expert_ids"),
                    (lora_indices, "lora_indices")):
@@ -732,7 +743,7 @@ def moe_bgmv(x: torch.Tensor, lora_a: torch.Tensor, lora_b: torch.Tensor,
     if H2 != H or tuple(lora_b.shape) != (nl, E, N, r) or E != num_experts:
         raise ValueError("bgmv: lora_a must be [nl, E, rank, H] and lora_b [nl, E, N, rank]")
     P = sorted_token_ids.numel()
-    d = MoeBgmvDesc(T, P, H, N, r, nl, num_experts)
+    d = MoeBgmvDesc(T, P, H, N, r, nl, num_experts, 0 if grouped is None else (2 if grouped else 1))
     h = lib()
     if workspace is None:
         workspace = torch.empty(max(h.moe_bgmv_workspace_size(ctypes.byref(d)), 16), dtype=torch.uint8,

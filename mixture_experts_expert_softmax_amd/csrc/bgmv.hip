@@ -17,14 +17,37 @@
 // B row (rank values) it reads with 16-byte loads. The shrink publishes each pair in
 // a 16-slot token -> pair index; the expand sorts a token's slots ascending, or
 // scans all pairs in order for a token with more than 16.
+//
+// Grouped pipeline (BGMV page, Parameters: grouped), for many routes per (LoRA,
+// expert) bin: the pairs are sorted stably by bin (moe_sort's kernels, one bin per
+// (LoRA, expert)); the shrink is then a ragged grouped GEMM over the bins (x rows
+// gathered through the sorted pairs' tokens, the bin's A as weights, K = hidden) and
+// the expand another (shrink rows, the bin's B, K = rank), both on the bf16 MFMA
+// kernels of gemm_bf16.hip, so each bin's weights are streamed once per tile of
+// routes; the expand writes w[p] times its fp32 result as pair p's partial row, and a
+// per-token combine sums a token's partials in ascending pair order.
 #include <algorithm>
 
 #include "common.h"
 
 namespace moe {
+// defined in sort.hip / gemm_bf16.hip
+size_t sort_workspace_bytes(int64_t T, int32_t k, int32_t L);
+moe_status sort_enqueue(const int32_t* ids, int64_t T, int32_t k, int32_t E, int32_t L,
+                        int32_t off, int32_t* offs, int32_t* m_indptr, int32_t* e2p,
+                        int32_t* p2e, int32_t* n_local, void* ws, hipStream_t st,
+                        int32_t* zero, int n_zero);
+moe_status gemm_nt_enqueue(int epi, const void* A, const int32_t* a_gather, int a_div,
+                           const void* B, int NB, int E, const int32_t* ends, int64_t M, int N,
+                           int K, void* C, int64_t ldc, int I, const float* limits,
+                           float def_limit, const float* route_w, const int32_t* p2e, int top_k,
+                           hipStream_t st, void* split_ws, int32_t* split_cnt, void* h_out,
+                           int tm);
+
 namespace {
 
 constexpr int BG_SLOTS = 16;
+constexpr int EPI_ROWMAP = 4, EPI_ROWMAP_F32W = 5;   // the bf16 NT kernel's row-mapped epilogues
 constexpr int BG_SPLIT_MAX = 8;
 constexpr int BG_XSEG = 2048;   // 16-byte x chunks staged per shrink workgroup (32 KB)
 
@@ -229,7 +252,124 @@ __global__ __launch_bounds__(256) void k_bgmv_expand(BgArgs a, int col_tiles) {
   if (col_ok) a.y[t * a.ldy + c] = acc;
 }
 
+// Grouped pipeline, step 1: each valid pair's bin (LoRA * E + expert; -1 for a pair
+// that contributes nothing) and its slot in the token -> pair index.
+__global__ __launch_bounds__(256) void k_bgmv_bins(BgArgs a, int32_t* __restrict__ bins) {
+  const int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (p >= a.P) return;
+  int t, e, l;
+  if (!pair_ok(a, p, t, e, l)) {   // contributes nothing; its shrink row reads as zeros
+    bins[p] = -1;
+    for (int j = 0; j < a.r; ++j) a.s[p * a.r + j] = 0;
+    return;
+  }
+  bins[p] = l * a.E + e;
+  const int slot = atomicAdd(a.cnt + t, 1);
+  if (slot < BG_SLOTS) a.ri[(int64_t)t * BG_SLOTS + slot] = (int32_t)p;
+}
+
+// Step 2: the token of each sorted pair (the shrink's gathered x rows).
+__global__ __launch_bounds__(256) void k_bgmv_gtok(const int32_t* __restrict__ p2e,
+                                                   const int32_t* __restrict__ n_sorted,
+                                                   const int32_t* __restrict__ tok,
+                                                   int32_t* __restrict__ gtok, int64_t P) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < P && i < *n_sorted) gtok[i] = tok[p2e[i]];
+}
+
+// Last step: y[t, c] = sum over t's valid pairs, ascending p, of part[p, c]. One
+// workgroup per (token, 256 columns), thread = column; a token's pairs come from the
+// index (ranked ascending) or, beyond 16 pairs, from a scan of all pairs in order.
+__global__ __launch_bounds__(256) void k_bgmv_combine(BgArgs a, const float* __restrict__ part,
+                                                      int col_tiles) {
+  __shared__ int32_t plist[256];
+  __shared__ int nlist;
+  __shared__ int wcount[4];
+  const int64_t t = blockIdx.x / col_tiles;
+  const int ct = (int)(blockIdx.x - t * col_tiles);
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int c = ct * 256 + tid;
+  const bool col_ok = c < a.N;
+  float acc = 0.f;
+  auto add_list = [&](int nb) {   // plist[0 .. nb), loads first, then the ordered sum
+    for (int i0 = 0; i0 < nb; i0 += 8) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        v[u] = (i0 + u < nb && col_ok) ? part[(int64_t)plist[i0 + u] * a.N + c] : 0.f;
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (i0 + u < nb) acc += v[u];
+    }
+  };
+  const int n = a.cnt[t];
+  if (n <= BG_SLOTS) {
+    if (tid < n) {
+      const int v = a.ri[t * BG_SLOTS + tid];
+      int rank = 0;
+      for (int k = 0; k < n; ++k) rank += a.ri[t * BG_SLOTS + k] < v;
+      plist[rank] = v;
+    }
+    __syncthreads();
+    add_list(n);
+  } else {   // more than 16 routes: scan every pair in order, 256 at a time
+    for (int64_t base = 0; base < a.P; base += 256) {
+      const int64_t p = base + tid;
+      int tt = -1, ee = 0, ll = 0;
+      const bool hit = p < a.P && pair_ok(a, p, tt, ee, ll) && tt == t;
+      const uint64_t m = __ballot(hit);
+      if (lane == 0) wcount[wid] = __popcll(m);
+      __syncthreads();
+      const int before = (wid > 0 ? wcount[0] : 0) + (wid > 1 ? wcount[1] : 0) + (wid > 2 ? wcount[2] : 0);
+      if (hit) plist[before + __popcll(m & ((1ull << lane) - 1))] = (int32_t)p;
+      if (tid == 0) nlist = wcount[0] + wcount[1] + wcount[2] + wcount[3];
+      __syncthreads();
+      add_list(nlist);
+      __syncthreads();   // wcount / nlist / plist are rewritten by the next chunk
+    }
+  }
+  if (col_ok) a.y[t * a.ldy + c] = acc;
+}
+
 }  // namespace
+
+// The grouped pipeline serves at most this many (LoRA, expert) bins (moe_sort's limit).
+constexpr int BG_GROUP_MAX_BINS = 1024;
+
+bool bgmv_grouped(int mode, int64_t P, int nl, int E) {
+  const int64_t bins = (int64_t)nl * E;
+  if (bins > BG_GROUP_MAX_BINS || P == 0) return false;
+  if (mode == MOE_BGMV_GROUPED) return true;
+  if (mode == MOE_BGMV_PER_PAIR) return false;
+  // measured crossover (hidden 3072, rank 32, 4 LoRAs x 8 experts on MI355X): the
+  // grouped pipeline's sort and combine pay off from about 100 routes per bin
+  return P >= 96 * bins;
+}
+
+struct BgGroupLayout {
+  size_t cnt, ri, bins, offs, e2p, p2e, n_sorted, gtok, s, part, sort_ws, split, split_cnt, total;
+};
+
+BgGroupLayout bgmv_group_layout(int64_t T, int64_t P, int r, int N, int nl, int E) {
+  BgGroupLayout g{};
+  const int L = nl * E;
+  size_t o = 0;
+  g.cnt = o;      o += align_up((size_t)T * 4, 256);
+  g.ri = o;       o += align_up((size_t)T * BG_SLOTS * 4, 256);
+  g.bins = o;     o += align_up((size_t)P * 4, 256);
+  g.offs = o;     o += align_up((size_t)L * 4, 256);
+  g.e2p = o;      o += align_up((size_t)P * 4, 256);
+  g.p2e = o;      o += align_up((size_t)P * 4, 256);
+  g.n_sorted = o; o += 256;
+  g.gtok = o;     o += align_up((size_t)P * 4, 256);
+  g.s = o;        o += align_up((size_t)P * r * 2, 256);
+  g.part = o;     o += align_up((size_t)P * N * 4, 256);
+  g.sort_ws = o;  o += align_up(sort_workspace_bytes(P, 1, L), 256);
+  g.split = o;    o += (size_t)SPLIT_SLOTS * SPLIT_TILE_BYTES;
+  g.split_cnt = o; o += align_up((size_t)SPLIT_SLOTS * 4, 256);
+  g.total = o;
+  return g;
+}
 
 size_t bgmv_workspace_bytes(int64_t T, int64_t P, int r) {
   size_t o = 0;
@@ -239,6 +379,67 @@ size_t bgmv_workspace_bytes(int64_t T, int64_t P, int r) {
   o += align_up((size_t)P * 4, 256);                       // split arrivals
   o += align_up((size_t)P * r * 2, 256);                   // shrink rows (if not the caller's)
   return o;
+}
+
+// The grouped pipeline: bins + token index, stable sort by bin, the gathered-token
+// list, the shrink and expand grouped GEMMs, the per-token combine.
+moe_status bgmv_group_enqueue(const void* x, const void* A, const void* B, const int32_t* tok,
+                              const int32_t* ex, const int32_t* lidx, const float* w,
+                              void* shrink, float* y, int64_t ldy, int64_t T, int64_t P, int H,
+                              int N, int r, int nl, int E, void* ws, hipStream_t st) {
+  const BgGroupLayout g = bgmv_group_layout(T, P, r, N, nl, E);
+  char* wp = reinterpret_cast<char*>(ws);
+  const int L = nl * E;
+  BgArgs a{};
+  a.tok = tok;
+  a.ex = ex;
+  a.lidx = lidx;
+  a.w = w;
+  a.y = y;
+  a.ldy = ldy;
+  a.T = T;
+  a.P = P;
+  a.H8 = H / 8;
+  a.N = N;
+  a.r = r;
+  a.nl = nl;
+  a.E = E;
+  a.cnt = reinterpret_cast<int32_t*>(wp + g.cnt);
+  a.ri = reinterpret_cast<int32_t*>(wp + g.ri);
+  int32_t* bins = reinterpret_cast<int32_t*>(wp + g.bins);
+  int32_t* offs = reinterpret_cast<int32_t*>(wp + g.offs);
+  int32_t* e2p = reinterpret_cast<int32_t*>(wp + g.e2p);
+  int32_t* p2e = reinterpret_cast<int32_t*>(wp + g.p2e);
+  int32_t* n_sorted = reinterpret_cast<int32_t*>(wp + g.n_sorted);
+  int32_t* gtok = reinterpret_cast<int32_t*>(wp + g.gtok);
+  void* s = shrink ? shrink : (void*)(wp + g.s);
+  a.s = reinterpret_cast<uint16_t*>(s);
+  float* part = reinterpret_cast<float*>(wp + g.part);
+  int32_t* split_cnt = reinterpret_cast<int32_t*>(wp + g.split_cnt);
+  k_bgmv_zero<<<(unsigned)((T + 255) / 256), 256, 0, st>>>(a.cnt, T, nullptr, 0);
+  moe_status st_ = launch_status();
+  if (st_ != MOE_OK) return st_;
+  k_bgmv_bins<<<(unsigned)((P + 255) / 256), 256, 0, st>>>(a, bins);
+  if ((st_ = launch_status()) != MOE_OK) return st_;
+  // stable sort of the pairs by bin (invalid pairs are foreign); also clears the
+  // split-tile counters of the two grouped GEMMs
+  st_ = sort_enqueue(bins, P, 1, L, L, 0, offs, nullptr, e2p, p2e, n_sorted, wp + g.sort_ws, st,
+                     split_cnt, SPLIT_SLOTS);
+  if (st_ != MOE_OK) return st_;
+  k_bgmv_gtok<<<(unsigned)((P + 255) / 256), 256, 0, st>>>(p2e, n_sorted, tok, gtok, P);
+  if ((st_ = launch_status()) != MOE_OK) return st_;
+  // shrink: s[p2e[i]] = bf16(x[gtok[i]] @ A[bin].T) for the sorted rows i of each bin
+  st_ = gemm_nt_enqueue(EPI_ROWMAP, x, gtok, 1, A, r, L, offs, P, r, H, s, r, 0, nullptr, 0.f,
+                        nullptr, p2e, 1, st, wp + g.split, split_cnt, nullptr, 256);
+  if (st_ != MOE_OK) return st_;
+  // expand: part[p2e[i]] = w[p2e[i]] * (s[p2e[i]] @ B[bin].T), fp32
+  st_ = gemm_nt_enqueue(EPI_ROWMAP_F32W, s, p2e, 1, B, N, L, offs, P, N, r, part, N, 0, nullptr,
+                        0.f, w, p2e, 1, st, wp + g.split, split_cnt, nullptr, 256);
+  if (st_ != MOE_OK) return st_;
+  const int col_tiles = (N + 255) / 256;
+  if (T * col_tiles > INT32_MAX) return MOE_ERR_UNSUPPORTED;
+  k_bgmv_combine<<<(unsigned)(T * col_tiles), 256, 0, st>>>(a, part, col_tiles);
+  return launch_status();
 }
 
 moe_status bgmv_enqueue(const void* x, const void* A, const void* B, const int32_t* tok,
@@ -323,13 +524,23 @@ static moe_status check_bgmv(const moe_bgmv_desc* d) {
   if (d->hidden < 8 || d->hidden % 8 || d->feat_out < 8 || d->feat_out % 8) return MOE_ERR_SHAPE;
   if (d->rank != 8 && d->rank != 16 && d->rank != 32 && d->rank != 64) return MOE_ERR_SHAPE;
   if (d->num_loras < 1 || d->num_experts < 1) return MOE_ERR_SHAPE;
+  if (d->mode < MOE_BGMV_AUTO || d->mode > MOE_BGMV_GROUPED) return MOE_ERR_DTYPE;
+  if (d->mode == MOE_BGMV_GROUPED && (int64_t)d->num_loras * d->num_experts > BG_GROUP_MAX_BINS)
+    return MOE_ERR_UNSUPPORTED;
   if (d->hidden / 8 > BG_XSEG * BG_SPLIT_MAX) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
+static size_t bgmv_ws_bytes(const moe_bgmv_desc* d) {
+  if (bgmv_grouped(d->mode, d->num_pairs, d->num_loras, d->num_experts))
+    return bgmv_group_layout(d->num_tokens, d->num_pairs, d->rank, d->feat_out, d->num_loras,
+                             d->num_experts).total;
+  return bgmv_workspace_bytes(d->num_tokens, d->num_pairs, d->rank);
+}
+
 extern "C" size_t moe_bgmv_workspace_size(const moe_bgmv_desc* d) {
   if (check_bgmv(d) != MOE_OK) return 0;
-  return bgmv_workspace_bytes(d->num_tokens, d->num_pairs, d->rank);
+  return bgmv_ws_bytes(d);
 }
 
 extern "C" moe_status moe_bgmv(const moe_bgmv_desc* d, const void* x, const void* lora_a,
@@ -347,8 +558,16 @@ extern "C" moe_status moe_bgmv(const moe_bgmv_desc* d, const void* x, const void
   if (!aligned16(x) || !aligned16(lora_a) || !aligned16(lora_b) ||
       (shrink_out && !aligned16(shrink_out)))
     return MOE_ERR_ALIGN;
-  if (!ws || ws_bytes < bgmv_workspace_bytes(d->num_tokens, d->num_pairs, d->rank) || !aligned16(ws))
-    return MOE_ERR_WORKSPACE;
+  if (!ws || ws_bytes < bgmv_ws_bytes(d) || !aligned16(ws)) return MOE_ERR_WORKSPACE;
+  if (bgmv_grouped(d->mode, d->num_pairs, d->num_loras, d->num_experts)) {
+    if ((int64_t)d->num_tokens * d->hidden >= ((int64_t)1 << 32) ||
+        (int64_t)d->num_pairs * d->feat_out >= ((int64_t)1 << 31))
+      return MOE_ERR_UNSUPPORTED;
+    return bgmv_group_enqueue(x, lora_a, lora_b, sorted_token_ids, expert_ids, lora_indices,
+                              topk_weights, shrink_out, y_accum, ldy, d->num_tokens,
+                              d->num_pairs, d->hidden, d->feat_out, d->rank, d->num_loras,
+                              d->num_experts, ws, as_stream(stream));
+  }
   return bgmv_enqueue(x, lora_a, lora_b, sorted_token_ids, expert_ids, lora_indices, topk_weights,
                       shrink_out, y_accum, ldy, d->num_tokens, d->num_pairs, d->hidden, d->feat_out,
                       d->rank, d->num_loras, d->num_experts, ws, as_stream(stream));

@@ -47,7 +47,11 @@ constexpr int TK = 64;         // contraction per stage
 constexpr int NTHREADS = 256;  // 4 waves
 constexpr int TILE_U4 = TB * TK * 2 / 16;  // uint4 slots per operand tile (2048)
 
-enum Epi { EPI_STORE = 0, EPI_SWIGLU = 1, EPI_SWIGLU_STEP = 2, EPI_FUSED = 3 };
+// EPI_ROWMAP stores bf16 row p at row p2e[p] of C; EPI_ROWMAP_F32W stores it in
+// float32 at row p2e[p], times route_w[p2e[p]] (the BGMV grouped pipeline's shrink rows
+// and weighted expand partials, written in pair order).
+enum Epi { EPI_STORE = 0, EPI_SWIGLU = 1, EPI_SWIGLU_STEP = 2, EPI_FUSED = 3, EPI_ROWMAP = 4,
+           EPI_ROWMAP_F32W = 5 };
 constexpr int SPLIT_MAX = 8;   // parts a split tile is cut into at most
 
 struct NtArgs {
@@ -142,24 +146,42 @@ __device__ __forceinline__ bool deal_tile_split(const int32_t* ends, int E, int 
   return true;
 }
 
+// Which of a wave's 16 32x32 accumulator blocks (bit i * 4 + j of the result) hold
+// results: block rows r0 + j * 32 (j < jn) below rend, block columns c0 + i * 32 below cend.
+__device__ __forceinline__ int block_mask(int r0, int rend, int jn, int c0, int cend) {
+  int m = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (j < jn && r0 + j * 32 < rend && c0 + i * 32 < cend) m |= 1 << (i * 4 + j);
+  return m;
+}
+
 // Part `part` of S of a split tile publishes its fp32 partial into slot `slot` of
 // the split workspace; the last of the S parts to arrive (counter cidx) sums all of
 // them in part order -- the same result whichever part arrives last -- into acc and
-// returns true (it goes on to the epilogue); the others return false.
+// returns true (it goes on to the epilogue); the others return false. Only the blocks
+// in the wave's mask vmask (wave-uniform, the same for every part) are written and
+// summed. The sum is a single workgroup's job and bound by the loads it keeps in
+// flight: it takes the parts two at a time, with all of one accumulator row's loads
+// of both issued before any is used.
 __device__ __forceinline__ bool split_reduce(f32x16 (&acc)[4][4], float* split_ws, int32_t* split_cnt,
                                              int slot, int part, int S, int cidx, uint4* smem,
-                                             int tid) {
+                                             int tid, int vmask) {
   constexpr int TILE_F4 = TB * TB / 4;
   float4* mine = reinterpret_cast<float4*>(split_ws) + (size_t)slot * TILE_F4;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 4; ++j) {
+      if (!(vmask >> (i * 4 + j) & 1)) continue;
 #pragma unroll
       for (int q = 0; q < 4; ++q)
         mine[((i * 4 + j) * 4 + q) * NTHREADS + tid] =
             make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
                         acc[i][j][4 * q + 3]);
+    }
   __syncthreads();
   int* flag = reinterpret_cast<int*>(smem);
   if (tid == 0) {
@@ -172,25 +194,50 @@ __device__ __forceinline__ bool split_reduce(f32x16 (&acc)[4][4], float* split_w
   if (!flag[0]) return false;
   const float4* first = reinterpret_cast<const float4*>(split_ws) + (size_t)(slot - part) * TILE_F4;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 4; ++i) {
+    if (!(vmask >> (i * 4) & 15)) continue;
+    for (int p = 0; p < S; p += 2) {
+      const bool two = p + 1 < S;
+      const float4* s0 = first + (size_t)p * TILE_F4;
+      const float4* s1 = two ? s0 + TILE_F4 : s0;   // never past the last part
+      float4 w0[4][4], w1[4][4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < 4; ++j) {
+        if (!(vmask >> (i * 4 + j) & 1)) continue;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int idx = ((i * 4 + j) * 4 + q) * NTHREADS + tid;
-        float4 v = first[idx];
-        for (int p = 1; p < S; ++p) {
-          const float4 w = first[(size_t)p * TILE_F4 + idx];
-          v.x += w.x;
-          v.y += w.y;
-          v.z += w.z;
-          v.w += w.w;
+        for (int q = 0; q < 4; ++q) {
+          const int idx = ((i * 4 + j) * 4 + q) * NTHREADS + tid;
+          w0[j][q] = s0[idx];
+          w1[j][q] = two ? s1[idx] : make_float4(0.f, 0.f, 0.f, 0.f);
         }
-        acc[i][j][4 * q] = v.x;
-        acc[i][j][4 * q + 1] = v.y;
-        acc[i][j][4 * q + 2] = v.z;
-        acc[i][j][4 * q + 3] = v.w;
       }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (!(vmask >> (i * 4 + j) & 1)) continue;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float4 a0 = w0[j][q], a1 = w1[j][q];
+          if (p == 0) {   // ((p0 + p1) + p2) + ...: part order
+            acc[i][j][4 * q] = a0.x;
+            acc[i][j][4 * q + 1] = a0.y;
+            acc[i][j][4 * q + 2] = a0.z;
+            acc[i][j][4 * q + 3] = a0.w;
+          } else {
+            acc[i][j][4 * q] += a0.x;
+            acc[i][j][4 * q + 1] += a0.y;
+            acc[i][j][4 * q + 2] += a0.z;
+            acc[i][j][4 * q + 3] += a0.w;
+          }
+          if (two) {
+            acc[i][j][4 * q] += a1.x;
+            acc[i][j][4 * q + 1] += a1.y;
+            acc[i][j][4 * q + 2] += a1.z;
+            acc[i][j][4 * q + 3] += a1.w;
+          }
+        }
+      }
+    }
+  }
   return true;
 }
 
@@ -534,11 +581,13 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_nt(NtArgs a) {
     int wrow;
     if (EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_STEP) {
       int c = nt * 128 + (R >> 7) * 64 + (R & 63);
-      c = c < a.I ? c : a.I - 1;
+      // rows past the edge load distinct valid rows (their results are masked): many
+      // copies of one row in a stage serialize on its cache line
+      c = c < a.I ? c : c % a.I;
       wrow = ((R >> 6) & 1) * a.I + c;
     } else {
       wrow = nt * TB + R;
-      wrow = wrow < a.NB ? wrow : a.NB - 1;
+      wrow = wrow < a.NB ? wrow : wrow % a.NB;
     }
     lb.off[j] = (uint32_t)wrow * (uint32_t)a.K;
   }
@@ -560,11 +609,11 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_nt(NtArgs a) {
       int wrow;
       if (EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_STEP) {
         int c = nt * 128 + (R >> 7) * 64 + (R & 63);
-        c = c < a.I ? c : a.I - 1;
+        c = c < a.I ? c : c % a.I;
         wrow = ((R >> 6) & 1) * a.I + c;
       } else {
         wrow = nt * TB + R;
-        wrow = wrow < a.NB ? wrow : a.NB - 1;
+        wrow = wrow < a.NB ? wrow : wrow % a.NB;
       }
       boff[j] = (uint32_t)wrow * (uint32_t)a.K;
     }
@@ -588,7 +637,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_nt(NtArgs a) {
       mainloop_dma_g<false, false, 4>(sw, sx, smem, k0 * TK, nk * 2, tid, lane, wn, wm, acc);
     }
     // a part of a split tile: the last of its parts to arrive finishes the tile
-    if (S > 1 && !split_reduce(acc, a.split_ws, a.split_cnt, slot, part, S, cidx, smem, tid))
+    if (S > 1 && !split_reduce(acc, a.split_ws, a.split_cnt, slot, part, S, cidx, smem, tid,
+                               block_mask(m0 + wm * jn * 32, mend, jn, nt * TB + wn * 128,
+                                          EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_STEP ? TB * a.n_tiles
+                                                                                      : a.N)))
       return;
   } else {
     la.load(0);
@@ -670,12 +722,31 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_nt(NtArgs a) {
           atomic_add_bf16x2(crow + col + 2, wgt * acc[i][j][q * 4 + 2], wgt * acc[i][j][q * 4 + 3]);
         }
     }
+  } else if (EPI == EPI_ROWMAP_F32W) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int p = m0 + wm * jn * 32 + j * 32 + (lane & 31);
+      if (j >= jn || p >= mend) continue;
+      const int row = a.p2e[p];
+      const float wgt = a.route_w[row];
+      float* crow = reinterpret_cast<float*>(a.C) + (int64_t)row * a.ldc;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int col = nt * TB + wn * 128 + i * 32 + q * 8 + hi4;
+          if (col >= a.N) continue;
+          *reinterpret_cast<float4*>(crow + col) =
+              make_float4(wgt * acc[i][j][q * 4 + 0], wgt * acc[i][j][q * 4 + 1],
+                          wgt * acc[i][j][q * 4 + 2], wgt * acc[i][j][q * 4 + 3]);
+        }
+    }
   } else {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int p = m0 + wm * jn * 32 + j * 32 + (lane & 31);
       if (j >= jn || p >= mend) continue;
-      uint16_t* crow = a.C + (int64_t)p * a.ldc;
+      uint16_t* crow = a.C + (int64_t)(EPI == EPI_ROWMAP ? a.p2e[p] : p) * a.ldc;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -738,7 +809,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_dgrad(DgradArgs a) {
   }
   sg.init(tid);
   mainloop_dma_g<true, false, 4>(sw, sg, smem, k0 * 32, nk, tid, lane, wn, wm, acc);
-  if (S > 1 && !split_reduce(acc, a.split_ws, a.split_cnt, slot, part, S, cidx, smem, tid)) return;
+  if (S > 1 && !split_reduce(acc, a.split_ws, a.split_cnt, slot, part, S, cidx, smem, tid,
+                             block_mask(m0 + wm * 128, mend, 4, c0 + wn * 128, a.K)))
+    return;
   const int hi4 = (lane >> 5) * 4;
   float lim = 0.f;
   if (ACT == 2) lim = a.limits ? a.limits[e] : a.def_limit;
@@ -960,6 +1033,8 @@ moe_status gemm_nt_enqueue(int epi, const void* A, const int32_t* a_gather, int 
     case EPI_SWIGLU: MOE_LAUNCH_NT(EPI_SWIGLU); break;
     case EPI_SWIGLU_STEP: MOE_LAUNCH_NT(EPI_SWIGLU_STEP); break;
     case EPI_FUSED: MOE_LAUNCH_NT(EPI_FUSED); break;
+    case EPI_ROWMAP: MOE_LAUNCH_NT(EPI_ROWMAP); break;
+    case EPI_ROWMAP_F32W: MOE_LAUNCH_NT(EPI_ROWMAP_F32W); break;
     default: return MOE_ERR_DTYPE;
   }
 #undef MOE_LAUNCH_NT

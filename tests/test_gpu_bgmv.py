@@ -5,7 +5,10 @@ library rounds its float32 sum. Bar, element by element: a shrink value within o
 bf16 step (2^-7 relative) of the oracle's plus the float32 accumulation error of its
 sum (H 2^-24 of the absolute sum), and y within that shrink error carried through
 |w| |s| |B| plus the float32 accumulation of the expand; at least 99% of the shrink
-values equal bit for bit.
+values equal bit for bit. Both pipelines (per pair, and grouped by (LoRA, expert)
+bin, BGMV page Parameters: grouped) are held to this bar; the grouped one's weighted
+expand rows are rounded once more (w times the row, then the ordered sum), covered by
+one more 2^-24 of the absolute terms.
 """
 import numpy as np
 import pytest
@@ -52,33 +55,36 @@ def _check(c, y, s, tok=None, ex=None, li=None, w=None):
     kmax = np.bincount(np.asarray(tok)[(np.asarray(tok) >= 0) & (np.asarray(tok) < x.shape[0])],
                        minlength=1).max(initial=0)
     by = O.bgmv_expand(bs, np.abs(B), tok, ex, li, np.abs(w), x.shape[0])
-    by += (r + kmax) * 2.0 ** -24 * O.bgmv_expand(np.abs(s_ref) + bs, np.abs(B), tok, ex, li,
+    by += (r + kmax + 1) * 2.0 ** -24 * O.bgmv_expand(np.abs(s_ref) + bs, np.abs(B), tok, ex, li,
                                                    np.abs(w), x.shape[0])
     y_got = to_np(y).astype(np.float64)
     assert np.all(np.abs(y_got - y_ref) <= by + 1e-30), "y beyond the derived bound"
     return y_ref
 
 
+@pytest.mark.parametrize("grouped", [None, True])
 @pytest.mark.parametrize("order", ["contiguous", "expert", "random"])
 @pytest.mark.parametrize("rank", [8, 16, 32, 64])
-def test_bgmv_orders_and_ranks(order, rank):
+def test_bgmv_orders_and_ranks(order, rank, grouped):
     c = S.bgmv_case(seed=rank, T=96, H=512, rank=rank, num_loras=3, E=8, top_k=2, order=order)
-    y, s = _run(c)
+    y, s = _run(c, grouped=grouped)
     _check(c, y, s)
 
 
+@pytest.mark.parametrize("grouped", [None, True])
 @pytest.mark.parametrize("H,feat_out,top_k,T", [(2688, 2688, 2, 64), (3072, 1024, 8, 40),
                                                  (520, 264, 1, 33)])
-def test_bgmv_shapes(H, feat_out, top_k, T):
+def test_bgmv_shapes(H, feat_out, top_k, T, grouped):
     """Hidden sizes of the page (2688, 3072), feat_out != H, top-1 / top-8, widths that
     are multiples of 8 but not of 64 or 256 (partial column tiles)."""
     c = S.bgmv_case(seed=H, T=T, H=H, rank=32, num_loras=2, E=16, top_k=top_k, feat_out=feat_out,
                     order="random")
-    y, s = _run(c)
+    y, s = _run(c, grouped=grouped)
     _check(c, y, s)
 
 
-def test_bgmv_few_pairs_split_hidden_and_invalid_indices():
+@pytest.mark.parametrize("grouped", [None, True])
+def test_bgmv_few_pairs_split_hidden_and_invalid_indices(grouped):
     """3 tokens, 4 pairs: the shrink splits the hidden dimension (last-arriving split
     sums the partials); invalid token / expert / LoRA indices contribute nothing and
     tokens without a pair get zero rows."""
@@ -91,13 +97,14 @@ def test_bgmv_few_pairs_split_hidden_and_invalid_indices():
     d = _dev(c)
     d.update(tok=torch.from_numpy(tok).to(DEV), ex=torch.from_numpy(ex).to(DEV),
              li=torch.from_numpy(li).to(DEV))
-    y, s = _run(c, d)
+    y, s = _run(c, d, grouped=grouped)
     y_ref = _check(c, y, s, tok, ex, li, w)
     assert np.all(to_np(y)[2] == 0) and np.all(y_ref[2] == 0)
     assert np.all(to_np(s)[1] == 0) and np.all(to_np(s)[4] == 0)
 
 
-def test_bgmv_token_with_many_pairs_uses_ordered_scan():
+@pytest.mark.parametrize("grouped", [None, True])
+def test_bgmv_token_with_many_pairs_uses_ordered_scan(grouped):
     """Token 0 owns 24 pairs (beyond the 16-slot route index): its routes are found by
     an ordered scan of all pairs."""
     c = S.bgmv_case(seed=9, T=16, H=256, rank=32, num_loras=2, E=32, top_k=2, order="random")
@@ -111,7 +118,7 @@ def test_bgmv_token_with_many_pairs_uses_ordered_scan():
     d = _dev(c)
     d.update(tok=torch.from_numpy(tok).to(DEV), ex=torch.from_numpy(ex).to(DEV),
              w=torch.from_numpy(w).to(DEV))
-    y, s = _run(c, d)
+    y, s = _run(c, d, grouped=grouped)
     _check(c, y, s, tok, ex, None, w)
 
 
@@ -147,10 +154,22 @@ def test_bgmv_strided_output_replay_and_graph():
         assert torch.equal(got, ref)
 
 
-def test_bgmv_page_shape_full_size():
+@pytest.mark.parametrize("grouped", [False, True])
+def test_bgmv_page_shape_full_size(grouped):
     """The page's measured shape: hidden 3072, rank 32, 2048 tokens, top-2 contiguous
-    (4 LoRAs x 8 experts)."""
+    (4 LoRAs x 8 experts: 128 routes per bin, where the library picks the grouped
+    pipeline itself), both pipelines; each replays bit for bit, and the strided output
+    of the grouped one equals its contiguous output."""
     c = S.bgmv_case(seed=0, T=2048, H=3072, rank=32, num_loras=4, E=8, top_k=2)
-    y, s = _run(c)
+    d = _dev(c)
+    y, s = _run(c, d, grouped=grouped)
     torch.cuda.synchronize()
     _check(c, y, s)
+    y2, _ = _run(c, d, grouped=grouped)
+    assert torch.equal(y, y2)
+    if grouped:
+        y_auto, _ = _run(c, d)
+        assert torch.equal(y_auto, y)
+        wide = torch.full((2048, 3200), 7.0, dtype=torch.float32, device=DEV)
+        y3, _ = _run(c, d, grouped=True, y_accum=wide[:, 64:64 + 3072])
+        assert torch.equal(y3, y) and torch.all(wide[:, :64] == 7.0)
