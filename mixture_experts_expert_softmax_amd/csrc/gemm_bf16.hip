@@ -332,22 +332,26 @@ __device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
   asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(lds) : "memory");
 }
 
-// The full-K main loop (mainloop_dma_g below, for the forward and both backward
-// products) is a pipeline of DMA_SLOTS 32-deep stages fetched straight into LDS
-// without passing through registers (32 KB a stage: the 256 activation rows, then
-// the 256 weight rows, 64 bytes each in the row-major layout). Stage s + DMA_SLOTS - 1 is requested while stage s is
-// consumed, so a copy has three stages of MFMA work to land, and each copy is issued
-// right after one fragment read so the copies go out spread over the stage's MFMAs
-// (issued back to back, they stall the wave on the address unit ahead of its
-// MFMAs). A row's four 16-byte chunks are stored at chunk ^ ((row / 4) % 4), which
-// keeps the 32-row fragment reads free of bank conflicts; copy j of wave w covers
-// rows 64 j + 16 w + lane / 4, so lane l fetches global chunk (l % 4) ^ ((l / 16) % 4).
-// The loop is rotated by one 16-deep step: the last step of a stage runs after the
-// barrier, under the first fragment reads of the next. Stages past the end re-load
-// the last one into a slot nobody reads, which keeps the copy count uniform.
+// The full-K main loops (mainloop_dma_g below for the backward products,
+// mainloop_fwd_w64 for the forward) are pipelines of 32-deep stages fetched straight
+// into LDS without passing through registers (32 KB a stage: the 256 activation
+// rows, then the 256 weight rows; 64 bytes of a row-major operand's row). Stage
+// s + DMA_DIST is requested while stage s is consumed, so a copy has about two
+// stages of MFMA work to land, and each copy is issued right after one fragment read
+// so the copies go out spread over the stage's MFMAs (issued back to back, they stall
+// the wave on the address unit ahead of its MFMAs). A row-major row's four 16-byte
+// chunks are stored at chunk ^ ((row / 4) % 4), which keeps the 32-row fragment
+// reads free of bank conflicts; copy j of wave w covers rows 64 j + 16 w + lane / 4,
+// so lane l fetches global chunk (l % 4) ^ ((l / 16) % 4). The loop is rotated by one
+// 16-deep step: the last step of a stage runs after the barrier, under the first
+// fragment reads of the next. Stages past the end re-load the last one into a slot
+// nobody reads, which keeps the copy count uniform.
 constexpr int DMA_SLOTS = 4;
+constexpr int DMA_DIST = DMA_SLOTS - 1;   // stages between a copy and its use
 constexpr int DMA_STAGE_U4 = 2 * TB * 32 * 2 / 16;   // uint4 slots per 32-deep stage
-static_assert(DMA_SLOTS * DMA_STAGE_U4 <= 4 * TILE_U4, "stages exceed the kernel's LDS");
+constexpr int LDS_U4 = DMA_SLOTS * DMA_STAGE_U4;      // 128 KB: dgrad / wgrad
+constexpr int LDS_FWD_U4 = (4 * TB * 64 + 3 * TB * 128) / 16;   // 160 KB: mainloop_fwd_w64
+static_assert(LDS_U4 >= 4 * TILE_U4, "the partial-K path's two 64-deep stages fit");
 
 
 // Copy of one 16-byte chunk per lane through a buffer resource: lands at LDS byte
@@ -400,9 +404,9 @@ struct KmSrc {              // K-major operand: contraction row 0, first output 
   }
 };
 
-// Backward main loop: the forward's direct-to-LDS pipeline (four 32-deep slots,
-// copies three stages ahead interleaved with fragment reads, rotated by one step)
-// for operands in either layout. A = weight side (output columns), B = activation
+// Backward main loop: the direct-to-LDS pipeline above (four 32-deep slots, copies
+// three stages ahead interleaved with fragment reads, rotated by one step) for a
+// K-major weight side and an activation side in either layout. A = weight side (output columns), B = activation
 // side (output rows); kbase is the row-major operand's first contraction element.
 // JN = 32-row activation blocks per wave: 4 for the whole 256-row tile; 1 (row-major
 // activation side only) for a tile of at most 64 rows, where row-wave wm takes rows
@@ -412,6 +416,7 @@ template <bool A_K, bool B_K, int JN, class SA, class SB>
 __device__ __forceinline__ void mainloop_dma_g(const SA& sa, const SB& sb, uint4* smem, int kbase,
                                                int nsub, int tid, int lane, int wn, int wm,
                                                f32x16 (&acc)[4][4]) {
+  static_assert(A_K, "the forward (both operands row-major) runs mainloop_fwd_w64");
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const uint32_t lds0 = (uint32_t)(uintptr_t)smem + (uint32_t)w * 1024u;
   const int rsel = lane & 31, kg = lane >> 5, sw = (rsel >> 2) & 3;
@@ -451,7 +456,7 @@ __device__ __forceinline__ void mainloop_dma_g(const SA& sa, const SB& sb, uint4
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) rd_b(Bs, kk, set, j);
-    } else if constexpr (A_K || B_K) {
+    } else {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         rd_a(As, kk, set, i);
@@ -459,18 +464,6 @@ __device__ __forceinline__ void mainloop_dma_g(const SA& sa, const SB& sb, uint4
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) rd_b(Bs, kk, set, j);
-    } else {   // both row-major (the forward): a copy after every second read
-      constexpr int NC = H == 0 ? JN : 4;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        rd_a(As, kk, set, i);
-        if ((i & 1) && (i >> 1) < NC) copy_rm(src, sub, d, i >> 1);
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if (j < JN) rd_b(Bs, kk, set, j);
-        if ((j & 1) && 2 + (j >> 1) < NC) copy_rm(src, sub, d, 2 + (j >> 1));
-      }
     }
   };
   auto mm = [&](int set) {
@@ -500,9 +493,9 @@ __device__ __forceinline__ void mainloop_dma_g(const SA& sa, const SB& sb, uint4
     }
   };
   auto body = [&](int sub, bool first) {
-    const int slot = sub & (DMA_SLOTS - 1);
-    const int nxt = sub + DMA_SLOTS - 1 < nsub ? sub + DMA_SLOTS - 1 : nsub - 1;
-    const int dslot = (sub + DMA_SLOTS - 1) & (DMA_SLOTS - 1);
+    const int slot = sub % DMA_SLOTS;
+    const int nxt = sub + DMA_DIST < nsub ? sub + DMA_DIST : nsub - 1;
+    const int dslot = (sub + DMA_DIST) % DMA_SLOTS;
     rd_issue(slot, 0, 0, nxt, dslot, std::integral_constant<int, 0>{});
     if (!first) mm(1);
     rd_issue(slot, 1, 1, nxt, dslot, std::integral_constant<int, 1>{});
@@ -513,7 +506,108 @@ __device__ __forceinline__ void mainloop_dma_g(const SA& sa, const SB& sb, uint4
     constexpr int NM = 4 * JN;
     if (first) __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
     for (int q = 0; q < (first ? 1 : 2); ++q) {
-      if constexpr (!A_K && !B_K && JN == 4) {   // 8 reads: one between each pair of MFMAs
+      for (int r = 0; r < (NM > NR ? NM : NR); ++r) {
+        if (r < NM) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (r < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NCOPY * (DMA_DIST - 1)) : "memory");
+    __syncthreads();
+  };
+#pragma unroll
+  for (int q = 0; q < DMA_DIST; ++q) issue(q < nsub ? q : nsub - 1, q);
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NCOPY * (DMA_DIST - 1)) : "memory");
+  __syncthreads();
+  body(0, true);
+  for (int sub = 1; sub < nsub; ++sub) body(sub, false);
+  mm(1);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+// Forward main loop with whole 128-byte weight rows per copy. The weight rows are
+// fetched as 64-deep stages (each lane group of 8 copies one row's 128 bytes, so a
+// request is a whole cache line) into a ring of 3 slots of 32 KB; the activation rows
+// keep the 32-deep, 64-byte stages in a ring of 4 slots of 16 KB (160 KB in all).
+// Iteration t consumes activation stage t and half t % 2 of weight stage t / 2; it
+// copies activation stage t + 3 and half of the copies of weight stage t / 2 + 2, so
+// each wave issues 4 + JN copies per iteration as in mainloop_dma_g, and the same
+// vmcnt bound before each barrier leaves both rings' next stages landed. A weight
+// row's 8 chunks sit at chunk ^ ((row / 2) % 8), which keeps the 32-row fragment reads
+// (16 lanes at a time, 16 bytes each) on distinct banks; copy j of wave w covers
+// weight rows 32 j + 8 w + lane / 8. nsub (32-deep stages) must be even.
+template <int JN>
+__device__ __forceinline__ void mainloop_fwd_w64(const uint16_t* wbase, const uint32_t (&woff)[8], int wgch,
+                                                 const RmSrc& sx, uint4* smem, int kbase, int nsub,
+                                                 int tid, int lane, int wn, int wm, f32x16 (&acc)[4][4]) {
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const uint32_t lds0 = (uint32_t)(uintptr_t)smem + (uint32_t)w * 1024u;
+  constexpr uint32_t XSLOT_B = TB * 64, WSLOT_B = TB * 128, WRING_B = 4 * XSLOT_B;
+  const uint4* Xring = smem;
+  const uint4* Wring = smem + WRING_B / 16;
+  const int rsel = lane & 31, kg = lane >> 5, swx = (rsel >> 2) & 3, sww = (rsel >> 1) & 7;
+  const int nw = nsub >> 1;
+  constexpr int NCOPY = 4 + JN;   // copies per wave per iteration
+  auto copy_x = [&](int st, int slot, int j) {
+    dma16(sx.base + sx.off[j] + kbase + st * 32 + sx.gch * 8, lds0 + (uint32_t)slot * XSLOT_B + j * 4096u);
+  };
+  auto copy_w = [&](int m, int slot, int j) {   // j a compile-time index
+    dma16(wbase + woff[j] + kbase + m * 64 + wgch * 8, lds0 + WRING_B + (uint32_t)slot * WSLOT_B + j * 4096u);
+  };
+
+  bf16x8 wf[2][4], xf[2][4];
+  // fragment reads of step kk of iteration t, the first with the activation copies of
+  // stage xs, the second with half h of the weight copies of stage ws (slot wsl)
+  auto rd_issue = [&](int t, auto hsel, int kk, int set, int xs, int ws, int wsl) {
+    constexpr int H = decltype(hsel)::value;   // t % 2, compile-time so woff stays in registers
+    const uint4* Ws = Wring + (size_t)((t >> 1) % 3) * (WSLOT_B / 16);
+    const uint4* Xs = Xring + (size_t)(t & 3) * (XSLOT_B / 16);
+    const int q = (H << 1) + kk;   // 16-deep step within the weight stage
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      wf[set][i] = as_bf16x8(Ws[(wn * 128 + i * 32 + rsel) * 8 + (((q << 1) + kg) ^ sww)]);
+      if (i & 1) {
+        const int c = i >> 1;
+        if (kk == 0) {
+          if (c < JN) copy_x(xs, (t + 3) & 3, c);
+        } else {
+          copy_w(ws, wsl, 4 * H + c);
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (j < JN) xf[set][j] = as_bf16x8(Xs[(wm * JN * 32 + j * 32 + rsel) * 4 + (((kk << 1) + kg) ^ swx)]);
+      if (j & 1) {
+        const int c = 2 + (j >> 1);
+        if (kk == 0) {
+          if (c < JN) copy_x(xs, (t + 3) & 3, c);
+        } else {
+          copy_w(ws, wsl, 4 * H + c);
+        }
+      }
+    }
+  };
+  auto mm = [&](int set) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < JN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[set][i], xf[set][j], acc[i][j], 0, 0, 0);
+  };
+  auto body = [&](int t, auto hsel, bool first) {
+    const int xs = t + 3 < nsub ? t + 3 : nsub - 1;
+    const int wm_ = (t >> 1) + 2;
+    const int ws = wm_ < nw ? wm_ : nw - 1;
+    rd_issue(t, hsel, 0, 0, xs, ws, wm_ % 3);
+    if (!first) mm(1);
+    rd_issue(t, hsel, 1, 1, xs, ws, wm_ % 3);
+    mm(0);
+    constexpr int NR = 4 + JN;
+    constexpr int NM = 4 * JN;
+    if (first) __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
+    for (int q = 0; q < (first ? 1 : 2); ++q) {
+      if constexpr (JN == 4) {   // 8 reads: one between each pair of MFMAs
         for (int r = 0; r < 8; ++r) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
           __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
@@ -527,15 +621,31 @@ __device__ __forceinline__ void mainloop_dma_g(const SA& sa, const SB& sb, uint4
       }
     }
     __builtin_amdgcn_sched_barrier(0);
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NCOPY * (DMA_SLOTS - 2)) : "memory");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NCOPY * 2) : "memory");
     __syncthreads();
   };
+  // prologue: weight stage 0, activation stages 0 and 1, weight stage 1, activation
+  // stage 2; then wait for weight stage 0 and activation stage 0
 #pragma unroll
-  for (int q = 0; q < DMA_SLOTS - 1; ++q) issue(q < nsub ? q : nsub - 1, q);
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NCOPY * (DMA_SLOTS - 2)) : "memory");
+  for (int j = 0; j < 8; ++j) copy_w(0, 0, j);
+#pragma unroll
+  for (int j = 0; j < JN; ++j) copy_x(0, 0, j);
+#pragma unroll
+  for (int j = 0; j < JN; ++j) copy_x(1, 1, j);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) copy_w(nw > 1 ? 1 : 0, 1, j);
+#pragma unroll
+  for (int j = 0; j < JN; ++j) copy_x(nsub > 2 ? 2 : nsub - 1, 2, j);
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NCOPY * 2) : "memory");
   __syncthreads();
-  body(0, true);
-  for (int sub = 1; sub < nsub; ++sub) body(sub, false);
+  constexpr std::integral_constant<int, 0> even{};
+  constexpr std::integral_constant<int, 1> odd{};
+  body(0, even, true);
+  body(1, odd, false);
+  for (int t = 2; t < nsub; t += 2) {
+    body(t, even, false);
+    body(t + 1, odd, false);
+  }
   mm(1);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
@@ -549,7 +659,7 @@ template <int EPI, bool KFULL, int TM = TB>
 __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_nt(NtArgs a) {
   static_assert(TM == TB || (TM == 128 && KFULL), "128-row tiles need whole 64-deep stages");
   // 128 KB: two 64-deep stages [A tile | B tile], or the full-K path's four 32-deep ones
-  __shared__ uint4 smem[4 * TILE_U4];
+  __shared__ uint4 smem[LDS_FWD_U4];
   const int ktiles = (a.K + TK - 1) / TK;
   int e, m0, mend, nt, k0 = 0, nk = ktiles, part = 0, S = 1, slot = 0, cidx = 0;
   if (KFULL) {
@@ -597,44 +707,27 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_nt(NtArgs a) {
   int jn = 4;   // 32-row blocks per wave
 
   if (KFULL) {
-    // rows (tid / 4) + 64 j of both operands, in the order the copies fill a stage
-    uint32_t aoff[4], boff[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int R = (tid >> 2) + 64 * j;
-      int p = m0 + R;
-      p = p < mend ? p : mend - 1;
-      const int src = a.a_gather ? a.a_gather[p] / a.a_div : p;
-      aoff[j] = (uint32_t)src * (uint32_t)a.K;
-      int wrow;
-      if (EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_STEP) {
-        int c = nt * 128 + (R >> 7) * 64 + (R & 63);
-        c = c < a.I ? c : c % a.I;
-        wrow = ((R >> 6) & 1) * a.I + c;
-      } else {
-        wrow = nt * TB + R;
-        wrow = wrow < a.NB ? wrow : wrow % a.NB;
-      }
-      boff[j] = (uint32_t)wrow * (uint32_t)a.K;
-    }
-    RmSrc sw, sx;   // weight side, activation side
-    sw.base = lb.base;
+    // activation rows (tid / 4) + 64 j, in the order the copies fill a stage; the
+    // weight rows are lrow + 32 j (lb.off)
+    RmSrc sx;
     sx.base = a.A;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      sw.off[j] = boff[j];
-      sx.off[j] = aoff[j];
+      int p = m0 + (tid >> 2) + 64 * j;
+      p = p < mend ? p : mend - 1;
+      const int src = a.a_gather ? a.a_gather[p] / a.a_div : p;
+      sx.off[j] = (uint32_t)src * (uint32_t)a.K;
     }
-    sw.init(tid);
     sx.init(tid);
+    const int wgch = (lane & 7) ^ ((4 * wid + (lane >> 4)) & 7);
     if (mend - m0 <= 64) {   // a short last tile of its group: a quarter of the work
       jn = 1;
-      mainloop_dma_g<false, false, 1>(sw, sx, smem, k0 * TK, nk * 2, tid, lane, wn, wm, acc);
+      mainloop_fwd_w64<1>(lb.base, lb.off, wgch, sx, smem, k0 * TK, nk * 2, tid, lane, wn, wm, acc);
     } else if (TM == 128) {
       jn = 2;
-      mainloop_dma_g<false, false, 2>(sw, sx, smem, k0 * TK, nk * 2, tid, lane, wn, wm, acc);
+      mainloop_fwd_w64<2>(lb.base, lb.off, wgch, sx, smem, k0 * TK, nk * 2, tid, lane, wn, wm, acc);
     } else {
-      mainloop_dma_g<false, false, 4>(sw, sx, smem, k0 * TK, nk * 2, tid, lane, wn, wm, acc);
+      mainloop_fwd_w64<4>(lb.base, lb.off, wgch, sx, smem, k0 * TK, nk * 2, tid, lane, wn, wm, acc);
     }
     // a part of a split tile: the last of its parts to arrive finishes the tile
     if (S > 1 && !split_reduce(acc, a.split_ws, a.split_cnt, slot, part, S, cidx, smem, tid,
@@ -779,7 +872,7 @@ struct DgradArgs {
 // da, the gradient of the SwiGLU / SwiGLUStep output, and store dh = act'(h) da.
 template <int ACT>
 __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_dgrad(DgradArgs a) {
-  __shared__ uint4 smem[4 * TILE_U4];
+  __shared__ uint4 smem[LDS_U4];
   // nt: tile of K (output columns); [k0, k0 + nk): this workgroup's 32-deep stages of N
   int e, m0, mend, nt, k0, nk, part, S, slot = 0, cidx = 0;
   if (!deal_tile_split(a.ends, a.E, a.m_cap, a.n_tiles, a.n_res, a.N / 32, e, m0, mend, nt, k0, nk,
@@ -872,7 +965,7 @@ struct WgradArgs {
 
 template <bool OUT_F32>
 __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_wgrad(WgradArgs a) {
-  __shared__ uint4 smem[4 * TILE_U4];
+  __shared__ uint4 smem[LDS_U4];
   // A tile's cost is its group's row count. Chunks of k_tiles tiles (one row of
   // output tiles, sharing one G slice) go round-robin over the 8 XCDs, so every XCD
   // works through its share of each group at the same time: contiguous ranges would
