@@ -332,25 +332,25 @@ __device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
   asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(lds) : "memory");
 }
 
-// The full-K main loops (mainloop_dma_g below for the backward products,
-// mainloop_fwd_w64 for the forward) are pipelines of 32-deep stages fetched straight
-// into LDS without passing through registers (32 KB a stage: the 256 activation
-// rows, then the 256 weight rows; 64 bytes of a row-major operand's row). Stage
-// s + DMA_DIST is requested while stage s is consumed, so a copy has about two
-// stages of MFMA work to land, and each copy is issued right after one fragment read
-// so the copies go out spread over the stage's MFMAs (issued back to back, they stall
-// the wave on the address unit ahead of its MFMAs). A row-major row's four 16-byte
-// chunks are stored at chunk ^ ((row / 4) % 4), which keeps the 32-row fragment
-// reads free of bank conflicts; copy j of wave w covers rows 64 j + 16 w + lane / 4,
-// so lane l fetches global chunk (l % 4) ^ ((l / 16) % 4). The loop is rotated by one
-// 16-deep step: the last step of a stage runs after the barrier, under the first
-// fragment reads of the next. Stages past the end re-load the last one into a slot
-// nobody reads, which keeps the copy count uniform.
+// The backward products' full-K main loop (mainloop_dma_g below; the forward's is
+// mainloop_fwd64) is a pipeline of 32-deep stages fetched straight into LDS without
+// passing through registers (32 KB a stage: the 256 activation rows, then the 256
+// weight rows; 64 bytes of a row-major operand's row). Stage s + DMA_DIST is requested
+// while stage s is consumed, so a copy has about two stages of MFMA work to land, and
+// each copy is issued right after one fragment read so the copies go out spread over
+// the stage's MFMAs (issued back to back, they stall the wave on the address unit
+// ahead of its MFMAs). A row-major row's four 16-byte chunks are stored at
+// chunk ^ ((row / 4) % 4), which keeps the 32-row fragment reads free of bank
+// conflicts; copy j of wave w covers rows 64 j + 16 w + lane / 4, so lane l fetches
+// global chunk (l % 4) ^ ((l / 16) % 4). The loop is rotated by one 16-deep step: the
+// last step of a stage runs after the barrier, under the first fragment reads of the
+// next. Stages past the end re-load the last one into a slot nobody reads, which keeps
+// the copy count uniform.
 constexpr int DMA_SLOTS = 4;
 constexpr int DMA_DIST = DMA_SLOTS - 1;   // stages between a copy and its use
 constexpr int DMA_STAGE_U4 = 2 * TB * 32 * 2 / 16;   // uint4 slots per 32-deep stage
 constexpr int LDS_U4 = DMA_SLOTS * DMA_STAGE_U4;      // 128 KB: dgrad / wgrad
-constexpr int LDS_FWD_U4 = (4 * TB * 64 + 3 * TB * 128) / 16;   // 160 KB: mainloop_fwd_w64
+constexpr int LDS_FWD_U4 = 5 * TB * 128 / 16;                    // 160 KB: mainloop_fwd64
 static_assert(LDS_U4 >= 4 * TILE_U4, "the partial-K path's two 64-deep stages fit");
 
 
@@ -416,7 +416,7 @@ template <bool A_K, bool B_K, int JN, class SA, class SB>
 __device__ __forceinline__ void mainloop_dma_g(const SA& sa, const SB& sb, uint4* smem, int kbase,
                                                int nsub, int tid, int lane, int wn, int wm,
                                                f32x16 (&acc)[4][4]) {
-  static_assert(A_K, "the forward (both operands row-major) runs mainloop_fwd_w64");
+  static_assert(A_K, "the forward (both operands row-major) runs mainloop_fwd64");
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const uint32_t lds0 = (uint32_t)(uintptr_t)smem + (uint32_t)w * 1024u;
   const int rsel = lane & 31, kg = lane >> 5, sw = (rsel >> 2) & 3;
@@ -525,67 +525,57 @@ __device__ __forceinline__ void mainloop_dma_g(const SA& sa, const SB& sb, uint4
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
-// Forward main loop with whole 128-byte weight rows per copy. The weight rows are
-// fetched as 64-deep stages (each lane group of 8 copies one row's 128 bytes, so a
-// request is a whole cache line) into a ring of 3 slots of 32 KB; the activation rows
-// keep the 32-deep, 64-byte stages in a ring of 4 slots of 16 KB (160 KB in all).
-// Iteration t consumes activation stage t and half t % 2 of weight stage t / 2; it
-// copies activation stage t + 3 and half of the copies of weight stage t / 2 + 2, so
-// each wave issues 4 + JN copies per iteration as in mainloop_dma_g, and the same
-// vmcnt bound before each barrier leaves both rings' next stages landed. A weight
-// row's 8 chunks sit at chunk ^ ((row / 2) % 8), which keeps the 32-row fragment reads
-// (16 lanes at a time, 16 bytes each) on distinct banks; copy j of wave w covers
-// weight rows 32 j + 8 w + lane / 8. nsub (32-deep stages) must be even.
+// Forward main loop over 64-deep stages with whole 128-byte rows for both operands:
+// each lane group of 8 copies one row's 128 bytes (a whole cache line), and a row's 8
+// chunks sit at chunk ^ ((row / 2) % 8) in LDS, which keeps the 32-row fragment reads
+// (16 lanes at a time, 16 bytes each) on distinct banks. The weight rows go to a ring
+// of 3 slots of 32 KB, the activation rows (64 JN of them) to a ring of 2 slots of
+// 32 KB (160 KB in all). Iteration m consumes stage m; in its first half it copies
+// activation stage m + 1 into the other activation slot, in its second half weight
+// stage m + 2, and it ends with one barrier after waiting for all but its own weight
+// copies, so both rings' next stages have landed. Copy j of wave w covers rows
+// 32 j + 8 w + lane / 8 of either operand (woff, xoff: row offsets in elements;
+// gch: the global chunk lane l fetches, (l % 8) ^ ((row / 2) % 8)).
 template <int JN>
-__device__ __forceinline__ void mainloop_fwd_w64(const uint16_t* wbase, const uint32_t (&woff)[8], int wgch,
-                                                 const RmSrc& sx, uint4* smem, int kbase, int nsub,
-                                                 int tid, int lane, int wn, int wm, f32x16 (&acc)[4][4]) {
+__device__ __forceinline__ void mainloop_fwd64(const uint16_t* wbase, const uint32_t (&woff)[8],
+                                               const uint16_t* xbase, const uint32_t (&xoff)[8], int gch,
+                                               uint4* smem, int kbase, int nst, int tid, int lane, int wn,
+                                               int wm, f32x16 (&acc)[4][4]) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const uint32_t lds0 = (uint32_t)(uintptr_t)smem + (uint32_t)w * 1024u;
-  constexpr uint32_t XSLOT_B = TB * 64, WSLOT_B = TB * 128, WRING_B = 4 * XSLOT_B;
-  const uint4* Xring = smem;
-  const uint4* Wring = smem + WRING_B / 16;
-  const int rsel = lane & 31, kg = lane >> 5, swx = (rsel >> 2) & 3, sww = (rsel >> 1) & 7;
-  const int nw = nsub >> 1;
-  constexpr int NCOPY = 4 + JN;   // copies per wave per iteration
-  auto copy_x = [&](int st, int slot, int j) {
-    dma16(sx.base + sx.off[j] + kbase + st * 32 + sx.gch * 8, lds0 + (uint32_t)slot * XSLOT_B + j * 4096u);
+  constexpr uint32_t SLOT_B = TB * 128, XRING_B = 3 * SLOT_B;
+  constexpr int NXC = 2 * JN;     // activation copies per wave per stage (64 JN rows)
+  const int rsel = lane & 31, kg = lane >> 5, sw = (rsel >> 1) & 7;
+  auto copy_w = [&](int m, int slot, int j) {
+    dma16(wbase + woff[j] + kbase + m * 64 + gch * 8, lds0 + (uint32_t)slot * SLOT_B + j * 4096u);
   };
-  auto copy_w = [&](int m, int slot, int j) {   // j a compile-time index
-    dma16(wbase + woff[j] + kbase + m * 64 + wgch * 8, lds0 + WRING_B + (uint32_t)slot * WSLOT_B + j * 4096u);
+  auto copy_x = [&](int m, int slot, int j) {
+    dma16(xbase + xoff[j] + kbase + m * 64 + gch * 8, lds0 + XRING_B + (uint32_t)slot * SLOT_B + j * 4096u);
   };
-
   bf16x8 wf[2][4], xf[2][4];
-  // fragment reads of step kk of iteration t, the first with the activation copies of
-  // stage xs, the second with half h of the weight copies of stage ws (slot wsl)
-  auto rd_issue = [&](int t, auto hsel, int kk, int set, int xs, int ws, int wsl) {
-    constexpr int H = decltype(hsel)::value;   // t % 2, compile-time so woff stays in registers
-    const uint4* Ws = Wring + (size_t)((t >> 1) % 3) * (WSLOT_B / 16);
-    const uint4* Xs = Xring + (size_t)(t & 3) * (XSLOT_B / 16);
-    const int q = (H << 1) + kk;   // 16-deep step within the weight stage
+  // fragment reads of 16-deep step q of stage m into register set `set`; copy c of
+  // the step's 4 (after every second read) is activation copy 4 q + c of stage xs
+  // (steps 0 and 1) or weight copy 4 (q - 2) + c of stage ws (steps 2 and 3)
+  auto rd_issue = [&](int m, auto qsel, int set, int xs, int xsl, int ws, int wsl) {
+    constexpr int Q = decltype(qsel)::value;
+    const uint4* Ws = smem + (size_t)(m % 3) * (SLOT_B / 16);
+    const uint4* Xs = smem + (XRING_B + (size_t)(m & 1) * SLOT_B) / 16;
+    auto cp = [&](int c) {
+      if constexpr (Q < 2) {
+        if (4 * Q + c < NXC) copy_x(xs, xsl, 4 * Q + c);
+      } else {
+        copy_w(ws, wsl, 4 * (Q - 2) + c);
+      }
+    };
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      wf[set][i] = as_bf16x8(Ws[(wn * 128 + i * 32 + rsel) * 8 + (((q << 1) + kg) ^ sww)]);
-      if (i & 1) {
-        const int c = i >> 1;
-        if (kk == 0) {
-          if (c < JN) copy_x(xs, (t + 3) & 3, c);
-        } else {
-          copy_w(ws, wsl, 4 * H + c);
-        }
-      }
+      wf[set][i] = as_bf16x8(Ws[(wn * 128 + i * 32 + rsel) * 8 + (((Q << 1) + kg) ^ sw)]);
+      if (i & 1) cp(i >> 1);
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      if (j < JN) xf[set][j] = as_bf16x8(Xs[(wm * JN * 32 + j * 32 + rsel) * 4 + (((kk << 1) + kg) ^ swx)]);
-      if (j & 1) {
-        const int c = 2 + (j >> 1);
-        if (kk == 0) {
-          if (c < JN) copy_x(xs, (t + 3) & 3, c);
-        } else {
-          copy_w(ws, wsl, 4 * H + c);
-        }
-      }
+      if (j < JN) xf[set][j] = as_bf16x8(Xs[(wm * JN * 32 + j * 32 + rsel) * 8 + (((Q << 1) + kg) ^ sw)]);
+      if (j & 1) cp(2 + (j >> 1));
     }
   };
   auto mm = [&](int set) {
@@ -595,18 +585,9 @@ __device__ __forceinline__ void mainloop_fwd_w64(const uint16_t* wbase, const ui
       for (int j = 0; j < JN; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[set][i], xf[set][j], acc[i][j], 0, 0, 0);
   };
-  auto body = [&](int t, auto hsel, bool first) {
-    const int xs = t + 3 < nsub ? t + 3 : nsub - 1;
-    const int wm_ = (t >> 1) + 2;
-    const int ws = wm_ < nw ? wm_ : nw - 1;
-    rd_issue(t, hsel, 0, 0, xs, ws, wm_ % 3);
-    if (!first) mm(1);
-    rd_issue(t, hsel, 1, 1, xs, ws, wm_ % 3);
-    mm(0);
-    constexpr int NR = 4 + JN;
-    constexpr int NM = 4 * JN;
-    if (first) __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
-    for (int q = 0; q < (first ? 1 : 2); ++q) {
+  auto interleave = [&](int nsteps) {
+    constexpr int NR = 4 + JN, NM = 4 * JN;
+    for (int q = 0; q < nsteps; ++q) {
       if constexpr (JN == 4) {   // 8 reads: one between each pair of MFMAs
         for (int r = 0; r < 8; ++r) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -620,32 +601,38 @@ __device__ __forceinline__ void mainloop_fwd_w64(const uint16_t* wbase, const ui
         }
       }
     }
+  };
+  // iteration m: the reads of step q + 1 go between the MFMAs of step q; the first
+  // MFMAs finish the previous stage's last step (rotated loop)
+  auto body = [&](int m, bool first) {
+    const int xs = m + 1 < nst ? m + 1 : nst - 1;
+    const int ws = m + 2 < nst ? m + 2 : nst - 1;
+    const int xsl = (m + 1) & 1, wsl = (m + 2) % 3;
+    rd_issue(m, std::integral_constant<int, 0>{}, 0, xs, xsl, ws, wsl);
+    if (!first) mm(1);
+    rd_issue(m, std::integral_constant<int, 1>{}, 1, xs, xsl, ws, wsl);
+    mm(0);
+    rd_issue(m, std::integral_constant<int, 2>{}, 0, xs, xsl, ws, wsl);
+    mm(1);
+    rd_issue(m, std::integral_constant<int, 3>{}, 1, xs, xsl, ws, wsl);
+    mm(0);
+    if (first) __builtin_amdgcn_sched_group_barrier(0x100, 4 + JN, 0);
+    interleave(first ? 3 : 4);
     __builtin_amdgcn_sched_barrier(0);
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NCOPY * 2) : "memory");
+    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");   // only this stage's weight copies in flight
     __syncthreads();
   };
-  // prologue: weight stage 0, activation stages 0 and 1, weight stage 1, activation
-  // stage 2; then wait for weight stage 0 and activation stage 0
+  // prologue: weight stage 0, activation stage 0, weight stage 1; wait for the first two
 #pragma unroll
   for (int j = 0; j < 8; ++j) copy_w(0, 0, j);
 #pragma unroll
-  for (int j = 0; j < JN; ++j) copy_x(0, 0, j);
+  for (int j = 0; j < NXC; ++j) copy_x(0, 0, j);
 #pragma unroll
-  for (int j = 0; j < JN; ++j) copy_x(1, 1, j);
-#pragma unroll
-  for (int j = 0; j < 8; ++j) copy_w(nw > 1 ? 1 : 0, 1, j);
-#pragma unroll
-  for (int j = 0; j < JN; ++j) copy_x(nsub > 2 ? 2 : nsub - 1, 2, j);
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NCOPY * 2) : "memory");
+  for (int j = 0; j < 8; ++j) copy_w(nst > 1 ? 1 : 0, 1, j);
+  asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
   __syncthreads();
-  constexpr std::integral_constant<int, 0> even{};
-  constexpr std::integral_constant<int, 1> odd{};
-  body(0, even, true);
-  body(1, odd, false);
-  for (int t = 2; t < nsub; t += 2) {
-    body(t, even, false);
-    body(t + 1, odd, false);
-  }
+  body(0, true);
+  for (int m = 1; m < nst; ++m) body(m, false);
   mm(1);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
@@ -707,27 +694,16 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_nt(NtArgs a) {
   int jn = 4;   // 32-row blocks per wave
 
   if (KFULL) {
-    // activation rows (tid / 4) + 64 j, in the order the copies fill a stage; the
-    // weight rows are lrow + 32 j (lb.off)
-    RmSrc sx;
-    sx.base = a.A;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      int p = m0 + (tid >> 2) + 64 * j;
-      p = p < mend ? p : mend - 1;
-      const int src = a.a_gather ? a.a_gather[p] / a.a_div : p;
-      sx.off[j] = (uint32_t)src * (uint32_t)a.K;
-    }
-    sx.init(tid);
+    // rows lrow + 32 j of both operands (la.off, lb.off), whole 128-byte rows per copy
     const int wgch = (lane & 7) ^ ((4 * wid + (lane >> 4)) & 7);
     if (mend - m0 <= 64) {   // a short last tile of its group: a quarter of the work
       jn = 1;
-      mainloop_fwd_w64<1>(lb.base, lb.off, wgch, sx, smem, k0 * TK, nk * 2, tid, lane, wn, wm, acc);
+      mainloop_fwd64<1>(lb.base, lb.off, la.base, la.off, wgch, smem, k0 * TK, nk, tid, lane, wn, wm, acc);
     } else if (TM == 128) {
       jn = 2;
-      mainloop_fwd_w64<2>(lb.base, lb.off, wgch, sx, smem, k0 * TK, nk * 2, tid, lane, wn, wm, acc);
+      mainloop_fwd64<2>(lb.base, lb.off, la.base, la.off, wgch, smem, k0 * TK, nk, tid, lane, wn, wm, acc);
     } else {
-      mainloop_fwd_w64<4>(lb.base, lb.off, wgch, sx, smem, k0 * TK, nk * 2, tid, lane, wn, wm, acc);
+      mainloop_fwd64<4>(lb.base, lb.off, la.base, la.off, wgch, smem, k0 * TK, nk, tid, lane, wn, wm, acc);
     }
     // a part of a split tile: the last of its parts to arrive finishes the tile
     if (S > 1 && !split_reduce(acc, a.split_ws, a.split_cnt, slot, part, S, cidx, smem, tid,
