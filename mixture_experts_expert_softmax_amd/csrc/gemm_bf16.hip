@@ -528,22 +528,27 @@ __device__ __forceinline__ void mainloop_dma_g(const SA& sa, const SB& sb, uint4
 // Forward main loop over 64-deep stages with whole 128-byte rows for both operands:
 // each lane group of 8 copies one row's 128 bytes (a whole cache line), and a row's 8
 // chunks sit at chunk ^ ((row / 2) % 8) in LDS, which keeps the 32-row fragment reads
-// (16 lanes at a time, 16 bytes each) on distinct banks. The weight rows go to a ring
-// of 3 slots of 32 KB, the activation rows (64 JN of them) to a ring of 2 slots of
-// 32 KB (160 KB in all). Iteration m consumes stage m; in its first half it copies
-// activation stage m + 1 into the other activation slot, in its second half weight
-// stage m + 2, and it ends with one barrier after waiting for all but its own weight
-// copies, so both rings' next stages have landed. Copy j of wave w covers rows
-// 32 j + 8 w + lane / 8 of either operand (woff, xoff: row offsets in elements;
-// gch: the global chunk lane l fetches, (l % 8) ^ ((row / 2) % 8)).
-template <int JN>
+// (16 lanes at a time, 16 bytes each) on distinct banks. The five 32 KB slots of LDS
+// (160 KB) hold NWS weight slots and 5 - NWS activation slots (64 JN rows each); a
+// ring of n slots has its stage m + n - 1 copied while stage m is consumed. Iteration
+// m copies the shorter ring's next stage in its first half and the longer ring's in
+// its second half, and ends with one barrier after waiting for all but the longer
+// ring's copies, so both rings' next stages have landed. Two weight and three
+// activation slots measured best (the activation rows, gathered or shared by many
+// column tiles, come from L2 and the Infinity Cache and gain from the longer lead;
+// expert shard -4%, the Mixtral layer unchanged). Copy j of wave w covers rows
+// 32 j + 8 w + lane / 8 of either operand (woff, xoff: row offsets in elements; gch:
+// the global chunk lane l fetches, (l % 8) ^ ((row / 2) % 8)).
+template <int JN, int NWS = 2>
 __device__ __forceinline__ void mainloop_fwd64(const uint16_t* wbase, const uint32_t (&woff)[8],
                                                const uint16_t* xbase, const uint32_t (&xoff)[8], int gch,
                                                uint4* smem, int kbase, int nst, int tid, int lane, int wn,
                                                int wm, f32x16 (&acc)[4][4]) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const uint32_t lds0 = (uint32_t)(uintptr_t)smem + (uint32_t)w * 1024u;
-  constexpr uint32_t SLOT_B = TB * 128, XRING_B = 3 * SLOT_B;
+  constexpr int NXS = 5 - NWS;   // weight / activation slots; a stage is copied NWS - 1 / NXS - 1 ahead
+  constexpr uint32_t SLOT_B = TB * 128, XRING_B = NWS * SLOT_B;
+  static_assert(NWS >= 2 && NXS >= 2, "both rings need a slot beside the one being read");
   constexpr int NXC = 2 * JN;     // activation copies per wave per stage (64 JN rows)
   const int rsel = lane & 31, kg = lane >> 5, sw = (rsel >> 1) & 7;
   auto copy_w = [&](int m, int slot, int j) {
@@ -558,13 +563,15 @@ __device__ __forceinline__ void mainloop_fwd64(const uint16_t* wbase, const uint
   // (steps 0 and 1) or weight copy 4 (q - 2) + c of stage ws (steps 2 and 3)
   auto rd_issue = [&](int m, auto qsel, int set, int xs, int xsl, int ws, int wsl) {
     constexpr int Q = decltype(qsel)::value;
-    const uint4* Ws = smem + (size_t)(m % 3) * (SLOT_B / 16);
-    const uint4* Xs = smem + (XRING_B + (size_t)(m & 1) * SLOT_B) / 16;
-    auto cp = [&](int c) {
-      if constexpr (Q < 2) {
-        if (4 * Q + c < NXC) copy_x(xs, xsl, 4 * Q + c);
+    const uint4* Ws = smem + (size_t)(m % NWS) * (SLOT_B / 16);
+    const uint4* Xs = smem + (XRING_B + (size_t)(m % NXS) * SLOT_B) / 16;
+    auto cp = [&](int c) {   // the ring with the shorter distance is copied first
+      constexpr bool XFIRST = NXS <= NWS;
+      constexpr int QX = XFIRST ? 0 : 2, QW = XFIRST ? 2 : 0;
+      if constexpr (Q >= QX && Q < QX + 2) {
+        if (4 * (Q - QX) + c < NXC) copy_x(xs, xsl, 4 * (Q - QX) + c);
       } else {
-        copy_w(ws, wsl, 4 * (Q - 2) + c);
+        copy_w(ws, wsl, 4 * (Q - QW) + c);
       }
     };
 #pragma unroll
@@ -605,9 +612,9 @@ __device__ __forceinline__ void mainloop_fwd64(const uint16_t* wbase, const uint
   // iteration m: the reads of step q + 1 go between the MFMAs of step q; the first
   // MFMAs finish the previous stage's last step (rotated loop)
   auto body = [&](int m, bool first) {
-    const int xs = m + 1 < nst ? m + 1 : nst - 1;
-    const int ws = m + 2 < nst ? m + 2 : nst - 1;
-    const int xsl = (m + 1) & 1, wsl = (m + 2) % 3;
+    const int xs = m + NXS - 1 < nst ? m + NXS - 1 : nst - 1;
+    const int ws = m + NWS - 1 < nst ? m + NWS - 1 : nst - 1;
+    const int xsl = (m + NXS - 1) % NXS, wsl = (m + NWS - 1) % NWS;
     rd_issue(m, std::integral_constant<int, 0>{}, 0, xs, xsl, ws, wsl);
     if (!first) mm(1);
     rd_issue(m, std::integral_constant<int, 1>{}, 1, xs, xsl, ws, wsl);
@@ -619,17 +626,23 @@ __device__ __forceinline__ void mainloop_fwd64(const uint16_t* wbase, const uint
     if (first) __builtin_amdgcn_sched_group_barrier(0x100, 4 + JN, 0);
     interleave(first ? 3 : 4);
     __builtin_amdgcn_sched_barrier(0);
-    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");   // only this stage's weight copies in flight
+    // only the copies of the ring with the longer distance, issued last, stay in flight
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NXS <= NWS ? 8 : NXC) : "memory");
     __syncthreads();
   };
-  // prologue: weight stage 0, activation stage 0, weight stage 1; wait for the first two
+  // prologue: stage 0 of both rings, then the longer ring's stage 1; wait for stage 0
 #pragma unroll
   for (int j = 0; j < 8; ++j) copy_w(0, 0, j);
 #pragma unroll
   for (int j = 0; j < NXC; ++j) copy_x(0, 0, j);
+  if constexpr (NWS > NXS) {
 #pragma unroll
-  for (int j = 0; j < 8; ++j) copy_w(nst > 1 ? 1 : 0, 1, j);
-  asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    for (int j = 0; j < 8; ++j) copy_w(nst > 1 ? 1 : 0, 1, j);
+  } else if constexpr (NXS > NWS) {
+#pragma unroll
+    for (int j = 0; j < NXC; ++j) copy_x(nst > 1 ? 1 : 0, 1, j);
+  }
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NWS > NXS ? 8 : NXS > NWS ? NXC : 0) : "memory");
   __syncthreads();
   body(0, true);
   for (int m = 1; m < nst; ++m) body(m, false);
