@@ -895,29 +895,52 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_dgrad(DgradArgs a) {
                              block_mask(m0 + wm * 128, mend, 4, c0 + wn * 128, a.K)))
     return;
   const int hi4 = (lane >> 5) * 4;
-  float lim = 0.f;
-  if (ACT == 2) lim = a.limits ? a.limits[e] : a.def_limit;
+  if constexpr (ACT == 0) {
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int p = m0 + wm * 128 + j * 32 + (lane & 31);
-    if (p >= mend) continue;
-    uint16_t* crow = a.DX + (int64_t)p * (ACT ? 2 * a.K : a.K);
-    const float* hrow = ACT ? a.h + (int64_t)p * 2 * a.K : nullptr;
+    for (int j = 0; j < 4; ++j) {
+      const int p = m0 + wm * 128 + j * 32 + (lane & 31);
+      if (p >= mend) continue;
+      uint16_t* crow = a.DX + (int64_t)p * a.K;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int col = c0 + wn * 128 + i * 32 + q * 8 + hi4;
-        if (col >= a.K) continue;
-        if (ACT == 0) {
+        for (int q = 0; q < 4; ++q) {
+          const int col = c0 + wn * 128 + i * 32 + q * 8 + hi4;
+          if (col >= a.K) continue;
           *reinterpret_cast<uint2*>(crow + col) =
               make_uint2(pack_bf16x2(acc[i][j][q * 4 + 0], acc[i][j][q * 4 + 1]),
                          pack_bf16x2(acc[i][j][q * 4 + 2], acc[i][j][q * 4 + 3]));
-        } else {
-          const float4 hu = *reinterpret_cast<const float4*>(hrow + col);
-          const float4 hg = *reinterpret_cast<const float4*>(hrow + a.K + col);
-          const float us[4] = {hu.x, hu.y, hu.z, hu.w};
-          const float gs[4] = {hg.x, hg.y, hg.z, hg.w};
+        }
+    }
+  } else {
+    // activation backward: per 32-row block, all 32 float4 of the rows' h (u and g) are
+    // loaded before any is used (rows past the group and columns past K read a valid
+    // address and store nothing), so a block costs one memory latency, not several
+    float lim = 0.f;
+    if (ACT == 2) lim = a.limits ? a.limits[e] : a.def_limit;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int p = m0 + wm * 128 + j * 32 + (lane & 31);
+      const bool prow = p < mend;
+      const float* hrow = a.h + (int64_t)(prow ? p : mend - 1) * 2 * a.K;
+      float4 hu[4][4], hg[4][4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          int col = c0 + wn * 128 + i * 32 + q * 8 + hi4;
+          col = col < a.K ? col : a.K - 4;
+          hu[i][q] = *reinterpret_cast<const float4*>(hrow + col);
+          hg[i][q] = *reinterpret_cast<const float4*>(hrow + a.K + col);
+        }
+      uint16_t* crow = a.DX + (int64_t)p * 2 * a.K;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int col = c0 + wn * 128 + i * 32 + q * 8 + hi4;
+          const float us[4] = {hu[i][q].x, hu[i][q].y, hu[i][q].z, hu[i][q].w};
+          const float gs[4] = {hg[i][q].x, hg[i][q].y, hg[i][q].z, hg[i][q].w};
           float du[4], dg[4];
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
@@ -934,11 +957,14 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_dgrad(DgradArgs a) {
             du[r] = da * (g * sg) * mu;
             dg[r] = da * u * (sg * (1.0f + g * (1.0f - sg))) * mg;
           }
-          *reinterpret_cast<uint2*>(crow + col) = make_uint2(pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3]));
-          *reinterpret_cast<uint2*>(crow + a.K + col) =
-              make_uint2(pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3]));
+          if (prow && col < a.K) {
+            *reinterpret_cast<uint2*>(crow + col) =
+                make_uint2(pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3]));
+            *reinterpret_cast<uint2*>(crow + a.K + col) =
+                make_uint2(pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3]));
+          }
         }
-      }
+    }
   }
 }
 
