@@ -539,23 +539,29 @@ __device__ __forceinline__ void mainloop_dma_g(const SA& sa, const SB& sb, uint4
 // expert shard -4%, the Mixtral layer unchanged). Copy j of wave w covers rows
 // 32 j + 8 w + lane / 8 of either operand (woff, xoff: row offsets in elements; gch:
 // the global chunk lane l fetches, (l % 8) ^ ((row / 2) % 8)).
-template <int JN, int NWS = 2>
+template <int JN>
 __device__ __forceinline__ void mainloop_fwd64(const uint16_t* wbase, const uint32_t (&woff)[8],
                                                const uint16_t* xbase, const uint32_t (&xoff)[8], int gch,
                                                uint4* smem, int kbase, int nst, int tid, int lane, int wn,
                                                int wm, f32x16 (&acc)[4][4]) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const uint32_t lds0 = (uint32_t)(uintptr_t)smem + (uint32_t)w * 1024u;
-  constexpr int NXS = 5 - NWS;   // weight / activation slots; a stage is copied NWS - 1 / NXS - 1 ahead
-  constexpr uint32_t SLOT_B = TB * 128, XRING_B = NWS * SLOT_B;
+  // weight / activation slots (a ring of n slots copies its stages n - 1 ahead): the
+  // activation slot holds 64 JN rows, so smaller tiles get more of them
+  constexpr uint32_t SLOT_B = TB * 128, XSLOT_B = 64 * JN * 128;
+  constexpr int NWS = JN == 4 ? 2 : 3;
+  constexpr int NXS = (int)((5 * SLOT_B - NWS * SLOT_B) / XSLOT_B);
+  constexpr uint32_t XRING_B = NWS * SLOT_B;
   static_assert(NWS >= 2 && NXS >= 2, "both rings need a slot beside the one being read");
+  static_assert(NWS * SLOT_B + NXS * XSLOT_B <= 5 * SLOT_B, "the rings exceed 160 KB");
+  constexpr int DW = NWS - 1, DX = NXS - 1;   // copy lead of each ring, in stages
   constexpr int NXC = 2 * JN;     // activation copies per wave per stage (64 JN rows)
   const int rsel = lane & 31, kg = lane >> 5, sw = (rsel >> 1) & 7;
   auto copy_w = [&](int m, int slot, int j) {
     dma16(wbase + woff[j] + kbase + m * 64 + gch * 8, lds0 + (uint32_t)slot * SLOT_B + j * 4096u);
   };
   auto copy_x = [&](int m, int slot, int j) {
-    dma16(xbase + xoff[j] + kbase + m * 64 + gch * 8, lds0 + XRING_B + (uint32_t)slot * SLOT_B + j * 4096u);
+    dma16(xbase + xoff[j] + kbase + m * 64 + gch * 8, lds0 + XRING_B + (uint32_t)slot * XSLOT_B + j * 4096u);
   };
   bf16x8 wf[2][4], xf[2][4];
   // fragment reads of 16-deep step q of stage m into register set `set`; copy c of
@@ -564,7 +570,7 @@ __device__ __forceinline__ void mainloop_fwd64(const uint16_t* wbase, const uint
   auto rd_issue = [&](int m, auto qsel, int set, int xs, int xsl, int ws, int wsl) {
     constexpr int Q = decltype(qsel)::value;
     const uint4* Ws = smem + (size_t)(m % NWS) * (SLOT_B / 16);
-    const uint4* Xs = smem + (XRING_B + (size_t)(m % NXS) * SLOT_B) / 16;
+    const uint4* Xs = smem + (XRING_B + (size_t)(m % NXS) * XSLOT_B) / 16;
     auto cp = [&](int c) {   // the ring with the shorter distance is copied first
       constexpr bool XFIRST = NXS <= NWS;
       constexpr int QX = XFIRST ? 0 : 2, QW = XFIRST ? 2 : 0;
@@ -630,19 +636,22 @@ __device__ __forceinline__ void mainloop_fwd64(const uint16_t* wbase, const uint
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NXS <= NWS ? 8 : NXC) : "memory");
     __syncthreads();
   };
-  // prologue: stage 0 of both rings, then the longer ring's stage 1; wait for stage 0
+  // prologue: the stages before each ring's first in-loop copy, in stage order; then
+  // wait for stage 0 of both (all copies of later stages may stay in flight)
 #pragma unroll
-  for (int j = 0; j < 8; ++j) copy_w(0, 0, j);
+  for (int st = 0; st < (DW > DX ? DW : DX); ++st) {
+    if (st < DW) {
 #pragma unroll
-  for (int j = 0; j < NXC; ++j) copy_x(0, 0, j);
-  if constexpr (NWS > NXS) {
+      for (int j = 0; j < 8; ++j) copy_w(st < nst ? st : nst - 1, st, j);
+    }
+    if (st < DX) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) copy_w(nst > 1 ? 1 : 0, 1, j);
-  } else if constexpr (NXS > NWS) {
-#pragma unroll
-    for (int j = 0; j < NXC; ++j) copy_x(nst > 1 ? 1 : 0, 1, j);
+      for (int j = 0; j < NXC; ++j) copy_x(st < nst ? st : nst - 1, st, j);
+    }
   }
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NWS > NXS ? 8 : NXS > NWS ? NXC : 0) : "memory");
+  constexpr int LATER = 8 * (DW - 1) + NXC * (DX - 1);
+  static_assert(LATER + 8 + NXC <= 63, "copies in flight exceed the vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LATER) : "memory");
   __syncthreads();
   body(0, true);
   for (int m = 1; m < nst; ++m) body(m, false);
