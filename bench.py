@@ -524,7 +524,6 @@ def secondary_measurements(progress):
 
     progress("secondary: BGMV MoE-LoRA H=3072 rank 32, 4 LoRAs x 8 experts, top-2")
     res["bgmv"] = _bgmv_points(flush, dev)
-    del flush
 
     progress("secondary: route + sort at T=262144, 256 experts, top-8")
     T2, E2, k2 = 262144, 256, 8
@@ -535,6 +534,7 @@ def secondary_measurements(progress):
     ws2 = torch.empty(M.lib().moe_sort_workspace_size(T2, k2, E2), dtype=torch.uint8, device=dev)
     so2 = M.moe_sort(ids2, E2, workspace=ws2)
     ms_s = _time(lambda: M.moe_sort(ids2, E2, workspace=ws2, out=so2), reps=20, flush=flush)  # 34 MB
+    del flush
     route_bytes = T2 * E2 * 4 + T2 * k2 * 8
     sort_bytes = T2 * k2 * 4 * 2 + T2 * k2 * 8   # ids read twice, e2p + p2e written
     res["route_large"] = {"ms": round(ms_r, 4), "gbs": round(route_bytes / (ms_r * 1e-3) / 1e9, 1),

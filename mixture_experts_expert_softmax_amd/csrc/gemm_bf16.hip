@@ -580,16 +580,28 @@ __device__ __forceinline__ void mainloop_fwd64(const uint16_t* wbase, const uint
         copy_w(ws, wsl, 4 * (Q - QW) + c);
       }
     };
+    // read order wf[0], xf[0 .. JN-1], wf[1 .. 3]: the order in which the next step's
+    // MFMAs (weight fragment outer) first need them, so that each read is issued at
+    // least six MFMAs before its first use; a copy follows every second read
+    auto rd = [&](int r) {
+      if (r == 0) {
+        wf[set][0] = as_bf16x8(Ws[(wn * 128 + rsel) * 8 + (((Q << 1) + kg) ^ sw)]);
+      } else if (r <= JN) {
+        const int j = r - 1;
+        xf[set][j] = as_bf16x8(Xs[(wm * JN * 32 + j * 32 + rsel) * 8 + (((Q << 1) + kg) ^ sw)]);
+      } else {
+        const int i = r - JN;
+        wf[set][i] = as_bf16x8(Ws[(wn * 128 + i * 32 + rsel) * 8 + (((Q << 1) + kg) ^ sw)]);
+      }
+    };
+    constexpr int NRD = 4 + JN;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      wf[set][i] = as_bf16x8(Ws[(wn * 128 + i * 32 + rsel) * 8 + (((Q << 1) + kg) ^ sw)]);
-      if (i & 1) cp(i >> 1);
+    for (int r = 0; r < NRD; ++r) {
+      rd(r);
+      if ((r & 1) && (r >> 1) < 4) cp(r >> 1);
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if (j < JN) xf[set][j] = as_bf16x8(Xs[(wm * JN * 32 + j * 32 + rsel) * 8 + (((Q << 1) + kg) ^ sw)]);
-      if (j & 1) cp(2 + (j >> 1));
-    }
+    for (int c = NRD / 2; c < 4; ++c) cp(c);
   };
   auto mm = [&](int set) {
 #pragma unroll
