@@ -730,18 +730,15 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_nt(NtArgs a) {
   if (KFULL) {
     // rows lrow + 32 j of both operands (la.off, lb.off), whole 128-byte rows per copy
     const int wgch = (lane & 7) ^ ((4 * wid + (lane >> 4)) & 7);
-    // a short last tile of its group runs only the 32-row blocks it needs per row
-    // wave (JN of 4), and copies only those 64 JN activation rows
+    // a short last tile of its group (at most 64 rows) runs one 32-row block per row
+    // wave and copies only its first 64 activation rows
     const int rows = mend - m0;
     if (rows <= 64) {
       jn = 1;
       mainloop_fwd64<1>(lb.base, lb.off, la.base, la.off, wgch, smem, k0 * TK, nk, tid, lane, wn, wm, acc);
-    } else if (TM == 128 || rows <= 128) {
+    } else if (TM == 128) {
       jn = 2;
       mainloop_fwd64<2>(lb.base, lb.off, la.base, la.off, wgch, smem, k0 * TK, nk, tid, lane, wn, wm, acc);
-    } else if (rows <= 192) {
-      jn = 3;
-      mainloop_fwd64<3>(lb.base, lb.off, la.base, la.off, wgch, smem, k0 * TK, nk, tid, lane, wn, wm, acc);
     } else {
       mainloop_fwd64<4>(lb.base, lb.off, la.base, la.off, wgch, smem, k0 * TK, nk, tid, lane, wn, wm, acc);
     }
