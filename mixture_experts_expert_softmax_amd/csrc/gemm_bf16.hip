@@ -1000,24 +1000,40 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_dgrad(DgradArgs a) {
 struct WgradArgs {
   const uint16_t* G; const uint16_t* X; const int32_t* ends; int E; int m_cap;
   int N; int K; int n_tiles; int k_tiles; void* DW;
+  int chunk;   // consecutive tiles an XCD takes at a time
 };
+constexpr int WG_KG = 8;       // k tiles per group in the blocked tile order
 
 template <bool OUT_F32>
 __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_wgrad(WgradArgs a) {
   __shared__ uint4 smem[LDS_U4];
-  // A tile's cost is its group's row count. Chunks of k_tiles tiles (one row of
-  // output tiles, sharing one G slice) go round-robin over the 8 XCDs, so every XCD
-  // works through its share of each group at the same time: contiguous ranges would
-  // hand whole groups to single XCDs, and the XCDs with small groups would idle
-  // while the one with the largest group still takes new workgroups.
+  // A tile's cost is its group's row count. Within a group the tiles are ordered in
+  // groups of WG_KG k tiles: all n tiles of k tiles 0..7, then of 8..15, ..., so a run
+  // of consecutive tiles is a compact block (4 n x 8 k for a chunk of 32) whose G and
+  // X slices the XCD's L2 shares (a run of one n row would re-read every X slice for
+  // each n). Chunks of a.chunk consecutive tiles go round-robin over the 8 XCDs, so
+  // every XCD works through its share of each group at the same time: contiguous
+  // ranges would hand whole groups to single XCDs, and the XCDs with small groups
+  // would idle while the one with the largest group still takes new workgroups.
   const int x = (int)(blockIdx.x & 7), s = (int)(blockIdx.x >> 3);
-  const int t = ((s / a.k_tiles) * 8 + x) * a.k_tiles + s % a.k_tiles;
   const int per_e = a.n_tiles * a.k_tiles;
+  const int t = ((s / a.chunk) * 8 + x) * a.chunk + s % a.chunk;
   const int e = t / per_e;
   if (e >= a.E) return;
   const int rem = t - e * per_e;
-  const int ntile = rem / a.k_tiles;   // rows n of dW
-  const int ktile = rem - ntile * a.k_tiles;
+  const int full_kg = a.k_tiles / WG_KG, per_full = a.n_tiles * WG_KG;
+  int kg, kgs, q;
+  if (rem < full_kg * per_full) {
+    kg = rem / per_full;
+    kgs = WG_KG;
+    q = rem - kg * per_full;
+  } else {   // the last, narrower group of k tiles
+    kg = full_kg;
+    kgs = a.k_tiles - full_kg * WG_KG;
+    q = rem - full_kg * per_full;
+  }
+  const int ntile = q / kgs;   // rows n of dW
+  const int ktile = kg * WG_KG + q % kgs;
   int start = 0;
   for (int g = 0; g < e; ++g) {
     int v = a.ends[g];
@@ -1203,9 +1219,14 @@ moe_status gemm_dgrad_enqueue(const void* G, const void* W, const int32_t* ends,
 moe_status gemm_wgrad_enqueue(const void* G, const void* X, const int32_t* ends, int E, int64_t M,
                               int N, int K, void* DW, bool out_f32, hipStream_t st) {
   WgradArgs a{reinterpret_cast<const uint16_t*>(G), reinterpret_cast<const uint16_t*>(X), ends, E,
-              (int)M, N, K, (N + TB - 1) / TB, (K + TB - 1) / TB, DW};
-  // every XCD holds ceil(chunks / 8) chunks of k_tiles tiles; the excess exits
-  const int grid = 8 * ((E * a.n_tiles + 7) / 8) * a.k_tiles;
+              (int)M, N, K, (N + TB - 1) / TB, (K + TB - 1) / TB, DW, 0};
+  // chunks of up to 32 tiles, but at least 8 chunks per group so that every XCD takes
+  // a share of every group (group sizes differ: a group's tiles cost its row count)
+  const int per_e = a.n_tiles * a.k_tiles;
+  a.chunk = std::max(1, std::min(32, per_e / 8));
+  // every XCD holds ceil(chunks / 8) chunks; the excess exits
+  const int64_t chunks = ((int64_t)E * per_e + a.chunk - 1) / a.chunk;
+  const int grid = (int)(8 * ((chunks + 7) / 8) * a.chunk);
   if (out_f32)
     k_gemm_wgrad<true><<<grid, NTHREADS, 0, st>>>(a);
   else
