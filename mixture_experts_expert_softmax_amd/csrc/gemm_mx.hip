@@ -26,7 +26,8 @@
 //
 // Tile: 256 weight rows x 256 activation rows, 4 waves of 128 x 128 (4 x 4
 // accumulators), weights as the A operand so a lane holds 4 consecutive output
-// columns. Operands are copied straight from global memory into LDS, several stages
+// columns; a tile that holds fewer rows (a small expert, an expert's tail) copies
+// and multiplies only its 32-row blocks that hold rows. Operands are copied straight from global memory into LDS, several stages
 // ahead. MXFP4: 128-deep stages of activation codes [256][8 x 16 B], weight codes
 // [256][4 x 16 B] and both operands' 4 scale bytes per row (50 KB), three slots.
 // MXFP8 / FP8: 64-deep stages of activation and weight codes [256][4 x 16 B] each
@@ -45,7 +46,9 @@ namespace {
 constexpr int MTB = 256;          // tile rows on each side
 constexpr int MTK = 128;          // contraction per stage
 constexpr int MNT = 256;          // threads
-constexpr int XT_U4 = MTB * MTK / 16;        // 2048 uint4: activation codes
+// activation codes of a 128-deep MXFP4 stage of a tile with JV 32-row blocks per
+// row-wave (64 JV rows), in uint4
+template <int JV> constexpr int xt_u4() { return JV * 64 * MTK / 16; }
 
 // Weight formats (the order of MOE_WFMT_MXFP4, MOE_WFMT_MXFP8, MOE_WFMT_FP8 minus 1).
 constexpr int WF_MXFP4 = 0, WF_MXFP8 = 1, WF_FP8 = 2;
@@ -53,8 +56,8 @@ template <int WF> constexpr int wbits() { return WF == WF_MXFP4 ? 4 : 8; }
 template <int WF> constexpr bool block_scaled() { return WF != WF_FP8; }
 // 16-byte chunks per weight row and stage, and the stage size in uint4
 template <int WF> constexpr int wch() { return MTK * wbits<WF>() / 8 / 16; }
-template <int WF> constexpr int stage_u4() {
-  return XT_U4 + MTB * wch<WF>() + (block_scaled<WF>() ? 2 * MTB / 4 : 0);
+template <int WF, int JV> constexpr int stage_u4() {
+  return xt_u4<JV>() + MTB * wch<WF>() + (block_scaled<WF>() ? 2 * MTB / 4 : 0);
 }
 // scaled-MFMA format code of the weight (A-slot) operand
 template <int WF> constexpr int a_fmt() { return WF == WF_MXFP4 ? 4 : 0; }
@@ -74,12 +77,20 @@ __device__ __forceinline__ void mx_dma16(const void* g, uint32_t lds) {
 __device__ __forceinline__ void mx_dma4(const void* g, uint32_t lds) {
   asm volatile("global_load_lds_dword %0, off" ::"v"(g), "{m0}"(lds) : "memory");
 }
-// MXFP4 stages in LDS: three slots (150 KB), copies two stages ahead
-constexpr int MX_DMA_SLOTS = 3;
-// 8-bit weight families: four slots of 64-deep stages (activation and weight codes,
-// 16 KB each, then both operands' scale words for MXFP8), copies three stages ahead
+// MXFP4 stages in LDS: three slots (up to 150 KB) two stages ahead, or four slots
+// three stages ahead when the tile has at most 128 activation rows (34 KB a stage)
+template <int JV> constexpr int mx_dma_slots() { return JV <= 2 ? 4 : 3; }
+// 8-bit weight families: four slots of 64-deep stages (activation codes 64 JV x 64 B,
+// weight codes 16 KB, then both operands' scale words for MXFP8), copies three
+// stages ahead
 constexpr int MX8_SLOTS = 4;
-template <int WF> constexpr int MX8_STAGE_U4() { return 2 * 1024 + (WF == 2 ? 0 : 2 * 64); }
+template <int WF, int JV> constexpr int mx8_stage_u4() {
+  return JV * 256 + 1024 + (WF == 2 ? 0 : 2 * 64);
+}
+// LDS of the 256-row kernel: the largest layout over JV = 1..4
+constexpr int mx_lds_u4_max(int wf) {
+  return wf == 0 ? 3 * (4 * 512 + 1024 + 128) : MX8_SLOTS * (4 * 256 + 1024 + 128);
+}
 
 struct MxArgs {
   const uint8_t* A;        // activation codes [rows][K]
@@ -129,15 +140,43 @@ __device__ __forceinline__ uint32_t ue8m0_round_up_448(float amax) {
   return (uint32_t)c;
 }
 
-template <int EPI, int WF>
-__global__ __launch_bounds__(MNT, 1) void k_gemm_mx(MxArgs a) {
+// Issue order for the scheduler: NM MFMAs (group 0x008), each followed by its even
+// share of NR LDS reads (group 0x100).
+template <int NM, int NR>
+__device__ __forceinline__ void sched_mfma_reads() {
+  static_assert(NR <= 5 * NM, "at most five reads per MFMA");
+#pragma unroll
+  for (int r = 0; r < NM; ++r) {
+    const int c = ((r + 1) * NR) / NM - (r * NR) / NM;
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if (c > 0) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    if (c > 1) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    if (c > 2) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    if (c > 3) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    if (c > 4) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+}
+
+// One tile of up to 256 activation rows, of which the first 64 JV exist: the
+// activation rows come in 32-row blocks, block b = 2 j + wm going to row-wave wm
+// (j < JV), so the two row-waves share the tile's rows evenly and a tile holding the
+// few rows of a small expert, or an expert's tail, copies and multiplies only
+// those (JV = 4: the whole 256-row tile). Every output element takes the same MFMA
+// sequence whatever JV is.
+template <int EPI, int WF, int JV>
+__device__ __forceinline__ void mx_tile(const MxArgs& a, uint4* smem, int e, int m0, int mend,
+                                        int nt) {
   constexpr int WB = wbits<WF>();
   constexpr bool BS = block_scaled<WF>();
-  constexpr int WCH = wch<WF>(), WT_U4 = MTB * WCH, STAGE_U4 = stage_u4<WF>();
+  constexpr int JN = JV;             // 32-row activation blocks per wave
+  constexpr int XROWS = 64 * JV;     // activation rows copied
+  constexpr int XT_U4 = xt_u4<JV>();
+  constexpr int WCH = wch<WF>(), WT_U4 = MTB * WCH, STAGE_U4 = stage_u4<WF, JV>();
   constexpr int WLD = WT_U4 / MNT;   // weight loads per thread and stage (4 or 8)
-  __shared__ uint4 smem[WF == WF_MXFP4 ? MX_DMA_SLOTS * STAGE_U4 : MX8_SLOTS * MX8_STAGE_U4<WF>()];
-  int e, m0, mend, nt;
-  if (!deal_tile<MTB>(a.ends, a.E, a.m_cap, a.n_tiles, e, m0, mend, nt)) return;
+  constexpr int NSLOT = mx_dma_slots<JV>();
+  static_assert((WF == WF_MXFP4 ? NSLOT * STAGE_U4 : MX8_SLOTS * mx8_stage_u4<WF, JV>()) <=
+                    mx_lds_u4_max(WF == WF_MXFP4 ? 0 : 1),
+                "stage layout exceeds the kernel's LDS");
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int wn = wid & 1, wm = wid >> 1;
   const int rsel = lane & 31, g = lane >> 5;
@@ -146,12 +185,12 @@ __global__ __launch_bounds__(MNT, 1) void k_gemm_mx(MxArgs a) {
 
   // per-thread source rows: activation codes rows (tid>>3)+32j, weight codes rows
   // tid/WCH + (256/WCH)j (the MXFP4 copies use these rows), scales: row tid of each
-  // operand
+  // operand (activation rows taken modulo XROWS)
   const int xr = tid >> 3, xc = tid & 7, wr = tid / WCH, wc = tid % WCH;
   const uint32_t kw = (uint32_t)K * WB / 8;   // weight bytes per row
-  uint32_t xoff[8], woff[WLD];
+  uint32_t xoff[XROWS / 32], woff[WLD];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
+  for (int j = 0; j < XROWS / 32; ++j) {
     int p = m0 + xr + 32 * j;
     p = p < mend ? p : mend - 1;
     const int src = a.a_gather ? a.a_gather[p] / a.a_div : p;
@@ -172,67 +211,71 @@ __global__ __launch_bounds__(MNT, 1) void k_gemm_mx(MxArgs a) {
   for (int j = 0; j < WLD; ++j) woff[j] = (uint32_t)wrow_of(wr + (MTB / WLD) * j) * kw + wc * 16;
   uint32_t xsoff, wsoff;
   {
-    int p = m0 + tid;
+    int p = m0 + tid % XROWS;
     p = p < mend ? p : mend - 1;
     const int src = a.a_gather ? a.a_gather[p] / a.a_div : p;
     xsoff = (uint32_t)src * (uint32_t)ks;
     wsoff = (uint32_t)wrow_of(tid) * (uint32_t)ks;
   }
-  f32x16 acc[4][4];
+  f32x16 acc[4][JN];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < JN; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
   const int ktiles = K / MTK;
   if constexpr (WF == WF_MXFP4) {
-    // MXFP4: stages copied straight into LDS, MX_DMA_SLOTS slots, two stages ahead.
+    // MXFP4: stages copied straight into LDS, NSLOT slots, NSLOT - 1 stages ahead.
     // Copy j of wave w: activation rows 32 j + 8 w + lane / 8 (whole 128-byte rows,
     // global chunk (lane % 8) ^ ((row / 2) % 8)); weight rows 64 j + 16 w + lane / 4
     // (64-byte rows, chunk (lane % 4) ^ ((row / 4) % 4)); scale words of rows
-    // 64 w + lane. These are the layouts the fragment reads below expect. The loop
-    // is rotated by one step: a stage's second step runs after the barrier, under
-    // the first fragment reads of the next stage.
+    // 64 w + lane (activation rows modulo XROWS). These are the layouts the fragment
+    // reads below expect. The loop is rotated by one step: a stage's second step runs
+    // after the barrier, under the first fragment reads of the next stage.
+    constexpr int XC = XROWS / 32;              // activation-row copies per wave and stage
+    constexpr int NC = XC + 6;               // + 4 weight-row copies + 2 scale words
+    constexpr int NC2 = NC / 2;              // issued with each step's fragment reads
+    constexpr int NWAIT = (NSLOT - 2) * NC;  // copies of the younger stages in flight
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const uint32_t lds0 = (uint32_t)(uintptr_t)smem + (uint32_t)w * 1024u;
     const uint32_t lds0s = (uint32_t)(uintptr_t)smem + (uint32_t)w * 256u;
     constexpr uint32_t XT_B = XT_U4 * 16, WT_B = WT_U4 * 16, STAGE_B = STAGE_U4 * 16;
     const int gx = (lane & 7) ^ ((4 * w + (lane >> 4)) & 7);
     const int gw = (lane & 3) ^ ((lane >> 4) & 3);
-    uint32_t xrow[8], wrowb[4];
+    uint32_t xrow[XC], wrowb[4];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) xrow[j] = xoff[j] - xc * 16;
+    for (int j = 0; j < XC; ++j) xrow[j] = xoff[j] - xc * 16;
 #pragma unroll
     for (int j = 0; j < 4; ++j) wrowb[j] = woff[j] - wc * 16;
-    // copy c (0..13) of stage q into the slot at byte offset d: 8 activation-row
+    // copy c (0..NC-1) of stage q into the slot at byte offset d: XC activation-row
     // copies, 4 weight-row copies, then the two scale words
     auto cp = [&](int c, int q, uint32_t d) {
-      if (c < 8) {
+      if (c < XC) {
         mx_dma16(a.A + xrow[c] + q * MTK + gx * 16, lds0 + d + c * 4096u);
-      } else if (c < 12) {
-        mx_dma16(Bb + wrowb[c - 8] + q * (MTK / 2) + gw * 16, lds0 + d + XT_B + (c - 8) * 4096u);
-      } else if (c == 12) {
+      } else if (c < XC + 4) {
+        mx_dma16(Bb + wrowb[c - XC] + q * (MTK / 2) + gw * 16, lds0 + d + XT_B + (c - XC) * 4096u);
+      } else if (c == XC + 4) {
         mx_dma4(a.A_sf + xsoff + q * (MTK / 32), lds0s + d + XT_B + WT_B);
       } else {
         mx_dma4(Bs + wsoff + q * (MTK / 32), lds0s + d + XT_B + WT_B + 1024u);
       }
     };
-    v8i wf[2][4], xf[2][4];
+    v8i wf[2][4], xf[2][JN];
     // scale words of the current stage and of the previous one (whose second step
     // runs at the start of the current stage)
-    uint32_t wsr[4], xsr[4], wsp[4], xsp[4];
+    uint32_t wsr[4], xsr[JN], wsp[4], xsp[JN];
     auto rd_scales = [&](int slot) {
       const uint32_t* XS = reinterpret_cast<const uint32_t*>(smem + slot * STAGE_U4 + XT_U4 + WT_U4);
       const uint32_t* WS = XS + MTB;
 #pragma unroll
       for (int i = 0; i < 4; ++i) wsr[i] = WS[wn * 128 + i * 32 + rsel];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) xsr[j] = XS[wm * 128 + j * 32 + rsel];
+      for (int j = 0; j < JN; ++j) xsr[j] = XS[(2 * j + wm) * 32 + rsel];
     };
-    // fragment reads of step kk of `slot` (4 weight, 8 activation), copies c0..c0+6
-    // of stage q into slot offset d after the first seven of them
+    // fragment reads of step kk of `slot` (4 weight, 2 JN activation), copies
+    // c0..c0+NC2-1 of stage q into slot offset d among them
     auto rd_issue = [&](int slot, int kk, int set, int q, uint32_t d, int c0) {
       const uint4* X = smem + slot * STAGE_U4;
       const uint4* W = X + XT_U4;
@@ -244,64 +287,71 @@ __global__ __launch_bounds__(MNT, 1) void k_gemm_mx(MxArgs a) {
         cp(c0 + i, q, d);
       }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int r = wm * 128 + j * 32 + rsel;
+      for (int j = 0; j < JN; ++j) {
+        const int r = (2 * j + wm) * 32 + rsel;
         const uint4 lo = X[r * 8 + ((4 * kk + g) ^ ((r >> 1) & 7))];
-        if (j < 3) cp(c0 + 4 + j, q, d);
+        if (j < NC2 - 4) cp(c0 + 4 + j, q, d);
         const uint4 hi = X[r * 8 + ((4 * kk + 2 + g) ^ ((r >> 1) & 7))];
         xf[set][j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
       }
     };
-    auto mm = [&](int set, int kk, const uint32_t (&ws)[4], const uint32_t (&xs)[4]) {
+    auto mm = [&](int set, int kk, const uint32_t (&ws)[4], const uint32_t (&xs)[JN]) {
       const int sh = 8 * (2 * kk + g);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < JN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
               wf[set][i], xf[set][j], acc[i][j], a_fmt<WF>(), 0, 0, (int)((ws[i] >> sh) & 0xFF), 0,
               (int)((xs[j] >> sh) & 0xFF));
     };
     auto body = [&](int st, bool first) {
-      const int slot = st % MX_DMA_SLOTS;
-      const int q = st + MX_DMA_SLOTS - 1 < ktiles ? st + MX_DMA_SLOTS - 1 : ktiles - 1;
-      const uint32_t d = (uint32_t)((st + MX_DMA_SLOTS - 1) % MX_DMA_SLOTS) * STAGE_B;
+      const int slot = st % NSLOT;
+      const int q = st + NSLOT - 1 < ktiles ? st + NSLOT - 1 : ktiles - 1;
+      const uint32_t d = (uint32_t)((st + NSLOT - 1) % NSLOT) * STAGE_B;
       rd_scales(slot);
       rd_issue(slot, 0, 0, q, d, 0);
       if (!first) mm(1, 1, wsp, xsp);   // the previous stage's second step
-      rd_issue(slot, 1, 1, q, d, 7);
+      rd_issue(slot, 1, 1, q, d, NC2);
       mm(0, 0, wsr, xsr);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        wsp[i] = wsr[i];
-        xsp[i] = xsr[i];
-      }
-      // issue order (0x008 MFMA, 0x100 LDS read): the 8 scale reads and step 0's 12
-      // fragment reads, then step 1's 12 between step 0's MFMAs (non-first: the
-      // 20 between the previous stage's last step)
+      for (int i = 0; i < 4; ++i) wsp[i] = wsr[i];
+#pragma unroll
+      for (int j = 0; j < JN; ++j) xsp[j] = xsr[j];
+      // issue order (0x008 MFMA, 0x100 LDS read): the 4 + JN scale reads and step 0's
+      // 4 + 2 JN fragment reads, then step 1's between step 0's 4 JN MFMAs
+      // (non-first: the former between the previous stage's last step)
       if (first) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 20, 0);
-      } else {
+        __builtin_amdgcn_sched_group_barrier(0x100, 8 + 3 * JN, 0);
+      } else if (JV == 4) {
+#pragma unroll
         for (int r = 0; r < 16; ++r) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
           __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
           if (r & 3) {} else __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
+      } else {
+        sched_mfma_reads<4 * JN, 8 + 3 * JN>();
       }
-      for (int r = 0; r < 16; ++r) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        if (r < 12) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      if (JV == 4) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          if (r < 12) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+      } else {
+        sched_mfma_reads<4 * JN, 4 + 2 * JN>();
       }
       __builtin_amdgcn_sched_barrier(0);
-      // copies complete in issue order: the younger stage's 14 may still be in flight
-      asm volatile("s_waitcnt vmcnt(14)" ::: "memory");
+      // copies complete in issue order: the younger stages' may still be in flight
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NWAIT) : "memory");
       __syncthreads();
     };
 #pragma unroll
-    for (int q = 0; q < MX_DMA_SLOTS - 1; ++q)
+    for (int q = 0; q < NSLOT - 1; ++q)
 #pragma unroll
-      for (int c = 0; c < 14; ++c) cp(c, q < ktiles ? q : ktiles - 1, (uint32_t)q * STAGE_B);
-    asm volatile("s_waitcnt vmcnt(14)" ::: "memory");
+      for (int c = 0; c < NC; ++c) cp(c, q < ktiles ? q : ktiles - 1, (uint32_t)q * STAGE_B);
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NWAIT) : "memory");
     __syncthreads();
     body(0, true);
     for (int st = 1; st < ktiles; ++st) body(st, false);
@@ -310,13 +360,14 @@ __global__ __launch_bounds__(MNT, 1) void k_gemm_mx(MxArgs a) {
   } else {
     // MXFP8 / FP8: 64-deep stages copied straight into LDS, MX8_SLOTS slots, three
     // stages ahead; each stage is one scaled-MFMA step. Copy j of wave w covers rows
-    // 64 j + 16 w + lane / 4 of the activation and of the weight codes (64-byte rows,
-    // global chunk (lane % 4) ^ ((row / 4) % 4)); MXFP8 also copies the scale word of
-    // the stage's 128-deep block for rows 64 w + lane. Loop rotated by one step: the
-    // previous stage's MFMAs run under the current stage's fragment reads.
-    constexpr uint32_t CODE_B = 16384, SLOT_B = MX8_STAGE_U4<WF>() * 16;
-    // Copies per wave: 8 code copies per stage, plus (MXFP8) the 2 scale words for
-    // even stages only -- both stages of a 128-deep block use the even one's words.
+    // 64 j + 16 w + lane / 4 of the activation (j < XROWS / 64) and of the weight codes
+    // (64-byte rows, global chunk (lane % 4) ^ ((row / 4) % 4)); MXFP8 also copies the
+    // scale word of the stage's 128-deep block for rows 64 w + lane. Loop rotated by
+    // one step: the previous stage's MFMAs run under the current stage's fragment reads.
+    constexpr int XC8 = XROWS / 64;   // activation copies per wave and stage
+    constexpr uint32_t XCODE_B = XROWS * 64, WCODE_B = 16384, SLOT_B = mx8_stage_u4<WF, JV>() * 16;
+    // Copies per wave: XC8 + 4 code copies per stage, plus (MXFP8) the 2 scale words
+    // for even stages only -- both stages of a 128-deep block use the even one's words.
     // An odd-parity body issues an even stage (or, clamped at the end, a copy nobody
     // reads) and copies the words; an even-parity body does not. Any two consecutive
     // bodies therefore have NWAIT copies in flight at a barrier.
@@ -324,38 +375,42 @@ __global__ __launch_bounds__(MNT, 1) void k_gemm_mx(MxArgs a) {
     const uint32_t lds0 = (uint32_t)(uintptr_t)smem + (uint32_t)w * 1024u;
     const uint32_t lds0s = (uint32_t)(uintptr_t)smem + (uint32_t)w * 256u;
     const int gc = (lane & 3) ^ ((lane >> 4) & 3);
-    uint32_t xrow[4], wrow[4];
+    uint32_t xrow[XC8], wrow[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int R = (tid >> 2) + 64 * j;
-      int p = m0 + R;
-      p = p < mend ? p : mend - 1;
-      const int src = a.a_gather ? a.a_gather[p] / a.a_div : p;
-      xrow[j] = (uint32_t)src * (uint32_t)K + gc * 16;
+      if (j < XC8) {
+        int p = m0 + R;
+        p = p < mend ? p : mend - 1;
+        const int src = a.a_gather ? a.a_gather[p] / a.a_div : p;
+        xrow[j] = (uint32_t)src * (uint32_t)K + gc * 16;
+      }
       wrow[j] = (uint32_t)wrow_of(R) * kw + gc * 16;
     }
     const int nsub = K / 64;
     auto cp = [&](int c, int q, uint32_t d) {
-      if (c < 4) {
+      if (c < XC8) {
         mx_dma16(a.A + xrow[c] + q * 64, lds0 + d + c * 4096u);
-      } else if (c < 8) {
-        mx_dma16(Bb + wrow[c - 4] + q * 64, lds0 + d + CODE_B + (c - 4) * 4096u);
-      } else if (c == 8) {
-        mx_dma4(a.A_sf + xsoff + (q >> 1) * 4, lds0s + d + 2 * CODE_B);
+      } else if (c < XC8 + 4) {
+        mx_dma16(Bb + wrow[c - XC8] + q * 64, lds0 + d + XCODE_B + (c - XC8) * 4096u);
+      } else if (c == XC8 + 4) {
+        mx_dma4(a.A_sf + xsoff + (q >> 1) * 4, lds0s + d + XCODE_B + WCODE_B);
       } else {
-        mx_dma4(Bs + wsoff + (q >> 1) * 4, lds0s + d + 2 * CODE_B + 1024u);
+        mx_dma4(Bs + wsoff + (q >> 1) * 4, lds0s + d + XCODE_B + WCODE_B + 1024u);
       }
     };
-    v8i wf[2][4], xf[2][4];
-    uint32_t wsr[4], xsr[4], wsp[4], xsp[4];
+    v8i wf[2][4], xf[2][JN];
+    uint32_t wsr[4], xsr[JN], wsp[4], xsp[JN];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) wsr[i] = xsr[i] = wsp[i] = xsp[i] = UNIT_SCALE4;
-    constexpr int NWAIT = BS ? 18 : 16;
+    for (int i = 0; i < 4; ++i) wsr[i] = wsp[i] = UNIT_SCALE4;
+#pragma unroll
+    for (int j = 0; j < JN; ++j) xsr[j] = xsp[j] = UNIT_SCALE4;
+    constexpr int NWAIT = 2 * (XC8 + 4) + (BS ? 2 : 0);
     // fragment reads of the stage in `slot` (two 16-byte chunks per fragment), with
     // the copies of stage q into slot offset d spread among them
     auto rd_issue = [&](int slot, int set, int q, uint32_t d) {
-      const uint4* X = smem + slot * MX8_STAGE_U4<WF>();
-      const uint4* W = X + 1024;
+      const uint4* X = smem + slot * mx8_stage_u4<WF, JV>();
+      const uint4* W = X + XROWS * 4;
       // the two stages of a 128-deep block share their scale words: the odd stage
       // keeps the even one's in registers
       if (BS && set == 0) {
@@ -364,7 +419,7 @@ __global__ __launch_bounds__(MNT, 1) void k_gemm_mx(MxArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) wsr[i] = WS[wn * 128 + i * 32 + rsel];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) xsr[j] = XS[wm * 128 + j * 32 + rsel];
+        for (int j = 0; j < JN; ++j) xsr[j] = XS[(2 * j + wm) * 32 + rsel];
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -375,25 +430,25 @@ __global__ __launch_bounds__(MNT, 1) void k_gemm_mx(MxArgs a) {
         cp(i, q, d);
       }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int r = wm * 128 + j * 32 + rsel;
+      for (int j = 0; j < JN; ++j) {
+        const int r = (2 * j + wm) * 32 + rsel;
         const uint4 lo = X[r * 4 + (g ^ ((r >> 2) & 3))];
         const uint4 hi = X[r * 4 + ((2 + g) ^ ((r >> 2) & 3))];
         xf[set][j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
         cp(4 + j, q, d);
       }
       if (BS && set == 1) {   // this body issues an even stage
-        cp(8, q, d);
-        cp(9, q, d);
+        cp(XC8 + 4, q, d);
+        cp(XC8 + 5, q, d);
       }
     };
     // MFMAs of the stage with parity sp (its scale byte is 2 (sp) + g of the word)
-    auto mm = [&](int set, int sp, const uint32_t (&ws)[4], const uint32_t (&xs)[4]) {
+    auto mm = [&](int set, int sp, const uint32_t (&ws)[4], const uint32_t (&xs)[JN]) {
       const int sh = 8 * (2 * sp + g);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < JN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
               wf[set][i], xf[set][j], acc[i][j], a_fmt<WF>(), 0, 0, (int)((ws[i] >> sh) & 0xFF), 0,
               (int)((xs[j] >> sh) & 0xFF));
@@ -408,21 +463,23 @@ __global__ __launch_bounds__(MNT, 1) void k_gemm_mx(MxArgs a) {
       rd_issue(slot, P, q, d);
       if (!first) mm(P ^ 1, P ^ 1, wsp, xsp);   // the previous stage
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        wsp[i] = wsr[i];
-        xsp[i] = xsr[i];
-      }
-      // issue order (0x008 MFMA, 0x100 LDS read): the stage's (8 +) 16 reads between
-      // the previous stage's 16 MFMAs
-      constexpr int NR = 16 + (BS && P == 0 ? 8 : 0);
+      for (int i = 0; i < 4; ++i) wsp[i] = wsr[i];
+#pragma unroll
+      for (int j = 0; j < JN; ++j) xsp[j] = xsr[j];
+      // issue order (0x008 MFMA, 0x100 LDS read): the stage's (4 + JN +) 8 + 2 JN
+      // reads between the previous stage's 4 JN MFMAs
+      constexpr int NR = 8 + 2 * JN + (BS && P == 0 ? 4 + JN : 0);
       if (first) {
         __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
-      } else {
+      } else if (JV == 4) {
+#pragma unroll
         for (int r = 0; r < 16; ++r) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
           __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
           if (BS && P == 0 && (r & 1) == 0) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
+      } else {
+        sched_mfma_reads<4 * JN, NR>();
       }
       __builtin_amdgcn_sched_barrier(0);
       // copies complete in issue order: the two younger stages' may still be in flight
@@ -434,7 +491,7 @@ __global__ __launch_bounds__(MNT, 1) void k_gemm_mx(MxArgs a) {
 #pragma unroll
     for (int q = 0; q < MX8_SLOTS - 1; ++q)   // stages 0 (+words), 1, 2 (+words)
 #pragma unroll
-      for (int c = 0; c < ((BS && (q & 1) == 0) ? 10 : 8); ++c)
+      for (int c = 0; c < ((BS && (q & 1) == 0) ? XC8 + 6 : XC8 + 4); ++c)
         cp(c, q < nsub ? q : nsub - 1, (uint32_t)q * SLOT_B);
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NWAIT) : "memory");
     __syncthreads();
@@ -450,6 +507,14 @@ __global__ __launch_bounds__(MNT, 1) void k_gemm_mx(MxArgs a) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
 
+  // The epilogue below stores under per-lane row conditions. The MFMAs read every
+  // lane's operands, so none of them may be moved into those branches (where lanes
+  // beyond the tile's rows are switched off): pass each accumulator through an
+  // opaque, side-effecting asm before any branch.
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < JN; ++j) asm volatile("" : "+a"(acc[i][j]));
   const int hi4 = (lane >> 5) * 4;
   const float alpha = pt_alpha<WF>(a, e);
   if (fc1) {
@@ -457,8 +522,8 @@ __global__ __launch_bounds__(MNT, 1) void k_gemm_mx(MxArgs a) {
     if (EPI == MX_FC1_STEP) lim = a.limits ? a.limits[e] : a.def_limit;
     const float qinv = BS ? 1.f : 1.0f / a.q_scale[0];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int p = m0 + wm * 128 + j * 32 + rsel;
+    for (int j = 0; j < JN; ++j) {
+      const int p = m0 + (2 * j + wm) * 32 + rsel;
       const bool row_ok = p < mend;
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
@@ -498,8 +563,8 @@ __global__ __launch_bounds__(MNT, 1) void k_gemm_mx(MxArgs a) {
     }
   } else {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int p = m0 + wm * 128 + j * 32 + rsel;
+    for (int j = 0; j < JN; ++j) {
+      const int p = m0 + (2 * j + wm) * 32 + rsel;
       if (p >= mend) continue;
       uint16_t* crow = a.C + (int64_t)p * a.ldc;
 #pragma unroll
@@ -514,6 +579,23 @@ __global__ __launch_bounds__(MNT, 1) void k_gemm_mx(MxArgs a) {
         }
     }
   }
+}
+
+// 256-row tiles; each picks the number of 32-row blocks per row-wave that hold rows.
+template <int EPI, int WF>
+__global__ __launch_bounds__(MNT, 1) void k_gemm_mx(MxArgs a) {
+  __shared__ uint4 smem[mx_lds_u4_max(WF == WF_MXFP4 ? 0 : 1)];
+  int e, m0, mend, nt;
+  if (!deal_tile<MTB>(a.ends, a.E, a.m_cap, a.n_tiles, e, m0, mend, nt)) return;
+  const int jv = (mend - m0 + 63) >> 6;   // 1..4
+  if (jv >= 4)
+    mx_tile<EPI, WF, 4>(a, smem, e, m0, mend, nt);
+  else if (jv == 3)
+    mx_tile<EPI, WF, 3>(a, smem, e, m0, mend, nt);
+  else if (jv == 2)
+    mx_tile<EPI, WF, 2>(a, smem, e, m0, mend, nt);
+  else
+    mx_tile<EPI, WF, 1>(a, smem, e, m0, mend, nt);
 }
 
 // Few rows per expert (decode): the cost is streaming the expert bank once. Tile:
@@ -758,10 +840,15 @@ __global__ __launch_bounds__(256, 2) void k_gemm_mx_stream(MxArgs a) {
   }
 }
 
-// The decode kernel takes over while the experts hold few rows on average: there
-// the 256-row tiles would be mostly padding and too few to fill the chip. Measured
-// crossover (H=7168, I=2048, 64 experts, MXFP4): about 32 rows per expert for FC1
-// and 24 for FC2 (its contraction is 3.5x shorter, so its blocks live shorter).
+// The decode kernel takes over while the experts hold few rows on average. The
+// 256-row tiles multiply only the 32-row blocks that hold rows, so the crossover is
+// low; measured at H=7168, I=2048, 64 experts (rows per expert, on average): FC1
+// 12 (MXFP4), 20 (MXFP8), 24 (fp8 per-tensor); FC2 never for MXFP4 (the 256-row tile
+// is faster even at one token), 2 for the 8-bit weights.
+inline int mx_stream_rows(int wf, int stage) {
+  if (stage == 1) return wf == WF_MXFP4 ? 12 : wf == WF_MXFP8 ? 20 : 24;
+  return wf == WF_MXFP4 ? 0 : 2;
+}
 inline bool mx_small_fits(int K, int NB, int64_t act_rows, int wb) {
   const int stage_k = 128 * 8 / wb;
   return K % stage_k == 0 && K <= 4 * SMAX_K && (int64_t)NB * K * wb / 8 < (1LL << 31) &&
@@ -840,7 +927,7 @@ moe_status mx_fc1_enqueue(int activation, int wf, const void* x, const void* x_s
   a.a_scale = reinterpret_cast<const float*>(x_sf);
   a.w_scale = reinterpret_cast<const float*>(w1_sf);
   a.q_scale = act_scale;
-  const bool small = mx_use_small(R, L, H, 2 * I, R, 32, wf_bits(wf), 1, wf, force);
+  const bool small = mx_use_small(R, L, H, 2 * I, R, mx_stream_rows(wf, 1), wf_bits(wf), 1, wf, force);
   a.n_tiles = small ? I / 32 : (I + 127) / 128;
   const int64_t tiles = mx_row_tiles(R, L, small ? STB : MTB) * a.n_tiles;
   if (activation == MOE_ACT_SWIGLU_STEP) return mx_launch_w<MX_FC1_STEP>(a, wf, small, tiles, st);
@@ -871,7 +958,7 @@ moe_status mx_fc2_enqueue(int wf, const void* act, const void* act_sf, const voi
   a.ldc = H;
   a.a_scale = reinterpret_cast<const float*>(act_sf);
   a.w_scale = reinterpret_cast<const float*>(w2_sf);
-  const bool small = mx_use_small(R, L, I, H, R, 24, wf_bits(wf), 2, wf, force);
+  const bool small = mx_use_small(R, L, I, H, R, mx_stream_rows(wf, 2), wf_bits(wf), 2, wf, force);
   a.n_tiles = small ? (H + 63) / 64 : (H + MTB - 1) / MTB;
   const int64_t tiles = mx_row_tiles(R, L, small ? STB : MTB) * a.n_tiles;
   return mx_launch_w<MX_FC2>(a, wf, small, tiles, st);

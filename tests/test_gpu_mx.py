@@ -15,7 +15,7 @@ import torch
 import mixture_experts_expert_softmax_amd as M
 import moe_synth as S
 import oracle as O
-from parity import assert_close_bf16, mx_dequant_table, to_np
+from parity import assert_close_bf16, bf16_round, mx_dequant_table, to_np
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -111,7 +111,11 @@ def test_mx_decode_uneven_contraction_split(wfmt):
     of 128 (MXFP8), split unevenly over the decode kernel's 4 waves (with MXFP4 one
     wave of FC2 gets none)."""
     c = S.w4a8_moe(seed=9, T=5, H=1280, I=768, E=16, top_k=4, wfmt=wfmt)
+    M.moe_tune_clear()
+    for stage in (1, 2):   # both stages on the decode kernel
+        M.moe_tune_set(c.T, c.H, c.I, c.num_experts, c.top_k, stage, 1, weight_format=wfmt)
     out, ids, w = _run(c, _dev(c))
+    M.moe_tune_clear()
     assert_close_bf16(out, _oracle(c, ids, w), MX_MAX_ABS, MX_REL, what=f"{wfmt} uneven split")
 
 
@@ -123,7 +127,8 @@ def test_mxfp8_decode_short_contraction():
     assert_close_bf16(out, _oracle(c, ids, w), MX_MAX_ABS, MX_REL, what="mxfp8 I=128")
 
 
-# T=200 runs the 256-row tile kernel, T=12 the decode kernel (few rows per expert)
+# T=200 runs the 256-row tile kernel, T=12 the decode kernel for FC1 (few rows per
+# expert) and the 256-row one, on tiles of 8 rows or so, for FC2
 @pytest.mark.parametrize("wfmt", WFMTS)
 @pytest.mark.parametrize("T", [200, 12])
 def test_mx_shard_and_step_activation(T, wfmt):
@@ -223,6 +228,36 @@ def test_fp8_fc1_per_tensor_requant_matches_oracle_rule(T):
     da = 2.0 ** -14 * (np.abs(g * sig) * habs[:, :I] + dsilu * np.abs(u) * habs[:, I:])
     step = np.maximum(np.abs(rv), np.abs(gv)) * 2.0 ** -3 + 2.0 ** -9 * s
     assert np.all(np.abs(gv - rv) <= step + da)
+
+
+@pytest.mark.parametrize("wfmt", ["mxfp4", "mxfp8"])
+def test_mx_fc2_every_tile_height_exact(wfmt):
+    """FC2 of the 256-row kernel on operands whose fp32 sums are all exact (e4m3
+    activations holding integers up to 6, weights that are multiples of 1/2 up to 6 or
+    8, block scales 2^-1 .. 2^2): the output is the bf16 rounding of the exact grouped
+    product, bit for bit. The experts' row counts give tiles holding 1..64, 65..128,
+    129..192 and 193..256 rows (the 32-row blocks a tile multiplies follow its rows),
+    empty experts and several tiles per expert."""
+    rng = np.random.default_rng(43)
+    sizes = np.array([1, 64, 65, 128, 0, 129, 192, 193, 256, 300, 511, 37, 0, 90])
+    L, R, H, I = len(sizes), int(sizes.sum()), 512, 256
+    ends = np.cumsum(sizes).astype(np.int32)
+    act_v = rng.integers(-6, 7, size=(R, I)).astype(np.float32)
+    act = torch.from_numpy(act_v).to(torch.float8_e4m3fn).view(torch.uint8)
+    act_sf = rng.integers(126, 130, size=(R, I // 32)).astype(np.uint8)
+    if wfmt == "mxfp4":
+        w2 = rng.integers(0, 256, size=(L, H, I // 2)).astype(np.uint8)
+    else:
+        w2_v = rng.integers(-12, 13, size=(L, H, I)).astype(np.float32) / 2
+        w2 = torch.from_numpy(w2_v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    w2_sf = rng.integers(126, 129, size=(L, H, I // 32)).astype(np.uint8)
+    y = M.moe_fc2_mx(act.to(DEV), torch.from_numpy(act_sf).to(DEV), torch.from_numpy(w2).to(DEV),
+                     torch.from_numpy(w2_sf).to(DEV), torch.from_numpy(ends).to(DEV), R, 1, L)
+    torch.cuda.synchronize()
+    a_deq = O.mx_dequant_fp8(act.numpy(), act_sf)
+    w_deq = mx_dequant_table(wfmt, w2, w2_sf)
+    ref = O.grouped_gemm_fwd(a_deq, w_deq, ends)
+    np.testing.assert_array_equal(to_np(y)[:R], bf16_round(ref))
 
 
 @pytest.mark.parametrize("wfmt", WFMTS)

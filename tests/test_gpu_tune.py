@@ -36,6 +36,40 @@ def test_tuned_choice_keeps_parity_and_clear_restores(wfmt, T):
     assert torch.equal(before, after)
 
 
+MX_FAMILY_CASES = [
+    # (T, H, I, E, k, L, off): ragged experts of about 175 and 75 rows, and a local
+    # shard
+    (700, 512, 384, 8, 2, 8, 0),
+    (300, 768, 256, 16, 4, 6, 5),
+]
+
+
+@pytest.mark.parametrize("wfmt", ["mxfp4", "mxfp8", "fp8"])
+@pytest.mark.parametrize("T,H,I,E,k,L,off", MX_FAMILY_CASES)
+def test_mx_tile_families_match_oracle(T, H, I, E, k, L, off, wfmt):
+    """Both fp8-activation stages recorded to each tile family in turn -- the 256-row
+    tile (0; its tiles multiply only the 32-row blocks that hold rows) and the
+    streaming tile (1, where the shape allows it) -- against the oracle, with ragged
+    experts over several tiles, a local shard and the clamped activation."""
+    c = S.w4a8_moe(seed=T + I, T=T, H=H, I=I, E=E, top_k=k, x_scale=2.0, wfmt=wfmt)
+    d = _dev(c)
+    ids, w = M.moe_route(torch.from_numpy(c.logits).to(DEV), c.top_k)
+    lim = torch.tensor(np.linspace(2.0, 4.0, L), dtype=torch.float32, device=DEV)
+    sl = slice(off, off + L)
+    ref = _oracle(c, ids, w, L=L, local_offset=off, activation="swiglu_step",
+                  limits=lim.cpu().numpy())
+    for choice in (0, 1):
+        M.moe_tune_clear()
+        for stage in (1, 2):
+            M.moe_tune_set(T, H, I, E, k, stage, choice, num_local_experts=L, local_expert_offset=off,
+                           weight_format=wfmt)
+        out = _fwd(c, d, ids, w, d["w1"][sl], d["w1_sf"][sl], d["w2"][sl], d["w2_sf"][sl],
+                   num_local_experts=L, local_expert_offset=off, activation="swiglu_step",
+                   clamp_limit=lim)
+        assert_close_bf16(out, ref, MX_MAX_ABS, MX_REL, what=f"{wfmt} family {choice}")
+    M.moe_tune_clear()
+
+
 def _layer(c, ids, w, finalize="deterministic"):
     lim = None if c.limits is None else torch.from_numpy(c.limits).to(DEV)
     return M.moe_ffn_forward(c.x.to(DEV), ids, w, c.w1.to(DEV), c.w2.to(DEV), c.num_experts,
