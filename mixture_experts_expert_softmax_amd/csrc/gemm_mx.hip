@@ -56,9 +56,12 @@ template <int WF> constexpr int wbits() { return WF == WF_MXFP4 ? 4 : 8; }
 template <int WF> constexpr bool block_scaled() { return WF != WF_FP8; }
 // 16-byte chunks per weight row and stage, and the stage size in uint4
 template <int WF> constexpr int wch() { return MTK * wbits<WF>() / 8 / 16; }
-template <int WF, int JV> constexpr int stage_u4() {
-  return xt_u4<JV>() + MTB * wch<WF>() + (block_scaled<WF>() ? 2 * MTB / 4 : 0);
+// SG: the block scales come in groups of four stages (16 bytes per row, their own
+// two-group LDS ring of 16 KB) instead of one 4-byte word per row and stage
+template <int WF, int JV, bool SG = false> constexpr int stage_u4() {
+  return xt_u4<JV>() + MTB * wch<WF>() + (block_scaled<WF>() && !SG ? 2 * MTB / 4 : 0);
 }
+constexpr int MX_SG_U4 = 2 * 2 * MTB;   // two groups of x and w scales, [256][16 B] each
 // scaled-MFMA format code of the weight (A-slot) operand
 template <int WF> constexpr int a_fmt() { return WF == WF_MXFP4 ? 4 : 0; }
 constexpr int UNIT_SCALE = 127;              // UE8M0 code of 1.0
@@ -84,12 +87,12 @@ template <int JV> constexpr int mx_dma_slots() { return JV <= 2 ? 4 : 3; }
 // weight codes 16 KB, then both operands' scale words for MXFP8), copies three
 // stages ahead
 constexpr int MX8_SLOTS = 4;
-template <int WF, int JV> constexpr int mx8_stage_u4() {
-  return JV * 256 + 1024 + (WF == 2 ? 0 : 2 * 64);
+template <int WF, int JV, bool SG = false> constexpr int mx8_stage_u4() {
+  return JV * 256 + 1024 + (WF == 2 || SG ? 0 : 2 * 64);
 }
 // LDS of the 256-row kernel: the largest layout over JV = 1..4
 constexpr int mx_lds_u4_max(int wf) {
-  return wf == 0 ? 3 * (4 * 512 + 1024 + 128) : MX8_SLOTS * (4 * 256 + 1024 + 128);
+  return wf == 0 ? 3 * (4 * 512 + 1024) + MX_SG_U4 : MX8_SLOTS * (4 * 256 + 1024) + MX_SG_U4;
 }
 
 struct MxArgs {
@@ -163,18 +166,20 @@ __device__ __forceinline__ void sched_mfma_reads() {
 // few rows of a small expert, or an expert's tail, copies and multiplies only
 // those (JV = 4: the whole 256-row tile). Every output element takes the same MFMA
 // sequence whatever JV is.
-template <int EPI, int WF, int JV>
+template <int EPI, int WF, int JV, bool SG>
 __device__ __forceinline__ void mx_tile(const MxArgs& a, uint4* smem, int e, int m0, int mend,
                                         int nt) {
+  static_assert(!SG || block_scaled<WF>(), "scale groups: block-scaled weights only");
   constexpr int WB = wbits<WF>();
   constexpr bool BS = block_scaled<WF>();
   constexpr int JN = JV;             // 32-row activation blocks per wave
   constexpr int XROWS = 64 * JV;     // activation rows copied
   constexpr int XT_U4 = xt_u4<JV>();
-  constexpr int WCH = wch<WF>(), WT_U4 = MTB * WCH, STAGE_U4 = stage_u4<WF, JV>();
+  constexpr int WCH = wch<WF>(), WT_U4 = MTB * WCH, STAGE_U4 = stage_u4<WF, JV, SG>();
   constexpr int WLD = WT_U4 / MNT;   // weight loads per thread and stage (4 or 8)
   constexpr int NSLOT = mx_dma_slots<JV>();
-  static_assert((WF == WF_MXFP4 ? NSLOT * STAGE_U4 : MX8_SLOTS * mx8_stage_u4<WF, JV>()) <=
+  static_assert((WF == WF_MXFP4 ? NSLOT * STAGE_U4 : MX8_SLOTS * mx8_stage_u4<WF, JV, SG>()) +
+                        (SG ? MX_SG_U4 : 0) <=
                     mx_lds_u4_max(WF == WF_MXFP4 ? 0 : 1),
                 "stage layout exceeds the kernel's LDS");
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
@@ -234,14 +239,22 @@ __device__ __forceinline__ void mx_tile(const MxArgs& a, uint4* smem, int e, int
     // 64 w + lane (activation rows modulo XROWS). These are the layouts the fragment
     // reads below expect. The loop is rotated by one step: a stage's second step runs
     // after the barrier, under the first fragment reads of the next stage.
+    // SG: no scale words in the stages; instead, with the copies of every fourth stage
+    // 4g, each wave first copies 16 bytes of scales (stages 4g .. 4g+3) for its 64
+    // activation and 64 weight rows into group buffer g % 2 ([256 rows][16 B] each of
+    // x and w). Those two copies precede the stage's own, so a barrier that has seen a
+    // stage's copies land has seen its scale group land too.
     constexpr int XC = XROWS / 32;              // activation-row copies per wave and stage
-    constexpr int NC = XC + 6;               // + 4 weight-row copies + 2 scale words
+    constexpr int NC = XC + (SG ? 4 : 6);    // + 4 weight-row copies (+ 2 scale words)
     constexpr int NC2 = NC / 2;              // issued with each step's fragment reads
-    constexpr int NWAIT = (NSLOT - 2) * NC;  // copies of the younger stages in flight
+    // copies allowed in flight at a barrier: the younger stages' (a scale group issued
+    // with them is waited for as well, which costs little: it was issued first)
+    constexpr int NWAIT = (NSLOT - 2) * NC;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const uint32_t lds0 = (uint32_t)(uintptr_t)smem + (uint32_t)w * 1024u;
     const uint32_t lds0s = (uint32_t)(uintptr_t)smem + (uint32_t)w * 256u;
     constexpr uint32_t XT_B = XT_U4 * 16, WT_B = WT_U4 * 16, STAGE_B = STAGE_U4 * 16;
+    constexpr uint32_t SG_B = NSLOT * STAGE_B;   // scale-group ring (SG)
     const int gx = (lane & 7) ^ ((4 * w + (lane >> 4)) & 7);
     const int gw = (lane & 3) ^ ((lane >> 4) & 3);
     uint32_t xrow[XC], wrowb[4];
@@ -262,17 +275,33 @@ __device__ __forceinline__ void mx_tile(const MxArgs& a, uint4* smem, int e, int
         mx_dma4(Bs + wsoff + q * (MTK / 32), lds0s + d + XT_B + WT_B + 1024u);
       }
     };
+    // SG: the scale group of stage q (a multiple of 4) into buffer (q / 4) % 2
+    auto cp_group = [&](int q) {
+      const uint32_t gb = SG_B + (uint32_t)((q >> 2) & 1) * 8192u + (uint32_t)w * 1024u;
+      mx_dma16(a.A_sf + xsoff + q * (MTK / 32), (uint32_t)(uintptr_t)smem + gb);
+      mx_dma16(Bs + wsoff + q * (MTK / 32), (uint32_t)(uintptr_t)smem + gb + 4096u);
+    };
     v8i wf[2][4], xf[2][JN];
     // scale words of the current stage and of the previous one (whose second step
     // runs at the start of the current stage)
     uint32_t wsr[4], xsr[JN], wsp[4], xsp[JN];
-    auto rd_scales = [&](int slot) {
-      const uint32_t* XS = reinterpret_cast<const uint32_t*>(smem + slot * STAGE_U4 + XT_U4 + WT_U4);
-      const uint32_t* WS = XS + MTB;
+    auto rd_scales = [&](int slot, int st) {
+      if (SG) {
+        const uint32_t* XS = reinterpret_cast<const uint32_t*>(smem + SG_B / 16 + ((st >> 2) & 1) * 512);
+        const uint32_t* WS = XS + 4 * MTB;
+        const int ph = st & 3;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) wsr[i] = WS[wn * 128 + i * 32 + rsel];
+        for (int i = 0; i < 4; ++i) wsr[i] = WS[(wn * 128 + i * 32 + rsel) * 4 + ph];
 #pragma unroll
-      for (int j = 0; j < JN; ++j) xsr[j] = XS[(2 * j + wm) * 32 + rsel];
+        for (int j = 0; j < JN; ++j) xsr[j] = XS[((2 * j + wm) * 32 + rsel) * 4 + ph];
+      } else {
+        const uint32_t* XS = reinterpret_cast<const uint32_t*>(smem + slot * STAGE_U4 + XT_U4 + WT_U4);
+        const uint32_t* WS = XS + MTB;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) wsr[i] = WS[wn * 128 + i * 32 + rsel];
+#pragma unroll
+        for (int j = 0; j < JN; ++j) xsr[j] = XS[(2 * j + wm) * 32 + rsel];
+      }
     };
     // fragment reads of step kk of `slot` (4 weight, 2 JN activation), copies
     // c0..c0+NC2-1 of stage q into slot offset d among them
@@ -284,7 +313,7 @@ __device__ __forceinline__ void mx_tile(const MxArgs& a, uint4* smem, int e, int
         const int r = wn * 128 + i * 32 + rsel;
         const uint4 v = W[r * 4 + ((2 * kk + g) ^ ((r >> 2) & 3))];
         wf[set][i] = v8i{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
-        cp(c0 + i, q, d);
+        if (i < NC2) cp(c0 + i, q, d);
       }
 #pragma unroll
       for (int j = 0; j < JN; ++j) {
@@ -309,7 +338,8 @@ __device__ __forceinline__ void mx_tile(const MxArgs& a, uint4* smem, int e, int
       const int slot = st % NSLOT;
       const int q = st + NSLOT - 1 < ktiles ? st + NSLOT - 1 : ktiles - 1;
       const uint32_t d = (uint32_t)((st + NSLOT - 1) % NSLOT) * STAGE_B;
-      rd_scales(slot);
+      if (SG && ((st + NSLOT - 1) & 3) == 0 && st + NSLOT - 1 < ktiles) cp_group(q);
+      rd_scales(slot, st);
       rd_issue(slot, 0, 0, q, d, 0);
       if (!first) mm(1, 1, wsp, xsp);   // the previous stage's second step
       rd_issue(slot, 1, 1, q, d, NC2);
@@ -348,9 +378,11 @@ __device__ __forceinline__ void mx_tile(const MxArgs& a, uint4* smem, int e, int
       __syncthreads();
     };
 #pragma unroll
-    for (int q = 0; q < NSLOT - 1; ++q)
+    for (int q = 0; q < NSLOT - 1; ++q) {
+      if (SG && (q & 3) == 0 && q < ktiles) cp_group(q);
 #pragma unroll
       for (int c = 0; c < NC; ++c) cp(c, q < ktiles ? q : ktiles - 1, (uint32_t)q * STAGE_B);
+    }
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NWAIT) : "memory");
     __syncthreads();
     body(0, true);
@@ -364,8 +396,14 @@ __device__ __forceinline__ void mx_tile(const MxArgs& a, uint4* smem, int e, int
     // (64-byte rows, global chunk (lane % 4) ^ ((row / 4) % 4)); MXFP8 also copies the
     // scale word of the stage's 128-deep block for rows 64 w + lane. Loop rotated by
     // one step: the previous stage's MFMAs run under the current stage's fragment reads.
+    // SG (MXFP8, K a multiple of 512): no words in the stages; with the copies of every
+    // eighth stage 8g each wave first copies 16 bytes of scales (the four words of
+    // stages 8g .. 8g+7) for its 64 activation and 64 weight rows into group buffer
+    // g % 2, as in the MXFP4 loop.
     constexpr int XC8 = XROWS / 64;   // activation copies per wave and stage
-    constexpr uint32_t XCODE_B = XROWS * 64, WCODE_B = 16384, SLOT_B = mx8_stage_u4<WF, JV>() * 16;
+    constexpr uint32_t XCODE_B = XROWS * 64, WCODE_B = 16384,
+                       SLOT_B = mx8_stage_u4<WF, JV, SG>() * 16;
+    constexpr uint32_t SG_B = MX8_SLOTS * SLOT_B;   // scale-group ring (SG)
     // Copies per wave: XC8 + 4 code copies per stage, plus (MXFP8) the 2 scale words
     // for even stages only -- both stages of a 128-deep block use the even one's words.
     // An odd-parity body issues an even stage (or, clamped at the end, a copy nobody
@@ -399,27 +437,47 @@ __device__ __forceinline__ void mx_tile(const MxArgs& a, uint4* smem, int e, int
         mx_dma4(Bs + wsoff + (q >> 1) * 4, lds0s + d + XCODE_B + WCODE_B + 1024u);
       }
     };
+    // SG: the scale group of stage q (a multiple of 8) into buffer (q / 8) % 2
+    auto cp_group = [&](int q) {
+      const uint32_t gb = SG_B + (uint32_t)((q >> 3) & 1) * 8192u + (uint32_t)w * 1024u;
+      mx_dma16(a.A_sf + xsoff + (q >> 1) * 4, (uint32_t)(uintptr_t)smem + gb);
+      mx_dma16(Bs + wsoff + (q >> 1) * 4, (uint32_t)(uintptr_t)smem + gb + 4096u);
+    };
     v8i wf[2][4], xf[2][JN];
     uint32_t wsr[4], xsr[JN], wsp[4], xsp[JN];
 #pragma unroll
     for (int i = 0; i < 4; ++i) wsr[i] = wsp[i] = UNIT_SCALE4;
 #pragma unroll
     for (int j = 0; j < JN; ++j) xsr[j] = xsp[j] = UNIT_SCALE4;
-    constexpr int NWAIT = 2 * (XC8 + 4) + (BS ? 2 : 0);
-    // fragment reads of the stage in `slot` (two 16-byte chunks per fragment), with
+    // SG: a scale group issued with the younger stages is waited for as well (it was
+    // issued first, so this costs little)
+    constexpr int NWAIT = 2 * (XC8 + 4) + (BS && !SG ? 2 : 0);
+    // fragment reads of stage st in `slot` (two 16-byte chunks per fragment), with
     // the copies of stage q into slot offset d spread among them
-    auto rd_issue = [&](int slot, int set, int q, uint32_t d) {
-      const uint4* X = smem + slot * mx8_stage_u4<WF, JV>();
+    auto rd_issue = [&](int slot, int st, int set, int q, uint32_t d) {
+      const uint4* X = smem + slot * mx8_stage_u4<WF, JV, SG>();
       const uint4* W = X + XROWS * 4;
       // the two stages of a 128-deep block share their scale words: the odd stage
       // keeps the even one's in registers
       if (BS && set == 0) {
-        const uint32_t* XS = reinterpret_cast<const uint32_t*>(W + 1024);
-        const uint32_t* WS = XS + MTB;
+        const uint32_t* XS;
+        int ws_off, stride, ph;
+        if (SG) {
+          XS = reinterpret_cast<const uint32_t*>(smem + SG_B / 16 + ((st >> 3) & 1) * 512);
+          ws_off = 4 * MTB;
+          stride = 4;
+          ph = (st >> 1) & 3;
+        } else {
+          XS = reinterpret_cast<const uint32_t*>(W + 1024);
+          ws_off = MTB;
+          stride = 1;
+          ph = 0;
+        }
+        const uint32_t* WS = XS + ws_off;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) wsr[i] = WS[wn * 128 + i * 32 + rsel];
+        for (int i = 0; i < 4; ++i) wsr[i] = WS[(wn * 128 + i * 32 + rsel) * stride + ph];
 #pragma unroll
-        for (int j = 0; j < JN; ++j) xsr[j] = XS[(2 * j + wm) * 32 + rsel];
+        for (int j = 0; j < JN; ++j) xsr[j] = XS[((2 * j + wm) * 32 + rsel) * stride + ph];
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -437,7 +495,7 @@ __device__ __forceinline__ void mx_tile(const MxArgs& a, uint4* smem, int e, int
         xf[set][j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
         cp(4 + j, q, d);
       }
-      if (BS && set == 1) {   // this body issues an even stage
+      if (BS && !SG && set == 1) {   // this body issues an even stage
         cp(XC8 + 4, q, d);
         cp(XC8 + 5, q, d);
       }
@@ -460,7 +518,8 @@ __device__ __forceinline__ void mx_tile(const MxArgs& a, uint4* smem, int e, int
       const int slot = st & (MX8_SLOTS - 1);
       const int q = st + MX8_SLOTS - 1 < nsub ? st + MX8_SLOTS - 1 : nsub - 1;
       const uint32_t d = (uint32_t)((st + MX8_SLOTS - 1) & (MX8_SLOTS - 1)) * SLOT_B;
-      rd_issue(slot, P, q, d);
+      if (SG && ((st + MX8_SLOTS - 1) & 7) == 0 && st + MX8_SLOTS - 1 < nsub) cp_group(q);
+      rd_issue(slot, st, P, q, d);
       if (!first) mm(P ^ 1, P ^ 1, wsp, xsp);   // the previous stage
 #pragma unroll
       for (int i = 0; i < 4; ++i) wsp[i] = wsr[i];
@@ -489,10 +548,12 @@ __device__ __forceinline__ void mx_tile(const MxArgs& a, uint4* smem, int e, int
     static_assert((MX8_SLOTS & (MX8_SLOTS - 1)) == 0, "slot index is taken with a mask");
     static_assert(MX8_SLOTS == 4, "the prologue and the wait count assume four slots");
 #pragma unroll
-    for (int q = 0; q < MX8_SLOTS - 1; ++q)   // stages 0 (+words), 1, 2 (+words)
+    for (int q = 0; q < MX8_SLOTS - 1; ++q) {   // stages 0 (+words / group), 1, 2 (+words)
+      if (SG && q == 0) cp_group(0);
 #pragma unroll
-      for (int c = 0; c < ((BS && (q & 1) == 0) ? XC8 + 6 : XC8 + 4); ++c)
+      for (int c = 0; c < ((BS && !SG && (q & 1) == 0) ? XC8 + 6 : XC8 + 4); ++c)
         cp(c, q < nsub ? q : nsub - 1, (uint32_t)q * SLOT_B);
+    }
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NWAIT) : "memory");
     __syncthreads();
     using P0 = std::integral_constant<int, 0>;
@@ -582,20 +643,22 @@ __device__ __forceinline__ void mx_tile(const MxArgs& a, uint4* smem, int e, int
 }
 
 // 256-row tiles; each picks the number of 32-row blocks per row-wave that hold rows.
-template <int EPI, int WF>
+// SG (block-scaled weights, K a multiple of 512): block scales copied in groups of
+// 512 contraction values per row.
+template <int EPI, int WF, bool SG>
 __global__ __launch_bounds__(MNT, 1) void k_gemm_mx(MxArgs a) {
   __shared__ uint4 smem[mx_lds_u4_max(WF == WF_MXFP4 ? 0 : 1)];
   int e, m0, mend, nt;
   if (!deal_tile<MTB>(a.ends, a.E, a.m_cap, a.n_tiles, e, m0, mend, nt)) return;
   const int jv = (mend - m0 + 63) >> 6;   // 1..4
   if (jv >= 4)
-    mx_tile<EPI, WF, 4>(a, smem, e, m0, mend, nt);
+    mx_tile<EPI, WF, 4, SG>(a, smem, e, m0, mend, nt);
   else if (jv == 3)
-    mx_tile<EPI, WF, 3>(a, smem, e, m0, mend, nt);
+    mx_tile<EPI, WF, 3, SG>(a, smem, e, m0, mend, nt);
   else if (jv == 2)
-    mx_tile<EPI, WF, 2>(a, smem, e, m0, mend, nt);
+    mx_tile<EPI, WF, 2, SG>(a, smem, e, m0, mend, nt);
   else
-    mx_tile<EPI, WF, 1>(a, smem, e, m0, mend, nt);
+    mx_tile<EPI, WF, 1, SG>(a, smem, e, m0, mend, nt);
 }
 
 // Few rows per expert (decode): the cost is streaming the expert bank once. Tile:
@@ -877,8 +940,10 @@ moe_status mx_launch(const MxArgs& a, bool small, int64_t tiles, hipStream_t st)
   const int grid = (int)((tiles + 7) / 8 * 8);
   if (small)
     k_gemm_mx_stream<EPI, WF><<<grid, 256, 0, st>>>(a);
+  else if (block_scaled<WF>() && a.K % 512 == 0)
+    k_gemm_mx<EPI, WF, block_scaled<WF>()><<<grid, MNT, 0, st>>>(a);
   else
-    k_gemm_mx<EPI, WF><<<grid, MNT, 0, st>>>(a);
+    k_gemm_mx<EPI, WF, false><<<grid, MNT, 0, st>>>(a);
   return launch_status();
 }
 

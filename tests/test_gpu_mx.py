@@ -230,17 +230,18 @@ def test_fp8_fc1_per_tensor_requant_matches_oracle_rule(T):
     assert np.all(np.abs(gv - rv) <= step + da)
 
 
-@pytest.mark.parametrize("wfmt", ["mxfp4", "mxfp8"])
-def test_mx_fc2_every_tile_height_exact(wfmt):
+@pytest.mark.parametrize("wfmt,I", [("mxfp4", 256), ("mxfp4", 2048), ("mxfp8", 256), ("mxfp8", 2048)])
+def test_mx_fc2_every_tile_height_exact(wfmt, I):
     """FC2 of the 256-row kernel on operands whose fp32 sums are all exact (e4m3
     activations holding integers up to 6, weights that are multiples of 1/2 up to 6 or
     8, block scales 2^-1 .. 2^2): the output is the bf16 rounding of the exact grouped
     product, bit for bit. The experts' row counts give tiles holding 1..64, 65..128,
     129..192 and 193..256 rows (the 32-row blocks a tile multiplies follow its rows),
-    empty experts and several tiles per expert."""
+    empty experts and several tiles per expert. With a contraction of 2048 the block
+    scales are copied in groups of 512 values per row (two buffers, each reused)."""
     rng = np.random.default_rng(43)
     sizes = np.array([1, 64, 65, 128, 0, 129, 192, 193, 256, 300, 511, 37, 0, 90])
-    L, R, H, I = len(sizes), int(sizes.sum()), 512, 256
+    L, R, H = len(sizes), int(sizes.sum()), 512
     ends = np.cumsum(sizes).astype(np.int32)
     act_v = rng.integers(-6, 7, size=(R, I)).astype(np.float32)
     act = torch.from_numpy(act_v).to(torch.float8_e4m3fn).view(torch.uint8)
