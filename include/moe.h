@@ -298,7 +298,7 @@ moe_status moe_fc2_mx(const moe_ffn_desc* desc, const void* act, const void* act
  * (moe_ffn_forward and its variants, moe_fc1 / moe_fc2 and the fp8-activation stages),
  * use the recorded family; everything else keeps the built-in rule (bf16: the 128-row
  * tile when T * top_k <= 64 * num_experts, else the 256-row tile; fp8 activations: the
- * streaming tile up to 12 / 20 / 24 rows per local expert for FC1 (MXFP4 / MXFP8 /
+ * streaming tile up to 3 / 12 / 24 rows per local expert for FC1 (MXFP4 / MXFP8 /
  * FP8) and up to 2 for FC2 with 8-bit weights, never for the MXFP4 FC2). choice (optional, [2]) receives the FC1 / FC2 picks: 1 the smaller family
  * (128-row or streaming), 0 the 256-row tile.
  * This call and moe_tune_clear are the exceptions to the conventions above: moe_tune

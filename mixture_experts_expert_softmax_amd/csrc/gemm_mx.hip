@@ -906,10 +906,10 @@ __global__ __launch_bounds__(256, 2) void k_gemm_mx_stream(MxArgs a) {
 // The decode kernel takes over while the experts hold few rows on average. The
 // 256-row tiles multiply only the 32-row blocks that hold rows, so the crossover is
 // low; measured at H=7168, I=2048, 64 experts (rows per expert, on average): FC1
-// 12 (MXFP4), 20 (MXFP8), 24 (fp8 per-tensor); FC2 never for MXFP4 (the 256-row tile
+// 3 (MXFP4), 12 (MXFP8), 24 (fp8 per-tensor); FC2 never for MXFP4 (the 256-row tile
 // is faster even at one token), 2 for the 8-bit weights.
 inline int mx_stream_rows(int wf, int stage) {
-  if (stage == 1) return wf == WF_MXFP4 ? 12 : wf == WF_MXFP8 ? 20 : 24;
+  if (stage == 1) return wf == WF_MXFP4 ? 3 : wf == WF_MXFP8 ? 12 : 24;
   return wf == WF_MXFP4 ? 0 : 2;
 }
 inline bool mx_small_fits(int K, int NB, int64_t act_rows, int wb) {

@@ -83,6 +83,16 @@ def _fwd(c, d, ids, w, w1, w1s, w2, w2s, **kw):
     return M.moe_ffn_forward_mx(d["x"], d["x_sf"], ids, w, w1, w1s, w2, w2s, c.num_experts, **kw)
 
 
+def _force_family(c, family, stages=(1, 2), L=None, off=0):
+    """Record tile family `family` (0 the 256-row tile, 1 the decode kernel) for the
+    given stages of case c's shape and bucket; None leaves the built-in rule."""
+    M.moe_tune_clear()
+    if family is not None:
+        for st in stages:
+            M.moe_tune_set(c.T, c.H, c.I, c.num_experts, c.top_k, st, family, num_local_experts=L,
+                           local_expert_offset=off, weight_format=c.wfmt)
+
+
 def _run(c, d, ids=None, w=None, **kw):
     if ids is None:
         ids, w = M.moe_route(torch.from_numpy(c.logits).to(DEV), c.top_k)
@@ -111,9 +121,7 @@ def test_mx_decode_uneven_contraction_split(wfmt):
     of 128 (MXFP8), split unevenly over the decode kernel's 4 waves (with MXFP4 one
     wave of FC2 gets none)."""
     c = S.w4a8_moe(seed=9, T=5, H=1280, I=768, E=16, top_k=4, wfmt=wfmt)
-    M.moe_tune_clear()
-    for stage in (1, 2):   # both stages on the decode kernel
-        M.moe_tune_set(c.T, c.H, c.I, c.num_experts, c.top_k, stage, 1, weight_format=wfmt)
+    _force_family(c, 1)   # both stages on the decode kernel
     out, ids, w = _run(c, _dev(c))
     M.moe_tune_clear()
     assert_close_bf16(out, _oracle(c, ids, w), MX_MAX_ABS, MX_REL, what=f"{wfmt} uneven split")
@@ -127,37 +135,40 @@ def test_mxfp8_decode_short_contraction():
     assert_close_bf16(out, _oracle(c, ids, w), MX_MAX_ABS, MX_REL, what="mxfp8 I=128")
 
 
-# T=200 runs the 256-row tile kernel, T=12 the decode kernel for FC1 (few rows per
-# expert) and the 256-row one, on tiles of 8 rows or so, for FC2
+# T=200 with the built-in rule (the 256-row tile kernel), T=12 on the decode kernel
 @pytest.mark.parametrize("wfmt", WFMTS)
-@pytest.mark.parametrize("T", [200, 12])
-def test_mx_shard_and_step_activation(T, wfmt):
+@pytest.mark.parametrize("T,family", [(200, None), (12, 1)])
+def test_mx_shard_and_step_activation(T, family, wfmt):
     c = S.w4a8_moe(seed=6, T=T, H=256, I=256, E=16, top_k=4, x_scale=4.0, wfmt=wfmt)
     d = _dev(c)
     L, off = 6, 5
     lim = torch.tensor(np.linspace(2.0, 4.0, L), dtype=torch.float32, device=DEV)
     ids, w = M.moe_route(torch.from_numpy(c.logits).to(DEV), c.top_k)
+    _force_family(c, family, L=L, off=off)
     out = _fwd(c, d, ids, w, d["w1"][off:off + L], d["w1_sf"][off:off + L], d["w2"][off:off + L],
                d["w2_sf"][off:off + L], num_local_experts=L, local_expert_offset=off,
                activation="swiglu_step", clamp_limit=lim)
+    M.moe_tune_clear()
     ref = _oracle(c, ids, w, L=L, local_offset=off, activation="swiglu_step",
                   limits=lim.cpu().numpy())
     assert_close_bf16(out, ref, MX_MAX_ABS, MX_REL, what=f"{wfmt} shard step")
 
 
 @pytest.mark.parametrize("wfmt", ["mxfp4", "mxfp8"])
-@pytest.mark.parametrize("T", [256, 24])
-def test_fc1_requant_matches_oracle_rule(T, wfmt):
+@pytest.mark.parametrize("T,family", [(256, 0), (24, 1)])
+def test_fc1_requant_matches_oracle_rule(T, family, wfmt):
     """The fused UE8M0 round-up requantization: scale codes equal the oracle's (rare
     one-step flips allowed where the float32 activations differ in the last bits),
     and the dequantized act stays within half an e4m3 step of the exact activation.
-    T=256 runs the 256-row tile kernel, T=24 the decode kernel."""
+    T=256 on the 256-row tile kernel, T=24 on the decode kernel."""
     c = S.w4a8_moe(seed=7, T=T, H=512, I=512, E=4, top_k=2, wfmt=wfmt)
     d = _dev(c)
     ids, w = M.moe_route(torch.from_numpy(c.logits).to(DEV), c.top_k)
     srt = M.moe_sort(ids, c.num_experts)
+    _force_family(c, family, stages=(1,))
     act, act_sf = M.moe_fc1_mx(d["x"], d["x_sf"], d["w1"], d["w1_sf"], srt["offs"], srt["p2e"],
                                c.top_k, c.num_experts)
+    M.moe_tune_clear()
     n = int(srt["n_local"].item())
     p2e = srt["p2e"][:n].cpu().numpy()
     offs = srt["offs"].cpu().numpy()
@@ -180,19 +191,21 @@ def test_fc1_requant_matches_oracle_rule(T, wfmt):
     assert np.mean(np.abs(deq - a_ref) <= bound) > 0.999
 
 
-@pytest.mark.parametrize("T", [256, 24])
-def test_fp8_fc1_per_tensor_requant_matches_oracle_rule(T):
+@pytest.mark.parametrize("T,family", [(256, 0), (24, 1)])
+def test_fp8_fc1_per_tensor_requant_matches_oracle_rule(T, family):
     """The per-tensor requantization (static scale, float32 reciprocal, saturation at
     +-448): codes equal the oracle's apart from rare flips within the float32
     accumulation error of the activation. x_scale 4 drives some activations past the
-    saturation point 448 * act_scale = 16. T=256 runs the 256-row tile kernel, T=24
+    saturation point 448 * act_scale = 16. T=256 on the 256-row tile kernel, T=24 on
     the decode kernel."""
     c = S.w4a8_moe(seed=7, T=T, H=512, I=512, E=4, top_k=2, wfmt="fp8", x_scale=4.0)
     d = _dev(c)
     ids, w = M.moe_route(torch.from_numpy(c.logits).to(DEV), c.top_k)
     srt = M.moe_sort(ids, c.num_experts)
+    _force_family(c, family, stages=(1,))
     act = M.moe_fc1_fp8(d["x"], d["x_sf"], d["w1"], d["w1_sf"], d["act_scale"], srt["offs"],
                         srt["p2e"], c.top_k, c.num_experts)
+    M.moe_tune_clear()
     n = int(srt["n_local"].item())
     p2e = srt["p2e"][:n].cpu().numpy()
     offs = srt["offs"].cpu().numpy()
