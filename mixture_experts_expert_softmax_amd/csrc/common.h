@@ -128,9 +128,64 @@ __device__ __forceinline__ void tile_locate(const int32_t* __restrict__ ends, in
   }
 }
 
+// Source rows of gathered activation rows: v holds permuted rows p on entry and
+// g[p] / div on return when g is given (all loads issued before any is used, so
+// a tile's prologue waits once for them, not once per row).
+template <int N>
+__device__ __forceinline__ void gather_rows(const int32_t* __restrict__ g, int div, int (&v)[N]) {
+  if (g) {
+#pragma unroll
+    for (int j = 0; j < N; ++j) v[j] = g[v[j]];
+#pragma unroll
+    for (int j = 0; j < N; ++j) v[j] /= div;
+  }
+}
+
+// Up to 64 groups: one scan pass serves both the count and the lookup (one load of
+// the ends per tile instead of two), kept in the lane registers.
+struct TileScan64 {
+  int cend, pend, incl, total;
+};
+template <int TM>
+__device__ __forceinline__ TileScan64 tile_scan64(const int32_t* __restrict__ ends, int E, int m_cap,
+                                                  int n_tiles) {
+  const int lane = threadIdx.x & 63;
+  int ce = 0, tc = 0;
+  TileScan64 s;
+  tile_scan_pass<TM>(ends, E, m_cap, n_tiles, 0, lane, ce, tc, s.cend, s.pend, s.incl);
+  s.total = tc;
+  return s;
+}
+// tile_locate from a scan taken with n_scanned column tiles, for n_used column tiles
+// (every group's tile count is a multiple of n_scanned, so the division is exact)
+template <int TM>
+__device__ __forceinline__ void tile_locate64(const TileScan64& s, int n_scanned, int n_used, int t,
+                                              int& e, int& m0, int& mend, int& nt) {
+  const int inc = s.incl / n_scanned * n_used;
+  const unsigned long long hit = __ballot(inc > t);
+  const int L = __ffsll(hit) - 1;
+  const int ge = __builtin_amdgcn_readlane(s.cend, L);
+  const int gs = __builtin_amdgcn_readlane(s.pend, L);
+  const int te = (ge - gs + TM - 1) / TM;
+  const int r = t - (__builtin_amdgcn_readlane(inc, L) - te * n_used);
+  nt = r / te;
+  e = L;
+  m0 = gs + (r - nt * te) * TM;
+  mend = ge;
+}
+
 template <int TM>
 __device__ __forceinline__ bool deal_tile(const int32_t* __restrict__ ends, int E, int m_cap,
                                           int n_tiles, int& e, int& m0, int& mend, int& nt) {
+  if (E <= 64) {
+    const TileScan64 s = tile_scan64<TM>(ends, E, m_cap, n_tiles);
+    const int per = (s.total + 7) >> 3;
+    const int slot = (int)(blockIdx.x >> 3);
+    const int t = (int)(blockIdx.x & 7) * per + slot;
+    if (slot >= per || t >= s.total) return false;
+    tile_locate64<TM>(s, n_tiles, n_tiles, t, e, m0, mend, nt);
+    return true;
+  }
   const int total = tile_count<TM>(ends, E, m_cap, n_tiles);
   const int per = (total + 7) >> 3;
   const int slot = (int)(blockIdx.x >> 3);

@@ -101,7 +101,10 @@ __device__ __forceinline__ bool deal_tile_split(const int32_t* ends, int E, int 
                                                 int n_res, int ktiles, int& e, int& m0, int& mend,
                                                 int& nt, int& k0, int& nk, int& part, int& S,
                                                 int& slot, int& cidx, bool mmajor = false) {
-  const int total = tile_count<TM>(ends, E, m_cap, n_tiles);
+  const bool one_pass = E <= 64;   // a single scan serves count and lookup
+  TileScan64 sc{};
+  if (one_pass) sc = tile_scan64<TM>(ends, E, m_cap, n_tiles);
+  const int total = one_pass ? sc.total : tile_count<TM>(ends, E, m_cap, n_tiles);
   const int b = (int)blockIdx.x;
   int full = total, rem = 0;
   S = 1;
@@ -136,8 +139,13 @@ __device__ __forceinline__ bool deal_tile_split(const int32_t* ends, int E, int 
   if (mmajor) {
     const int rb = total / n_tiles;   // row blocks over all groups
     int unused;
-    tile_locate<TM>(ends, E, m_cap, 1, t % rb, e, m0, mend, unused);
+    if (one_pass)
+      tile_locate64<TM>(sc, n_tiles, 1, t % rb, e, m0, mend, unused);
+    else
+      tile_locate<TM>(ends, E, m_cap, 1, t % rb, e, m0, mend, unused);
     nt = t / rb;
+  } else if (one_pass) {
+    tile_locate64<TM>(sc, n_tiles, n_tiles, t, e, m0, mend, nt);
   } else {
     tile_locate<TM>(ends, E, m_cap, n_tiles, t, e, m0, mend, nt);
   }
@@ -702,12 +710,18 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_nt(NtArgs a) {
   lb.base = a.B + (int64_t)e * a.b_stride;
   lb.K = a.K;
   lb.ch = tid & 7;
+  // source rows of the activation copies: the gathered indices are loaded together
+  // (one wait for all eight, not one per row)
+  int src[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    int p = m0 + lrow + 32 * j;
-    p = p < mend ? p : mend - 1;
-    const int src = a.a_gather ? a.a_gather[p] / a.a_div : p;
-    la.off[j] = (uint32_t)src * (uint32_t)a.K;
+    const int p = m0 + lrow + 32 * j;
+    src[j] = p < mend ? p : mend - 1;
+  }
+  gather_rows(a.a_gather, a.a_div, src);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    la.off[j] = (uint32_t)src[j] * (uint32_t)a.K;
     const int R = lrow + 32 * j;
     int wrow;
     if (EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_STEP) {

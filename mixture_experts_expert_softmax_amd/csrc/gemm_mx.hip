@@ -194,12 +194,23 @@ __device__ __forceinline__ void mx_tile(const MxArgs& a, uint4* smem, int e, int
   const int xr = tid >> 3, xc = tid & 7, wr = tid / WCH, wc = tid % WCH;
   const uint32_t kw = (uint32_t)K * WB / 8;   // weight bytes per row
   uint32_t xoff[XROWS / 32], woff[WLD];
+  // source rows, gathered together: the MXFP4 copy rows xr + 32 j, the 8-bit copy
+  // rows (tid >> 2) + 64 j, and the scale row tid % XROWS
+  constexpr int NXR = WF == WF_MXFP4 ? XROWS / 32 : JV;
+  int src[NXR + 1];
 #pragma unroll
-  for (int j = 0; j < XROWS / 32; ++j) {
-    int p = m0 + xr + 32 * j;
-    p = p < mend ? p : mend - 1;
-    const int src = a.a_gather ? a.a_gather[p] / a.a_div : p;
-    xoff[j] = (uint32_t)src * (uint32_t)K + xc * 16;
+  for (int j = 0; j < NXR; ++j) {
+    const int p = m0 + (WF == WF_MXFP4 ? xr + 32 * j : (tid >> 2) + 64 * j);
+    src[j] = p < mend ? p : mend - 1;
+  }
+  {
+    const int p = m0 + tid % XROWS;
+    src[NXR] = p < mend ? p : mend - 1;
+  }
+  gather_rows(a.a_gather, a.a_div, src);
+  if constexpr (WF == WF_MXFP4) {
+#pragma unroll
+    for (int j = 0; j < XROWS / 32; ++j) xoff[j] = (uint32_t)src[j] * (uint32_t)K + xc * 16;
   }
   auto wrow_of = [&](int R) {
     if (fc1) {
@@ -215,13 +226,8 @@ __device__ __forceinline__ void mx_tile(const MxArgs& a, uint4* smem, int e, int
 #pragma unroll
   for (int j = 0; j < WLD; ++j) woff[j] = (uint32_t)wrow_of(wr + (MTB / WLD) * j) * kw + wc * 16;
   uint32_t xsoff, wsoff;
-  {
-    int p = m0 + tid % XROWS;
-    p = p < mend ? p : mend - 1;
-    const int src = a.a_gather ? a.a_gather[p] / a.a_div : p;
-    xsoff = (uint32_t)src * (uint32_t)ks;
-    wsoff = (uint32_t)wrow_of(tid) * (uint32_t)ks;
-  }
+  xsoff = (uint32_t)src[NXR] * (uint32_t)ks;
+  wsoff = (uint32_t)wrow_of(tid) * (uint32_t)ks;
   f32x16 acc[4][JN];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -417,12 +423,7 @@ __device__ __forceinline__ void mx_tile(const MxArgs& a, uint4* smem, int e, int
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int R = (tid >> 2) + 64 * j;
-      if (j < XC8) {
-        int p = m0 + R;
-        p = p < mend ? p : mend - 1;
-        const int src = a.a_gather ? a.a_gather[p] / a.a_div : p;
-        xrow[j] = (uint32_t)src * (uint32_t)K + gc * 16;
-      }
+      if (j < XC8) xrow[j] = (uint32_t)src[j] * (uint32_t)K + gc * 16;
       wrow[j] = (uint32_t)wrow_of(R) * kw + gc * 16;
     }
     const int nsub = K / 64;
