@@ -81,6 +81,7 @@ struct NtArgs {
   int32_t* split_cnt;        // split tiles: arrival counters, 0 between launches
   int n_res;                 // workgroups resident at once (0: never split)
   bool mmajor;               // deal tiles column tile first (deal_tile_split)
+  bool lds_epi;              // C and its row stride allow 16-byte stores (staged epilogue)
 };
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
@@ -325,11 +326,13 @@ __device__ __forceinline__ void zero_acc(f32x16 (&acc)[4][4]) {
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 }
 
-__device__ __forceinline__ void atomic_add_bf16x2(uint16_t* p, float a, float b) {
+__device__ __forceinline__ void atomic_add_bf16x2_bits(uint16_t* p, uint32_t bits) {
   typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-  const uint32_t bits = pack_bf16x2(a, b);
   __builtin_amdgcn_global_atomic_fadd_v2bf16(reinterpret_cast<bf16x2_t*>(p),
                                              __builtin_bit_cast(bf16x2_t, bits));
+}
+__device__ __forceinline__ void atomic_add_bf16x2(uint16_t* p, float a, float b) {
+  atomic_add_bf16x2_bits(p, pack_bf16x2(a, b));
 }
 
 // Direct-to-LDS copy of one 16-byte chunk per lane: the chunk at g lands at LDS byte
@@ -787,6 +790,91 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_nt(NtArgs a) {
   // ---- epilogue: lane holds rows m, 4 consecutive columns per (i, q); row block j
   // of wave row wm starts at row 32 (wm jn + j) of the tile
   const int hi4 = (lane >> 5) * 4;
+  constexpr bool FC1 = EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_STEP;
+  if constexpr (EPI != EPI_ROWMAP_F32W) {
+    if (a.lds_epi && !(FC1 && a.h_out)) {
+      // Staged through LDS (free once every wave is past the loop): in registers a lane
+      // holds 4 columns of one row per store, so direct stores put 32 rows x 16 bytes in
+      // each instruction -- 32 partial cache lines, whose write requests then bound the
+      // epilogue (about 10 us per 256 x 256 tile with every CU storing at once). The
+      // tile goes to LDS as bf16 rows (16-byte chunks XOR-swizzled by row, so the 32
+      // rows of a write and the chunks of a read fall on distinct banks) and leaves in
+      // whole rows: 16 bytes per lane, each instruction covering whole 128-byte lines.
+      // The values are exactly those of the direct path.
+      constexpr int TC = FC1 ? 128 : TB;   // output columns of the tile
+      constexpr int NCH = TC / 8;          // 16-byte chunks per tile row
+      constexpr int RSB = TC * 2;          // LDS bytes per tile row
+      constexpr int NI = FC1 ? 2 : 4;      // 32-column blocks per wave
+      constexpr int CW = TC / 2;           // tile columns per wave
+      char* lds = reinterpret_cast<char*>(smem);
+      float lim = 0.f;
+      if (EPI == EPI_SWIGLU_STEP) lim = a.limits ? a.limits[e] : a.def_limit;
+      float wgt[4] = {1.f, 1.f, 1.f, 1.f};
+      if (EPI == EPI_FUSED) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int p = m0 + wm * jn * 32 + j * 32 + (lane & 31);
+          wgt[j] = (j < jn && p < mend) ? a.route_w[a.p2e[p]] : 0.f;
+        }
+      }
+      __syncthreads();   // no wave still reads a stage or has a copy in flight
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (j >= jn) continue;
+        const int R = wm * jn * 32 + j * 32 + (lane & 31);
+#pragma unroll
+        for (int i = 0; i < NI; ++i)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int c = wn * CW + i * 32 + q * 8 + hi4;
+            float v[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              if (FC1) {
+                float u = acc[i][j][q * 4 + r];
+                float g = acc[i + 2][j][q * 4 + r];
+                if (EPI == EPI_SWIGLU_STEP) {
+                  u = fminf(fmaxf(u, -lim), lim);
+                  g = fminf(fmaxf(g, -lim), lim);
+                }
+                v[r] = silu_f32(g) * u;
+              } else {
+                v[r] = EPI == EPI_FUSED ? wgt[j] * acc[i][j][q * 4 + r] : acc[i][j][q * 4 + r];
+              }
+            }
+            const uint32_t off = (uint32_t)(R * RSB + ((((c >> 3) ^ (R % NCH)) << 4) | (hi4 << 1)));
+            *reinterpret_cast<uint2*>(lds + off) =
+                make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+          }
+      }
+      __syncthreads();
+      // read back: lane k of a row's NCH lanes takes chunk k; 64 / NCH rows per instruction
+      constexpr int RPI = 64 / NCH;
+      const int rows = mend - m0 < 64 * jn ? mend - m0 : 64 * jn;
+      const int k = lane % NCH;
+      const int col = nt * TC + k * 8;
+      if (col < (FC1 ? a.I : a.N)) {
+#pragma unroll 4
+        for (int r0 = wid * RPI; r0 < rows; r0 += 4 * RPI) {
+          const int R = r0 + lane / NCH;
+          if (R >= rows) continue;
+          const uint4 v = *reinterpret_cast<const uint4*>(lds + R * RSB + ((k ^ (R % NCH)) << 4));
+          const int p = m0 + R;
+          if (EPI == EPI_FUSED) {
+            uint16_t* d = a.C + (int64_t)(a.p2e[p] / a.top_k) * a.ldc + col;
+            atomic_add_bf16x2_bits(d, v.x);
+            atomic_add_bf16x2_bits(d + 2, v.y);
+            atomic_add_bf16x2_bits(d + 4, v.z);
+            atomic_add_bf16x2_bits(d + 6, v.w);
+          } else {
+            const int64_t row = EPI == EPI_ROWMAP ? a.p2e[p] : p;
+            *reinterpret_cast<uint4*>(a.C + row * a.ldc + col) = v;
+          }
+        }
+      }
+      return;
+    }
+  }
   if (EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_STEP) {
     float lim = 0.f;
     if (EPI == EPI_SWIGLU_STEP) lim = a.limits ? a.limits[e] : a.def_limit;
@@ -1179,6 +1267,7 @@ moe_status gemm_nt_enqueue(int epi, const void* A, const int32_t* a_gather, int 
   const size_t out_bytes = (size_t)(M / (top_k > 0 ? top_k : 1)) * N * 2;
   a.mmajor = epi == EPI_FUSED && ((K <= 192 && out_bytes >= (32u << 20)) ||
                                   (K <= 384 && out_bytes >= (64u << 20)));
+  a.lds_epi = ((uintptr_t)C % 16) == 0 && (ldc % 8) == 0;
   if (split_ws && split_cnt && kfull) {
     const int cu = device_cu_count();
     a.n_res = (cu < SPLIT_SLOTS ? cu : SPLIT_SLOTS) & ~7;  // one 128 KB-LDS workgroup per CU
