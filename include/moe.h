@@ -26,6 +26,8 @@
  * ---------------------------------------
  * - Every tensor argument is a DEVICE pointer to dense row-major memory owned by
  *   the caller; bf16 tensors are passed as `const void*` (IEEE bfloat16 bits).
+ *   Tensor pointers are 16-byte aligned (MOE_ERR_ALIGN otherwise): the kernels move
+ *   whole 16-byte chunks of rows.
  * - `stream` is a hipStream_t (NULL = the null stream). Work is only enqueued:
  *   no call allocates device or host memory, synchronises the host, or reads
  *   device memory from the host. Outputs are valid once the stream reaches them.

@@ -470,7 +470,8 @@ extern "C" moe_status moe_fc1_mx(const moe_ffn_desc* d, const void* x, const voi
   if (!block_scaled(d->weight_format)) return MOE_ERR_DTYPE;
   if (d->T == 0) return MOE_OK;
   if (!x || !x_sf || !w1 || !w1_sf || !offs || !p2e || !act || !act_sf) return MOE_ERR_NULL;
-  if (!aligned16(x) || !aligned16(w1) || !aligned16(act) || !aligned16(x_sf) || !aligned16(w1_sf))
+  if (!aligned16(x) || !aligned16(w1) || !aligned16(act) || !aligned16(x_sf) || !aligned16(w1_sf) ||
+      !aligned16(act_sf))
     return MOE_ERR_ALIGN;
   const int32_t L = d->num_local_experts > 0 ? d->num_local_experts : d->num_experts;
   return mx_fc1_enqueue(d->activation, mx_wf(d->weight_format), x, x_sf, p2e, d->top_k, w1, w1_sf,

@@ -81,7 +81,6 @@ struct NtArgs {
   int32_t* split_cnt;        // split tiles: arrival counters, 0 between launches
   int n_res;                 // workgroups resident at once (0: never split)
   bool mmajor;               // deal tiles column tile first (deal_tile_split)
-  bool lds_epi;              // C and its row stride allow 16-byte stores (staged epilogue)
 };
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
@@ -791,66 +790,88 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_nt(NtArgs a) {
   // of wave row wm starts at row 32 (wm jn + j) of the tile
   const int hi4 = (lane >> 5) * 4;
   constexpr bool FC1 = EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_STEP;
-  if constexpr (EPI != EPI_ROWMAP_F32W) {
-    if (a.lds_epi && !(FC1 && a.h_out)) {
-      // Staged through LDS (free once every wave is past the loop): in registers a lane
-      // holds 4 columns of one row per store, so direct stores put 32 rows x 16 bytes in
-      // each instruction -- 32 partial cache lines, whose write requests then bound the
-      // epilogue (about 10 us per 256 x 256 tile with every CU storing at once). The
-      // tile goes to LDS as bf16 rows (16-byte chunks XOR-swizzled by row, so the 32
-      // rows of a write and the chunks of a read fall on distinct banks) and leaves in
-      // whole rows: 16 bytes per lane, each instruction covering whole 128-byte lines.
-      // The values are exactly those of the direct path.
-      constexpr int TC = FC1 ? 128 : TB;   // output columns of the tile
-      constexpr int NCH = TC / 8;          // 16-byte chunks per tile row
-      constexpr int RSB = TC * 2;          // LDS bytes per tile row
-      constexpr int NI = FC1 ? 2 : 4;      // 32-column blocks per wave
-      constexpr int CW = TC / 2;           // tile columns per wave
-      char* lds = reinterpret_cast<char*>(smem);
-      float lim = 0.f;
-      if (EPI == EPI_SWIGLU_STEP) lim = a.limits ? a.limits[e] : a.def_limit;
-      float wgt[4] = {1.f, 1.f, 1.f, 1.f};
-      if (EPI == EPI_FUSED) {
+  if constexpr (EPI == EPI_ROWMAP_F32W) {
+    // the BGMV expand's fp32 partials: few columns (the LoRA output width), stored
+    // straight from registers
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int p = m0 + wm * jn * 32 + j * 32 + (lane & 31);
-          wgt[j] = (j < jn && p < mend) ? a.route_w[a.p2e[p]] : 0.f;
+    for (int j = 0; j < 4; ++j) {
+      const int p = m0 + wm * jn * 32 + j * 32 + (lane & 31);
+      if (j >= jn || p >= mend) continue;
+      const int row = a.p2e[p];
+      const float wgt = a.route_w[row];
+      float* crow = reinterpret_cast<float*>(a.C) + (int64_t)row * a.ldc;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int col = nt * TB + wn * 128 + i * 32 + q * 8 + hi4;
+          if (col >= a.N) continue;
+          *reinterpret_cast<float4*>(crow + col) =
+              make_float4(wgt * acc[i][j][q * 4 + 0], wgt * acc[i][j][q * 4 + 1],
+                          wgt * acc[i][j][q * 4 + 2], wgt * acc[i][j][q * 4 + 3]);
         }
-      }
-      __syncthreads();   // no wave still reads a stage or has a copy in flight
+    }
+  } else {
+    // Staged through LDS (free once every wave is past the loop): in registers a lane
+    // holds 4 columns of one row, so stores straight from registers would put 32 rows
+    // x 8 bytes in each instruction -- 32 partial cache lines, whose write requests
+    // then bound the epilogue (about 10 us per 256 x 256 tile with every CU storing at
+    // once). The tile goes to LDS in rows (16-byte chunks XOR-swizzled by row, so the
+    // 32 rows of a write and the chunks of a read fall on distinct banks) and leaves
+    // in whole rows: 16 bytes per lane, each instruction covering whole 128-byte
+    // lines. Every output pointer is 16-byte aligned and every row stride a multiple
+    // of 16 bytes (the entry points' rules).
+    constexpr int TC = FC1 ? 128 : TB;   // output columns of the tile
+    constexpr int NCH = TC / 8;          // 16-byte bf16 chunks per tile row
+    constexpr int RSB = TC * 2;          // LDS bytes per bf16 tile row
+    constexpr int NI = FC1 ? 2 : 4;      // 32-column blocks per wave
+    constexpr int CW = TC / 2;           // tile columns per wave
+    char* lds = reinterpret_cast<char*>(smem);
+    const int rows = mend - m0 < 64 * jn ? mend - m0 : 64 * jn;
+    float lim = 0.f;
+    if (EPI == EPI_SWIGLU_STEP) lim = a.limits ? a.limits[e] : a.def_limit;
+    float wgt[4] = {1.f, 1.f, 1.f, 1.f};
+    if (EPI == EPI_FUSED) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        if (j >= jn) continue;
-        const int R = wm * jn * 32 + j * 32 + (lane & 31);
-#pragma unroll
-        for (int i = 0; i < NI; ++i)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int c = wn * CW + i * 32 + q * 8 + hi4;
-            float v[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              if (FC1) {
-                float u = acc[i][j][q * 4 + r];
-                float g = acc[i + 2][j][q * 4 + r];
-                if (EPI == EPI_SWIGLU_STEP) {
-                  u = fminf(fmaxf(u, -lim), lim);
-                  g = fminf(fmaxf(g, -lim), lim);
-                }
-                v[r] = silu_f32(g) * u;
-              } else {
-                v[r] = EPI == EPI_FUSED ? wgt[j] * acc[i][j][q * 4 + r] : acc[i][j][q * 4 + r];
-              }
-            }
-            const uint32_t off = (uint32_t)(R * RSB + ((((c >> 3) ^ (R % NCH)) << 4) | (hi4 << 1)));
-            *reinterpret_cast<uint2*>(lds + off) =
-                make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
-          }
+        const int p = m0 + wm * jn * 32 + j * 32 + (lane & 31);
+        wgt[j] = (j < jn && p < mend) ? a.route_w[a.p2e[p]] : 0.f;
       }
-      __syncthreads();
-      // read back: lane k of a row's NCH lanes takes chunk k; 64 / NCH rows per instruction
+    }
+    __syncthreads();   // no wave still reads a stage or has a copy in flight
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (j >= jn) continue;
+      const int R = wm * jn * 32 + j * 32 + (lane & 31);
+#pragma unroll
+      for (int i = 0; i < NI; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int c = wn * CW + i * 32 + q * 8 + hi4;
+          float v[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            if (FC1) {
+              float u = acc[i][j][q * 4 + r];
+              float g = acc[i + 2][j][q * 4 + r];
+              if (EPI == EPI_SWIGLU_STEP) {
+                u = fminf(fmaxf(u, -lim), lim);
+                g = fminf(fmaxf(g, -lim), lim);
+              }
+              v[r] = silu_f32(g) * u;
+            } else {
+              v[r] = EPI == EPI_FUSED ? wgt[j] * acc[i][j][q * 4 + r] : acc[i][j][q * 4 + r];
+            }
+          }
+          const uint32_t off = (uint32_t)(R * RSB + ((((c >> 3) ^ (R % NCH)) << 4) | (hi4 << 1)));
+          *reinterpret_cast<uint2*>(lds + off) =
+              make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+        }
+    }
+    __syncthreads();
+    {
+      // read back: lane k of a row's NCH lanes takes chunk k; 64 / NCH rows per read
       constexpr int RPI = 64 / NCH;
-      const int rows = mend - m0 < 64 * jn ? mend - m0 : 64 * jn;
       const int k = lane % NCH;
       const int col = nt * TC + k * 8;
       if (col < (FC1 ? a.I : a.N)) {
@@ -872,99 +893,43 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_nt(NtArgs a) {
           }
         }
       }
-      return;
     }
-  }
-  if (EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_STEP) {
-    float lim = 0.f;
-    if (EPI == EPI_SWIGLU_STEP) lim = a.limits ? a.limits[e] : a.def_limit;
+    if constexpr (FC1) {
+      // the training forward also keeps the fp32 pre-activations h = [up | gate]
+      // (exactly the values the activation above saw): two more passes of
+      // [256 rows][128 floats], up then gate, each leaving in whole rows
+      if (a.h_out) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int p = m0 + wm * jn * 32 + j * 32 + (lane & 31);
-      if (j >= jn || p >= mend) continue;
-      uint16_t* crow = a.C + (int64_t)p * a.ldc;
+        for (int half = 0; half < 2; ++half) {
+          __syncthreads();   // the previous pass's reads are done
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+          for (int j = 0; j < 4; ++j) {
+            if (j >= jn) continue;
+            const int R = wm * jn * 32 + j * 32 + (lane & 31);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int col = nt * 128 + wn * 64 + i * 32 + q * 8 + hi4;
-          if (col >= a.I) continue;
-          if (a.h_out) {   // exactly the values the activation below sees
-            float* hrow = a.h_out + (int64_t)p * 2 * a.I;
-            *reinterpret_cast<float4*>(hrow + col) =
-                make_float4(acc[i][j][q * 4 + 0], acc[i][j][q * 4 + 1], acc[i][j][q * 4 + 2],
-                            acc[i][j][q * 4 + 3]);
-            *reinterpret_cast<float4*>(hrow + a.I + col) =
-                make_float4(acc[i + 2][j][q * 4 + 0], acc[i + 2][j][q * 4 + 1],
-                            acc[i + 2][j][q * 4 + 2], acc[i + 2][j][q * 4 + 3]);
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                const int c = wn * 64 + i * 32 + q * 8 + hi4;   // 4 floats: one chunk
+                const f32x16& s4 = acc[i + 2 * half][j];
+                *reinterpret_cast<float4*>(lds + R * 512 + (((c >> 2) ^ (R & 31)) << 4)) =
+                    make_float4(s4[q * 4 + 0], s4[q * 4 + 1], s4[q * 4 + 2], s4[q * 4 + 3]);
+              }
           }
-          float v[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            float u = acc[i][j][q * 4 + r];
-            float g = acc[i + 2][j][q * 4 + r];
-            if (EPI == EPI_SWIGLU_STEP) {
-              u = fminf(fmaxf(u, -lim), lim);
-              g = fminf(fmaxf(g, -lim), lim);
+          __syncthreads();
+          const int k = lane & 31;   // 16-byte chunk of a 512-byte row; 2 rows per read
+          const int col = nt * 128 + k * 4;
+          if (col < a.I) {
+#pragma unroll 4
+            for (int r0 = wid * 2; r0 < rows; r0 += 8) {
+              const int R = r0 + (lane >> 5);
+              if (R >= rows) continue;
+              const float4 v = *reinterpret_cast<const float4*>(lds + R * 512 + ((k ^ (R & 31)) << 4));
+              *reinterpret_cast<float4*>(a.h_out + (int64_t)(m0 + R) * 2 * a.I + half * a.I + col) = v;
             }
-            v[r] = silu_f32(g) * u;
           }
-          *reinterpret_cast<uint2*>(crow + col) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
         }
-    }
-  } else if (EPI == EPI_FUSED) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int p = m0 + wm * jn * 32 + j * 32 + (lane & 31);
-      if (j >= jn || p >= mend) continue;
-      const int route = a.p2e[p];
-      const float wgt = a.route_w[route];
-      uint16_t* crow = a.C + (int64_t)(route / a.top_k) * a.ldc;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int col = nt * TB + wn * 128 + i * 32 + q * 8 + hi4;
-          if (col >= a.N) continue;
-          atomic_add_bf16x2(crow + col, wgt * acc[i][j][q * 4 + 0], wgt * acc[i][j][q * 4 + 1]);
-          atomic_add_bf16x2(crow + col + 2, wgt * acc[i][j][q * 4 + 2], wgt * acc[i][j][q * 4 + 3]);
-        }
-    }
-  } else if (EPI == EPI_ROWMAP_F32W) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int p = m0 + wm * jn * 32 + j * 32 + (lane & 31);
-      if (j >= jn || p >= mend) continue;
-      const int row = a.p2e[p];
-      const float wgt = a.route_w[row];
-      float* crow = reinterpret_cast<float*>(a.C) + (int64_t)row * a.ldc;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int col = nt * TB + wn * 128 + i * 32 + q * 8 + hi4;
-          if (col >= a.N) continue;
-          *reinterpret_cast<float4*>(crow + col) =
-              make_float4(wgt * acc[i][j][q * 4 + 0], wgt * acc[i][j][q * 4 + 1],
-                          wgt * acc[i][j][q * 4 + 2], wgt * acc[i][j][q * 4 + 3]);
-        }
-    }
-  } else {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int p = m0 + wm * jn * 32 + j * 32 + (lane & 31);
-      if (j >= jn || p >= mend) continue;
-      uint16_t* crow = a.C + (int64_t)(EPI == EPI_ROWMAP ? a.p2e[p] : p) * a.ldc;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int col = nt * TB + wn * 128 + i * 32 + q * 8 + hi4;
-          if (col >= a.N) continue;
-          *reinterpret_cast<uint2*>(crow + col) =
-              make_uint2(pack_bf16x2(acc[i][j][q * 4 + 0], acc[i][j][q * 4 + 1]),
-                         pack_bf16x2(acc[i][j][q * 4 + 2], acc[i][j][q * 4 + 3]));
-        }
+      }
     }
   }
 }
@@ -1267,7 +1232,6 @@ moe_status gemm_nt_enqueue(int epi, const void* A, const int32_t* a_gather, int 
   const size_t out_bytes = (size_t)(M / (top_k > 0 ? top_k : 1)) * N * 2;
   a.mmajor = epi == EPI_FUSED && ((K <= 192 && out_bytes >= (32u << 20)) ||
                                   (K <= 384 && out_bytes >= (64u << 20)));
-  a.lds_epi = ((uintptr_t)C % 16) == 0 && (ldc % 8) == 0;
   if (split_ws && split_cnt && kfull) {
     const int cu = device_cu_count();
     a.n_res = (cu < SPLIT_SLOTS ? cu : SPLIT_SLOTS) & ~7;  // one 128 KB-LDS workgroup per CU

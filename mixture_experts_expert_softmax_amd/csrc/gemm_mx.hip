@@ -579,17 +579,26 @@ __device__ __forceinline__ void mx_tile(const MxArgs& a, uint4* smem, int e, int
     for (int j = 0; j < JN; ++j) asm volatile("" : "+a"(acc[i][j]));
   const int hi4 = (lane >> 5) * 4;
   const float alpha = pt_alpha<WF>(a, e);
+  // Staged through LDS, as in the bf16 forward kernels: in registers a lane holds 4
+  // columns of one row, so stores straight from registers would cover 32 rows x 4
+  // (FC1) or 8 (FC2) bytes per instruction. The tile goes to LDS (16-byte chunks
+  // XOR-swizzled by row) and leaves in whole 128-byte lines; FC1's block scale codes
+  // leave as one 4-byte word per row (I is a multiple of 128, so a tile's four codes
+  // of a row are one aligned word; outputs are 16-byte aligned by the entry points).
+  char* lds = reinterpret_cast<char*>(smem);
+  const int rows = mend - m0 < 64 * JN ? mend - m0 : 64 * JN;
+  __syncthreads();   // no wave still reads a stage or has a copy in flight
   if (fc1) {
+    // e4m3 tile [256 rows][128 B] at 0, scale codes [256 rows][4 B] after it
+    constexpr int SC_OFF = 256 * 128;
     float lim = 0.f;
     if (EPI == MX_FC1_STEP) lim = a.limits ? a.limits[e] : a.def_limit;
     const float qinv = BS ? 1.f : 1.0f / a.q_scale[0];
 #pragma unroll
     for (int j = 0; j < JN; ++j) {
-      const int p = m0 + (2 * j + wm) * 32 + rsel;
-      const bool row_ok = p < mend;
+      const int R = (2 * j + wm) * 32 + rsel;
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
-        const int col0 = nt * 128 + wn * 64 + i * 32;   // one 32-column scale block
         float v[16];
         float amax = 0.f;
 #pragma unroll
@@ -610,35 +619,67 @@ __device__ __forceinline__ void mx_tile(const MxArgs& a, uint4* smem, int e, int
           code = ue8m0_round_up_448(amax);
           inv = __uint_as_float((254u - code) << 23);   // 2^(127 - code)
         }
-        if (!row_ok || col0 >= a.I) continue;
-        uint8_t* crow = a.Cq + (int64_t)p * a.I;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          int pk = __builtin_amdgcn_cvt_pk_fp8_f32(q_in<WF>(v[4 * q], inv), q_in<WF>(v[4 * q + 1], inv),
-                                                   0, false);
-          pk = __builtin_amdgcn_cvt_pk_fp8_f32(q_in<WF>(v[4 * q + 2], inv), q_in<WF>(v[4 * q + 3], inv),
-                                               pk, true);
-          *reinterpret_cast<uint32_t*>(crow + col0 + q * 8 + hi4) = (uint32_t)pk;
+          int pk = __builtin_amdgcn_cvt_pk_fp8_f32(q_in<WF>(v[4 * q], inv),
+                                                   q_in<WF>(v[4 * q + 1], inv), 0, false);
+          pk = __builtin_amdgcn_cvt_pk_fp8_f32(q_in<WF>(v[4 * q + 2], inv),
+                                               q_in<WF>(v[4 * q + 3], inv), pk, true);
+          const int c = wn * 64 + i * 32 + q * 8 + hi4;   // byte column of the tile
+          const int off = R * 128 + ((((c >> 4) ^ ((R >> 1) & 7)) << 4) | (c & 15));
+          *reinterpret_cast<uint32_t*>(lds + off) = (uint32_t)pk;
         }
-        if (BS && g == 0) a.Cq_sf[(int64_t)p * (a.I >> 5) + (col0 >> 5)] = (uint8_t)code;
+        if (BS && g == 0) lds[SC_OFF + R * 4 + wn * 2 + i] = (char)code;
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
+    __syncthreads();
+    const int k = lane & 7;   // 16-byte chunk of a 128-byte tile row; 8 rows per read
+    const int col = nt * 128 + k * 16;
+    if (col < a.I) {
+#pragma unroll 2
+      for (int r0 = wid * 8; r0 < rows; r0 += 32) {
+        const int R = r0 + (lane >> 3);
+        if (R >= rows) continue;
+        const uint4 v = *reinterpret_cast<const uint4*>(lds + R * 128 + ((k ^ ((R >> 1) & 7)) << 4));
+        *reinterpret_cast<uint4*>(a.Cq + (int64_t)(m0 + R) * a.I + col) = v;
+      }
+    }
+    if (BS) {
+      const int R = wid * 64 + lane;
+      if (R < rows)
+        *reinterpret_cast<uint32_t*>(a.Cq_sf + (int64_t)(m0 + R) * (a.I >> 5) + nt * 4) =
+            *reinterpret_cast<const uint32_t*>(lds + SC_OFF + R * 4);
+    }
   } else {
+    // bf16 tile [256 rows][512 B]
 #pragma unroll
     for (int j = 0; j < JN; ++j) {
-      const int p = m0 + (2 * j + wm) * 32 + rsel;
-      if (p >= mend) continue;
-      uint16_t* crow = a.C + (int64_t)p * a.ldc;
+      const int R = (2 * j + wm) * 32 + rsel;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int col = nt * MTB + wn * 128 + i * 32 + q * 8 + hi4;
-          if (col >= a.N) continue;
-          *reinterpret_cast<uint2*>(crow + col) =
+          const int c = wn * 128 + i * 32 + q * 8 + hi4;
+          const int off = R * 512 + ((((c >> 3) ^ (R & 31)) << 4) | (hi4 << 1));
+          *reinterpret_cast<uint2*>(lds + off) =
               make_uint2(pack_bf16x2(acc[i][j][q * 4 + 0] * alpha, acc[i][j][q * 4 + 1] * alpha),
                          pack_bf16x2(acc[i][j][q * 4 + 2] * alpha, acc[i][j][q * 4 + 3] * alpha));
+          // one block at a time: batching all blocks' values costs registers
+          if (q == 3) __builtin_amdgcn_sched_barrier(0);
         }
+    }
+    __syncthreads();
+    const int k = lane & 31;   // 16-byte chunk of a 512-byte tile row; 2 rows per read
+    const int col = nt * MTB + k * 8;
+    if (col < a.N) {
+#pragma unroll 4
+      for (int r0 = wid * 2; r0 < rows; r0 += 8) {
+        const int R = r0 + (lane >> 5);
+        if (R >= rows) continue;
+        const uint4 v = *reinterpret_cast<const uint4*>(lds + R * 512 + ((k ^ (R & 31)) << 4));
+        *reinterpret_cast<uint4*>(a.C + (int64_t)(m0 + R) * a.ldc + col) = v;
+      }
     }
   }
 }
