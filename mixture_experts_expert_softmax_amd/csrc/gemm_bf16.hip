@@ -935,6 +935,57 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_nt(NtArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Epilogue staging of the backward products (LDS_U4 = 128 KB, free once every wave
+// is past its main loop; callers barrier before and after). A lane holds 4 columns
+// of one row per (i, q), so stores straight from registers would put 32 rows x 8 or
+// 16 bytes in each instruction (32 partial cache lines); staged, the tile leaves in
+// whole rows. Row R of the staged tile is 512 bytes whose 16-byte chunk c sits at
+// chunk c ^ (R % 32), so the 32 rows of a write and the chunks of a read fall on
+// distinct banks.
+// The whole 256 x 256 tile as bf16 (chunk = 8 columns).
+__device__ __forceinline__ void stage_tile_bf16(const f32x16 (&acc)[4][4], char* lds, int wn, int wm,
+                                                int lane) {
+  const int hi4 = (lane >> 5) * 4;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int R = wm * 128 + j * 32 + (lane & 31);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int c = wn * 128 + i * 32 + q * 8 + hi4;
+        *reinterpret_cast<uint2*>(lds + R * 512 + ((((c >> 3) ^ (R & 31)) << 4) | (hi4 << 1))) =
+            make_uint2(pack_bf16x2(acc[i][j][q * 4 + 0], acc[i][j][q * 4 + 1]),
+                       pack_bf16x2(acc[i][j][q * 4 + 2], acc[i][j][q * 4 + 3]));
+      }
+  }
+}
+// Tile columns [128 h, 128 h + 128) as fp32 (chunk = 4 columns); the two waves that
+// hold them (wn == h) write.
+__device__ __forceinline__ void stage_half_f32(const f32x16 (&acc)[4][4], char* lds, int h, int wn,
+                                               int wm, int lane) {
+  if (wn != h) return;
+  const int hi4 = (lane >> 5) * 4;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int R = wm * 128 + j * 32 + (lane & 31);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int c = i * 32 + q * 8 + hi4;
+        *reinterpret_cast<float4*>(lds + R * 512 + (((c >> 2) ^ (R & 31)) << 4)) =
+            make_float4(acc[i][j][q * 4 + 0], acc[i][j][q * 4 + 1], acc[i][j][q * 4 + 2],
+                        acc[i][j][q * 4 + 3]);
+      }
+  }
+}
+// 16-byte chunk k (lane % 32) of staged row R (two rows per read: R = r0 + lane / 32)
+__device__ __forceinline__ uint4 staged_chunk(const char* lds, int R, int k) {
+  return *reinterpret_cast<const uint4*>(lds + R * 512 + ((k ^ (R & 31)) << 4));
+}
+
+// ---------------------------------------------------------------------------
 // dgrad: dX[m, k] = sum_n G[m, n] W[e, n, k]. Weight side = k (read transposed
 // from W rows n), activation side = G rows m, contraction n.
 // ---------------------------------------------------------------------------
@@ -985,57 +1036,52 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_dgrad(DgradArgs a) {
   if (S > 1 && !split_reduce(acc, a.split_ws, a.split_cnt, slot, part, S, cidx, smem, tid,
                              block_mask(m0 + wm * 128, mend, 4, c0 + wn * 128, a.K)))
     return;
-  const int hi4 = (lane >> 5) * 4;
+  char* lds = reinterpret_cast<char*>(smem);
+  const int rows = mend - m0 < TB ? mend - m0 : TB;
+  const int k = lane & 31;
   if constexpr (ACT == 0) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int p = m0 + wm * 128 + j * 32 + (lane & 31);
-      if (p >= mend) continue;
-      uint16_t* crow = a.DX + (int64_t)p * a.K;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int col = c0 + wn * 128 + i * 32 + q * 8 + hi4;
-          if (col >= a.K) continue;
-          *reinterpret_cast<uint2*>(crow + col) =
-              make_uint2(pack_bf16x2(acc[i][j][q * 4 + 0], acc[i][j][q * 4 + 1]),
-                         pack_bf16x2(acc[i][j][q * 4 + 2], acc[i][j][q * 4 + 3]));
-        }
+    __syncthreads();   // no wave still reads a stage or has a copy in flight
+    stage_tile_bf16(acc, lds, wn, wm, lane);
+    __syncthreads();
+    const int col = c0 + k * 8;
+    if (col < a.K) {
+#pragma unroll 4
+      for (int r0 = wid * 2; r0 < rows; r0 += 8) {
+        const int R = r0 + (lane >> 5);
+        if (R >= rows) continue;
+        *reinterpret_cast<uint4*>(a.DX + (int64_t)(m0 + R) * a.K + col) = staged_chunk(lds, R, k);
+      }
     }
   } else {
-    // activation backward: per 32-row block, all 32 float4 of the rows' h (u and g) are
-    // loaded before any is used (rows past the group and columns past K read a valid
-    // address and store nothing), so a block costs one memory latency, not several
+    // activation backward, one column half of the tile at a time: a lane takes 4
+    // consecutive da of a row from LDS, loads the matching fp32 u and g (16 bytes each,
+    // whole lines across the row's lanes) and writes du and dg
     float lim = 0.f;
     if (ACT == 2) lim = a.limits ? a.limits[e] : a.def_limit;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int p = m0 + wm * 128 + j * 32 + (lane & 31);
-      const bool prow = p < mend;
-      const float* hrow = a.h + (int64_t)(prow ? p : mend - 1) * 2 * a.K;
-      float4 hu[4][4], hg[4][4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          int col = c0 + wn * 128 + i * 32 + q * 8 + hi4;
-          col = col < a.K ? col : a.K - 4;
-          hu[i][q] = *reinterpret_cast<const float4*>(hrow + col);
-          hg[i][q] = *reinterpret_cast<const float4*>(hrow + a.K + col);
-        }
-      uint16_t* crow = a.DX + (int64_t)p * 2 * a.K;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int col = c0 + wn * 128 + i * 32 + q * 8 + hi4;
-          const float us[4] = {hu[i][q].x, hu[i][q].y, hu[i][q].z, hu[i][q].w};
-          const float gs[4] = {hg[i][q].x, hg[i][q].y, hg[i][q].z, hg[i][q].w};
+    for (int h = 0; h < 2; ++h) {
+      __syncthreads();   // the main loop's (or the previous half's) LDS reads are done
+      stage_half_f32(acc, lds, h, wn, wm, lane);
+      __syncthreads();
+      const int col = c0 + h * 128 + k * 4;
+      if (col < a.K) {
+#pragma unroll 4
+        for (int r0 = wid * 2; r0 < rows; r0 += 8) {
+          const int R = r0 + (lane >> 5);
+          if (R >= rows) continue;
+          const int p = m0 + R;
+          const uint4 dv = staged_chunk(lds, R, k);
+          const float* hrow = a.h + (int64_t)p * 2 * a.K;
+          const float4 u4 = *reinterpret_cast<const float4*>(hrow + col);
+          const float4 g4 = *reinterpret_cast<const float4*>(hrow + a.K + col);
+          const float das[4] = {__uint_as_float(dv.x), __uint_as_float(dv.y), __uint_as_float(dv.z),
+                                __uint_as_float(dv.w)};
+          const float us[4] = {u4.x, u4.y, u4.z, u4.w};
+          const float gs[4] = {g4.x, g4.y, g4.z, g4.w};
           float du[4], dg[4];
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const float da = acc[i][j][q * 4 + r];
+            const float da = das[r];
             float u = us[r], g = gs[r];
             float mu = 1.f, mg = 1.f;
             if (ACT == 2) {   // the clamp passes the gradient where -L <= v <= L
@@ -1048,13 +1094,13 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_dgrad(DgradArgs a) {
             du[r] = da * (g * sg) * mu;
             dg[r] = da * u * (sg * (1.0f + g * (1.0f - sg))) * mg;
           }
-          if (prow && col < a.K) {
-            *reinterpret_cast<uint2*>(crow + col) =
-                make_uint2(pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3]));
-            *reinterpret_cast<uint2*>(crow + a.K + col) =
-                make_uint2(pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3]));
-          }
+          uint16_t* crow = a.DX + (int64_t)p * 2 * a.K;
+          *reinterpret_cast<uint2*>(crow + col) =
+              make_uint2(pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3]));
+          *reinterpret_cast<uint2*>(crow + a.K + col) =
+              make_uint2(pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3]));
         }
+      }
     }
   }
 }
@@ -1134,29 +1180,41 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_wgrad(WgradArgs a) {
   zero_acc(acc);
   const int nsub = (rows + 31) / 32;
   if (nsub > 0) mainloop_dma_g<true, true, 4>(sx, sgd, smem, 0, nsub, tid, lane, wn, wm, acc);
-  const int hi4 = (lane >> 5) * 4;
+  // staged through LDS (an empty group stages its zero tile like any other)
+  char* lds = reinterpret_cast<char*>(smem);
+  const int nrows = a.N - n0 < TB ? a.N - n0 : TB;
+  const int k = lane & 31;
+  if (OUT_F32) {
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int n = n0 + wm * 128 + j * 32 + (lane & 31);
-    if (n >= a.N) continue;
-    const int64_t rowoff = ((int64_t)e * a.N + n) * a.K;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int col = c0 + wn * 128 + i * 32 + q * 8 + hi4;
-        if (col >= a.K) continue;
-        if (OUT_F32) {
-          float* d = reinterpret_cast<float*>(a.DW) + rowoff + col;
-          *reinterpret_cast<float4*>(d) =
-              make_float4(acc[i][j][q * 4 + 0], acc[i][j][q * 4 + 1], acc[i][j][q * 4 + 2], acc[i][j][q * 4 + 3]);
-        } else {
-          uint16_t* d = reinterpret_cast<uint16_t*>(a.DW) + rowoff + col;
-          *reinterpret_cast<uint2*>(d) =
-              make_uint2(pack_bf16x2(acc[i][j][q * 4 + 0], acc[i][j][q * 4 + 1]),
-                         pack_bf16x2(acc[i][j][q * 4 + 2], acc[i][j][q * 4 + 3]));
+    for (int h = 0; h < 2; ++h) {
+      __syncthreads();
+      stage_half_f32(acc, lds, h, wn, wm, lane);
+      __syncthreads();
+      const int col = c0 + h * 128 + k * 4;
+      if (col < a.K) {
+#pragma unroll 4
+        for (int r0 = wid * 2; r0 < nrows; r0 += 8) {
+          const int R = r0 + (lane >> 5);
+          if (R >= nrows) continue;
+          float* d = reinterpret_cast<float*>(a.DW) + ((int64_t)e * a.N + n0 + R) * a.K + col;
+          *reinterpret_cast<uint4*>(d) = staged_chunk(lds, R, k);
         }
       }
+    }
+  } else {
+    __syncthreads();
+    stage_tile_bf16(acc, lds, wn, wm, lane);
+    __syncthreads();
+    const int col = c0 + k * 8;
+    if (col < a.K) {
+#pragma unroll 4
+      for (int r0 = wid * 2; r0 < nrows; r0 += 8) {
+        const int R = r0 + (lane >> 5);
+        if (R >= nrows) continue;
+        uint16_t* d = reinterpret_cast<uint16_t*>(a.DW) + ((int64_t)e * a.N + n0 + R) * a.K + col;
+        *reinterpret_cast<uint4*>(d) = staged_chunk(lds, R, k);
+      }
+    }
   }
 }
 
