@@ -19,7 +19,8 @@ moe_status gemm_nt_enqueue(int epi, const void* A, const int32_t* a_gather, int 
                            int K, void* C, int64_t ldc, int I, const float* limits,
                            float def_limit, const float* route_w, const int32_t* p2e, int top_k,
                            hipStream_t st, void* split_ws = nullptr,
-                           int32_t* split_cnt = nullptr, void* h_out = nullptr, int tm = 256);
+                           int32_t* split_cnt = nullptr, void* h_out = nullptr, int tm = 256,
+                           int rows_hint = 0);
 moe_status gemm_dgrad_enqueue(const void* G, const void* W, const int32_t* ends, int E, int64_t M,
                               int N, int K, void* DX, hipStream_t st, int act = 0,
                               const void* h = nullptr, const float* limits = nullptr,
@@ -194,7 +195,7 @@ extern "C" moe_status grouped_gemm_fwd(const void* x, const void* w, const int32
   if (s != MOE_OK) return s;
   return gemm_nt_enqueue(EPI_STORE, x, nullptr, 1, w, N, E, ends_of(offs, kind), M, N, K, y, N, 0,
                          nullptr, 0.f, nullptr, nullptr, 1, as_stream(stream), split_ws,
-                         split_cnt);
+                         split_cnt, nullptr, 256, (int)(M / E));
 }
 
 extern "C" moe_status grouped_gemm_dgrad(const void* g, const void* w, const int32_t* offs,
@@ -268,6 +269,12 @@ static int bf16_tile_rows(const moe_ffn_desc* d, int stage, int K, int NB, int L
   return force == 1 ? 128 : 256;
 }
 
+// Rows a local expert holds on average, as far as the host can tell without reading
+// the routing: the routes spread over all experts (a shard's share is its experts').
+static int expected_rows(const moe_ffn_desc* d) {
+  return (int)(d->T * d->top_k / (d->num_experts > 0 ? d->num_experts : 1));
+}
+
 // FC1 over gathered token rows; the activation runs in the GEMM epilogue.
 static moe_status fc1_enqueue(const moe_ffn_desc* d, const void* x, const void* w1,
                               const float* limits, const int32_t* offs, const int32_t* p2e,
@@ -279,7 +286,8 @@ static moe_status fc1_enqueue(const moe_ffn_desc* d, const void* x, const void* 
   const int epi = d->activation == MOE_ACT_SWIGLU_STEP ? EPI_SWIGLU_STEP : EPI_SWIGLU;
   return gemm_nt_enqueue(epi, x, p2e, d->top_k, w1, 2 * d->I, L, offs, R, d->I, d->H, act, d->I,
                          d->I, limits, 7.0f, nullptr, nullptr, d->top_k, st, split_ws, split_cnt,
-                         h_out, bf16_tile_rows(d, 1, d->H, 2 * d->I, L, R, force));
+                         h_out, bf16_tile_rows(d, 1, d->H, 2 * d->I, L, R, force),
+                         expected_rows(d));
 }
 
 // FC2: unscaled rows in permuted order, or the fused scaled scatter-add into out.
@@ -295,11 +303,11 @@ static moe_status fc2_enqueue(const moe_ffn_desc* d, const void* act, const void
     if (s != MOE_OK) return s;
     return gemm_nt_enqueue(EPI_FUSED, act, nullptr, 1, w2, d->H, L, offs, R, d->H, d->I, dst, d->H,
                            0, nullptr, 0.f, topk_weights, p2e, d->top_k, st, split_ws, split_cnt,
-                           nullptr, tm);
+                           nullptr, tm, expected_rows(d));
   }
   return gemm_nt_enqueue(EPI_STORE, act, nullptr, 1, w2, d->H, L, offs, R, d->H, d->I, dst, d->H, 0,
                          nullptr, 0.f, nullptr, nullptr, d->top_k, st, split_ws, split_cnt, nullptr,
-                         tm);
+                         tm, expected_rows(d));
 }
 
 extern "C" size_t moe_ffn_workspace_size(const moe_ffn_desc* d) {

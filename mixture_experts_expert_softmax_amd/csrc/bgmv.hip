@@ -42,7 +42,7 @@ moe_status gemm_nt_enqueue(int epi, const void* A, const int32_t* a_gather, int 
                            int K, void* C, int64_t ldc, int I, const float* limits,
                            float def_limit, const float* route_w, const int32_t* p2e, int top_k,
                            hipStream_t st, void* split_ws, int32_t* split_cnt, void* h_out,
-                           int tm);
+                           int tm, int rows_hint = 0);
 
 namespace {
 

@@ -53,6 +53,15 @@ constexpr int TILE_U4 = TB * TK * 2 / 16;  // uint4 slots per operand tile (2048
 enum Epi { EPI_STORE = 0, EPI_SWIGLU = 1, EPI_SWIGLU_STEP = 2, EPI_FUSED = 3, EPI_ROWMAP = 4,
            EPI_ROWMAP_F32W = 5 };
 constexpr int SPLIT_MAX = 8;   // parts a split tile is cut into at most
+// The forward GEMMs take the work-queue kernel (k_gemm_nt_q) for at least QUEUE_GROUPS
+// groups of at most QUEUE_ROWS expected rows each: there about half the groups end in a
+// short tile and the tiles take many rounds. Measured (ms, queue / one tile per
+// workgroup with the split last round): expert shard (32 of 256 experts, ~256 rows
+// each) FC1 0.741 / 0.755, FC2 0.342 / 0.366; Mixtral T = 2048 (8 experts, ~512 rows)
+// FC2 0.617 / 0.513 -- its last round is better cut along K; grouped fwd (16 groups,
+// ~512 rows) 0.195 / 0.185.
+constexpr int QUEUE_ROWS = 384;
+constexpr int QUEUE_GROUPS = 16;
 
 struct NtArgs {
   const uint16_t* A;         // activation rows, row stride K
@@ -686,22 +695,16 @@ __device__ __forceinline__ void mainloop_fwd64(const uint16_t* wbase, const uint
 // ---------------------------------------------------------------------------
 // TM: activation rows per tile, 256 or (full-K path only) 128 -- the family for few
 // rows per expert, where each row-wave takes 64 rows (two 32-row blocks).
-template <int EPI, bool KFULL, int TM = TB>
-__global__ __launch_bounds__(NTHREADS, 1) void k_gemm_nt(NtArgs a) {
-  static_assert(TM == TB || (TM == 128 && KFULL), "128-row tiles need whole 64-deep stages");
-  // 128 KB: two 64-deep stages [A tile | B tile], or the full-K path's four 32-deep ones
-  __shared__ uint4 smem[LDS_FWD_U4];
+// One tile of the forward kernels: rows [m0, mend) of group e, column tile nt,
+// contraction stages [k0, k0 + nk) (a part of a split tile when S > 1), computed by
+// the whole workgroup (t: the thread index) and stored by the epilogue.
+template <int EPI, bool KFULL, int TM>
+__device__ __forceinline__ void nt_tile(const NtArgs& a, uint4* smem, int e, int m0, int mend,
+                                        int nt, int k0, int nk, int part, int S, int slot,
+                                        int cidx, int t) {
   const int ktiles = (a.K + TK - 1) / TK;
-  int e, m0, mend, nt, k0 = 0, nk = ktiles, part = 0, S = 1, slot = 0, cidx = 0;
-  if (KFULL) {
-    if (!deal_tile_split<TM>(a.ends, a.E, a.m_cap, a.n_tiles, a.n_res, ktiles, e, m0, mend, nt,
-                             k0, nk, part, S, slot, cidx, a.mmajor))
-      return;
-  } else {
-    if (!deal_tile<TB>(a.ends, a.E, a.m_cap, a.n_tiles, e, m0, mend, nt)) return;
-  }
-
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  (void)ktiles;
+  const int tid = t, lane = tid & 63, wid = tid >> 6;
   const int wn = wid & 1, wm = wid >> 1;
   const int lrow = tid >> 3;
 
@@ -932,6 +935,85 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_nt(NtArgs a) {
       }
     }
   }
+}
+
+// Work-queue form of the whole-stage forward kernel, for groups of few rows, whose
+// short last tiles (at most 64 rows: a quarter of the MFMAs) finish well before the
+// others. Workgroups reach the XCDs in a fixed order, so with one workgroup per tile a
+// CU freed early waits until every XCD has a free CU; here one workgroup per CU takes
+// tiles until none are left. The tiles are dealt as in deal_tile -- XCD x owns the
+// contiguous range [x per, (x + 1) per) of the group-major order, so the row blocks
+// that share a weight tile run on one XCD -- and handed out in range order by a
+// counter per XCD; a workgroup whose range is used up takes tiles from the other
+// ranges (x + 1, x + 2, ...). Every tile runs its whole contraction: the results are
+// those of the one-tile-per-workgroup kernel without a split, bit for bit, whichever
+// workgroup computes a tile. The counters (q[0..7] per range, q[8] finished
+// workgroups) are zero at launch -- callers clear them as they clear the split-tile
+// counters -- and the last workgroup to finish sets them back to zero.
+template <int EPI, int TM>
+__global__ __launch_bounds__(NTHREADS, 1) void k_gemm_nt_q(NtArgs a) {
+  __shared__ uint4 smem[LDS_FWD_U4];
+  const int ktiles = (a.K + TK - 1) / TK;
+  const bool one_pass = a.E <= 64;
+  TileScan64 sc{};
+  if (one_pass) sc = tile_scan64<TM>(a.ends, a.E, a.m_cap, a.n_tiles);
+  const int total = one_pass ? sc.total : tile_count<TM>(a.ends, a.E, a.m_cap, a.n_tiles);
+  const int per = (total + 7) >> 3;
+  const int x = (int)(blockIdx.x & 7);
+  int* q = a.split_cnt;
+  int* flag = reinterpret_cast<int*>(smem);
+  for (;;) {
+    // thread index through an opaque move per tile: address arithmetic derived from it
+    // is redone per tile instead of being held across the loop
+    int t = (int)threadIdx.x;
+    asm volatile("" : "+v"(t));
+    __syncthreads();   // the previous tile's epilogue has read LDS
+    if (t == 0) {
+      int tile = -1;
+      for (int d = 0; d < 8 && tile < 0; ++d) {
+        const int xx = (x + d) & 7;
+        const int cnt = total - xx * per < per ? total - xx * per : per;
+        if (cnt <= 0) continue;
+        const int i = __hip_atomic_fetch_add(q + xx, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (i < cnt) tile = xx * per + i;
+      }
+      flag[0] = tile;
+    }
+    __syncthreads();
+    const int tile = flag[0];
+    __syncthreads();   // read by every wave before the tile's copies rewrite LDS
+    if (tile < 0) break;
+    int e, m0, mend, nt;
+    if (one_pass)
+      tile_locate64<TM>(sc, a.n_tiles, a.n_tiles, tile, e, m0, mend, nt);
+    else
+      tile_locate<TM>(a.ends, a.E, a.m_cap, a.n_tiles, tile, e, m0, mend, nt);
+    nt_tile<EPI, true, TM>(a, smem, e, m0, mend, nt, 0, ktiles, 0, 1, 0, 0, t);
+  }
+  if (threadIdx.x == 0) {
+    const int done = __hip_atomic_fetch_add(q + 8, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    if (done == (int)gridDim.x - 1) {   // every other workgroup has taken its last tile
+#pragma unroll
+      for (int i = 0; i < 9; ++i) __hip_atomic_store(q + i, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
+template <int EPI, bool KFULL, int TM = TB>
+__global__ __launch_bounds__(NTHREADS, 1) void k_gemm_nt(NtArgs a) {
+  static_assert(TM == TB || (TM == 128 && KFULL), "128-row tiles need whole 64-deep stages");
+  // 160 KB: the five 32 KB slots of mainloop_fwd64, or the partial-K path's two stages
+  __shared__ uint4 smem[LDS_FWD_U4];
+  const int ktiles = (a.K + TK - 1) / TK;
+  int e, m0, mend, nt, k0 = 0, nk = ktiles, part = 0, S = 1, slot = 0, cidx = 0;
+  if (KFULL) {
+    if (!deal_tile_split<TM>(a.ends, a.E, a.m_cap, a.n_tiles, a.n_res, ktiles, e, m0, mend, nt,
+                             k0, nk, part, S, slot, cidx, a.mmajor))
+      return;
+  } else {
+    if (!deal_tile<TB>(a.ends, a.E, a.m_cap, a.n_tiles, e, m0, mend, nt)) return;
+  }
+  nt_tile<EPI, KFULL, TM>(a, smem, e, m0, mend, nt, k0, nk, part, S, slot, cidx, (int)threadIdx.x);
 }
 
 // ---------------------------------------------------------------------------
@@ -1250,7 +1332,7 @@ moe_status gemm_nt_enqueue(int epi, const void* A, const int32_t* a_gather, int 
                            int K, void* C, int64_t ldc, int I, const float* limits,
                            float def_limit, const float* route_w, const int32_t* p2e, int top_k,
                            hipStream_t st, void* split_ws, int32_t* split_cnt, void* h_out,
-                           int tm) {
+                           int tm, int rows_hint) {
   if (M == 0) return MOE_OK;
   NtArgs a;
   a.A = reinterpret_cast<const uint16_t*>(A);
@@ -1296,20 +1378,34 @@ moe_status gemm_nt_enqueue(int epi, const void* A, const int32_t* a_gather, int 
   }
   const int64_t tiles = (int64_t)a.m_tiles * a.n_tiles;
   // parts of split tiles take at most n_res + 8 * SPLIT_MAX workgroups past the whole ones
-  const int grid = round_up8(tiles + (a.n_res > 0 ? a.n_res + 8 * SPLIT_MAX : 0));
+  int grid = round_up8(tiles + (a.n_res > 0 ? a.n_res + 8 * SPLIT_MAX : 0));
+  // few rows per group (the caller's estimate): the work-queue kernel, one workgroup
+  // per CU, whole contractions (no split), counters in the split-tile counter area
+  const bool queue = kfull && tm == TB && split_cnt && rows_hint > 0 && rows_hint <= QUEUE_ROWS &&
+                     E >= QUEUE_GROUPS &&
+                     (epi == EPI_STORE || epi == EPI_SWIGLU || epi == EPI_SWIGLU_STEP ||
+                      epi == EPI_FUSED);
+  if (queue) {
+    a.n_res = 0;
+    const int pers = std::max(8, device_cu_count() & ~7);
+    grid = grid < pers ? grid : pers;
+  }
 #define MOE_LAUNCH_NT(E_)                                                  \
   (tm == 128 ? k_gemm_nt<E_, true, 128><<<grid, NTHREADS, 0, st>>>(a)      \
    : kfull   ? k_gemm_nt<E_, true><<<grid, NTHREADS, 0, st>>>(a)           \
              : k_gemm_nt<E_, false><<<grid, NTHREADS, 0, st>>>(a))
+#define MOE_LAUNCH_NTQ(E_)                                                                     \
+  (queue ? k_gemm_nt_q<E_, TB><<<grid, NTHREADS, 0, st>>>(a) : MOE_LAUNCH_NT(E_))
   switch (epi) {
-    case EPI_STORE: MOE_LAUNCH_NT(EPI_STORE); break;
-    case EPI_SWIGLU: MOE_LAUNCH_NT(EPI_SWIGLU); break;
-    case EPI_SWIGLU_STEP: MOE_LAUNCH_NT(EPI_SWIGLU_STEP); break;
-    case EPI_FUSED: MOE_LAUNCH_NT(EPI_FUSED); break;
+    case EPI_STORE: MOE_LAUNCH_NTQ(EPI_STORE); break;
+    case EPI_SWIGLU: MOE_LAUNCH_NTQ(EPI_SWIGLU); break;
+    case EPI_SWIGLU_STEP: MOE_LAUNCH_NTQ(EPI_SWIGLU_STEP); break;
+    case EPI_FUSED: MOE_LAUNCH_NTQ(EPI_FUSED); break;
     case EPI_ROWMAP: MOE_LAUNCH_NT(EPI_ROWMAP); break;
     case EPI_ROWMAP_F32W: MOE_LAUNCH_NT(EPI_ROWMAP_F32W); break;
     default: return MOE_ERR_DTYPE;
   }
+#undef MOE_LAUNCH_NTQ
 #undef MOE_LAUNCH_NT
   return launch_status();
 }

@@ -232,3 +232,41 @@ def test_finalize_parity_one_hot_and_replay():
     o1 = M.moe_finalize(y.to(DEV), e2p, torch.from_numpy(onehot).to(DEV))
     r1 = O.finalize(S.bf16_to_f32(y), srt["e2p"], onehot)
     np.testing.assert_array_equal(to_np(o1), r1)   # exact: one bf16 row, weight 1
+
+
+def test_work_queue_matches_one_tile_per_workgroup():
+    """Many experts of few rows (32 local of 128 experts, top-8: ~256 rows each) take the
+    work-queue form of the forward GEMM: one workgroup per CU takes tiles from per-XCD
+    ranges. Every tile still runs its whole contraction, so FC1's and FC2's rows (plain
+    and fused) equal those of the one-tile-per-workgroup kernel (the stage entries
+    without a workspace) bit for bit, on repeated calls too (the last workgroup resets
+    the queue counters), and the layer matches the oracle."""
+    c = S.moe_case("queue", 4096, 1024, 1024, 128, 8, num_local=32, local_offset=16,
+                   activation="swiglu_step", limit_range=(5.0, 9.0), seed=5)
+    x, w1, w2 = c.x.to(DEV), c.w1.to(DEV), c.w2.to(DEV)
+    lim = torch.from_numpy(c.limits).to(DEV)
+    ids, w = M.moe_route(torch.from_numpy(c.logits).to(DEV), c.top_k)
+    srt = M.moe_sort(ids, c.num_experts, c.num_local, c.local_offset)
+    n = int(srt["n_local"].item())
+    counts = np.diff(np.concatenate([[0], srt["offs"].cpu().numpy()]))
+    assert n > 7000 and np.any(counts % 256 <= 64)   # short last tiles are present
+    fc1 = lambda **kw: M.moe_fc1(x, w1, srt["offs"], srt["p2e"], c.top_k, c.num_experts,
+                                 c.local_offset, "swiglu_step", lim, **kw)
+    a0 = fc1(split=False)
+    ws = torch.empty(M.lib().moe_gemm_split_workspace_size(), dtype=torch.uint8, device=DEV)
+    a1, a2 = fc1(workspace=ws), fc1(workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(a0[:n], a1[:n]) and torch.equal(a1[:n], a2[:n])
+    fc2 = lambda **kw: M.moe_fc2(a0, w2, srt["offs"], c.T, c.top_k, c.num_experts,
+                                 c.local_offset, **kw)
+    y0, y1 = fc2(split=False), fc2(workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(y0[:n], y1[:n])
+    fu = lambda **kw: M.moe_fc2(a0, w2, srt["offs"], c.T, c.top_k, c.num_experts,
+                                c.local_offset, finalize="fused", p2e=srt["p2e"],
+                                topk_weights=w, **kw)
+    f0, f1 = fu(split=False), fu(workspace=ws)
+    torch.cuda.synchronize()
+    assert_close_bf16(to_np(f1), to_np(f0), what="fused, queue vs one tile per workgroup")
+    out, _, _ = _run(c, ids=ids, w=w)
+    assert_close_bf16(out, _oracle(c, ids, w), what="queue layer vs oracle")
