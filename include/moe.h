@@ -158,7 +158,9 @@ moe_status moe_sort(const int32_t* topk_ids, int64_t T, int32_t top_k, int32_t n
  * order: the same result on every run, whose rounding differs from the uncut order
  * within fp32 and depends on the tile count. Without it every tile is whole, and each
  * output element's summation order depends only on K (the same bits for a group
- * computed alone or among others).
+ * computed alone or among others). With it and at least 16 groups of at most 384 rows
+ * on average, fwd instead runs one workgroup per CU taking whole tiles from a queue
+ * (counters in the same workspace): the bits of the call without a workspace.
  */
 moe_status grouped_gemm_fwd(const void* x, const void* w, const int32_t* offs, int32_t offs_kind,
                             int32_t E, int64_t sum_m, int32_t N, int32_t K, void* y, void* ws,
@@ -256,8 +258,11 @@ moe_status moe_ffn_forward_noalloc(const moe_ffn_desc* desc, const moe_ffn_tenso
  * not shared by calls that may overlap. With it, the tiles of a last, mostly idle
  * round of workgroups are cut along the contraction and their fp32 partials summed
  * in a fixed order (same result on every run; rounding differs from the unsplit
- * order within fp32). Without it no tile is cut. moe_ffn_forward does this with
- * its own workspace. MOE_ERR_WORKSPACE if ws is given but too small or unaligned.
+ * order within fp32). Without it no tile is cut. Where the local experts are at least
+ * 16 and expect at most 384 rows each (T*top_k / num_experts), the workspace instead
+ * serves a work queue: one workgroup per CU takes whole tiles (the bits of the call
+ * without a workspace). moe_ffn_forward does this with its own workspace.
+ * MOE_ERR_WORKSPACE if ws is given but too small or unaligned.
  */
 size_t moe_gemm_split_workspace_size(void);
 moe_status moe_fc1(const moe_ffn_desc* desc, const void* x, const void* w1,
