@@ -39,10 +39,11 @@ moe_status mx_fc1_enqueue(int activation, int wf, const void* x, const void* x_s
                           const int32_t* p2e, int top_k, const void* w1, const void* w1_sf, int L,
                           const int32_t* offs, int64_t R, int H, int I, const float* limits,
                           void* act, void* act_sf, const float* act_scale, hipStream_t st,
-                          int force = -1);
+                          int force = -1, int32_t* qcnt = nullptr, int rows_hint = 0);
 moe_status mx_fc2_enqueue(int wf, const void* act, const void* act_sf, const void* w2,
                           const void* w2_sf, int L, const int32_t* offs, int64_t R, int H, int I,
-                          void* y, hipStream_t st, int force = -1);
+                          void* y, hipStream_t st, int force = -1, int32_t* qcnt = nullptr,
+                          int rows_hint = 0);
 bool mx_small_possible(int stage, int wf, int H, int I, int64_t R);
 // defined in tune.hip
 void tune_store(int stage, int wf, int K, int NB, int L, int64_t R, int choice);
@@ -117,8 +118,9 @@ FfnLayout ffn_layout(const moe_ffn_desc* d, bool train = false) {
   // bf16 FC1 / FC2 may cut their last round's tiles along K (fp32 partial tiles)
   l.split = o;
   if (!mx) o += (size_t)SPLIT_SLOTS * SPLIT_TILE_BYTES;
+  // bf16: the split tiles' arrival counters; every format: the work-queue counters
   l.split_cnt = o;
-  if (!mx) o += align_up((size_t)SPLIT_SLOTS * 4, 256);
+  o += align_up((size_t)SPLIT_SLOTS * 4, 256);
   l.h = o;
   if (train) o += align_up((size_t)R * 2 * d->I * 4, 256);
   l.total = o;
@@ -350,11 +352,11 @@ static moe_status ffn_forward(const moe_ffn_desc* d, const moe_ffn_tensors* t, v
   void* y = fm == MOE_FINALIZE_NONE ? t->y : w + l.y;
   const int H = d->H;
 
-  int32_t* split_cnt = mx ? nullptr : reinterpret_cast<int32_t*>(w + l.split_cnt);
+  int32_t* split_cnt = reinterpret_cast<int32_t*>(w + l.split_cnt);
   void* split_ws = mx ? nullptr : w + l.split;
-  // the sort also clears the split-tile arrival counters
+  // the sort also clears the split-tile arrival / work-queue counters
   s = sort_enqueue(t->topk_ids, d->T, d->top_k, d->num_experts, L, d->local_expert_offset, offs,
-                   nullptr, e2p, p2e, nloc, w + l.sort_ws, st, split_cnt, mx ? 0 : SPLIT_SLOTS);
+                   nullptr, e2p, p2e, nloc, w + l.sort_ws, st, split_cnt, SPLIT_SLOTS);
   if (s != MOE_OK) return s;
   if (mx) {
     const int64_t R = d->T * d->top_k;
@@ -363,9 +365,11 @@ static moe_status ffn_forward(const moe_ffn_desc* d, const moe_ffn_tensors* t, v
     const void* act_sf = block_scaled(d->weight_format) ? (const void*)(w + l.act_sf)
                                                         : (const void*)t->act_scale;
     s = mx_fc1_enqueue(d->activation, wf, t->x, t->x_sf, p2e, d->top_k, t->w1, t->w1_sf, L, offs,
-                       R, H, d->I, t->clamp_limit, act, w + l.act_sf, t->act_scale, st);
+                       R, H, d->I, t->clamp_limit, act, w + l.act_sf, t->act_scale, st, -1,
+                       split_cnt, expected_rows(d));
     if (s != MOE_OK) return s;
-    s = mx_fc2_enqueue(wf, act, act_sf, t->w2, t->w2_sf, L, offs, R, H, d->I, y, st);
+    s = mx_fc2_enqueue(wf, act, act_sf, t->w2, t->w2_sf, L, offs, R, H, d->I, y, st, -1,
+                       split_cnt, expected_rows(d));
   } else {
     s = fc1_enqueue(d, t->x, t->w1, t->clamp_limit, offs, p2e, act, st, split_ws, split_cnt,
                     train ? w + l.h : nullptr);
@@ -545,7 +549,8 @@ static moe_status tune_fc1(void* p) {
                        c.split_ws, c.split_cnt, nullptr, c.force);
   return mx_fc1_enqueue(c.d->activation, mx_wf(c.d->weight_format), c.t->x, c.t->x_sf, c.p2e,
                         c.d->top_k, c.t->w1, c.t->w1_sf, L, c.offs, c.d->T * c.d->top_k, c.d->H,
-                        c.d->I, c.t->clamp_limit, c.act, c.act_sf, c.t->act_scale, c.st, c.force);
+                        c.d->I, c.t->clamp_limit, c.act, c.act_sf, c.t->act_scale, c.st, c.force,
+                        c.split_cnt, expected_rows(c.d));
 }
 
 static moe_status tune_fc2(void* p) {
@@ -555,7 +560,8 @@ static moe_status tune_fc2(void* p) {
     return fc2_enqueue(c.d, c.act, c.t->w2, c.offs, nullptr, nullptr, c.y, c.st, c.split_ws,
                        c.split_cnt, c.force);
   return mx_fc2_enqueue(mx_wf(c.d->weight_format), c.act, c.act_sf_in, c.t->w2, c.t->w2_sf, L,
-                        c.offs, c.d->T * c.d->top_k, c.d->H, c.d->I, c.y, c.st, c.force);
+                        c.offs, c.d->T * c.d->top_k, c.d->H, c.d->I, c.y, c.st, c.force,
+                        c.split_cnt, expected_rows(c.d));
 }
 
 extern "C" moe_status moe_tune_set(const moe_ffn_desc* d, int32_t stage, int32_t choice) {
@@ -595,11 +601,11 @@ extern "C" moe_status moe_tune(const moe_ffn_desc* d, const moe_ffn_tensors* t, 
   char* w = reinterpret_cast<char*>(ws);
   int32_t* offs = reinterpret_cast<int32_t*>(w + l.offs);
   int32_t* p2e = reinterpret_cast<int32_t*>(w + l.p2e);
-  int32_t* split_cnt = mx ? nullptr : reinterpret_cast<int32_t*>(w + l.split_cnt);
+  int32_t* split_cnt = reinterpret_cast<int32_t*>(w + l.split_cnt);
   s = sort_enqueue(t->topk_ids, d->T, d->top_k, d->num_experts, L, d->local_expert_offset, offs,
                    nullptr, reinterpret_cast<int32_t*>(w + l.e2p), p2e,
                    reinterpret_cast<int32_t*>(w + l.n_local), w + l.sort_ws, st, split_cnt,
-                   mx ? 0 : SPLIT_SLOTS);
+                   SPLIT_SLOTS);
   if (s != MOE_OK) return s;
   TuneCtx c{&dd, t, offs, p2e, w + l.act, w + l.act_sf,
             block_scaled(d->weight_format) ? (const void*)(w + l.act_sf) : (const void*)t->act_scale,

@@ -339,9 +339,6 @@ __device__ __forceinline__ void atomic_add_bf16x2_bits(uint16_t* p, uint32_t bit
   __builtin_amdgcn_global_atomic_fadd_v2bf16(reinterpret_cast<bf16x2_t*>(p),
                                              __builtin_bit_cast(bf16x2_t, bits));
 }
-__device__ __forceinline__ void atomic_add_bf16x2(uint16_t* p, float a, float b) {
-  atomic_add_bf16x2_bits(p, pack_bf16x2(a, b));
-}
 
 // Direct-to-LDS copy of one 16-byte chunk per lane: the chunk at g lands at LDS byte
 // address lds + 16 * lane (lds goes to M0). The compiler does not see this LDS

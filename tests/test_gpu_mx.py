@@ -327,3 +327,34 @@ def test_mx_full_shape(mx_full, T):
     ref = _oracle(c, ids, w, tokens=tokens, cache1=cache1, cache2=cache2)
     got = to_np(out) if tokens is None else to_np(out)[tokens]
     assert_close_bf16(got, ref, MX_MAX_ABS, MX_REL, what=f"{full.wfmt} full T={T}")
+
+
+@pytest.mark.parametrize("wfmt", WFMTS)
+def test_mx_work_queue_matches_stage_entries(wfmt):
+    """With 256 rows per expert on average (T=1024, 16 experts, top-4) the layer runs
+    both 256-row GEMMs as the work-queue kernel; the stage entry points run the kernel
+    with one tile per workgroup. Both compute every tile the same way, so the stage
+    chain (sort, FC1, FC2, deterministic finalize) reproduces the layer bit for bit, on
+    two calls in a row (the queue counters reset themselves)."""
+    c = S.w4a8_moe(seed=11, T=1024, H=1024, I=512, E=16, top_k=4, wfmt=wfmt)
+    d = _dev(c)
+    M.moe_tune_clear()
+    out1, ids, w = _run(c, d)
+    out2, _, _ = _run(c, d, ids, w)
+    srt = M.moe_sort(ids, c.num_experts)
+    if wfmt == "fp8":
+        act = M.moe_fc1_fp8(d["x"], d["x_sf"], d["w1"], d["w1_sf"], d["act_scale"], srt["offs"],
+                            srt["p2e"], c.top_k, c.num_experts)
+        y = M.moe_fc2_fp8(act, d["act_scale"], d["w2"], d["w2_sf"], srt["offs"], c.T, c.top_k,
+                          c.num_experts)
+    else:
+        act, act_sf = M.moe_fc1_mx(d["x"], d["x_sf"], d["w1"], d["w1_sf"], srt["offs"],
+                                   srt["p2e"], c.top_k, c.num_experts)
+        y = M.moe_fc2_mx(act, act_sf, d["w2"], d["w2_sf"], srt["offs"], c.T, c.top_k,
+                         c.num_experts)
+    ref = M.moe_finalize(y, srt["e2p"], w)
+    torch.cuda.synchronize()
+    assert torch.equal(out1, ref)
+    assert torch.equal(out2, ref)
+    oracle = _oracle(c, ids, w)
+    assert_close_bf16(to_np(out1), oracle, MX_MAX_ABS, MX_REL, what=f"{wfmt} queue layer")
