@@ -640,6 +640,18 @@ def _profile_calls(name):
                               M.moe_ffn_forward_mx(dw["x"], dw["x_sf"], idsw, wtsw, dw["w1"],
                                                    dw["w1_sf"], dw["w2"], dw["w2_sf"], cw.num_experts,
                                                    out=outw, workspace=wsw)))])
+    if name.startswith("bgmv_"):
+        Tb = int(name.split("_")[1])
+        c = S.bgmv_case(seed=0, T=Tb, H=3072, rank=32, num_loras=4, E=8, top_k=2)
+        d = [c.x.to(dev), c.lora_a.to(dev), c.lora_b.to(dev)] + [
+            torch.from_numpy(v).to(dev) for v in (c.sorted_token_ids, c.expert_ids, c.lora_indices,
+                                                  c.topk_weights)]
+        yb = torch.empty((Tb, 3072), dtype=torch.float32, device=dev)
+        P = c.sorted_token_ids.shape[0]
+        wsb = torch.empty(M.moe_bgmv_workspace_bytes(Tb, P, 3072, 3072, 32, 4, 8), dtype=torch.uint8,
+                          device=dev)
+        return (f"BGMV T={Tb}, hidden 3072, rank 32, top-2, 4 LoRAs x 8 experts", [
+            ("bgmv", lambda: M.moe_bgmv(*d, c.num_experts, y_accum=yb, workspace=wsb))])
     if name == "route_sort":
         T2, E2, k2 = 262144, 256, 8
         lg2 = torch.from_numpy(S.route_logits(np.random.default_rng(1), T2, E2)).to(dev)
@@ -663,7 +675,7 @@ def _profile_calls(name):
 
 
 PROFILE_WORKLOADS = ("layer", "backward", "grouped_gemm", "expert_shard", "w4a8_1024", "w4a8_8192",
-                     "route_sort", "finalize")
+                     "route_sort", "finalize", "bgmv_2048")
 
 
 def profile_workload(name, warmup=3, reps=5):

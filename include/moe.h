@@ -432,12 +432,12 @@ typedef struct moe_bgmv_desc {
 
 /* Pipelines of moe_bgmv ([BGMV] Parameters: grouped). The per-pair pipeline reads
  * every pair's LoRA slices; the grouped one sorts the pairs stably by (LoRA, expert)
- * bin, runs the shrink and the expand as ragged grouped GEMMs over the bins (each
- * bin's weights streamed once per tile of pairs), stores w[p] times each pair's fp32
- * expand row and sums a token's rows in ascending pair order. Both are deterministic;
- * they round differently within float32 (the expand's rank sum runs in another
- * order). AUTO takes the grouped pipeline when num_pairs >= 96 * num_loras *
- * num_experts; GROUPED needs num_loras * num_experts <= 1024. */
+ * bin, runs the shrink and the expand on MFMA tiles of 32 sorted pairs of one bin
+ * (each bin's weights streamed once per tile of pairs), stores w[p] times each pair's
+ * fp32 expand row and sums a token's rows in ascending pair order. Both are
+ * deterministic; they round differently within float32 (the shrink's and the expand's
+ * sums run in other orders). AUTO takes the grouped pipeline when num_pairs >= 48 *
+ * num_loras * num_experts; GROUPED needs num_loras * num_experts <= 1024. */
 #define MOE_BGMV_AUTO     0
 #define MOE_BGMV_PER_PAIR 1
 #define MOE_BGMV_GROUPED  2

@@ -20,12 +20,15 @@
 //
 // Grouped pipeline (BGMV page, Parameters: grouped), for many routes per (LoRA,
 // expert) bin: the pairs are sorted stably by bin (moe_sort's kernels, one bin per
-// (LoRA, expert)); the shrink is then a ragged grouped GEMM over the bins (x rows
-// gathered through the sorted pairs' tokens, the bin's A as weights, K = hidden) and
-// the expand another (shrink rows, the bin's B, K = rank), both on the bf16 MFMA
-// kernels of gemm_bf16.hip, so each bin's weights are streamed once per tile of
-// routes; the expand writes w[p] times its fp32 result as pair p's partial row, and a
-// per-token combine sums a token's partials in ascending pair order.
+// (LoRA, expert)); the shrink and the expand then run on bf16 MFMAs over tiles of 32
+// sorted routes of one bin (x rows gathered through the routes' tokens against the
+// bin's A, K = hidden; shrink rows against the bin's B, K = rank), so each bin's
+// weights are streamed once per tile of routes rather than once per pair. Both keep
+// their operands in registers: the rank (8-64) is far narrower than the 256-wide
+// tiles of the layer GEMMs. The expand writes w[p] times its fp32 result as pair p's
+// partial row, and a per-token combine sums a token's partials in ascending pair
+// order.
+#include <type_traits>
 #include <algorithm>
 
 #include "common.h"
@@ -37,17 +40,10 @@ moe_status sort_enqueue(const int32_t* ids, int64_t T, int32_t k, int32_t E, int
                         int32_t off, int32_t* offs, int32_t* m_indptr, int32_t* e2p,
                         int32_t* p2e, int32_t* n_local, void* ws, hipStream_t st,
                         int32_t* zero, int n_zero);
-moe_status gemm_nt_enqueue(int epi, const void* A, const int32_t* a_gather, int a_div,
-                           const void* B, int NB, int E, const int32_t* ends, int64_t M, int N,
-                           int K, void* C, int64_t ldc, int I, const float* limits,
-                           float def_limit, const float* route_w, const int32_t* p2e, int top_k,
-                           hipStream_t st, void* split_ws, int32_t* split_cnt, void* h_out,
-                           int tm, int rows_hint = 0);
 
 namespace {
 
 constexpr int BG_SLOTS = 16;
-constexpr int EPI_ROWMAP = 4, EPI_ROWMAP_F32W = 5;   // the bf16 NT kernel's row-mapped epilogues
 constexpr int BG_SPLIT_MAX = 8;
 constexpr int BG_XSEG = 2048;   // 16-byte x chunks staged per shrink workgroup (32 KB)
 
@@ -268,38 +264,215 @@ __global__ __launch_bounds__(256) void k_bgmv_bins(BgArgs a, int32_t* __restrict
   if (slot < BG_SLOTS) a.ri[(int64_t)t * BG_SLOTS + slot] = (int32_t)p;
 }
 
-// Step 2: the token of each sorted pair (the shrink's gathered x rows).
-__global__ __launch_bounds__(256) void k_bgmv_gtok(const int32_t* __restrict__ p2e,
-                                                   const int32_t* __restrict__ n_sorted,
-                                                   const int32_t* __restrict__ tok,
-                                                   int32_t* __restrict__ gtok, int64_t P) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < P && i < *n_sorted) gtok[i] = tok[p2e[i]];
+// Grouped pipeline, step 2 (after the sort by bin), the shrink: s[p] = bf16(x[tok[p]] . A[bin]^T) for the routes of each bin in
+// sorted order, 32 routes (one MFMA column block) per workgroup, dealt XCD by XCD so a
+// bin's workgroups share its A slice in one L2. The rank is only 8-64 wide, so the
+// 256 x 256 GEMM tile would spend most of its MFMAs on masked columns; here the
+// operands go straight from global memory into registers. Lane l takes route / A row
+// l % 32 and, of every 64-value block of the contraction, the 32 values from
+// 32 (l / 32): four 16-byte loads, fed to four MFMA steps in that order (the same
+// permutation of the contraction on both operands). The 8 waves take every 8th block
+// and their sums meet in LDS, added in wave order.
+constexpr int GS_WAVES = 8;
+
+template <int NCB>
+__global__ __launch_bounds__(GS_WAVES * 64) void k_bgmv_gshrink(BgArgs a,
+                                                              const int32_t* __restrict__ offs,
+                                                              int L, const int32_t* __restrict__ p2e) {
+  // 64-value blocks a wave loads before it multiplies (all of them issued before the
+  // first MFMA: one memory round trip per batch; hidden 3072 is one batch below rank 64)
+  constexpr int GS_BATCH = 6 / NCB;
+  __shared__ float red[GS_WAVES][NCB][16][64];
+  int e, m0, mend, nt;
+  if (!deal_tile<32>(offs, L, (int)a.P, 1, e, m0, mend, nt)) return;
+  const int tid = threadIdx.x, lane = tid & 63;
+  // wave-uniform in a scalar register: the contraction loop below is then not a
+  // lane-masked loop (an MFMA must run with every lane of the wave)
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int j = lane & 31, h = lane >> 5;
+  const int i = m0 + j < mend ? m0 + j : mend - 1;   // rows past the bin repeat a valid one
+  const int tok = a.tok[p2e[i]];
+  // element offsets from the argument pointers (global loads, kept in flight together;
+  // a lane outside the operands loads chunk 0 of its row and zeroes the value)
+  const int64_t xo = (int64_t)tok * a.H8;
+  int64_t wo[NCB];
+  bool wok[NCB];
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) {
+    const int wrow = cb * 32 + j;
+    wok[cb] = wrow < a.r;
+    wo[cb] = ((int64_t)e * a.r + (wok[cb] ? wrow : 0)) * a.H8;
+  }
+  f32x16 acc[NCB];
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[cb][v] = 0.f;
+  const int nb = (a.H8 + 7) >> 3;
+  const uint4 z = make_uint4(0, 0, 0, 0);
+  for (int c0 = wid; c0 < nb; c0 += GS_WAVES * GS_BATCH) {
+    uint4 xv[GS_BATCH][4], wv[GS_BATCH][NCB][4];
+#pragma unroll
+    for (int g = 0; g < GS_BATCH; ++g)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int k8 = 8 * (c0 + GS_WAVES * g) + 4 * h + u;   // 16-byte chunk of the row
+        const bool ok = c0 + GS_WAVES * g < nb && k8 < a.H8;
+        const int kk = ok ? k8 : 0;
+        xv[g][u] = a.x[xo + kk];
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) wv[g][cb][u] = a.A[wo[cb] + kk];
+      }
+    __builtin_amdgcn_sched_barrier(0);   // keep the batch's loads ahead of its MFMAs
+#pragma unroll
+    for (int g = 0; g < GS_BATCH; ++g)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int k8 = 8 * (c0 + GS_WAVES * g) + 4 * h + u;
+        const bool ok = c0 + GS_WAVES * g < nb && k8 < a.H8;
+        const uint4 xq = ok ? xv[g][u] : z;
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb)
+          acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              __builtin_bit_cast(bf16x8, ok && wok[cb] ? wv[g][cb][u] : z),
+              __builtin_bit_cast(bf16x8, xq), acc[cb], 0, 0, 0);
+      }
+  }
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) red[wid][cb][v][lane] = acc[cb][v];
+  __syncthreads();
+  if (wid != 0 || m0 + j >= mend) return;
+  // lane holds A rows 8 q + 4 h + 0..3 (accumulator entries 4 q + 0..3) of route j
+  uint16_t* out = a.s + (int64_t)p2e[m0 + j] * a.r;
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int c = cb * 32 + 8 * q + 4 * h;
+      if (c >= a.r) continue;
+      float f[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float t = red[0][cb][4 * q + r][lane];
+#pragma unroll
+        for (int w = 1; w < GS_WAVES; ++w) t += red[w][cb][4 * q + r][lane];
+        f[r] = t;
+      }
+      *reinterpret_cast<uint2*>(out + c) = make_uint2(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]));
+    }
+}
+
+// Step 3, the expand: part[p] = w[p] * (s[p] . B[bin]^T) in fp32 for the sorted routes
+// of each bin: 32 routes x 512 output columns per workgroup, each wave 128 columns (4
+// MFMA blocks), contraction = the rank (one or more 16-value MFMA steps). The routes
+// are the MFMA's row operand and the B rows its column operand, so lane l holds output
+// column l % 32 of routes 8 q + 4 (l / 32) + 0..3 and every store instruction writes 2
+// routes x 32 adjacent floats (two whole 128-byte lines). Little LDS: several
+// workgroups share a CU.
+constexpr int GX_COLS = 512;
+
+template <int R>
+__global__ __launch_bounds__(256) void k_bgmv_gexpand(BgArgs a, const int32_t* __restrict__ offs,
+                                                      int L, const int32_t* __restrict__ p2e,
+                                                      float* __restrict__ part, int col_tiles) {
+  constexpr int NS = (R + 15) / 16;   // MFMA steps
+  constexpr int RC = R / 8;           // 16-byte chunks per rank row
+  __shared__ int rmap[32];
+  __shared__ float wmap[32];
+  int e, m0, mend, nt;
+  if (!deal_tile<32>(offs, L, (int)a.P, col_tiles, e, m0, mend, nt)) return;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int j = lane & 31, h = lane >> 5;
+  if (tid < 32) {
+    const int p = m0 + tid < mend ? p2e[m0 + tid] : -1;
+    rmap[tid] = p;
+    wmap[tid] = p >= 0 ? a.w[p] : 0.f;
+  }
+  const uint4 z = make_uint4(0, 0, 0, 0);
+  const uint4* S4 = reinterpret_cast<const uint4*>(a.s);
+  const int i = m0 + j < mend ? m0 + j : mend - 1;   // rows past the bin repeat a valid one
+  const int64_t so = (int64_t)p2e[i] * RC;
+  uint4 sv[NS], bv[4][NS];
+#pragma unroll
+  for (int u = 0; u < NS; ++u) {
+    const int k8 = 2 * u + h;
+    sv[u] = S4[so + (k8 < RC ? k8 : 0)];
+  }
+  const int c0 = nt * GX_COLS + wid * 128;
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb) {
+    const int col = c0 + cb * 32 + j;
+    const int64_t bo = ((int64_t)e * a.N + (col < a.N ? col : a.N - 1)) * RC;
+#pragma unroll
+    for (int u = 0; u < NS; ++u) {
+      const int k8 = 2 * u + h;
+      bv[cb][u] = a.B[bo + (k8 < RC ? k8 : 0)];
+    }
+  }
+  f32x16 acc[4];
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[cb][v] = 0.f;
+#pragma unroll
+    for (int u = 0; u < NS; ++u) {
+      const bool ok = 2 * u + h < RC;   // rank 8: the upper half of the step is padding
+      acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          __builtin_bit_cast(bf16x8, ok ? sv[u] : z), __builtin_bit_cast(bf16x8, ok ? bv[cb][u] : z),
+          acc[cb], 0, 0, 0);
+    }
+  }
+  __syncthreads();   // rmap / wmap
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb) {
+    const int col = c0 + cb * 32 + j;
+    if (col >= a.N) continue;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int ri = 8 * q + 4 * h + r;
+        const int p = rmap[ri];
+        if (p >= 0) part[(int64_t)p * a.N + col] = wmap[ri] * acc[cb][4 * q + r];
+      }
+  }
 }
 
 // Last step: y[t, c] = sum over t's valid pairs, ascending p, of part[p, c]. One
-// workgroup per (token, 256 columns), thread = column; a token's pairs come from the
+// workgroup per (token, 256 x CPT columns), thread = CPT adjacent columns (4 when y's
+// rows are 16-byte aligned: 16-byte loads and stores); a token's pairs come from the
 // index (ranked ascending) or, beyond 16 pairs, from a scan of all pairs in order.
+template <int CPT>
 __global__ __launch_bounds__(256) void k_bgmv_combine(BgArgs a, const float* __restrict__ part,
                                                       int col_tiles) {
+  using V = typename std::conditional<CPT == 4, float4, float>::type;
   __shared__ int32_t plist[256];
   __shared__ int nlist;
   __shared__ int wcount[4];
   const int64_t t = blockIdx.x / col_tiles;
   const int ct = (int)(blockIdx.x - t * col_tiles);
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int c = ct * 256 + tid;
-  const bool col_ok = c < a.N;
-  float acc = 0.f;
+  const int c = (ct * 256 + tid) * CPT;
+  const bool col_ok = c < a.N;   // N is a multiple of 8
+  float acc[CPT];
+#pragma unroll
+  for (int u = 0; u < CPT; ++u) acc[u] = 0.f;
   auto add_list = [&](int nb) {   // plist[0 .. nb), loads first, then the ordered sum
     for (int i0 = 0; i0 < nb; i0 += 8) {
-      float v[8];
+      V v[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u)
-        v[u] = (i0 + u < nb && col_ok) ? part[(int64_t)plist[i0 + u] * a.N + c] : 0.f;
+        if (i0 + u < nb && col_ok) v[u] = *reinterpret_cast<const V*>(part + (int64_t)plist[i0 + u] * a.N + c);
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
-        if (i0 + u < nb) acc += v[u];
+      for (int u = 0; u < 8; ++u) {
+        if (!(i0 + u < nb && col_ok)) continue;
+        const float* f = reinterpret_cast<const float*>(&v[u]);
+#pragma unroll
+        for (int q = 0; q < CPT; ++q) acc[q] += f[q];
+      }
     }
   };
   const int n = a.cnt[t];
@@ -328,7 +501,13 @@ __global__ __launch_bounds__(256) void k_bgmv_combine(BgArgs a, const float* __r
       __syncthreads();   // wcount / nlist / plist are rewritten by the next chunk
     }
   }
-  if (col_ok) a.y[t * a.ldy + c] = acc;
+  if (col_ok) {
+    V o;
+    float* f = reinterpret_cast<float*>(&o);
+#pragma unroll
+    for (int q = 0; q < CPT; ++q) f[q] = acc[q];
+    *reinterpret_cast<V*>(a.y + t * a.ldy + c) = o;
+  }
 }
 
 }  // namespace
@@ -341,13 +520,14 @@ bool bgmv_grouped(int mode, int64_t P, int nl, int E) {
   if (bins > BG_GROUP_MAX_BINS || P == 0) return false;
   if (mode == MOE_BGMV_GROUPED) return true;
   if (mode == MOE_BGMV_PER_PAIR) return false;
-  // measured crossover (hidden 3072, rank 32, 4 LoRAs x 8 experts on MI355X): the
-  // grouped pipeline's sort and combine pay off from about 100 routes per bin
-  return P >= 96 * bins;
+  // measured crossover (hidden 3072, rank 32, 4 LoRAs x 8 experts on MI355X, cold
+  // cache): per pair / grouped 47.6 / 60.0 us at 32 routes per bin, 64.4 / 61.4 at 48,
+  // 77.6 / 62.2 at 64
+  return P >= 48 * bins;
 }
 
 struct BgGroupLayout {
-  size_t cnt, ri, bins, offs, e2p, p2e, n_sorted, gtok, s, part, sort_ws, split, split_cnt, total;
+  size_t cnt, ri, bins, offs, e2p, p2e, n_sorted, s, part, sort_ws, total;
 };
 
 BgGroupLayout bgmv_group_layout(int64_t T, int64_t P, int r, int N, int nl, int E) {
@@ -361,12 +541,9 @@ BgGroupLayout bgmv_group_layout(int64_t T, int64_t P, int r, int N, int nl, int 
   g.e2p = o;      o += align_up((size_t)P * 4, 256);
   g.p2e = o;      o += align_up((size_t)P * 4, 256);
   g.n_sorted = o; o += 256;
-  g.gtok = o;     o += align_up((size_t)P * 4, 256);
   g.s = o;        o += align_up((size_t)P * r * 2, 256);
   g.part = o;     o += align_up((size_t)P * N * 4, 256);
   g.sort_ws = o;  o += align_up(sort_workspace_bytes(P, 1, L), 256);
-  g.split = o;    o += (size_t)SPLIT_SLOTS * SPLIT_TILE_BYTES;
-  g.split_cnt = o; o += align_up((size_t)SPLIT_SLOTS * 4, 256);
   g.total = o;
   return g;
 }
@@ -381,8 +558,8 @@ size_t bgmv_workspace_bytes(int64_t T, int64_t P, int r) {
   return o;
 }
 
-// The grouped pipeline: bins + token index, stable sort by bin, the gathered-token
-// list, the shrink and expand grouped GEMMs, the per-token combine.
+// The grouped pipeline: bins + token index, stable sort by bin, the shrink (32 routes
+// of a bin per workgroup), the expand grouped GEMM, the per-token combine.
 moe_status bgmv_group_enqueue(const void* x, const void* A, const void* B, const int32_t* tok,
                               const int32_t* ex, const int32_t* lidx, const float* w,
                               void* shrink, float* y, int64_t ldy, int64_t T, int64_t P, int H,
@@ -411,34 +588,47 @@ moe_status bgmv_group_enqueue(const void* x, const void* A, const void* B, const
   int32_t* e2p = reinterpret_cast<int32_t*>(wp + g.e2p);
   int32_t* p2e = reinterpret_cast<int32_t*>(wp + g.p2e);
   int32_t* n_sorted = reinterpret_cast<int32_t*>(wp + g.n_sorted);
-  int32_t* gtok = reinterpret_cast<int32_t*>(wp + g.gtok);
   void* s = shrink ? shrink : (void*)(wp + g.s);
   a.s = reinterpret_cast<uint16_t*>(s);
   float* part = reinterpret_cast<float*>(wp + g.part);
-  int32_t* split_cnt = reinterpret_cast<int32_t*>(wp + g.split_cnt);
   k_bgmv_zero<<<(unsigned)((T + 255) / 256), 256, 0, st>>>(a.cnt, T, nullptr, 0);
   moe_status st_ = launch_status();
   if (st_ != MOE_OK) return st_;
   k_bgmv_bins<<<(unsigned)((P + 255) / 256), 256, 0, st>>>(a, bins);
   if ((st_ = launch_status()) != MOE_OK) return st_;
-  // stable sort of the pairs by bin (invalid pairs are foreign); also clears the
-  // split-tile counters of the two grouped GEMMs
+  // stable sort of the pairs by bin (invalid pairs are foreign)
   st_ = sort_enqueue(bins, P, 1, L, L, 0, offs, nullptr, e2p, p2e, n_sorted, wp + g.sort_ws, st,
-                     split_cnt, SPLIT_SLOTS);
+                     nullptr, 0);
   if (st_ != MOE_OK) return st_;
-  k_bgmv_gtok<<<(unsigned)((P + 255) / 256), 256, 0, st>>>(p2e, n_sorted, tok, gtok, P);
+  // shrink: s[p2e[i]] = bf16(x[tok[p2e[i]]] @ A[bin].T) for the sorted rows i of each bin
+  a.x = reinterpret_cast<const uint4*>(x);
+  a.A = reinterpret_cast<const uint4*>(A);
+  const int64_t chunks = P / 32 + std::min<int64_t>(L, P);   // 32-row tiles over L bins
+  const unsigned gsg = (unsigned)((chunks + 7) / 8 * 8);
+  if (r == 64)
+    k_bgmv_gshrink<2><<<gsg, GS_WAVES * 64, 0, st>>>(a, offs, L, p2e);
+  else
+    k_bgmv_gshrink<1><<<gsg, GS_WAVES * 64, 0, st>>>(a, offs, L, p2e);
   if ((st_ = launch_status()) != MOE_OK) return st_;
-  // shrink: s[p2e[i]] = bf16(x[gtok[i]] @ A[bin].T) for the sorted rows i of each bin
-  st_ = gemm_nt_enqueue(EPI_ROWMAP, x, gtok, 1, A, r, L, offs, P, r, H, s, r, 0, nullptr, 0.f,
-                        nullptr, p2e, 1, st, wp + g.split, split_cnt, nullptr, 256);
-  if (st_ != MOE_OK) return st_;
   // expand: part[p2e[i]] = w[p2e[i]] * (s[p2e[i]] @ B[bin].T), fp32
-  st_ = gemm_nt_enqueue(EPI_ROWMAP_F32W, s, p2e, 1, B, N, L, offs, P, N, r, part, N, 0, nullptr,
-                        0.f, w, p2e, 1, st, wp + g.split, split_cnt, nullptr, 256);
-  if (st_ != MOE_OK) return st_;
-  const int col_tiles = (N + 255) / 256;
+  a.B = reinterpret_cast<const uint4*>(B);
+  const int xt = (N + GX_COLS - 1) / GX_COLS;
+  const unsigned gxg = (unsigned)((chunks * xt + 7) / 8 * 8);
+  switch (r) {
+    case 8: k_bgmv_gexpand<8><<<gxg, 256, 0, st>>>(a, offs, L, p2e, part, xt); break;
+    case 16: k_bgmv_gexpand<16><<<gxg, 256, 0, st>>>(a, offs, L, p2e, part, xt); break;
+    case 32: k_bgmv_gexpand<32><<<gxg, 256, 0, st>>>(a, offs, L, p2e, part, xt); break;
+    default: k_bgmv_gexpand<64><<<gxg, 256, 0, st>>>(a, offs, L, p2e, part, xt); break;
+  }
+  if ((st_ = launch_status()) != MOE_OK) return st_;
+  // 4 columns per thread where every row of y starts 16-byte aligned
+  const bool vec = reinterpret_cast<uintptr_t>(y) % 16 == 0 && ldy % 4 == 0;
+  const int col_tiles = (N + (vec ? 1023 : 255)) / (vec ? 1024 : 256);
   if (T * col_tiles > INT32_MAX) return MOE_ERR_UNSUPPORTED;
-  k_bgmv_combine<<<(unsigned)(T * col_tiles), 256, 0, st>>>(a, part, col_tiles);
+  if (vec)
+    k_bgmv_combine<4><<<(unsigned)(T * col_tiles), 256, 0, st>>>(a, part, col_tiles);
+  else
+    k_bgmv_combine<1><<<(unsigned)(T * col_tiles), 256, 0, st>>>(a, part, col_tiles);
   return launch_status();
 }
 

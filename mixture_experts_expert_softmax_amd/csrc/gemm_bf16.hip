@@ -47,11 +47,7 @@ constexpr int TK = 64;         // contraction per stage
 constexpr int NTHREADS = 256;  // 4 waves
 constexpr int TILE_U4 = TB * TK * 2 / 16;  // uint4 slots per operand tile (2048)
 
-// EPI_ROWMAP stores bf16 row p at row p2e[p] of C; EPI_ROWMAP_F32W stores it in
-// float32 at row p2e[p], times route_w[p2e[p]] (the BGMV grouped pipeline's shrink rows
-// and weighted expand partials, written in pair order).
-enum Epi { EPI_STORE = 0, EPI_SWIGLU = 1, EPI_SWIGLU_STEP = 2, EPI_FUSED = 3, EPI_ROWMAP = 4,
-           EPI_ROWMAP_F32W = 5 };
+enum Epi { EPI_STORE = 0, EPI_SWIGLU = 1, EPI_SWIGLU_STEP = 2, EPI_FUSED = 3 };
 constexpr int SPLIT_MAX = 8;   // parts a split tile is cut into at most
 // The forward GEMMs take the work-queue kernel (k_gemm_nt_q) for at least QUEUE_GROUPS
 // groups of at most QUEUE_ROWS expected rows each: there about half the groups end in a
@@ -790,28 +786,7 @@ __device__ __forceinline__ void nt_tile(const NtArgs& a, uint4* smem, int e, int
   // of wave row wm starts at row 32 (wm jn + j) of the tile
   const int hi4 = (lane >> 5) * 4;
   constexpr bool FC1 = EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_STEP;
-  if constexpr (EPI == EPI_ROWMAP_F32W) {
-    // the BGMV expand's fp32 partials: few columns (the LoRA output width), stored
-    // straight from registers
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int p = m0 + wm * jn * 32 + j * 32 + (lane & 31);
-      if (j >= jn || p >= mend) continue;
-      const int row = a.p2e[p];
-      const float wgt = a.route_w[row];
-      float* crow = reinterpret_cast<float*>(a.C) + (int64_t)row * a.ldc;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int col = nt * TB + wn * 128 + i * 32 + q * 8 + hi4;
-          if (col >= a.N) continue;
-          *reinterpret_cast<float4*>(crow + col) =
-              make_float4(wgt * acc[i][j][q * 4 + 0], wgt * acc[i][j][q * 4 + 1],
-                          wgt * acc[i][j][q * 4 + 2], wgt * acc[i][j][q * 4 + 3]);
-        }
-    }
-  } else {
+  {
     // Staged through LDS (free once every wave is past the loop): in registers a lane
     // holds 4 columns of one row, so stores straight from registers would put 32 rows
     // x 8 bytes in each instruction -- 32 partial cache lines, whose write requests
@@ -888,8 +863,7 @@ __device__ __forceinline__ void nt_tile(const NtArgs& a, uint4* smem, int e, int
             atomic_add_bf16x2_bits(d + 4, v.z);
             atomic_add_bf16x2_bits(d + 6, v.w);
           } else {
-            const int64_t row = EPI == EPI_ROWMAP ? a.p2e[p] : p;
-            *reinterpret_cast<uint4*>(a.C + row * a.ldc + col) = v;
+            *reinterpret_cast<uint4*>(a.C + (int64_t)p * a.ldc + col) = v;
           }
         }
       }
@@ -1398,8 +1372,6 @@ moe_status gemm_nt_enqueue(int epi, const void* A, const int32_t* a_gather, int 
     case EPI_SWIGLU: MOE_LAUNCH_NTQ(EPI_SWIGLU); break;
     case EPI_SWIGLU_STEP: MOE_LAUNCH_NTQ(EPI_SWIGLU_STEP); break;
     case EPI_FUSED: MOE_LAUNCH_NTQ(EPI_FUSED); break;
-    case EPI_ROWMAP: MOE_LAUNCH_NT(EPI_ROWMAP); break;
-    case EPI_ROWMAP_F32W: MOE_LAUNCH_NT(EPI_ROWMAP_F32W); break;
     default: return MOE_ERR_DTYPE;
   }
 #undef MOE_LAUNCH_NTQ

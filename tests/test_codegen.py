@@ -15,7 +15,7 @@ import pytest
 
 from mixture_experts_expert_softmax_amd import _build
 
-SOURCES = ["gemm_bf16.hip", "gemm_mx.hip"]   # every MFMA kernel of the library
+SOURCES = ["gemm_bf16.hip", "gemm_mx.hip", "bgmv.hip"]   # every MFMA kernel of the library
 
 
 def _functions(asm: str):
