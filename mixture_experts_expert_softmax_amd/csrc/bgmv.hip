@@ -7,8 +7,8 @@
 //   expand  y[t, :] = sum over t's pairs, ascending p, of w[p] * (s[p] @ B[l, e].T)
 // with y in float32. Every output has one owner that sums its routes in that fixed
 // order, so results are the same on every run. Few pairs: the shrink splits the
-// hidden dimension over extra workgroups and the last one of a pair to finish sums
-// the fp32 partials in split order.
+// hidden dimension over extra workgroups and a second launch sums each pair's fp32
+// partials in split order.
 //
 // Both steps stream LoRA weights (cache- / HBM-bound GEMV work): one workgroup per
 // (pair, hidden split) for the shrink -- the x segment staged in LDS, each wave
@@ -61,7 +61,6 @@ struct BgArgs {
   int32_t* cnt;                // [T] routes published per token
   int32_t* ri;                 // [T][BG_SLOTS]
   float* part;                 // [P][S][r]
-  int32_t* scnt;               // [P] arrivals
   int64_t T, P;
   int H8, N, r, nl, E, S;
 };
@@ -85,11 +84,9 @@ __device__ __forceinline__ float dot8(uint4 u, uint4 v, float acc) {
   return acc;
 }
 
-__global__ __launch_bounds__(256) void k_bgmv_zero(int32_t* __restrict__ cnt, int64_t T,
-                                                   int32_t* __restrict__ scnt, int64_t P) {
+__global__ __launch_bounds__(256) void k_bgmv_zero(int32_t* __restrict__ cnt, int64_t T) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < T) cnt[i] = 0;
-  if (scnt && i < P) scnt[i] = 0;
 }
 
 // Workgroup (pair p, split sp) of the shrink; wave w owns rank rows w + 4i (RPW of
@@ -99,7 +96,6 @@ __global__ __launch_bounds__(256) void k_bgmv_zero(int32_t* __restrict__ cnt, in
 template <int RPW>
 __global__ __launch_bounds__(256) void k_bgmv_shrink(BgArgs a) {
   __shared__ uint4 xs[BG_XSEG];
-  __shared__ int last;
   const int64_t p = blockIdx.x / a.S;
   const int sp = (int)(blockIdx.x - p * a.S);
   const int tid = threadIdx.x, lane = tid & 63;
@@ -145,22 +141,22 @@ __global__ __launch_bounds__(256) void k_bgmv_shrink(BgArgs a) {
       else
         a.part[(p * a.S + sp) * a.r + j] = acc[i];
     }
-    if (a.S > 1) __threadfence();   // visible to the split that sums the partials
   }
-  if (a.S == 1) return;
-  // the last split of the pair to arrive sums the partials in split order
-  __syncthreads();
-  if (tid == 0) {
-    const int old = __hip_atomic_fetch_add(a.scnt + p, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    last = old == a.S - 1;
-  }
-  __syncthreads();
-  if (!last || tid >= a.r) return;
-  __atomic_thread_fence(__ATOMIC_ACQUIRE);
+}
+
+// Split shrink, second launch: s[p, j] = bf16 of the sum of pair p's S fp32 partials
+// in split order (the launch boundary orders the partials' stores before these loads;
+// a cross-workgroup release at agent scope, which writes back the XCD's L2, cost more
+// than the rest of the shrink). Thread = (pair, rank row).
+__global__ __launch_bounds__(256) void k_bgmv_split_sum(BgArgs a) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= a.P * a.r) return;
+  const int64_t p = i / a.r;
+  int t, e, l;
+  if (!pair_ok(a, p, t, e, l)) return;   // its row was zeroed by the shrink
   float v = 0.f;
-  for (int q = 0; q < a.S; ++q)
-    v += __hip_atomic_load(a.part + (p * a.S + q) * a.r + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  a.s[p * a.r + tid] = (uint16_t)(pack_bf16x2(v, 0.f) & 0xFFFFu);
+  for (int q = 0; q < a.S; ++q) v += a.part[p * a.S * a.r + q * a.r + (i - p * a.r)];
+  a.s[i] = (uint16_t)(pack_bf16x2(v, 0.f) & 0xFFFFu);
 }
 
 // Workgroup (token t, 256-column tile) of the expand; thread = output column. The
@@ -553,7 +549,6 @@ size_t bgmv_workspace_bytes(int64_t T, int64_t P, int r) {
   o += align_up((size_t)T * 4, 256);                       // cnt
   o += align_up((size_t)T * BG_SLOTS * 4, 256);            // ri
   o += align_up((size_t)P * BG_SPLIT_MAX * r * 4, 256);    // split partials
-  o += align_up((size_t)P * 4, 256);                       // split arrivals
   o += align_up((size_t)P * r * 2, 256);                   // shrink rows (if not the caller's)
   return o;
 }
@@ -591,7 +586,7 @@ moe_status bgmv_group_enqueue(const void* x, const void* A, const void* B, const
   void* s = shrink ? shrink : (void*)(wp + g.s);
   a.s = reinterpret_cast<uint16_t*>(s);
   float* part = reinterpret_cast<float*>(wp + g.part);
-  k_bgmv_zero<<<(unsigned)((T + 255) / 256), 256, 0, st>>>(a.cnt, T, nullptr, 0);
+  k_bgmv_zero<<<(unsigned)((T + 255) / 256), 256, 0, st>>>(a.cnt, T);
   moe_status st_ = launch_status();
   if (st_ != MOE_OK) return st_;
   k_bgmv_bins<<<(unsigned)((P + 255) / 256), 256, 0, st>>>(a, bins);
@@ -659,7 +654,6 @@ moe_status bgmv_enqueue(const void* x, const void* A, const void* B, const int32
   a.cnt = reinterpret_cast<int32_t*>(wp + o);  o += align_up((size_t)T * 4, 256);
   a.ri = reinterpret_cast<int32_t*>(wp + o);   o += align_up((size_t)T * BG_SLOTS * 4, 256);
   a.part = reinterpret_cast<float*>(wp + o);   o += align_up((size_t)P * BG_SPLIT_MAX * r * 4, 256);
-  a.scnt = reinterpret_cast<int32_t*>(wp + o); o += align_up((size_t)P * 4, 256);
   a.s = shrink ? reinterpret_cast<uint16_t*>(shrink) : reinterpret_cast<uint16_t*>(wp + o);
   // hidden splits: enough workgroups for two per CU, each split at least 64 chunks
   // per lane row pass and at most BG_XSEG chunks (its x segment lives in LDS)
@@ -672,8 +666,7 @@ moe_status bgmv_enqueue(const void* x, const void* A, const void* B, const int32
   while ((a.H8 + S - 1) / S > BG_XSEG) ++S;
   if (S > BG_SPLIT_MAX) return MOE_ERR_UNSUPPORTED;
   a.S = S;
-  const int64_t nz = std::max(T, P);
-  k_bgmv_zero<<<(unsigned)((nz + 255) / 256), 256, 0, st>>>(a.cnt, T, a.scnt, P);
+  k_bgmv_zero<<<(unsigned)((T + 255) / 256), 256, 0, st>>>(a.cnt, T);
   moe_status s = launch_status();
   if (s != MOE_OK) return s;
   if (P > 0) {
@@ -689,6 +682,11 @@ moe_status bgmv_enqueue(const void* x, const void* A, const void* B, const int32
       k_bgmv_shrink<16><<<g, 256, 0, st>>>(a);
     s = launch_status();
     if (s != MOE_OK) return s;
+    if (S > 1) {
+      k_bgmv_split_sum<<<(unsigned)((P * r + 255) / 256), 256, 0, st>>>(a);
+      s = launch_status();
+      if (s != MOE_OK) return s;
+    }
   }
   const int col_tiles = (N + 255) / 256;
   if (T * col_tiles > INT32_MAX) return MOE_ERR_UNSUPPORTED;
