@@ -274,13 +274,16 @@ constexpr int GS_WAVES = 8;
 template <int NCB>
 __global__ __launch_bounds__(GS_WAVES * 64) void k_bgmv_gshrink(BgArgs a,
                                                               const int32_t* __restrict__ offs,
-                                                              int L, const int32_t* __restrict__ p2e) {
+                                                              int L, const int32_t* __restrict__ p2e,
+                                                              int ks, float* __restrict__ hs) {
   // 64-value blocks a wave loads before it multiplies (all of them issued before the
   // first MFMA: one memory round trip per batch; hidden 3072 is one batch below rank 64)
   constexpr int GS_BATCH = 6 / NCB;
   __shared__ float red[GS_WAVES][NCB][16][64];
   int e, m0, mend, nt;
-  if (!deal_tile<32>(offs, L, (int)a.P, 1, e, m0, mend, nt)) return;
+  // nt: the tile's part of the contraction (ks parts; ks = 2 when the tiles would
+  // occupy at most half the CUs -- each part then leaves fp32 sums that the expand adds)
+  if (!deal_tile<32>(offs, L, (int)a.P, ks, e, m0, mend, nt)) return;
   const int tid = threadIdx.x, lane = tid & 63;
   // wave-uniform in a scalar register: the contraction loop below is then not a
   // lane-masked loop (an MFMA must run with every lane of the wave)
@@ -305,15 +308,16 @@ __global__ __launch_bounds__(GS_WAVES * 64) void k_bgmv_gshrink(BgArgs a,
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc[cb][v] = 0.f;
   const int nb = (a.H8 + 7) >> 3;
+  const int cbeg = nb * nt / ks, cend = nb * (nt + 1) / ks;   // this part's 64-value blocks
   const uint4 z = make_uint4(0, 0, 0, 0);
-  for (int c0 = wid; c0 < nb; c0 += GS_WAVES * GS_BATCH) {
+  for (int c0 = cbeg + wid; c0 < cend; c0 += GS_WAVES * GS_BATCH) {
     uint4 xv[GS_BATCH][4], wv[GS_BATCH][NCB][4];
 #pragma unroll
     for (int g = 0; g < GS_BATCH; ++g)
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int k8 = 8 * (c0 + GS_WAVES * g) + 4 * h + u;   // 16-byte chunk of the row
-        const bool ok = c0 + GS_WAVES * g < nb && k8 < a.H8;
+        const bool ok = c0 + GS_WAVES * g < cend && k8 < a.H8;
         const int kk = ok ? k8 : 0;
         xv[g][u] = a.x[xo + kk];
 #pragma unroll
@@ -325,7 +329,7 @@ __global__ __launch_bounds__(GS_WAVES * 64) void k_bgmv_gshrink(BgArgs a,
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int k8 = 8 * (c0 + GS_WAVES * g) + 4 * h + u;
-        const bool ok = c0 + GS_WAVES * g < nb && k8 < a.H8;
+        const bool ok = c0 + GS_WAVES * g < cend && k8 < a.H8;
         const uint4 xq = ok ? xv[g][u] : z;
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb)
@@ -341,7 +345,9 @@ __global__ __launch_bounds__(GS_WAVES * 64) void k_bgmv_gshrink(BgArgs a,
   __syncthreads();
   if (wid != 0 || m0 + j >= mend) return;
   // lane holds A rows 8 q + 4 h + 0..3 (accumulator entries 4 q + 0..3) of route j
-  uint16_t* out = a.s + (int64_t)p2e[m0 + j] * a.r;
+  const int64_t pj = p2e[m0 + j];
+  uint16_t* out = a.s + pj * a.r;
+  float* hout = hs + (pj * ks + nt) * a.r;
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
@@ -356,7 +362,10 @@ __global__ __launch_bounds__(GS_WAVES * 64) void k_bgmv_gshrink(BgArgs a,
         for (int w = 1; w < GS_WAVES; ++w) t += red[w][cb][4 * q + r][lane];
         f[r] = t;
       }
-      *reinterpret_cast<uint2*>(out + c) = make_uint2(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]));
+      if (ks == 1)
+        *reinterpret_cast<uint2*>(out + c) = make_uint2(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]));
+      else
+        *reinterpret_cast<float4*>(hout + c) = make_float4(f[0], f[1], f[2], f[3]);
     }
 }
 
@@ -372,7 +381,8 @@ constexpr int GX_COLS = 512;
 template <int R>
 __global__ __launch_bounds__(256) void k_bgmv_gexpand(BgArgs a, const int32_t* __restrict__ offs,
                                                       int L, const int32_t* __restrict__ p2e,
-                                                      float* __restrict__ part, int col_tiles) {
+                                                      float* __restrict__ part, int col_tiles,
+                                                      int ks, const float* __restrict__ hs) {
   constexpr int NS = (R + 15) / 16;   // MFMA steps
   constexpr int RC = R / 8;           // 16-byte chunks per rank row
   __shared__ int rmap[32];
@@ -390,12 +400,25 @@ __global__ __launch_bounds__(256) void k_bgmv_gexpand(BgArgs a, const int32_t* _
   const uint4 z = make_uint4(0, 0, 0, 0);
   const uint4* S4 = reinterpret_cast<const uint4*>(a.s);
   const int i = m0 + j < mend ? m0 + j : mend - 1;   // rows past the bin repeat a valid one
-  const int64_t so = (int64_t)p2e[i] * RC;
+  const int64_t pi = p2e[i];
+  const int64_t so = pi * RC;
   uint4 sv[NS], bv[4][NS];
 #pragma unroll
   for (int u = 0; u < NS; ++u) {
     const int k8 = 2 * u + h;
-    sv[u] = S4[so + (k8 < RC ? k8 : 0)];
+    const int kk = k8 < RC ? k8 : 0;
+    if (ks == 1) {
+      sv[u] = S4[so + kk];
+    } else {
+      // a shrink cut in two parts: s = bf16(part 0 + part 1), written out by the
+      // route's first column tile
+      const float4* h0 = reinterpret_cast<const float4*>(hs + pi * 2 * R) + 2 * kk;
+      const float4* h1 = h0 + R / 4;
+      const float4 a0 = h0[0], a1 = h0[1], b0 = h1[0], b1 = h1[1];
+      sv[u] = make_uint4(pack_bf16x2(a0.x + b0.x, a0.y + b0.y), pack_bf16x2(a0.z + b0.z, a0.w + b0.w),
+                         pack_bf16x2(a1.x + b1.x, a1.y + b1.y), pack_bf16x2(a1.z + b1.z, a1.w + b1.w));
+      if (nt == 0 && m0 + j < mend && k8 < RC) reinterpret_cast<uint4*>(a.s)[so + k8] = sv[u];
+    }
   }
   const int c0 = nt * GX_COLS + wid * 128;
 #pragma unroll
@@ -523,7 +546,7 @@ bool bgmv_grouped(int mode, int64_t P, int nl, int E) {
 }
 
 struct BgGroupLayout {
-  size_t cnt, ri, bins, offs, e2p, p2e, n_sorted, s, part, sort_ws, total;
+  size_t cnt, ri, bins, offs, e2p, p2e, n_sorted, s, hs, part, sort_ws, total;
 };
 
 BgGroupLayout bgmv_group_layout(int64_t T, int64_t P, int r, int N, int nl, int E) {
@@ -538,6 +561,7 @@ BgGroupLayout bgmv_group_layout(int64_t T, int64_t P, int r, int N, int nl, int 
   g.p2e = o;      o += align_up((size_t)P * 4, 256);
   g.n_sorted = o; o += 256;
   g.s = o;        o += align_up((size_t)P * r * 2, 256);
+  g.hs = o;       o += align_up((size_t)P * 2 * r * 4, 256);   // two-part shrink sums
   g.part = o;     o += align_up((size_t)P * N * 4, 256);
   g.sort_ws = o;  o += align_up(sort_workspace_bytes(P, 1, L), 256);
   g.total = o;
@@ -599,21 +623,28 @@ moe_status bgmv_group_enqueue(const void* x, const void* A, const void* B, const
   a.x = reinterpret_cast<const uint4*>(x);
   a.A = reinterpret_cast<const uint4*>(A);
   const int64_t chunks = P / 32 + std::min<int64_t>(L, P);   // 32-row tiles over L bins
-  const unsigned gsg = (unsigned)((chunks + 7) / 8 * 8);
+  // at most half as many tiles as CUs: cut each tile's contraction in two (twice the
+  // workgroups, each moving half the bytes, still one round of one per CU). Measured
+  // (hidden 3072, rank 32, 32 bins, cold cache): 1024 tokens 62.3 -> 60.4 us, 512
+  // tokens 60.1 -> 56.2 us; at 2048 tokens the doubled grid takes a second round and
+  // the shrink went from 19 to 31 us.
+  const int ks = 2 * chunks <= device_cu_count() ? 2 : 1;
+  float* hs = reinterpret_cast<float*>(wp + g.hs);
+  const unsigned gsg = (unsigned)((chunks * ks + 7) / 8 * 8);
   if (r == 64)
-    k_bgmv_gshrink<2><<<gsg, GS_WAVES * 64, 0, st>>>(a, offs, L, p2e);
+    k_bgmv_gshrink<2><<<gsg, GS_WAVES * 64, 0, st>>>(a, offs, L, p2e, ks, hs);
   else
-    k_bgmv_gshrink<1><<<gsg, GS_WAVES * 64, 0, st>>>(a, offs, L, p2e);
+    k_bgmv_gshrink<1><<<gsg, GS_WAVES * 64, 0, st>>>(a, offs, L, p2e, ks, hs);
   if ((st_ = launch_status()) != MOE_OK) return st_;
   // expand: part[p2e[i]] = w[p2e[i]] * (s[p2e[i]] @ B[bin].T), fp32
   a.B = reinterpret_cast<const uint4*>(B);
   const int xt = (N + GX_COLS - 1) / GX_COLS;
   const unsigned gxg = (unsigned)((chunks * xt + 7) / 8 * 8);
   switch (r) {
-    case 8: k_bgmv_gexpand<8><<<gxg, 256, 0, st>>>(a, offs, L, p2e, part, xt); break;
-    case 16: k_bgmv_gexpand<16><<<gxg, 256, 0, st>>>(a, offs, L, p2e, part, xt); break;
-    case 32: k_bgmv_gexpand<32><<<gxg, 256, 0, st>>>(a, offs, L, p2e, part, xt); break;
-    default: k_bgmv_gexpand<64><<<gxg, 256, 0, st>>>(a, offs, L, p2e, part, xt); break;
+    case 8: k_bgmv_gexpand<8><<<gxg, 256, 0, st>>>(a, offs, L, p2e, part, xt, ks, hs); break;
+    case 16: k_bgmv_gexpand<16><<<gxg, 256, 0, st>>>(a, offs, L, p2e, part, xt, ks, hs); break;
+    case 32: k_bgmv_gexpand<32><<<gxg, 256, 0, st>>>(a, offs, L, p2e, part, xt, ks, hs); break;
+    default: k_bgmv_gexpand<64><<<gxg, 256, 0, st>>>(a, offs, L, p2e, part, xt, ks, hs); break;
   }
   if ((st_ = launch_status()) != MOE_OK) return st_;
   // 4 columns per thread where every row of y starts 16-byte aligned
