@@ -83,11 +83,25 @@ def test_bgmv_shapes(H, feat_out, top_k, T, grouped):
     _check(c, y, s)
 
 
+@pytest.mark.parametrize("rank", [16, 64])
+@pytest.mark.parametrize("T", [96, 2048])
+def test_bgmv_grouped_contraction_whole_and_in_two(T, rank):
+    """The grouped shrink cuts each 32-route tile's contraction in two when the tiles
+    would fill at most half the CUs (T=96) and keeps it whole otherwise (T=2048, 160
+    tiles); rank 64 takes two MFMA column blocks per tile. Hidden 1032 ends in a partial
+    64-value block and 520 output columns in a partial 512-column tile; all against
+    the oracle's bound."""
+    c = S.bgmv_case(seed=T + rank, T=T, H=1032, rank=rank, num_loras=4, E=8, top_k=2,
+                    feat_out=520, order="random")
+    y, s = _run(c, grouped=True)
+    _check(c, y, s)
+
+
 @pytest.mark.parametrize("grouped", [None, True])
 def test_bgmv_few_pairs_split_hidden_and_invalid_indices(grouped):
-    """3 tokens, 4 pairs: the shrink splits the hidden dimension (last-arriving split
-    sums the partials); invalid token / expert / LoRA indices contribute nothing and
-    tokens without a pair get zero rows."""
+    """3 tokens, 4 pairs: the shrink splits the hidden dimension (a second launch sums
+    the partials); invalid token / expert / LoRA indices contribute nothing and tokens
+    without a pair get zero rows."""
     c = S.bgmv_case(seed=7, T=3, H=4096, rank=16, num_loras=2, E=8, top_k=2, order="random")
     tok, ex, li, w = (c.sorted_token_ids.copy(), c.expert_ids.copy(), c.lora_indices.copy(),
                       c.topk_weights.copy())
