@@ -84,11 +84,13 @@ def test_bgmv_shapes(H, feat_out, top_k, T, grouped):
 
 
 @pytest.mark.parametrize("rank", [16, 64])
-@pytest.mark.parametrize("T", [96, 2048])
+@pytest.mark.parametrize("T", [96, 2048, 2560])
 def test_bgmv_grouped_contraction_whole_and_in_two(T, rank):
     """The grouped shrink cuts each 32-route tile's contraction in two when the tiles
     would fill at most half the CUs (T=96) and keeps it whole otherwise (T=2048, 160
-    tiles); rank 64 takes two MFMA column blocks per tile. Hidden 1032 ends in a partial
+    tiles); rank 64 takes two MFMA column blocks per tile. Up to 4096 pairs one
+    workgroup bins and places the pairs; 5120 pairs (T=2560) take the clear, bin and
+    stable-sort launches. Hidden 1032 ends in a partial
     64-value block and 520 output columns in a partial 512-column tile; all against
     the oracle's bound."""
     c = S.bgmv_case(seed=T + rank, T=T, H=1032, rank=rank, num_loras=4, E=8, top_k=2,
