@@ -431,8 +431,9 @@ typedef struct moe_bgmv_desc {
 } moe_bgmv_desc;
 
 /* Pipelines of moe_bgmv ([BGMV] Parameters: grouped). The per-pair pipeline reads
- * every pair's LoRA slices; the grouped one sorts the pairs stably by (LoRA, expert)
- * bin, runs the shrink and the expand on MFMA tiles of 32 sorted pairs of one bin
+ * every pair's LoRA slices; the grouped one groups the pairs by (LoRA, expert) bin
+ * (order within a bin does not affect the results), runs the shrink and the expand on
+ * MFMA tiles of 32 pairs of one bin
  * (each bin's weights streamed once per tile of pairs), stores w[p] times each pair's
  * fp32 expand row and sums a token's rows in ascending pair order. Both are
  * deterministic; they round differently within float32 (the shrink's and the expand's

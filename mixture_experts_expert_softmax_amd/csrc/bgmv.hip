@@ -19,9 +19,9 @@
 // scans all pairs in order for a token with more than 16.
 //
 // Grouped pipeline (BGMV page, Parameters: grouped), for many routes per (LoRA,
-// expert) bin: the pairs are sorted stably by bin (moe_sort's kernels, one bin per
-// (LoRA, expert)); the shrink and the expand then run on bf16 MFMAs over tiles of 32
-// sorted routes of one bin (x rows gathered through the routes' tokens against the
+// expert) bin: the pairs are grouped by bin (one workgroup up to 4096 pairs, else
+// moe_sort's kernels with one bin per (LoRA, expert)); the shrink and the expand then
+// run on bf16 MFMAs over tiles of 32 routes of one bin (x rows gathered through the routes' tokens against the
 // bin's A, K = hidden; shrink rows against the bin's B, K = rank), so each bin's
 // weights are streamed once per tile of routes rather than once per pair. Both keep
 // their operands in registers: the rank (8-64) is far narrower than the 256-wide
