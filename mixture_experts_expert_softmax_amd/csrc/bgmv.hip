@@ -268,8 +268,9 @@ __global__ __launch_bounds__(256) void k_bgmv_bins(BgArgs a, int32_t* __restrict
 // sits in its tile and the combine adds by pair index, so the results do not depend
 // on it.
 // Measured (hidden 3072, rank 32, 32 bins, cold cache, whole grouped call): 4096
-// pairs 76.3 -> 72.8 us, 2048 pairs 60.2 -> 53.9 us; at 16384 pairs one workgroup is
-// too little (204.8 -> 220.3 us), so the three launches stay there.
+// pairs 76.3 -> 69.4 us, 2048 pairs 60.2 -> 52.6 us; at 16384 pairs one workgroup is
+// too little (204.8 -> 220.3 us with 16 pairs per thread), so the three launches stay
+// there.
 constexpr int GP_THREADS = 1024;
 constexpr int GP_PER_THREAD = 4;
 constexpr int GP_MAX_PAIRS = GP_THREADS * GP_PER_THREAD;
@@ -285,22 +286,38 @@ __global__ __launch_bounds__(GP_THREADS) void k_bgmv_prep(BgArgs a, int L, int32
   for (int64_t t = tid; t < a.T; t += GP_THREADS)
     __hip_atomic_store(a.cnt + t, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
-  int bin[GP_PER_THREAD], slot[GP_PER_THREAD];
+  // each stage for all of the thread's pairs before the next (loads, then the
+  // dependent loads, then the atomics), so their latencies overlap
+  int tk[GP_PER_THREAD], ek[GP_PER_THREAD], lk[GP_PER_THREAD], bin[GP_PER_THREAD],
+      slot[GP_PER_THREAD], ts[GP_PER_THREAD];
 #pragma unroll
   for (int k = 0; k < GP_PER_THREAD; ++k) {
-    const int64_t p = tid + (int64_t)k * GP_THREADS;
-    bin[k] = -1;
-    if (p >= a.P) continue;
-    int t, e, l;
-    if (!pair_ok(a, p, t, e, l)) {   // contributes nothing; its shrink row reads as zeros
-      for (int j = 0; j < a.r; ++j) a.s[p * a.r + j] = 0;
-      continue;
-    }
-    bin[k] = l * a.E + e;
-    slot[k] = atomicAdd(&cntb[bin[k]], 1);
-    const int ts = atomicAdd(a.cnt + t, 1);
-    if (ts < BG_SLOTS) a.ri[(int64_t)t * BG_SLOTS + ts] = (int32_t)p;
+    const int p = tid + k * GP_THREADS;
+    tk[k] = p < a.P ? a.tok[p] : -1;
+    ek[k] = p < a.P ? a.ex[p] : -1;
   }
+#pragma unroll
+  for (int k = 0; k < GP_PER_THREAD; ++k) {
+    const bool ok = tk[k] >= 0 && tk[k] < a.T && ek[k] >= 0 && ek[k] < a.E;
+    lk[k] = ok ? a.lidx[tk[k]] : -1;
+  }
+#pragma unroll
+  for (int k = 0; k < GP_PER_THREAD; ++k) {
+    const int p = tid + k * GP_THREADS;
+    const bool valid = tk[k] >= 0 && tk[k] < a.T && ek[k] >= 0 && ek[k] < a.E && lk[k] >= 0 &&
+                       lk[k] < a.nl;
+    bin[k] = valid ? lk[k] * a.E + ek[k] : -1;
+    if (valid) {
+      slot[k] = atomicAdd(&cntb[bin[k]], 1);
+      ts[k] = atomicAdd(a.cnt + tk[k], 1);
+    } else if (p < a.P) {   // contributes nothing; its shrink row reads as zeros
+      for (int j = 0; j < a.r; ++j) a.s[(int64_t)p * a.r + j] = 0;
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < GP_PER_THREAD; ++k)
+    if (bin[k] >= 0 && ts[k] < BG_SLOTS)
+      a.ri[(int64_t)tk[k] * BG_SLOTS + ts[k]] = tid + k * GP_THREADS;
   __syncthreads();
   // bin ends: inclusive scan of the counts (waves, then the wave totals)
   const int v = tid < L ? cntb[tid] : 0;
